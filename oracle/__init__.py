@@ -1,0 +1,215 @@
+"""fp64 CPU oracle for the SSM scan + causal conv1d path -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The product path (``ssm_sequence_models_amd``) never does, and the
+two share no code: this package wraps ``ssm_oracle.c`` (plain C, double precision, written
+straight from the definitions on the pages) through ctypes.
+
+Every function takes CPU arrays (numpy or torch, any float dtype; bf16 and fp32 widen to
+fp64 exactly), returns new numpy float64 arrays, and never modifies its inputs.  Outputs are
+rounded once to the storage type named by ``out_dtype`` ("bf16", "f32" or "f64").
+
+Definitions followed (page title and section):
+  * conv1d_fwd      causal-conv1d tutorial ch. 7, "defining the state through the extended
+                    sequence" and "packed-sequence boundaries";
+  * conv1d_update   same chapter, "single-token update maths", "the physical cache may exceed
+                    the minimal history", "state indices for continuous batching";
+  * scan_fwd, step  length-generalization reading notes, Sec. 2.1 Eq. (1) and Sec. 2.5
+                    Eq. (4), with the initial state in and the final state out (Sec. 2.6);
+  * conv_scan_fwd   conv1d_fwd (phi applied, output rounded to the input dtype) followed by
+                    the split into x | B | C channels and scan_fwd.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssm_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+ROUND = {"f64": 0, "f32": 1, "bf16": 2}
+ACT = {"none": 0, "silu": 1}
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (fp64, OpenMP, no fp contraction)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", src, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, out)
+    return out
+
+
+def load_library(path: str):
+    lib = ctypes.CDLL(path)
+    lib.orc_round.restype = ctypes.c_double
+    lib.orc_round.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.orc_max_threads.restype = ctypes.c_int
+    lib.orc_conv1d_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _ip, _dp, _i64, _i64, _i64, _i64,
+                                   ctypes.c_int, ctypes.c_int]
+    lib.orc_conv1d_update.argtypes = [_dp, _dp, _dp, _dp, _ip, _ip, _dp, _i64, _i64, _i64, _i64,
+                                      _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.orc_scan_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _i64, _i64, _i64,
+                                 _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.orc_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _i64, _i64, _i64, _i64,
+                             _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    for f in ("orc_conv1d_fwd", "orc_conv1d_update", "orc_scan_fwd", "orc_step"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+def _get():
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = load_library(build())
+        return _lib
+
+
+def max_threads() -> int:
+    return int(_get().orc_max_threads())
+
+
+def _f64(a):
+    """Widen a CPU array (numpy or torch, any float dtype) to a contiguous float64 array."""
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return np.ascontiguousarray(a.detach().cpu().to(torch.float64).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a):
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p(a, t=_dp):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def round_to(a, out_dtype: str) -> np.ndarray:
+    """Round every element once to ``out_dtype`` (nearest even)."""
+    lib = _get()
+    arr = _f64(a)
+    flat = arr.reshape(-1)
+    out = np.empty_like(flat)
+    mode = ROUND[out_dtype]
+    for i in range(flat.size):
+        out[i] = lib.orc_round(float(flat[i]), mode)
+    return out.reshape(arr.shape)
+
+
+def conv1d_fwd(x, w, bias=None, init_state=None, seq_idx=None, act="none", out_dtype="f64",
+               lib=None):
+    """x [B, L, C]; w [C, K]; bias [C]; init_state [B, C, K-1]; seq_idx [B, L].
+
+    Returns (out [B, L, C], final_state [B, C, K-1])."""
+    lib = lib or _get()
+    x, w, bias, init_state = _f64(x), _f64(w), _f64(bias), _f64(init_state)
+    seq_idx = _i32(seq_idx)
+    B, L, C = x.shape
+    K = w.shape[1]
+    out = np.zeros((B, L, C))
+    fin = np.zeros((B, C, K - 1))
+    lib.orc_conv1d_fwd(_p(x), _p(w), _p(bias), _p(init_state), _p(fin), _p(seq_idx, _ip),
+                       _p(out), B, L, C, K, ACT[act], ROUND[out_dtype])
+    return out, fin
+
+
+def conv1d_update(x, pool, w, bias=None, indices=None, cache_seqlens=None, act="none",
+                  out_dtype="f64", lib=None):
+    """x [B, C, L_new]; pool [n_slots, C, state_len]; indices, cache_seqlens [B].
+
+    Returns (out [B, C, L_new], new_pool)."""
+    lib = lib or _get()
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    pool = _f64(pool).copy()
+    indices, cache_seqlens = _i32(indices), _i32(cache_seqlens)
+    B, C, L_new = x.shape
+    n_slots, _, state_len = pool.shape
+    K = w.shape[1]
+    out = np.zeros((B, C, L_new))
+    lib.orc_conv1d_update(_p(x), _p(pool), _p(w), _p(bias), _p(indices, _ip),
+                          _p(cache_seqlens, _ip), _p(out), B, C, L_new, K, state_len, n_slots,
+                          ACT[act], ROUND[out_dtype])
+    return out, pool
+
+
+def scan_fwd(x, dt, A, Bm, Cm, init_state=None, seq_idx=None, out_dtype="f64",
+             state_dtype="f64", lib=None):
+    """x [B, L, H, P]; dt [B, L, H]; A [H]; Bm, Cm [B, L, G, N]; init_state [B, H, P, N].
+
+    Returns (y [B, L, H, P], final_state [B, H, P, N])."""
+    lib = lib or _get()
+    x, dt, A, Bm, Cm, init_state = (_f64(v) for v in (x, dt, A, Bm, Cm, init_state))
+    seq_idx = _i32(seq_idx)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    y = np.zeros((B, L, H, P))
+    fin = np.zeros((B, H, P, N))
+    lib.orc_scan_fwd(_p(x), _p(dt), _p(A), _p(Bm), _p(Cm), _p(init_state), _p(fin),
+                     _p(seq_idx, _ip), _p(y), B, L, H, P, G, N, ROUND[out_dtype],
+                     ROUND[state_dtype])
+    return y, fin
+
+
+def step(x, dt, A, Bm, Cm, pool, indices=None, out_dtype="f64", state_dtype="f64", lib=None):
+    """x [B, L_new, H, P]; dt [B, L_new, H]; Bm, Cm [B, L_new, G, N];
+    pool [n_slots, H, P, N]; indices [B].
+
+    Returns (y [B, L_new, H, P], new_pool)."""
+    lib = lib or _get()
+    x, dt, A, Bm, Cm = (_f64(v) for v in (x, dt, A, Bm, Cm))
+    pool = _f64(pool).copy()
+    indices = _i32(indices)
+    B, L_new, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    n_slots = pool.shape[0]
+    y = np.zeros((B, L_new, H, P))
+    lib.orc_step(_p(x), _p(dt), _p(A), _p(Bm), _p(Cm), _p(pool), _p(indices, _ip), _p(y), B,
+                 L_new, H, P, G, N, n_slots, ROUND[out_dtype], ROUND[state_dtype])
+    return y, pool
+
+
+def conv_scan_fwd(xBC, conv_w, conv_bias, conv_init, dt, A, ssm_init, seq_idx, H, P, G, N,
+                  act="silu", out_dtype="bf16", state_dtype="f32", lib=None):
+    """The fused prefill: conv1d_fwd over the x | B | C channels of xBC [B, L, H*P + 2*G*N]
+    (phi applied, output rounded to the input dtype ``out_dtype``), split, then scan_fwd.
+
+    Returns (y [B, L, H, P], conv_final [B, C, K-1], ssm_final [B, H, P, N])."""
+    conv_out, conv_fin = conv1d_fwd(xBC, conv_w, conv_bias, conv_init, seq_idx, act=act,
+                                    out_dtype=out_dtype, lib=lib)
+    B, L, Ctot = conv_out.shape
+    assert Ctot == H * P + 2 * G * N
+    x = conv_out[:, :, :H * P].reshape(B, L, H, P)
+    Bm = conv_out[:, :, H * P:H * P + G * N].reshape(B, L, G, N)
+    Cm = conv_out[:, :, H * P + G * N:].reshape(B, L, G, N)
+    y, ssm_fin = scan_fwd(x, dt, A, Bm, Cm, ssm_init, seq_idx, out_dtype=out_dtype,
+                          state_dtype=state_dtype, lib=lib)
+    return y, conv_fin, ssm_fin

@@ -1,0 +1,310 @@
+/*
+ * ssm_oracle.c -- plain, slow fp64 CPU oracle for the SSM scan + causal conv1d path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load this file's library.  The product path (the HIP library under
+ * ssm_sequence_models_amd/) shares no code with it and never calls it.
+ *
+ * Sources (cited by page title and section; no line numbers):
+ *   [LG]  "Understanding and Improving Length Generalization in Recurrent Models: reading
+ *         notes" (arXiv:2507.02782v2).  Sec. 2.1 Eq. (1) (the recurrence and the initial
+ *         state h_{-1}); Sec. 2.5 Eq. (4) (unrolling with a non-zero initial state);
+ *         Sec. 2.6 (State Passing / TBTT: initial state in, final state out).
+ *   [CC]  Causal-conv1d tutorial, chapter 7 "State, chunking and incremental inference".
+ *         Sections: "defining the state through the extended sequence" (u, z_t, F);
+ *         "single-token update maths"; "the physical cache may exceed the minimal history"
+ *         (state_len, circular mode with cache_seqlens); "state indices for continuous
+ *         batching" (conv_state_indices); "packed-sequence boundaries" (seq_idx).
+ *
+ * Everything is computed in double precision straight from the definitions: no chunking,
+ * no blocking, no reordering.  Inputs arrive as doubles (the Python wrapper widens bf16 and
+ * fp32 exactly); outputs are rounded once to the requested storage type.
+ *
+ * Readings taken where the pages leave a step open (all listed in the design notes):
+ *   - a_t = exp(dt_t * A_h) and the input term dt_t * B_t * x_t (Mamba-2-style scalar decay;
+ *     [LG] Sec. 2.5 says the transition enters in log space).  Parity unpinned beyond
+ *     convention for the dt factor on B; with dt = 1 it is exactly Eq. (1).
+ *   - each of a head's P channels is one copy of Eq. (1) sharing a_t, B_t, C_t; head h uses
+ *     group g = h / (H / G).
+ *   - seq_idx in the scan: the state is zeroed where seq_idx changes between t-1 and t;
+ *     in the conv, the initial state S belongs to the segment of token 0.
+ *   - phi is either the identity or SiLU, z * sigmoid(z).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of threads the parallel loops below use (1 without OpenMP). */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Rounding modes for outputs. */
+#define ORC_ROUND_NONE 0 /* keep fp64 */
+#define ORC_ROUND_F32 1  /* round to nearest even fp32 */
+#define ORC_ROUND_BF16 2 /* round to nearest even bfloat16 (8 significant bits) */
+
+#define ORC_ACT_NONE 0
+#define ORC_ACT_SILU 1
+
+/* Round a double to bfloat16 precision, nearest-even, straight from the double (no
+ * intermediate fp32 step, so no double rounding).  bfloat16 keeps 8 significant bits for
+ * normal numbers (exponent down to 2^-126) and a fixed quantum of 2^-133 below that. */
+static double round_bf16(double v) {
+    if (v != v || v == 0.0 || isinf(v)) return v;
+    int e;
+    (void)frexp(fabs(v), &e); /* |v| = m * 2^e with m in [0.5, 1) */
+    int q = e - 8;            /* quantum of an 8-significant-bit number of that size */
+    if (q < -133) q = -133;
+    double r = ldexp(nearbyint(ldexp(fabs(v), -q)), q);
+    const double bf16_max = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    if (r > bf16_max) r = INFINITY;
+    return copysign(r, v);
+}
+
+double orc_round(double v, int mode) {
+    if (mode == ORC_ROUND_F32) return (double)(float)v;
+    if (mode == ORC_ROUND_BF16) return round_bf16(v);
+    return v;
+}
+
+static double act_apply(double z, int act) {
+    if (act == ORC_ACT_SILU) return z / (1.0 + exp(-z));
+    return z;
+}
+
+static int64_t floor_mod(int64_t a, int64_t m) {
+    int64_t r = a % m;
+    return r < 0 ? r + m : r;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Causal depthwise conv1d with state in / out ([CC] "defining the state through the
+ * extended sequence", "packed-sequence boundaries").
+ *
+ *   u = [S_0 .. S_{K-2}, x_0 .. x_{L-1}]           (S oldest -> newest; S = 0 if absent)
+ *   z_t = beta + sum_k w_k u_{t+k}                  (w_{K-1} multiplies the current x_t)
+ *   out_t = round(phi(z_t)),   F = u[L : L+K-1]     (a raw copy; also right for L < K-1)
+ *
+ * With seq_idx, a tap contributes only when its token carries the same identity as the
+ * output token (identity equality, as the page describes); S carries the identity of
+ * token 0.  F stays the unmasked raw slice.
+ *
+ * Layouts: x, out [B][L][C]; w [C][K]; bias [C]; init_state, final_state [B][C][K-1];
+ * seq_idx [B][L].
+ * ------------------------------------------------------------------------------------- */
+int orc_conv1d_fwd(const double* x, const double* w, const double* bias,
+                   const double* init_state, double* final_state, const int32_t* seq_idx,
+                   double* out, int64_t B, int64_t L, int64_t C, int64_t K, int act,
+                   int out_round) {
+    const int64_t U = K - 1 + L;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t c = 0; c < C; ++c) {
+            double* u = (double*)malloc(sizeof(double) * (size_t)(U > 0 ? U : 1));
+            int32_t* id = (int32_t*)malloc(sizeof(int32_t) * (size_t)(U > 0 ? U : 1));
+            for (int64_t j = 0; j < U; ++j) {
+                if (j < K - 1) {
+                    u[j] = init_state ? init_state[(b * C + c) * (K - 1) + j] : 0.0;
+                    id[j] = (seq_idx && L > 0) ? seq_idx[b * L + 0] : 0;
+                } else {
+                    u[j] = x[(b * L + (j - (K - 1))) * C + c];
+                    id[j] = seq_idx ? seq_idx[b * L + (j - (K - 1))] : 0;
+                }
+            }
+            for (int64_t t = 0; t < L; ++t) {
+                double z = bias ? bias[c] : 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    if (seq_idx && id[t + k] != id[t + K - 1]) continue;
+                    z += w[c * K + k] * u[t + k];
+                }
+                out[(b * L + t) * C + c] = orc_round(act_apply(z, act), out_round);
+            }
+            if (final_state) {
+                for (int64_t r = 0; r < K - 1; ++r)
+                    final_state[(b * C + c) * (K - 1) + r] = u[L + r];
+            }
+            free(u);
+            free(id);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Decode update of the conv state ([CC] "single-token update maths", "the physical cache
+ * may exceed the minimal history", "state indices for continuous batching").
+ *
+ * Row b uses pool slot s = indices[b] (or b).  A slot outside [0, n_slots) is skipped and
+ * its output row is zero-filled.
+ *
+ * The K-1 history values are read from the pool BEFORE anything is written:
+ *   circular (cache_seqlens given, p = cache_seqlens[b]):
+ *       history j (j = 1 .. K-1 steps back) sits in slot floor_mod(p - j, state_len);
+ *       new token i is written to slot floor_mod(p + i, state_len);
+ *   linear (cache_seqlens NULL): the row holds the newest state_len inputs, oldest first;
+ *       the history is its last K-1 entries; afterwards the row becomes the last state_len
+ *       entries of (old row ++ new tokens).
+ * Outputs follow the extended-sequence definition over [history, new tokens]; the pool
+ * stores the raw inputs x (never the outputs).  cache_seqlens is read, never advanced.
+ *
+ * Layouts: x, out [B][C][L_new]; pool [n_slots][C][state_len]; w [C][K].
+ * ------------------------------------------------------------------------------------- */
+int orc_conv1d_update(const double* x, double* pool, const double* w, const double* bias,
+                      const int32_t* indices, const int32_t* cache_seqlens, double* out,
+                      int64_t B, int64_t C, int64_t L_new, int64_t K, int64_t state_len,
+                      int64_t n_slots, int act, int out_round) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t s = indices ? (int64_t)indices[b] : b;
+            double* o = out + (b * C + c) * L_new;
+            if (s < 0 || s >= n_slots) {
+                for (int64_t i = 0; i < L_new; ++i) o[i] = 0.0;
+                continue;
+            }
+            double* row = pool + (s * C + c) * state_len;
+            const double* xr = x + (b * C + c) * L_new;
+            const int64_t U = K - 1 + L_new;
+            double* u = (double*)malloc(sizeof(double) * (size_t)U);
+            /* u[0 .. K-2] = history oldest -> newest; u[K-1 ..] = new tokens */
+            for (int64_t j = 1; j <= K - 1; ++j) {
+                double h;
+                if (cache_seqlens) {
+                    const int64_t p = cache_seqlens[b];
+                    h = row[floor_mod(p - j, state_len)];
+                } else {
+                    h = row[state_len - j];
+                }
+                u[K - 1 - j] = h;
+            }
+            for (int64_t i = 0; i < L_new; ++i) u[K - 1 + i] = xr[i];
+            for (int64_t i = 0; i < L_new; ++i) {
+                double z = bias ? bias[c] : 0.0;
+                for (int64_t k = 0; k < K; ++k) z += w[c * K + k] * u[i + k];
+                o[i] = orc_round(act_apply(z, act), out_round);
+            }
+            /* write the raw new inputs into the cache */
+            if (cache_seqlens) {
+                const int64_t p = cache_seqlens[b];
+                for (int64_t i = 0; i < L_new; ++i) row[floor_mod(p + i, state_len)] = xr[i];
+            } else {
+                const int64_t total = state_len + L_new;
+                double* ext = (double*)malloc(sizeof(double) * (size_t)total);
+                for (int64_t i = 0; i < state_len; ++i) ext[i] = row[i];
+                for (int64_t i = 0; i < L_new; ++i) ext[state_len + i] = xr[i];
+                for (int64_t i = 0; i < state_len; ++i) row[i] = ext[total - state_len + i];
+                free(ext);
+            }
+            free(u);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Selective scan with initial state in and final state out ([LG] Sec. 2.1 Eq. (1),
+ * Sec. 2.5 Eq. (4), Sec. 2.6).  For every (b, h), with g = h / (H / G):
+ *
+ *   state[p][n] = h_{-1}[b][h][p][n]  (0 if absent)
+ *   for t:  (state = 0 where seq_idx[b][t] != seq_idx[b][t-1], t > 0)
+ *           a = exp(dt[b][t][h] * A[h])
+ *           state[p][n] = a * state[p][n] + dt[b][t][h] * x[b][t][h][p] * Bm[b][t][g][n]
+ *           y[b][t][h][p] = round(sum_n Cm[b][t][g][n] * state[p][n])
+ *   final_state = round(state)
+ *
+ * Layouts: x, y [B][L][H][P]; dt [B][L][H]; A [H]; Bm, Cm [B][L][G][N];
+ * init_state, final_state [B][H][P][N]; seq_idx [B][L].
+ * ------------------------------------------------------------------------------------- */
+int orc_scan_fwd(const double* x, const double* dt, const double* A, const double* Bm,
+                 const double* Cm, const double* init_state, double* final_state,
+                 const int32_t* seq_idx, double* y, int64_t B, int64_t L, int64_t H,
+                 int64_t P, int64_t G, int64_t N, int y_round, int state_round) {
+    const int64_t heads_per_group = H / G;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t g = h / heads_per_group;
+            double* st = (double*)malloc(sizeof(double) * (size_t)(P * N));
+            for (int64_t e = 0; e < P * N; ++e)
+                st[e] = init_state ? init_state[(b * H + h) * P * N + e] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                if (seq_idx && t > 0 && seq_idx[b * L + t] != seq_idx[b * L + t - 1])
+                    for (int64_t e = 0; e < P * N; ++e) st[e] = 0.0;
+                const double d = dt[(b * L + t) * H + h];
+                const double a = exp(d * A[h]);
+                const double* xt = x + ((b * L + t) * H + h) * P;
+                const double* Bt = Bm + ((b * L + t) * G + g) * N;
+                const double* Ct = Cm + ((b * L + t) * G + g) * N;
+                for (int64_t p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        st[p * N + n] = a * st[p * N + n] + d * xt[p] * Bt[n];
+                        acc += Ct[n] * st[p * N + n];
+                    }
+                    y[((b * L + t) * H + h) * P + p] = orc_round(acc, y_round);
+                }
+            }
+            if (final_state)
+                for (int64_t e = 0; e < P * N; ++e)
+                    final_state[(b * H + h) * P * N + e] = orc_round(st[e], state_round);
+            free(st);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Decode step of the scan on a state pool: the same recurrence as orc_scan_fwd, token by
+ * token over the L_new new tokens of request b, on pool slot s = indices[b] (or b).  The
+ * state is carried in double precision across the L_new tokens of one call and stored back
+ * rounded (state_round) at the end.  A slot outside [0, n_slots) is skipped and its y rows
+ * are zero-filled; the pool is left untouched for it.
+ *
+ * Layouts: x, y [B][L_new][H][P]; dt [B][L_new][H]; Bm, Cm [B][L_new][G][N];
+ * pool [n_slots][H][P][N].
+ * ------------------------------------------------------------------------------------- */
+int orc_step(const double* x, const double* dt, const double* A, const double* Bm,
+             const double* Cm, double* pool, const int32_t* indices, double* y, int64_t B,
+             int64_t L_new, int64_t H, int64_t P, int64_t G, int64_t N, int64_t n_slots,
+             int y_round, int state_round) {
+    const int64_t heads_per_group = H / G;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t s = indices ? (int64_t)indices[b] : b;
+            if (s < 0 || s >= n_slots) {
+                for (int64_t t = 0; t < L_new; ++t)
+                    for (int64_t p = 0; p < P; ++p) y[((b * L_new + t) * H + h) * P + p] = 0.0;
+                continue;
+            }
+            const int64_t g = h / heads_per_group;
+            double* st = pool + (s * H + h) * P * N;
+            for (int64_t t = 0; t < L_new; ++t) {
+                const double d = dt[(b * L_new + t) * H + h];
+                const double a = exp(d * A[h]);
+                const double* xt = x + ((b * L_new + t) * H + h) * P;
+                const double* Bt = Bm + ((b * L_new + t) * G + g) * N;
+                const double* Ct = Cm + ((b * L_new + t) * G + g) * N;
+                for (int64_t p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        st[p * N + n] = a * st[p * N + n] + d * xt[p] * Bt[n];
+                        acc += Ct[n] * st[p * N + n];
+                    }
+                    y[((b * L_new + t) * H + h) * P + p] = orc_round(acc, y_round);
+                }
+            }
+            for (int64_t e = 0; e < P * N; ++e) st[e] = orc_round(st[e], state_round);
+        }
+    }
+    return 0;
+}

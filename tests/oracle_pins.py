@@ -1,0 +1,545 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+Each ``check_*`` takes the oracle's ctypes library (so the same checks can be run against
+deliberately broken copies of the oracle) and raises AssertionError on a mismatch.  None of
+them re-types the oracle's own loop: they use the pages' worked examples, closed forms,
+brute-force unrollings, library routines (torch fp64 conv1d / cumsum / silu / bf16 cast) and
+invariants.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------------------------------
+# causal conv1d with state
+# ------------------------------------------------------------------------------------------
+
+def check_conv_worked_example_k4(lib):
+    """causal-conv1d ch. 7, extended-sequence section: K = 4, S = [a,b,c], x = [d]."""
+    g = _golden("conv_state_k4.json")
+    sym = g["symbols"]
+    K = g["K"]
+    S = np.array([[[sym[s] for s in g["S"]]]])           # [1, 1, 3]
+    x = np.array([[[sym[s]] for s in g["x"]]])           # [1, 1, 1]
+    w = np.array([[1.0, 10.0, 100.0, 1000.0]])           # distinct decimal digits per tap
+    out, fin = oracle.conv1d_fwd(x, w, None, S, lib=lib)
+    window = [sym[s] for s in g["window"]]
+    expect_z = sum(w[0, k] * window[k] for k in range(K))
+    assert out[0, 0, 0] == expect_z, (out, expect_z)
+    expect_F = [sym[s] for s in g["F"]]
+    assert fin[0, 0].tolist() == expect_F, fin
+    wrong = [sym[s] if isinstance(s, str) else s for s in g["wrong_zero_padded_F"]]
+    assert fin[0, 0].tolist() != wrong
+
+
+def check_conv_single_token_k3(lib):
+    """causal-conv1d ch. 7, single-token chunk example (forward): z and F = [b, c]."""
+    g = _golden("conv_single_token_k3.json")
+    sym = g["symbols"]
+    S = np.array([[[sym["a"], sym["b"]]]])
+    x = np.array([[[sym["c"]]]])
+    w = np.array([g["w"]])
+    out, fin = oracle.conv1d_fwd(x, w, np.array([g["beta"]]), S, lib=lib)
+    assert out[0, 0, 0] == g["z"], out
+    assert fin[0, 0].tolist() == [sym[s] for s in g["F"]], fin
+
+
+def check_conv_matches_torch(lib):
+    """General case against torch fp64 conv1d (cross-correlation, groups = C) over
+    cat(S, x): the extended-sequence definition is exactly that library routine."""
+    r = _rng(1)
+    for (B, L, C, K) in [(2, 37, 5, 4), (1, 9, 3, 2), (3, 20, 4, 3), (1, 2, 6, 4)]:
+        x = r.standard_normal((B, L, C))
+        w = r.standard_normal((C, K))
+        bias = r.standard_normal(C)
+        S = r.standard_normal((B, C, K - 1))
+        out, fin = oracle.conv1d_fwd(x, w, bias, S, lib=lib)
+        u = torch.cat([torch.from_numpy(S), torch.from_numpy(x).transpose(1, 2)], dim=2)
+        ref = torch.nn.functional.conv1d(u, torch.from_numpy(w)[:, None, :],
+                                         torch.from_numpy(bias), groups=C)
+        np.testing.assert_allclose(out, ref.transpose(1, 2).numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(fin, u[:, :, L:L + K - 1].numpy())
+        # absent state means zeros
+        out0, _ = oracle.conv1d_fwd(x, w, bias, None, lib=lib)
+        u0 = torch.cat([torch.zeros(B, C, K - 1, dtype=torch.float64),
+                        torch.from_numpy(x).transpose(1, 2)], dim=2)
+        ref0 = torch.nn.functional.conv1d(u0, torch.from_numpy(w)[:, None, :],
+                                          torch.from_numpy(bias), groups=C)
+        np.testing.assert_allclose(out0, ref0.transpose(1, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def check_conv_silu_matches_torch(lib):
+    """phi = SiLU against torch fp64 silu (identity tap w = [0, .., 0, 1], no bias)."""
+    r = _rng(2)
+    x = r.standard_normal((2, 50, 3)) * 6.0
+    w = np.zeros((3, 4))
+    w[:, 3] = 1.0
+    out, _ = oracle.conv1d_fwd(x, w, None, None, act="silu", lib=lib)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-300)
+
+
+def check_conv_short_chunks_keep_state(lib):
+    """L < K-1: F still holds entries of S (extended-sequence section)."""
+    K = 4
+    S = np.array([[[11.0, 12.0, 13.0]]])
+    w = np.ones((1, K))
+    for L in (0, 1, 2):
+        x = np.arange(1, L + 1, dtype=np.float64).reshape(1, L, 1)
+        _, fin = oracle.conv1d_fwd(x, w, None, S, lib=lib)
+        u = [11.0, 12.0, 13.0] + list(range(1, L + 1))
+        assert fin[0, 0].tolist() == u[L:L + K - 1], (L, fin)
+
+
+def check_conv_chunk_continuation(lib):
+    """Running chunk A then chunk B with S_B = F_A equals the full run (ch. 7, 'chunked
+    training and truncated backprop'), for every split point, bit-exact in fp64."""
+    r = _rng(3)
+    B, L, C, K = 2, 11, 3, 4
+    x = r.standard_normal((B, L, C))
+    w = r.standard_normal((C, K))
+    bias = r.standard_normal(C)
+    S = r.standard_normal((B, C, K - 1))
+    full, ffin = oracle.conv1d_fwd(x, w, bias, S, act="silu", lib=lib)
+    for cut in range(0, L + 1):
+        oa, fa = oracle.conv1d_fwd(x[:, :cut], w, bias, S, act="silu", lib=lib)
+        ob, fb = oracle.conv1d_fwd(x[:, cut:], w, bias, fa, act="silu", lib=lib)
+        np.testing.assert_array_equal(np.concatenate([oa, ob], axis=1), full)
+        np.testing.assert_array_equal(fb, ffin)
+
+
+def check_conv_seq_idx_segments(lib):
+    """Packed sequences with distinct (monotone) ids equal separate runs: the first segment
+    continues from S, later ones start from zero history (ch. 7, 'packed-sequence
+    boundaries')."""
+    r = _rng(4)
+    B, L, C, K = 1, 23, 3, 4
+    x = r.standard_normal((B, L, C))
+    w = r.standard_normal((C, K))
+    bias = r.standard_normal(C)
+    S = r.standard_normal((B, C, K - 1))
+    bounds = [0, 1, 7, 9, 23]       # segments of length 1, 6, 2, 14
+    seq = np.zeros((B, L), dtype=np.int32)
+    for i in range(len(bounds) - 1):
+        seq[0, bounds[i]:bounds[i + 1]] = i
+    out, fin = oracle.conv1d_fwd(x, w, bias, S, seq_idx=seq, act="silu", lib=lib)
+    for i in range(len(bounds) - 1):
+        a, b = bounds[i], bounds[i + 1]
+        ref, _ = oracle.conv1d_fwd(x[:, a:b], w, bias, S if i == 0 else None, act="silu",
+                                   lib=lib)
+        np.testing.assert_array_equal(out[:, a:b], ref)
+    # the final state is the unmasked raw tail
+    np.testing.assert_array_equal(fin[0], x[0, L - (K - 1):].T)
+
+
+def check_conv_seq_idx_reuse_caveat(lib):
+    """ids A, B, A with a short B: identity equality does not see the reset, so the second
+    A segment still reads the first A's tail (the page's stated caveat)."""
+    K = 4
+    x = np.array([[[1.0], [2.0], [3.0], [100.0], [5.0]]])     # ids 0 0 0 1 0
+    seq = np.array([[0, 0, 0, 1, 0]], dtype=np.int32)
+    w = np.array([[1.0, 10.0, 1000.0, 10000.0]])
+    out, _ = oracle.conv1d_fwd(x, w, None, None, seq_idx=seq, lib=lib)
+    # token 4 (id 0): window u[4..7] = x[1], x[2], x[3], x[4]; x[3] (id 1) masked
+    assert out[0, 4, 0] == 1.0 * 2.0 + 10.0 * 3.0 + 10000.0 * 5.0, out[0, :, 0]
+    # token 3 (id 1): only itself
+    assert out[0, 3, 0] == 10000.0 * 100.0
+
+
+# ------------------------------------------------------------------------------------------
+# conv decode update
+# ------------------------------------------------------------------------------------------
+
+def check_ring_buffer_worked_example(lib):
+    """ch. 7 circular mode: K = 3, S_len = 4, p = 5 -> history in slots 3 and 0, the new
+    input goes to slot 1."""
+    g = _golden("ring_buffer_k3.json")
+    K, S_len, p = g["K"], g["state_len"], g["p"]
+    pool = np.array([[[10.0, 20.0, 30.0, 40.0]]])            # slot s holds 10*(s+1)
+    w = np.array([[1.0, 100.0, 10000.0]])                    # w0 oldest .. w2 current
+    x = np.array([[[7.0]]])
+    out, newpool = oracle.conv1d_update(x, pool, w, None, None, np.array([p], np.int32),
+                                        lib=lib)
+    older, newer = g["history_slots"]                        # logical 3 -> slot 3, 4 -> 0
+    expect = w[0, 0] * pool[0, 0, older] + w[0, 1] * pool[0, 0, newer] + w[0, 2] * 7.0
+    assert out[0, 0, 0] == expect, (out, expect)
+    ws = g["write_slot"]
+    after = pool[0, 0].copy()
+    after[ws] = 7.0
+    np.testing.assert_array_equal(newpool[0, 0], after)
+
+
+def check_ring_wraps_backwards(lib):
+    """Circular mode before K-1 tokens were written (p < K-1): history j sits in slot
+    (p - j) mod S_len taken as a non-negative remainder (the page's slot rule; what such
+    never-written slots hold is the caller's business)."""
+    K, S_len, p = 4, 4, 1
+    pool = np.array([[[10.0, 20.0, 30.0, 40.0]]])
+    w = np.array([[1.0, 100.0, 10000.0, 0.0]])               # oldest .. newest history
+    out, newpool = oracle.conv1d_update(np.array([[[5.0]]]), pool, w, None, None,
+                                        np.array([p], np.int32), lib=lib)
+    # j = 3, 2, 1 steps back -> slots (1-3) mod 4 = 2, (1-2) mod 4 = 3, (1-1) mod 4 = 0
+    assert out[0, 0, 0] == 1.0 * 30.0 + 100.0 * 40.0 + 10000.0 * 10.0, out
+    assert newpool[0, 0].tolist() == [10.0, 5.0, 30.0, 40.0]
+
+
+def _write_history(pool_row, hist, state_len):
+    """Place a logical history (positions 0 .. len-1) into a circular row."""
+    for q, v in enumerate(hist):
+        pool_row[q % state_len] = v
+
+
+def check_update_equals_fwd(lib):
+    """Decode update over [history, new tokens] equals conv1d_fwd with the last K-1
+    history inputs as S, in circular and linear modes, for L_new in {1, 3, 4}; the pool then
+    holds the raw inputs x (never y)."""
+    r = _rng(5)
+    C, K = 3, 4
+    w = r.standard_normal((C, K))
+    bias = r.standard_normal(C)
+    for S_len in (3, 4, 6):
+        for p in (3, 5, 9, 12):
+            for L_new in (1, 3, 4):
+                hist = r.standard_normal((C, p))
+                x = r.standard_normal((1, C, L_new))
+                pool = r.standard_normal((2, C, S_len))      # slot 1 is the request's
+                for c in range(C):
+                    _write_history(pool[1, c], hist[c], S_len)
+                out, newpool = oracle.conv1d_update(x, pool, w, bias, np.array([1], np.int32),
+                                                    np.array([p], np.int32), act="silu",
+                                                    lib=lib)
+                S = hist[:, p - (K - 1):][None]
+                ref, _ = oracle.conv1d_fwd(x.transpose(0, 2, 1), w, bias, S, act="silu",
+                                           lib=lib)
+                np.testing.assert_array_equal(out, ref.transpose(0, 2, 1))
+                expect_row = pool[1].copy()
+                for c in range(C):
+                    _write_history(expect_row[c], list(hist[c]) + list(x[0, c]), S_len)
+                np.testing.assert_array_equal(newpool[1], expect_row)
+                np.testing.assert_array_equal(newpool[0], pool[0])   # untouched slot
+                # linear mode: the row holds the newest S_len inputs, oldest first
+                lin = np.stack([np.concatenate([np.zeros(S_len), hist[c]])[-S_len:]
+                                for c in range(C)])
+                pool_l = pool.copy()
+                pool_l[1] = lin
+                out_l, newpool_l = oracle.conv1d_update(x, pool_l, w, bias,
+                                                        np.array([1], np.int32), None,
+                                                        act="silu", lib=lib)
+                np.testing.assert_array_equal(out_l, out)
+                for c in range(C):
+                    seq = list(lin[c]) + list(x[0, c])
+                    np.testing.assert_array_equal(newpool_l[1, c], seq[-S_len:])
+
+
+def check_update_state_len_invariance(lib):
+    """A linear cache longer than K-1 does not change the receptive field (ch. 7, 'the
+    physical cache may exceed the minimal history')."""
+    r = _rng(6)
+    C, K = 4, 4
+    w = r.standard_normal((C, K))
+    x = r.standard_normal((2, C, 2))
+    tail = r.standard_normal((2, C, K - 1))
+    short = tail.copy()
+    long_ = np.concatenate([r.standard_normal((2, C, 6)), tail], axis=2)   # K + 5 = 9
+    o1, _ = oracle.conv1d_update(x, short, w, lib=lib)
+    o2, _ = oracle.conv1d_update(x, long_, w, lib=lib)
+    np.testing.assert_array_equal(o1, o2)
+
+
+def check_update_indices_and_range(lib):
+    """conv_state_indices maps rows to slots; out-of-range rows are skipped with zero
+    outputs; untouched slots stay bit-identical; cache_seqlens is not advanced."""
+    r = _rng(7)
+    C, K, S_len, n_slots = 3, 4, 4, 6
+    w = r.standard_normal((C, K))
+    pool = r.standard_normal((n_slots, C, S_len))
+    x = r.standard_normal((4, C, 2))
+    idx = np.array([4, -1, 1, n_slots], np.int32)
+    seqlens = np.array([7, 3, 0, 2], np.int32)
+    seqlens_before = seqlens.copy()
+    out, newpool = oracle.conv1d_update(x, pool, w, None, idx, seqlens, lib=lib)
+    assert np.all(out[1] == 0) and np.all(out[3] == 0)
+    np.testing.assert_array_equal(seqlens, seqlens_before)
+    for s in (0, 2, 3, 5):
+        np.testing.assert_array_equal(newpool[s], pool[s])
+    # row 0 -> slot 4 behaves like a single request on slot 0 of a one-slot pool
+    o0, p0 = oracle.conv1d_update(x[:1], pool[4:5], w, None, None, seqlens[:1], lib=lib)
+    np.testing.assert_array_equal(out[0], o0[0])
+    np.testing.assert_array_equal(newpool[4], p0[0])
+
+
+# ------------------------------------------------------------------------------------------
+# scan
+# ------------------------------------------------------------------------------------------
+
+def _scalar_ar1_inputs(n_chains_b, H, P, L, a, sigma0=None, seed=8):
+    r = _rng(seed)
+    x = r.standard_normal((n_chains_b, L, H, P))
+    dt = np.ones((n_chains_b, L, H))
+    A = np.full(H, math.log(a))
+    ones = np.ones((n_chains_b, L, 1, 1))
+    init = None
+    if sigma0 is not None:
+        init = r.standard_normal((n_chains_b, H, P, 1)) * sigma0
+    return x, dt, A, ones, init
+
+
+def check_scan_variance_closed_form(lib):
+    """Sec. 2.4 teaching example: h_t = a h_{t-1} + x_t, h_{-1} = 0 has
+    Var(h_t) = (1 - a^(2(t+1))) / (1 - a^2); at a = 0.99 the page prints ~47.4 % of the
+    steady state after 32 tokens and near-steady after 512.  Monte Carlo over 262,144
+    chains (dt = 1, A = ln a, B = C = 1, N = 1), within 4 standard errors."""
+    g = _golden("variance_ar1.json")
+    a = g["a"]
+    vinf = 1.0 / (1.0 - a * a)
+
+    def ratio(t):
+        return (1.0 - a ** (2 * (t + 1))) / (1.0 - a * a) / vinf
+
+    t32 = g["after_32_tokens_t_index"]
+    assert round(ratio(t32), g["printed_digits"]) == g["after_32_tokens_ratio_printed"]
+    assert ratio(g["after_512_tokens_t_index"]) > g["after_512_tokens_min_ratio"]
+    # 64 x 64 x 64 = 262,144 chains over 32 tokens
+    x, dt, A, ones, _ = _scalar_ar1_inputs(64, 64, 64, 32, a)
+    y, fin = oracle.scan_fwd(x, dt, A, ones, ones, lib=lib)
+    M = y.shape[0] * y.shape[2] * y.shape[3]
+    se = math.sqrt(2.0 / M)
+    for t in (0, 7, t32):
+        est = y[:, t].var() / vinf
+        assert abs(est / ratio(t) - 1.0) < 4 * se, (t, est, ratio(t))
+    # the final state is h_{L-1}
+    np.testing.assert_array_equal(fin[..., 0], y[:, -1])
+    # near-steady after 512 tokens (65,536 chains), and a non-zero initial state
+    # h_{-1} ~ N(0, s0^2) adds a^(2(t+1)) s0^2
+    s0 = 3.0
+    x, dt, A, ones, init = _scalar_ar1_inputs(16, 64, 64, 512, a, sigma0=s0, seed=9)
+    y, _ = oracle.scan_fwd(x, dt, A, ones, ones, init_state=init, lib=lib)
+    M = y.shape[0] * y.shape[2] * y.shape[3]
+    se = math.sqrt(2.0 / M)
+    for t in (0, 31, 511):
+        expect = ratio(t) * vinf + a ** (2 * (t + 1)) * s0 * s0
+        assert abs(y[:, t].var() / expect - 1.0) < 4 * se, (t, y[:, t].var(), expect)
+
+
+def _bruteforce_eq4(x, dt, A, Bm, Cm, h0):
+    """Sec. 2.5 Eq. (4), written out with explicit time-ordered products:
+    y_t = C_t^T sum_{s<=t} (prod_{tau=s+1..t} a_tau) B_s dt_s x_s
+          + C_t^T (prod_{tau=0..t} a_tau) h_{-1}."""
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    y = np.zeros((B, L, H, P))
+    for b in range(B):
+        for h in range(H):
+            g = h * G // H
+            a = [math.exp(dt[b, tau, h] * A[h]) for tau in range(L)]
+            for t in range(L):
+                for p in range(P):
+                    tot = 0.0
+                    for s in range(t + 1):
+                        prod = 1.0
+                        for tau in range(s + 1, t + 1):
+                            prod *= a[tau]
+                        cb = sum(Cm[b, t, g, n] * Bm[b, s, g, n] for n in range(N))
+                        tot += prod * cb * dt[b, s, h] * x[b, s, h, p]
+                    if h0 is not None:
+                        prod = 1.0
+                        for tau in range(0, t + 1):
+                            prod *= a[tau]
+                        tot += prod * sum(Cm[b, t, g, n] * h0[b, h, p, n] for n in range(N))
+                    y[b, t, h, p] = tot
+    return y
+
+
+def _small_scan_inputs(seed, B=2, L=9, H=4, P=3, N=5, G=2):
+    r = _rng(seed)
+    x = r.standard_normal((B, L, H, P))
+    dt = np.log1p(np.exp(r.standard_normal((B, L, H)) - 1.0))
+    A = -np.exp(r.uniform(0.0, math.log(4.0), H))
+    Bm = r.standard_normal((B, L, G, N))
+    Cm = r.standard_normal((B, L, G, N))
+    h0 = r.standard_normal((B, H, P, N))
+    return x, dt, A, Bm, Cm, h0
+
+
+def check_scan_bruteforce_eq4(lib):
+    """The recurrence equals the explicit Eq. (4) unrolling (tiny shapes, G = 2 groups)."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(10)
+    y, _ = oracle.scan_fwd(x, dt, A, Bm, Cm, h0, lib=lib)
+    ref = _bruteforce_eq4(x, dt, A, Bm, Cm, h0)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_scan_initial_state_term(lib):
+    """With x = 0 only the initial-state term of Eq. (4) remains:
+    y_t = C_t^T (prod_{tau<=t} a_tau) h_{-1}; the final state is (prod a) h_{-1}."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(11, B=2, L=6, H=3, P=2, N=4, G=1)
+    x[:] = 0.0
+    y, fin = oracle.scan_fwd(x, dt, A, Bm, Cm, h0, lib=lib)
+    B, L, H, P = x.shape
+    for b in range(B):
+        for h in range(H):
+            prod = 1.0
+            for t in range(L):
+                prod *= math.exp(dt[b, t, h] * A[h])
+                for p in range(P):
+                    expect = prod * float(np.dot(Cm[b, t, 0], h0[b, h, p]))
+                    assert abs(y[b, t, h, p] - expect) <= 1e-12 * (1 + abs(expect))
+            np.testing.assert_allclose(fin[b, h], prod * h0[b, h], rtol=1e-12)
+
+
+def check_scan_superposition(lib):
+    """Affine in (x, h_{-1}): y(x, h0) = y(x, 0) + y(0, h0) (the split of Eq. (4))."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(12, B=2, L=15, H=4, P=3, N=6, G=1)
+    y, f = oracle.scan_fwd(x, dt, A, Bm, Cm, h0, lib=lib)
+    y1, f1 = oracle.scan_fwd(x, dt, A, Bm, Cm, None, lib=lib)
+    y2, f2 = oracle.scan_fwd(np.zeros_like(x), dt, A, Bm, Cm, h0, lib=lib)
+    np.testing.assert_allclose(y, y1 + y2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(f, f1 + f2, rtol=1e-12, atol=1e-12)
+
+
+def check_scan_special_cases(lib):
+    """A = 0 (a = 1): the state is h_{-1} plus the running sum of dt x B (torch cumsum), and
+    a perturbation of h_{-1} persists unchanged.  A -> -inf (a = 0): y_t = dt_t x_t C_t.B_t."""
+    x, dt, _, Bm, Cm, h0 = _small_scan_inputs(13, B=2, L=12, H=3, P=2, N=4, G=1)
+    A0 = np.zeros(3)
+    y, fin = oracle.scan_fwd(x, dt, A0, Bm, Cm, h0, lib=lib)
+    xt = torch.from_numpy(x)
+    inc = torch.einsum("blh,blhp,bln->blhpn", torch.from_numpy(dt), xt,
+                       torch.from_numpy(Bm[:, :, 0]))
+    st = torch.cumsum(inc, dim=1) + torch.from_numpy(h0)[:, None]
+    ref = torch.einsum("blhpn,bln->blhp", st, torch.from_numpy(Cm[:, :, 0])).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(fin, st[:, -1].numpy(), rtol=1e-12, atol=1e-12)
+    delta = np.zeros_like(h0)
+    delta[0, 1, 1, 2] = 0.5
+    _, fin2 = oracle.scan_fwd(x, dt, A0, Bm, Cm, h0 + delta, lib=lib)
+    np.testing.assert_allclose(fin2 - fin, delta, atol=1e-12)
+    Aneg = np.full(3, -1e300)
+    y, _ = oracle.scan_fwd(x, dt, Aneg, Bm, Cm, h0, lib=lib)
+    cb = np.einsum("bln,bln->bl", Cm[:, :, 0], Bm[:, :, 0])
+    ref = dt[..., None] * x * cb[:, :, None, None]
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_scan_chunk_continuation(lib):
+    """State passing: scan(A) then scan(B, h_{-1} = final_A) equals the full scan, for every
+    split point, bit-exact in fp64 (Sec. 2.6 SP / TBTT)."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(14, B=2, L=10, H=2, P=3, N=4, G=1)
+    full, ffin = oracle.scan_fwd(x, dt, A, Bm, Cm, h0, lib=lib)
+    for cut in range(0, 11):
+        ya, fa = oracle.scan_fwd(x[:, :cut], dt[:, :cut], A, Bm[:, :cut], Cm[:, :cut], h0,
+                                 lib=lib)
+        yb, fb = oracle.scan_fwd(x[:, cut:], dt[:, cut:], A, Bm[:, cut:], Cm[:, cut:], fa,
+                                 lib=lib)
+        np.testing.assert_array_equal(np.concatenate([ya, yb], axis=1), full)
+        np.testing.assert_array_equal(fb, ffin)
+
+
+def check_scan_seq_idx_segments(lib):
+    """Packed sequences: monotone ids equal separate runs, the first from h_{-1} and the
+    rest from zero; the final state is the last segment's."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(15, B=1, L=17, H=2, P=2, N=3, G=1)
+    bounds = [0, 5, 6, 12, 17]
+    seq = np.zeros((1, 17), np.int32)
+    for i in range(4):
+        seq[0, bounds[i]:bounds[i + 1]] = i
+    y, fin = oracle.scan_fwd(x, dt, A, Bm, Cm, h0, seq_idx=seq, lib=lib)
+    for i in range(4):
+        a, b = bounds[i], bounds[i + 1]
+        ref, rf = oracle.scan_fwd(x[:, a:b], dt[:, a:b], A, Bm[:, a:b], Cm[:, a:b],
+                                  h0 if i == 0 else None, lib=lib)
+        np.testing.assert_array_equal(y[:, a:b], ref)
+    np.testing.assert_array_equal(fin, rf)
+
+
+def check_step_equals_scan(lib):
+    """Decode step == scan: one call over all tokens is bit-exact, token-by-token calls with
+    fp64 pool storage are bit-exact too; slots are addressed through indices; an
+    out-of-range slot is skipped (zero y, pool untouched)."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(16, B=2, L=7, H=4, P=3, N=5, G=2)
+    y, fin = oracle.scan_fwd(x, dt, A, Bm, Cm, h0, lib=lib)
+    n_slots = 5
+    pool = _rng(17).standard_normal((n_slots, 4, 3, 5))
+    idx = np.array([3, 0], np.int32)
+    pool[idx] = h0
+    ys, newpool = oracle.step(x, dt, A, Bm, Cm, pool, idx, lib=lib)
+    np.testing.assert_array_equal(ys, y)
+    np.testing.assert_array_equal(newpool[idx], fin)
+    for s in (1, 2, 4):
+        np.testing.assert_array_equal(newpool[s], pool[s])
+    cur = pool.copy()
+    for t in range(7):
+        yt, cur = oracle.step(x[:, t:t + 1], dt[:, t:t + 1], A, Bm[:, t:t + 1],
+                              Cm[:, t:t + 1], cur, idx, lib=lib)
+        np.testing.assert_array_equal(yt[:, 0], y[:, t])
+    np.testing.assert_array_equal(cur[idx], fin)
+    yo, po = oracle.step(x, dt, A, Bm, Cm, pool, np.array([-1, 5], np.int32), lib=lib)
+    assert np.all(yo == 0)
+    np.testing.assert_array_equal(po, pool)
+
+
+# ------------------------------------------------------------------------------------------
+# rounding
+# ------------------------------------------------------------------------------------------
+
+def check_round_bf16(lib):
+    """Nearest-even bfloat16 rounding against torch's fp32 -> bf16 cast (for fp32-exact
+    values), plus ties, subnormals and overflow."""
+    r = _rng(18)
+    v = np.concatenate([r.standard_normal(4000) * 10.0 ** r.integers(-30, 30, 4000),
+                        r.standard_normal(200) * 1e-39])
+    v32 = v.astype(np.float32)
+    ours = np.array([lib.orc_round(float(t), 2) for t in v32.astype(np.float64)])
+    ref = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    ties = {1.0 + 2.0 ** -8: 1.0, 1.0 + 3 * 2.0 ** -8: 1.0 + 2.0 ** -6,
+            -(1.0 + 2.0 ** -8): -1.0, 2.0 ** -133 * 1.5: 2.0 ** -132}
+    for k, e in ties.items():
+        assert lib.orc_round(k, 2) == e, (k, lib.orc_round(k, 2), e)
+    assert math.isinf(lib.orc_round(3.5e38, 2))
+    assert lib.orc_round(1.0 + 2.0 ** -30, 1) == 1.0
+
+
+ALL_CHECKS = [
+    check_conv_worked_example_k4,
+    check_conv_single_token_k3,
+    check_conv_matches_torch,
+    check_conv_silu_matches_torch,
+    check_conv_short_chunks_keep_state,
+    check_conv_chunk_continuation,
+    check_conv_seq_idx_segments,
+    check_conv_seq_idx_reuse_caveat,
+    check_ring_buffer_worked_example,
+    check_ring_wraps_backwards,
+    check_update_equals_fwd,
+    check_update_state_len_invariance,
+    check_update_indices_and_range,
+    check_scan_variance_closed_form,
+    check_scan_bruteforce_eq4,
+    check_scan_initial_state_term,
+    check_scan_superposition,
+    check_scan_special_cases,
+    check_scan_chunk_continuation,
+    check_scan_seq_idx_segments,
+    check_step_equals_scan,
+    check_round_bf16,
+]

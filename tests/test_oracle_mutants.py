@@ -1,0 +1,94 @@
+"""Each plausible mistake planted in a copy of the oracle must fail at least one pin.
+
+The mutants are built on the CPU from the oracle's source text with one edit each (a
+dropped term, a wrong sign or index, a transposed operand, a wrong reading of the pages),
+compiled into a temporary library and run through the pins of ``oracle_pins``.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    # conv: taps reversed (true convolution instead of the page's w_k u_{t+k})
+    "conv_taps_reversed": ("z += w[c * K + k] * u[t + k];",
+                           "z += w[c * K + (K - 1 - k)] * u[t + k];"),
+    # conv: bias dropped
+    "conv_bias_dropped": ("double z = bias ? bias[c] : 0.0;\n                for (int64_t k = 0; k < K; ++k) {",
+                          "double z = 0.0;\n                for (int64_t k = 0; k < K; ++k) {"),
+    # conv: final state taken from x alone and zero-padded (the page's warned-against reading)
+    "conv_F_zero_padded": ("final_state[(b * C + c) * (K - 1) + r] = u[L + r];",
+                           "final_state[(b * C + c) * (K - 1) + r] = (L + r >= K - 1) ? u[L + r] : 0.0;"),
+    # conv: the state is treated as a different segment from token 0
+    "conv_state_other_segment": ("id[j] = (seq_idx && L > 0) ? seq_idx[b * L + 0] : 0;",
+                                 "id[j] = (seq_idx && L > 0) ? seq_idx[b * L + 0] - 1 : 0;"),
+    # conv: seq_idx mask compares with the previous token instead of the output token
+    "conv_mask_wrong_anchor": ("if (seq_idx && id[t + k] != id[t + K - 1]) continue;",
+                               "if (seq_idx && id[t + k] != id[t + (K > 1 ? K - 2 : 0)]) continue;"),
+    # SiLU with the wrong sign
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    # update: ring history off by one slot
+    "ring_off_by_one": ("h = row[floor_mod(p - j, state_len)];",
+                        "h = row[floor_mod(p - j + 1, state_len)];"),
+    # update: negative ring positions clamped to slot 0 instead of wrapped (floor-mod)
+    "ring_no_wrap": ("h = row[floor_mod(p - j, state_len)];",
+                     "h = row[(p - j) < 0 ? 0 : (p - j) % state_len];"),
+    # update: stores the output y instead of the input x
+    "update_stores_y": ("row[floor_mod(p + i, state_len)] = xr[i];",
+                        "row[floor_mod(p + i, state_len)] = o[i];"),
+    # scan: dt dropped from the decay
+    "scan_decay_no_dt": ("const double a = exp(d * A[h]);\n                const double* xt = x + ((b * L + t) * H + h) * P;",
+                         "const double a = exp(A[h]);\n                const double* xt = x + ((b * L + t) * H + h) * P;"),
+    # scan: dt dropped from the input term
+    "scan_input_no_dt": ("st[p * N + n] = a * st[p * N + n] + d * xt[p] * Bt[n];\n                        acc += Ct[n] * st[p * N + n];\n                    }\n                    y[((b * L + t) * H + h) * P + p]",
+                         "st[p * N + n] = a * st[p * N + n] + xt[p] * Bt[n];\n                        acc += Ct[n] * st[p * N + n];\n                    }\n                    y[((b * L + t) * H + h) * P + p]"),
+    # scan: output read before the state update (off by one step)
+    "scan_output_lag": ("st[p * N + n] = a * st[p * N + n] + d * xt[p] * Bt[n];\n                        acc += Ct[n] * st[p * N + n];\n                    }\n                    y[((b * L + t) * H + h) * P + p]",
+                        "acc += Ct[n] * st[p * N + n];\n                        st[p * N + n] = a * st[p * N + n] + d * xt[p] * Bt[n];\n                    }\n                    y[((b * L + t) * H + h) * P + p]"),
+    # scan: B and C swapped in the read-out
+    "scan_B_C_swapped": ("acc += Ct[n] * st[p * N + n];\n                    }\n                    y[((b * L + t) * H + h) * P + p]",
+                         "acc += Bt[n] * st[p * N + n];\n                    }\n                    y[((b * L + t) * H + h) * P + p]"),
+    # scan: wrong head -> group map
+    "scan_group_map": ("const int64_t g = h / heads_per_group;\n            double* st = (double*)malloc",
+                       "const int64_t g = h % G;\n            double* st = (double*)malloc"),
+    # scan: initial state indexed [H][B] instead of [B][H]
+    "scan_init_transposed": ("st[e] = init_state ? init_state[(b * H + h) * P * N + e] : 0.0;",
+                             "st[e] = init_state ? init_state[(h * B + b) * P * N + e] : 0.0;"),
+    # scan: initial state ignored
+    "scan_init_ignored": ("st[e] = init_state ? init_state[(b * H + h) * P * N + e] : 0.0;",
+                          "st[e] = 0.0;"),
+    # scan: no reset at packed-sequence boundaries
+    "scan_no_reset": ("if (seq_idx && t > 0 && seq_idx[b * L + t] != seq_idx[b * L + t - 1])",
+                      "if (0)"),
+    # step: slot indices ignored
+    "step_ignores_indices": ("const int64_t s = indices ? (int64_t)indices[b] : b;\n            if (s < 0 || s >= n_slots) {\n                for (int64_t t = 0; t < L_new; ++t)",
+                             "const int64_t s = b;\n            if (s < 0 || s >= n_slots) {\n                for (int64_t t = 0; t < L_new; ++t)"),
+    # bf16 rounding keeps 9 bits
+    "bf16_nine_bits": ("int q = e - 8;", "int q = e - 9;"),
+    # bf16 rounding truncates instead of nearest-even
+    "bf16_truncates": ("double r = ldexp(nearbyint(ldexp(fabs(v), -q)), q);",
+                       "double r = ldexp(floor(ldexp(fabs(v), -q)), q);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    find, repl = MUTANTS[name]
+    with open(oracle._SRC) as f:
+        src = f.read()
+    assert src.count(find) == 1, f"mutation anchor for {name} not unique/found"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(find, repl))
+    so = str(tmp_path / "libmutant.so")
+    oracle.build(force=True, src=str(path), out=so)
+    lib = oracle.load_library(so)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(lib)
+        except AssertionError:
+            caught.append(check.__name__)
+            break
+    assert caught, f"mutant {name} passed every pin"
