@@ -1,0 +1,171 @@
+"""Benchmark of the fused SSM scan + causal conv1d prefill on one MI355X.
+
+A step is one pass of the whole hot path over one batch: ssm_conv_scan_fwd on a Mamba-2
+1.3B-like layer (batch 4 x 8192 tokens, 64 heads x headdim 64, state 128, conv width 4 over
+4352 x|B|C channels, bf16 activations, fp32 states) whose initial conv / SSM states are the
+final states of a preceding 8192-token call (state passing).  Inputs are seeded synthetic
+tensors already resident in HBM.
+
+Prints one JSON line: whole-job tokens/s, the roofline of the dominant kernel (the chunked
+scan main kernel; its launch time comes from HIP events the library records around it on the
+call's stream) and the fp64 CPU oracle timed on the host cores on the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "SSM scan+conv tokens/sec (B×L, 1.3B layer, L=8K) and % HBM/MFMA roofline"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(s):
+    """Bytes the fused prefill must move at least once (inputs read, outputs written)."""
+    tok = s.B * s.L
+    per_tok = s.C * 2 + s.H * 4 + s.H * s.P * 2          # xBC in, dt in, y out
+    states = 2 * s.B * s.H * s.P * s.N * 4 + 2 * s.B * s.C * (s.K - 1) * 2
+    main_per_tok = s.H * s.P * 2 + s.H * 4 + s.H * s.P * 2  # x channels, dt, y
+    main_states = 2 * s.B * s.H * s.P * s.N * 4 + 2 * s.B * s.H * s.P * (s.K - 1) * 2
+    return tok * per_tok + states, tok * main_per_tok + main_states
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("ssd.hip", "internal.h"):
+        with open(os.path.join(ROOT, "ssm_sequence_models_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the main kernel from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "ssd_main_layer1p3b_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(s, w, b, A, inp, cinit, sinit):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.conv_scan_fwd(inp["xBC"], w, b, cinit, inp["dt"], A, sinit, None, s.H, s.P, s.G, s.N)
+    dt = time.perf_counter() - t0
+    return {"value": s.B * s.L / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"one whole step (batch {s.B} x {s.L} tokens, all {s.H} heads), "
+                      f"fp64 C oracle, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus "
+              f"{args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ssm_sequence_models_amd as ssm
+    import workloads
+
+    cfg = workloads.CONFIGS["layer1p3b"]
+    s = workloads.shape_of("layer1p3b")
+    dev = torch.device("cuda:0")
+    w, b, A = workloads.layer_params(s, cfg["seed"])
+    pre = workloads.prefill_inputs(s, cfg["pre_seed"])
+    inp = workloads.prefill_inputs(s, cfg["seed"])
+    W, Bb, AA = w.to(dev), b.to(dev), A.to(dev)
+    X, D = inp["xBC"].to(dev), inp["dt"].to(dev)
+    ws = torch.empty(ssm.workspace_size(s.B, s.L, s.H, s.P, s.G, s.N), dtype=torch.uint8,
+                     device=dev)
+    log("bench: preceding call for the initial states")
+    _, cinit, sinit = ssm.conv_scan_fwd(pre["xBC"].to(dev), W, Bb, pre["dt"].to(dev), AA, s.H,
+                                        s.P, s.G, s.N, workspace=ws)
+    y = torch.empty(s.B, s.L, s.H, s.P, dtype=torch.bfloat16, device=dev)
+    cfin = torch.empty_like(cinit)
+    sfin = torch.empty_like(sinit)
+
+    def step():
+        ssm.conv_scan_fwd(X, W, Bb, D, AA, s.H, s.P, s.G, s.N, conv_initial_state=cinit,
+                          initial_state=sinit, conv_final_state=cfin, final_state=sfin, y=y,
+                          workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done; timing {args.steps}")
+    ssm.timing_read()  # clear
+    ssm.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ssm.timing_enable(False)
+    main_ms, launches = ssm.timing_read()
+    assert launches == args.steps, (launches, args.steps)
+    ms_per_step = wall * 1e3 / args.steps
+    main_ms_avg = main_ms / launches
+    tokens = s.B * s.L
+    op_bytes, main_bytes = algorithmic_bytes(s)
+    achieved = main_bytes / (main_ms_avg * 1e-3) / 1e9
+    log(f"bench: {ms_per_step:.4f} ms/step, main kernel {main_ms_avg:.4f} ms")
+
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mamba2-1.3b-like layer prefill with state passing: fused causal "
+                               "conv1d (width 4, 4352 x|B|C channels, SiLU) + selective scan",
+                   "batch": s.B, "seq_len": s.L, "nheads": s.H, "headdim": s.P,
+                   "dstate": s.N, "ngroups": s.G, "conv_width": s.K,
+                   "initial_state": "final states of a preceding 8192-token call"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "ssd_main_kernel", "kernel_ms": main_ms_avg,
+                     "algorithmic_bytes_per_launch": main_bytes},
+        "op_roofline": {"algorithmic_bytes": op_bytes, "ms": ms_per_step,
+                        "achieved_GBs": op_bytes / (ms_per_step * 1e-3) / 1e9,
+                        "frac": op_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: fp64 oracle on the host (cpu baseline)")
+        result["cpu_baseline"] = cpu_baseline(s, w, b, A, inp, cinit.cpu(), sinit.cpu())
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * ssm_mi355x.h -- C ABI of the MI355X (gfx950) selective-scan + causal-conv1d library.
+ *
+ * The library computes a Mamba-2-style selective state-space scan with an explicit initial
+ * state in and the final state out, fused with its causal depthwise conv1d front end that
+ * carries a K-1 input history, plus the two decode-time updates.  Sources, cited by page
+ * title and section:
+ *
+ *   [LG] "Understanding and Improving Length Generalization in Recurrent Models" -- reading
+ *        notes on arXiv:2507.02782v2.  Sec. 2.1, Eq. (1): h_t = A_t h_{t-1} + B_t x_t,
+ *        y_t = C_t^T h_t with initial state h_{-1}.  Sec. 2.5, Eq. (4): the unrolling with a
+ *        non-zero h_{-1} and the note that the transition enters in log space.  Sec. 2.6:
+ *        State Passing / TBTT (the final state of one call is the initial state of the next).
+ *   [CC] Causal-conv1d tutorial, chapter 7 "State, chunking and incremental inference":
+ *        "defining the state through the extended sequence" (u = [S, x], z_t, F);
+ *        "chunked training and truncated backprop" (S_B = F_A); "single-token update
+ *        maths"; "the physical cache may exceed the minimal history" (state_len, circular
+ *        mode through cache_seqlens); "state indices for continuous batching"
+ *        (conv_state_indices); "packed-sequence boundaries" (seq_idx).
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller, laid out contiguously
+ *     (row-major) exactly as stated, unless explicit strides are given.  Inputs are const.
+ *   - The library allocates nothing per call and keeps no state between calls except the
+ *     loaded kernels, the thread-local error text and the optional timing events.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream) and
+ *     never synchronises.  Host-side argument errors return a status and enqueue nothing.
+ *   - dtype is the storage type of the activations (x, B, C, conv states, outputs):
+ *     SSM_F32 or SSM_BF16.  Weights, bias, dt and A are fp32; SSM states are fp32.
+ *     Floating point outputs are rounded once to the storage type (round to nearest even).
+ *   - Integer index arrays are int32.  Sizes are int64.
+ *   - Permitted aliasing: final_state == initial_state (in-place state passing), for the
+ *     conv pair and for the SSM pair.  Pools are updated in place.  No other aliasing.
+ *   - Nothing throws, aborts or prints.  ssm_last_error() gives the detail of the last
+ *     failure on the calling thread.
+ */
+#ifndef SSM_MI355X_H
+#define SSM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+/* hipStream_t is `struct ihipStream_t*`; this typedef is the same type. */
+struct ihipStream_t;
+typedef struct ihipStream_t* ssm_stream_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, bad enum, H % G != 0 ... */
+    SSM_ERR_UNSUPPORTED = 2, /* valid arguments outside what the kernels implement */
+    SSM_ERR_ALIGNMENT = 3,   /* a pointer not aligned to its element size */
+    SSM_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the query returned */
+    SSM_ERR_HIP = 5          /* a HIP launch/runtime error; see ssm_last_error() */
+} ssm_status_t;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+/* phi of [CC] "single-token update maths": identity or SiLU(z) = z / (1 + exp(-z)). */
+typedef enum { SSM_ACT_NONE = 0, SSM_ACT_SILU = 1 } ssm_act_t;
+
+/* Library ABI version (SSM_ABI_VERSION of the build). */
+int ssm_abi_version(void);
+/* Static English text for a status code. */
+const char* ssm_status_string(ssm_status_t status);
+/* Detail of the last failure on the calling thread ("" if none).  Valid until the next call
+ * on the same thread. */
+const char* ssm_last_error(void);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_conv1d_fwd -- causal depthwise conv1d with state in / out.
+ * Defined in [CC] "defining the state through the extended sequence": with
+ * u = [S_0 .. S_{K-2}, x_0 .. x_{L-1}] (S oldest first, zeros when absent),
+ *     out_t = phi(bias + sum_{k<K} w_k u_{t+k}),     F = u[L : L+K-1]  (raw copy).
+ * seq_idx ([CC] "packed-sequence boundaries"): a tap contributes only when its token has
+ * the same id as the output token (S carries the id of token 0); F stays unmasked.
+ *
+ *   x             [batch, seqlen, channels]   dtype, channel-last
+ *   w             [channels, width]           fp32 (w[c][width-1] multiplies x_t)
+ *   bias          [channels]                  fp32, or NULL (= 0)
+ *   initial_state [batch, channels, width-1]  dtype, or NULL (= zeros)
+ *   final_state   [batch, channels, width-1]  dtype, or NULL (not written); may alias
+ *                                             initial_state
+ *   seq_idx       [batch, seqlen]             int32, or NULL (one sequence per row)
+ *   out           [batch, seqlen, channels]   dtype
+ * width in [2, 8]; seqlen = 0 is legal (final_state = initial_state); batch = 0 is a no-op.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_conv1d_fwd(const void* x, const float* w, const float* bias,
+                            const void* initial_state, void* final_state,
+                            const int32_t* seq_idx, void* out, int64_t batch, int64_t seqlen,
+                            int64_t channels, int64_t width, ssm_dtype_t dtype, ssm_act_t act,
+                            ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_conv1d_update -- decode-time update of the conv state pool, n_new >= 1 new tokens.
+ * Defined in [CC] "single-token update maths", "the physical cache may exceed the minimal
+ * history" and "state indices for continuous batching".  Row b uses pool slot
+ * s = conv_state_indices[b] (b when NULL).  The K-1 history values are read before
+ * anything is overwritten:
+ *   circular (cache_seqlens != NULL, p = cache_seqlens[b]): history j steps back is slot
+ *       (p - j) mod state_len (non-negative remainder); new token i goes to slot
+ *       (p + i) mod state_len;
+ *   linear (cache_seqlens == NULL): the row holds the newest state_len inputs, oldest
+ *       first; the history is its last K-1 entries; afterwards the row is the last
+ *       state_len entries of (old row ++ new tokens).
+ * out_i = phi(bias + sum_k w_k u_{i+k}) over u = [history, new tokens].  The pool stores
+ * the raw inputs, never the outputs.  cache_seqlens is read, never advanced: the caller
+ * adds n_new afterwards.
+ *
+ *   x                  [batch, channels, n_new]           dtype
+ *   conv_state         [n_slots, channels, state_len]     dtype, in / out
+ *   w, bias            as ssm_conv1d_fwd
+ *   conv_state_indices [batch] int32, or NULL
+ *   cache_seqlens      [batch] int32 (>= 0), or NULL (linear mode)
+ *   out                [batch, channels, n_new]           dtype
+ * state_len >= width-1.  A row whose slot is outside [0, n_slots) is skipped: its out row
+ * is zero-filled and the pool is not touched.  Two rows on the same slot: undefined (a
+ * caller-contract error); a reused slot must have been initialised by the caller.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_conv1d_update(const void* x, void* conv_state, const float* w,
+                               const float* bias, const int32_t* conv_state_indices,
+                               const int32_t* cache_seqlens, void* out, int64_t batch,
+                               int64_t channels, int64_t n_new, int64_t width,
+                               int64_t state_len, int64_t n_slots, ssm_dtype_t dtype,
+                               ssm_act_t act, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Workspace bytes that ssm_scan_fwd / ssm_conv_scan_fwd need for these sizes (0 if none).
+ * ------------------------------------------------------------------------------------- */
+size_t ssm_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t ngroups, int64_t dstate, ssm_dtype_t dtype);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_scan_fwd -- selective scan with initial state in, final state out.
+ * Defined in [LG] Sec. 2.1 Eq. (1) and Sec. 2.5 Eq. (4), per head h (group
+ * g = h / (nheads / ngroups)) and channel p:
+ *     a_t = exp(dt[t,h] * A[h])
+ *     state_t[p,:] = a_t * state_{t-1}[p,:] + dt[t,h] * x[t,h,p] * B[t,g,:]
+ *     y[t,h,p] = C[t,g,:] . state_t[p,:]
+ * starting from state_{-1} = initial_state (zeros when NULL); final_state = state_{L-1}.
+ * seq_idx: the state restarts from zero where seq_idx[b,t] != seq_idx[b,t-1].
+ *
+ *   x             [batch, seqlen, nheads, headdim]   dtype
+ *   dt            [batch, seqlen, nheads]            fp32 (used as given, no softplus)
+ *   A             [nheads]                           fp32
+ *   Bm, Cm        [batch, seqlen, ngroups, dstate]   dtype
+ *   initial_state [batch, nheads, headdim, dstate]   fp32, or NULL
+ *   final_state   [batch, nheads, headdim, dstate]   fp32, or NULL; may alias initial_state
+ *   seq_idx       [batch, seqlen] int32, or NULL
+ *   y             [batch, seqlen, nheads, headdim]   dtype
+ *   workspace     device scratch of >= ssm_scan_workspace_size(...) bytes (NULL if 0)
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const void* Bm,
+                          const void* Cm, const float* initial_state, float* final_state,
+                          const int32_t* seq_idx, void* y, int64_t batch, int64_t seqlen,
+                          int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                          ssm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_conv_scan_fwd -- the fused prefill: ssm_conv1d_fwd over the channels of xBC (with
+ * phi; its output rounded to dtype exactly as the standalone call would store it), split
+ * into x | B | C channel ranges, then ssm_scan_fwd.  One pass over HBM for x.
+ *
+ *   xBC                [batch, seqlen, nheads*headdim + 2*ngroups*dstate]  dtype;
+ *                      channels [0, H*P) are x (head-major), then B (group-major), then C
+ *   conv_w, conv_bias  [C_conv, width], [C_conv] fp32 (bias may be NULL)
+ *   conv_initial_state, conv_final_state   [batch, C_conv, width-1] dtype, or NULL
+ *   dt, A, initial_state, final_state, seq_idx, y, workspace: as ssm_scan_fwd
+ *   (seq_idx also masks the conv taps as in ssm_conv1d_fwd)
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float* conv_bias,
+                               const void* conv_initial_state, void* conv_final_state,
+                               const float* dt, const float* A, const float* initial_state,
+                               float* final_state, const int32_t* seq_idx, void* y,
+                               int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t ngroups, int64_t dstate, int64_t width,
+                               ssm_dtype_t dtype, ssm_act_t act, void* workspace,
+                               size_t workspace_bytes, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_step -- decode-time scan update on a state pool, n_new >= 1 tokens per request.
+ * Same recurrence as ssm_scan_fwd ([LG] Eq. (1)), token by token, on pool slot
+ * s = state_indices[b] (b when NULL); the state is kept in fp32 registers across the n_new
+ * tokens and written back once.  A row whose slot is outside [0, n_slots) is skipped: its
+ * y rows are zero-filled and the pool is not touched.  Two rows on one slot: undefined.
+ *
+ *   x   element (b, t, h, p) at x[b*x_sb + t*x_st + (h*headdim + p)*x_sc]     dtype
+ *   Bm  element (b, t, g, n) at Bm[b*B_sb + t*B_st + (g*dstate + n)*B_sc]     dtype
+ *   Cm  element (b, t, g, n) at Cm[b*C_sb + t*C_st + (g*dstate + n)*C_sc]     dtype
+ *       (strides in elements: contiguous [batch, n_new, ...] inputs and the
+ *       [batch, channels, n_new] output of ssm_conv1d_update both fit)
+ *   dt     [batch, n_new, nheads] fp32;   A [nheads] fp32
+ *   state  [n_slots, nheads, headdim, dstate] fp32, in / out
+ *   state_indices [batch] int32, or NULL
+ *   y      [batch, n_new, nheads, headdim] dtype
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, const float* dt,
+                      const float* A, const void* Bm, int64_t B_sb, int64_t B_st, int64_t B_sc,
+                      const void* Cm, int64_t C_sb, int64_t C_st, int64_t C_sc, float* state,
+                      const int32_t* state_indices, void* y, int64_t batch, int64_t n_new,
+                      int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                      int64_t n_slots, ssm_dtype_t dtype, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Measurement support (does not change any result).  When enabled, every launch of the
+ * chunked-scan main kernel (the dominant kernel of ssm_scan_fwd / ssm_conv_scan_fwd) is
+ * bracketed by a pair of HIP events recorded on the call's stream.  ssm_timing_read waits
+ * for the recorded events, returns the summed kernel time in milliseconds and the number of
+ * launches, and clears the record.  Not thread-safe with concurrent calls on other threads.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_timing_enable(int enable);
+ssm_status_t ssm_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_MI355X_H */

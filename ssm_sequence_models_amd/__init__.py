@@ -1,0 +1,289 @@
+"""Thin Python binding of libssm_mi355x.so (the C ABI in include/ssm_mi355x.h).
+
+Argument marshalling only: this module checks devices / dtypes / shapes of torch tensors,
+allocates outputs and workspaces with torch (device memory and streams are PyTorch's
+plumbing), and calls the C entry point of the same name on the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; there is no fallback, and the
+import fails loudly if the library has not been built.
+
+Sources of the operations (page title and section): the length-generalization reading
+notes on arXiv:2507.02782v2, Sec. 2.1 Eq. (1), Sec. 2.5 Eq. (4), Sec. 2.6 (scan with
+initial / final state); the causal-conv1d tutorial ch. 7 (conv state S / F, decode update,
+cache_seqlens, conv_state_indices, seq_idx).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # must precede the library load: it binds the process's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+ACT = {None: 0, "none": 0, "silu": 1}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "misaligned pointer",
+           4: "workspace", 5: "HIP error"}
+
+
+class SSMError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -m ssm_sequence_models_amd.build "
+            "or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32p, fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+    ci = ctypes.c_int
+    lib.ssm_abi_version.restype = ci
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_status_string.argtypes = [ci]
+    lib.ssm_conv1d_fwd.argtypes = [vp, fp, fp, vp, vp, i32p, vp, i64, i64, i64, i64, ci, ci, vp]
+    lib.ssm_conv1d_update.argtypes = [vp, vp, fp, fp, i32p, i32p, vp, i64, i64, i64, i64, i64,
+                                      i64, ci, ci, vp]
+    lib.ssm_scan_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_scan_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+    lib.ssm_scan_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp, i32p, vp, i64, i64, i64, i64, i64,
+                                 i64, ci, vp, ctypes.c_size_t, vp]
+    lib.ssm_conv_scan_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp, fp, fp, i32p, vp, i64, i64, i64,
+                                      i64, i64, i64, i64, ci, ci, vp, ctypes.c_size_t, vp]
+    lib.ssm_step.argtypes = [vp, i64, i64, i64, fp, fp, vp, i64, i64, i64, vp, i64, i64, i64, fp,
+                             i32p, vp, i64, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.ssm_timing_enable.argtypes = [ci]
+    lib.ssm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64)]
+    for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
+              "ssm_step", "ssm_timing_enable", "ssm_timing_read"):
+        getattr(lib, f).restype = ci
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return int(_lib.ssm_abi_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SSMError(fn, status, _lib.ssm_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    if t.dtype == torch.float32:
+        return SSM_F32
+    raise TypeError(f"activations must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, contiguous=True):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, dtype=torch.bfloat16) -> int:
+    code = SSM_BF16 if dtype == torch.bfloat16 else SSM_F32
+    return int(_lib.ssm_scan_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate,
+                                            code))
+
+
+def _workspace(ws, nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace must hold {nbytes} bytes")
+    return ws, ws.numel() * ws.element_size()
+
+
+def conv1d_fwd(x, weight, bias=None, initial_state=None, seq_idx=None, activation=None,
+               return_final_state=True, final_state=None, out=None):
+    """x [B, L, C] (bf16 / fp32, channel-last); weight [C, K] fp32; bias [C] fp32;
+    initial_state [B, C, K-1]; seq_idx [B, L] int32.  Returns (out, final_state)."""
+    B, L, C = x.shape
+    K = weight.shape[1]
+    _need(x, "x")
+    _need(weight, "weight", torch.float32, (C, K))
+    _need(bias, "bias", torch.float32, (C,))
+    _need(initial_state, "initial_state", x.dtype, (B, C, K - 1))
+    _need(seq_idx, "seq_idx", torch.int32, (B, L))
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, (B, L, C))
+    if final_state is None and return_final_state:
+        final_state = torch.empty((B, C, K - 1), dtype=x.dtype, device=x.device)
+    _need(final_state, "final_state", x.dtype, (B, C, K - 1))
+    _check("ssm_conv1d_fwd", _lib.ssm_conv1d_fwd(
+        _ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(final_state), _ptr(seq_idx),
+        _ptr(out), B, L, C, K, _dtype_code(x), ACT[activation], _stream()))
+    return out, final_state
+
+
+def conv1d_update(x, conv_state, weight, bias=None, conv_state_indices=None,
+                  cache_seqlens=None, activation=None, out=None):
+    """x [B, C, L_new]; conv_state [n_slots, C, state_len] (updated in place);
+    conv_state_indices, cache_seqlens [B] int32 (cache_seqlens is not advanced).
+    Returns out [B, C, L_new]."""
+    B, C, L_new = x.shape
+    n_slots, _, state_len = conv_state.shape
+    K = weight.shape[1]
+    _need(x, "x")
+    _need(conv_state, "conv_state", x.dtype, (n_slots, C, state_len))
+    _need(weight, "weight", torch.float32, (C, K))
+    _need(bias, "bias", torch.float32, (C,))
+    _need(conv_state_indices, "conv_state_indices", torch.int32, (B,))
+    _need(cache_seqlens, "cache_seqlens", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, (B, C, L_new))
+    _check("ssm_conv1d_update", _lib.ssm_conv1d_update(
+        _ptr(x), _ptr(conv_state), _ptr(weight), _ptr(bias), _ptr(conv_state_indices),
+        _ptr(cache_seqlens), _ptr(out), B, C, L_new, K, state_len, n_slots, _dtype_code(x),
+        ACT[activation], _stream()))
+    return out
+
+
+def scan_fwd(x, dt, A, B, C, initial_state=None, seq_idx=None, return_final_state=True,
+             final_state=None, y=None, workspace=None):
+    """x [b, L, H, P]; dt [b, L, H] fp32; A [H] fp32; B, C [b, L, G, N]; initial_state
+    [b, H, P, N] fp32 (may be the same tensor as final_state).  Returns (y, final_state)."""
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _need(x, "x")
+    _need(dt, "dt", torch.float32, (bsz, L, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(B, "B", x.dtype, (bsz, L, G, N))
+    _need(C, "C", x.dtype, (bsz, L, G, N))
+    _need(initial_state, "initial_state", torch.float32, (bsz, H, P, N))
+    _need(seq_idx, "seq_idx", torch.int32, (bsz, L))
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, (bsz, L, H, P))
+    if final_state is None and return_final_state:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
+    _need(final_state, "final_state", torch.float32, (bsz, H, P, N))
+    ws, nbytes = _workspace(workspace, workspace_size(bsz, L, H, P, G, N, x.dtype), x.device)
+    _check("ssm_scan_fwd", _lib.ssm_scan_fwd(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(initial_state), _ptr(final_state),
+        _ptr(seq_idx), _ptr(y), bsz, L, H, P, G, N, _dtype_code(x), _ptr(ws), nbytes, _stream()))
+    return y, final_state
+
+
+def conv_scan_fwd(xBC, conv_weight, conv_bias, dt, A, nheads, headdim, ngroups, dstate,
+                  conv_initial_state=None, initial_state=None, seq_idx=None,
+                  activation="silu", return_final_states=True, conv_final_state=None,
+                  final_state=None, y=None, workspace=None):
+    """The fused prefill.  xBC [b, L, H*P + 2*G*N] (x | B | C channels); conv_weight
+    [C_conv, K] fp32; conv_bias [C_conv]; dt [b, L, H]; A [H]; conv states [b, C_conv, K-1];
+    SSM states [b, H, P, N] fp32.  Returns (y [b, L, H, P], conv_final_state, final_state)."""
+    bsz, L, Cc = xBC.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    if Cc != H * P + 2 * G * N:
+        raise ValueError("xBC channel count must be nheads*headdim + 2*ngroups*dstate")
+    K = conv_weight.shape[1]
+    _need(xBC, "xBC")
+    _need(conv_weight, "conv_weight", torch.float32, (Cc, K))
+    _need(conv_bias, "conv_bias", torch.float32, (Cc,))
+    _need(conv_initial_state, "conv_initial_state", xBC.dtype, (bsz, Cc, K - 1))
+    _need(dt, "dt", torch.float32, (bsz, L, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(initial_state, "initial_state", torch.float32, (bsz, H, P, N))
+    _need(seq_idx, "seq_idx", torch.int32, (bsz, L))
+    if y is None:
+        y = torch.empty((bsz, L, H, P), dtype=xBC.dtype, device=xBC.device)
+    _need(y, "y", xBC.dtype, (bsz, L, H, P))
+    if return_final_states:
+        if conv_final_state is None:
+            conv_final_state = torch.empty((bsz, Cc, K - 1), dtype=xBC.dtype, device=xBC.device)
+        if final_state is None:
+            final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=xBC.device)
+    _need(conv_final_state, "conv_final_state", xBC.dtype, (bsz, Cc, K - 1))
+    _need(final_state, "final_state", torch.float32, (bsz, H, P, N))
+    ws, nbytes = _workspace(workspace, workspace_size(bsz, L, H, P, G, N, xBC.dtype), xBC.device)
+    _check("ssm_conv_scan_fwd", _lib.ssm_conv_scan_fwd(
+        _ptr(xBC), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_initial_state),
+        _ptr(conv_final_state), _ptr(dt), _ptr(A), _ptr(initial_state), _ptr(final_state),
+        _ptr(seq_idx), _ptr(y), bsz, L, H, P, G, N, K, _dtype_code(xBC), ACT[activation], _ptr(ws),
+        nbytes, _stream()))
+    return y, conv_final_state, final_state
+
+
+def step(x, dt, A, B, C, state, state_indices=None, y=None, nheads=None, ngroups=None):
+    """Decode update of a state pool.  x [b, n_new, H*P], B / C [b, n_new, G*N] -- any
+    strides (e.g. channel ranges of the [b, C_conv, n_new] conv-update output, transposed);
+    dt [b, n_new, H] fp32; state [n_slots, H, P, N] fp32 (updated in place);
+    state_indices [b] int32.  Returns y [b, n_new, H, P]."""
+    n_slots, H, P, N = state.shape
+    bsz, n_new, HP = x.shape
+    G = B.shape[2] // N
+    if HP != H * P or C.shape != B.shape or B.shape[:2] != x.shape[:2]:
+        raise ValueError("x must be [b, n_new, H*P] and B, C [b, n_new, G*N]")
+    for t, name in ((x, "x"), (B, "B"), (C, "C")):
+        _need(t, name, contiguous=False)
+    _need(dt, "dt", torch.float32, (bsz, n_new, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(state, "state", torch.float32)
+    _need(state_indices, "state_indices", torch.int32, (bsz,))
+    if y is None:
+        y = torch.empty((bsz, n_new, H, P), dtype=x.dtype, device=x.device)
+    _need(y, "y", x.dtype, (bsz, n_new, H, P))
+    sx, sb, sc = x.stride(), B.stride(), C.stride()
+    _check("ssm_step", _lib.ssm_step(
+        _ptr(x), sx[0], sx[1], sx[2], _ptr(dt), _ptr(A), _ptr(B), sb[0], sb[1], sb[2], _ptr(C),
+        sc[0], sc[1], sc[2], _ptr(state), _ptr(state_indices), _ptr(y), bsz, n_new, H, P, G, N,
+        n_slots, _dtype_code(x), _stream()))
+    return y
+
+
+def decode_step(x_new, conv_state, conv_weight, conv_bias, dt, A, ssm_state, nheads, headdim,
+                ngroups, dstate, conv_state_indices=None, cache_seqlens=None,
+                state_indices=None, activation="silu", conv_out=None, y=None):
+    """One decode step: conv1d_update over x_new [b, C_conv, n_new], then step reading the
+    x | B | C channel ranges of the conv output in place.  Both pools update in place;
+    cache_seqlens is not advanced.  Returns y [b, n_new, H, P]."""
+    HP, GN = nheads * headdim, ngroups * dstate
+    co = conv1d_update(x_new, conv_state, conv_weight, conv_bias, conv_state_indices,
+                       cache_seqlens, activation, out=conv_out)
+    xv = co[:, :HP, :].transpose(1, 2)
+    Bv = co[:, HP:HP + GN, :].transpose(1, 2)
+    Cv = co[:, HP + GN:, :].transpose(1, 2)
+    return step(xv, dt, A, Bv, Cv, ssm_state, state_indices if state_indices is not None
+                else conv_state_indices, y=y)
+
+
+def timing_enable(enable: bool = True):
+    _check("ssm_timing_enable", _lib.ssm_timing_enable(1 if enable else 0))
+
+
+def timing_read():
+    """(summed main-kernel milliseconds, launches) since the last read."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check("ssm_timing_read", _lib.ssm_timing_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

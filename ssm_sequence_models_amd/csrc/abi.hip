@@ -1,0 +1,480 @@
+// abi.hip -- the C ABI (include/ssm_mi355x.h): argument checks, path selection, launches.
+// Host code only; every computation runs in the kernels of conv.hip, recurrent.hip and
+// ssd.hip.  Nothing here allocates device memory, synchronises, throws or prints.
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ssm_status_t fail(ssm_status_t s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+ssm_status_t ok() {
+    g_err.clear();
+    return SSM_OK;
+}
+ssm_status_t hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return ok();
+    g_err = std::string(where) + ": " + hipGetErrorString(e);
+    return SSM_ERR_HIP;
+}
+size_t esize(ssm_dtype_t d) { return d == SSM_BF16 ? 2 : 4; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool valid_dtype(int d) { return d == SSM_F32 || d == SSM_BF16; }
+bool valid_act(int a) { return a == SSM_ACT_NONE || a == SSM_ACT_SILU; }
+
+// ---- optional kernel timing (measurement only) ----
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
+
+// Pointer arguments: name, pointer, required?, element alignment.
+struct PtrCheck {
+    const char* name;
+    const void* p;
+    bool required;
+    size_t align;
+};
+ssm_status_t check_ptrs(const char* fn, std::initializer_list<PtrCheck> list) {
+    for (const auto& c : list) {
+        if (c.p == nullptr) {
+            if (c.required) return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": " + c.name + " is NULL");
+            continue;
+        }
+        if (!aligned(c.p, c.align))
+            return fail(SSM_ERR_ALIGNMENT, std::string(fn) + ": " + c.name + " is not aligned to " +
+                                               std::to_string(c.align) + " bytes");
+    }
+    return SSM_OK;
+}
+
+ssm_status_t check_scan_dims(const char* fn, int64_t batch, int64_t seqlen, int64_t nheads,
+                             int64_t headdim, int64_t ngroups, int64_t dstate, int dtype) {
+    if (!valid_dtype(dtype)) return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": bad dtype");
+    if (batch < 0 || seqlen < 0)
+        return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": negative batch or seqlen");
+    if (nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1)
+        return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": nheads, headdim, ngroups, dstate must be >= 1");
+    if (nheads % ngroups != 0)
+        return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": nheads is not a multiple of ngroups");
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(ssm_status_t s) {
+    switch (s) {
+        case SSM_OK: return "ok";
+        case SSM_ERR_INVALID_ARG: return "invalid argument";
+        case SSM_ERR_UNSUPPORTED: return "unsupported sizes or dtype";
+        case SSM_ERR_ALIGNMENT: return "misaligned pointer";
+        case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* ssm_last_error(void) { return g_err.c_str(); }
+
+ssm_status_t ssm_conv1d_fwd(const void* x, const float* w, const float* bias,
+                            const void* initial_state, void* final_state,
+                            const int32_t* seq_idx, void* out, int64_t batch, int64_t seqlen,
+                            int64_t channels, int64_t width, ssm_dtype_t dtype, ssm_act_t act,
+                            ssm_stream_t stream) {
+    const char* fn = "ssm_conv1d_fwd";
+    if (!valid_dtype(dtype)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_fwd: bad dtype");
+    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_fwd: bad activation");
+    if (batch < 0 || seqlen < 0 || channels < 1)
+        return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_fwd: need batch >= 0, seqlen >= 0, channels >= 1");
+    if (width < 2 || width > 8)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv1d_fwd: width must be in [2, 8]");
+    const size_t es = esize(dtype);
+    const bool work = batch > 0 && seqlen > 0;
+    ssm_status_t st = check_ptrs(fn, {{"x", x, work, es},
+                                      {"w", w, work, 4},
+                                      {"bias", bias, false, 4},
+                                      {"initial_state", initial_state, false, es},
+                                      {"final_state", final_state, false, es},
+                                      {"seq_idx", seq_idx, false, 4},
+                                      {"out", out, work, es}});
+    if (st != SSM_OK) return st;
+    if (batch == 0) return ok();
+    return hip_status(ssm::launch_conv1d_fwd(x, w, bias, initial_state, final_state, seq_idx, out,
+                                             batch, seqlen, channels, width, dtype, act,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+ssm_status_t ssm_conv1d_update(const void* x, void* conv_state, const float* w,
+                               const float* bias, const int32_t* conv_state_indices,
+                               const int32_t* cache_seqlens, void* out, int64_t batch,
+                               int64_t channels, int64_t n_new, int64_t width,
+                               int64_t state_len, int64_t n_slots, ssm_dtype_t dtype,
+                               ssm_act_t act, ssm_stream_t stream) {
+    const char* fn = "ssm_conv1d_update";
+    if (!valid_dtype(dtype)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_update: bad dtype");
+    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_update: bad activation");
+    if (batch < 0 || n_new < 0 || channels < 1 || n_slots < 1)
+        return fail(SSM_ERR_INVALID_ARG,
+                    "ssm_conv1d_update: need batch >= 0, n_new >= 0, channels >= 1, n_slots >= 1");
+    if (width < 2 || width > 8)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv1d_update: width must be in [2, 8]");
+    if (state_len < width - 1)
+        return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_update: state_len < width - 1");
+    const size_t es = esize(dtype);
+    const bool work = batch > 0 && n_new > 0;
+    ssm_status_t st = check_ptrs(fn, {{"x", x, work, es},
+                                      {"conv_state", conv_state, work, es},
+                                      {"w", w, work, 4},
+                                      {"bias", bias, false, 4},
+                                      {"conv_state_indices", conv_state_indices, false, 4},
+                                      {"cache_seqlens", cache_seqlens, false, 4},
+                                      {"out", out, work, es}});
+    if (st != SSM_OK) return st;
+    if (!work) return ok();
+    return hip_status(ssm::launch_conv1d_update(x, conv_state, w, bias, conv_state_indices,
+                                                cache_seqlens, out, batch, channels, n_new, width,
+                                                state_len, n_slots, dtype, act,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+size_t ssm_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t ngroups, int64_t dstate, ssm_dtype_t dtype) {
+    if (batch <= 0 || seqlen <= 0 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1 ||
+        !valid_dtype(dtype))
+        return 0;
+    if (ssm::chunked_supported(headdim, dstate, dtype))
+        return ssm::chunked_workspace_bytes(batch, seqlen, ngroups, dstate);
+    // general-shape path of the fused call: the conv output is staged in the workspace
+    return static_cast<size_t>(batch * seqlen * (nheads * headdim + 2 * ngroups * dstate)) *
+           esize(dtype);
+}
+
+namespace {
+
+// Shared tail of ssm_scan_fwd / ssm_conv_scan_fwd on the token-sequential path.
+ssm_status_t run_recurrent_scan(const char* fn, const void* x, int64_t x_row, const void* Bm,
+                                const void* Cm, int64_t bc_row, const float* dt, const float* A,
+                                const float* initial_state, float* final_state,
+                                const int32_t* seq_idx, void* y, int64_t batch, int64_t seqlen,
+                                int64_t nheads, int64_t headdim, int64_t ngroups,
+                                int64_t dstate, ssm_dtype_t dtype, hipStream_t s) {
+    ssm::RecurrentArgs r{};
+    r.x = x;
+    r.x_sb = seqlen * x_row;
+    r.x_st = x_row;
+    r.x_sc = 1;
+    r.dt = dt;
+    r.A = A;
+    r.Bm = Bm;
+    r.B_sb = seqlen * bc_row;
+    r.B_st = bc_row;
+    r.B_sc = 1;
+    r.Cm = Cm;
+    r.C_sb = seqlen * bc_row;
+    r.C_st = bc_row;
+    r.C_sc = 1;
+    r.state_in = initial_state;
+    r.state_out = final_state;
+    r.indices = nullptr;
+    r.n_slots = batch;
+    r.seq_idx = seq_idx;
+    r.y = y;
+    r.B = batch;
+    r.T = seqlen;
+    r.H = nheads;
+    r.P = headdim;
+    r.G = ngroups;
+    r.N = dstate;
+    return hip_status(ssm::launch_recurrent(r, dtype, s), fn);
+}
+
+hipEvent_t g_none = nullptr;
+
+// Events for the timing record (both NULL when timing is off).
+ssm_status_t timing_events(hipEvent_t* ev0, hipEvent_t* ev1) {
+    *ev0 = *ev1 = g_none;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_timing) return SSM_OK;
+    hipError_t e = hipEventCreate(ev0);
+    if (e == hipSuccess) e = hipEventCreate(ev1);
+    if (e != hipSuccess) return hip_status(e, "timing");
+    g_events.emplace_back(*ev0, *ev1);
+    return SSM_OK;
+}
+
+}  // namespace
+
+ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const void* Bm,
+                          const void* Cm, const float* initial_state, float* final_state,
+                          const int32_t* seq_idx, void* y, int64_t batch, int64_t seqlen,
+                          int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                          ssm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          ssm_stream_t stream) {
+    const char* fn = "ssm_scan_fwd";
+    ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate, dtype);
+    if (st != SSM_OK) return st;
+    const size_t es = esize(dtype);
+    const bool work = batch > 0 && seqlen > 0;
+    st = check_ptrs(fn, {{"x", x, work, es},
+                         {"dt", dt, work, 4},
+                         {"A", A, work, 4},
+                         {"Bm", Bm, work, es},
+                         {"Cm", Cm, work, es},
+                         {"initial_state", initial_state, false, 16},
+                         {"final_state", final_state, false, 16},
+                         {"seq_idx", seq_idx, false, 4},
+                         {"y", y, work, es}});
+    if (st != SSM_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (batch == 0) return ok();
+    if (seqlen == 0)
+        return hip_status(ssm::launch_copy_or_zero_f32(final_state, initial_state,
+                                                       batch * nheads * headdim * dstate, s),
+                          fn);
+    if (ssm::chunked_supported(headdim, dstate, dtype)) {
+        const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, ngroups, dstate);
+        if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+            return fail(SSM_ERR_WORKSPACE, "ssm_scan_fwd: workspace must be >= " +
+                                               std::to_string(need) + " bytes, 16-byte aligned");
+        if (!aligned(x, 16) || !aligned(y, 8))
+            return fail(SSM_ERR_ALIGNMENT, "ssm_scan_fwd: x must be 16-byte and y 8-byte aligned");
+        ssm::ChunkedArgs a{};
+        a.x = static_cast<const uint16_t*>(x);
+        a.x_row = nheads * headdim;
+        a.x_col0 = 0;
+        a.bsrc = static_cast<const uint16_t*>(Bm);
+        a.b_row = ngroups * dstate;
+        a.b_col0 = 0;
+        a.csrc = static_cast<const uint16_t*>(Cm);
+        a.c_row = ngroups * dstate;
+        a.c_col0 = 0;
+        a.fused_conv = false;
+        a.K = 2;  // no conv: one halo row staged and ignored
+        a.C_conv = 0;
+        a.act = SSM_ACT_NONE;
+        a.dt = dt;
+        a.A = A;
+        a.init_state = initial_state;
+        a.final_state = final_state;
+        a.seq_idx = seq_idx;
+        a.y = static_cast<uint16_t*>(y);
+        a.B = batch;
+        a.L = seqlen;
+        a.H = nheads;
+        a.P = headdim;
+        a.G = ngroups;
+        a.N = dstate;
+        a.workspace = workspace;
+        hipEvent_t e0, e1;
+        st = timing_events(&e0, &e1);
+        if (st != SSM_OK) return st;
+        return hip_status(ssm::launch_chunked(a, s, e0, e1), fn);
+    }
+    if (!ssm::recurrent_supported(headdim, dstate))
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_scan_fwd: dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
+    return run_recurrent_scan(fn, x, nheads * headdim, Bm, Cm, ngroups * dstate, dt, A,
+                              initial_state, final_state, seq_idx, y, batch, seqlen, nheads,
+                              headdim, ngroups, dstate, dtype, s);
+}
+
+ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float* conv_bias,
+                               const void* conv_initial_state, void* conv_final_state,
+                               const float* dt, const float* A, const float* initial_state,
+                               float* final_state, const int32_t* seq_idx, void* y,
+                               int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t ngroups, int64_t dstate, int64_t width,
+                               ssm_dtype_t dtype, ssm_act_t act, void* workspace,
+                               size_t workspace_bytes, ssm_stream_t stream) {
+    const char* fn = "ssm_conv_scan_fwd";
+    ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate, dtype);
+    if (st != SSM_OK) return st;
+    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv_scan_fwd: bad activation");
+    if (width < 2 || width > 8)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv_scan_fwd: width must be in [2, 8]");
+    const size_t es = esize(dtype);
+    const bool work = batch > 0 && seqlen > 0;
+    st = check_ptrs(fn, {{"xBC", xBC, work, es},
+                         {"conv_w", conv_w, work, 4},
+                         {"conv_bias", conv_bias, false, 4},
+                         {"conv_initial_state", conv_initial_state, false, es},
+                         {"conv_final_state", conv_final_state, false, es},
+                         {"dt", dt, work, 4},
+                         {"A", A, work, 4},
+                         {"initial_state", initial_state, false, 16},
+                         {"final_state", final_state, false, 16},
+                         {"seq_idx", seq_idx, false, 4},
+                         {"y", y, work, es}});
+    if (st != SSM_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t C_conv = nheads * headdim + 2 * ngroups * dstate;
+    if (batch == 0) return ok();
+    if (seqlen == 0) {
+        hipError_t e = ssm::launch_conv1d_fwd(nullptr, conv_w, conv_bias, conv_initial_state,
+                                              conv_final_state, nullptr, nullptr, batch, 0,
+                                              C_conv, width, dtype, act, s);
+        if (e == hipSuccess)
+            e = ssm::launch_copy_or_zero_f32(final_state, initial_state,
+                                             batch * nheads * headdim * dstate, s);
+        return hip_status(e, fn);
+    }
+    if (ssm::chunked_supported(headdim, dstate, dtype)) {
+        const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, ngroups, dstate);
+        if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+            return fail(SSM_ERR_WORKSPACE, "ssm_conv_scan_fwd: workspace must be >= " +
+                                               std::to_string(need) + " bytes, 16-byte aligned");
+        if (!aligned(xBC, 16) || C_conv % 8 != 0 || !aligned(y, 8))
+            return fail(SSM_ERR_ALIGNMENT,
+                        "ssm_conv_scan_fwd: xBC must be 16-byte aligned with a channel count "
+                        "divisible by 8, y 8-byte aligned");
+        ssm::ChunkedArgs a{};
+        a.x = static_cast<const uint16_t*>(xBC);
+        a.x_row = C_conv;
+        a.x_col0 = 0;
+        a.bsrc = a.x;
+        a.b_row = C_conv;
+        a.b_col0 = nheads * headdim;
+        a.csrc = a.x;
+        a.c_row = C_conv;
+        a.c_col0 = nheads * headdim + ngroups * dstate;
+        a.fused_conv = true;
+        a.conv_w = conv_w;
+        a.conv_b = conv_bias;
+        a.conv_init = static_cast<const uint16_t*>(conv_initial_state);
+        a.conv_final = static_cast<uint16_t*>(conv_final_state);
+        a.C_conv = C_conv;
+        a.K = width;
+        a.act = act;
+        a.dt = dt;
+        a.A = A;
+        a.init_state = initial_state;
+        a.final_state = final_state;
+        a.seq_idx = seq_idx;
+        a.y = static_cast<uint16_t*>(y);
+        a.B = batch;
+        a.L = seqlen;
+        a.H = nheads;
+        a.P = headdim;
+        a.G = ngroups;
+        a.N = dstate;
+        a.workspace = workspace;
+        hipEvent_t e0, e1;
+        st = timing_events(&e0, &e1);
+        if (st != SSM_OK) return st;
+        return hip_status(ssm::launch_chunked(a, s, e0, e1), fn);
+    }
+    // general shapes: conv into the workspace, then the token-sequential scan reading its
+    // x | B | C channel ranges in place
+    if (!ssm::recurrent_supported(headdim, dstate))
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv_scan_fwd: dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
+    const size_t need = static_cast<size_t>(batch * seqlen * C_conv) * es;
+    if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(SSM_ERR_WORKSPACE, "ssm_conv_scan_fwd: workspace must be >= " +
+                                           std::to_string(need) + " bytes, 16-byte aligned");
+    hipError_t e = ssm::launch_conv1d_fwd(xBC, conv_w, conv_bias, conv_initial_state,
+                                          conv_final_state, seq_idx, workspace, batch, seqlen,
+                                          C_conv, width, dtype, act, s);
+    if (e != hipSuccess) return hip_status(e, fn);
+    const uint8_t* base = static_cast<const uint8_t*>(workspace);
+    return run_recurrent_scan(fn, base, C_conv, base + nheads * headdim * es,
+                              base + (nheads * headdim + ngroups * dstate) * es, C_conv, dt, A,
+                              initial_state, final_state, seq_idx, y, batch, seqlen, nheads,
+                              headdim, ngroups, dstate, dtype, s);
+}
+
+ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, const float* dt,
+                      const float* A, const void* Bm, int64_t B_sb, int64_t B_st, int64_t B_sc,
+                      const void* Cm, int64_t C_sb, int64_t C_st, int64_t C_sc, float* state,
+                      const int32_t* state_indices, void* y, int64_t batch, int64_t n_new,
+                      int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                      int64_t n_slots, ssm_dtype_t dtype, ssm_stream_t stream) {
+    const char* fn = "ssm_step";
+    ssm_status_t st = check_scan_dims(fn, batch, n_new, nheads, headdim, ngroups, dstate, dtype);
+    if (st != SSM_OK) return st;
+    if (n_slots < 1) return fail(SSM_ERR_INVALID_ARG, "ssm_step: n_slots must be >= 1");
+    if (!ssm::recurrent_supported(headdim, dstate))
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_step: dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
+    const size_t es = esize(dtype);
+    const bool work = batch > 0 && n_new > 0;
+    st = check_ptrs(fn, {{"x", x, work, es},
+                         {"dt", dt, work, 4},
+                         {"A", A, work, 4},
+                         {"Bm", Bm, work, es},
+                         {"Cm", Cm, work, es},
+                         {"state", state, work, 16},
+                         {"state_indices", state_indices, false, 4},
+                         {"y", y, work, es}});
+    if (st != SSM_OK) return st;
+    if (!work) return ok();
+    ssm::RecurrentArgs r{};
+    r.x = x;
+    r.x_sb = x_sb;
+    r.x_st = x_st;
+    r.x_sc = x_sc;
+    r.dt = dt;
+    r.A = A;
+    r.Bm = Bm;
+    r.B_sb = B_sb;
+    r.B_st = B_st;
+    r.B_sc = B_sc;
+    r.Cm = Cm;
+    r.C_sb = C_sb;
+    r.C_st = C_st;
+    r.C_sc = C_sc;
+    r.state_in = state;
+    r.state_out = state;
+    r.indices = state_indices;
+    r.n_slots = n_slots;
+    r.seq_idx = nullptr;
+    r.y = y;
+    r.B = batch;
+    r.T = n_new;
+    r.H = nheads;
+    r.P = headdim;
+    r.G = ngroups;
+    r.N = dstate;
+    return hip_status(ssm::launch_recurrent(r, dtype, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+ssm_status_t ssm_timing_enable(int enable) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing = enable != 0;
+    return ok();
+}
+
+ssm_status_t ssm_timing_read(double* total_ms, int64_t* launches) {
+    if (!total_ms || !launches) return fail(SSM_ERR_INVALID_ARG, "ssm_timing_read: NULL output");
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> evs;
+    {
+        std::lock_guard<std::mutex> lk(g_tmu);
+        evs.swap(g_events);
+    }
+    double sum = 0.0;
+    hipError_t err = hipSuccess;
+    for (auto& pr : evs) {
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(pr.second);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+        if (e != hipSuccess && err == hipSuccess) err = e;
+        sum += ms;
+        hipEventDestroy(pr.first);
+        hipEventDestroy(pr.second);
+    }
+    *total_ms = sum;
+    *launches = static_cast<int64_t>(evs.size());
+    return hip_status(err, "ssm_timing_read");
+}
+
+}  // extern "C"

@@ -1,0 +1,350 @@
+// conv.hip -- causal depthwise conv1d with state (prefill) and its decode-time update.
+//
+// Prefill, causal-conv1d tutorial ch. 7, "defining the state through the extended sequence"
+// and "packed-sequence boundaries": out_t = phi(bias + sum_k w_k u_{t+k}) over
+// u = [S, x]; F = u[L : L+K-1].  Each thread owns V adjacent channels of one batch row and a
+// run of TT tokens; the K-1 previous inputs live in registers and slide along the run, so
+// every input element is read from HBM once (plus a K-1 halo per run).  Channel-last rows
+// give 16-byte coalesced loads/stores (V = 8 bf16 or 4 fp32 channels per thread).
+//
+// Decode, same chapter, "single-token update maths", "the physical cache may exceed the
+// minimal history", "state indices for continuous batching": one thread per (row, channel)
+// reads its K-1 history values from the pool row into registers first, then produces the
+// n_new outputs and only then writes the raw new inputs back into the ring (or shifts the
+// linear row), so nothing it still needs is overwritten.
+#include "internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kConvThreads = 64;  // one wavefront per block
+constexpr int kConvTokens = 32;   // tokens per thread run (>= K-1 for every K <= 8)
+
+template <class D, int V>
+struct Vec;
+template <>
+struct Vec<BF16, 8> {
+    __device__ static void load(const uint16_t* p, float (&v)[8]) {
+        uint4 q = *reinterpret_cast<const uint4*>(p);
+        uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ static void store(uint16_t* p, const float (&v)[8]) {
+        uint4 q;
+        q.x = pack_bf16x2(v[0], v[1]);
+        q.y = pack_bf16x2(v[2], v[3]);
+        q.z = pack_bf16x2(v[4], v[5]);
+        q.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(p) = q;
+    }
+};
+template <>
+struct Vec<F32, 4> {
+    __device__ static void load(const float* p, float (&v)[4]) {
+        float4 q = *reinterpret_cast<const float4*>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+    __device__ static void store(float* p, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+template <class D>
+struct Vec<D, 1> {
+    __device__ static void load(const typename D::T* p, float (&v)[1]) { v[0] = D::load(p, 0); }
+    __device__ static void store(typename D::T* p, const float (&v)[1]) { D::store(p, 0, v[0]); }
+};
+
+// Accumulation: fp32 for fp32 storage; double for bf16 storage, where the products of fp32
+// weights and bf16 inputs are exact and the output's bf16 rounding then matches the exact
+// conv value's (see act_to_bf16).
+template <class D>
+struct Acc;
+template <>
+struct Acc<F32> {
+    using T = float;
+    __device__ static float out(float z, int act) { return apply_act(z, act); }
+};
+template <>
+struct Acc<BF16> {
+    using T = double;
+    // returns the bf16 result widened to float (exact), for the float-valued store path
+    __device__ static float out(double z, int act) { return bf16_to_f32(act_to_bf16(z, act)); }
+};
+
+template <class D, int V, int K, bool HAS_SEQ>
+__global__ void __launch_bounds__(kConvThreads)
+conv1d_fwd_kernel(const typename D::T* __restrict__ x, const float* __restrict__ w,
+                  const float* __restrict__ bias, const typename D::T* init_state,
+                  typename D::T* final_state, const int32_t* __restrict__ seq_idx,
+                  typename D::T* __restrict__ out, int64_t L, int64_t C, int act) {
+    using T = typename D::T;
+    const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x) * V;
+    if (c0 >= C) return;
+    const int64_t b = blockIdx.z;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kConvTokens;
+    const int64_t t1 = min(t0 + kConvTokens, L);
+
+    using AT = typename Acc<D>::T;
+    AT wr[V][K];
+    AT bv[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) wr[v][k] = w[(c0 + v) * K + k];
+        bv[v] = bias ? bias[c0 + v] : 0.0f;
+    }
+
+    // u-positions t0-K+1 .. t0-1 (oldest first): from x, or from the state for pos < 0
+    AT hist[K - 1][V];
+    int32_t hid[K - 1];
+    const int32_t id0 = HAS_SEQ ? seq_idx[b * L] : 0;
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+        const int64_t pos = t0 - (K - 1) + j;
+        if (pos >= 0) {
+            float tmp[V];
+            Vec<D, V>::load(x + (b * L + pos) * C + c0, tmp);
+#pragma unroll
+            for (int v = 0; v < V; ++v) hist[j][v] = tmp[v];
+            hid[j] = HAS_SEQ ? seq_idx[b * L + pos] : 0;
+        } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                hist[j][v] = init_state ? D::load(init_state, ((b * C + c0 + v) * (K - 1)) + (K - 1) + pos) : 0.0f;
+            hid[j] = id0;
+        }
+    }
+
+    for (int64_t t = t0; t < t1; ++t) {
+        float xf[V];
+        Vec<D, V>::load(x + (b * L + t) * C + c0, xf);
+        const int32_t idt = HAS_SEQ ? seq_idx[b * L + t] : 0;
+        float z[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const AT xv = xf[v];
+            AT acc = bv[v];
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) {
+                const AT tap = (!HAS_SEQ || hid[k] == idt) ? hist[k][v] : AT(0);
+                acc = fma(wr[v][k], tap, acc);
+            }
+            acc = fma(wr[v][K - 1], xv, acc);
+            z[v] = Acc<D>::out(acc, act);
+        }
+        Vec<D, V>::store(out + (b * L + t) * C + c0, z);
+#pragma unroll
+        for (int k = 0; k < K - 2; ++k) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) hist[k][v] = hist[k + 1][v];
+            hid[k] = hid[k + 1];
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) hist[K - 2][v] = xf[v];
+        hid[K - 2] = idt;
+    }
+
+    // F = u[L .. L+K-2], written by the run that read the initial state (so an in-place
+    // state pair is read before it is overwritten)
+    if (final_state != nullptr && t0 == 0) {
+        T fv[V][K - 1];
+#pragma unroll
+        for (int r = 0; r < K - 1; ++r) {
+            const int64_t m = L + r;  // index into u
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (m < K - 1) {
+                    fv[v][r] = init_state ? init_state[(b * C + c0 + v) * (K - 1) + m] : T(0);
+                } else {
+                    fv[v][r] = x[(b * L + (m - (K - 1))) * C + c0 + v];
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int r = 0; r < K - 1; ++r) final_state[(b * C + c0 + v) * (K - 1) + r] = fv[v][r];
+    }
+}
+
+// seqlen == 0: F = S (or zeros)
+template <class D>
+__global__ void conv_state_passthrough_kernel(const typename D::T* init_state,
+                                              typename D::T* final_state, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) final_state[i] = init_state ? init_state[i] : typename D::T(0);
+}
+
+template <class D, int V, int K>
+hipError_t conv_fwd_dispatch_seq(const void* x, const float* w, const float* bias,
+                                 const void* init_state, void* final_state,
+                                 const int32_t* seq_idx, void* out, int64_t B, int64_t L,
+                                 int64_t C, int act, hipStream_t stream) {
+    using T = typename D::T;
+    const int64_t threads_needed = (C + V - 1) / V;
+    dim3 grid((threads_needed + kConvThreads - 1) / kConvThreads,
+              (L + kConvTokens - 1) / kConvTokens, B);
+    if (seq_idx)
+        conv1d_fwd_kernel<D, V, K, true><<<grid, kConvThreads, 0, stream>>>(
+            (const T*)x, w, bias, (const T*)init_state, (T*)final_state, seq_idx, (T*)out, L,
+            C, act);
+    else
+        conv1d_fwd_kernel<D, V, K, false><<<grid, kConvThreads, 0, stream>>>(
+            (const T*)x, w, bias, (const T*)init_state, (T*)final_state, seq_idx, (T*)out, L,
+            C, act);
+    return hipGetLastError();
+}
+
+template <class D, int V>
+hipError_t conv_fwd_dispatch_k(int64_t K, const void* x, const float* w, const float* bias,
+                               const void* init_state, void* final_state,
+                               const int32_t* seq_idx, void* out, int64_t B, int64_t L,
+                               int64_t C, int act, hipStream_t stream) {
+#define SSM_CONV_K(KK)                                                                    \
+    case KK:                                                                              \
+        return conv_fwd_dispatch_seq<D, V, KK>(x, w, bias, init_state, final_state,      \
+                                               seq_idx, out, B, L, C, act, stream);
+    switch (K) {
+        SSM_CONV_K(2) SSM_CONV_K(3) SSM_CONV_K(4) SSM_CONV_K(5) SSM_CONV_K(6) SSM_CONV_K(7)
+        SSM_CONV_K(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef SSM_CONV_K
+}
+
+// ---------------------------------------------------------------------------------------
+// decode update
+// ---------------------------------------------------------------------------------------
+template <class D, int K>
+__global__ void __launch_bounds__(256)
+conv1d_update_kernel(const typename D::T* __restrict__ x, typename D::T* pool,
+                     const float* __restrict__ w, const float* __restrict__ bias,
+                     const int32_t* __restrict__ indices, const int32_t* __restrict__ seqlens,
+                     typename D::T* __restrict__ out, int64_t C, int64_t L_new,
+                     int64_t state_len, int64_t n_slots, int act) {
+    using T = typename D::T;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    const int64_t b = blockIdx.y;
+    const int64_t s = indices ? static_cast<int64_t>(indices[b]) : b;
+    T* o = out + (b * C + c) * L_new;
+    if (s < 0 || s >= n_slots) {
+        for (int64_t i = 0; i < L_new; ++i) D::store(o, i, 0.0f);
+        return;
+    }
+    T* row = pool + (s * C + c) * state_len;
+    const T* xr = x + (b * C + c) * L_new;
+    const int64_t p = seqlens ? static_cast<int64_t>(seqlens[b]) : 0;
+
+    using AT = typename Acc<D>::T;
+    AT wr[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wr[k] = w[c * K + k];
+    const AT bv = bias ? bias[c] : 0.0f;
+
+    // history, oldest first: hist[K-1-j] = value j steps back (read before any write)
+    AT hist[K - 1];
+#pragma unroll
+    for (int j = 1; j <= K - 1; ++j) {
+        const int64_t slot = seqlens ? floor_mod(p - j, state_len) : state_len - j;
+        hist[K - 1 - j] = D::load(row, slot);
+    }
+    for (int64_t i = 0; i < L_new; ++i) {
+        const AT xv = D::load(xr, i);
+        AT acc = bv;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) acc = fma(wr[k], hist[k], acc);
+        acc = fma(wr[K - 1], xv, acc);
+        D::store(o, i, Acc<D>::out(acc, act));
+#pragma unroll
+        for (int k = 0; k < K - 2; ++k) hist[k] = hist[k + 1];
+        hist[K - 2] = xv;
+    }
+    // write the raw inputs (never the outputs) back into the cache
+    if (seqlens) {
+        for (int64_t i = 0; i < L_new; ++i) row[floor_mod(p + i, state_len)] = xr[i];
+    } else {
+        // row <- last state_len entries of (row ++ x); sources sit at or after their
+        // destinations, so a forward copy is safe in place
+        for (int64_t i = 0; i < state_len; ++i) {
+            const int64_t q = L_new + i;
+            row[i] = q < state_len ? row[q] : xr[q - state_len];
+        }
+    }
+}
+
+template <class D>
+hipError_t conv_update_dispatch(int64_t K, const void* x, void* pool, const float* w,
+                                const float* bias, const int32_t* indices,
+                                const int32_t* seqlens, void* out, int64_t B, int64_t C,
+                                int64_t L_new, int64_t state_len, int64_t n_slots, int act,
+                                hipStream_t stream) {
+    using T = typename D::T;
+    dim3 grid((C + 255) / 256, B);
+#define SSM_UPD_K(KK)                                                                      \
+    case KK:                                                                               \
+        conv1d_update_kernel<D, KK><<<grid, 256, 0, stream>>>(                             \
+            (const T*)x, (T*)pool, w, bias, indices, seqlens, (T*)out, C, L_new, state_len, \
+            n_slots, act);                                                                 \
+        break;
+    switch (K) {
+        SSM_UPD_K(2) SSM_UPD_K(3) SSM_UPD_K(4) SSM_UPD_K(5) SSM_UPD_K(6) SSM_UPD_K(7)
+        SSM_UPD_K(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef SSM_UPD_K
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv1d_fwd(const void* x, const float* w, const float* bias,
+                             const void* init_state, void* final_state, const int32_t* seq_idx,
+                             void* out, int64_t B, int64_t L, int64_t C, int64_t K,
+                             ssm_dtype_t dtype, int act, hipStream_t stream) {
+    if (B == 0) return hipSuccess;
+    if (L == 0) {
+        if (!final_state) return hipSuccess;
+        const int64_t n = B * C * (K - 1);
+        const int blocks = static_cast<int>((n + 255) / 256);
+        if (dtype == SSM_BF16)
+            conv_state_passthrough_kernel<BF16><<<blocks, 256, 0, stream>>>(
+                (const uint16_t*)init_state, (uint16_t*)final_state, n);
+        else
+            conv_state_passthrough_kernel<F32><<<blocks, 256, 0, stream>>>(
+                (const float*)init_state, (float*)final_state, n);
+        return hipGetLastError();
+    }
+    const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out);
+    if (dtype == SSM_BF16) {
+        if (C % 8 == 0 && (align & 15) == 0)
+            return conv_fwd_dispatch_k<BF16, 8>(K, x, w, bias, init_state, final_state, seq_idx,
+                                               out, B, L, C, act, stream);
+        return conv_fwd_dispatch_k<BF16, 1>(K, x, w, bias, init_state, final_state, seq_idx,
+                                           out, B, L, C, act, stream);
+    }
+    if (C % 4 == 0 && (align & 15) == 0)
+        return conv_fwd_dispatch_k<F32, 4>(K, x, w, bias, init_state, final_state, seq_idx, out,
+                                          B, L, C, act, stream);
+    return conv_fwd_dispatch_k<F32, 1>(K, x, w, bias, init_state, final_state, seq_idx, out, B,
+                                      L, C, act, stream);
+}
+
+hipError_t launch_conv1d_update(const void* x, void* pool, const float* w, const float* bias,
+                                const int32_t* indices, const int32_t* cache_seqlens, void* out,
+                                int64_t B, int64_t C, int64_t L_new, int64_t K,
+                                int64_t state_len, int64_t n_slots, ssm_dtype_t dtype, int act,
+                                hipStream_t stream) {
+    if (B == 0 || L_new == 0) return hipSuccess;
+    if (dtype == SSM_BF16)
+        return conv_update_dispatch<BF16>(K, x, pool, w, bias, indices, cache_seqlens, out, B, C,
+                                          L_new, state_len, n_slots, act, stream);
+    return conv_update_dispatch<F32>(K, x, pool, w, bias, indices, cache_seqlens, out, B, C,
+                                     L_new, state_len, n_slots, act, stream);
+}
+
+}  // namespace ssm

@@ -1,0 +1,151 @@
+// internal.h -- shared device helpers and launcher declarations of the HIP library.
+// Not part of the public ABI (see include/ssm_mi355x.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ssm_mi355x.h"
+
+namespace ssm {
+
+// ---------------------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 b = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+struct F32 {
+    using T = float;
+    static constexpr int kBytes = 4;
+    __device__ __forceinline__ static float load(const T* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = v; }
+};
+struct BF16 {
+    using T = uint16_t;
+    static constexpr int kBytes = 2;
+    __device__ __forceinline__ static float load(const T* p, int64_t i) { return bf16_to_f32(p[i]); }
+    __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// phi: identity or SiLU(z) = z / (1 + exp(-z)); exp(-z) = inf gives -0 for very negative z
+__device__ __forceinline__ float apply_act(float z, int act) {
+    if (act == SSM_ACT_SILU) return z * __frcp_rn(1.0f + __expf(-z));
+    return z;
+}
+
+// Round a double to bf16, nearest even, without the double rounding of a plain
+// double -> float -> bf16 chain: when the float lands exactly on a bf16 midpoint, the part
+// the float dropped decides the direction.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+    const float f = static_cast<float>(v);
+    const uint32_t b = __float_as_uint(f);
+    if ((b & 0xFFFFu) == 0x8000u && static_cast<double>(f) != v) {
+        const bool away = fabs(v) > fabs(static_cast<double>(f));
+        return static_cast<uint16_t>((away ? b + 0x8000u : b - 0x8000u) >> 16);
+    }
+    return f32_to_bf16(f);
+}
+
+// bf16(phi(z)) for a conv sum z held in double (exact products of fp32 weights and 16-bit
+// inputs), rounded as the exact phi(z) rounds.  SiLU runs in fp32; its error is below
+// 4 + 2|z| fp32 ulps (argument rounding through the condition number 1 + |z|, the exp
+// argument's relative rounding, v_exp / v_rcp and three roundings).  Only results closer
+// than twice that to a bf16 rounding midpoint are recomputed in double, so the rounding
+// decision matches the exact value's.
+__device__ __forceinline__ uint16_t act_to_bf16(double z, int act) {
+    if (act != SSM_ACT_SILU) return f64_to_bf16(z);
+    const float zf = static_cast<float>(z);
+    const float s = zf * __frcp_rn(1.0f + __expf(-zf));
+    const int dist = abs(static_cast<int>(__float_as_uint(s) & 0xFFFFu) - 0x8000);
+    if (static_cast<float>(dist) > 8.0f + 4.0f * fabsf(zf)) return f32_to_bf16(s);
+    return f64_to_bf16(z / (1.0 + exp(-z)));
+}
+
+__host__ __device__ __forceinline__ int64_t floor_mod(int64_t a, int64_t m) {
+    int64_t r = a % m;
+    return r < 0 ? r + m : r;
+}
+
+// ---------------------------------------------------------------------------------------
+// launchers (return hipSuccess or the launch error); arguments are validated by the ABI
+// ---------------------------------------------------------------------------------------
+hipError_t launch_conv1d_fwd(const void* x, const float* w, const float* bias,
+                             const void* init_state, void* final_state, const int32_t* seq_idx,
+                             void* out, int64_t B, int64_t L, int64_t C, int64_t K,
+                             ssm_dtype_t dtype, int act, hipStream_t stream);
+
+hipError_t launch_conv1d_update(const void* x, void* pool, const float* w, const float* bias,
+                                const int32_t* indices, const int32_t* cache_seqlens, void* out,
+                                int64_t B, int64_t C, int64_t L_new, int64_t K,
+                                int64_t state_len, int64_t n_slots, ssm_dtype_t dtype, int act,
+                                hipStream_t stream);
+
+// Recurrent (token-sequential) scan used by ssm_step and as the general-shape scan path.
+struct RecurrentArgs {
+    const void* x;
+    int64_t x_sb, x_st, x_sc;
+    const float* dt;  // [B, T, H]
+    const float* A;   // [H]
+    const void* Bm;
+    int64_t B_sb, B_st, B_sc;
+    const void* Cm;
+    int64_t C_sb, C_st, C_sc;
+    const float* state_in;    // base of [slots or B, H, P, N] (NULL -> zeros)
+    float* state_out;         // base of [slots or B, H, P, N] (NULL -> not written)
+    const int32_t* indices;   // [B] slot per row or NULL (slot = b)
+    int64_t n_slots;          // bound for indices (rows outside are skipped, y zeroed)
+    const int32_t* seq_idx;   // [B, T] or NULL
+    void* y;                  // [B, T, H, P]
+    int64_t B, T, H, P, G, N;
+};
+bool recurrent_supported(int64_t P, int64_t N);
+hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream);
+
+// Chunked (SSD) scan on MFMA for bf16 inputs with headdim 64, dstate 128.
+bool chunked_supported(int64_t P, int64_t N, ssm_dtype_t dtype);
+size_t chunked_workspace_bytes(int64_t B, int64_t L, int64_t G, int64_t N);
+struct ChunkedArgs {
+    // x channels: element (b, t, h*P + p) at x[(b*L + t)*x_row + x_col0 + h*P + p]  (bf16)
+    const uint16_t* x;
+    int64_t x_row, x_col0;
+    // B / C channels: element (b, t, g, n) at src[(b*L + t)*row + col0 + g*N + n]  (bf16);
+    // in the fused call both point into xBC, otherwise at the Bm / Cm arrays
+    const uint16_t* bsrc;
+    int64_t b_row, b_col0;
+    const uint16_t* csrc;
+    int64_t c_row, c_col0;
+    // fused conv (x_col0 = 0, b_col0 = H*P, c_col0 = H*P + G*N inside xBC rows of C_conv)
+    bool fused_conv;
+    const float* conv_w;        // [C_conv, K]
+    const float* conv_b;        // [C_conv] or NULL
+    const uint16_t* conv_init;  // [B, C_conv, K-1] or NULL
+    uint16_t* conv_final;       // [B, C_conv, K-1] or NULL
+    int64_t C_conv, K;
+    int act;
+    const float* dt;            // [B, L, H]
+    const float* A;             // [H]
+    const float* init_state;    // [B, H, P, N] or NULL
+    float* final_state;         // [B, H, P, N] or NULL
+    const int32_t* seq_idx;     // [B, L] or NULL
+    uint16_t* y;                // [B, L, H, P]
+    int64_t B, L, H, P, G, N;
+    void* workspace;            // chunked_workspace_bytes(B, L, G, N)
+};
+hipError_t launch_chunked(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev_before_main,
+                          hipEvent_t ev_after_main);
+
+// small helpers
+hipError_t launch_copy_or_zero_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+hipError_t launch_copy_or_zero_bytes(void* dst, const void* src, int64_t nbytes, hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,94 @@
+"""The C-ABI library loads and exports every entry point its header declares; argument
+checks that fail before any HIP call return the documented status codes (CPU only: none of
+these calls reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_mi355x.h")
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import ssm_sequence_models_amd as s
+    return s._lib
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
+              "ssm_step", "ssm_scan_workspace_size", "ssm_abi_version", "ssm_status_string",
+              "ssm_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ssm_abi_version() == 1
+    for code in range(6):
+        assert lib.ssm_status_string(code)
+
+
+def test_workspace_query():
+    import ssm_sequence_models_amd as s
+    # chunked path: per (row, chunk of 64, group): C 16 KiB + B^T 16 KiB + G 16 KiB
+    assert s.workspace_size(4, 8192, 64, 64, 1, 128) == 4 * 128 * 48 * 1024
+    assert s.workspace_size(2, 65, 4, 64, 2, 128) == 2 * 2 * 2 * 48 * 1024
+    # general shapes: room for the conv output of the fused call
+    import torch
+    assert s.workspace_size(1, 64, 1, 4, 1, 4, torch.float32) == 64 * 12 * 4
+    assert s.workspace_size(0, 64, 1, 4, 1, 4) == 0
+
+
+def _c(v):
+    return ctypes.c_void_p(v)
+
+
+def test_argument_errors_return_status(lib):
+    dummy = _c(256)  # never dereferenced: every call below fails its host-side checks
+    # width outside [2, 8]
+    assert lib.ssm_conv1d_fwd(dummy, dummy, None, None, None, None, dummy, 1, 4, 8, 9, 1, 0,
+                              None) == 2
+    # bad dtype / activation
+    assert lib.ssm_conv1d_fwd(dummy, dummy, None, None, None, None, dummy, 1, 4, 8, 4, 7, 0,
+                              None) == 1
+    assert lib.ssm_conv1d_fwd(dummy, dummy, None, None, None, None, dummy, 1, 4, 8, 4, 1, 5,
+                              None) == 1
+    # NULL required pointer
+    assert lib.ssm_conv1d_fwd(None, dummy, None, None, None, None, dummy, 1, 4, 8, 4, 1, 0,
+                              None) == 1
+    assert b"x is NULL" in lib.ssm_last_error()
+    # misaligned bf16 pointer
+    assert lib.ssm_conv1d_fwd(_c(257), dummy, None, None, None, None, dummy, 1, 4, 8, 4, 1, 0,
+                              None) == 3
+    # state_len < width - 1
+    assert lib.ssm_conv1d_update(dummy, dummy, dummy, None, None, None, dummy, 2, 8, 1, 4, 2,
+                                 4, 1, 0, None) == 1
+    # nheads not a multiple of ngroups
+    assert lib.ssm_scan_fwd(dummy, dummy, dummy, dummy, dummy, None, None, None, dummy, 1, 64,
+                            3, 64, 2, 128, 1, None, 0, None) == 1
+    # chunked path without workspace
+    assert lib.ssm_scan_fwd(dummy, dummy, dummy, dummy, dummy, None, None, None, dummy, 1, 64,
+                            4, 64, 1, 128, 1, None, 0, None) == 4
+    # unsupported state size for the general path
+    assert lib.ssm_step(dummy, 0, 0, 1, dummy, dummy, dummy, 0, 0, 1, dummy, 0, 0, 1, dummy,
+                        None, dummy, 1, 1, 1, 4, 1, 6, 4, 0, None) == 2
+    # zero-sized work is a no-op that succeeds without touching the device
+    assert lib.ssm_conv1d_update(None, None, None, None, None, None, None, 0, 8, 1, 4, 3, 4, 1,
+                                 0, None) == 0
+    assert lib.ssm_step(None, 0, 0, 1, None, None, None, 0, 0, 1, None, 0, 0, 1, None, None,
+                        None, 3, 0, 2, 4, 1, 8, 4, 0, None) == 0

@@ -1,0 +1,239 @@
+"""GPU parity of ssm_scan_fwd, ssm_conv_scan_fwd and ssm_step against the fp64 oracle, at
+sizes the oracle finishes in seconds that still span several 64-token chunks and a ragged
+tail, plus the degenerate cases.  y and final states within |g - o| <= 1e-3 + 2e-2 |o|;
+conv final states bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import assert_bitexact, assert_close, dev
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+ODT = {BF16: "bf16", F32: "f32"}
+
+
+def _scan_inputs(B, L, H, P, N, G, dtype, seed, with_init=True, segs=0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(B, L, H, P, generator=g).to(dtype)
+    dt = torch.nn.functional.softplus(torch.randn(B, L, H, generator=g) - 2.0)
+    A = -torch.exp(torch.rand(H, generator=g) * float(np.log(16.0)))
+    Bm = torch.randn(B, L, G, N, generator=g).to(dtype)
+    Cm = torch.randn(B, L, G, N, generator=g).to(dtype)
+    init = torch.randn(B, H, P, N, generator=g) if with_init else None
+    seq = workloads.packed_seq_idx(B, L, seed + 7, segs) if segs and L > segs else None
+    return x, dt, A, Bm, Cm, init, seq
+
+
+SCAN_CASES = [
+    # B, L, H, P, N, G, dtype, init, segments
+    (2, 200, 4, 64, 128, 1, BF16, True, 0),    # chunked: 3 full chunks + ragged 8
+    (2, 200, 4, 64, 128, 2, BF16, True, 0),    # two groups
+    (2, 200, 4, 64, 128, 1, BF16, True, 4),    # packed sequences
+    (1, 64, 2, 64, 128, 1, BF16, False, 0),    # exactly one chunk, zero state
+    (1, 1, 2, 64, 128, 1, BF16, True, 0),      # one token
+    (1, 129, 2, 64, 128, 1, BF16, True, 3),    # resets near chunk edges possible
+    (1, 64, 1, 4, 4, 1, F32, True, 0),         # the tiny layer (token-sequential path)
+    (2, 50, 3, 4, 8, 1, F32, True, 3),
+    (2, 70, 2, 16, 32, 2, BF16, True, 0),      # general shape in bf16
+]
+
+
+@pytest.mark.parametrize("B,L,H,P,N,G,dtype,with_init,segs", SCAN_CASES)
+def test_scan_fwd_matches_oracle(B, L, H, P, N, G, dtype, with_init, segs):
+    import ssm_sequence_models_amd as ssm
+    x, dt, A, Bm, Cm, init, seq = _scan_inputs(B, L, H, P, N, G, dtype,
+                                               seed=B + L + H + P + N + G, with_init=with_init,
+                                               segs=segs)
+    y, fin = ssm.scan_fwd(dev(x), dev(dt), dev(A), dev(Bm), dev(Cm), dev(init), dev(seq))
+    torch.cuda.synchronize()
+    ry, rfin = oracle.scan_fwd(x, dt, A, Bm, Cm, init, seq, out_dtype=ODT[dtype],
+                               state_dtype="f32")
+    assert_close(y, ry, "y")
+    assert_close(fin, rfin, "final state")
+
+
+def test_scan_fwd_len0_and_inplace():
+    import ssm_sequence_models_amd as ssm
+    x, dt, A, Bm, Cm, init, _ = _scan_inputs(2, 0, 4, 64, 128, 1, BF16, seed=3)
+    _, fin = ssm.scan_fwd(dev(x), dev(dt), dev(A), dev(Bm), dev(Cm), dev(init))
+    assert_bitexact(fin, init, "L = 0 returns the initial state")
+    x, dt, A, Bm, Cm, init, _ = _scan_inputs(2, 150, 4, 64, 128, 1, BF16, seed=4)
+    st = dev(init).clone()
+    y, _ = ssm.scan_fwd(dev(x), dev(dt), dev(A), dev(Bm), dev(Cm), st, final_state=st)
+    ry, rfin = oracle.scan_fwd(x, dt, A, Bm, Cm, init, out_dtype="bf16", state_dtype="f32")
+    assert_close(y, ry, "y (in place)")
+    assert_close(st, rfin, "final state (in place)")
+
+
+def _fused_inputs(B, L, H, P, N, G, K, dtype, seed, with_init=True, segs=0):
+    C = H * P + 2 * G * N
+    g = torch.Generator().manual_seed(seed)
+    xBC = torch.randn(B, L, C, generator=g).to(dtype)
+    w = torch.rand(C, K, generator=g) - 0.5
+    b = torch.rand(C, generator=g) - 0.5
+    dt = torch.nn.functional.softplus(torch.randn(B, L, H, generator=g) - 2.0)
+    A = -torch.exp(torch.rand(H, generator=g) * float(np.log(16.0)))
+    cinit = torch.randn(B, C, K - 1, generator=g).to(dtype) if with_init else None
+    sinit = torch.randn(B, H, P, N, generator=g) if with_init else None
+    seq = workloads.packed_seq_idx(B, L, seed + 7, segs) if segs and L > segs else None
+    return xBC, w, b, dt, A, cinit, sinit, seq
+
+
+FUSED_CASES = [
+    # B, L, H, P, N, G, K, dtype, init, segments
+    (1, 64, 1, 4, 4, 1, 4, F32, True, 0),      # the tiny layer
+    (2, 200, 4, 64, 128, 1, 4, BF16, True, 0),
+    (2, 200, 4, 64, 128, 1, 4, BF16, True, 4),
+    (2, 200, 4, 64, 128, 2, 4, BF16, False, 0),
+    (1, 2, 2, 64, 128, 1, 4, BF16, True, 0),   # L < K-1
+    (1, 130, 2, 64, 128, 1, 3, BF16, True, 2),
+    (1, 100, 2, 64, 128, 1, 8, BF16, True, 0),
+    (2, 40, 2, 16, 32, 1, 4, BF16, True, 2),   # general shape, bf16
+]
+
+
+@pytest.mark.parametrize("B,L,H,P,N,G,K,dtype,with_init,segs", FUSED_CASES)
+def test_conv_scan_fwd_matches_oracle(B, L, H, P, N, G, K, dtype, with_init, segs):
+    import ssm_sequence_models_amd as ssm
+    xBC, w, b, dt, A, cinit, sinit, seq = _fused_inputs(B, L, H, P, N, G, K, dtype,
+                                                        seed=B * 7 + L + H + K, with_init=with_init,
+                                                        segs=segs)
+    y, cfin, sfin = ssm.conv_scan_fwd(dev(xBC), dev(w), dev(b), dev(dt), dev(A), H, P, G, N,
+                                      conv_initial_state=dev(cinit), initial_state=dev(sinit),
+                                      seq_idx=dev(seq))
+    torch.cuda.synchronize()
+    ry, rc, rs = oracle.conv_scan_fwd(xBC, w, b, cinit, dt, A, sinit, seq, H, P, G, N,
+                                      act="silu", out_dtype=ODT[dtype], state_dtype="f32")
+    assert_close(y, ry, "y")
+    assert_close(sfin, rs, "ssm final state")
+    assert_bitexact(cfin, torch.from_numpy(rc).to(dtype), "conv final state")
+
+
+def test_conv_scan_fwd_inplace_states_and_len0():
+    import ssm_sequence_models_amd as ssm
+    H, P, N, G, K = 2, 64, 128, 1, 4
+    xBC, w, b, dt, A, cinit, sinit, _ = _fused_inputs(2, 0, H, P, N, G, K, BF16, seed=21)
+    _, cf, sf = ssm.conv_scan_fwd(dev(xBC), dev(w), dev(b), dev(dt), dev(A), H, P, G, N,
+                                  conv_initial_state=dev(cinit), initial_state=dev(sinit))
+    assert_bitexact(cf, cinit, "L = 0 conv state")
+    assert_bitexact(sf, sinit, "L = 0 ssm state")
+    xBC, w, b, dt, A, cinit, sinit, _ = _fused_inputs(2, 150, H, P, N, G, K, BF16, seed=22)
+    cs, ss = dev(cinit).clone(), dev(sinit).clone()
+    y, _, _ = ssm.conv_scan_fwd(dev(xBC), dev(w), dev(b), dev(dt), dev(A), H, P, G, N,
+                                conv_initial_state=cs, initial_state=ss, conv_final_state=cs,
+                                final_state=ss)
+    ry, rc, rs = oracle.conv_scan_fwd(xBC, w, b, cinit, dt, A, sinit, None, H, P, G, N)
+    assert_close(y, ry, "y (in place)")
+    assert_close(ss, rs, "ssm state (in place)")
+    assert_bitexact(cs, torch.from_numpy(rc).to(BF16), "conv state (in place)")
+
+
+def test_conv_scan_fwd_chunked_calls_equal_one_call():
+    """State passing: calls over A then B with S_B = F_A and h_B = final_A reproduce the
+    single call (length-generalization notes Sec. 2.6; causal-conv1d ch. 7)."""
+    import ssm_sequence_models_amd as ssm
+    H, P, N, G, K = 2, 64, 128, 1, 4
+    xBC, w, b, dt, A, cinit, sinit, _ = _fused_inputs(1, 300, H, P, N, G, K, BF16, seed=23)
+    X, W, Bb, D, AA = dev(xBC), dev(w), dev(b), dev(dt), dev(A)
+    y, cf, sf = ssm.conv_scan_fwd(X, W, Bb, D, AA, H, P, G, N, conv_initial_state=dev(cinit),
+                                  initial_state=dev(sinit))
+    cs, ss = dev(cinit).clone(), dev(sinit).clone()
+    parts = []
+    for a, e in ((0, 2), (2, 64), (64, 100), (100, 300)):
+        yp, _, _ = ssm.conv_scan_fwd(X[:, a:e].contiguous(), W, Bb, D[:, a:e].contiguous(), AA,
+                                     H, P, G, N, conv_initial_state=cs, initial_state=ss,
+                                     conv_final_state=cs, final_state=ss)
+        parts.append(yp)
+    yc = torch.cat(parts, 1)
+    ry, rc, rs = oracle.conv_scan_fwd(xBC, w, b, cinit, dt, A, sinit, None, H, P, G, N)
+    assert_close(yc, ry, "chained y vs oracle")
+    assert_close(ss, rs, "chained state vs oracle")
+    assert_close(yc, y.float().cpu().double().numpy(), "chained y vs one call")
+    assert_bitexact(cs, cf, "chained conv state vs one call")
+
+
+def _step_case(R, n_slots, H, P, N, G, L_new, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(R, L_new, H * P, generator=g).to(dtype)
+    Bm = torch.randn(R, L_new, G * N, generator=g).to(dtype)
+    Cm = torch.randn(R, L_new, G * N, generator=g).to(dtype)
+    dt = torch.nn.functional.softplus(torch.randn(R, L_new, H, generator=g) - 2.0)
+    A = -torch.exp(torch.rand(H, generator=g) * float(np.log(16.0)))
+    pool = torch.randn(n_slots, H, P, N, generator=g)
+    idx = torch.randperm(n_slots, generator=g)[:R].to(torch.int32)
+    return x, Bm, Cm, dt, A, pool, idx
+
+
+@pytest.mark.parametrize("L_new,dtype,P,N", [(1, BF16, 64, 128), (4, BF16, 64, 128),
+                                              (3, F32, 4, 4), (2, BF16, 16, 64)])
+def test_step_matches_oracle(L_new, dtype, P, N):
+    import ssm_sequence_models_amd as ssm
+    R, n_slots, H, G = 6, 10, 4, 2
+    x, Bm, Cm, dt, A, pool, idx = _step_case(R, n_slots, H, P, N, G, L_new, dtype, seed=L_new + P)
+    idx[1] = -1
+    idx[4] = n_slots  # skipped rows
+    S = dev(pool)
+    y = ssm.step(dev(x), dev(dt), dev(A), dev(Bm), dev(Cm), S, dev(idx))
+    torch.cuda.synchronize()
+    ry, rpool = oracle.step(x.reshape(R, L_new, H, P), dt, A, Bm.reshape(R, L_new, G, N),
+                            Cm.reshape(R, L_new, G, N), pool, idx, out_dtype=ODT[dtype],
+                            state_dtype="f32")
+    assert_close(y, ry, "step y")
+    assert np.all(ry[1] == 0) and np.all(ry[4] == 0)
+    assert_close(S, rpool, "state pool")
+    untouched = [s for s in range(n_slots) if s not in set(idx.tolist())]
+    assert_bitexact(S[untouched], pool[untouched], "untouched slots")
+
+
+def test_step_token_by_token_equals_scan():
+    """Decode == prefill: n_new = 1 steps reproduce ssm_scan_fwd."""
+    import ssm_sequence_models_amd as ssm
+    B, L, H, P, N, G = 2, 70, 4, 64, 128, 1
+    x, dt, A, Bm, Cm, init, _ = _scan_inputs(B, L, H, P, N, G, BF16, seed=31)
+    y, fin = ssm.scan_fwd(dev(x), dev(dt), dev(A), dev(Bm), dev(Cm), dev(init))
+    pool = dev(init).clone()
+    X, D, BB, CC = dev(x), dev(dt), dev(Bm), dev(Cm)
+    ys = []
+    for t in range(L):
+        ys.append(ssm.step(X[:, t:t + 1].reshape(B, 1, H * P), D[:, t:t + 1].contiguous(), dev(A),
+                           BB[:, t:t + 1].reshape(B, 1, G * N), CC[:, t:t + 1].reshape(B, 1, G * N),
+                           pool))
+    ystep = torch.cat(ys, 1)
+    ry, rfin = oracle.scan_fwd(x, dt, A, Bm, Cm, init, out_dtype="bf16", state_dtype="f32")
+    assert_close(ystep, ry, "token-by-token y vs oracle")
+    assert_close(pool, rfin, "token-by-token state vs oracle")
+    assert_close(ystep, y.float().cpu().double().numpy(), "token-by-token vs chunked scan")
+
+
+def test_decode_step_chain_matches_oracle():
+    """conv1d_update then step reading the conv output's x | B | C ranges in place."""
+    import ssm_sequence_models_amd as ssm
+    H, P, N, G, K, L_new = 4, 64, 128, 1, 4, 4
+    C = H * P + 2 * G * N
+    R, n_slots = 5, 8
+    g = torch.Generator().manual_seed(41)
+    x_new = torch.randn(R, C, L_new, generator=g).to(BF16)
+    cpool = torch.randn(n_slots, C, 4, generator=g).to(BF16)
+    spool = torch.randn(n_slots, H, P, N, generator=g)
+    w = torch.rand(C, K, generator=g) - 0.5
+    b = torch.rand(C, generator=g) - 0.5
+    dt = torch.nn.functional.softplus(torch.randn(R, L_new, H, generator=g) - 2.0)
+    A = -torch.exp(torch.rand(H, generator=g) * float(np.log(16.0)))
+    idx = torch.tensor([6, 0, 3, 7, 1], dtype=torch.int32)
+    seqlens = torch.tensor([0, 2, 3, 99999, 17], dtype=torch.int32)
+    CP, SP = dev(cpool), dev(spool)
+    y = ssm.decode_step(dev(x_new), CP, dev(w), dev(b), dev(dt), dev(A), SP, H, P, G, N,
+                        conv_state_indices=dev(idx), cache_seqlens=dev(seqlens))
+    torch.cuda.synchronize()
+    co, rcp = oracle.conv1d_update(x_new, cpool, w, b, idx, seqlens, act="silu", out_dtype="bf16")
+    xs = co[:, :H * P].transpose(0, 2, 1).reshape(R, L_new, H, P)
+    Bs = co[:, H * P:H * P + N].transpose(0, 2, 1).reshape(R, L_new, 1, N)
+    Cs = co[:, H * P + N:].transpose(0, 2, 1).reshape(R, L_new, 1, N)
+    ry, rsp = oracle.step(xs, dt, A, Bs, Cs, spool, idx, out_dtype="bf16", state_dtype="f32")
+    assert_close(y, ry, "decode y")
+    assert_bitexact(CP, torch.from_numpy(rcp).to(BF16), "conv pool")
+    assert_close(SP, rsp, "ssm pool")
