@@ -37,9 +37,10 @@ struct BF16 {
     __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
-// phi: identity or SiLU(z) = z / (1 + exp(-z)); exp(-z) = inf gives -0 for very negative z
+// phi: identity or SiLU(z) = z / (1 + exp(-z)) with the hardware exp and reciprocal (about 2
+// ulp); exp(-z) = inf gives -0 for very negative z
 __device__ __forceinline__ float apply_act(float z, int act) {
-    if (act == SSM_ACT_SILU) return z * __frcp_rn(1.0f + __expf(-z));
+    if (act == SSM_ACT_SILU) return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
     return z;
 }
 
@@ -65,7 +66,7 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 __device__ __forceinline__ uint16_t act_to_bf16(double z, int act) {
     if (act != SSM_ACT_SILU) return f64_to_bf16(z);
     const float zf = static_cast<float>(z);
-    const float s = zf * __frcp_rn(1.0f + __expf(-zf));
+    const float s = zf * __builtin_amdgcn_rcpf(1.0f + __expf(-zf));
     const int dist = abs(static_cast<int>(__float_as_uint(s) & 0xFFFFu) - 0x8000);
     if (static_cast<float>(dist) > 8.0f + 4.0f * fabsf(zf)) return f32_to_bf16(s);
     return f64_to_bf16(z / (1.0 + exp(-z)));

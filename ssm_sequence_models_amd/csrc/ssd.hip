@@ -15,54 +15,42 @@
 // last reset (the state restarts from zero there).
 //
 // Work split:
-//  * ssd_prep_kernel, one block per (batch row, chunk, group): runs the conv (+phi, bf16
-//    rounding) over the chunk's B and C channels once for all heads of the group and writes
-//    C (token-major), B (channel-major) and G = C B^T (fp32, MFMA) to the workspace.  Doing
-//    this per head would repeat the B/C conv nheads times.
-//  * ssd_main_kernel, one block per (batch row, head), 4 wavefronts, each owning 16 of the
-//    64 head channels: it streams the head's x channels through the register-window conv,
-//    keeps its [16 x 128] slice of the fp32 state in MFMA accumulators for the whole
-//    sequence, and per chunk issues the three contractions on v_mfma_f32_16x16x32_bf16:
-//        Y^T   += h^T-slice x C^T           (initial-state part)
-//        Y^T   += X^T x M^T                 (intra-chunk part, M = G o decay mask)
-//        h^T   += B^T x (W o X)             (state update)
-//    The fp32 operands (h, M, W o X) enter as a hi + lo pair of bf16 (v = hi + lo with
-//    |v - hi - lo| <= 2^-17 |v|); the other operand (x, B, C) is exact in bf16, so each
-//    contraction is accurate to about fp32 while running at the bf16 MFMA rate.
-//  * the next chunk's x / B / C / G tiles are fetched into registers while the current
-//    chunk computes and dropped into the other half of a double-buffered LDS stage.
+//  * ssd_prep_kernel, one block per (batch row, chunk, group): the conv (+phi, rounded to
+//    bf16 as the exact value rounds) over the chunk's B and C channels, once for all heads of
+//    the group; writes C (token-major), B (channel-major) and G = C B^T (fp32, MFMA) to the
+//    workspace.  Doing this per head would repeat the B/C conv nheads times.
+//  * ssd_main_kernel, one block per (batch row, head) with 8 wavefronts, two per SIMD:
+//      - 4 consumer waves each own 16 of the 64 head channels and keep their [16 x 128] slice
+//        of the fp32 state in MFMA accumulators for the whole sequence.  Per chunk they issue
+//        the contractions on v_mfma_f32_16x16x32_bf16:
+//            Y^T += h-slice x C^T      (initial-state part)
+//            Y^T += X^T x M^T          (intra-chunk part, M = G o decay mask)
+//            h^T += B^T x (W o X)      (state update)
+//        The fp32 operands (h, M, W o X) enter as a hi + lo pair of bf16 (v = hi + lo with
+//        |v - hi - lo| <= 2^-17 |v|); the other operand (x, B, C) is exact in bf16, so each
+//        contraction is accurate to about fp32 at the bf16 MFMA rate.
+//      - 4 producer waves run one chunk ahead: fetch the next chunk's x rows and C / B^T / G
+//        tiles from HBM / L2, run the register-window conv + SiLU of the head's x channels,
+//        the in-chunk cumulative log-decay (a DPP prefix scan per wavefront) and the M tiles,
+//        and leave everything in the other half of a double-buffered LDS stage.
+//    One block barrier per chunk hands the stage over.  Sharing each SIMD between a producer
+//    and a consumer wave lets the conv's VALU work run under the consumer's MFMA work.
 #include "internal.h"
 
 namespace ssm {
 namespace {
 
 constexpr int kQ = 64;       // tokens per chunk
-constexpr int kP = 64;       // head channels (4 waves x 16)
+constexpr int kP = 64;       // head channels (4 consumer waves x 16)
 constexpr int kN = 128;      // state size
 constexpr int kKmax = 8;     // widest conv handled
-constexpr int kThreads = 256;
-constexpr int kRowsMax = kQ + kKmax - 1;  // staged x rows incl. the conv halo
-
-// LDS strides (bytes); +16 breaks power-of-two row strides
-constexpr int kXStride = kP * 2 + 16;    // x rows [token][channel] bf16
-constexpr int kCStride = kN * 2 + 16;    // C rows [token][n] bf16
-constexpr int kBtStride = kQ * 2 + 16;   // B^T rows [n][token] bf16
-constexpr int kMStride = kQ * 2 + 16;    // M rows [i][j] bf16
-
-constexpr int kXBytes = ((kRowsMax * kXStride + 255) / 256) * 256;
-constexpr int kCBytes = kQ * kCStride;
-constexpr int kBtBytes = kN * kBtStride;
-constexpr int kSeqBytes = ((kRowsMax * 4 + 15) / 16) * 16;
-constexpr int kStageBytes = kXBytes + kCBytes + kBtBytes + kSeqBytes;
-constexpr int kMBytes = kQ * kMStride;
-constexpr int kScalarBytes = 5 * kQ * 4 + 16;
-constexpr int kMainLds = 2 * kStageBytes + 2 * kMBytes + kScalarBytes;
-static_assert(kMainLds <= 160 * 1024, "LDS budget");
+constexpr int kPrepThreads = 256;
+constexpr int kMainThreads = 512;
 
 // workspace per (row, chunk, group)
-constexpr int64_t kWsC = static_cast<int64_t>(kQ) * kN;    // bf16 elements
-constexpr int64_t kWsBt = static_cast<int64_t>(kN) * kQ;   // bf16 elements
-constexpr int64_t kWsG = static_cast<int64_t>(kQ) * kQ;    // fp32 elements
+constexpr int64_t kWsC = static_cast<int64_t>(kQ) * kN;    // bf16 elements, [token][n]
+constexpr int64_t kWsBt = static_cast<int64_t>(kN) * kQ;   // bf16 elements, [n][token]
+constexpr int64_t kWsG = static_cast<int64_t>(kQ) * kQ;    // fp32 elements, [i][j]
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -72,8 +60,13 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 lds_bf16x8(const uint8_t* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
+template <class T>
+__device__ __forceinline__ T lds_ld(const uint8_t* base, int off) {
+    return *reinterpret_cast<const T*>(base + off);
+}
+template <class T>
+__device__ __forceinline__ void lds_st(uint8_t* base, int off, const T& v) {
+    *reinterpret_cast<T*>(base + off) = v;
 }
 
 // v = hi + lo, hi = rne(v), lo = rne(v - hi)
@@ -86,70 +79,50 @@ __device__ __forceinline__ void split_hilo(const float (&v)[8], bf16x8& hi, bf16
     }
 }
 
-__device__ __forceinline__ float warp_incl_sum(float v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
+// Inclusive prefix over the 64 lanes of a wavefront with DPP: row_shr 1/2/4/8 inside each
+// row of 16 lanes, then row_bcast 15 / 31 carry the row totals forward.
+__device__ __forceinline__ float wave_incl_sum(float v) {
+    const int z = __float_as_int(0.0f);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x143, 0xc, 0xf, false));
     return v;
 }
-__device__ __forceinline__ int warp_incl_max(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(v, off);
-        if (lane >= off) v = max(v, o);
-    }
+__device__ __forceinline__ int wave_incl_max(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x111, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x112, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x114, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x118, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x142, 0xa, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x143, 0xc, 0xf, false));
     return v;
 }
 
-__device__ __forceinline__ int64_t ws_base(const ChunkedArgs& a, int64_t b, int64_t c,
+__device__ __forceinline__ int64_t ws_unit(const ChunkedArgs& a, int64_t b, int64_t c,
                                            int64_t g, int64_t nC) {
     return (b * nC + c) * a.G + g;
-}
-
-// conv of one channel over 8 consecutive outputs, rounded to bf16 as the exact value rounds
-// (double sums: the products of fp32 weights and bf16 inputs are exact); u[0 .. 8+K-2] are
-// the inputs of the window starting K-1 before the first output, ids likewise (a tap counts
-// only if its id equals the output token's)
-template <bool HAS_SEQ>
-__device__ __forceinline__ void conv8(const double (&u)[kKmax + 7], const int32_t (&id)[kKmax + 7],
-                                      const double (&w)[kKmax], double bias, int K, int act,
-                                      uint16_t (&out)[8]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        double z = bias;
-        int32_t idc = 0;
-        if (HAS_SEQ) {
-#pragma unroll
-            for (int k = 0; k < kKmax; ++k)
-                if (k == K - 1) idc = id[e + k];
-        }
-#pragma unroll
-        for (int k = 0; k < kKmax; ++k) {
-            if (k < K) {
-                const double tap = (!HAS_SEQ || id[e + k] == idc) ? u[e + k] : 0.0;
-                z = fma(w[k], tap, z);
-            }
-        }
-        out[e] = act_to_bf16(z, act);
-    }
 }
 
 // =======================================================================================
 // prep: conv + bf16 rounding of the B / C channels of one (row, chunk, group), then
 // C token-major, B channel-major and G = C B^T into the workspace
 // =======================================================================================
-__global__ void __launch_bounds__(kThreads)
+constexpr int kPrepStride = kN * 2 + 16;  // [token][n] bf16 rows in LDS
+
+template <int K>
+__global__ void __launch_bounds__(kPrepThreads)
 ssd_prep_kernel(ChunkedArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t sm[2 * kQ * kCStride + kSeqBytes];
-    uint8_t* sB = sm;                 // [token][n] bf16
-    uint8_t* sC = sm + kQ * kCStride; // [token][n] bf16
-    int32_t* sSeq = reinterpret_cast<int32_t*>(sm + 2 * kQ * kCStride);
+    __shared__ __attribute__((aligned(16))) uint8_t sm[2 * kQ * kPrepStride + 128 * 4];
+    uint8_t* sB = sm;
+    uint8_t* sC = sm + kQ * kPrepStride;
+    int32_t* sSeq = reinterpret_cast<int32_t*>(sm + 2 * kQ * kPrepStride);
 
     const int tid = threadIdx.x;
     const int64_t cn = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int64_t L = a.L, K = a.K;
+    const int64_t L = a.L;
     const int64_t nC = (L + kQ - 1) / kQ;
     const int64_t t0 = cn * kQ;
     const bool has_seq = a.seq_idx != nullptr;
@@ -161,470 +134,521 @@ ssd_prep_kernel(ChunkedArgs a) {
     }
     __syncthreads();
 
-    for (int ch = tid; ch < 2 * kN; ch += kThreads) {
+    for (int ch = tid; ch < 2 * kN; ch += kPrepThreads) {
         const bool isC = ch >= kN;
         const int n = isC ? ch - kN : ch;
-        const uint16_t* src = isC ? a.csrc : a.bsrc;
         const int64_t row = isC ? a.c_row : a.b_row;
         const int64_t col = (isC ? a.c_col0 : a.b_col0) + g * kN + n;
+        const uint16_t* src = (isC ? a.csrc : a.bsrc) + b * L * row + col;
         uint8_t* dst = isC ? sC : sB;
         if (a.fused_conv) {
-            double w[kKmax];
+            double w[K];
 #pragma unroll
-            for (int k = 0; k < kKmax; ++k) w[k] = k < K ? a.conv_w[col * K + k] : 0.0f;
+            for (int k = 0; k < K; ++k) w[k] = a.conv_w[col * K + k];
             const double bias = a.conv_b ? a.conv_b[col] : 0.0f;
-            // sliding window: win[kKmax-1-(K-1) ..] oldest -> newest; idw likewise
-            double win[kKmax];
-            int32_t idw[kKmax];
+            double win[K];      // oldest -> newest; win[K-1] is the current token
+            int32_t idw[K];
 #pragma unroll
-            for (int k = 0; k < kKmax; ++k) { win[k] = 0.0; idw[k] = 0; }
-#pragma unroll
-            for (int k = 0; k < kKmax - 1; ++k) {
-                const int64_t tau = k - (kKmax - 1 - (K - 1));  // 0 .. K-2 for live slots
-                if (tau >= 0) {
-                    const int64_t t = t0 - (K - 1) + tau;
-                    float v = 0.0f;
-                    if (t >= 0)
-                        v = bf16_to_f32(src[(b * L + t) * row + col]);
-                    else if (a.conv_init)
-                        v = bf16_to_f32(a.conv_init[(b * a.C_conv + col) * (K - 1) + (K - 1) + t]);
-                    win[k] = v;
-                    idw[k] = has_seq ? sSeq[tau] : 0;
-                }
+            for (int k = 0; k < K - 1; ++k) {
+                const int64_t t = t0 - (K - 1) + k;
+                float v = 0.0f;
+                if (t >= 0)
+                    v = bf16_to_f32(src[t * row]);
+                else if (a.conv_init)
+                    v = bf16_to_f32(a.conv_init[(b * a.C_conv + col) * (K - 1) + (K - 1) + t]);
+                win[k] = v;
+                idw[k] = has_seq ? sSeq[k] : 0;
             }
             for (int j = 0; j < kQ; ++j) {
                 const int64_t t = t0 + j;
-                const double xv = t < L ? bf16_to_f32(src[(b * L + t) * row + col]) : 0.0f;
-                const int32_t idt = has_seq ? sSeq[j + K - 1] : 0;
-                win[kKmax - 1] = xv;
-                idw[kKmax - 1] = idt;
+                win[K - 1] = t < L ? bf16_to_f32(src[t * row]) : 0.0f;
+                idw[K - 1] = has_seq ? sSeq[j + K - 1] : 0;
                 double z = bias;
 #pragma unroll
-                for (int k = 0; k < kKmax; ++k) {
-                    const int kk = k - (kKmax - K);  // tap index 0 .. K-1 for live slots
-                    if (kk >= 0) {
-                        const double tap = (!has_seq || idw[k] == idt) ? win[k] : 0.0;
-                        z = fma(w[kk], tap, z);
-                    }
+                for (int k = 0; k < K; ++k) {
+                    const double tap = (!has_seq || idw[k] == idw[K - 1]) ? win[k] : 0.0;
+                    z = fma(w[k], tap, z);
                 }
                 const uint16_t v = t < L ? act_to_bf16(z, a.act) : uint16_t(0);
-                *reinterpret_cast<uint16_t*>(dst + j * kCStride + n * 2) = v;
+                *reinterpret_cast<uint16_t*>(dst + j * kPrepStride + n * 2) = v;
 #pragma unroll
-                for (int k = 0; k < kKmax - 1; ++k) { win[k] = win[k + 1]; idw[k] = idw[k + 1]; }
+                for (int k = 0; k < K - 1; ++k) { win[k] = win[k + 1]; idw[k] = idw[k + 1]; }
             }
         } else {
             for (int j = 0; j < kQ; ++j) {
                 const int64_t t = t0 + j;
-                const uint16_t v = t < L ? src[(b * L + t) * row + col] : uint16_t(0);
-                *reinterpret_cast<uint16_t*>(dst + j * kCStride + n * 2) = v;
+                const uint16_t v = t < L ? src[t * row] : uint16_t(0);
+                *reinterpret_cast<uint16_t*>(dst + j * kPrepStride + n * 2) = v;
             }
         }
     }
     __syncthreads();
 
-    const int64_t base = ws_base(a, b, cn, g, nC);
+    const int64_t unit = ws_unit(a, b, cn, g, nC);
     uint16_t* wsC = static_cast<uint16_t*>(a.workspace);
     uint16_t* wsBt = wsC + a.B * nC * a.G * kWsC;
     float* wsG = reinterpret_cast<float*>(wsBt + a.B * nC * a.G * kWsBt);
-    // C token-major: 16-byte pieces
-    for (int idx = tid; idx < kQ * kN / 8; idx += kThreads) {
+    for (int idx = tid; idx < kQ * kN / 8; idx += kPrepThreads) {
         const int i = idx >> 4, q = idx & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sC + i * kCStride + q * 16);
-        *reinterpret_cast<u32x4*>(wsC + base * kWsC + i * kN + q * 8) = v;
+        *reinterpret_cast<u32x4*>(wsC + unit * kWsC + i * kN + q * 8) =
+            lds_ld<u32x4>(sC, i * kPrepStride + q * 16);
     }
-    // B channel-major: gather 8 tokens of one channel
-    for (int idx = tid; idx < kN * kQ / 8; idx += kThreads) {
+    for (int idx = tid; idx < kN * kQ / 8; idx += kPrepThreads) {
         const int n = idx >> 3, jq = idx & 7;
         uint32_t w4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = *reinterpret_cast<const uint16_t*>(sB + (8 * jq + 2 * e) * kCStride + n * 2);
-            const uint32_t hi = *reinterpret_cast<const uint16_t*>(sB + (8 * jq + 2 * e + 1) * kCStride + n * 2);
+            const uint32_t lo = lds_ld<uint16_t>(sB, (8 * jq + 2 * e) * kPrepStride + n * 2);
+            const uint32_t hi = lds_ld<uint16_t>(sB, (8 * jq + 2 * e + 1) * kPrepStride + n * 2);
             w4[e] = lo | (hi << 16);
         }
-        u32x4 v = {w4[0], w4[1], w4[2], w4[3]};
-        *reinterpret_cast<u32x4*>(wsBt + base * kWsBt + n * kQ + jq * 8) = v;
+        *reinterpret_cast<u32x4*>(wsBt + unit * kWsBt + n * kQ + jq * 8) =
+            u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
-    // G = C B^T for the tiles on or below the diagonal; wave w owns rows 16w .. 16w+15
+    // G = C B^T for the 16x16 tiles on or below the diagonal; wave w owns rows 16w..16w+15
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
     for (int jt = 0; jt <= wave; ++jt) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int m = 0; m < kN / 32; ++m) {
-            const bf16x8 av = lds_bf16x8(sC + (16 * wave + li) * kCStride + (32 * m + 8 * g4) * 2);
-            const bf16x8 bv = lds_bf16x8(sB + (16 * jt + li) * kCStride + (32 * m + 8 * g4) * 2);
+            const bf16x8 av = lds_ld<bf16x8>(sC, (16 * wave + li) * kPrepStride + (32 * m + 8 * g4) * 2);
+            const bf16x8 bv = lds_ld<bf16x8>(sB, (16 * jt + li) * kPrepStride + (32 * m + 8 * g4) * 2);
             acc = mfma(av, bv, acc);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            wsG[base * kWsG + (16 * wave + 4 * g4 + r) * kQ + 16 * jt + li] = acc[r];
+            wsG[unit * kWsG + (16 * wave + 4 * g4 + r) * kQ + 16 * jt + li] = acc[r];
     }
 }
 
 // =======================================================================================
 // main kernel
 // =======================================================================================
-struct Stage {
-    u32x4 x[3];
+// One LDS stage (double-buffered): all tiles are rows of 16-byte pieces stored under an XOR
+// swizzle chosen so that each 16-lane group of a consumer's ds_read_b128 covers the 64
+// banks once.
+constexpr int kStC = 0;                          // C   [64 tok][16 pieces], piece ^ (tok & 15)
+constexpr int kStBt = kStC + kQ * 256;           // B^T [128 n][8 pieces], piece ^ bt_swz(n)
+constexpr int kStX = kStBt + kN * 128;           // X^T [64 p][8 pieces], piece ^ ((p >> 1) & 7)
+constexpr int kStMhi = kStX + kP * 128;          // M   [64 i][8 pieces], piece ^ ((i >> 1) & 7)
+constexpr int kStMlo = kStMhi + kQ * 128;
+constexpr int kStE = kStMlo + kQ * 128;          // E_i = exp(cum_i) on the leading segment
+constexpr int kStW = kStE + kQ * 4;              // W_j = exp(cum_last - cum_j) dt_j
+constexpr int kStDecay = kStW + kQ * 4;          // exp(cum_last) (0 after a reset)
+constexpr int kStageBytes = kStDecay + 16;
+// producer-private areas (one per producer wave)
+constexpr int kPxRows = 16 + kKmax - 1;          // x rows for 16 outputs + conv halo
+constexpr int kPxBytes = kPxRows * 128;
+constexpr int kPsBytes = 3 * kQ * 4 + 32 * 4;    // cum, dtv, r, conv ids
+constexpr int kPrivX = 2 * kStageBytes;
+constexpr int kPrivS = kPrivX + 4 * kPxBytes;
+constexpr int kMainLds = kPrivS + 4 * kPsBytes;
+static_assert(kMainLds <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ int sw_c(int tok, int q) { return tok * 256 + ((q ^ (tok & 15)) << 4); }
+__device__ __forceinline__ int sw_bt(int n, int q) {
+    return n * 128 + ((q ^ (((n >> 3) & 3) | (((n >> 1) & 1) << 2))) << 4);
+}
+__device__ __forceinline__ int sw_8(int row, int q) { return row * 128 + ((q ^ ((row >> 1) & 7)) << 4); }
+
+// M tiles computed by each producer wave: (row block I of 16, column half s of 32); the six
+// tiles cover j <= i
+__device__ __forceinline__ int unit_I(int pw, int u) {
+    constexpr int8_t t[4][2] = {{0, 3}, {1, 2}, {2, -1}, {3, -1}};
+    return t[pw][u];
+}
+__device__ __forceinline__ int unit_S(int pw, int u) {
+    constexpr int8_t t[4][2] = {{0, 0}, {0, 1}, {0, -1}, {1, -1}};
+    return t[pw][u];
+}
+
+// Registers a producer lane carries from the fetch of chunk c+1 to its use
+struct Fetch {
     u32x4 c[4];
     u32x4 bt[4];
-    f32x4 gm[4];
-    int32_t seq;
+    u32x4 x[3];
+    f32x4 gm[2][2];
     float dt;
+    int32_t seq_j, seq_jm1, seq_row;
 };
 
-__device__ __forceinline__ void stage_load(const ChunkedArgs& a, int64_t b, int64_t h,
-                                           int64_t g, int64_t cn, int64_t nC, int tid,
-                                           Stage& s) {
-    const int64_t L = a.L, K = a.K;
-    const int rows = static_cast<int>(kQ + K - 1);
+template <int K, bool FUSED, bool HAS_SEQ>
+__device__ __forceinline__ void fetch(const ChunkedArgs& a, const uint16_t* xrow_base,
+                                      int64_t b, int64_t h, int64_t g, int64_t cn, int64_t nC,
+                                      int pw, int lane, Fetch& f) {
+    const int64_t L = a.L;
     const int64_t t0 = cn * kQ;
-    // x rows (raw, pre-conv), 8 channels per piece
+    const int64_t unit = ws_unit(a, b, cn, g, nC);
+    const uint16_t* ws = static_cast<const uint16_t*>(a.workspace);
+    const uint16_t* wsC = ws + unit * kWsC;
+    const uint16_t* wsBt = ws + a.B * nC * a.G * kWsC + unit * kWsBt;
+    const float* wsG = reinterpret_cast<const float*>(ws + a.B * nC * a.G * (kWsC + kWsBt)) +
+                       unit * kWsG;
+    const int ptid = pw * 64 + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = ptid + 256 * k;
+        f.c[k] = *reinterpret_cast<const u32x4*>(wsC + idx * 8);
+        f.bt[k] = *reinterpret_cast<const u32x4*>(wsBt + idx * 8);
+    }
+    // x rows t0 + 16 pw - (K-1) + rho, rho < 16 + K - 1, 8 channels per piece
+    constexpr int kRows = 16 + K - 1;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        const int idx = tid + k * kThreads;
+        const int idx = lane + 64 * k;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (idx < rows * 8) {
+        if (idx < kRows * 8) {
             const int rho = idx >> 3, q = idx & 7;
-            const int64_t t = t0 - (K - 1) + rho;
-            const int64_t col = a.x_col0 + h * kP + q * 8;
+            const int64_t t = t0 + 16 * pw - (K - 1) + rho;
             if (t >= 0 && t < L) {
-                v = *reinterpret_cast<const u32x4*>(a.x + (b * L + t) * a.x_row + col);
-            } else if (t < 0 && a.fused_conv && a.conv_init) {
+                v = *reinterpret_cast<const u32x4*>(xrow_base + t * a.x_row + q * 8);
+            } else if (FUSED && t < 0 && a.conv_init) {
+                const int64_t cc0 = a.x_col0 + h * kP + q * 8;
                 uint32_t w4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = a.conv_init[(b * a.C_conv + col + 2 * e) * (K - 1) + (K - 1) + t];
-                    const uint32_t hi = a.conv_init[(b * a.C_conv + col + 2 * e + 1) * (K - 1) + (K - 1) + t];
+                    const uint32_t lo = a.conv_init[(b * a.C_conv + cc0 + 2 * e) * (K - 1) + (K - 1) + t];
+                    const uint32_t hi = a.conv_init[(b * a.C_conv + cc0 + 2 * e + 1) * (K - 1) + (K - 1) + t];
                     w4[e] = lo | (hi << 16);
                 }
                 v = u32x4{w4[0], w4[1], w4[2], w4[3]};
             }
         }
-        s.x[k] = v;
+        f.x[k] = v;
     }
-    const int64_t base = ws_base(a, b, cn, g, nC);
-    const uint16_t* wsC = static_cast<const uint16_t*>(a.workspace);
-    const uint16_t* wsBt = wsC + a.B * nC * a.G * kWsC;
-    const float* wsG = reinterpret_cast<const float*>(wsBt + a.B * nC * a.G * kWsBt);
+    // G pieces of this wave's M tiles: row i, columns 8q .. 8q+7
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int idx = tid + k * kThreads;
-        s.c[k] = *reinterpret_cast<const u32x4*>(wsC + base * kWsC + idx * 8);
-        s.bt[k] = *reinterpret_cast<const u32x4*>(wsBt + base * kWsBt + idx * 8);
-    }
-    {
-        const int i = tid >> 2, jb = (tid & 3) * 16;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (jb <= i) v = *reinterpret_cast<const f32x4*>(wsG + base * kWsG + i * kQ + jb + 4 * k);
-            s.gm[k] = v;
+    for (int u = 0; u < 2; ++u) {
+        const int I = unit_I(pw, u), s = unit_S(pw, u);
+        f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
+        if (I >= 0) {
+            const int i = 16 * I + (lane >> 2), q = 4 * s + (lane & 3);
+            if (8 * q <= i) {
+                v0 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q);
+                v1 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q + 4);
+            }
         }
+        f.gm[u][0] = v0;
+        f.gm[u][1] = v1;
     }
-    s.seq = 0;
-    if (a.seq_idx && tid < rows) {
-        int64_t t = t0 - (K - 1) + tid;
-        t = t < 0 ? 0 : (t >= L ? L - 1 : t);
-        s.seq = a.seq_idx[b * L + t];
+    const int64_t t = t0 + lane;
+    f.dt = t < L ? a.dt[(b * L + t) * a.H + h] : 0.0f;
+    f.seq_j = f.seq_jm1 = f.seq_row = 0;
+    if (HAS_SEQ) {
+        const int64_t tc = t < L ? t : L - 1;
+        f.seq_j = a.seq_idx[b * L + tc];
+        f.seq_jm1 = a.seq_idx[b * L + (tc > 0 ? tc - 1 : 0)];
+        int64_t tr = t0 + 16 * pw - (K - 1) + lane;
+        tr = tr < 0 ? 0 : (tr >= L ? L - 1 : tr);
+        f.seq_row = a.seq_idx[b * L + tr];
     }
-    s.dt = 0.0f;
-    if (tid < kQ && t0 + tid < L) s.dt = a.dt[(b * L + t0 + tid) * a.H + h];
 }
 
-__device__ __forceinline__ void stage_store(uint8_t* stage, const Stage& s, int tid, int rows) {
-    uint8_t* sX = stage;
-    uint8_t* sC = stage + kXBytes;
-    uint8_t* sBt = sC + kCBytes;
-    int32_t* sSeq = reinterpret_cast<int32_t*>(sBt + kBtBytes);
+// Producer work for chunk cn: drop the fetched tiles into `stage`, fetch chunk cn+1, then
+// compute the chunk scalars, the conv of the head's x channels and this wave's M tiles.
+template <int K, bool FUSED, bool HAS_SEQ>
+__device__ __forceinline__ void produce(const ChunkedArgs& a, const uint16_t* xrow_base,
+                                        int64_t b, int64_t h, int64_t g, int64_t cn,
+                                        int64_t nC, float Ah, const double (&cw)[K],
+                                        double cbias, int pw, int lane, uint8_t* stage,
+                                        uint8_t* px, uint8_t* ps, Fetch& f) {
+    constexpr int kRows = 16 + K - 1;
+    const int ptid = pw * 64 + lane;
+    // 1. fetched tiles -> LDS
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = ptid + 256 * k;
+        lds_st(stage, kStC + sw_c(idx >> 4, idx & 15), f.c[k]);
+        lds_st(stage, kStBt + sw_bt(idx >> 3, idx & 7), f.bt[k]);
+    }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        const int idx = tid + k * kThreads;
-        if (idx < rows * 8) {
-            const int rho = idx >> 3, q = idx & 7;
-            *reinterpret_cast<u32x4*>(sX + rho * kXStride + q * 16) = s.x[k];
-        }
+        const int idx = lane + 64 * k;
+        if (idx < kRows * 8) lds_st(px, idx * 16, f.x[k]);
     }
+    float* pcum = reinterpret_cast<float*>(ps);
+    float* pdtv = pcum + kQ;
+    int32_t* pr = reinterpret_cast<int32_t*>(pdtv + kQ);
+    int32_t* pid = pr + kQ;
+    if (HAS_SEQ && lane < kRows) pid[lane] = f.seq_row;
+    const float dtv = f.dt;
+    const int32_t seq_j = f.seq_j, seq_jm1 = f.seq_jm1;
+    const f32x4 gm[2][2] = {{f.gm[0][0], f.gm[0][1]}, {f.gm[1][0], f.gm[1][1]}};
+
+    // 2. fetch the next chunk while this one is computed
+    if (cn + 1 < nC) fetch<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, cn + 1, nC, pw, lane, f);
+
+    // 3. chunk scalars, lane = token
+    const int64_t t0 = cn * kQ;
+    const int j = lane;
+    const float cum = wave_incl_sum(dtv * Ah);
+    int rst = -1;
+    if (HAS_SEQ && t0 + j < a.L && t0 + j > 0 && seq_j != seq_jm1) rst = j;
+    const int r = HAS_SEQ ? wave_incl_max(rst) : -1;
+    pcum[j] = cum;
+    pdtv[j] = dtv;
+    pr[j] = r;
+    if (pw == 0) {
+        const float cum_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kQ - 1));
+        const int r_last = __builtin_amdgcn_readlane(r, kQ - 1);
+        float* sE = reinterpret_cast<float*>(stage + kStE);
+        float* sW = reinterpret_cast<float*>(stage + kStW);
+        sE[j] = r < 0 ? __expf(cum) : 0.0f;
+        sW[j] = j >= r_last ? __expf(cum_last - cum) * dtv : 0.0f;
+        if (j == 0) *reinterpret_cast<float*>(stage + kStDecay) = r_last < 0 ? __expf(cum_last) : 0.0f;
+    }
+
+    // 4. conv of channel p = lane over tokens 16 pw .. 16 pw + 15 -> X^T row p
+    {
+        const int p = lane;
+        uint32_t packed[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int idx = tid + k * kThreads;
-        const int i = idx >> 4, q = idx & 15;
-        *reinterpret_cast<u32x4*>(sC + i * kCStride + q * 16) = s.c[k];
-        const int n = idx >> 3, jq = idx & 7;
-        *reinterpret_cast<u32x4*>(sBt + n * kBtStride + jq * 16) = s.bt[k];
+        for (int half = 0; half < 2; ++half) {
+            uint16_t o[8];
+            if (FUSED) {
+                double u[8 + K - 1];
+                int32_t id[8 + K - 1];
+#pragma unroll
+                for (int tau = 0; tau < 8 + K - 1; ++tau) {
+                    u[tau] = bf16_to_f32(lds_ld<uint16_t>(px, (8 * half + tau) * 128 + 2 * p));
+                    id[tau] = HAS_SEQ ? pid[8 * half + tau] : 0;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    double z = cbias;
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        const double tap = (!HAS_SEQ || id[e + k] == id[e + K - 1]) ? u[e + k] : 0.0;
+                        z = fma(cw[k], tap, z);
+                    }
+                    o[e] = act_to_bf16(z, a.act);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = lds_ld<uint16_t>(px, (8 * half + e + K - 1) * 128 + 2 * p);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                packed[4 * half + e] = static_cast<uint32_t>(o[2 * e]) | (static_cast<uint32_t>(o[2 * e + 1]) << 16);
+        }
+        lds_st(stage, kStX + sw_8(p, 2 * pw), u32x4{packed[0], packed[1], packed[2], packed[3]});
+        lds_st(stage, kStX + sw_8(p, 2 * pw + 1), u32x4{packed[4], packed[5], packed[6], packed[7]});
     }
-    if (tid < rows) sSeq[tid] = s.seq;
+
+    // 5. this wave's M tiles: M[i][j] = G[i][j] exp(cum_i - cum_j) dt_j on r_i <= j <= i
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int I = unit_I(pw, u), s = unit_S(pw, u);
+        if (I < 0) continue;
+        const int i = 16 * I + (lane >> 2), q = 4 * s + (lane & 3), j0 = 8 * q;
+        float mv[8];
+        if (j0 <= i) {
+            const float ci = pcum[i];
+            const int ri = pr[i];
+            const f32x4 cj0 = lds_ld<f32x4>(ps, j0 * 4), cj1 = lds_ld<f32x4>(ps, j0 * 4 + 16);
+            const f32x4 dj0 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4), dj1 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4 + 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float cj = e < 4 ? cj0[e] : cj1[e - 4];
+                const float dj = e < 4 ? dj0[e] : dj1[e - 4];
+                const float gv = gm[u][e >> 2][e & 3];
+                const int jj = j0 + e;
+                const float m = gv * __expf(ci - cj) * dj;
+                mv[e] = (jj <= i && jj >= ri) ? m : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mv[e] = 0.0f;
+        }
+        bf16x8 hi, lo;
+        split_hilo(mv, hi, lo);
+        lds_st(stage, kStMhi + sw_8(i, q), hi);
+        lds_st(stage, kStMlo + sw_8(i, q), lo);
+    }
 }
 
-template <bool FUSED, bool HAS_SEQ>
-__global__ void __launch_bounds__(kThreads, 1)
+template <int K, bool FUSED, bool HAS_SEQ>
+__global__ void __launch_bounds__(kMainThreads, 1)
 ssd_main_kernel(ChunkedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t sm[kMainLds];
-    uint8_t* stages = sm;
-    uint8_t* sMhi = sm + 2 * kStageBytes;
-    uint8_t* sMlo = sMhi + kMBytes;
-    float* sCum = reinterpret_cast<float*>(sMlo + kMBytes);
-    float* sDtv = sCum + kQ;
-    int32_t* sR = reinterpret_cast<int32_t*>(sDtv + kQ);
-    float* sW = reinterpret_cast<float*>(sR + kQ);
-    float* sE = sW + kQ;
-    float* sDecay = sE + kQ;
-
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
+    const bool consumer = wave < 4;
 
     // block -> (row, head): consecutive units on one XCD (blocks are dealt round-robin over
     // the 8 XCDs), so the heads of one row share that XCD's L2 for the B/C/G tiles
     const int64_t nblk = gridDim.x;
-    const int64_t k = blockIdx.x;
-    const int64_t u = (nblk % 8 == 0) ? (k % 8) * (nblk / 8) + k / 8 : k;
+    const int64_t kb = blockIdx.x;
+    const int64_t u = (nblk % 8 == 0) ? (kb % 8) * (nblk / 8) + kb / 8 : kb;
     const int64_t b = u / a.H, h = u % a.H;
     const int64_t g = h / (a.H / a.G);
-    const int64_t L = a.L, K = a.K;
-    const int rows = static_cast<int>(kQ + K - 1);
+    const int64_t L = a.L;
     const int64_t nC = (L + kQ - 1) / kQ;
     const float Ah = a.A[h];
-    const int p_own = 16 * wave + li;  // channel whose x this lane convolves / owns in h
+    const uint16_t* xrow_base = a.x + b * L * a.x_row + a.x_col0 + h * kP;
+    uint16_t* y_base = a.y + (b * L * a.H + h) * kP;
 
-    // conv weights of this lane's channel
-    double cw[kKmax];
-    double cbias = 0.0;
-    if (FUSED) {
-        const int64_t cc = a.x_col0 + h * kP + p_own;
-#pragma unroll
-        for (int kk = 0; kk < kKmax; ++kk) cw[kk] = kk < K ? a.conv_w[cc * K + kk] : 0.0f;
-        cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
-    }
-
-    // state slice: acc[t][r] = h[p_own][n(t, 4*g4 + r)], n(t, rho) = 32(t/2) + 8(rho/4) +
-    // 4(t%2) + rho%4, i.e. for k-step m the lane holds n = 32m + 8*g4 + e, e = 0..7
-    f32x4 acc[8];
-    {
-        const float* src = a.init_state ? a.init_state + ((b * a.H + h) * kP + p_own) * kN : nullptr;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
-            if (src) {
-                v0 = *reinterpret_cast<const f32x4*>(src + 32 * m + 8 * g4);
-                v1 = *reinterpret_cast<const f32x4*>(src + 32 * m + 8 * g4 + 4);
-            }
-            acc[2 * m] = v0;
-            acc[2 * m + 1] = v1;
-        }
-    }
-
-    Stage st;
-    stage_load(a, b, h, g, 0, nC, tid, st);
-    stage_store(stages, st, tid, rows);
-    f32x4 gm[4] = {st.gm[0], st.gm[1], st.gm[2], st.gm[3]};
-    float dt_cur = st.dt;
-    __syncthreads();
-
-    for (int64_t cn = 0; cn < nC; ++cn) {
-        uint8_t* stage = stages + (cn & 1) * kStageBytes;
-        const uint8_t* sX = stage;
-        const uint8_t* sC = stage + kXBytes;
-        const uint8_t* sBt = sC + kCBytes;
-        const int32_t* sSeq = reinterpret_cast<const int32_t*>(sBt + kBtBytes);
-        const int64_t t0 = cn * kQ;
-        const bool more = cn + 1 < nC;
-        if (more) stage_load(a, b, h, g, cn + 1, nC, tid, st);
-
-        // ---- chunk scalars (wave 0, lane = token) ----
-        if (wave == 0) {
-            const int j = lane;
-            const bool valid = t0 + j < L;
-            const float dtv = valid ? dt_cur : 0.0f;
-            const float cum = warp_incl_sum(dtv * Ah, lane);
-            int rst = -1;
-            if (HAS_SEQ && valid && t0 + j > 0 && sSeq[j + K - 1] != sSeq[j + K - 2]) rst = j;
-            const int r = warp_incl_max(rst, lane);
-            const float cum_last = __shfl(cum, kQ - 1);
-            const int r_last = __shfl(r, kQ - 1);
-            sCum[j] = cum;
-            sDtv[j] = dtv;
-            sR[j] = r;
-            sE[j] = r < 0 ? __expf(cum) : 0.0f;
-            sW[j] = j >= r_last ? __expf(cum_last - cum) * dtv : 0.0f;
-            if (j == 0) *sDecay = r_last < 0 ? __expf(cum_last) : 0.0f;
-        }
-
-        // ---- conv of this lane's channel over its 16 tokens (j = 32s + 8*g4 + e) ----
-        bf16x8 xv[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int j0 = 32 * s + 8 * g4;
-            if (FUSED) {
-                double u[kKmax + 7];
-                int32_t id[kKmax + 7];
-#pragma unroll
-                for (int tau = 0; tau < kKmax + 7; ++tau) {
-                    if (tau < 8 + K - 1) {
-                        u[tau] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sX + (j0 + tau) * kXStride + p_own * 2));
-                        id[tau] = HAS_SEQ ? sSeq[j0 + tau] : 0;
-                    } else {
-                        u[tau] = 0.0;
-                        id[tau] = 0;
-                    }
-                }
-                uint16_t o[8];
-                conv8<HAS_SEQ>(u, id, cw, cbias, static_cast<int>(K), a.act, o);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xv[s][e] = __builtin_bit_cast(__bf16, o[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint16_t raw = *reinterpret_cast<const uint16_t*>(sX + (j0 + e + K - 1) * kXStride + p_own * 2);
-                    xv[s][e] = __builtin_bit_cast(__bf16, raw);
-                }
-            }
-        }
-        __syncthreads();  // scalars visible
-
-        // ---- M = G o exp(cum_i - cum_j) dt_j on j <= i within the segment; hi/lo -> LDS ----
+    // The two roles run separate loops (a wave's role never changes), so the register
+    // allocator sees the consumer's state and the producer's in-flight fetch as disjoint
+    // live ranges.  Both loops pass the same number of block barriers: one after the
+    // producers' first chunk, then one per chunk.
+    if (consumer) {
+        // state slice acc[t][r] = h[p][n], p = 16 wave + li, n = 32(t/2) + 8 g4 + 4(t%2) + r
+        // (the MFMA row of tile t that lane group g4 holds)
+        const int p_own = 16 * wave + li;
+        f32x4 acc[8];
         {
-            const int i = tid >> 2, jb = (tid & 3) * 16;
-            float mv[16];
-            if (jb <= i) {
-                const float ci = sCum[i];
-                const int ri = sR[i];
+            const float* src = a.init_state ? a.init_state + ((b * a.H + h) * kP + p_own) * kN : nullptr;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = jb + e;
-                    const float gv = gm[e >> 2][e & 3];
-                    const float m = gv * __expf(ci - sCum[j]) * sDtv[j];
-                    mv[e] = (j <= i && j >= ri) ? m : 0.0f;
+            for (int m = 0; m < 4; ++m) {
+                f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
+                if (src) {
+                    v0 = *reinterpret_cast<const f32x4*>(src + 32 * m + 8 * g4);
+                    v1 = *reinterpret_cast<const f32x4*>(src + 32 * m + 8 * g4 + 4);
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mv[e] = 0.0f;
+                acc[2 * m] = v0;
+                acc[2 * m + 1] = v1;
             }
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                float v8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v8[e] = mv[8 * half + e];
-                bf16x8 hi, lo;
-                split_hilo(v8, hi, lo);
-                *reinterpret_cast<bf16x8*>(sMhi + i * kMStride + (jb + 8 * half) * 2) = hi;
-                *reinterpret_cast<bf16x8*>(sMlo + i * kMStride + (jb + 8 * half) * 2) = lo;
-            }
-        }
-        // per-lane scalars for the contractions (read before the next barrier: wave 0
-        // rewrites them for the next chunk right after it)
-        float eI[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) eI[I] = sE[16 * I + li];
-        float wj[2][8];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wj[s][e] = sW[32 * s + 8 * g4 + e];
-        const float decay = *sDecay;
-        __syncthreads();  // M visible
-
-        // ---- Y^T[p][i] (p = 16*wave + 4*g4 + r, i = 16I + li) ----
-        f32x4 yo[4], yi[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            yo[I] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            yi[I] = yo[I];
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            float hv[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hv[e] = acc[2 * m][e];
-                hv[4 + e] = acc[2 * m + 1][e];
-            }
-            bf16x8 hhi, hlo;
-            split_hilo(hv, hhi, hlo);
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const bf16x8 cv = lds_bf16x8(sC + (16 * I + li) * kCStride + (32 * m + 8 * g4) * 2);
-                yo[I] = mfma(hhi, cv, yo[I]);
-                yo[I] = mfma(hlo, cv, yo[I]);
-            }
-        }
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (32 * s <= 16 * I + 15) {
-                    const bf16x8 mh = lds_bf16x8(sMhi + (16 * I + li) * kMStride + (32 * s + 8 * g4) * 2);
-                    const bf16x8 ml = lds_bf16x8(sMlo + (16 * I + li) * kMStride + (32 * s + 8 * g4) * 2);
-                    yi[I] = mfma(xv[s], mh, yi[I]);
-                    yi[I] = mfma(xv[s], ml, yi[I]);
-                }
-            }
-        }
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const int64_t t = t0 + 16 * I + li;
-            if (t < L) {
-                uint2 pk;
-                pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
-                pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
-                *reinterpret_cast<uint2*>(a.y + ((b * L + t) * a.H + h) * kP + 16 * wave + 4 * g4) = pk;
-            }
-        }
-
-        // ---- state update: h^T[n][p] = decay h^T + B^T (W o X) ----
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] *= decay;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            float wx[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wx[e] = wj[s][e] * static_cast<float>(xv[s][e]);
-            bf16x8 bh, bl;
-            split_hilo(wx, bh, bl);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int n_row = 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3);
-                const bf16x8 bv = lds_bf16x8(sBt + n_row * kBtStride + (32 * s + 8 * g4) * 2);
-                acc[t] = mfma(bv, bh, acc[t]);
-                acc[t] = mfma(bv, bl, acc[t]);
-            }
-        }
-
-        // ---- next chunk's tiles into the other stage ----
-        if (more) {
-            stage_store(stages + ((cn + 1) & 1) * kStageBytes, st, tid, rows);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) gm[q] = st.gm[q];
-            dt_cur = st.dt;
         }
         __syncthreads();
-    }
-
-    // ---- final SSM state ----
-    if (a.final_state) {
-        float* dst = a.final_state + ((b * a.H + h) * kP + p_own) * kN;
+        for (int64_t cn = 0; cn < nC; ++cn) {
+            const uint8_t* st = sm + (cn & 1) * kStageBytes;
+            const int64_t t0 = cn * kQ;
+            float eI[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4) = acc[2 * m];
-            *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
+            for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
+            float wj[2][8];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const f32x4 w0 = lds_ld<f32x4>(st, kStW + (32 * s + 8 * g4) * 4);
+                const f32x4 w1 = lds_ld<f32x4>(st, kStW + (32 * s + 8 * g4 + 4) * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { wj[s][e] = w0[e]; wj[s][4 + e] = w1[e]; }
+            }
+            const float decay = lds_ld<float>(st, kStDecay);
+            bf16x8 xv[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) xv[s] = lds_ld<bf16x8>(st, kStX + sw_8(p_own, 4 * s + g4));
+
+            // Y^T[p][i], p = 16 wave + 4 g4 + r, i = 16 I + li
+            f32x4 yo[4], yi[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                yo[I] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                yi[I] = yo[I];
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float hv[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hv[e] = acc[2 * m][e];
+                    hv[4 + e] = acc[2 * m + 1][e];
+                }
+                bf16x8 hhi, hlo;
+                split_hilo(hv, hhi, hlo);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const bf16x8 cv = lds_ld<bf16x8>(st, kStC + sw_c(16 * I + li, 4 * m + g4));
+                    yo[I] = mfma(hhi, cv, yo[I]);
+                    yo[I] = mfma(hlo, cv, yo[I]);
+                }
+            }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (32 * s <= 16 * I + 15) {
+                        const bf16x8 mh = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * s + g4));
+                        const bf16x8 ml = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * s + g4));
+                        yi[I] = mfma(xv[s], mh, yi[I]);
+                        yi[I] = mfma(xv[s], ml, yi[I]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int64_t t = t0 + 16 * I + li;
+                if (t < L) {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
+                    pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
+                    *reinterpret_cast<uint2*>(y_base + t * a.H * kP + 16 * wave + 4 * g4) = pk;
+                }
+            }
+            // state update: h^T[n][p] = decay h^T + B^T (W o X)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[t] *= decay;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float wx[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wx[e] = wj[s][e] * static_cast<float>(xv[s][e]);
+                bf16x8 bh, bl;
+                split_hilo(wx, bh, bl);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int n_row = 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3);
+                    const bf16x8 bv = lds_ld<bf16x8>(st, kStBt + sw_bt(n_row, 4 * s + g4));
+                    acc[t] = mfma(bv, bh, acc[t]);
+                    acc[t] = mfma(bv, bl, acc[t]);
+                }
+            }
+            __syncthreads();
+        }
+        if (a.final_state) {
+            float* dst = a.final_state + ((b * a.H + h) * kP + p_own) * kN;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4) = acc[2 * m];
+                *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
+            }
+        }
+    } else {
+        const int pw = wave - 4;
+        uint8_t* px = sm + kPrivX + pw * kPxBytes;
+        uint8_t* ps = sm + kPrivS + pw * kPsBytes;
+        // conv taps of channel p = lane
+        double cw[K];
+        double cbias = 0.0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) cw[k] = 0.0;
+        if (FUSED) {
+            const int64_t cc = a.x_col0 + h * kP + lane;
+#pragma unroll
+            for (int k = 0; k < K; ++k) cw[k] = a.conv_w[cc * K + k];
+            cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
+        }
+        Fetch f;
+        fetch<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, 0, nC, pw, lane, f);
+        produce<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, 0, nC, Ah, cw, cbias, pw, lane, sm, px,
+                                   ps, f);
+        __syncthreads();
+        for (int64_t cn = 0; cn < nC; ++cn) {
+            if (cn + 1 < nC)
+                produce<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, cn + 1, nC, Ah, cw, cbias, pw,
+                                           lane, sm + ((cn + 1) & 1) * kStageBytes, px, ps, f);
+            __syncthreads();
         }
     }
+
     // ---- final conv state F = u[L .. L+K-2] for this head's x channels and for slice h of
     // the B / C channels: all reads first, then a barrier, then the writes, so an in-place
     // state pair is never read after being overwritten ----
     if (FUSED && a.conv_final) {
-        const int64_t km1 = K - 1;
+        constexpr int km1 = K - 1;
         const int64_t nx = kP * km1;
         const int64_t nbc_all = 2 * a.G * kN * km1;
         const int64_t per = (nbc_all + a.H - 1) / a.H;
         const int64_t bc_lo = min(h * per, nbc_all), bc_hi = min((h + 1) * per, nbc_all);
         const int64_t total = nx + (bc_hi - bc_lo);
-        constexpr int kMaxItems = 12;  // >= ceil((64*7 + 2*128*7) / 256) for every G <= H
+        constexpr int kMaxItems = 6;  // >= ceil((64*7 + 2*128*7) / 512) for every G <= H
         uint16_t fv[kMaxItems];
         int64_t fidx[kMaxItems];
         int cnt = 0;
 #pragma unroll
         for (int q = 0; q < kMaxItems; ++q) {
-            const int64_t idx = tid + static_cast<int64_t>(q) * kThreads;
+            const int64_t idx = tid + static_cast<int64_t>(q) * kMainThreads;
             if (idx < total) {
                 int64_t cc, r;
                 if (idx < nx) {
@@ -653,6 +677,29 @@ ssd_main_kernel(ChunkedArgs a) {
     }
 }
 
+template <int K>
+hipError_t launch_k(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    const int64_t nC = (a.L + kQ - 1) / kQ;
+    ssd_prep_kernel<K><<<dim3(static_cast<unsigned>(nC), static_cast<unsigned>(a.G),
+                              static_cast<unsigned>(a.B)),
+                         kPrepThreads, 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev0) hipEventRecord(ev0, stream);
+    const dim3 grid(static_cast<unsigned>(a.B * a.H));
+    const bool seq = a.seq_idx != nullptr;
+    if (a.fused_conv) {
+        if (seq) ssd_main_kernel<K, true, true><<<grid, kMainThreads, 0, stream>>>(a);
+        else ssd_main_kernel<K, true, false><<<grid, kMainThreads, 0, stream>>>(a);
+    } else {
+        if (seq) ssd_main_kernel<K, false, true><<<grid, kMainThreads, 0, stream>>>(a);
+        else ssd_main_kernel<K, false, false><<<grid, kMainThreads, 0, stream>>>(a);
+    }
+    e = hipGetLastError();
+    if (ev1) hipEventRecord(ev1, stream);
+    return e;
+}
+
 }  // namespace
 
 bool chunked_supported(int64_t P, int64_t N, ssm_dtype_t dtype) {
@@ -669,25 +716,16 @@ size_t chunked_workspace_bytes(int64_t B, int64_t L, int64_t G, int64_t N) {
 hipError_t launch_chunked(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev_before_main,
                           hipEvent_t ev_after_main) {
     if (a.B == 0 || a.L == 0) return hipSuccess;
-    const int64_t nC = (a.L + kQ - 1) / kQ;
-    ssd_prep_kernel<<<dim3(static_cast<unsigned>(nC), static_cast<unsigned>(a.G),
-                           static_cast<unsigned>(a.B)),
-                      kThreads, 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (ev_before_main) hipEventRecord(ev_before_main, stream);
-    const dim3 grid(static_cast<unsigned>(a.B * a.H));
-    const bool seq = a.seq_idx != nullptr;
-    if (a.fused_conv) {
-        if (seq) ssd_main_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
-        else ssd_main_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
-    } else {
-        if (seq) ssd_main_kernel<false, true><<<grid, kThreads, 0, stream>>>(a);
-        else ssd_main_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
+    switch (a.K) {
+        case 2: return launch_k<2>(a, stream, ev_before_main, ev_after_main);
+        case 3: return launch_k<3>(a, stream, ev_before_main, ev_after_main);
+        case 4: return launch_k<4>(a, stream, ev_before_main, ev_after_main);
+        case 5: return launch_k<5>(a, stream, ev_before_main, ev_after_main);
+        case 6: return launch_k<6>(a, stream, ev_before_main, ev_after_main);
+        case 7: return launch_k<7>(a, stream, ev_before_main, ev_after_main);
+        case 8: return launch_k<8>(a, stream, ev_before_main, ev_after_main);
+        default: return hipErrorInvalidValue;
     }
-    e = hipGetLastError();
-    if (ev_after_main) hipEventRecord(ev_after_main, stream);
-    return e;
 }
 
 }  // namespace ssm
