@@ -63,13 +63,45 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 // argument's relative rounding, v_exp / v_rcp and three roundings).  Only results closer
 // than twice that to a bf16 rounding midpoint are recomputed in double, so the rounding
 // decision matches the exact value's.
-__device__ __forceinline__ uint16_t act_to_bf16(double z, int act) {
-    if (act != SSM_ACT_SILU) return f64_to_bf16(z);
+__device__ __forceinline__ float silu_f32(double z, bool& near_midpoint) {
     const float zf = static_cast<float>(z);
     const float s = zf * __builtin_amdgcn_rcpf(1.0f + __expf(-zf));
     const int dist = abs(static_cast<int>(__float_as_uint(s) & 0xFFFFu) - 0x8000);
-    if (static_cast<float>(dist) > 8.0f + 4.0f * fabsf(zf)) return f32_to_bf16(s);
+    near_midpoint = static_cast<float>(dist) <= 8.0f + 4.0f * fabsf(zf);
+    return s;
+}
+__device__ __forceinline__ uint16_t silu_f64_to_bf16(double z) {
     return f64_to_bf16(z / (1.0 + exp(-z)));
+}
+__device__ __forceinline__ uint16_t act_to_bf16(double z, int act) {
+    if (act != SSM_ACT_SILU) return f64_to_bf16(z);
+    bool near;
+    const float s = silu_f32(z, near);
+    return near ? silu_f64_to_bf16(z) : f32_to_bf16(s);
+}
+// The same for NB values at once: all fast paths first (independent chains the scheduler
+// can interleave), then a single branch for the rare near-midpoint recomputations.
+template <int NB>
+__device__ __forceinline__ void act_to_bf16_batch(const double (&z)[NB], int act,
+                                                  uint16_t (&out)[NB]) {
+    if (act != SSM_ACT_SILU) {
+#pragma unroll
+        for (int e = 0; e < NB; ++e) out[e] = f64_to_bf16(z[e]);
+        return;
+    }
+    uint32_t near_mask = 0;
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+        bool near;
+        const float s = silu_f32(z[e], near);
+        out[e] = f32_to_bf16(s);
+        near_mask |= static_cast<uint32_t>(near) << e;
+    }
+    if (near_mask != 0) {
+#pragma unroll
+        for (int e = 0; e < NB; ++e)
+            if (near_mask & (1u << e)) out[e] = silu_f64_to_bf16(z[e]);
+    }
 }
 
 __host__ __device__ __forceinline__ int64_t floor_mod(int64_t a, int64_t m) {

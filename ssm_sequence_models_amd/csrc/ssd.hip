@@ -28,13 +28,15 @@
 //            h^T += B^T x (W o X)      (state update)
 //        The fp32 operands (h, M, W o X) enter as a hi + lo pair of bf16 (v = hi + lo with
 //        |v - hi - lo| <= 2^-17 |v|); the other operand (x, B, C) is exact in bf16, so each
-//        contraction is accurate to about fp32 at the bf16 MFMA rate.
-//      - 4 producer waves run one chunk ahead: fetch the next chunk's x rows and C / B^T / G
-//        tiles from HBM / L2, run the register-window conv + SiLU of the head's x channels,
-//        the in-chunk cumulative log-decay (a DPP prefix scan per wavefront) and the M tiles,
-//        and leave everything in the other half of a double-buffered LDS stage.
-//    One block barrier per chunk hands the stage over.  Sharing each SIMD between a producer
-//    and a consumer wave lets the conv's VALU work run under the consumer's MFMA work.
+//        contraction is accurate to about fp32 at the bf16 MFMA rate.  Each consumer lane
+//        also runs the register-window conv + SiLU of its channel over its 16 tokens, which
+//        directly yields its X operand.
+//      - 4 producer waves run one chunk ahead: fetch the next chunk's raw x rows and
+//        C / B^T / G tiles from HBM / L2, compute the in-chunk cumulative log-decay (a DPP
+//        prefix scan per wavefront) and the M tiles, and leave everything in the other half
+//        of a double-buffered LDS stage.
+//    One block barrier per chunk hands the stage over.  Each SIMD runs one producer and one
+//    consumer wave, so VALU work of one hides the latencies of the other.
 #include "internal.h"
 
 namespace ssm {
@@ -225,31 +227,36 @@ ssd_prep_kernel(ChunkedArgs a) {
 // main kernel
 // =======================================================================================
 // One LDS stage (double-buffered): all tiles are rows of 16-byte pieces stored under an XOR
-// swizzle chosen so that each 16-lane group of a consumer's ds_read_b128 covers the 64
-// banks once.
+// swizzle chosen so that every 8 consecutive lanes of a ds_read_b128 / ds_write_b128 (the
+// lanes one 128-byte LDS cycle serves) touch 8 different 16-byte bank groups.
+constexpr int kRowsMax = kQ + kKmax - 1;        // raw x rows of a chunk incl. the conv halo
 constexpr int kStC = 0;                          // C   [64 tok][16 pieces], piece ^ (tok & 15)
 constexpr int kStBt = kStC + kQ * 256;           // B^T [128 n][8 pieces], piece ^ bt_swz(n)
-constexpr int kStX = kStBt + kN * 128;           // X^T [64 p][8 pieces], piece ^ ((p >> 1) & 7)
-constexpr int kStMhi = kStX + kP * 128;          // M   [64 i][8 pieces], piece ^ ((i >> 1) & 7)
+constexpr int kStXr = kStBt + kN * 128;          // raw x [rows][8 pieces], piece ^ xr_swz(row)
+constexpr int kStMhi = kStXr + kRowsMax * 128;   // M   [64 i][8 pieces], piece ^ (i & 7)
 constexpr int kStMlo = kStMhi + kQ * 128;
 constexpr int kStE = kStMlo + kQ * 128;          // E_i = exp(cum_i) on the leading segment
 constexpr int kStW = kStE + kQ * 4;              // W_j = exp(cum_last - cum_j) dt_j
-constexpr int kStDecay = kStW + kQ * 4;          // exp(cum_last) (0 after a reset)
+constexpr int kStSeq = kStW + kQ * 4;            // seq ids of the raw x rows
+constexpr int kStDecay = kStSeq + 72 * 4;        // exp(cum_last) (0 after a reset)
 constexpr int kStageBytes = kStDecay + 16;
-// producer-private areas (one per producer wave)
-constexpr int kPxRows = 16 + kKmax - 1;          // x rows for 16 outputs + conv halo
-constexpr int kPxBytes = kPxRows * 128;
-constexpr int kPsBytes = 3 * kQ * 4 + 32 * 4;    // cum, dtv, r, conv ids
-constexpr int kPrivX = 2 * kStageBytes;
-constexpr int kPrivS = kPrivX + 4 * kPxBytes;
+// producer-private areas (one per producer wave): cum, dtv, r of the chunk
+constexpr int kPsBytes = 3 * kQ * 4;
+constexpr int kPrivS = 2 * kStageBytes;
 constexpr int kMainLds = kPrivS + 4 * kPsBytes;
 static_assert(kMainLds <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int sw_c(int tok, int q) { return tok * 256 + ((q ^ (tok & 15)) << 4); }
+// B^T rows are read through the state-tile row map n = 32T + 8(l>>2) + 4(t&1) + (l&3):
+// bits 0-1 and 3 of n differ across 8 consecutive lanes
 __device__ __forceinline__ int sw_bt(int n, int q) {
-    return n * 128 + ((q ^ (((n >> 3) & 3) | (((n >> 1) & 1) << 2))) << 4);
+    return n * 128 + ((q ^ ((n & 3) | (((n >> 3) & 1) << 2))) << 4);
 }
-__device__ __forceinline__ int sw_8(int row, int q) { return row * 128 + ((q ^ ((row >> 1) & 7)) << 4); }
+__device__ __forceinline__ int sw_8(int row, int q) { return row * 128 + ((q ^ (row & 7)) << 4); }
+// raw x rows: the consumers' 2-byte reads hit rows 8 apart in the four 16-lane groups
+__device__ __forceinline__ int sw_xr(int row, int q) {
+    return row * 128 + ((q ^ (((row >> 3) & 3) << 1)) << 4);
+}
 
 // M tiles computed by each producer wave: (row block I of 16, column half s of 32); the six
 // tiles cover j <= i
@@ -262,6 +269,15 @@ __device__ __forceinline__ int unit_S(int pw, int u) {
     return t[pw][u];
 }
 
+// Per-block bases; everything inside one (row, head) is addressed with 32-bit offsets
+// (the host checks that seqlen * channels fits).
+struct Blk {
+    const uint16_t* x;      // x channel 0 of this head at token 0 of this row
+    const float* dt;        // dt of this head at token 0 of this row
+    const int32_t* seq;     // seq_idx of this row, or NULL
+    int L, x_row, H;
+};
+
 // Registers a producer lane carries from the fetch of chunk c+1 to its use
 struct Fetch {
     u32x4 c[4];
@@ -271,13 +287,14 @@ struct Fetch {
     float dt;
     int32_t seq_j, seq_jm1, seq_row;
 };
+// raw x pieces of a chunk (rows t0 - (K-1) .. t0 + Q - 1, 8 channels each) handed to the
+// 256 producer lanes: piece ptid + 256 k
 
 template <int K, bool FUSED, bool HAS_SEQ>
-__device__ __forceinline__ void fetch(const ChunkedArgs& a, const uint16_t* xrow_base,
-                                      int64_t b, int64_t h, int64_t g, int64_t cn, int64_t nC,
-                                      int pw, int lane, Fetch& f) {
-    const int64_t L = a.L;
-    const int64_t t0 = cn * kQ;
+__device__ __forceinline__ void fetch(const ChunkedArgs& a, const Blk& bk, int64_t b, int64_t h,
+                                      int64_t g, int64_t cn, int64_t nC, int pw, int lane,
+                                      Fetch& f) {
+    const int t0 = static_cast<int>(cn) * kQ;
     const int64_t unit = ws_unit(a, b, cn, g, nC);
     const uint16_t* ws = static_cast<const uint16_t*>(a.workspace);
     const uint16_t* wsC = ws + unit * kWsC;
@@ -291,17 +308,17 @@ __device__ __forceinline__ void fetch(const ChunkedArgs& a, const uint16_t* xrow
         f.c[k] = *reinterpret_cast<const u32x4*>(wsC + idx * 8);
         f.bt[k] = *reinterpret_cast<const u32x4*>(wsBt + idx * 8);
     }
-    // x rows t0 + 16 pw - (K-1) + rho, rho < 16 + K - 1, 8 channels per piece
-    constexpr int kRows = 16 + K - 1;
+    // raw x rows t0 - (K-1) + rho, rho < Q + K - 1, 8 channels per piece
+    constexpr int kRows = kQ + K - 1;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        const int idx = lane + 64 * k;
+        const int idx = ptid + 256 * k;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (idx < kRows * 8) {
             const int rho = idx >> 3, q = idx & 7;
-            const int64_t t = t0 + 16 * pw - (K - 1) + rho;
-            if (t >= 0 && t < L) {
-                v = *reinterpret_cast<const u32x4*>(xrow_base + t * a.x_row + q * 8);
+            const int t = t0 - (K - 1) + rho;
+            if (t >= 0 && t < bk.L) {
+                v = *reinterpret_cast<const u32x4*>(bk.x + t * bk.x_row + q * 8);
             } else if (FUSED && t < 0 && a.conv_init) {
                 const int64_t cc0 = a.x_col0 + h * kP + q * 8;
                 uint32_t w4[4];
@@ -322,7 +339,7 @@ __device__ __forceinline__ void fetch(const ChunkedArgs& a, const uint16_t* xrow
         const int I = unit_I(pw, u), s = unit_S(pw, u);
         f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
         if (I >= 0) {
-            const int i = 16 * I + (lane >> 2), q = 4 * s + (lane & 3);
+            const int i = 16 * I + (lane & 15), q = 4 * s + (lane >> 4);
             if (8 * q <= i) {
                 v0 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q);
                 v1 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q + 4);
@@ -331,28 +348,27 @@ __device__ __forceinline__ void fetch(const ChunkedArgs& a, const uint16_t* xrow
         f.gm[u][0] = v0;
         f.gm[u][1] = v1;
     }
-    const int64_t t = t0 + lane;
-    f.dt = t < L ? a.dt[(b * L + t) * a.H + h] : 0.0f;
+    const int t = t0 + lane;
+    f.dt = t < bk.L ? bk.dt[t * bk.H] : 0.0f;
     f.seq_j = f.seq_jm1 = f.seq_row = 0;
     if (HAS_SEQ) {
-        const int64_t tc = t < L ? t : L - 1;
-        f.seq_j = a.seq_idx[b * L + tc];
-        f.seq_jm1 = a.seq_idx[b * L + (tc > 0 ? tc - 1 : 0)];
-        int64_t tr = t0 + 16 * pw - (K - 1) + lane;
-        tr = tr < 0 ? 0 : (tr >= L ? L - 1 : tr);
-        f.seq_row = a.seq_idx[b * L + tr];
+        const int tc = t < bk.L ? t : bk.L - 1;
+        f.seq_j = bk.seq[tc];
+        f.seq_jm1 = bk.seq[tc > 0 ? tc - 1 : 0];
+        int tr = t0 - (K - 1) + ptid;
+        tr = tr < 0 ? 0 : (tr >= bk.L ? bk.L - 1 : tr);
+        f.seq_row = bk.seq[tr];
     }
 }
 
-// Producer work for chunk cn: drop the fetched tiles into `stage`, fetch chunk cn+1, then
-// compute the chunk scalars, the conv of the head's x channels and this wave's M tiles.
+// Producer work for chunk cn: drop the fetched tiles and raw x rows into `stage`, fetch
+// chunk cn+1, then compute the chunk scalars and this wave's M tiles.
 template <int K, bool FUSED, bool HAS_SEQ>
-__device__ __forceinline__ void produce(const ChunkedArgs& a, const uint16_t* xrow_base,
-                                        int64_t b, int64_t h, int64_t g, int64_t cn,
-                                        int64_t nC, float Ah, const double (&cw)[K],
-                                        double cbias, int pw, int lane, uint8_t* stage,
-                                        uint8_t* px, uint8_t* ps, Fetch& f) {
-    constexpr int kRows = 16 + K - 1;
+__device__ __forceinline__ void produce(const ChunkedArgs& a, const Blk& bk, int64_t b,
+                                        int64_t h, int64_t g, int64_t cn, int64_t nC,
+                                        float Ah, int pw, int lane, uint8_t* stage,
+                                        uint8_t* ps, Fetch& f) {
+    constexpr int kRows = kQ + K - 1;
     const int ptid = pw * 64 + lane;
     // 1. fetched tiles -> LDS
 #pragma unroll
@@ -363,27 +379,26 @@ __device__ __forceinline__ void produce(const ChunkedArgs& a, const uint16_t* xr
     }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        const int idx = lane + 64 * k;
-        if (idx < kRows * 8) lds_st(px, idx * 16, f.x[k]);
+        const int idx = ptid + 256 * k;
+        if (idx < kRows * 8) lds_st(stage, kStXr + sw_xr(idx >> 3, idx & 7), f.x[k]);
     }
+    if (HAS_SEQ && ptid < kRows) reinterpret_cast<int32_t*>(stage + kStSeq)[ptid] = f.seq_row;
     float* pcum = reinterpret_cast<float*>(ps);
     float* pdtv = pcum + kQ;
     int32_t* pr = reinterpret_cast<int32_t*>(pdtv + kQ);
-    int32_t* pid = pr + kQ;
-    if (HAS_SEQ && lane < kRows) pid[lane] = f.seq_row;
     const float dtv = f.dt;
     const int32_t seq_j = f.seq_j, seq_jm1 = f.seq_jm1;
     const f32x4 gm[2][2] = {{f.gm[0][0], f.gm[0][1]}, {f.gm[1][0], f.gm[1][1]}};
 
     // 2. fetch the next chunk while this one is computed
-    if (cn + 1 < nC) fetch<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, cn + 1, nC, pw, lane, f);
+    if (cn + 1 < nC) fetch<K, FUSED, HAS_SEQ>(a, bk, b, h, g, cn + 1, nC, pw, lane, f);
 
     // 3. chunk scalars, lane = token
-    const int64_t t0 = cn * kQ;
+    const int t0 = static_cast<int>(cn) * kQ;
     const int j = lane;
     const float cum = wave_incl_sum(dtv * Ah);
     int rst = -1;
-    if (HAS_SEQ && t0 + j < a.L && t0 + j > 0 && seq_j != seq_jm1) rst = j;
+    if (HAS_SEQ && t0 + j < bk.L && t0 + j > 0 && seq_j != seq_jm1) rst = j;
     const int r = HAS_SEQ ? wave_incl_max(rst) : -1;
     pcum[j] = cum;
     pdtv[j] = dtv;
@@ -398,49 +413,12 @@ __device__ __forceinline__ void produce(const ChunkedArgs& a, const uint16_t* xr
         if (j == 0) *reinterpret_cast<float*>(stage + kStDecay) = r_last < 0 ? __expf(cum_last) : 0.0f;
     }
 
-    // 4. conv of channel p = lane over tokens 16 pw .. 16 pw + 15 -> X^T row p
-    {
-        const int p = lane;
-        uint32_t packed[8];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            uint16_t o[8];
-            if (FUSED) {
-                double u[8 + K - 1];
-                int32_t id[8 + K - 1];
-#pragma unroll
-                for (int tau = 0; tau < 8 + K - 1; ++tau) {
-                    u[tau] = bf16_to_f32(lds_ld<uint16_t>(px, (8 * half + tau) * 128 + 2 * p));
-                    id[tau] = HAS_SEQ ? pid[8 * half + tau] : 0;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    double z = cbias;
-#pragma unroll
-                    for (int k = 0; k < K; ++k) {
-                        const double tap = (!HAS_SEQ || id[e + k] == id[e + K - 1]) ? u[e + k] : 0.0;
-                        z = fma(cw[k], tap, z);
-                    }
-                    o[e] = act_to_bf16(z, a.act);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = lds_ld<uint16_t>(px, (8 * half + e + K - 1) * 128 + 2 * p);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                packed[4 * half + e] = static_cast<uint32_t>(o[2 * e]) | (static_cast<uint32_t>(o[2 * e + 1]) << 16);
-        }
-        lds_st(stage, kStX + sw_8(p, 2 * pw), u32x4{packed[0], packed[1], packed[2], packed[3]});
-        lds_st(stage, kStX + sw_8(p, 2 * pw + 1), u32x4{packed[4], packed[5], packed[6], packed[7]});
-    }
-
-    // 5. this wave's M tiles: M[i][j] = G[i][j] exp(cum_i - cum_j) dt_j on r_i <= j <= i
+    // 4. this wave's M tiles: M[i][j] = G[i][j] exp(cum_i - cum_j) dt_j on r_i <= j <= i
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int I = unit_I(pw, u), s = unit_S(pw, u);
         if (I < 0) continue;
-        const int i = 16 * I + (lane >> 2), q = 4 * s + (lane & 3), j0 = 8 * q;
+        const int i = 16 * I + (lane & 15), q = 4 * s + (lane >> 4), j0 = 8 * q;
         float mv[8];
         if (j0 <= i) {
             const float ci = pcum[i];
@@ -467,6 +445,43 @@ __device__ __forceinline__ void produce(const ChunkedArgs& a, const uint16_t* xr
     }
 }
 
+// Consumer: the conv of channel p over tokens j0 .. j0+7 of the chunk from the staged raw
+// rows (row rho <-> token t0 - (K-1) + rho), rounded to bf16 -> one MFMA operand
+template <int K, bool FUSED, bool HAS_SEQ>
+__device__ __forceinline__ bf16x8 conv_operand(const uint8_t* st, int p, int j0,
+                                               const double (&cw)[K], double cbias, int act) {
+    bf16x8 out;
+    const int q = p >> 3, byte = (p & 7) * 2;
+    if (FUSED) {
+        double u[8 + K - 1];
+        int32_t id[8 + K - 1];
+#pragma unroll
+        for (int tau = 0; tau < 8 + K - 1; ++tau) {
+            u[tau] = bf16_to_f32(lds_ld<uint16_t>(st, kStXr + sw_xr(j0 + tau, q) + byte));
+            id[tau] = HAS_SEQ ? lds_ld<int32_t>(st, kStSeq + (j0 + tau) * 4) : 0;
+        }
+        double z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            z[e] = cbias;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const double tap = (!HAS_SEQ || id[e + k] == id[e + K - 1]) ? u[e + k] : 0.0;
+                z[e] = fma(cw[k], tap, z[e]);
+            }
+        }
+        uint16_t o[8];
+        act_to_bf16_batch(z, act, o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = __builtin_bit_cast(__bf16, o[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            out[e] = __builtin_bit_cast(__bf16, lds_ld<uint16_t>(st, kStXr + sw_xr(j0 + e + K - 1, q) + byte));
+    }
+    return out;
+}
+
 template <int K, bool FUSED, bool HAS_SEQ>
 __global__ void __launch_bounds__(kMainThreads, 1)
 ssd_main_kernel(ChunkedArgs a) {
@@ -485,8 +500,15 @@ ssd_main_kernel(ChunkedArgs a) {
     const int64_t L = a.L;
     const int64_t nC = (L + kQ - 1) / kQ;
     const float Ah = a.A[h];
-    const uint16_t* xrow_base = a.x + b * L * a.x_row + a.x_col0 + h * kP;
+    Blk bk;
+    bk.x = a.x + b * L * a.x_row + a.x_col0 + h * kP;
+    bk.dt = a.dt + b * L * a.H + h;
+    bk.seq = a.seq_idx ? a.seq_idx + b * L : nullptr;
+    bk.L = static_cast<int>(L);
+    bk.x_row = static_cast<int>(a.x_row);
+    bk.H = static_cast<int>(a.H);
     uint16_t* y_base = a.y + (b * L * a.H + h) * kP;
+    const int y_row = bk.H * kP;
 
     // The two roles run separate loops (a wave's role never changes), so the register
     // allocator sees the consumer's state and the producer's in-flight fetch as disjoint
@@ -496,6 +518,17 @@ ssd_main_kernel(ChunkedArgs a) {
         // state slice acc[t][r] = h[p][n], p = 16 wave + li, n = 32(t/2) + 8 g4 + 4(t%2) + r
         // (the MFMA row of tile t that lane group g4 holds)
         const int p_own = 16 * wave + li;
+        // conv taps of channel p_own
+        double cw[K];
+        double cbias = 0.0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) cw[k] = 0.0;
+        if (FUSED) {
+            const int64_t cc = a.x_col0 + h * kP + p_own;
+#pragma unroll
+            for (int k = 0; k < K; ++k) cw[k] = a.conv_w[cc * K + k];
+            cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
+        }
         f32x4 acc[8];
         {
             const float* src = a.init_state ? a.init_state + ((b * a.H + h) * kP + p_own) * kN : nullptr;
@@ -513,7 +546,7 @@ ssd_main_kernel(ChunkedArgs a) {
         __syncthreads();
         for (int64_t cn = 0; cn < nC; ++cn) {
             const uint8_t* st = sm + (cn & 1) * kStageBytes;
-            const int64_t t0 = cn * kQ;
+            const int t0 = static_cast<int>(cn) * kQ;
             float eI[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
@@ -528,7 +561,8 @@ ssd_main_kernel(ChunkedArgs a) {
             const float decay = lds_ld<float>(st, kStDecay);
             bf16x8 xv[2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) xv[s] = lds_ld<bf16x8>(st, kStX + sw_8(p_own, 4 * s + g4));
+            for (int s = 0; s < 2; ++s)
+                xv[s] = conv_operand<K, FUSED, HAS_SEQ>(st, p_own, 32 * s + 8 * g4, cw, cbias, a.act);
 
             // Y^T[p][i], p = 16 wave + 4 g4 + r, i = 16 I + li
             f32x4 yo[4], yi[4];
@@ -568,12 +602,12 @@ ssd_main_kernel(ChunkedArgs a) {
             }
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                const int64_t t = t0 + 16 * I + li;
-                if (t < L) {
+                const int t = t0 + 16 * I + li;
+                if (t < bk.L) {
                     uint2 pk;
                     pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
                     pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
-                    *reinterpret_cast<uint2*>(y_base + t * a.H * kP + 16 * wave + 4 * g4) = pk;
+                    *reinterpret_cast<uint2*>(y_base + t * y_row + 16 * wave + 4 * g4) = pk;
                 }
             }
             // state update: h^T[n][p] = decay h^T + B^T (W o X)
@@ -606,28 +640,15 @@ ssd_main_kernel(ChunkedArgs a) {
         }
     } else {
         const int pw = wave - 4;
-        uint8_t* px = sm + kPrivX + pw * kPxBytes;
         uint8_t* ps = sm + kPrivS + pw * kPsBytes;
-        // conv taps of channel p = lane
-        double cw[K];
-        double cbias = 0.0;
-#pragma unroll
-        for (int k = 0; k < K; ++k) cw[k] = 0.0;
-        if (FUSED) {
-            const int64_t cc = a.x_col0 + h * kP + lane;
-#pragma unroll
-            for (int k = 0; k < K; ++k) cw[k] = a.conv_w[cc * K + k];
-            cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
-        }
         Fetch f;
-        fetch<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, 0, nC, pw, lane, f);
-        produce<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, 0, nC, Ah, cw, cbias, pw, lane, sm, px,
-                                   ps, f);
+        fetch<K, FUSED, HAS_SEQ>(a, bk, b, h, g, 0, nC, pw, lane, f);
+        produce<K, FUSED, HAS_SEQ>(a, bk, b, h, g, 0, nC, Ah, pw, lane, sm, ps, f);
         __syncthreads();
         for (int64_t cn = 0; cn < nC; ++cn) {
             if (cn + 1 < nC)
-                produce<K, FUSED, HAS_SEQ>(a, xrow_base, b, h, g, cn + 1, nC, Ah, cw, cbias, pw,
-                                           lane, sm + ((cn + 1) & 1) * kStageBytes, px, ps, f);
+                produce<K, FUSED, HAS_SEQ>(a, bk, b, h, g, cn + 1, nC, Ah, pw, lane,
+                                           sm + ((cn + 1) & 1) * kStageBytes, ps, f);
             __syncthreads();
         }
     }
