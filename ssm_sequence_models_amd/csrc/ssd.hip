@@ -226,24 +226,33 @@ ssd_prep_kernel(ChunkedArgs a) {
 // =======================================================================================
 // main kernel
 // =======================================================================================
-// One LDS stage (double-buffered): all tiles are rows of 16-byte pieces stored under an XOR
-// swizzle chosen so that every 8 consecutive lanes of a ds_read_b128 / ds_write_b128 (the
-// lanes one 128-byte LDS cycle serves) touch 8 different 16-byte bank groups.
-constexpr int kRowsMax = kQ + kKmax - 1;        // raw x rows of a chunk incl. the conv halo
+// LDS, all tiles stored as rows of 16-byte pieces under XOR swizzles chosen so that every 8
+// consecutive lanes of a ds_read_b128 / ds_write_b128 (the lanes one 128-byte LDS cycle
+// serves) touch 8 different 16-byte bank groups.
+//   stage s (two, by chunk parity), produced one chunk ahead of its use:
 constexpr int kStC = 0;                          // C   [64 tok][16 pieces], piece ^ (tok & 15)
 constexpr int kStBt = kStC + kQ * 256;           // B^T [128 n][8 pieces], piece ^ bt_swz(n)
-constexpr int kStXr = kStBt + kN * 128;          // raw x [rows][8 pieces], piece ^ xr_swz(row)
-constexpr int kStMhi = kStXr + kRowsMax * 128;   // M   [64 i][8 pieces], piece ^ (i & 7)
+constexpr int kStMhi = kStBt + kN * 128;         // M   [64 i][8 pieces], piece ^ (i & 7)
 constexpr int kStMlo = kStMhi + kQ * 128;
 constexpr int kStE = kStMlo + kQ * 128;          // E_i = exp(cum_i) on the leading segment
 constexpr int kStW = kStE + kQ * 4;              // W_j = exp(cum_last - cum_j) dt_j
-constexpr int kStSeq = kStW + kQ * 4;            // seq ids of the raw x rows
-constexpr int kStDecay = kStSeq + 72 * 4;        // exp(cum_last) (0 after a reset)
+constexpr int kStDecay = kStW + kQ * 4;          // exp(cum_last) (0 after a reset)
 constexpr int kStageBytes = kStDecay + 16;
-// producer-private areas (one per producer wave): cum, dtv, r of the chunk
+//   raw x slot (two, by chunk parity), staged two chunks ahead: the conv of chunk c+1 runs
+//   while chunk c is contracted
+constexpr int kRowsMax = kQ + kKmax - 1;         // raw x rows of a chunk incl. the conv halo
+constexpr int kRwX = 0;                          // raw x [rows][8 pieces], piece ^ xr_swz(row)
+constexpr int kRwSeq = kRowsMax * 128;           // seq ids of the raw rows
+constexpr int kRawBytes = kRwSeq + 72 * 4;
+//   y slot (two, by chunk parity): consumers write their Y^T tiles, producers store whole
+//   token rows one chunk later
+constexpr int kYBytes = kQ * kP * 2;             // [64 tok][16 slots of 8 B], slot ^ (tok & 15)
+//   producer-private scalars: cum, dtv, r of the chunk
 constexpr int kPsBytes = 3 * kQ * 4;
-constexpr int kPrivS = 2 * kStageBytes;
-constexpr int kMainLds = kPrivS + 4 * kPsBytes;
+constexpr int kOffRaw = 2 * kStageBytes;
+constexpr int kOffY = kOffRaw + 2 * kRawBytes;
+constexpr int kOffPs = kOffY + 2 * kYBytes;
+constexpr int kMainLds = kOffPs + 4 * kPsBytes;
 static_assert(kMainLds <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int sw_c(int tok, int q) { return tok * 256 + ((q ^ (tok & 15)) << 4); }
@@ -257,6 +266,8 @@ __device__ __forceinline__ int sw_8(int row, int q) { return row * 128 + ((q ^ (
 __device__ __forceinline__ int sw_xr(int row, int q) {
     return row * 128 + ((q ^ (((row >> 3) & 3) << 1)) << 4);
 }
+// y tile: 16 lanes of a ds_write_b64 write 16 tokens at the same 8-byte column
+__device__ __forceinline__ int sw_y(int tok, int slot8) { return tok * 128 + ((slot8 ^ (tok & 15)) << 3); }
 
 // M tiles computed by each producer wave: (row block I of 16, column half s of 32); the six
 // tiles cover j <= i
@@ -275,25 +286,26 @@ struct Blk {
     const uint16_t* x;      // x channel 0 of this head at token 0 of this row
     const float* dt;        // dt of this head at token 0 of this row
     const int32_t* seq;     // seq_idx of this row, or NULL
+    uint16_t* y;            // y channel 0 of this head at token 0 of this row
     int L, x_row, H;
 };
 
-// Registers a producer lane carries from the fetch of chunk c+1 to its use
+// Registers a producer lane carries between fetching and staging.  The tiles (C, B^T,
+// G, dt, ids) belong to chunk k, the raw x rows to chunk k+1.
 struct Fetch {
     u32x4 c[4];
     u32x4 bt[4];
-    u32x4 x[3];
     f32x4 gm[2][2];
     float dt;
-    int32_t seq_j, seq_jm1, seq_row;
+    int32_t seq_j, seq_jm1;
+    u32x4 x[3];
+    int32_t seq_row;
 };
-// raw x pieces of a chunk (rows t0 - (K-1) .. t0 + Q - 1, 8 channels each) handed to the
-// 256 producer lanes: piece ptid + 256 k
 
-template <int K, bool FUSED, bool HAS_SEQ>
-__device__ __forceinline__ void fetch(const ChunkedArgs& a, const Blk& bk, int64_t b, int64_t h,
-                                      int64_t g, int64_t cn, int64_t nC, int pw, int lane,
-                                      Fetch& f) {
+template <bool HAS_SEQ>
+__device__ __forceinline__ void fetch_tiles(const ChunkedArgs& a, const Blk& bk, int64_t b,
+                                            int64_t g, int64_t cn, int64_t nC, int pw, int lane,
+                                            Fetch& f) {
     const int t0 = static_cast<int>(cn) * kQ;
     const int64_t unit = ws_unit(a, b, cn, g, nC);
     const uint16_t* ws = static_cast<const uint16_t*>(a.workspace);
@@ -308,8 +320,39 @@ __device__ __forceinline__ void fetch(const ChunkedArgs& a, const Blk& bk, int64
         f.c[k] = *reinterpret_cast<const u32x4*>(wsC + idx * 8);
         f.bt[k] = *reinterpret_cast<const u32x4*>(wsBt + idx * 8);
     }
-    // raw x rows t0 - (K-1) + rho, rho < Q + K - 1, 8 channels per piece
+    // G pieces of this wave's M tiles: row i, columns 8q .. 8q+7
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int I = unit_I(pw, u), s = unit_S(pw, u);
+        f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
+        if (I >= 0) {
+            const int i = 16 * I + (lane & 15), q = 4 * s + (lane >> 4);
+            if (8 * q <= i) {
+                v0 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q);
+                v1 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q + 4);
+            }
+        }
+        f.gm[u][0] = v0;
+        f.gm[u][1] = v1;
+    }
+    const int t = t0 + lane;
+    f.dt = t < bk.L ? bk.dt[t * bk.H] : 0.0f;
+    f.seq_j = f.seq_jm1 = 0;
+    if (HAS_SEQ) {
+        const int tc = t < bk.L ? t : bk.L - 1;
+        f.seq_j = bk.seq[tc];
+        f.seq_jm1 = bk.seq[tc > 0 ? tc - 1 : 0];
+    }
+}
+
+// raw x rows t0 - (K-1) + rho, rho < Q + K - 1, 8 channels per piece, handed to the 256
+// producer lanes as pieces ptid + 256 k; rows before token 0 come from the conv state
+template <int K, bool FUSED, bool HAS_SEQ>
+__device__ __forceinline__ void fetch_raw(const ChunkedArgs& a, const Blk& bk, int64_t b,
+                                          int64_t h, int64_t cn, int pw, int lane, Fetch& f) {
     constexpr int kRows = kQ + K - 1;
+    const int t0 = static_cast<int>(cn) * kQ;
+    const int ptid = pw * 64 + lane;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const int idx = ptid + 256 * k;
@@ -333,56 +376,43 @@ __device__ __forceinline__ void fetch(const ChunkedArgs& a, const Blk& bk, int64
         }
         f.x[k] = v;
     }
-    // G pieces of this wave's M tiles: row i, columns 8q .. 8q+7
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int I = unit_I(pw, u), s = unit_S(pw, u);
-        f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
-        if (I >= 0) {
-            const int i = 16 * I + (lane & 15), q = 4 * s + (lane >> 4);
-            if (8 * q <= i) {
-                v0 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q);
-                v1 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q + 4);
-            }
-        }
-        f.gm[u][0] = v0;
-        f.gm[u][1] = v1;
-    }
-    const int t = t0 + lane;
-    f.dt = t < bk.L ? bk.dt[t * bk.H] : 0.0f;
-    f.seq_j = f.seq_jm1 = f.seq_row = 0;
+    f.seq_row = 0;
     if (HAS_SEQ) {
-        const int tc = t < bk.L ? t : bk.L - 1;
-        f.seq_j = bk.seq[tc];
-        f.seq_jm1 = bk.seq[tc > 0 ? tc - 1 : 0];
         int tr = t0 - (K - 1) + ptid;
         tr = tr < 0 ? 0 : (tr >= bk.L ? bk.L - 1 : tr);
         f.seq_row = bk.seq[tr];
     }
 }
 
-// Producer work for chunk cn: drop the fetched tiles and raw x rows into `stage`, fetch
-// chunk cn+1, then compute the chunk scalars and this wave's M tiles.
+template <int K, bool HAS_SEQ>
+__device__ __forceinline__ void stage_raw(uint8_t* raw, int pw, int lane, const Fetch& f) {
+    constexpr int kRows = kQ + K - 1;
+    const int ptid = pw * 64 + lane;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int idx = ptid + 256 * k;
+        if (idx < kRows * 8) lds_st(raw, kRwX + sw_xr(idx >> 3, idx & 7), f.x[k]);
+    }
+    if (HAS_SEQ && ptid < kRows) reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = f.seq_row;
+}
+
+// Producer work for chunk cn (one chunk ahead of the consumers): drop the fetched tiles of
+// chunk cn into `stage` and the raw rows of chunk cn+1 into `raw_next`, fetch the tiles of
+// chunk cn+1 and the raw rows of chunk cn+2, then compute the chunk scalars and this wave's
+// M tiles.
 template <int K, bool FUSED, bool HAS_SEQ>
 __device__ __forceinline__ void produce(const ChunkedArgs& a, const Blk& bk, int64_t b,
                                         int64_t h, int64_t g, int64_t cn, int64_t nC,
                                         float Ah, int pw, int lane, uint8_t* stage,
-                                        uint8_t* ps, Fetch& f) {
-    constexpr int kRows = kQ + K - 1;
+                                        uint8_t* raw_next, uint8_t* ps, Fetch& f) {
     const int ptid = pw * 64 + lane;
-    // 1. fetched tiles -> LDS
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int idx = ptid + 256 * k;
         lds_st(stage, kStC + sw_c(idx >> 4, idx & 15), f.c[k]);
         lds_st(stage, kStBt + sw_bt(idx >> 3, idx & 7), f.bt[k]);
     }
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int idx = ptid + 256 * k;
-        if (idx < kRows * 8) lds_st(stage, kStXr + sw_xr(idx >> 3, idx & 7), f.x[k]);
-    }
-    if (HAS_SEQ && ptid < kRows) reinterpret_cast<int32_t*>(stage + kStSeq)[ptid] = f.seq_row;
+    if (cn + 1 < nC) stage_raw<K, HAS_SEQ>(raw_next, pw, lane, f);
     float* pcum = reinterpret_cast<float*>(ps);
     float* pdtv = pcum + kQ;
     int32_t* pr = reinterpret_cast<int32_t*>(pdtv + kQ);
@@ -390,10 +420,10 @@ __device__ __forceinline__ void produce(const ChunkedArgs& a, const Blk& bk, int
     const int32_t seq_j = f.seq_j, seq_jm1 = f.seq_jm1;
     const f32x4 gm[2][2] = {{f.gm[0][0], f.gm[0][1]}, {f.gm[1][0], f.gm[1][1]}};
 
-    // 2. fetch the next chunk while this one is computed
-    if (cn + 1 < nC) fetch<K, FUSED, HAS_SEQ>(a, bk, b, h, g, cn + 1, nC, pw, lane, f);
+    if (cn + 1 < nC) fetch_tiles<HAS_SEQ>(a, bk, b, g, cn + 1, nC, pw, lane, f);
+    if (cn + 2 < nC) fetch_raw<K, FUSED, HAS_SEQ>(a, bk, b, h, cn + 2, pw, lane, f);
 
-    // 3. chunk scalars, lane = token
+    // chunk scalars, lane = token
     const int t0 = static_cast<int>(cn) * kQ;
     const int j = lane;
     const float cum = wave_incl_sum(dtv * Ah);
@@ -413,7 +443,7 @@ __device__ __forceinline__ void produce(const ChunkedArgs& a, const Blk& bk, int
         if (j == 0) *reinterpret_cast<float*>(stage + kStDecay) = r_last < 0 ? __expf(cum_last) : 0.0f;
     }
 
-    // 4. this wave's M tiles: M[i][j] = G[i][j] exp(cum_i - cum_j) dt_j on r_i <= j <= i
+    // this wave's M tiles: M[i][j] = G[i][j] exp(cum_i - cum_j) dt_j on r_i <= j <= i
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int I = unit_I(pw, u), s = unit_S(pw, u);
@@ -445,10 +475,28 @@ __device__ __forceinline__ void produce(const ChunkedArgs& a, const Blk& bk, int
     }
 }
 
-// Consumer: the conv of channel p over tokens j0 .. j0+7 of the chunk from the staged raw
-// rows (row rho <-> token t0 - (K-1) + rho), rounded to bf16 -> one MFMA operand
+// Producer: store the y rows of a finished chunk (consumers left them in `yt`): whole 128-byte
+// token rows, two 16-byte pieces per producer lane
+__device__ __forceinline__ void store_y(const Blk& bk, const uint8_t* yt, int64_t cn, int pw,
+                                        int lane) {
+    const int t0 = static_cast<int>(cn) * kQ;
+    const int ptid = pw * 64 + lane;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int idx = ptid + 256 * k;  // 512 pieces: token idx >> 3, piece idx & 7
+        const int tok = idx >> 3, q = idx & 7;
+        const uint2 lo = lds_ld<uint2>(yt, sw_y(tok, 2 * q));
+        const uint2 hi = lds_ld<uint2>(yt, sw_y(tok, 2 * q + 1));
+        const int t = t0 + tok;
+        if (t < bk.L)
+            *reinterpret_cast<u32x4*>(bk.y + t * (bk.H * kP) + q * 8) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+}
+
+// Consumer: the conv of channel p over tokens j0 .. j0+7 of a chunk from its staged raw rows
+// (row rho <-> token t0 - (K-1) + rho), rounded to bf16 -> one MFMA operand
 template <int K, bool FUSED, bool HAS_SEQ>
-__device__ __forceinline__ bf16x8 conv_operand(const uint8_t* st, int p, int j0,
+__device__ __forceinline__ bf16x8 conv_operand(const uint8_t* raw, int p, int j0,
                                                const double (&cw)[K], double cbias, int act) {
     bf16x8 out;
     const int q = p >> 3, byte = (p & 7) * 2;
@@ -457,8 +505,8 @@ __device__ __forceinline__ bf16x8 conv_operand(const uint8_t* st, int p, int j0,
         int32_t id[8 + K - 1];
 #pragma unroll
         for (int tau = 0; tau < 8 + K - 1; ++tau) {
-            u[tau] = bf16_to_f32(lds_ld<uint16_t>(st, kStXr + sw_xr(j0 + tau, q) + byte));
-            id[tau] = HAS_SEQ ? lds_ld<int32_t>(st, kStSeq + (j0 + tau) * 4) : 0;
+            u[tau] = bf16_to_f32(lds_ld<uint16_t>(raw, kRwX + sw_xr(j0 + tau, q) + byte));
+            id[tau] = HAS_SEQ ? lds_ld<int32_t>(raw, kRwSeq + (j0 + tau) * 4) : 0;
         }
         double z[8];
 #pragma unroll
@@ -477,7 +525,7 @@ __device__ __forceinline__ bf16x8 conv_operand(const uint8_t* st, int p, int j0,
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            out[e] = __builtin_bit_cast(__bf16, lds_ld<uint16_t>(st, kStXr + sw_xr(j0 + e + K - 1, q) + byte));
+            out[e] = __builtin_bit_cast(__bf16, lds_ld<uint16_t>(raw, kRwX + sw_xr(j0 + e + K - 1, q) + byte));
     }
     return out;
 }
@@ -504,16 +552,18 @@ ssd_main_kernel(ChunkedArgs a) {
     bk.x = a.x + b * L * a.x_row + a.x_col0 + h * kP;
     bk.dt = a.dt + b * L * a.H + h;
     bk.seq = a.seq_idx ? a.seq_idx + b * L : nullptr;
+    bk.y = a.y + (b * L * a.H + h) * kP;
     bk.L = static_cast<int>(L);
     bk.x_row = static_cast<int>(a.x_row);
     bk.H = static_cast<int>(a.H);
-    uint16_t* y_base = a.y + (b * L * a.H + h) * kP;
-    const int y_row = bk.H * kP;
 
     // The two roles run separate loops (a wave's role never changes), so the register
     // allocator sees the consumer's state and the producer's in-flight fetch as disjoint
-    // live ranges.  Both loops pass the same number of block barriers: one after the
-    // producers' first chunk, then one per chunk.
+    // live ranges.  Both loops pass the same number of block barriers: two in the prologue
+    // (raw rows of chunk 0 staged; chunk 0 produced), then one per chunk.  Between two
+    // barriers the consumers contract chunk c from stage c&1, convolve chunk c+1 from raw slot
+    // (c+1)&1 and write y(c) to y slot c&1, while the producers store y(c-1) from y slot
+    // (c-1)&1, fill stage (c+1)&1 and raw slot c&1 (chunk c+2).
     if (consumer) {
         // state slice acc[t][r] = h[p][n], p = 16 wave + li, n = 32(t/2) + 8 g4 + 4(t%2) + r
         // (the MFMA row of tile t that lane group g4 holds)
@@ -543,10 +593,17 @@ ssd_main_kernel(ChunkedArgs a) {
                 acc[2 * m + 1] = v1;
             }
         }
-        __syncthreads();
+        __syncthreads();  // raw rows of chunk 0 staged
+        // X operands of chunk 0 (lane: channel p_own, tokens 32 s + 8 g4 .. +7)
+        bf16x8 xv[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            xv[s] = conv_operand<K, FUSED, HAS_SEQ>(sm + kOffRaw, p_own, 32 * s + 8 * g4, cw, cbias, a.act);
+        __syncthreads();  // stage 0 and the raw rows of chunk 1 ready; raw slot 0 free
+
         for (int64_t cn = 0; cn < nC; ++cn) {
             const uint8_t* st = sm + (cn & 1) * kStageBytes;
-            const int t0 = static_cast<int>(cn) * kQ;
+            uint8_t* yt = sm + kOffY + (cn & 1) * kYBytes;
             float eI[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
@@ -559,10 +616,6 @@ ssd_main_kernel(ChunkedArgs a) {
                 for (int e = 0; e < 4; ++e) { wj[s][e] = w0[e]; wj[s][4 + e] = w1[e]; }
             }
             const float decay = lds_ld<float>(st, kStDecay);
-            bf16x8 xv[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                xv[s] = conv_operand<K, FUSED, HAS_SEQ>(st, p_own, 32 * s + 8 * g4, cw, cbias, a.act);
 
             // Y^T[p][i], p = 16 wave + 4 g4 + r, i = 16 I + li
             f32x4 yo[4], yi[4];
@@ -600,16 +653,6 @@ ssd_main_kernel(ChunkedArgs a) {
                     }
                 }
             }
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const int t = t0 + 16 * I + li;
-                if (t < bk.L) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
-                    pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
-                    *reinterpret_cast<uint2*>(y_base + t * y_row + 16 * wave + 4 * g4) = pk;
-                }
-            }
             // state update: h^T[n][p] = decay h^T + B^T (W o X)
 #pragma unroll
             for (int t = 0; t < 8; ++t) acc[t] *= decay;
@@ -628,6 +671,21 @@ ssd_main_kernel(ChunkedArgs a) {
                     acc[t] = mfma(bv, bl, acc[t]);
                 }
             }
+            // the next chunk's X operands (independent of the contractions above)
+            if (cn + 1 < nC) {
+                const uint8_t* raw = sm + kOffRaw + ((cn + 1) & 1) * kRawBytes;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    xv[s] = conv_operand<K, FUSED, HAS_SEQ>(raw, p_own, 32 * s + 8 * g4, cw, cbias, a.act);
+            }
+            // y tile of this chunk -> LDS (the producers store it next iteration)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                uint2 pk;
+                pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
+                pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
+                lds_st(yt, sw_y(16 * I + li, 4 * wave + g4), pk);
+            }
             __syncthreads();
         }
         if (a.final_state) {
@@ -640,17 +698,25 @@ ssd_main_kernel(ChunkedArgs a) {
         }
     } else {
         const int pw = wave - 4;
-        uint8_t* ps = sm + kPrivS + pw * kPsBytes;
+        uint8_t* ps = sm + kOffPs + pw * kPsBytes;
         Fetch f;
-        fetch<K, FUSED, HAS_SEQ>(a, bk, b, h, g, 0, nC, pw, lane, f);
-        produce<K, FUSED, HAS_SEQ>(a, bk, b, h, g, 0, nC, Ah, pw, lane, sm, ps, f);
+        fetch_raw<K, FUSED, HAS_SEQ>(a, bk, b, h, 0, pw, lane, f);
+        fetch_tiles<HAS_SEQ>(a, bk, b, g, 0, nC, pw, lane, f);
+        stage_raw<K, HAS_SEQ>(sm + kOffRaw, pw, lane, f);
+        if (nC > 1) fetch_raw<K, FUSED, HAS_SEQ>(a, bk, b, h, 1, pw, lane, f);
+        __syncthreads();  // raw rows of chunk 0 staged
+        produce<K, FUSED, HAS_SEQ>(a, bk, b, h, g, 0, nC, Ah, pw, lane, sm,
+                                   sm + kOffRaw + kRawBytes, ps, f);
         __syncthreads();
         for (int64_t cn = 0; cn < nC; ++cn) {
+            if (cn > 0) store_y(bk, sm + kOffY + ((cn - 1) & 1) * kYBytes, cn - 1, pw, lane);
             if (cn + 1 < nC)
                 produce<K, FUSED, HAS_SEQ>(a, bk, b, h, g, cn + 1, nC, Ah, pw, lane,
-                                           sm + ((cn + 1) & 1) * kStageBytes, ps, f);
+                                           sm + ((cn + 1) & 1) * kStageBytes,
+                                           sm + kOffRaw + ((cn + 2) & 1) * kRawBytes, ps, f);
             __syncthreads();
         }
+        store_y(bk, sm + kOffY + ((nC - 1) & 1) * kYBytes, nC - 1, pw, lane);
     }
 
     // ---- final conv state F = u[L .. L+K-2] for this head's x channels and for slice h of
