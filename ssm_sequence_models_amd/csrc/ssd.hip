@@ -71,14 +71,19 @@ __device__ __forceinline__ void lds_st(uint8_t* base, int off, const T& v) {
     *reinterpret_cast<T*>(base + off) = v;
 }
 
-// v = hi + lo, hi = rne(v), lo = rne(v - hi)
+// v = hi + lo, hi = rne(v), lo = rne(v - hi): one paired conversion for two his, their
+// widening by shift / mask, two exact subtractions and one paired conversion for the los
 __device__ __forceinline__ void split_hilo(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 h = static_cast<__bf16>(v[e]);
-        hi[e] = h;
-        lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(h));
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t hp = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xFFFF0000u);
+        h[e] = hp;
+        l[e] = pack_bf16x2(v[2 * e] - h0, v[2 * e + 1] - h1);
     }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // Inclusive prefix over the 64 lanes of a wavefront with DPP: row_shr 1/2/4/8 inside each
@@ -112,15 +117,19 @@ __device__ __forceinline__ int64_t ws_unit(const ChunkedArgs& a, int64_t b, int6
 // prep: conv + bf16 rounding of the B / C channels of one (row, chunk, group), then
 // C token-major, B channel-major and G = C B^T into the workspace
 // =======================================================================================
-constexpr int kPrepStride = kN * 2 + 16;  // [token][n] bf16 rows in LDS
+constexpr int kPrepStride = kN * 2 + 16;   // [token][n] bf16 rows in LDS (conv outputs)
+constexpr int kPrepRaw = 2 * kN * 2 + 16;  // [row][B n | C n] bf16 raw input rows in LDS
+constexpr int kPrepLds = 2 * kQ * kPrepStride + (kQ + kKmax - 1) * kPrepRaw + 72 * 4;
 
 template <int K>
 __global__ void __launch_bounds__(kPrepThreads)
 ssd_prep_kernel(ChunkedArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t sm[2 * kQ * kPrepStride + 128 * 4];
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kPrepLds];
+    constexpr int kRows = kQ + K - 1;
     uint8_t* sB = sm;
     uint8_t* sC = sm + kQ * kPrepStride;
-    int32_t* sSeq = reinterpret_cast<int32_t*>(sm + 2 * kQ * kPrepStride);
+    uint8_t* sRaw = sm + 2 * kQ * kPrepStride;
+    int32_t* sSeq = reinterpret_cast<int32_t*>(sRaw + (kQ + kKmax - 1) * kPrepRaw);
 
     const int tid = threadIdx.x;
     const int64_t cn = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -129,59 +138,78 @@ ssd_prep_kernel(ChunkedArgs a) {
     const int64_t t0 = cn * kQ;
     const bool has_seq = a.seq_idx != nullptr;
 
-    if (has_seq && tid < kQ + K - 1) {
+    if (has_seq && tid < kRows) {
         int64_t t = t0 - (K - 1) + tid;
         t = t < 0 ? 0 : (t >= L ? L - 1 : t);
         sSeq[tid] = a.seq_idx[b * L + t];
     }
+    // raw rows t0-(K-1) .. t0+Q-1 of the group's B and C channels, 16 bytes per load
+    // (B and C channels of a group are each 128 contiguous bf16 of a token row)
+    for (int idx = tid; idx < kRows * 32; idx += kPrepThreads) {
+        const int rho = idx >> 5, piece = idx & 31;
+        const bool isC = piece >= 16;
+        const int n0 = (piece & 15) * 8;
+        const int64_t t = t0 - (K - 1) + rho;
+        const int64_t row = isC ? a.c_row : a.b_row;
+        const int64_t col = (isC ? a.c_col0 : a.b_col0) + g * kN + n0;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (t >= 0 && t < L) {
+            v = *reinterpret_cast<const u32x4*>((isC ? a.csrc : a.bsrc) + (b * L + t) * row + col);
+        } else if (t < 0 && a.fused_conv && a.conv_init) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = a.conv_init[(b * a.C_conv + col + 2 * e) * (K - 1) + (K - 1) + t];
+                const uint32_t hi = a.conv_init[(b * a.C_conv + col + 2 * e + 1) * (K - 1) + (K - 1) + t];
+                w4[e] = lo | (hi << 16);
+            }
+            v = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+        lds_st(sRaw, rho * kPrepRaw + piece * 16, v);
+    }
     __syncthreads();
 
+    // one channel per thread (B channels 0..127, then C channels), 8 tokens per batch
     for (int ch = tid; ch < 2 * kN; ch += kPrepThreads) {
         const bool isC = ch >= kN;
         const int n = isC ? ch - kN : ch;
-        const int64_t row = isC ? a.c_row : a.b_row;
         const int64_t col = (isC ? a.c_col0 : a.b_col0) + g * kN + n;
-        const uint16_t* src = (isC ? a.csrc : a.bsrc) + b * L * row + col;
         uint8_t* dst = isC ? sC : sB;
         if (a.fused_conv) {
             double w[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) w[k] = a.conv_w[col * K + k];
             const double bias = a.conv_b ? a.conv_b[col] : 0.0f;
-            double win[K];      // oldest -> newest; win[K-1] is the current token
-            int32_t idw[K];
+            for (int j0 = 0; j0 < kQ; j0 += 8) {
+                double u[8 + K - 1];
+                int32_t id[8 + K - 1];
 #pragma unroll
-            for (int k = 0; k < K - 1; ++k) {
-                const int64_t t = t0 - (K - 1) + k;
-                float v = 0.0f;
-                if (t >= 0)
-                    v = bf16_to_f32(src[t * row]);
-                else if (a.conv_init)
-                    v = bf16_to_f32(a.conv_init[(b * a.C_conv + col) * (K - 1) + (K - 1) + t]);
-                win[k] = v;
-                idw[k] = has_seq ? sSeq[k] : 0;
-            }
-            for (int j = 0; j < kQ; ++j) {
-                const int64_t t = t0 + j;
-                win[K - 1] = t < L ? bf16_to_f32(src[t * row]) : 0.0f;
-                idw[K - 1] = has_seq ? sSeq[j + K - 1] : 0;
-                double z = bias;
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const double tap = (!has_seq || idw[k] == idw[K - 1]) ? win[k] : 0.0;
-                    z = fma(w[k], tap, z);
+                for (int tau = 0; tau < 8 + K - 1; ++tau) {
+                    u[tau] = bf16_to_f32(lds_ld<uint16_t>(sRaw, (j0 + tau) * kPrepRaw + ch * 2));
+                    id[tau] = has_seq ? sSeq[j0 + tau] : 0;
                 }
-                const uint16_t v = t < L ? act_to_bf16(z, a.act) : uint16_t(0);
-                *reinterpret_cast<uint16_t*>(dst + j * kPrepStride + n * 2) = v;
+                double z[8];
 #pragma unroll
-                for (int k = 0; k < K - 1; ++k) { win[k] = win[k + 1]; idw[k] = idw[k + 1]; }
+                for (int e = 0; e < 8; ++e) {
+                    z[e] = bias;
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        const double tap = (!has_seq || id[e + k] == id[e + K - 1]) ? u[e + k] : 0.0;
+                        z[e] = fma(w[k], tap, z[e]);
+                    }
+                }
+                uint16_t o[8];
+                act_to_bf16_batch(z, a.act, o);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t v = t0 + j0 + e < L ? o[e] : uint16_t(0);
+                    *reinterpret_cast<uint16_t*>(dst + (j0 + e) * kPrepStride + n * 2) = v;
+                }
             }
         } else {
-            for (int j = 0; j < kQ; ++j) {
-                const int64_t t = t0 + j;
-                const uint16_t v = t < L ? src[t * row] : uint16_t(0);
-                *reinterpret_cast<uint16_t*>(dst + j * kPrepStride + n * 2) = v;
-            }
+            for (int j = 0; j < kQ; ++j)
+                *reinterpret_cast<uint16_t*>(dst + j * kPrepStride + n * 2) =
+                    lds_ld<uint16_t>(sRaw, (j + K - 1) * kPrepRaw + ch * 2);
         }
     }
     __syncthreads();
@@ -207,19 +235,24 @@ ssd_prep_kernel(ChunkedArgs a) {
         *reinterpret_cast<u32x4*>(wsBt + unit * kWsBt + n * kQ + jq * 8) =
             u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
-    // G = C B^T for the 16x16 tiles on or below the diagonal; wave w owns rows 16w..16w+15
+    // G = C B^T with the causal mask applied (G[i][j] = 0 for j > i), all 16 tiles written;
+    // wave w owns rows 16w .. 16w+15
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
-    for (int jt = 0; jt <= wave; ++jt) {
+    for (int jt = 0; jt < kQ / 16; ++jt) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (jt <= wave) {
 #pragma unroll
-        for (int m = 0; m < kN / 32; ++m) {
-            const bf16x8 av = lds_ld<bf16x8>(sC, (16 * wave + li) * kPrepStride + (32 * m + 8 * g4) * 2);
-            const bf16x8 bv = lds_ld<bf16x8>(sB, (16 * jt + li) * kPrepStride + (32 * m + 8 * g4) * 2);
-            acc = mfma(av, bv, acc);
+            for (int m = 0; m < kN / 32; ++m) {
+                const bf16x8 av = lds_ld<bf16x8>(sC, (16 * wave + li) * kPrepStride + (32 * m + 8 * g4) * 2);
+                const bf16x8 bv = lds_ld<bf16x8>(sB, (16 * jt + li) * kPrepStride + (32 * m + 8 * g4) * 2);
+                acc = mfma(av, bv, acc);
+            }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            wsG[unit * kWsG + (16 * wave + 4 * g4 + r) * kQ + 16 * jt + li] = acc[r];
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * wave + 4 * g4 + r, j = 16 * jt + li;
+            wsG[unit * kWsG + i * kQ + j] = j <= i ? acc[r] : 0.0f;
+        }
     }
 }
 
@@ -269,15 +302,26 @@ __device__ __forceinline__ int sw_xr(int row, int q) {
 // y tile: 16 lanes of a ds_write_b64 write 16 tokens at the same 8-byte column
 __device__ __forceinline__ int sw_y(int tok, int slot8) { return tok * 128 + ((slot8 ^ (tok & 15)) << 3); }
 
-// M tiles computed by each producer wave: (row block I of 16, column half s of 32); the six
-// tiles cover j <= i
-__device__ __forceinline__ int unit_I(int pw, int u) {
-    constexpr int8_t t[4][2] = {{0, 3}, {1, 2}, {2, -1}, {3, -1}};
-    return t[pw][u];
+// M tiles computed by each producer wave pw (uniform): unit u is the 16 x 32 tile (row
+// block I, column half S); the six tiles cover j <= i.
+//   pw 0: (0,0) (3,0)   pw 1: (1,0) (2,1)   pw 2: (2,0)   pw 3: (3,1)
+__device__ __forceinline__ int unit_I(int pw, int u) { return u == 0 ? pw : 3 - pw; }
+__device__ __forceinline__ int unit_S(int pw, int u) { return u == 0 ? (pw == 3 ? 1 : 0) : pw; }
+__device__ __forceinline__ bool unit_valid(int pw, int u) { return u == 0 || pw < 2; }
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores past
+// it are dropped by the hardware range check, which handles the ragged last chunk.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFFLL ? 0x7FFFFFFFLL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
+                                             0x00020000);
 }
-__device__ __forceinline__ int unit_S(int pw, int u) {
-    constexpr int8_t t[4][2] = {{0, 0}, {0, 1}, {0, -1}, {1, -1}};
-    return t[pw][u];
+__device__ __forceinline__ u32x4 bload128(Rsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload32(Rsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 // Per-block bases; everything inside one (row, head) is addressed with 32-bit offsets
@@ -287,81 +331,94 @@ struct Blk {
     const float* dt;        // dt of this head at token 0 of this row
     const int32_t* seq;     // seq_idx of this row, or NULL
     uint16_t* y;            // y channel 0 of this head at token 0 of this row
+    const uint16_t* wsC;    // workspace tiles of (this row, chunk 0, this group)
+    const uint16_t* wsBt;
+    const float* wsG;
+    int64_t ws_step;        // elements between consecutive chunks' tiles (G units)
     int L, x_row, H;
 };
 
-// Registers a producer lane carries between fetching and staging.  The tiles (C, B^T,
-// G, dt, ids) belong to chunk k, the raw x rows to chunk k+1.
+// Per-lane constant byte offsets of the producer's loads and stores
+struct POff {
+    uint32_t tile;          // C and B^T tile pieces ptid (+ 4096 k)
+    uint32_t g[2];          // G piece of unit u: row i, columns 8q .. 8q+7
+    uint32_t x[3];          // raw x piece ptid + 256 k: row rho, 8 channels q
+    uint32_t dt;            // token = lane
+    uint32_t y[2];          // y piece ptid + 256 k: token, 8 channels
+};
+
+// Registers a producer lane carries from issuing its loads to staging them (one chunk
+// later): the tiles, dt and ids of chunk k and the raw x rows of chunk k+1.  Two of these
+// alternate, so loads stay in flight across the block barrier.
 struct Fetch {
     u32x4 c[4];
     u32x4 bt[4];
-    f32x4 gm[2][2];
-    float dt;
-    int32_t seq_j, seq_jm1;
+    u32x4 gm[2][2];
+    uint32_t dt;
+    int32_t seq_j, seq_prev;
     u32x4 x[3];
     int32_t seq_row;
 };
 
-template <bool HAS_SEQ>
-__device__ __forceinline__ void fetch_tiles(const ChunkedArgs& a, const Blk& bk, int64_t b,
-                                            int64_t g, int64_t cn, int64_t nC, int pw, int lane,
-                                            Fetch& f) {
-    const int t0 = static_cast<int>(cn) * kQ;
-    const int64_t unit = ws_unit(a, b, cn, g, nC);
-    const uint16_t* ws = static_cast<const uint16_t*>(a.workspace);
-    const uint16_t* wsC = ws + unit * kWsC;
-    const uint16_t* wsBt = ws + a.B * nC * a.G * kWsC + unit * kWsBt;
-    const float* wsG = reinterpret_cast<const float*>(ws + a.B * nC * a.G * (kWsC + kWsBt)) +
-                       unit * kWsG;
-    const int ptid = pw * 64 + lane;
+// Loads for chunk k (tiles, dt, ids) and, if present, the raw rows of chunk k+1 (whose first
+// row t0 + Q - (K-1) >= 0).
+template <int K, bool HAS_SEQ>
+__device__ __forceinline__ void fetch(const Blk& bk, const POff& o, int64_t k, int64_t nC,
+                                      int pw, int lane, Fetch& f) {
+    constexpr int kRows = kQ + K - 1;
+    const int t0 = static_cast<int>(k) * kQ;
+    const Rsrc rc = make_rsrc(bk.wsC + k * bk.ws_step * kWsC, kWsC * 2);
+    const Rsrc rb = make_rsrc(bk.wsBt + k * bk.ws_step * kWsBt, kWsBt * 2);
+    const Rsrc rg = make_rsrc(bk.wsG + k * bk.ws_step * kWsG, kWsG * 4);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int idx = ptid + 256 * k;
-        f.c[k] = *reinterpret_cast<const u32x4*>(wsC + idx * 8);
-        f.bt[k] = *reinterpret_cast<const u32x4*>(wsBt + idx * 8);
+    for (int q = 0; q < 4; ++q) {
+        f.c[q] = bload128(rc, o.tile + 4096 * q);
+        f.bt[q] = bload128(rb, o.tile + 4096 * q);
     }
-    // G pieces of this wave's M tiles: row i, columns 8q .. 8q+7
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int I = unit_I(pw, u), s = unit_S(pw, u);
-        f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
-        if (I >= 0) {
-            const int i = 16 * I + (lane & 15), q = 4 * s + (lane >> 4);
-            if (8 * q <= i) {
-                v0 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q);
-                v1 = *reinterpret_cast<const f32x4*>(wsG + i * kQ + 8 * q + 4);
-            }
+        if (unit_valid(pw, u)) {
+            f.gm[u][0] = bload128(rg, o.g[u]);
+            f.gm[u][1] = bload128(rg, o.g[u] + 16);
         }
-        f.gm[u][0] = v0;
-        f.gm[u][1] = v1;
     }
-    const int t = t0 + lane;
-    f.dt = t < bk.L ? bk.dt[t * bk.H] : 0.0f;
-    f.seq_j = f.seq_jm1 = 0;
+    const Rsrc rd = make_rsrc(bk.dt + static_cast<int64_t>(t0) * bk.H, static_cast<int64_t>(bk.L - t0) * bk.H * 4);
+    f.dt = bload32(rd, o.dt);
     if (HAS_SEQ) {
-        const int tc = t < bk.L ? t : bk.L - 1;
-        f.seq_j = bk.seq[tc];
-        f.seq_jm1 = bk.seq[tc > 0 ? tc - 1 : 0];
+        const Rsrc rs = make_rsrc(bk.seq + t0, static_cast<int64_t>(bk.L - t0) * 4);
+        f.seq_j = static_cast<int32_t>(bload32(rs, lane * 4));
+        f.seq_prev = t0 > 0 ? bk.seq[t0 - 1] : 0;
+    }
+    if (k + 1 < nC) {
+        const int r0 = t0 + kQ - (K - 1);
+        const Rsrc rx = make_rsrc(bk.x + static_cast<int64_t>(r0) * bk.x_row,
+                                  static_cast<int64_t>(bk.L - r0) * bk.x_row * 2);
+        const int ptid = pw * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            if (ptid + 256 * q < kRows * 8) f.x[q] = bload128(rx, o.x[q]);
+        if (HAS_SEQ && ptid < kRows) {
+            const Rsrc rs = make_rsrc(bk.seq + r0, static_cast<int64_t>(bk.L - r0) * 4);
+            f.seq_row = static_cast<int32_t>(bload32(rs, ptid * 4));
+        }
     }
 }
 
-// raw x rows t0 - (K-1) + rho, rho < Q + K - 1, 8 channels per piece, handed to the 256
-// producer lanes as pieces ptid + 256 k; rows before token 0 come from the conv state
+// raw x rows of chunk 0 (rows before token 0 come from the conv state), straight to LDS
 template <int K, bool FUSED, bool HAS_SEQ>
-__device__ __forceinline__ void fetch_raw(const ChunkedArgs& a, const Blk& bk, int64_t b,
-                                          int64_t h, int64_t cn, int pw, int lane, Fetch& f) {
+__device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk& bk, int64_t b,
+                                                int64_t h, int pw, int lane, uint8_t* raw) {
     constexpr int kRows = kQ + K - 1;
-    const int t0 = static_cast<int>(cn) * kQ;
     const int ptid = pw * 64 + lane;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const int idx = ptid + 256 * k;
-        u32x4 v = {0u, 0u, 0u, 0u};
         if (idx < kRows * 8) {
             const int rho = idx >> 3, q = idx & 7;
-            const int t = t0 - (K - 1) + rho;
+            const int t = rho - (K - 1);
+            u32x4 v = {0u, 0u, 0u, 0u};
             if (t >= 0 && t < bk.L) {
-                v = *reinterpret_cast<const u32x4*>(bk.x + t * bk.x_row + q * 8);
+                v = *reinterpret_cast<const u32x4*>(bk.x + static_cast<int64_t>(t) * bk.x_row + q * 8);
             } else if (FUSED && t < 0 && a.conv_init) {
                 const int64_t cc0 = a.x_col0 + h * kP + q * 8;
                 uint32_t w4[4];
@@ -373,123 +430,114 @@ __device__ __forceinline__ void fetch_raw(const ChunkedArgs& a, const Blk& bk, i
                 }
                 v = u32x4{w4[0], w4[1], w4[2], w4[3]};
             }
+            lds_st(raw, kRwX + sw_xr(rho, q), v);
         }
-        f.x[k] = v;
     }
-    f.seq_row = 0;
-    if (HAS_SEQ) {
-        int tr = t0 - (K - 1) + ptid;
+    if (HAS_SEQ && ptid < kRows) {
+        int tr = ptid - (K - 1);
         tr = tr < 0 ? 0 : (tr >= bk.L ? bk.L - 1 : tr);
-        f.seq_row = bk.seq[tr];
+        reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = bk.seq[tr];
     }
 }
 
+// Stage chunk k's tiles (stage k&1) and, if present, chunk k+1's raw rows (raw slot (k+1)&1)
 template <int K, bool HAS_SEQ>
-__device__ __forceinline__ void stage_raw(uint8_t* raw, int pw, int lane, const Fetch& f) {
+__device__ __forceinline__ void stage(const Fetch& f, int64_t k, int64_t nC, int pw, int lane,
+                                      uint8_t* st, uint8_t* raw) {
     constexpr int kRows = kQ + K - 1;
     const int ptid = pw * 64 + lane;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int idx = ptid + 256 * k;
-        if (idx < kRows * 8) lds_st(raw, kRwX + sw_xr(idx >> 3, idx & 7), f.x[k]);
+    for (int q = 0; q < 4; ++q) {
+        const int idx = ptid + 256 * q;
+        lds_st(st, kStC + sw_c(idx >> 4, idx & 15), f.c[q]);
+        lds_st(st, kStBt + sw_bt(idx >> 3, idx & 7), f.bt[q]);
     }
-    if (HAS_SEQ && ptid < kRows) reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = f.seq_row;
+    if (k + 1 < nC) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int idx = ptid + 256 * q;
+            if (idx < kRows * 8) lds_st(raw, kRwX + sw_xr(idx >> 3, idx & 7), f.x[q]);
+        }
+        if (HAS_SEQ && ptid < kRows) reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = f.seq_row;
+    }
 }
 
-// Producer work for chunk cn (one chunk ahead of the consumers): drop the fetched tiles of
-// chunk cn into `stage` and the raw rows of chunk cn+1 into `raw_next`, fetch the tiles of
-// chunk cn+1 and the raw rows of chunk cn+2, then compute the chunk scalars and this wave's
-// M tiles.
-template <int K, bool FUSED, bool HAS_SEQ>
-__device__ __forceinline__ void produce(const ChunkedArgs& a, const Blk& bk, int64_t b,
-                                        int64_t h, int64_t g, int64_t cn, int64_t nC,
-                                        float Ah, int pw, int lane, uint8_t* stage,
-                                        uint8_t* raw_next, uint8_t* ps, Fetch& f) {
-    const int ptid = pw * 64 + lane;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int idx = ptid + 256 * k;
-        lds_st(stage, kStC + sw_c(idx >> 4, idx & 15), f.c[k]);
-        lds_st(stage, kStBt + sw_bt(idx >> 3, idx & 7), f.bt[k]);
-    }
-    if (cn + 1 < nC) stage_raw<K, HAS_SEQ>(raw_next, pw, lane, f);
+// Chunk scalars and this wave's M tiles for chunk k, from the fetched dt / ids / G pieces:
+//   cum2_j = log2(e) * sum_{tau<=j} dt_tau A (wave prefix scan), r_j = last reset <= j,
+//   E_i = 2^cum2_i, W_j = 2^(cum2_last - cum2_j) dt_j, decay = 2^cum2_last,
+//   M[i][j] = G[i][j] 2^(cum2_i - cum2_j) dt_j on r_i <= j <= i (G is 0 above the diagonal)
+template <bool HAS_SEQ>
+__device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, float Ah2,
+                                              int pw, int lane, uint8_t* st, uint8_t* ps) {
     float* pcum = reinterpret_cast<float*>(ps);
     float* pdtv = pcum + kQ;
     int32_t* pr = reinterpret_cast<int32_t*>(pdtv + kQ);
-    const float dtv = f.dt;
-    const int32_t seq_j = f.seq_j, seq_jm1 = f.seq_jm1;
-    const f32x4 gm[2][2] = {{f.gm[0][0], f.gm[0][1]}, {f.gm[1][0], f.gm[1][1]}};
-
-    if (cn + 1 < nC) fetch_tiles<HAS_SEQ>(a, bk, b, g, cn + 1, nC, pw, lane, f);
-    if (cn + 2 < nC) fetch_raw<K, FUSED, HAS_SEQ>(a, bk, b, h, cn + 2, pw, lane, f);
-
-    // chunk scalars, lane = token
-    const int t0 = static_cast<int>(cn) * kQ;
+    const int t0 = static_cast<int>(k) * kQ;
     const int j = lane;
-    const float cum = wave_incl_sum(dtv * Ah);
-    int rst = -1;
-    if (HAS_SEQ && t0 + j < bk.L && t0 + j > 0 && seq_j != seq_jm1) rst = j;
-    const int r = HAS_SEQ ? wave_incl_max(rst) : -1;
+    const float dtv = __uint_as_float(f.dt);
+    const float cum = wave_incl_sum(dtv * Ah2);
+    int r = -1;
+    if (HAS_SEQ) {
+        int32_t sjm1 = __shfl_up(f.seq_j, 1);
+        if (lane == 0) sjm1 = f.seq_prev;
+        const int rst = (t0 + j < L && t0 + j > 0 && f.seq_j != sjm1) ? j : -1;
+        r = wave_incl_max(rst);
+    }
     pcum[j] = cum;
     pdtv[j] = dtv;
-    pr[j] = r;
+    if (HAS_SEQ) pr[j] = r;
     if (pw == 0) {
         const float cum_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kQ - 1));
-        const int r_last = __builtin_amdgcn_readlane(r, kQ - 1);
-        float* sE = reinterpret_cast<float*>(stage + kStE);
-        float* sW = reinterpret_cast<float*>(stage + kStW);
-        sE[j] = r < 0 ? __expf(cum) : 0.0f;
-        sW[j] = j >= r_last ? __expf(cum_last - cum) * dtv : 0.0f;
-        if (j == 0) *reinterpret_cast<float*>(stage + kStDecay) = r_last < 0 ? __expf(cum_last) : 0.0f;
+        const int r_last = HAS_SEQ ? __builtin_amdgcn_readlane(r, kQ - 1) : -1;
+        float* sE = reinterpret_cast<float*>(st + kStE);
+        float* sW = reinterpret_cast<float*>(st + kStW);
+        sE[j] = r < 0 ? __builtin_amdgcn_exp2f(cum) : 0.0f;
+        sW[j] = j >= r_last ? __builtin_amdgcn_exp2f(cum_last - cum) * dtv : 0.0f;
+        if (j == 0) *reinterpret_cast<float*>(st + kStDecay) = r_last < 0 ? __builtin_amdgcn_exp2f(cum_last) : 0.0f;
     }
-
-    // this wave's M tiles: M[i][j] = G[i][j] exp(cum_i - cum_j) dt_j on r_i <= j <= i
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int I = unit_I(pw, u), s = unit_S(pw, u);
-        if (I < 0) continue;
-        const int i = 16 * I + (lane & 15), q = 4 * s + (lane >> 4), j0 = 8 * q;
+        if (!unit_valid(pw, u)) continue;
+        const int I = unit_I(pw, u), S = unit_S(pw, u);
+        const bool diag = 32 * S + 31 > 16 * I;
+        const int i = 16 * I + (lane & 15), q = 4 * S + (lane >> 4), j0 = 8 * q;
+        const float ci = pcum[i];
+        const int ri = HAS_SEQ ? pr[i] : -1;
+        const f32x4 cj0 = lds_ld<f32x4>(ps, j0 * 4), cj1 = lds_ld<f32x4>(ps, j0 * 4 + 16);
+        const f32x4 dj0 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4), dj1 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4 + 16);
         float mv[8];
-        if (j0 <= i) {
-            const float ci = pcum[i];
-            const int ri = pr[i];
-            const f32x4 cj0 = lds_ld<f32x4>(ps, j0 * 4), cj1 = lds_ld<f32x4>(ps, j0 * 4 + 16);
-            const f32x4 dj0 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4), dj1 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4 + 16);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float cj = e < 4 ? cj0[e] : cj1[e - 4];
-                const float dj = e < 4 ? dj0[e] : dj1[e - 4];
-                const float gv = gm[u][e >> 2][e & 3];
-                const int jj = j0 + e;
-                const float m = gv * __expf(ci - cj) * dj;
-                mv[e] = (jj <= i && jj >= ri) ? m : 0.0f;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mv[e] = 0.0f;
+        for (int e = 0; e < 8; ++e) {
+            const float cj = e < 4 ? cj0[e] : cj1[e - 4];
+            const float dj = e < 4 ? dj0[e] : dj1[e - 4];
+            const float gv = __uint_as_float(f.gm[u][e >> 2][e & 3]);
+            float m = gv * __builtin_amdgcn_exp2f(ci - cj) * dj;
+            if (diag) m = j0 + e <= i ? m : 0.0f;   // 0 * inf above the diagonal
+            if (HAS_SEQ) m = j0 + e >= ri ? m : 0.0f;
+            mv[e] = m;
         }
         bf16x8 hi, lo;
         split_hilo(mv, hi, lo);
-        lds_st(stage, kStMhi + sw_8(i, q), hi);
-        lds_st(stage, kStMlo + sw_8(i, q), lo);
+        lds_st(st, kStMhi + sw_8(i, q), hi);
+        lds_st(st, kStMlo + sw_8(i, q), lo);
     }
 }
 
-// Producer: store the y rows of a finished chunk (consumers left them in `yt`): whole 128-byte
-// token rows, two 16-byte pieces per producer lane
-__device__ __forceinline__ void store_y(const Blk& bk, const uint8_t* yt, int64_t cn, int pw,
-                                        int lane) {
-    const int t0 = static_cast<int>(cn) * kQ;
+// Store the y rows of chunk k (left in `yt` by the consumers): whole 128-byte token rows,
+// two 16-byte pieces per producer lane; rows past the end are dropped by the range check
+__device__ __forceinline__ void store_y(const Blk& bk, const POff& o, const uint8_t* yt,
+                                        int64_t k, int pw, int lane) {
+    const int t0 = static_cast<int>(k) * kQ;
+    const Rsrc ry = make_rsrc(bk.y + static_cast<int64_t>(t0) * bk.H * kP,
+                              static_cast<int64_t>(bk.L - t0) * bk.H * kP * 2);
     const int ptid = pw * 64 + lane;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int idx = ptid + 256 * k;  // 512 pieces: token idx >> 3, piece idx & 7
-        const int tok = idx >> 3, q = idx & 7;
-        const uint2 lo = lds_ld<uint2>(yt, sw_y(tok, 2 * q));
-        const uint2 hi = lds_ld<uint2>(yt, sw_y(tok, 2 * q + 1));
-        const int t = t0 + tok;
-        if (t < bk.L)
-            *reinterpret_cast<u32x4*>(bk.y + t * (bk.H * kP) + q * 8) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    for (int q = 0; q < 2; ++q) {
+        const int idx = ptid + 256 * q;
+        const int tok = idx >> 3, c8 = idx & 7;
+        const uint2 lo = lds_ld<uint2>(yt, sw_y(tok, 2 * c8));
+        const uint2 hi = lds_ld<uint2>(yt, sw_y(tok, 2 * c8 + 1));
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo.x, lo.y, hi.x, hi.y}, ry, o.y[q], 0, 0);
     }
 }
 
@@ -553,6 +601,15 @@ ssd_main_kernel(ChunkedArgs a) {
     bk.dt = a.dt + b * L * a.H + h;
     bk.seq = a.seq_idx ? a.seq_idx + b * L : nullptr;
     bk.y = a.y + (b * L * a.H + h) * kP;
+    {
+        const uint16_t* ws = static_cast<const uint16_t*>(a.workspace);
+        const int64_t units = a.B * nC * a.G;
+        const int64_t unit0 = ws_unit(a, b, 0, g, nC);
+        bk.wsC = ws + unit0 * kWsC;
+        bk.wsBt = ws + units * kWsC + unit0 * kWsBt;
+        bk.wsG = reinterpret_cast<const float*>(ws + units * (kWsC + kWsBt)) + unit0 * kWsG;
+        bk.ws_step = a.G;
+    }
     bk.L = static_cast<int>(L);
     bk.x_row = static_cast<int>(a.x_row);
     bk.H = static_cast<int>(a.H);
@@ -697,26 +754,62 @@ ssd_main_kernel(ChunkedArgs a) {
             }
         }
     } else {
-        const int pw = wave - 4;
+        const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
         uint8_t* ps = sm + kOffPs + pw * kPsBytes;
-        Fetch f;
-        fetch_raw<K, FUSED, HAS_SEQ>(a, bk, b, h, 0, pw, lane, f);
-        fetch_tiles<HAS_SEQ>(a, bk, b, g, 0, nC, pw, lane, f);
-        stage_raw<K, HAS_SEQ>(sm + kOffRaw, pw, lane, f);
-        if (nC > 1) fetch_raw<K, FUSED, HAS_SEQ>(a, bk, b, h, 1, pw, lane, f);
-        __syncthreads();  // raw rows of chunk 0 staged
-        produce<K, FUSED, HAS_SEQ>(a, bk, b, h, g, 0, nC, Ah, pw, lane, sm,
-                                   sm + kOffRaw + kRawBytes, ps, f);
-        __syncthreads();
-        for (int64_t cn = 0; cn < nC; ++cn) {
-            if (cn > 0) store_y(bk, sm + kOffY + ((cn - 1) & 1) * kYBytes, cn - 1, pw, lane);
-            if (cn + 1 < nC)
-                produce<K, FUSED, HAS_SEQ>(a, bk, b, h, g, cn + 1, nC, Ah, pw, lane,
-                                           sm + ((cn + 1) & 1) * kStageBytes,
-                                           sm + kOffRaw + ((cn + 2) & 1) * kRawBytes, ps, f);
-            __syncthreads();
+        const float Ah2 = Ah * 1.4426950408889634f;  // exponents in base 2
+        POff o;
+        {
+            const int ptid = pw * 64 + lane;
+            o.tile = ptid * 16;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = 16 * unit_I(pw, u) + (lane & 15), q = 4 * unit_S(pw, u) + (lane >> 4);
+                o.g[u] = (i * kQ + 8 * q) * 4;
+            }
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const int idx = ptid + 256 * q;
+                o.x[q] = (idx >> 3) * bk.x_row * 2 + (idx & 7) * 16;
+            }
+            o.dt = lane * bk.H * 4;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int idx = ptid + 256 * q;
+                o.y[q] = (idx >> 3) * bk.H * kP * 2 + (idx & 7) * 16;
+            }
         }
-        store_y(bk, sm + kOffY + ((nC - 1) & 1) * kYBytes, nC - 1, pw, lane);
+        Fetch fa, fb;
+        // prologue: raw rows of chunk 0, then chunk 0 produced (its tiles fetched into fa;
+        // chunk 1's loads into fb)
+        fetch<K, HAS_SEQ>(bk, o, 0, nC, pw, lane, fa);
+        stage_raw_first<K, FUSED, HAS_SEQ>(a, bk, b, h, pw, lane, sm + kOffRaw);
+        __syncthreads();  // raw rows of chunk 0 staged
+        stage<K, HAS_SEQ>(fa, 0, nC, pw, lane, sm, sm + kOffRaw + kRawBytes);
+        if (nC > 1) fetch<K, HAS_SEQ>(bk, o, 1, nC, pw, lane, fb);
+        scalars_and_m<HAS_SEQ>(fa, 0, bk.L, Ah2, pw, lane, sm, ps);
+        __syncthreads();
+        // chunk cn: store y(cn-1), produce chunk cn+1 from the buffer its loads went to and
+        // issue chunk cn+2's loads into the other one.  Unrolled by two so each buffer keeps
+        // its registers (no copies, no wait on loads still in flight).
+        for (int64_t cn = 0; cn < nC; cn += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int64_t c = cn + half;
+                if (c >= nC) break;
+                Fetch& cur = half == 0 ? fb : fa;
+                Fetch& nxt = half == 0 ? fa : fb;
+                const int64_t k = c + 1;
+                if (k < nC) {
+                    stage<K, HAS_SEQ>(cur, k, nC, pw, lane, sm + (k & 1) * kStageBytes,
+                                      sm + kOffRaw + ((k + 1) & 1) * kRawBytes);
+                    if (k + 1 < nC) fetch<K, HAS_SEQ>(bk, o, k + 1, nC, pw, lane, nxt);
+                }
+                if (c > 0) store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c - 1, pw, lane);
+                if (k < nC) scalars_and_m<HAS_SEQ>(cur, k, bk.L, Ah2, pw, lane, sm + (k & 1) * kStageBytes, ps);
+                __syncthreads();
+            }
+        }
+        store_y(bk, o, sm + kOffY + ((nC - 1) & 1) * kYBytes, nC - 1, pw, lane);
     }
 
     // ---- final conv state F = u[L .. L+K-2] for this head's x channels and for slice h of
