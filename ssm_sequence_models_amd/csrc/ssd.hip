@@ -19,7 +19,7 @@
 //    bf16 as the exact value rounds) over the chunk's B and C channels, once for all heads of
 //    the group; writes C (token-major), B (channel-major) and G = C B^T (fp32, MFMA) to the
 //    workspace.  Doing this per head would repeat the B/C conv nheads times.
-//  * ssd_main_kernel, one block per (batch row, head) with 8 wavefronts, two per SIMD:
+//  * ssd_main_kernel, one block per (batch row, head) with 12 wavefronts, three per SIMD:
 //      - 4 consumer waves each own 16 of the 64 head channels and keep their [16 x 128] slice
 //        of the fp32 state in MFMA accumulators for the whole sequence.  Per chunk they issue
 //        the contractions on v_mfma_f32_16x16x32_bf16:
@@ -28,15 +28,15 @@
 //            h^T += B^T x (W o X)      (state update)
 //        The fp32 operands (h, M, W o X) enter as a hi + lo pair of bf16 (v = hi + lo with
 //        |v - hi - lo| <= 2^-17 |v|); the other operand (x, B, C) is exact in bf16, so each
-//        contraction is accurate to about fp32 at the bf16 MFMA rate.  Each consumer lane
-//        also runs the register-window conv + SiLU of its channel over its 16 tokens, which
-//        directly yields its X operand.
-//      - 4 producer waves run one chunk ahead: fetch the next chunk's raw x rows and
-//        C / B^T / G tiles from HBM / L2, compute the in-chunk cumulative log-decay (a DPP
-//        prefix scan per wavefront) and the M tiles, and leave everything in the other half
-//        of a double-buffered LDS stage.
-//    One block barrier per chunk hands the stage over.  Each SIMD runs one producer and one
-//    consumer wave, so VALU work of one hides the latencies of the other.
+//        contraction is accurate to about fp32 at the bf16 MFMA rate.
+//      - 4 producer waves run one chunk ahead: move the next chunk's C / B^T tiles and the
+//        raw x rows of the chunk after it from L2 / HBM straight into LDS, compute the
+//        in-chunk cumulative log-decay (a DPP prefix scan per wavefront) and the M tiles,
+//        and store the previous chunk's y rows.
+//      - 4 conv waves run the register-window conv + SiLU of the head's x channels for the
+//        next chunk from the staged raw rows; each lane's 16 outputs are exactly the X
+//        operand of the consumer lane with the same index.
+//    One block barrier per chunk hands the double-buffered LDS stages over.
 #include "internal.h"
 
 namespace ssm {
@@ -47,7 +47,7 @@ constexpr int kP = 64;       // head channels (4 consumer waves x 16)
 constexpr int kN = 128;      // state size
 constexpr int kKmax = 8;     // widest conv handled
 constexpr int kPrepThreads = 256;
-constexpr int kMainThreads = 512;
+constexpr int kMainThreads = 768;  // 4 consumer, 4 producer and 4 conv wavefronts
 
 // workspace per (row, chunk, group)
 constexpr int64_t kWsC = static_cast<int64_t>(kQ) * kN;    // bf16 elements, [token][n]
@@ -261,17 +261,22 @@ ssd_prep_kernel(ChunkedArgs a) {
 // =======================================================================================
 // LDS, all tiles stored as rows of 16-byte pieces under XOR swizzles chosen so that every 8
 // consecutive lanes of a ds_read_b128 / ds_write_b128 (the lanes one 128-byte LDS cycle
-// serves) touch 8 different 16-byte bank groups.
+// serves) touch 8 different 16-byte bank groups.  Three separate arrays: the two that the
+// producers fill by memory-to-LDS transfers (tiles, raw x rows) and the rest, so that the
+// compiler orders an LDS access after an outstanding transfer only when it may touch the
+// transfer's array.
+//   tile stage s (two, by chunk parity), loaded one chunk ahead of its use:
+constexpr int kCbC = 0;                          // C   [64 tok][16 pieces], piece ^ (tok & 15)
+constexpr int kCbBt = kCbC + kQ * 256;           // B^T [128 n][8 pieces], piece ^ bt_swz(n)
+constexpr int kCbBytes = kCbBt + kN * 128;
 //   stage s (two, by chunk parity), produced one chunk ahead of its use:
-constexpr int kStC = 0;                          // C   [64 tok][16 pieces], piece ^ (tok & 15)
-constexpr int kStBt = kStC + kQ * 256;           // B^T [128 n][8 pieces], piece ^ bt_swz(n)
-constexpr int kStMhi = kStBt + kN * 128;         // M   [64 i][8 pieces], piece ^ (i & 7)
+constexpr int kStMhi = 0;                        // M   [64 i][8 pieces], piece ^ (i & 7)
 constexpr int kStMlo = kStMhi + kQ * 128;
 constexpr int kStE = kStMlo + kQ * 128;          // E_i = exp(cum_i) on the leading segment
 constexpr int kStW = kStE + kQ * 4;              // W_j = exp(cum_last - cum_j) dt_j
 constexpr int kStDecay = kStW + kQ * 4;          // exp(cum_last) (0 after a reset)
 constexpr int kStageBytes = kStDecay + 16;
-//   raw x slot (two, by chunk parity), staged two chunks ahead: the conv of chunk c+1 runs
+//   raw x slot (two, by chunk parity), loaded two chunks ahead: the conv of chunk c+1 runs
 //   while chunk c is contracted
 constexpr int kRowsMax = kQ + kKmax - 1;         // raw x rows of a chunk incl. the conv halo
 constexpr int kRwX = 0;                          // raw x [rows][8 pieces], piece ^ xr_swz(row)
@@ -282,11 +287,14 @@ constexpr int kRawBytes = kRwSeq + 72 * 4;
 constexpr int kYBytes = kQ * kP * 2;             // [64 tok][16 slots of 8 B], slot ^ (tok & 15)
 //   producer-private scalars: cum, dtv, r of the chunk
 constexpr int kPsBytes = 3 * kQ * 4;
-constexpr int kOffRaw = 2 * kStageBytes;
-constexpr int kOffY = kOffRaw + 2 * kRawBytes;
+//   X slot (two, by chunk parity): the conv waves' bf16 outputs (X operands), 16 bytes per
+//   (wave, lane, run), read back by the consumer lane with the same wave-in-role and lane index
+constexpr int kXBytes = kQ * kP * 2;
+constexpr int kOffY = 2 * kStageBytes;
 constexpr int kOffPs = kOffY + 2 * kYBytes;
-constexpr int kMainLds = kOffPs + 4 * kPsBytes;
-static_assert(kMainLds <= 160 * 1024, "LDS budget");
+constexpr int kOffX = kOffPs + 4 * kPsBytes;
+constexpr int kMainLds = kOffX + 2 * kXBytes;
+static_assert(kMainLds + 2 * kCbBytes + 2 * kRawBytes <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int sw_c(int tok, int q) { return tok * 256 + ((q ^ (tok & 15)) << 4); }
 // B^T rows are read through the state-tile row map n = 32T + 8(l>>2) + 4(t&1) + (l&3):
@@ -312,6 +320,10 @@ __device__ __forceinline__ bool unit_valid(int pw, int u) { return u == 0 || pw 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores past
 // it are dropped by the hardware range check, which handles the ragged last chunk.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8): wait until at most 0 / 2 vector-memory operations are outstanding
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm2 = 0x0F72;
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFFLL ? 0x7FFFFFFFLL : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
@@ -338,43 +350,48 @@ struct Blk {
     int L, x_row, H;
 };
 
-// Per-lane constant byte offsets of the producer's loads and stores
+// Per-lane constant byte offsets of the producer's loads and stores.  The C, B^T and raw x
+// tiles go straight from memory into LDS (buffer loads with the lds modifier): one
+// instruction moves 64 x 16 bytes to 1 KB of consecutive LDS, lane l at byte 16 l, so each
+// lane loads the global piece that the LDS swizzle puts in its slot.
 struct POff {
-    uint32_t tile;          // C and B^T tile pieces ptid (+ 4096 k)
-    uint32_t g[2];          // G piece of unit u: row i, columns 8q .. 8q+7
-    uint32_t x[3];          // raw x piece ptid + 256 k: row rho, 8 channels q
+    uint32_t c[4];          // C tile LDS block r = 4 pw + k: token 4r + l/16, slot l%16
+    uint32_t bt[4];         // B^T tile LDS block r = 4 pw + k: row n = 8r + l/8, slot l%8
+    uint32_t x[3];          // raw x LDS block r = pw + 4k: row 8r + l/8, slot l%8
+    uint32_t g[2];          // G piece of M unit u: row i, columns 8q .. 8q+7
     uint32_t dt;            // token = lane
     uint32_t y[2];          // y piece ptid + 256 k: token, 8 channels
 };
 
-// Registers a producer lane carries from issuing its loads to staging them (one chunk
-// later): the tiles, dt and ids of chunk k and the raw x rows of chunk k+1.  Two of these
-// alternate, so loads stay in flight across the block barrier.
+// Registers a producer lane loads for chunk k (its M tiles and scalars)
 struct Fetch {
-    u32x4 c[4];
-    u32x4 bt[4];
     u32x4 gm[2][2];
     uint32_t dt;
     int32_t seq_j, seq_prev;
-    u32x4 x[3];
-    int32_t seq_row;
 };
 
-// Loads for chunk k (tiles, dt, ids) and, if present, the raw rows of chunk k+1 (whose first
-// row t0 + Q - (K-1) >= 0).
-template <int K, bool HAS_SEQ>
-__device__ __forceinline__ void fetch(const Blk& bk, const POff& o, int64_t k, int64_t nC,
-                                      int pw, int lane, Fetch& f) {
-    constexpr int kRows = kQ + K - 1;
-    const int t0 = static_cast<int>(k) * kQ;
+__device__ __forceinline__ void dma16(Rsrc r, uint32_t voff, uint8_t* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Chunk k's C / B^T tiles into tile stage `st`
+__device__ __forceinline__ void fetch_tiles(const Blk& bk, const POff& o, int64_t k, int pw,
+                                            uint8_t* st) {
     const Rsrc rc = make_rsrc(bk.wsC + k * bk.ws_step * kWsC, kWsC * 2);
     const Rsrc rb = make_rsrc(bk.wsBt + k * bk.ws_step * kWsBt, kWsBt * 2);
-    const Rsrc rg = make_rsrc(bk.wsG + k * bk.ws_step * kWsG, kWsG * 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        f.c[q] = bload128(rc, o.tile + 4096 * q);
-        f.bt[q] = bload128(rb, o.tile + 4096 * q);
+        dma16(rc, o.c[q], st + kCbC + (4 * pw + q) * 1024);
+        dma16(rb, o.bt[q], st + kCbBt + (4 * pw + q) * 1024);
     }
+}
+
+// Chunk k's G pieces, dt and ids into registers
+template <bool HAS_SEQ>
+__device__ __forceinline__ void fetch_regs(const Blk& bk, const POff& o, int64_t k, int pw,
+                                           int lane, Fetch& f) {
+    const int t0 = static_cast<int>(k) * kQ;
+    const Rsrc rg = make_rsrc(bk.wsG + k * bk.ws_step * kWsG, kWsG * 4);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         if (unit_valid(pw, u)) {
@@ -389,17 +406,28 @@ __device__ __forceinline__ void fetch(const Blk& bk, const POff& o, int64_t k, i
         f.seq_j = static_cast<int32_t>(bload32(rs, lane * 4));
         f.seq_prev = t0 > 0 ? bk.seq[t0 - 1] : 0;
     }
-    if (k + 1 < nC) {
-        const int r0 = t0 + kQ - (K - 1);
-        const Rsrc rx = make_rsrc(bk.x + static_cast<int64_t>(r0) * bk.x_row,
-                                  static_cast<int64_t>(bk.L - r0) * bk.x_row * 2);
-        const int ptid = pw * 64 + lane;
+}
+
+// Raw x rows of chunk k >= 1 (first row t0 - (K-1) >= 0) into raw slot `raw`; rows past the
+// end arrive as zeros.  With seq_idx the rows' ids come back in *seq_row, to be stored once
+// the load has landed.
+template <int K, bool HAS_SEQ>
+__device__ __forceinline__ void fetch_raw(const Blk& bk, const POff& o, int64_t k, int pw,
+                                          int lane, uint8_t* raw, int32_t* seq_row) {
+    constexpr int kRows = kQ + K - 1;
+    const int r0 = static_cast<int>(k) * kQ - (K - 1);
+    const Rsrc rx = make_rsrc(bk.x + static_cast<int64_t>(r0) * bk.x_row,
+                              static_cast<int64_t>(bk.L - r0) * bk.x_row * 2);
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
-            if (ptid + 256 * q < kRows * 8) f.x[q] = bload128(rx, o.x[q]);
-        if (HAS_SEQ && ptid < kRows) {
+    for (int q = 0; q < 3; ++q) {
+        const int r = pw + 4 * q;
+        if (8 * r < kRows && 8 * r + (lane >> 3) < kRows) dma16(rx, o.x[q], raw + kRwX + r * 1024);
+    }
+    if (HAS_SEQ) {
+        const int ptid = pw * 64 + lane;
+        if (ptid < kRows) {
             const Rsrc rs = make_rsrc(bk.seq + r0, static_cast<int64_t>(bk.L - r0) * 4);
-            f.seq_row = static_cast<int32_t>(bload32(rs, ptid * 4));
+            *seq_row = static_cast<int32_t>(bload32(rs, ptid * 4));
         }
     }
 }
@@ -437,28 +465,6 @@ __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk&
         int tr = ptid - (K - 1);
         tr = tr < 0 ? 0 : (tr >= bk.L ? bk.L - 1 : tr);
         reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = bk.seq[tr];
-    }
-}
-
-// Stage chunk k's tiles (stage k&1) and, if present, chunk k+1's raw rows (raw slot (k+1)&1)
-template <int K, bool HAS_SEQ>
-__device__ __forceinline__ void stage(const Fetch& f, int64_t k, int64_t nC, int pw, int lane,
-                                      uint8_t* st, uint8_t* raw) {
-    constexpr int kRows = kQ + K - 1;
-    const int ptid = pw * 64 + lane;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int idx = ptid + 256 * q;
-        lds_st(st, kStC + sw_c(idx >> 4, idx & 15), f.c[q]);
-        lds_st(st, kStBt + sw_bt(idx >> 3, idx & 7), f.bt[q]);
-    }
-    if (k + 1 < nC) {
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int idx = ptid + 256 * q;
-            if (idx < kRows * 8) lds_st(raw, kRwX + sw_xr(idx >> 3, idx & 7), f.x[q]);
-        }
-        if (HAS_SEQ && ptid < kRows) reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = f.seq_row;
     }
 }
 
@@ -542,49 +548,91 @@ __device__ __forceinline__ void store_y(const Blk& bk, const POff& o, const uint
 }
 
 // Consumer: the conv of channel p over tokens j0 .. j0+7 of a chunk from its staged raw rows
-// (row rho <-> token t0 - (K-1) + rho), rounded to bf16 -> one MFMA operand
-template <int K, bool FUSED, bool HAS_SEQ>
-__device__ __forceinline__ bf16x8 conv_operand(const uint8_t* raw, int p, int j0,
-                                               const double (&cw)[K], double cbias, int act) {
+// (row rho <-> token t0 - (K-1) + rho), rounded to bf16 -> one MFMA operand.  MODE 0: no conv
+// (the rows already hold x); 1: conv, identity phi; 2: conv + SiLU.  The fast path has no
+// branches, so the scheduler can spread it between the contractions of the previous chunk;
+// for SiLU it flags, in *near, outputs that lie too close to a bf16 rounding midpoint for
+// the fp32 evaluation to decide (conv_fix redoes those in double).
+template <int K, int MODE, bool HAS_SEQ>
+__device__ __forceinline__ double conv_z(const uint8_t* raw, int q, int byte, int r0,
+                                         const double (&cw)[K], double cbias) {
+    double z = cbias;
+    int32_t idl = 0;
+    if (HAS_SEQ) idl = lds_ld<int32_t>(raw, kRwSeq + (r0 + K - 1) * 4);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        double u = bf16_to_f32(lds_ld<uint16_t>(raw, kRwX + sw_xr(r0 + k, q) + byte));
+        if (HAS_SEQ && lds_ld<int32_t>(raw, kRwSeq + (r0 + k) * 4) != idl) u = 0.0;
+        z = fma(cw[k], u, z);
+    }
+    return z;
+}
+
+template <int K, int MODE, bool HAS_SEQ>
+__device__ __forceinline__ bf16x8 conv_fast(const uint8_t* raw, int p, int j0,
+                                            const double (&cw)[K], double cbias, uint32_t* near) {
     bf16x8 out;
     const int q = p >> 3, byte = (p & 7) * 2;
-    if (FUSED) {
-        double u[8 + K - 1];
-        int32_t id[8 + K - 1];
-#pragma unroll
-        for (int tau = 0; tau < 8 + K - 1; ++tau) {
-            u[tau] = bf16_to_f32(lds_ld<uint16_t>(raw, kRwX + sw_xr(j0 + tau, q) + byte));
-            id[tau] = HAS_SEQ ? lds_ld<int32_t>(raw, kRwSeq + (j0 + tau) * 4) : 0;
-        }
-        double z[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            z[e] = cbias;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const double tap = (!HAS_SEQ || id[e + k] == id[e + K - 1]) ? u[e + k] : 0.0;
-                z[e] = fma(cw[k], tap, z[e]);
-            }
-        }
-        uint16_t o[8];
-        act_to_bf16_batch(z, act, o);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = __builtin_bit_cast(__bf16, o[e]);
-    } else {
+    if (MODE == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             out[e] = __builtin_bit_cast(__bf16, lds_ld<uint16_t>(raw, kRwX + sw_xr(j0 + e + K - 1, q) + byte));
+        return out;
     }
+    double u[8 + K - 1];
+    int32_t id[8 + K - 1];
+#pragma unroll
+    for (int tau = 0; tau < 8 + K - 1; ++tau) {
+        u[tau] = bf16_to_f32(lds_ld<uint16_t>(raw, kRwX + sw_xr(j0 + tau, q) + byte));
+        id[tau] = HAS_SEQ ? lds_ld<int32_t>(raw, kRwSeq + (j0 + tau) * 4) : 0;
+    }
+    uint32_t nb = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        double z = cbias;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const double tap = (!HAS_SEQ || id[e + k] == id[e + K - 1]) ? u[e + k] : 0.0;
+            z = fma(cw[k], tap, z);
+        }
+        if (MODE == 2) {
+            bool nr;
+            const float sv = silu_f32(z, nr);
+            out[e] = static_cast<__bf16>(sv);
+            nb |= static_cast<uint32_t>(nr) << e;
+        } else {
+            out[e] = __builtin_bit_cast(__bf16, f64_to_bf16(z));
+        }
+    }
+    if (MODE == 2) *near |= nb << (8 * (j0 >> 5));   // bits 0-7: s = 0 run, 8-15: s = 1 run
     return out;
 }
 
-template <int K, bool FUSED, bool HAS_SEQ>
+// Redo the flagged SiLU outputs of one run (tokens j0 + e) in double
+template <int K, bool HAS_SEQ>
+__device__ __forceinline__ bf16x8 conv_fix(const uint8_t* raw, int p, int j0,
+                                           const double (&cw)[K], double cbias, uint32_t near,
+                                           bf16x8 x) {
+    const int q = p >> 3, byte = (p & 7) * 2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (near & (1u << e)) {
+            const double z = conv_z<K, 2, HAS_SEQ>(raw, q, byte, j0 + e, cw, cbias);
+            x[e] = __builtin_bit_cast(__bf16, silu_f64_to_bf16(z));
+        }
+    }
+    return x;
+}
+
+template <int K, int MODE, bool HAS_SEQ>
 __global__ void __launch_bounds__(kMainThreads, 1)
 ssd_main_kernel(ChunkedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t sm[kMainLds];
+    __shared__ __attribute__((aligned(16))) uint8_t sm_cb[2 * kCbBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t sm_raw[2 * kRawBytes];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
-    const bool consumer = wave < 4;
+    const int role = wave >> 2;  // 0 consumer, 1 producer, 2 conv
 
     // block -> (row, head): consecutive units on one XCD (blocks are dealt round-robin over
     // the 8 XCDs), so the heads of one row share that XCD's L2 for the B/C/G tiles
@@ -614,28 +662,20 @@ ssd_main_kernel(ChunkedArgs a) {
     bk.x_row = static_cast<int>(a.x_row);
     bk.H = static_cast<int>(a.H);
 
-    // The two roles run separate loops (a wave's role never changes), so the register
-    // allocator sees the consumer's state and the producer's in-flight fetch as disjoint
-    // live ranges.  Both loops pass the same number of block barriers: two in the prologue
-    // (raw rows of chunk 0 staged; chunk 0 produced), then one per chunk.  Between two
-    // barriers the consumers contract chunk c from stage c&1, convolve chunk c+1 from raw slot
-    // (c+1)&1 and write y(c) to y slot c&1, while the producers store y(c-1) from y slot
-    // (c-1)&1, fill stage (c+1)&1 and raw slot c&1 (chunk c+2).
-    if (consumer) {
+    // The three roles run separate loops (a wave's role never changes), so the register
+    // allocator sees each role's live ranges alone, and each SIMD holds one wave of each role
+    // to interleave.  All loops pass the same number of block barriers: two in the prologue
+    // (raw rows of chunk 0 staged; chunk 0 produced and convolved), then one per chunk.
+    // Between two barriers:
+    //   consumers  contract chunk c from stage c&1 and X slot c&1, write y(c) to y slot c&1;
+    //   producers  load chunk c+1's tiles into stage (c+1)&1 and chunk c+2's raw rows into
+    //              raw slot c&1, store y(c-1) from y slot (c-1)&1, compute chunk c+1's
+    //              scalars and M tiles;
+    //   conv waves convolve chunk c+1 from raw slot (c+1)&1 into X slot (c+1)&1.
+    if (role == 0) {
         // state slice acc[t][r] = h[p][n], p = 16 wave + li, n = 32(t/2) + 8 g4 + 4(t%2) + r
         // (the MFMA row of tile t that lane group g4 holds)
         const int p_own = 16 * wave + li;
-        // conv taps of channel p_own
-        double cw[K];
-        double cbias = 0.0;
-#pragma unroll
-        for (int k = 0; k < K; ++k) cw[k] = 0.0;
-        if (FUSED) {
-            const int64_t cc = a.x_col0 + h * kP + p_own;
-#pragma unroll
-            for (int k = 0; k < K; ++k) cw[k] = a.conv_w[cc * K + k];
-            cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
-        }
         f32x4 acc[8];
         {
             const float* src = a.init_state ? a.init_state + ((b * a.H + h) * kP + p_own) * kN : nullptr;
@@ -651,16 +691,17 @@ ssd_main_kernel(ChunkedArgs a) {
             }
         }
         __syncthreads();  // raw rows of chunk 0 staged
-        // X operands of chunk 0 (lane: channel p_own, tokens 32 s + 8 g4 .. +7)
-        bf16x8 xv[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            xv[s] = conv_operand<K, FUSED, HAS_SEQ>(sm + kOffRaw, p_own, 32 * s + 8 * g4, cw, cbias, a.act);
-        __syncthreads();  // stage 0 and the raw rows of chunk 1 ready; raw slot 0 free
-
+        __syncthreads();  // stage 0 and X(0) ready
+        // X operands (lane: channel p_own, tokens 32 s + 8 g4 .. +7), convolved by the conv
+        // wave with this wave's index
+        const int xoff = (wave * 64 + lane) * 32;
         for (int64_t cn = 0; cn < nC; ++cn) {
             const uint8_t* st = sm + (cn & 1) * kStageBytes;
+            const uint8_t* cbt = sm_cb + (cn & 1) * kCbBytes;
             uint8_t* yt = sm + kOffY + (cn & 1) * kYBytes;
+            bf16x8 xv[2];
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) xv[sh] = lds_ld<bf16x8>(sm + kOffX + (cn & 1) * kXBytes, xoff + 16 * sh);
             float eI[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
@@ -674,15 +715,46 @@ ssd_main_kernel(ChunkedArgs a) {
             }
             const float decay = lds_ld<float>(st, kStDecay);
 
-            // Y^T[p][i], p = 16 wave + 4 g4 + r, i = 16 I + li
+            // Y^T[p][i], p = 16 wave + 4 g4 + r, i = 16 I + li.  Each phase loads its LDS
+            // operands before its MFMAs, and consecutive MFMAs use different accumulators
+            // (all hi products, then all lo products), so neither LDS latency nor the MFMA
+            // result latency sits between two issues.
             f32x4 yo[4], yi[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 yo[I] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 yi[I] = yo[I];
             }
+            // intra-chunk part: M tiles (I, s) with 32 s <= 16 I + 15
+            bf16x8 mh[6], ml[6];
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                mh[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
+                ml[u] = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * sh + g4));
+            }
+            bf16x8 cb[2][4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) cb[0][I] = lds_ld<bf16x8>(cbt, kCbC + sw_c(16 * I + li, g4));
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                yi[I] = mfma(xv[sh], mh[u], yi[I]);
+            }
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                yi[I] = mfma(xv[sh], ml[u], yi[I]);
+            }
+            // initial-state part, one 32-wide slice m of the state at a time; the next
+            // slice's C tiles load while this slice's MFMAs run
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                if (m + 1 < 4) {
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+                        cb[(m + 1) & 1][I] = lds_ld<bf16x8>(cbt, kCbC + sw_c(16 * I + li, 4 * (m + 1) + g4));
+                }
                 float hv[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -692,48 +764,30 @@ ssd_main_kernel(ChunkedArgs a) {
                 bf16x8 hhi, hlo;
                 split_hilo(hv, hhi, hlo);
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const bf16x8 cv = lds_ld<bf16x8>(st, kStC + sw_c(16 * I + li, 4 * m + g4));
-                    yo[I] = mfma(hhi, cv, yo[I]);
-                    yo[I] = mfma(hlo, cv, yo[I]);
-                }
-            }
+                for (int I = 0; I < 4; ++I) yo[I] = mfma(hhi, cb[m & 1][I], yo[I]);
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    if (32 * s <= 16 * I + 15) {
-                        const bf16x8 mh = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * s + g4));
-                        const bf16x8 ml = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * s + g4));
-                        yi[I] = mfma(xv[s], mh, yi[I]);
-                        yi[I] = mfma(xv[s], ml, yi[I]);
-                    }
-                }
+                for (int I = 0; I < 4; ++I) yo[I] = mfma(hlo, cb[m & 1][I], yo[I]);
             }
             // state update: h^T[n][p] = decay h^T + B^T (W o X)
 #pragma unroll
             for (int t = 0; t < 8; ++t) acc[t] *= decay;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                float wx[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) wx[e] = wj[s][e] * static_cast<float>(xv[s][e]);
-                bf16x8 bh, bl;
-                split_hilo(wx, bh, bl);
+            for (int sh = 0; sh < 2; ++sh) {
+                bf16x8 bv[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const int n_row = 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3);
-                    const bf16x8 bv = lds_ld<bf16x8>(st, kStBt + sw_bt(n_row, 4 * s + g4));
-                    acc[t] = mfma(bv, bh, acc[t]);
-                    acc[t] = mfma(bv, bl, acc[t]);
+                    bv[t] = lds_ld<bf16x8>(cbt, kCbBt + sw_bt(n_row, 4 * sh + g4));
                 }
-            }
-            // the next chunk's X operands (independent of the contractions above)
-            if (cn + 1 < nC) {
-                const uint8_t* raw = sm + kOffRaw + ((cn + 1) & 1) * kRawBytes;
+                float wx[8];
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    xv[s] = conv_operand<K, FUSED, HAS_SEQ>(raw, p_own, 32 * s + 8 * g4, cw, cbias, a.act);
+                for (int e = 0; e < 8; ++e) wx[e] = wj[sh][e] * static_cast<float>(xv[sh][e]);
+                bf16x8 bh, bl;
+                split_hilo(wx, bh, bl);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[t] = mfma(bv[t], bh, acc[t]);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[t] = mfma(bv[t], bl, acc[t]);
             }
             // y tile of this chunk -> LDS (the producers store it next iteration)
 #pragma unroll
@@ -753,69 +807,133 @@ ssd_main_kernel(ChunkedArgs a) {
                 *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
             }
         }
-    } else {
+    } else if (role == 1) {
         const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
         uint8_t* ps = sm + kOffPs + pw * kPsBytes;
         const float Ah2 = Ah * 1.4426950408889634f;  // exponents in base 2
         POff o;
         {
-            const int ptid = pw * 64 + lane;
-            o.tile = ptid * 16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 4 * pw + q;
+                const int tok = 4 * r + (lane >> 4), slot = lane & 15;
+                o.c[q] = tok * 256 + ((slot ^ (tok & 15)) << 4);
+                const int n = 8 * r + (lane >> 3), sl = lane & 7;
+                o.bt[q] = n * 128 + ((sl ^ ((n & 3) | (((n >> 3) & 1) << 2))) << 4);
+            }
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const int row = 8 * (pw + 4 * q) + (lane >> 3), sl = lane & 7;
+                o.x[q] = row * bk.x_row * 2 + ((sl ^ (((row >> 3) & 3) << 1)) << 4);
+            }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int i = 16 * unit_I(pw, u) + (lane & 15), q = 4 * unit_S(pw, u) + (lane >> 4);
                 o.g[u] = (i * kQ + 8 * q) * 4;
             }
-#pragma unroll
-            for (int q = 0; q < 3; ++q) {
-                const int idx = ptid + 256 * q;
-                o.x[q] = (idx >> 3) * bk.x_row * 2 + (idx & 7) * 16;
-            }
             o.dt = lane * bk.H * 4;
+            const int ptid = pw * 64 + lane;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int idx = ptid + 256 * q;
                 o.y[q] = (idx >> 3) * bk.H * kP * 2 + (idx & 7) * 16;
             }
         }
+        const int ptid = pw * 64 + lane;
+        constexpr int kRows = kQ + K - 1;
         Fetch fa, fb;
-        // prologue: raw rows of chunk 0, then chunk 0 produced (its tiles fetched into fa;
-        // chunk 1's loads into fb)
-        fetch<K, HAS_SEQ>(bk, o, 0, nC, pw, lane, fa);
-        stage_raw_first<K, FUSED, HAS_SEQ>(a, bk, b, h, pw, lane, sm + kOffRaw);
+        int32_t seq_row = 0;
+        // prologue: chunk 0's tiles, registers and raw rows, chunk 1's raw rows and
+        // registers; then chunk 0 produced
+        fetch_tiles(bk, o, 0, pw, sm_cb);
+        fetch_regs<HAS_SEQ>(bk, o, 0, pw, lane, fa);
+        if (nC > 1) fetch_raw<K, HAS_SEQ>(bk, o, 1, pw, lane, sm_raw + kRawBytes, &seq_row);
+        stage_raw_first<K, MODE != 0, HAS_SEQ>(a, bk, b, h, pw, lane, sm_raw);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        if (nC > 1) fetch_regs<HAS_SEQ>(bk, o, 1, pw, lane, fb);
+        if (HAS_SEQ && nC > 1 && ptid < kRows)
+            reinterpret_cast<int32_t*>(sm_raw + kRawBytes + kRwSeq)[ptid] = seq_row;
         __syncthreads();  // raw rows of chunk 0 staged
-        stage<K, HAS_SEQ>(fa, 0, nC, pw, lane, sm, sm + kOffRaw + kRawBytes);
-        if (nC > 1) fetch<K, HAS_SEQ>(bk, o, 1, nC, pw, lane, fb);
         scalars_and_m<HAS_SEQ>(fa, 0, bk.L, Ah2, pw, lane, sm, ps);
         __syncthreads();
-        // chunk cn: store y(cn-1), produce chunk cn+1 from the buffer its loads went to and
-        // issue chunk cn+2's loads into the other one.  Unrolled by two so each buffer keeps
-        // its registers (no copies, no wait on loads still in flight).
+        // chunk cn: load chunk cn+1's tiles (into stage (cn+1)&1, free since chunk cn-1 was
+        // contracted), chunk cn+2's raw rows (into raw slot cn&1, free since chunk cn was
+        // convolved) and chunk cn+2's registers; store y(cn-1), compute chunk cn+1's scalars
+        // and M tiles from the registers loaded one chunk earlier.  Every load lands before
+        // the barrier.  Unrolled by two so each register set keeps its registers.
         for (int64_t cn = 0; cn < nC; cn += 2) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int64_t c = cn + half;
                 if (c >= nC) break;
-                Fetch& cur = half == 0 ? fb : fa;
-                Fetch& nxt = half == 0 ? fa : fb;
+                Fetch& cur = half == 0 ? fb : fa;   // chunk c+1
+                Fetch& nxt = half == 0 ? fa : fb;   // chunk c+2
                 const int64_t k = c + 1;
-                if (k < nC) {
-                    stage<K, HAS_SEQ>(cur, k, nC, pw, lane, sm + (k & 1) * kStageBytes,
-                                      sm + kOffRaw + ((k + 1) & 1) * kRawBytes);
-                    if (k + 1 < nC) fetch<K, HAS_SEQ>(bk, o, k + 1, nC, pw, lane, nxt);
+                uint8_t* stk = sm + (k & 1) * kStageBytes;
+                if (k < nC) fetch_tiles(bk, o, k, pw, sm_cb + (k & 1) * kCbBytes);
+                if (k + 1 < nC) {
+                    fetch_raw<K, HAS_SEQ>(bk, o, k + 1, pw, lane, sm_raw + (c & 1) * kRawBytes, &seq_row);
+                    fetch_regs<HAS_SEQ>(bk, o, k + 1, pw, lane, nxt);
                 }
+                // the y stores are the iteration's last vector-memory operations (the empty asm
+                // keeps the compiler from moving loads after them); the loads complete in issue
+                // order, so waiting until only the two stores are outstanding waits for every
+                // load, while the stores' write latency overlaps the next chunk
+                asm volatile("" ::: "memory");
                 if (c > 0) store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c - 1, pw, lane);
-                if (k < nC) scalars_and_m<HAS_SEQ>(cur, k, bk.L, Ah2, pw, lane, sm + (k & 1) * kStageBytes, ps);
+                if (k < nC) scalars_and_m<HAS_SEQ>(cur, k, bk.L, Ah2, pw, lane, stk, ps);
+                if (c > 0) __builtin_amdgcn_s_waitcnt(kWaitVm2);
+                else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                if (HAS_SEQ && k + 1 < nC && ptid < kRows)
+                    reinterpret_cast<int32_t*>(sm_raw + (c & 1) * kRawBytes + kRwSeq)[ptid] = seq_row;
                 __syncthreads();
             }
         }
         store_y(bk, o, sm + kOffY + ((nC - 1) & 1) * kYBytes, nC - 1, pw, lane);
+    } else {
+        const int cv = wave - 8;
+        // the conv of channel p = 16 cv + li over tokens 32 s + 8 g4 .. +7 of a chunk, into
+        // the X slot lane the consumer wave cv reads
+        const int p_conv = 16 * cv + li;
+        const int xoff = (cv * 64 + lane) * 32;
+        double cw[K];
+        double cbias = 0.0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) cw[k] = 0.0;
+        if (MODE != 0) {
+            const int64_t cc = a.x_col0 + h * kP + p_conv;
+#pragma unroll
+            for (int k = 0; k < K; ++k) cw[k] = a.conv_w[cc * K + k];
+            cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
+        }
+        auto conv_chunk = [&](const uint8_t* raw, uint8_t* xs) {
+            uint32_t near = 0;
+            bf16x8 xv[2];
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh)
+                xv[sh] = conv_fast<K, MODE, HAS_SEQ>(raw, p_conv, 32 * sh + 8 * g4, cw, cbias, &near);
+            if (MODE == 2 && near) {
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh)
+                    xv[sh] = conv_fix<K, HAS_SEQ>(raw, p_conv, 32 * sh + 8 * g4, cw, cbias, near >> (8 * sh), xv[sh]);
+            }
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) lds_st(xs, xoff + 16 * sh, xv[sh]);
+        };
+        __syncthreads();  // raw rows of chunk 0 staged
+        conv_chunk(sm_raw, sm + kOffX);
+        __syncthreads();
+        for (int64_t cn = 0; cn < nC; ++cn) {
+            if (cn + 1 < nC)
+                conv_chunk(sm_raw + ((cn + 1) & 1) * kRawBytes, sm + kOffX + ((cn + 1) & 1) * kXBytes);
+            __syncthreads();
+        }
     }
 
     // ---- final conv state F = u[L .. L+K-2] for this head's x channels and for slice h of
     // the B / C channels: all reads first, then a barrier, then the writes, so an in-place
     // state pair is never read after being overwritten ----
-    if (FUSED && a.conv_final) {
+    if (MODE != 0 && a.conv_final) {
         constexpr int km1 = K - 1;
         const int64_t nx = kP * km1;
         const int64_t nbc_all = 2 * a.G * kN * km1;
@@ -857,6 +975,14 @@ ssd_main_kernel(ChunkedArgs a) {
     }
 }
 
+template <int K, int MODE>
+hipError_t launch_main(const ChunkedArgs& a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.B * a.H));
+    if (a.seq_idx) ssd_main_kernel<K, MODE, true><<<grid, kMainThreads, 0, stream>>>(a);
+    else ssd_main_kernel<K, MODE, false><<<grid, kMainThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 template <int K>
 hipError_t launch_k(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     const int64_t nC = (a.L + kQ - 1) / kQ;
@@ -865,18 +991,14 @@ hipError_t launch_k(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev0, hi
                          kPrepThreads, 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (ev0) hipEventRecord(ev0, stream);
-    const dim3 grid(static_cast<unsigned>(a.B * a.H));
-    const bool seq = a.seq_idx != nullptr;
-    if (a.fused_conv) {
-        if (seq) ssd_main_kernel<K, true, true><<<grid, kMainThreads, 0, stream>>>(a);
-        else ssd_main_kernel<K, true, false><<<grid, kMainThreads, 0, stream>>>(a);
-    } else {
-        if (seq) ssd_main_kernel<K, false, true><<<grid, kMainThreads, 0, stream>>>(a);
-        else ssd_main_kernel<K, false, false><<<grid, kMainThreads, 0, stream>>>(a);
+    if (ev0) (void)hipEventRecord(ev0, stream);
+    if (!a.fused_conv) {
+        if constexpr (K == 2) e = launch_main<K, 0>(a, stream);  // no conv: one halo row
+        else e = hipErrorInvalidValue;
     }
-    e = hipGetLastError();
-    if (ev1) hipEventRecord(ev1, stream);
+    else if (a.act == SSM_ACT_SILU) e = launch_main<K, 2>(a, stream);
+    else e = launch_main<K, 1>(a, stream);
+    if (ev1) (void)hipEventRecord(ev1, stream);
     return e;
 }
 
