@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -63,6 +64,99 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def _time_gpu(torch, fn, reps, warm=2):
+    """Mean milliseconds of fn() over reps calls, by events on torch's current stream (the
+    library launches on that stream)."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def other_ops(torch, ssm, workloads):
+    """Achieved bandwidth of the other entry points on their workloads: the unfused conv at the
+    1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
+    370M-like prefill and the 131072-token 780M-like call.  Seeded inputs drawn on the GPU
+    (timing only; parity is the test suite's job)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    res = []
+
+    def rep(op, workload, ms, tokens, nbytes):
+        res.append({"op": op, "workload": workload, "ms": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                    "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+                    "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+
+    def prefill_inputs(s, seed):
+        g.manual_seed(seed)
+        x = torch.randn(s.B, s.L, s.C, generator=g, device=dev).to(torch.bfloat16)
+        dt = torch.nn.functional.softplus(torch.randn(s.B, s.L, s.H, generator=g, device=dev) - 2)
+        w = (torch.rand(s.C, s.K, generator=g, device=dev) - 0.5).contiguous()
+        b = torch.rand(s.C, generator=g, device=dev) - 0.5
+        A = -torch.exp(torch.rand(s.H, generator=g, device=dev) * math.log(16.0))
+        return x, dt.contiguous(), w, b, A
+
+    # unfused conv at the 1.3B shape, with conv states in and out
+    s = workloads.shape_of("layer1p3b")
+    x, dt, w, b, A = prefill_inputs(s, 11)
+    init = torch.zeros(s.B, s.C, s.K - 1, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(x)
+    fin = torch.empty_like(init)
+    ms = _time_gpu(torch, lambda: ssm.conv1d_fwd(x, w, b, initial_state=init, activation="silu",
+                                                  final_state=fin, out=out), 10)
+    rep("conv1d_fwd", f"B{s.B} L{s.L} C{s.C} K{s.K} bf16 SiLU, states in/out", ms, s.B * s.L,
+        2 * s.B * s.L * s.C * 2 + 2 * s.B * s.C * (s.K - 1) * 2 + s.C * (s.K + 1) * 4)
+    del x, out
+
+    # 370M-like prefill, zero initial states
+    s = workloads.shape_of("layer370m")
+    x, dt, w, b, A = prefill_inputs(s, 12)
+    ws = torch.empty(ssm.workspace_size(s.B, s.L, s.H, s.P, s.G, s.N), dtype=torch.uint8, device=dev)
+    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, workspace=ws), 10)
+    nb = s.B * s.L * (s.C * 2 + s.H * 4 + s.H * s.P * 2) + s.B * s.H * s.P * s.N * 4 + s.B * s.C * (s.K - 1) * 2
+    rep("conv_scan_fwd", f"370M-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N}, zero initial state", ms,
+        s.B * s.L, nb)
+    del x, ws
+
+    # 780M-like layer, one 131072-token call
+    s = workloads.shape_of("layer780m")
+    x, dt, w, b, A = prefill_inputs(s, 13)
+    ws = torch.empty(ssm.workspace_size(s.B, s.L, s.H, s.P, s.G, s.N), dtype=torch.uint8, device=dev)
+    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, workspace=ws), 3, 1)
+    nb = s.B * s.L * (s.C * 2 + s.H * 4 + s.H * s.P * 2) + s.B * s.H * s.P * s.N * 4 + s.B * s.C * (s.K - 1) * 2
+    rep("conv_scan_fwd", f"780M-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N}, one call", ms, s.B * s.L, nb)
+    del x, ws
+
+    # decode step: conv update + SSM step on 512-slot pools, 256 requests
+    d = workloads.DECODE
+    H, P, N, G, K = d["H"], d["P"], d["N"], d["G"], d["K"]
+    C = H * P + 2 * G * N
+    R, S = d["R"], d["n_slots"]
+    g.manual_seed(14)
+    conv_pool = torch.randn(S, C, d["state_len"], generator=g, device=dev).to(torch.bfloat16)
+    ssm_pool = torch.randn(S, H, P, N, generator=g, device=dev)
+    idx = torch.randperm(S, generator=g, device=dev)[:R].to(torch.int32)
+    seqlens = torch.randint(0, d["max_seqlen"] + 1, (R,), generator=g, device=dev).to(torch.int32)
+    w = (torch.rand(C, K, generator=g, device=dev) - 0.5).contiguous()
+    b = torch.rand(C, generator=g, device=dev) - 0.5
+    A = -torch.exp(torch.rand(H, generator=g, device=dev) * math.log(16.0))
+    for L_new in (1, 4):
+        xn = torch.randn(R, C, L_new, generator=g, device=dev).to(torch.bfloat16)
+        dtn = torch.nn.functional.softplus(torch.randn(R, L_new, H, generator=g, device=dev) - 2).contiguous()
+        ms = _time_gpu(torch, lambda: ssm.decode_step(xn, conv_pool, w, b, dtn, A, ssm_pool, H, P, G, N,
+                                                       conv_state_indices=idx, cache_seqlens=seqlens), 20)
+        nb = (2 * R * H * P * N * 4 + 2 * R * C * d["state_len"] * 2 + 3 * R * C * L_new * 2
+              + R * L_new * H * 4 + R * L_new * H * P * 2)
+        rep("decode_step", f"{R} requests, {S}-slot pools (1.3B dims), L_new {L_new}", ms, R * L_new, nb)
+    return res
+
+
 def cpu_baseline(s, w, b, A, inp, cinit, sinit):
     import oracle
     t0 = time.perf_counter()
@@ -80,6 +174,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-ops", action="store_true",
+                    help="skip the bandwidth figures of the other entry points")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times), the reference "
                          "the HBM traffic counters are scaled by")
@@ -174,7 +270,11 @@ def main():
                         "achieved_GBs": op_bytes / (ms_per_step * 1e-3) / 1e9,
                         "frac": op_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "cpu_baseline": None,
+        "other_ops": None,
     }
+    if not args.no_other_ops:
+        log("bench: other entry points")
+        result["other_ops"] = other_ops(torch, ssm, workloads)
     if not args.no_cpu_baseline:
         log("bench: fp64 oracle on the host (cpu baseline)")
         result["cpu_baseline"] = cpu_baseline(s, w, b, A, inp, cinit.cpu(), sinit.cpu())
