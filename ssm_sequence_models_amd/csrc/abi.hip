@@ -156,7 +156,7 @@ size_t ssm_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, in
         !valid_dtype(dtype))
         return 0;
     if (ssm::chunked_supported(headdim, dstate, dtype))
-        return ssm::chunked_workspace_bytes(batch, seqlen, ngroups, dstate);
+        return ssm::chunked_workspace_bytes(batch, seqlen, nheads, ngroups, dstate);
     // general-shape path of the fused call: the conv output is staged in the workspace
     return static_cast<size_t>(batch * seqlen * (nheads * headdim + 2 * ngroups * dstate)) *
            esize(dtype);
@@ -245,7 +245,7 @@ ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const 
                                                        batch * nheads * headdim * dstate, s),
                           fn);
     if (ssm::chunked_supported(headdim, dstate, dtype)) {
-        const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, ngroups, dstate);
+        const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, nheads, ngroups, dstate);
         if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
             return fail(SSM_ERR_WORKSPACE, "ssm_scan_fwd: workspace must be >= " +
                                                std::to_string(need) + " bytes, 16-byte aligned");
@@ -331,7 +331,7 @@ ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float
         return hip_status(e, fn);
     }
     if (ssm::chunked_supported(headdim, dstate, dtype)) {
-        const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, ngroups, dstate);
+        const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, nheads, ngroups, dstate);
         if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
             return fail(SSM_ERR_WORKSPACE, "ssm_conv_scan_fwd: workspace must be >= " +
                                                std::to_string(need) + " bytes, 16-byte aligned");

@@ -149,7 +149,7 @@ hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream
 
 // Chunked (SSD) scan on MFMA for bf16 inputs with headdim 64, dstate 128.
 bool chunked_supported(int64_t P, int64_t N, ssm_dtype_t dtype);
-size_t chunked_workspace_bytes(int64_t B, int64_t L, int64_t G, int64_t N);
+size_t chunked_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t G, int64_t N);
 struct ChunkedArgs {
     // x channels: element (b, t, h*P + p) at x[(b*L + t)*x_row + x_col0 + h*P + p]  (bf16)
     const uint16_t* x;
@@ -175,7 +175,13 @@ struct ChunkedArgs {
     const int32_t* seq_idx;     // [B, L] or NULL
     uint16_t* y;                // [B, L, H, P]
     int64_t B, L, H, P, G, N;
-    void* workspace;            // chunked_workspace_bytes(B, L, G, N)
+    void* workspace;            // chunked_workspace_bytes(B, L, H, G, N)
+    // Set by launch_chunked.  Rows with few heads split into nseg segments of seg_chunks
+    // chunks run side by side: seg_state [B, H, nseg, P, N] holds each segment's entry state
+    // (first its local end state), seg_decay [B, H, nseg] each segment's decay product.
+    int64_t nseg, seg_chunks;
+    float* seg_state;
+    float* seg_decay;
 };
 hipError_t launch_chunked(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev_before_main,
                           hipEvent_t ev_after_main);

@@ -374,27 +374,28 @@ __device__ __forceinline__ void dma16(Rsrc r, uint32_t voff, uint8_t* lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
-// Chunk k's C / B^T tiles into tile stage `st`
+// Chunk k's C / B^T tiles into tile stage `st` (the state-only pass needs B^T alone)
+template <int PASS>
 __device__ __forceinline__ void fetch_tiles(const Blk& bk, const POff& o, int64_t k, int pw,
                                             uint8_t* st) {
     const Rsrc rc = make_rsrc(bk.wsC + k * bk.ws_step * kWsC, kWsC * 2);
     const Rsrc rb = make_rsrc(bk.wsBt + k * bk.ws_step * kWsBt, kWsBt * 2);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        dma16(rc, o.c[q], st + kCbC + (4 * pw + q) * 1024);
+        if (PASS == 0) dma16(rc, o.c[q], st + kCbC + (4 * pw + q) * 1024);
         dma16(rb, o.bt[q], st + kCbBt + (4 * pw + q) * 1024);
     }
 }
 
-// Chunk k's G pieces, dt and ids into registers
-template <bool HAS_SEQ>
+// Chunk k's G pieces (not in the state-only pass), dt and ids into registers
+template <bool HAS_SEQ, int PASS>
 __device__ __forceinline__ void fetch_regs(const Blk& bk, const POff& o, int64_t k, int pw,
                                            int lane, Fetch& f) {
     const int t0 = static_cast<int>(k) * kQ;
     const Rsrc rg = make_rsrc(bk.wsG + k * bk.ws_step * kWsG, kWsG * 4);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        if (unit_valid(pw, u)) {
+        if (PASS == 0 && unit_valid(pw, u)) {
             f.gm[u][0] = bload128(rg, o.g[u]);
             f.gm[u][1] = bload128(rg, o.g[u] + 16);
         }
@@ -432,10 +433,11 @@ __device__ __forceinline__ void fetch_raw(const Blk& bk, const POff& o, int64_t 
     }
 }
 
-// raw x rows of chunk 0 (rows before token 0 come from the conv state), straight to LDS
+// raw x rows of a block's first chunk (first token t0; rows before token 0 come from the
+// conv state), straight to LDS
 template <int K, bool FUSED, bool HAS_SEQ>
 __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk& bk, int64_t b,
-                                                int64_t h, int pw, int lane, uint8_t* raw) {
+                                                int64_t h, int t0, int pw, int lane, uint8_t* raw) {
     constexpr int kRows = kQ + K - 1;
     const int ptid = pw * 64 + lane;
 #pragma unroll
@@ -443,7 +445,7 @@ __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk&
         const int idx = ptid + 256 * k;
         if (idx < kRows * 8) {
             const int rho = idx >> 3, q = idx & 7;
-            const int t = rho - (K - 1);
+            const int t = t0 + rho - (K - 1);
             u32x4 v = {0u, 0u, 0u, 0u};
             if (t >= 0 && t < bk.L) {
                 v = *reinterpret_cast<const u32x4*>(bk.x + static_cast<int64_t>(t) * bk.x_row + q * 8);
@@ -462,7 +464,7 @@ __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk&
         }
     }
     if (HAS_SEQ && ptid < kRows) {
-        int tr = ptid - (K - 1);
+        int tr = t0 + ptid - (K - 1);
         tr = tr < 0 ? 0 : (tr >= bk.L ? bk.L - 1 : tr);
         reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = bk.seq[tr];
     }
@@ -472,7 +474,7 @@ __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk&
 //   cum2_j = log2(e) * sum_{tau<=j} dt_tau A (wave prefix scan), r_j = last reset <= j,
 //   E_i = 2^cum2_i, W_j = 2^(cum2_last - cum2_j) dt_j, decay = 2^cum2_last,
 //   M[i][j] = G[i][j] 2^(cum2_i - cum2_j) dt_j on r_i <= j <= i (G is 0 above the diagonal)
-template <bool HAS_SEQ>
+template <bool HAS_SEQ, int PASS>
 __device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, float Ah2,
                                               int pw, int lane, uint8_t* st, uint8_t* ps) {
     float* pcum = reinterpret_cast<float*>(ps);
@@ -501,6 +503,7 @@ __device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, 
         sW[j] = j >= r_last ? __builtin_amdgcn_exp2f(cum_last - cum) * dtv : 0.0f;
         if (j == 0) *reinterpret_cast<float*>(st + kStDecay) = r_last < 0 ? __builtin_amdgcn_exp2f(cum_last) : 0.0f;
     }
+    if (PASS == 1) return;  // the state-only pass needs W and the decay alone
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         if (!unit_valid(pw, u)) continue;
@@ -624,7 +627,9 @@ __device__ __forceinline__ bf16x8 conv_fix(const uint8_t* raw, int p, int j0,
     return x;
 }
 
-template <int K, int MODE, bool HAS_SEQ>
+// PASS 0: the full scan of a block's chunks.  PASS 1 (long rows split into segments): the
+// end state of every segment but the last from a zero start, and its decay product.
+template <int K, int MODE, bool HAS_SEQ, int PASS>
 __global__ void __launch_bounds__(kMainThreads, 1)
 ssd_main_kernel(ChunkedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t sm[kMainLds];
@@ -634,15 +639,20 @@ ssd_main_kernel(ChunkedArgs a) {
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
     const int role = wave >> 2;  // 0 consumer, 1 producer, 2 conv
 
-    // block -> (row, head): consecutive units on one XCD (blocks are dealt round-robin over
-    // the 8 XCDs), so the heads of one row share that XCD's L2 for the B/C/G tiles
+    // block -> (row, segment, head): consecutive units on one XCD (blocks are dealt round-robin
+    // over the 8 XCDs), so the heads of one row segment share that XCD's L2 for the B/C/G tiles
+    const int64_t nsl = PASS == 1 ? a.nseg - 1 : a.nseg;
     const int64_t nblk = gridDim.x;
     const int64_t kb = blockIdx.x;
     const int64_t u = (nblk % 8 == 0) ? (kb % 8) * (nblk / 8) + kb / 8 : kb;
-    const int64_t b = u / a.H, h = u % a.H;
+    const int64_t h = u % a.H, bsg = u / a.H;
+    const int64_t b = bsg / nsl, seg = bsg % nsl;
     const int64_t g = h / (a.H / a.G);
     const int64_t L = a.L;
     const int64_t nC = (L + kQ - 1) / kQ;
+    // this block's chunks: global chunk c0 + c for c < nCl
+    const int64_t c0 = seg * a.seg_chunks;
+    const int64_t nCl = min(a.seg_chunks, nC - c0);
     const float Ah = a.A[h];
     Blk bk;
     bk.x = a.x + b * L * a.x_row + a.x_col0 + h * kP;
@@ -678,7 +688,10 @@ ssd_main_kernel(ChunkedArgs a) {
         const int p_own = 16 * wave + li;
         f32x4 acc[8];
         {
-            const float* src = a.init_state ? a.init_state + ((b * a.H + h) * kP + p_own) * kN : nullptr;
+            const float* src =
+                PASS == 1 ? nullptr
+                : a.nseg > 1 ? a.seg_state + (((b * a.H + h) * a.nseg + seg) * kP + p_own) * kN
+                : a.init_state ? a.init_state + ((b * a.H + h) * kP + p_own) * kN : nullptr;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
@@ -695,7 +708,8 @@ ssd_main_kernel(ChunkedArgs a) {
         // X operands (lane: channel p_own, tokens 32 s + 8 g4 .. +7), convolved by the conv
         // wave with this wave's index
         const int xoff = (wave * 64 + lane) * 32;
-        for (int64_t cn = 0; cn < nC; ++cn) {
+        float dprod = 1.0f;  // decay product of the block's chunks (state-only pass)
+        for (int64_t cn = 0; cn < nCl; ++cn) {
             const uint8_t* st = sm + (cn & 1) * kStageBytes;
             const uint8_t* cbt = sm_cb + (cn & 1) * kCbBytes;
             uint8_t* yt = sm + kOffY + (cn & 1) * kYBytes;
@@ -725,6 +739,7 @@ ssd_main_kernel(ChunkedArgs a) {
                 yo[I] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 yi[I] = yo[I];
             }
+            if constexpr (PASS == 0) {
             // intra-chunk part: M tiles (I, s) with 32 s <= 16 I + 15
             bf16x8 mh[6], ml[6];
 #pragma unroll
@@ -768,6 +783,7 @@ ssd_main_kernel(ChunkedArgs a) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) yo[I] = mfma(hlo, cb[m & 1][I], yo[I]);
             }
+            }
             // state update: h^T[n][p] = decay h^T + B^T (W o X)
 #pragma unroll
             for (int t = 0; t < 8; ++t) acc[t] *= decay;
@@ -789,24 +805,36 @@ ssd_main_kernel(ChunkedArgs a) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) acc[t] = mfma(bv[t], bl, acc[t]);
             }
-            // y tile of this chunk -> LDS (the producers store it next iteration)
+            if constexpr (PASS == 0) {
+                // y tile of this chunk -> LDS (the producers store it next iteration)
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                uint2 pk;
-                pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
-                pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
-                lds_st(yt, sw_y(16 * I + li, 4 * wave + g4), pk);
+                for (int I = 0; I < 4; ++I) {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
+                    pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
+                    lds_st(yt, sw_y(16 * I + li, 4 * wave + g4), pk);
+                }
+            } else {
+                dprod *= decay;
             }
             __syncthreads();
         }
-        if (a.final_state) {
-            float* dst = a.final_state + ((b * a.H + h) * kP + p_own) * kN;
+        // end state: a segment's local end state goes to the next segment's entry slot (the
+        // combine step turns it into that segment's entry state); the last segment (or the
+        // only one) writes the final state
+        float* dst = nullptr;
+        if (PASS == 1)
+            dst = a.seg_state + (((b * a.H + h) * a.nseg + seg + 1) * kP + p_own) * kN;
+        else if (a.final_state && seg == a.nseg - 1)
+            dst = a.final_state + ((b * a.H + h) * kP + p_own) * kN;
+        if (dst) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4) = acc[2 * m];
                 *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
             }
         }
+        if (PASS == 1 && wave == 0 && lane == 0) a.seg_decay[(b * a.H + h) * a.nseg + seg] = dprod;
     } else if (role == 1) {
         const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
         uint8_t* ps = sm + kOffPs + pw * kPsBytes;
@@ -843,53 +871,55 @@ ssd_main_kernel(ChunkedArgs a) {
         constexpr int kRows = kQ + K - 1;
         Fetch fa, fb;
         int32_t seq_row = 0;
-        // prologue: chunk 0's tiles, registers and raw rows, chunk 1's raw rows and
-        // registers; then chunk 0 produced
-        fetch_tiles(bk, o, 0, pw, sm_cb);
-        fetch_regs<HAS_SEQ>(bk, o, 0, pw, lane, fa);
-        if (nC > 1) fetch_raw<K, HAS_SEQ>(bk, o, 1, pw, lane, sm_raw + kRawBytes, &seq_row);
-        stage_raw_first<K, MODE != 0, HAS_SEQ>(a, bk, b, h, pw, lane, sm_raw);
+        // prologue: the block's first chunk's tiles, registers and raw rows, the second
+        // chunk's raw rows and registers; then the first chunk produced.  Local chunk c is
+        // global chunk c0 + c (LDS slots go by the local index, memory by the global one).
+        fetch_tiles<PASS>(bk, o, c0, pw, sm_cb);
+        fetch_regs<HAS_SEQ, PASS>(bk, o, c0, pw, lane, fa);
+        if (nCl > 1) fetch_raw<K, HAS_SEQ>(bk, o, c0 + 1, pw, lane, sm_raw + kRawBytes, &seq_row);
+        stage_raw_first<K, MODE != 0, HAS_SEQ>(a, bk, b, h, static_cast<int>(c0 * kQ), pw, lane, sm_raw);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        if (nC > 1) fetch_regs<HAS_SEQ>(bk, o, 1, pw, lane, fb);
-        if (HAS_SEQ && nC > 1 && ptid < kRows)
+        if (nCl > 1) fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + 1, pw, lane, fb);
+        if (HAS_SEQ && nCl > 1 && ptid < kRows)
             reinterpret_cast<int32_t*>(sm_raw + kRawBytes + kRwSeq)[ptid] = seq_row;
         __syncthreads();  // raw rows of chunk 0 staged
-        scalars_and_m<HAS_SEQ>(fa, 0, bk.L, Ah2, pw, lane, sm, ps);
+        scalars_and_m<HAS_SEQ, PASS>(fa, c0, bk.L, Ah2, pw, lane, sm, ps);
         __syncthreads();
         // chunk cn: load chunk cn+1's tiles (into stage (cn+1)&1, free since chunk cn-1 was
         // contracted), chunk cn+2's raw rows (into raw slot cn&1, free since chunk cn was
         // convolved) and chunk cn+2's registers; store y(cn-1), compute chunk cn+1's scalars
         // and M tiles from the registers loaded one chunk earlier.  Every load lands before
         // the barrier.  Unrolled by two so each register set keeps its registers.
-        for (int64_t cn = 0; cn < nC; cn += 2) {
+        for (int64_t cn = 0; cn < nCl; cn += 2) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int64_t c = cn + half;
-                if (c >= nC) break;
+                if (c >= nCl) break;
                 Fetch& cur = half == 0 ? fb : fa;   // chunk c+1
                 Fetch& nxt = half == 0 ? fa : fb;   // chunk c+2
                 const int64_t k = c + 1;
                 uint8_t* stk = sm + (k & 1) * kStageBytes;
-                if (k < nC) fetch_tiles(bk, o, k, pw, sm_cb + (k & 1) * kCbBytes);
-                if (k + 1 < nC) {
-                    fetch_raw<K, HAS_SEQ>(bk, o, k + 1, pw, lane, sm_raw + (c & 1) * kRawBytes, &seq_row);
-                    fetch_regs<HAS_SEQ>(bk, o, k + 1, pw, lane, nxt);
+                if (k < nCl) fetch_tiles<PASS>(bk, o, c0 + k, pw, sm_cb + (k & 1) * kCbBytes);
+                if (k + 1 < nCl) {
+                    fetch_raw<K, HAS_SEQ>(bk, o, c0 + k + 1, pw, lane, sm_raw + (c & 1) * kRawBytes, &seq_row);
+                    fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + k + 1, pw, lane, nxt);
                 }
                 // the y stores are the iteration's last vector-memory operations (the empty asm
                 // keeps the compiler from moving loads after them); the loads complete in issue
                 // order, so waiting until only the two stores are outstanding waits for every
                 // load, while the stores' write latency overlaps the next chunk
                 asm volatile("" ::: "memory");
-                if (c > 0) store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c - 1, pw, lane);
-                if (k < nC) scalars_and_m<HAS_SEQ>(cur, k, bk.L, Ah2, pw, lane, stk, ps);
-                if (c > 0) __builtin_amdgcn_s_waitcnt(kWaitVm2);
+                const bool stores = PASS == 0 && c > 0;
+                if (stores) store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c0 + c - 1, pw, lane);
+                if (k < nCl) scalars_and_m<HAS_SEQ, PASS>(cur, c0 + k, bk.L, Ah2, pw, lane, stk, ps);
+                if (stores) __builtin_amdgcn_s_waitcnt(kWaitVm2);
                 else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-                if (HAS_SEQ && k + 1 < nC && ptid < kRows)
+                if (HAS_SEQ && k + 1 < nCl && ptid < kRows)
                     reinterpret_cast<int32_t*>(sm_raw + (c & 1) * kRawBytes + kRwSeq)[ptid] = seq_row;
                 __syncthreads();
             }
         }
-        store_y(bk, o, sm + kOffY + ((nC - 1) & 1) * kYBytes, nC - 1, pw, lane);
+        if (PASS == 0) store_y(bk, o, sm + kOffY + ((nCl - 1) & 1) * kYBytes, c0 + nCl - 1, pw, lane);
     } else {
         const int cv = wave - 8;
         // the conv of channel p = 16 cv + li over tokens 32 s + 8 g4 .. +7 of a chunk, into
@@ -923,8 +953,8 @@ ssd_main_kernel(ChunkedArgs a) {
         __syncthreads();  // raw rows of chunk 0 staged
         conv_chunk(sm_raw, sm + kOffX);
         __syncthreads();
-        for (int64_t cn = 0; cn < nC; ++cn) {
-            if (cn + 1 < nC)
+        for (int64_t cn = 0; cn < nCl; ++cn) {
+            if (cn + 1 < nCl)
                 conv_chunk(sm_raw + ((cn + 1) & 1) * kRawBytes, sm + kOffX + ((cn + 1) & 1) * kXBytes);
             __syncthreads();
         }
@@ -933,7 +963,7 @@ ssd_main_kernel(ChunkedArgs a) {
     // ---- final conv state F = u[L .. L+K-2] for this head's x channels and for slice h of
     // the B / C channels: all reads first, then a barrier, then the writes, so an in-place
     // state pair is never read after being overwritten ----
-    if (MODE != 0 && a.conv_final) {
+    if (MODE != 0 && a.conv_final && PASS == 0 && seg == 0) {
         constexpr int km1 = K - 1;
         const int64_t nx = kP * km1;
         const int64_t nbc_all = 2 * a.G * kN * km1;
@@ -975,12 +1005,43 @@ ssd_main_kernel(ChunkedArgs a) {
     }
 }
 
-template <int K, int MODE>
-hipError_t launch_main(const ChunkedArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.B * a.H));
-    if (a.seq_idx) ssd_main_kernel<K, MODE, true><<<grid, kMainThreads, 0, stream>>>(a);
-    else ssd_main_kernel<K, MODE, false><<<grid, kMainThreads, 0, stream>>>(a);
+// Entry states of the segments, in order: e_0 = h_{-1} (or 0), e_s = D_{s-1} e_{s-1} + l_{s-1},
+// where l_{s-1} (the local end state of segment s-1 from a zero start) sits in e_s's slot and
+// D_{s-1} is that segment's decay product (0 if a reset falls inside it).  This is [LG]
+// Sec. 2.5's increment, applied to the state a segment starts from.
+__global__ void __launch_bounds__(256) seg_combine_kernel(ChunkedArgs a) {
+    const int64_t per = static_cast<int64_t>(kP) * kN;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= a.B * a.H * per) return;
+    const int64_t bh = i / per, e = i % per;
+    float hs = a.init_state ? a.init_state[bh * per + e] : 0.0f;
+    float* st = a.seg_state + bh * a.nseg * per + e;
+    st[0] = hs;
+    for (int64_t sg = 1; sg < a.nseg; ++sg) {
+        hs = a.seg_decay[bh * a.nseg + sg - 1] * hs + st[sg * per];
+        st[sg * per] = hs;
+    }
+}
+
+template <int K, int MODE, int PASS>
+hipError_t launch_main(const ChunkedArgs& a, hipStream_t stream, int64_t nsl) {
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * nsl));
+    if (a.seq_idx) ssd_main_kernel<K, MODE, true, PASS><<<grid, kMainThreads, 0, stream>>>(a);
+    else ssd_main_kernel<K, MODE, false, PASS><<<grid, kMainThreads, 0, stream>>>(a);
     return hipGetLastError();
+}
+
+template <int K, int MODE>
+hipError_t launch_passes(const ChunkedArgs& a, hipStream_t stream) {
+    if (a.nseg > 1) {
+        hipError_t e = launch_main<K, MODE, 1>(a, stream, a.nseg - 1);
+        if (e != hipSuccess) return e;
+        const int64_t n = a.B * a.H * kP * kN;
+        seg_combine_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_main<K, MODE, 0>(a, stream, a.nseg);
 }
 
 template <int K>
@@ -993,13 +1054,33 @@ hipError_t launch_k(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev0, hi
     if (e != hipSuccess) return e;
     if (ev0) (void)hipEventRecord(ev0, stream);
     if (!a.fused_conv) {
-        if constexpr (K == 2) e = launch_main<K, 0>(a, stream);  // no conv: one halo row
+        if constexpr (K == 2) e = launch_passes<K, 0>(a, stream);  // no conv: one halo row
         else e = hipErrorInvalidValue;
     }
-    else if (a.act == SSM_ACT_SILU) e = launch_main<K, 2>(a, stream);
-    else e = launch_main<K, 1>(a, stream);
+    else if (a.act == SSM_ACT_SILU) e = launch_passes<K, 2>(a, stream);
+    else e = launch_passes<K, 1>(a, stream);
     if (ev1) (void)hipEventRecord(ev1, stream);
     return e;
+}
+
+// Rows with few heads leave most CUs idle on the per-(row, head) sequential scan; they are
+// split into segments (at least kMinSegChunks chunks each) so about kTargetBlocks blocks run.
+constexpr int64_t kTargetBlocks = 256;
+constexpr int64_t kMinSegChunks = 16;
+
+int64_t chunked_nseg(int64_t B, int64_t L, int64_t H) {
+    const int64_t nC = (L + kQ - 1) / kQ;
+    int64_t nseg = kTargetBlocks / (B * H);
+    nseg = nseg < nC / kMinSegChunks ? nseg : nC / kMinSegChunks;
+    if (nseg < 2) return 1;
+    const int64_t sc = (nC + nseg - 1) / nseg;
+    return (nC + sc - 1) / sc;  // every segment non-empty
+}
+
+size_t tile_workspace_bytes(int64_t B, int64_t L, int64_t G) {
+    const int64_t nC = (L + kQ - 1) / kQ;
+    const int64_t units = B * nC * G;
+    return static_cast<size_t>(units * (kWsC * 2 + kWsBt * 2 + kWsG * 4));
 }
 
 }  // namespace
@@ -1008,16 +1089,28 @@ bool chunked_supported(int64_t P, int64_t N, ssm_dtype_t dtype) {
     return dtype == SSM_BF16 && P == kP && N == kN;
 }
 
-size_t chunked_workspace_bytes(int64_t B, int64_t L, int64_t G, int64_t N) {
+size_t chunked_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t G, int64_t N) {
     if (N != kN) return 0;
-    const int64_t nC = (L + kQ - 1) / kQ;
-    const int64_t units = B * nC * G;
-    return static_cast<size_t>(units * (kWsC * 2 + kWsBt * 2 + kWsG * 4));
+    size_t bytes = (tile_workspace_bytes(B, L, G) + 255) / 256 * 256;
+    const int64_t nseg = chunked_nseg(B, L, H);
+    if (nseg > 1) bytes += static_cast<size_t>(B * H * nseg * (kP * kN + 1)) * 4;
+    return bytes;
 }
 
-hipError_t launch_chunked(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev_before_main,
+hipError_t launch_chunked(const ChunkedArgs& args, hipStream_t stream, hipEvent_t ev_before_main,
                           hipEvent_t ev_after_main) {
-    if (a.B == 0 || a.L == 0) return hipSuccess;
+    if (args.B == 0 || args.L == 0) return hipSuccess;
+    ChunkedArgs a = args;
+    const int64_t nC = (a.L + kQ - 1) / kQ;
+    a.nseg = chunked_nseg(a.B, a.L, a.H);
+    a.seg_chunks = (nC + a.nseg - 1) / a.nseg;
+    a.seg_state = nullptr;
+    a.seg_decay = nullptr;
+    if (a.nseg > 1) {
+        const size_t off = (tile_workspace_bytes(a.B, a.L, a.G) + 255) / 256 * 256;
+        a.seg_state = reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + off);
+        a.seg_decay = a.seg_state + a.B * a.H * a.nseg * kP * kN;
+    }
     switch (a.K) {
         case 2: return launch_k<2>(a, stream, ev_before_main, ev_after_main);
         case 3: return launch_k<3>(a, stream, ev_before_main, ev_after_main);

@@ -48,6 +48,9 @@ def test_workspace_query():
     # chunked path: per (row, chunk of 64, group): C 16 KiB + B^T 16 KiB + G 16 KiB
     assert s.workspace_size(4, 8192, 64, 64, 1, 128) == 4 * 128 * 48 * 1024
     assert s.workspace_size(2, 65, 4, 64, 2, 128) == 2 * 2 * 2 * 48 * 1024
+    # few heads on a long row: 5 segments of 410 chunks (256 CUs / 48 heads, at least 16
+    # chunks each), plus each segment's entry state [P, N] fp32 and decay product
+    assert s.workspace_size(1, 131072, 48, 64, 1, 128) == 2048 * 48 * 1024 + 48 * 5 * (64 * 128 + 1) * 4
     # general shapes: room for the conv output of the fused call
     import torch
     assert s.workspace_size(1, 64, 1, 4, 1, 4, torch.float32) == 64 * 12 * 4

@@ -30,6 +30,7 @@ def _scan_inputs(B, L, H, P, N, G, dtype, seed, with_init=True, segs=0):
 
 SCAN_CASES = [
     # B, L, H, P, N, G, dtype, init, segments
+    (1, 3072, 2, 64, 128, 1, BF16, True, 3),   # few heads: the row runs as 3 segments of 16 chunks
     (2, 200, 4, 64, 128, 1, BF16, True, 0),    # chunked: 3 full chunks + ragged 8
     (2, 200, 4, 64, 128, 2, BF16, True, 0),    # two groups
     (2, 200, 4, 64, 128, 1, BF16, True, 4),    # packed sequences
@@ -86,6 +87,8 @@ def _fused_inputs(B, L, H, P, N, G, K, dtype, seed, with_init=True, segs=0):
 FUSED_CASES = [
     # B, L, H, P, N, G, K, dtype, init, segments
     (1, 64, 1, 4, 4, 1, 4, F32, True, 0),      # the tiny layer
+    (1, 3072, 2, 64, 128, 1, 4, BF16, True, 4),  # few heads: 3 row segments, ids change inside them
+    (2, 3000, 1, 64, 128, 1, 3, BF16, True, 0),  # 2 row segments of 24 + 23 chunks (ragged)
     (2, 200, 4, 64, 128, 1, 4, BF16, True, 0),
     (2, 200, 4, 64, 128, 1, 4, BF16, True, 4),
     (2, 200, 4, 64, 128, 2, 4, BF16, False, 0),
@@ -130,6 +133,23 @@ def test_conv_scan_fwd_inplace_states_and_len0():
     assert_close(y, ry, "y (in place)")
     assert_close(ss, rs, "ssm state (in place)")
     assert_bitexact(cs, torch.from_numpy(rc).to(BF16), "conv state (in place)")
+
+
+def test_conv_scan_fwd_segmented_inplace_states():
+    """A row long enough to run as segments side by side, with both state pairs updated in
+    place (the final states overwrite the initial ones)."""
+    import ssm_sequence_models_amd as ssm
+    H, P, N, G, K = 2, 64, 128, 1, 4
+    xBC, w, b, dt, A, cinit, sinit, _ = _fused_inputs(1, 4096, H, P, N, G, K, BF16, seed=23)
+    cs, ss = dev(cinit).clone(), dev(sinit).clone()
+    y, _, _ = ssm.conv_scan_fwd(dev(xBC), dev(w), dev(b), dev(dt), dev(A), H, P, G, N,
+                                conv_initial_state=cs, initial_state=ss, conv_final_state=cs,
+                                final_state=ss)
+    torch.cuda.synchronize()
+    ry, rc, rs = oracle.conv_scan_fwd(xBC, w, b, cinit, dt, A, sinit, None, H, P, G, N)
+    assert_close(y, ry, "y (segments, in place)")
+    assert_close(ss, rs, "ssm state (segments, in place)")
+    assert_bitexact(cs, torch.from_numpy(rc).to(BF16), "conv state (segments, in place)")
 
 
 def test_conv_scan_fwd_chunked_calls_equal_one_call():
