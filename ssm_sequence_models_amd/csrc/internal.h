@@ -61,10 +61,12 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 }
 
 // bf16(phi(z)) for a conv sum z held in double (exact products of fp32 weights and 16-bit
-// inputs), rounded as the exact phi(z) rounds.  SiLU runs in fp32; its error is below
-// 4 + 2|z| fp32 ulps (argument rounding through the condition number 1 + |z|, the exp
-// argument's relative rounding, v_exp / v_rcp and three roundings).  Only results closer
-// than twice that to a bf16 rounding midpoint are recomputed in double, so the rounding
+// inputs), rounded as the exact phi(z) rounds.  SiLU runs in fp32.  To first order its
+// relative error is below (7 + 3|z|) u, u = 2^-24: the rounding of z to fp32 through the
+// condition number 1 + |z|; the rounding of the exp argument, which scales e^-z by up to
+// 2|z| u; v_exp and v_rcp at one ulp (2u) each; and the roundings of 1 + e and of the
+// product.  A relative error r is at most r / u ulps of the result, so results within
+// 8 + 4|z| ulps of a bf16 rounding midpoint are recomputed in double and the rounding
 // decision matches the exact value's.
 __device__ __forceinline__ float silu_f32(double z, bool& near_midpoint) {
     const float zf = static_cast<float>(z);

@@ -280,13 +280,14 @@ constexpr int kStageBytes = kStDecay + 16;
 //   while chunk c is contracted
 constexpr int kRowsMax = kQ + kKmax - 1;         // raw x rows of a chunk incl. the conv halo
 constexpr int kRwX = 0;                          // raw x [rows][8 pieces], piece ^ xr_swz(row)
-constexpr int kRwSeq = kRowsMax * 128;           // seq ids of the raw rows
+constexpr int kRwSeq = (kRowsMax + 1) * 128;     // seq ids of the raw rows (after 72 row slots:
+                                                 // the loads fill 9 blocks of 8 rows)
 constexpr int kRawBytes = kRwSeq + 72 * 4;
 //   y slot (two, by chunk parity): consumers write their Y^T tiles, producers store whole
 //   token rows one chunk later
 constexpr int kYBytes = kQ * kP * 2;             // [64 tok][16 slots of 8 B], slot ^ (tok & 15)
 //   producer-private scalars: cum, dtv, r of the chunk
-constexpr int kPsBytes = 3 * kQ * 4;
+constexpr int kPsBytes = 4 * kQ * 4;  // per producer wave: cum2, dt, last reset, R
 //   X slot (two, by chunk parity): the conv waves' bf16 outputs (X operands), 16 bytes per
 //   (wave, lane, run), read back by the consumer lane with the same wave-in-role and lane index
 constexpr int kXBytes = kQ * kP * 2;
@@ -311,11 +312,14 @@ __device__ __forceinline__ int sw_xr(int row, int q) {
 __device__ __forceinline__ int sw_y(int tok, int slot8) { return tok * 128 + ((slot8 ^ (tok & 15)) << 3); }
 
 // M tiles computed by each producer wave pw (uniform): unit u is the 16 x 32 tile (row
-// block I, column half S); the six tiles cover j <= i.
-//   pw 0: (0,0) (3,0)   pw 1: (1,0) (2,1)   pw 2: (2,0)   pw 3: (3,1)
-__device__ __forceinline__ int unit_I(int pw, int u) { return u == 0 ? pw : 3 - pw; }
-__device__ __forceinline__ int unit_S(int pw, int u) { return u == 0 ? (pw == 3 ? 1 : 0) : pw; }
-__device__ __forceinline__ bool unit_valid(int pw, int u) { return u == 0 || pw < 2; }
+// block I, column half S); the six tiles cover j <= i.  Waves 2 and 3 have one tile each
+// and compute it twice (identical values to identical addresses), which keeps the code free
+// of branches.
+//   pw 0: (0,0) (3,0)   pw 1: (1,0) (2,1)   pw 2: (2,0) (2,0)   pw 3: (3,1) (3,1)
+__device__ __forceinline__ int unit_I(int pw, int u) { return (u == 0 || pw >= 2) ? pw : 3 - pw; }
+__device__ __forceinline__ int unit_S(int pw, int u) {
+    return (u == 0 || pw >= 2) ? (pw == 3 ? 1 : 0) : pw;
+}
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores past
 // it are dropped by the hardware range check, which handles the ragged last chunk.
@@ -323,7 +327,6 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
 // 11:8): wait until at most 0 / 2 vector-memory operations are outstanding
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm2 = 0x0F72;
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFFLL ? 0x7FFFFFFFLL : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
@@ -357,7 +360,7 @@ struct Blk {
 struct POff {
     uint32_t c[4];          // C tile LDS block r = 4 pw + k: token 4r + l/16, slot l%16
     uint32_t bt[4];         // B^T tile LDS block r = 4 pw + k: row n = 8r + l/8, slot l%8
-    uint32_t x[3];          // raw x LDS block r = pw + 4k: row 8r + l/8, slot l%8
+    uint32_t x[3];          // raw x LDS blocks r = pw, pw + 4, 8: row 8r + l/8, slot l%8
     uint32_t g[2];          // G piece of M unit u: row i, columns 8q .. 8q+7
     uint32_t dt;            // token = lane
     uint32_t y[2];          // y piece ptid + 256 k: token, 8 channels
@@ -395,7 +398,7 @@ __device__ __forceinline__ void fetch_regs(const Blk& bk, const POff& o, int64_t
     const Rsrc rg = make_rsrc(bk.wsG + k * bk.ws_step * kWsG, kWsG * 4);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        if (PASS == 0 && unit_valid(pw, u)) {
+        if (PASS == 0) {
             f.gm[u][0] = bload128(rg, o.g[u]);
             f.gm[u][1] = bload128(rg, o.g[u] + 16);
         }
@@ -405,29 +408,29 @@ __device__ __forceinline__ void fetch_regs(const Blk& bk, const POff& o, int64_t
     if (HAS_SEQ) {
         const Rsrc rs = make_rsrc(bk.seq + t0, static_cast<int64_t>(bk.L - t0) * 4);
         f.seq_j = static_cast<int32_t>(bload32(rs, lane * 4));
-        f.seq_prev = t0 > 0 ? bk.seq[t0 - 1] : 0;
+        f.seq_prev = bk.seq[t0 > 0 ? t0 - 1 : 0];
     }
 }
 
 // Raw x rows of chunk k >= 1 (first row t0 - (K-1) >= 0) into raw slot `raw`; rows past the
-// end arrive as zeros.  With seq_idx the rows' ids come back in *seq_row, to be stored once
-// the load has landed.
+// end arrive as zeros, and all of them when `live` is false.  Every wave loads LDS blocks pw
+// and pw + 4 (rows 0-63) and block 8 (rows 64-71, the same data from every wave), with no
+// branch.  With seq_idx the rows' ids come back in *seq_row, to be stored once the load has
+// landed.
 template <int K, bool HAS_SEQ>
-__device__ __forceinline__ void fetch_raw(const Blk& bk, const POff& o, int64_t k, int pw,
-                                          int lane, uint8_t* raw, int32_t* seq_row) {
+__device__ __forceinline__ void fetch_raw(const Blk& bk, const POff& o, int64_t k, bool live,
+                                          int pw, int lane, uint8_t* raw, int32_t* seq_row) {
     constexpr int kRows = kQ + K - 1;
-    const int r0 = static_cast<int>(k) * kQ - (K - 1);
+    const int r0 = live ? static_cast<int>(k) * kQ - (K - 1) : 0;
     const Rsrc rx = make_rsrc(bk.x + static_cast<int64_t>(r0) * bk.x_row,
-                              static_cast<int64_t>(bk.L - r0) * bk.x_row * 2);
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        const int r = pw + 4 * q;
-        if (8 * r < kRows && 8 * r + (lane >> 3) < kRows) dma16(rx, o.x[q], raw + kRwX + r * 1024);
-    }
+                              live ? static_cast<int64_t>(bk.L - r0) * bk.x_row * 2 : 0);
+    dma16(rx, o.x[0], raw + kRwX + pw * 1024);
+    dma16(rx, o.x[1], raw + kRwX + (pw + 4) * 1024);
+    dma16(rx, o.x[2], raw + kRwX + 8 * 1024);
     if (HAS_SEQ) {
         const int ptid = pw * 64 + lane;
         if (ptid < kRows) {
-            const Rsrc rs = make_rsrc(bk.seq + r0, static_cast<int64_t>(bk.L - r0) * 4);
+            const Rsrc rs = make_rsrc(bk.seq + r0, live ? static_cast<int64_t>(bk.L - r0) * 4 : 0);
             *seq_row = static_cast<int32_t>(bload32(rs, ptid * 4));
         }
     }
@@ -473,17 +476,25 @@ __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk&
 // Chunk scalars and this wave's M tiles for chunk k, from the fetched dt / ids / G pieces:
 //   cum2_j = log2(e) * sum_{tau<=j} dt_tau A (wave prefix scan), r_j = last reset <= j,
 //   E_i = 2^cum2_i, W_j = 2^(cum2_last - cum2_j) dt_j, decay = 2^cum2_last,
-//   M[i][j] = G[i][j] 2^(cum2_i - cum2_j) dt_j on r_i <= j <= i (G is 0 above the diagonal)
+//   M[i][j] = G[i][j] 2^(cum2_i - cum2_j) dt_j on r_i <= j <= i (G is 0 above the diagonal).
+// A lane's M entries share the row i and a group of 8 columns j0 = 8 floor(j/8) .. j0+7, so
+// the exponential splits into 2^(cum2_i - cum2_j0) (one per lane) times
+// R_j = 2^(cum2_j0 - cum2_j) dt_j (one per column, shared by all rows).  That product stays in
+// range when cum2 never increases within the chunk and each group spans at most 64 (then
+// R_j <= 2^64 dt_j and the row factor <= 1 on and below the diagonal); a chunk that breaks
+// either condition takes one exponential per entry.
 template <bool HAS_SEQ, int PASS>
 __device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, float Ah2,
                                               int pw, int lane, uint8_t* st, uint8_t* ps) {
     float* pcum = reinterpret_cast<float*>(ps);
     float* pdtv = pcum + kQ;
     int32_t* pr = reinterpret_cast<int32_t*>(pdtv + kQ);
+    float* pR = reinterpret_cast<float*>(pr + kQ);
     const int t0 = static_cast<int>(k) * kQ;
     const int j = lane;
     const float dtv = __uint_as_float(f.dt);
-    const float cum = wave_incl_sum(dtv * Ah2);
+    const float a2 = dtv * Ah2;
+    const float cum = wave_incl_sum(a2);
     int r = -1;
     if (HAS_SEQ) {
         int32_t sjm1 = __shfl_up(f.seq_j, 1);
@@ -494,34 +505,55 @@ __device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, 
     pcum[j] = cum;
     pdtv[j] = dtv;
     if (HAS_SEQ) pr[j] = r;
-    if (pw == 0) {
+    {
+        // every producer wave writes the same E / W / decay values (no branch)
         const float cum_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kQ - 1));
         const int r_last = HAS_SEQ ? __builtin_amdgcn_readlane(r, kQ - 1) : -1;
         float* sE = reinterpret_cast<float*>(st + kStE);
         float* sW = reinterpret_cast<float*>(st + kStW);
         sE[j] = r < 0 ? __builtin_amdgcn_exp2f(cum) : 0.0f;
         sW[j] = j >= r_last ? __builtin_amdgcn_exp2f(cum_last - cum) * dtv : 0.0f;
-        if (j == 0) *reinterpret_cast<float*>(st + kStDecay) = r_last < 0 ? __builtin_amdgcn_exp2f(cum_last) : 0.0f;
+        // decay slot: lanes 0-3 of each wave write 4 copies; consumers read copy 0
+        const float dec = r_last < 0 ? __builtin_amdgcn_exp2f(cum_last) : 0.0f;
+        reinterpret_cast<float*>(st + kStDecay)[j & 3] = dec;
     }
     if (PASS == 1) return;  // the state-only pass needs W and the decay alone
+    // column factors: cum2 of the group's first column from lane j & ~7 (swizzle within
+    // 32-lane halves: and-mask 0x18)
+    const float cg = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(cum), 0x0018));
+    const float span = cg - cum;
+    pR[j] = __builtin_amdgcn_exp2f(span) * dtv;
+    const bool factored = __ballot(!(a2 <= 0.0f && span <= 64.0f)) == 0;  // NaN -> direct
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        if (!unit_valid(pw, u)) continue;
         const int I = unit_I(pw, u), S = unit_S(pw, u);
         const bool diag = 32 * S + 31 > 16 * I;
         const int i = 16 * I + (lane & 15), q = 4 * S + (lane >> 4), j0 = 8 * q;
         const float ci = pcum[i];
         const int ri = HAS_SEQ ? pr[i] : -1;
-        const f32x4 cj0 = lds_ld<f32x4>(ps, j0 * 4), cj1 = lds_ld<f32x4>(ps, j0 * 4 + 16);
-        const f32x4 dj0 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4), dj1 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4 + 16);
         float mv[8];
+        if (factored) {
+            const float prow = __builtin_amdgcn_exp2f(ci - pcum[j0]);
+            const f32x4 r0 = lds_ld<f32x4>(ps, 3 * kQ * 4 + j0 * 4), r1 = lds_ld<f32x4>(ps, 3 * kQ * 4 + j0 * 4 + 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float rj = e < 4 ? r0[e] : r1[e - 4];
+                mv[e] = __uint_as_float(f.gm[u][e >> 2][e & 3]) * rj * prow;
+            }
+        } else {
+            const f32x4 cj0 = lds_ld<f32x4>(ps, j0 * 4), cj1 = lds_ld<f32x4>(ps, j0 * 4 + 16);
+            const f32x4 dj0 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4), dj1 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4 + 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float cj = e < 4 ? cj0[e] : cj1[e - 4];
+                const float dj = e < 4 ? dj0[e] : dj1[e - 4];
+                mv[e] = __uint_as_float(f.gm[u][e >> 2][e & 3]) * __builtin_amdgcn_exp2f(ci - cj) * dj;
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float cj = e < 4 ? cj0[e] : cj1[e - 4];
-            const float dj = e < 4 ? dj0[e] : dj1[e - 4];
-            const float gv = __uint_as_float(f.gm[u][e >> 2][e & 3]);
-            float m = gv * __builtin_amdgcn_exp2f(ci - cj) * dj;
-            if (diag) m = j0 + e <= i ? m : 0.0f;   // 0 * inf above the diagonal
+            float m = mv[e];
+            if (diag) m = j0 + e <= i ? m : 0.0f;   // overflow / 0 * inf above the diagonal
             if (HAS_SEQ) m = j0 + e >= ri ? m : 0.0f;
             mv[e] = m;
         }
@@ -533,12 +565,13 @@ __device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, 
 }
 
 // Store the y rows of chunk k (left in `yt` by the consumers): whole 128-byte token rows,
-// two 16-byte pieces per producer lane; rows past the end are dropped by the range check
+// two 16-byte pieces per producer lane; rows past the end are dropped by the range check,
+// and all of them when `live` is false
 __device__ __forceinline__ void store_y(const Blk& bk, const POff& o, const uint8_t* yt,
-                                        int64_t k, int pw, int lane) {
+                                        int64_t k, bool live, int pw, int lane) {
     const int t0 = static_cast<int>(k) * kQ;
-    const Rsrc ry = make_rsrc(bk.y + static_cast<int64_t>(t0) * bk.H * kP,
-                              static_cast<int64_t>(bk.L - t0) * bk.H * kP * 2);
+    const Rsrc ry = make_rsrc(bk.y + static_cast<int64_t>(live ? t0 : 0) * bk.H * kP,
+                              live ? static_cast<int64_t>(bk.L - t0) * bk.H * kP * 2 : 0);
     const int ptid = pw * 64 + lane;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -555,7 +588,7 @@ __device__ __forceinline__ void store_y(const Blk& bk, const POff& o, const uint
 // (the rows already hold x); 1: conv, identity phi; 2: conv + SiLU.  The fast path has no
 // branches, so the scheduler can spread it between the contractions of the previous chunk;
 // for SiLU it flags, in *near, outputs that lie too close to a bf16 rounding midpoint for
-// the fp32 evaluation to decide (conv_fix redoes those in double).
+// the fp32 evaluation to decide (conv_fixups redoes those in double).
 template <int K, int MODE, bool HAS_SEQ>
 __device__ __forceinline__ double conv_z(const uint8_t* raw, int q, int byte, int r0,
                                          const double (&cw)[K], double cbias) {
@@ -607,24 +640,42 @@ __device__ __forceinline__ bf16x8 conv_fast(const uint8_t* raw, int p, int j0,
             out[e] = __builtin_bit_cast(__bf16, f64_to_bf16(z));
         }
     }
-    if (MODE == 2) *near |= nb << (8 * (j0 >> 5));   // bits 0-7: s = 0 run, 8-15: s = 1 run
+    if (MODE == 2) *near = nb;   // bit e: output e
     return out;
 }
 
-// Redo the flagged SiLU outputs of one run (tokens j0 + e) in double
-template <int K, bool HAS_SEQ>
-__device__ __forceinline__ bf16x8 conv_fix(const uint8_t* raw, int p, int j0,
-                                           const double (&cw)[K], double cbias, uint32_t near,
-                                           bf16x8 x) {
-    const int q = p >> 3, byte = (p & 7) * 2;
+// Redo, in double, the SiLU outputs of one run (tokens j0 .. j0+7) that conv_fast flagged.
+// Flagged outputs are rare: one branch skips everything when no lane has a flag, and each
+// output's recomputation is skipped when no lane has that one.
+template <int K, int MODE, bool HAS_SEQ>
+__device__ __forceinline__ bf16x8 conv_fixups(const uint8_t* raw, int p, int j0,
+                                              const double (&cw)[K], double cbias,
+                                              uint32_t near, bf16x8 x) {
+    if (MODE == 2 && near) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        if (near & (1u << e)) {
-            const double z = conv_z<K, 2, HAS_SEQ>(raw, q, byte, j0 + e, cw, cbias);
-            x[e] = __builtin_bit_cast(__bf16, silu_f64_to_bf16(z));
+        for (int e = 0; e < 8; ++e) {
+            if (near & (1u << e)) {
+                const double z = conv_z<K, 2, HAS_SEQ>(raw, p >> 3, (p & 7) * 2, j0 + e, cw, cbias);
+                x[e] = __builtin_bit_cast(__bf16, silu_f64_to_bf16(z));
+            }
         }
     }
     return x;
+}
+
+// conv weights and bias of x channel p of head h, as doubles (zeros without a conv)
+template <int K, int MODE>
+__device__ __forceinline__ void conv_weights(const ChunkedArgs& a, int64_t h, int p,
+                                             double (&cw)[K], double& cbias) {
+    cbias = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) cw[k] = 0.0;
+    if (MODE != 0) {
+        const int64_t cc = a.x_col0 + h * kP + p;
+#pragma unroll
+        for (int k = 0; k < K; ++k) cw[k] = a.conv_w[cc * K + k];
+        cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
+    }
 }
 
 // PASS 0: the full scan of a block's chunks.  PASS 1 (long rows split into segments): the
@@ -634,7 +685,10 @@ __global__ void __launch_bounds__(kMainThreads, 1)
 ssd_main_kernel(ChunkedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t sm[kMainLds];
     __shared__ __attribute__((aligned(16))) uint8_t sm_cb[2 * kCbBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t sm_raw[2 * kRawBytes];
+    // raw slots 0 and 1 are separate arrays, so the compiler can tell a load into one slot
+    // from reads of the other
+    __shared__ __attribute__((aligned(16))) uint8_t sm_raw0[kRawBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t sm_raw1[kRawBytes];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
     const int role = wave >> 2;  // 0 consumer, 1 producer, 2 conv
@@ -680,7 +734,7 @@ ssd_main_kernel(ChunkedArgs a) {
     //   consumers  contract chunk c from stage c&1 and X slot c&1, write y(c) to y slot c&1;
     //   producers  load chunk c+1's tiles into stage (c+1)&1 and chunk c+2's raw rows into
     //              raw slot c&1, store y(c-1) from y slot (c-1)&1, compute chunk c+1's
-    //              scalars and M tiles;
+    //              scalars and M tiles, then load chunk c+2's registers;
     //   conv waves convolve chunk c+1 from raw slot (c+1)&1 into X slot (c+1)&1.
     if (role == 0) {
         // state slice acc[t][r] = h[p][n], p = 16 wave + li, n = 32(t/2) + 8 g4 + 4(t%2) + r
@@ -851,7 +905,8 @@ ssd_main_kernel(ChunkedArgs a) {
             }
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
-                const int row = 8 * (pw + 4 * q) + (lane >> 3), sl = lane & 7;
+                const int blk = q < 2 ? pw + 4 * q : 8;
+                const int row = 8 * blk + (lane >> 3), sl = lane & 7;
                 o.x[q] = row * bk.x_row * 2 + ((sl ^ (((row >> 3) & 3) << 1)) << 4);
             }
 #pragma unroll
@@ -869,93 +924,81 @@ ssd_main_kernel(ChunkedArgs a) {
         }
         const int ptid = pw * 64 + lane;
         constexpr int kRows = kQ + K - 1;
-        Fetch fa, fb;
+        Fetch f;  // registers of the next chunk to produce
         int32_t seq_row = 0;
-        // prologue: the block's first chunk's tiles, registers and raw rows, the second
-        // chunk's raw rows and registers; then the first chunk produced.  Local chunk c is
-        // global chunk c0 + c (LDS slots go by the local index, memory by the global one).
+        // prologue: the block's first chunk's tiles, registers and raw rows and the second
+        // chunk's raw rows; then the first chunk produced.  Local chunk c is global chunk
+        // c0 + c (LDS slots go by the local index, memory by the global one).
         fetch_tiles<PASS>(bk, o, c0, pw, sm_cb);
-        fetch_regs<HAS_SEQ, PASS>(bk, o, c0, pw, lane, fa);
-        if (nCl > 1) fetch_raw<K, HAS_SEQ>(bk, o, c0 + 1, pw, lane, sm_raw + kRawBytes, &seq_row);
-        stage_raw_first<K, MODE != 0, HAS_SEQ>(a, bk, b, h, static_cast<int>(c0 * kQ), pw, lane, sm_raw);
+        fetch_regs<HAS_SEQ, PASS>(bk, o, c0, pw, lane, f);
+        fetch_raw<K, HAS_SEQ>(bk, o, c0 + 1, nCl > 1, pw, lane, sm_raw1, &seq_row);
+        stage_raw_first<K, MODE != 0, HAS_SEQ>(a, bk, b, h, static_cast<int>(c0 * kQ), pw, lane, sm_raw0);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        if (nCl > 1) fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + 1, pw, lane, fb);
         if (HAS_SEQ && nCl > 1 && ptid < kRows)
-            reinterpret_cast<int32_t*>(sm_raw + kRawBytes + kRwSeq)[ptid] = seq_row;
+            reinterpret_cast<int32_t*>(sm_raw1 + kRwSeq)[ptid] = seq_row;
         __syncthreads();  // raw rows of chunk 0 staged
-        scalars_and_m<HAS_SEQ, PASS>(fa, c0, bk.L, Ah2, pw, lane, sm, ps);
+        scalars_and_m<HAS_SEQ, PASS>(f, c0, bk.L, Ah2, pw, lane, sm, ps);
+        fetch_regs<HAS_SEQ, PASS>(bk, o, nCl > 1 ? c0 + 1 : c0, pw, lane, f);
         __syncthreads();
-        // chunk cn: load chunk cn+1's tiles (into stage (cn+1)&1, free since chunk cn-1 was
-        // contracted), chunk cn+2's raw rows (into raw slot cn&1, free since chunk cn was
-        // convolved) and chunk cn+2's registers; store y(cn-1), compute chunk cn+1's scalars
-        // and M tiles from the registers loaded one chunk earlier.  Every load lands before
-        // the barrier.  Unrolled by two so each register set keeps its registers.
+        // chunk c: load chunk c+1's tiles (into stage (c+1)&1, free since chunk c-1 was
+        // contracted) and chunk c+2's raw rows (into raw slot c&1, free since chunk c was
+        // convolved), store y(c-1), convolve the second half of chunk c+1 and compute its
+        // scalars and M tiles from the registers loaded during the previous chunk; then, once
+        // this chunk's transfers have landed, load chunk c+2's registers, which only the next
+        // chunk's M tiles wait for.  Unrolled by two so the raw slots are compile-time arrays.
+        // The body has no branches between the loads and the LDS work (the compiler then
+        // keeps track of which LDS array an outstanding transfer writes): past the last
+        // chunk the indices are clamped, so the loads repeat the last chunk into slots
+        // nobody reads, the conv writes an X slot nobody reads, and the first iteration's y
+        // stores go to an empty range.
         for (int64_t cn = 0; cn < nCl; cn += 2) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int64_t c = cn + half;
                 if (c >= nCl) break;
-                Fetch& cur = half == 0 ? fb : fa;   // chunk c+1
-                Fetch& nxt = half == 0 ? fa : fb;   // chunk c+2
                 const int64_t k = c + 1;
+                const int64_t kt = k < nCl ? k : nCl - 1;          // tiles of chunk c+1
+                const int64_t kr = k + 1 < nCl ? k + 1 : nCl - 1;  // raw rows, registers of c+2
                 uint8_t* stk = sm + (k & 1) * kStageBytes;
-                if (k < nCl) fetch_tiles<PASS>(bk, o, c0 + k, pw, sm_cb + (k & 1) * kCbBytes);
-                if (k + 1 < nCl) {
-                    fetch_raw<K, HAS_SEQ>(bk, o, c0 + k + 1, pw, lane, sm_raw + (c & 1) * kRawBytes, &seq_row);
-                    fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + k + 1, pw, lane, nxt);
-                }
-                // the y stores are the iteration's last vector-memory operations (the empty asm
-                // keeps the compiler from moving loads after them); the loads complete in issue
-                // order, so waiting until only the two stores are outstanding waits for every
-                // load, while the stores' write latency overlaps the next chunk
+                uint8_t* raw_ld = half == 0 ? sm_raw0 : sm_raw1;  // slot c & 1
+                fetch_tiles<PASS>(bk, o, c0 + kt, pw, sm_cb + (k & 1) * kCbBytes);
+                fetch_raw<K, HAS_SEQ>(bk, o, c0 + kr, kr >= 1, pw, lane, raw_ld, &seq_row);
                 asm volatile("" ::: "memory");
-                const bool stores = PASS == 0 && c > 0;
-                if (stores) store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c0 + c - 1, pw, lane);
-                if (k < nCl) scalars_and_m<HAS_SEQ, PASS>(cur, c0 + k, bk.L, Ah2, pw, lane, stk, ps);
-                if (stores) __builtin_amdgcn_s_waitcnt(kWaitVm2);
-                else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                if (PASS == 0)
+                    store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c0 + c - 1, c > 0, pw, lane);
+                scalars_and_m<HAS_SEQ, PASS>(f, c0 + kt, bk.L, Ah2, pw, lane, stk, ps);
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + kr, pw, lane, f);
                 if (HAS_SEQ && k + 1 < nCl && ptid < kRows)
-                    reinterpret_cast<int32_t*>(sm_raw + (c & 1) * kRawBytes + kRwSeq)[ptid] = seq_row;
+                    reinterpret_cast<int32_t*>(raw_ld + kRwSeq)[ptid] = seq_row;
                 __syncthreads();
             }
         }
-        if (PASS == 0) store_y(bk, o, sm + kOffY + ((nCl - 1) & 1) * kYBytes, c0 + nCl - 1, pw, lane);
+        if (PASS == 0) store_y(bk, o, sm + kOffY + ((nCl - 1) & 1) * kYBytes, c0 + nCl - 1, true, pw, lane);
     } else {
         const int cv = wave - 8;
-        // the conv of channel p = 16 cv + li over tokens 32 s + 8 g4 .. +7 of a chunk, into
-        // the X slot lane the consumer wave cv reads
-        const int p_conv = 16 * cv + li;
+        // the conv of channel p = 16 cv + li over tokens 32 s + 8 g4 .. +7 of a chunk (s = 0, 1),
+        // into the X slot lane the consumer wave cv reads
+        const int p_conv = 16 * cv + li, j0_conv = 8 * g4;
         const int xoff = (cv * 64 + lane) * 32;
-        double cw[K];
-        double cbias = 0.0;
-#pragma unroll
-        for (int k = 0; k < K; ++k) cw[k] = 0.0;
-        if (MODE != 0) {
-            const int64_t cc = a.x_col0 + h * kP + p_conv;
-#pragma unroll
-            for (int k = 0; k < K; ++k) cw[k] = a.conv_w[cc * K + k];
-            cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
-        }
+        double cw[K], cbias;
+        conv_weights<K, MODE>(a, h, p_conv, cw, cbias);
         auto conv_chunk = [&](const uint8_t* raw, uint8_t* xs) {
-            uint32_t near = 0;
-            bf16x8 xv[2];
-#pragma unroll
-            for (int sh = 0; sh < 2; ++sh)
-                xv[sh] = conv_fast<K, MODE, HAS_SEQ>(raw, p_conv, 32 * sh + 8 * g4, cw, cbias, &near);
-            if (MODE == 2 && near) {
-#pragma unroll
-                for (int sh = 0; sh < 2; ++sh)
-                    xv[sh] = conv_fix<K, HAS_SEQ>(raw, p_conv, 32 * sh + 8 * g4, cw, cbias, near >> (8 * sh), xv[sh]);
-            }
-#pragma unroll
-            for (int sh = 0; sh < 2; ++sh) lds_st(xs, xoff + 16 * sh, xv[sh]);
+            // both runs' fast paths first (independent chains), then the rare fix-ups
+            uint32_t n0 = 0, n1 = 0;
+            bf16x8 x0 = conv_fast<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv, cw, cbias, &n0);
+            bf16x8 x1 = conv_fast<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv + 32, cw, cbias, &n1);
+            x0 = conv_fixups<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv, cw, cbias, n0, x0);
+            x1 = conv_fixups<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv + 32, cw, cbias, n1, x1);
+            lds_st(xs, xoff, x0);
+            lds_st(xs, xoff + 16, x1);
         };
         __syncthreads();  // raw rows of chunk 0 staged
-        conv_chunk(sm_raw, sm + kOffX);
+        conv_chunk(sm_raw0, sm + kOffX);
         __syncthreads();
         for (int64_t cn = 0; cn < nCl; ++cn) {
             if (cn + 1 < nCl)
-                conv_chunk(sm_raw + ((cn + 1) & 1) * kRawBytes, sm + kOffX + ((cn + 1) & 1) * kXBytes);
+                conv_chunk((cn & 1) ? sm_raw0 : sm_raw1, sm + kOffX + ((cn + 1) & 1) * kXBytes);
             __syncthreads();
         }
     }
