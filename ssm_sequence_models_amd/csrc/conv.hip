@@ -5,7 +5,8 @@
 // u = [S, x]; F = u[L : L+K-1].  Each thread owns V adjacent channels of one batch row and a
 // run of TT tokens; the K-1 previous inputs live in registers and slide along the run, so
 // every input element is read from HBM once (plus a K-1 halo per run).  Channel-last rows
-// give 16-byte coalesced loads/stores (V = 8 bf16 or 4 fp32 channels per thread).
+// give coalesced vector loads/stores (4 bf16 channels per thread in the bf16 kernel below,
+// 4 fp32 channels in the generic one).
 //
 // Decode, same chapter, "single-token update maths", "the physical cache may exceed the
 // minimal history", "state indices for continuous batching": one thread per (row, channel)
@@ -22,26 +23,6 @@ constexpr int kConvTokens = 32;   // tokens per thread run (>= K-1 for every K <
 
 template <class D, int V>
 struct Vec;
-template <>
-struct Vec<BF16, 8> {
-    __device__ static void load(const uint16_t* p, float (&v)[8]) {
-        uint4 q = *reinterpret_cast<const uint4*>(p);
-        uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-    __device__ static void store(uint16_t* p, const float (&v)[8]) {
-        uint4 q;
-        q.x = pack_bf16x2(v[0], v[1]);
-        q.y = pack_bf16x2(v[2], v[3]);
-        q.z = pack_bf16x2(v[4], v[5]);
-        q.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(p) = q;
-    }
-};
 template <>
 struct Vec<F32, 4> {
     __device__ static void load(const float* p, float (&v)[4]) {
@@ -169,6 +150,233 @@ conv1d_fwd_kernel(const typename D::T* __restrict__ x, const float* __restrict__
 #pragma unroll
             for (int r = 0; r < K - 1; ++r) final_state[(b * C + c0 + v) * (K - 1) + r] = fv[v][r];
     }
+}
+
+// bf16 prefill, the main case: each thread owns 4 adjacent channels of one batch row (8-byte
+// loads and stores, 512 contiguous bytes per wavefront) and a run of kConvTokens tokens.
+// Weights, bias and the K-1 previous inputs stay in registers as doubles (about 64 VGPRs, so
+// four wavefronts fit on a SIMD); the next group of kGroup tokens' inputs are loaded as
+// packed bf16 while the current group is computed.  SiLU outputs too close to a bf16
+// rounding midpoint for the fp32 evaluation (see silu_f32) are flagged (one bit mask per
+// group, kept in the thread's own LDS slots); after the run, when the fast path's registers
+// are free, one loop recomputes the flagged outputs in double from memory and overwrites
+// them.
+constexpr int kRun4 = 32;  // tokens per thread run (64 and 128 measured no faster)
+constexpr int kGroup = 4;   // tokens per prefetch group (2 slower, 8 no faster)
+constexpr int kGroupsPerRun = kRun4 / kGroup;
+
+// Exact conv value at token t, channel ch of batch row b (the slow path's recomputation):
+// taps at u-positions t-K+1 .. t, from x or from the initial state, each zeroed when its
+// sequence id differs from token t's (positions before the row start carry token 0's id).
+template <int K, bool HAS_SEQ>
+__device__ double conv_exact_bf16(const uint16_t* x, const float* w, const float* bias,
+                                  const uint16_t* init_state, const int32_t* srow, int64_t b,
+                                  int64_t L, int64_t C, int64_t t, int64_t ch) {
+    double z = bias ? bias[ch] : 0.0f;
+    const int32_t idt = HAS_SEQ ? srow[t] : 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t pos = t - (K - 1) + k;
+        double u;
+        if (pos >= 0)
+            u = bf16_to_f32(x[(b * L + pos) * C + ch]);
+        else
+            u = init_state ? bf16_to_f32(init_state[(b * C + ch) * (K - 1) + (K - 1) + pos]) : 0.0f;
+        if (HAS_SEQ && srow[pos >= 0 ? pos : 0] != idt) u = 0.0;
+        z = fma(static_cast<double>(w[ch * K + k]), u, z);
+    }
+    return z;
+}
+
+__device__ __forceinline__ void unpack4(uint2 q, double (&v)[4]) {
+    v[0] = __uint_as_float(q.x << 16);
+    v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16);
+    v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+
+template <int K, bool HAS_SEQ, bool SILU>
+__global__ void __launch_bounds__(kConvThreads) __attribute__((amdgpu_waves_per_eu(K <= 4 && SILU ? 4 : 1)))
+conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                         const float* __restrict__ bias, const uint16_t* init_state,
+                         uint16_t* final_state, const int32_t* __restrict__ seq_idx,
+                         uint16_t* __restrict__ out, int64_t L, int64_t C) {
+    constexpr int V = 4;
+    const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x) * V;
+    if (c0 >= C) return;
+    const int64_t b = blockIdx.z;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kRun4;
+    const int64_t t1 = min(t0 + kRun4, L);
+    const uint16_t* xrow = x + b * L * C + c0;
+    uint16_t* orow = out + b * L * C + c0;
+    const int32_t* srow = HAS_SEQ ? seq_idx + b * L : nullptr;
+
+    double wr[V][K], bv[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) wr[v][k] = w[(c0 + v) * K + k];
+        bv[v] = bias ? bias[c0 + v] : 0.0f;
+    }
+    // u-positions t0-K+1 .. t0-1 (oldest first): from x, or from the state for pos < 0
+    double hist[K - 1][V];
+    int32_t hid[K - 1];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+        const int64_t pos = t0 - (K - 1) + j;
+        if (pos >= 0) {
+            unpack4(*reinterpret_cast<const uint2*>(xrow + pos * C), hist[j]);
+            hid[j] = HAS_SEQ ? srow[pos] : 0;
+        } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                hist[j][v] = init_state ? bf16_to_f32(init_state[(b * C + c0 + v) * (K - 1) + (K - 1) + pos]) : 0.0f;
+            hid[j] = HAS_SEQ ? srow[0] : 0;
+        }
+    }
+
+    static_assert(4 * kGroup <= 32, "flag mask");
+    __shared__ uint32_t flags[kGroupsPerRun][kConvThreads];
+    uint2 xa[kGroup];
+    int32_t ia[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+        const int64_t t = t0 + u;
+        xa[u] = t < t1 ? *reinterpret_cast<const uint2*>(xrow + t * C) : uint2{0u, 0u};
+        ia[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
+    }
+    for (int64_t tg = t0; tg < t1; tg += kGroup) {
+        uint2 xb[kGroup];
+        int32_t ib[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const int64_t t = tg + kGroup + u;
+            xb[u] = t < t1 ? *reinterpret_cast<const uint2*>(xrow + t * C) : uint2{0u, 0u};
+            ib[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
+        }
+        uint32_t near = 0;  // bit 4u + v: output (token tg + u, channel c0 + v) flagged
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const int64_t t = tg + u;
+            if (t < t1) {
+                double xv[V];
+                unpack4(xa[u], xv);
+                double z[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    double acc = bv[v];
+#pragma unroll
+                    for (int k = 0; k < K - 1; ++k) {
+                        const double tap = (!HAS_SEQ || hid[k] == ia[u]) ? hist[k][v] : 0.0;
+                        acc = fma(wr[v][k], tap, acc);
+                    }
+                    z[v] = fma(wr[v][K - 1], xv[v], acc);
+                }
+                uint16_t o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    if (SILU) {
+                        bool nr;
+                        o[v] = f32_to_bf16(silu_f32(z[v], nr));
+                        near |= static_cast<uint32_t>(nr) << (4 * u + v);
+                    } else {
+                        o[v] = f64_to_bf16(z[v]);
+                    }
+                }
+                *reinterpret_cast<uint2*>(orow + t * C) =
+                    uint2{o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                          o[2] | (static_cast<uint32_t>(o[3]) << 16)};
+#pragma unroll
+                for (int k = 0; k < K - 2; ++k) {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) hist[k][v] = hist[k + 1][v];
+                    hid[k] = hid[k + 1];
+                }
+#pragma unroll
+                for (int v = 0; v < V; ++v) hist[K - 2][v] = xv[v];
+                hid[K - 2] = ia[u];
+            }
+        }
+        if (SILU) flags[(tg - t0) / kGroup][threadIdx.x] = near;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            xa[u] = xb[u];
+            ia[u] = ib[u];
+        }
+    }
+
+    // rare: each iteration redoes one flagged output per lane (this thread stored the fast
+    // value earlier, so the overwrite lands after it)
+    if (SILU) {
+        const int ng = static_cast<int>((t1 - t0 + kGroup - 1) / kGroup);
+        for (int g = 0; g < ng; ++g) {
+            for (uint32_t m = flags[g][threadIdx.x]; m != 0; m &= m - 1) {
+                const int bit = __builtin_ctz(m);
+                const int64_t t = t0 + g * kGroup + (bit >> 2), ch = c0 + (bit & 3);
+                const double z = conv_exact_bf16<K, HAS_SEQ>(x, w, bias, init_state, srow, b, L, C, t, ch);
+                out[(b * L + t) * C + ch] = silu_f64_to_bf16(z);
+            }
+        }
+    }
+
+    // F = u[L .. L+K-2], written by the run that read the initial state (so an in-place
+    // state pair is read before it is overwritten)
+    if (final_state != nullptr && t0 == 0) {
+        uint16_t fv[V][K - 1];
+#pragma unroll
+        for (int r = 0; r < K - 1; ++r) {
+            const int64_t m = L + r;  // index into u
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                fv[v][r] = m < K - 1 ? (init_state ? init_state[(b * C + c0 + v) * (K - 1) + m] : uint16_t(0))
+                                     : xrow[(m - (K - 1)) * C + v];
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int r = 0; r < K - 1; ++r) final_state[(b * C + c0 + v) * (K - 1) + r] = fv[v][r];
+    }
+}
+
+template <int K>
+hipError_t conv_fwd_bf16x4_dispatch_seq(const void* x, const float* w, const float* bias,
+                                        const void* init_state, void* final_state,
+                                        const int32_t* seq_idx, void* out, int64_t B, int64_t L,
+                                        int64_t C, int act, hipStream_t stream) {
+    const int64_t threads_needed = C / 4;
+    dim3 grid((threads_needed + kConvThreads - 1) / kConvThreads,
+              (L + kRun4 - 1) / kRun4, B);
+    using U16 = uint16_t;
+#define SSM_CONV4_LAUNCH(SEQ, SL)                                                             \
+    conv1d_fwd_bf16x4_kernel<K, SEQ, SL><<<grid, kConvThreads, 0, stream>>>(                  \
+        (const U16*)x, w, bias, (const U16*)init_state, (U16*)final_state, seq_idx, (U16*)out, \
+        L, C)
+    const bool silu = act == SSM_ACT_SILU;
+    if (seq_idx) {
+        if (silu) SSM_CONV4_LAUNCH(true, true);
+        else SSM_CONV4_LAUNCH(true, false);
+    } else {
+        if (silu) SSM_CONV4_LAUNCH(false, true);
+        else SSM_CONV4_LAUNCH(false, false);
+    }
+#undef SSM_CONV4_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t conv_fwd_bf16x4_dispatch(int64_t K, const void* x, const float* w, const float* bias,
+                                    const void* init_state, void* final_state,
+                                    const int32_t* seq_idx, void* out, int64_t B, int64_t L,
+                                    int64_t C, int act, hipStream_t stream) {
+#define SSM_CONV4_K(KK)                                                                      \
+    case KK:                                                                                 \
+        return conv_fwd_bf16x4_dispatch_seq<KK>(x, w, bias, init_state, final_state, seq_idx, \
+                                                out, B, L, C, act, stream);
+    switch (K) {
+        SSM_CONV4_K(2) SSM_CONV4_K(3) SSM_CONV4_K(4) SSM_CONV4_K(5) SSM_CONV4_K(6)
+        SSM_CONV4_K(7) SSM_CONV4_K(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef SSM_CONV4_K
 }
 
 // seqlen == 0: F = S (or zeros)
@@ -321,9 +529,9 @@ hipError_t launch_conv1d_fwd(const void* x, const float* w, const float* bias,
     }
     const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out);
     if (dtype == SSM_BF16) {
-        if (C % 8 == 0 && (align & 15) == 0)
-            return conv_fwd_dispatch_k<BF16, 8>(K, x, w, bias, init_state, final_state, seq_idx,
-                                               out, B, L, C, act, stream);
+        if (C % 4 == 0 && (align & 7) == 0)
+            return conv_fwd_bf16x4_dispatch(K, x, w, bias, init_state, final_state, seq_idx, out,
+                                            B, L, C, act, stream);
         return conv_fwd_dispatch_k<BF16, 1>(K, x, w, bias, init_state, final_state, seq_idx,
                                            out, B, L, C, act, stream);
     }

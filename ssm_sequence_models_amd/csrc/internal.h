@@ -71,8 +71,10 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 __device__ __forceinline__ float silu_f32(double z, bool& near_midpoint) {
     const float zf = static_cast<float>(z);
     const float s = zf * __builtin_amdgcn_rcpf(1.0f + __expf(-zf));
-    const int dist = abs(static_cast<int>(__float_as_uint(s) & 0xFFFFu) - 0x8000);
-    near_midpoint = static_cast<float>(dist) <= 8.0f + 4.0f * fabsf(zf);
+    // distance, in fp32 ulps, of s from the bf16 rounding midpoint: |low 16 bits - 0x8000|
+    // (exact in float; compiles to one add, one convert and the compare)
+    const float lo = static_cast<float>(__float_as_uint(s) & 0xFFFFu);
+    near_midpoint = fabsf(lo - 32768.0f) <= 8.0f + 4.0f * fabsf(zf);
     return s;
 }
 __device__ __forceinline__ uint16_t silu_f64_to_bf16(double z) {

@@ -1,6 +1,7 @@
 """GPU parity of ssm_conv1d_fwd and ssm_conv1d_update against the fp64 oracle.
 
-Outputs within |g - o| <= 1e-3 + 2e-2 |o|; conv states (raw input copies) and pool contents
+Outputs within |g - o| <= 1e-3 + 2e-2 |o|; bf16 prefill outputs also bit-exact (the kernel
+rounds as the exact conv value rounds); conv states (raw input copies) and pool contents
 bit-exact."""
 import numpy as np
 import pytest
@@ -30,7 +31,9 @@ CASES = [
     # B, L, C, K, dtype, init, segments, act
     (1, 64, 12, 4, F32, True, 0, "silu"),     # the tiny layer's 4 + 2*4 channels
     (1, 64, 12, 4, F32, True, 0, None),
-    (2, 200, 264, 4, BF16, True, 0, "silu"),  # 16-byte vector path, ragged token tiles
+    (2, 200, 264, 4, BF16, True, 0, "silu"),  # 4-channel vector path, ragged token runs
+    (2, 130, 36, 4, BF16, True, 0, "silu"),   # 9 threads per row: a partial wavefront
+    (1, 96, 24, 4, BF16, False, 0, None),     # vector path, identity, no initial state
     (2, 200, 264, 4, BF16, True, 4, "silu"),  # packed sequences
     (1, 77, 13, 3, BF16, True, 3, None),      # odd channel count: scalar path
     (3, 2, 16, 4, BF16, True, 0, "silu"),     # L < K-1: F keeps state entries
@@ -49,7 +52,30 @@ def test_conv1d_fwd_matches_oracle(B, L, C, K, dtype, with_init, segs, act):
     torch.cuda.synchronize()
     ref, rfin = oracle.conv1d_fwd(x, w, b, init, seq, act=act or "none", out_dtype=ODT[dtype])
     assert_close(out, ref, "conv out")
+    if dtype == BF16:
+        assert_bitexact(out, torch.from_numpy(np.ascontiguousarray(ref)).to(BF16), "conv out (bf16)")
     assert_bitexact(fin, torch.from_numpy(rfin).to(dtype), "conv final state")
+
+
+def test_conv1d_fwd_layer1p3b_sampled_channels():
+    """The 1.3B-like layer's conv at full size (B 4, L 8192, 4352 channels, K 4, SiLU, state
+    in / out): bf16 outputs and final states bit-exact on a sample of channels spread over the
+    row, including the last ones."""
+    import ssm_sequence_models_amd as ssm
+    cfg = workloads.CONFIGS["layer1p3b"]
+    s = workloads.shape_of("layer1p3b")
+    w, b, _ = workloads.layer_params(s, cfg["seed"])
+    inp = workloads.prefill_inputs(s, cfg["seed"], with_random_init=True)
+    x, init = inp["xBC"], inp["conv_init"]
+    out, fin = ssm.conv1d_fwd(dev(x), dev(w), dev(b), dev(init), None, "silu")
+    torch.cuda.synchronize()
+    chans = torch.tensor(sorted(set(list(range(0, s.C, 97)) + [1, 2, 3, s.C - 4, s.C - 3,
+                                                               s.C - 2, s.C - 1])))
+    ref, rfin = oracle.conv1d_fwd(x[:, :, chans], w[chans], b[chans], init[:, chans], None,
+                                  act="silu", out_dtype="bf16")
+    assert_bitexact(out[:, :, dev(chans)], torch.from_numpy(np.ascontiguousarray(ref)).to(BF16),
+                    "conv out (sampled channels)")
+    assert_bitexact(fin[:, dev(chans)], torch.from_numpy(rfin).to(BF16), "conv final state")
 
 
 def test_conv1d_fwd_len0_and_inplace_state():
