@@ -10,16 +10,77 @@
 // loop: thread `tid` owns the float4 runs e = j*4*NT + 4*tid .. +3 (row-major over [P, N]),
 // which makes the one read and one write of the state fully coalesced 16-byte accesses --
 // for the decode step the state traffic (2 x 32 KiB per request and head) is the whole cost.
-// The N/4 lanes that share a channel p are adjacent, so y[p] is a butterfly reduction over
-// that lane group.
+// The N/4 lanes that share a channel p are adjacent, so y[p] is a reduction over that lane
+// group.  When the runs tile the state exactly (P = 64, N = 128: 8 runs of 1024), the J sums
+// of a lane are reduced together, reduce-scatter style: at each halving of the lane span a
+// lane keeps half of its sums and adds its partner's matching half, so J = 8 sums over 32
+// lanes take 4 + 2 + 1 exchanges and two more for the last 4 lanes (9 instead of 40).
+// The token loop reads its inputs from LDS: tiles of up to 16 tokens of B, C, x and dt
+// (and the sequence resets) are staged by the whole block with loads ordered along the
+// contiguous dimension, so a token costs no memory round trip and the first tile's loads
+// overlap the state load.
 #include "internal.h"
 
 namespace ssm {
 namespace {
 
+// Sum over the LP adjacent lanes sharing each of the J channels v[j] belongs to.  Returns the
+// sum for channel index jr = (lane's reduce-scatter position) in v[0]; *jr gets that index,
+// and the lane is the group's writer when (lane % (LP / J')) == 0 (see the caller).
+template <int J, int LP>
+__device__ __forceinline__ float reduce_scatter(float (&v)[J], int lane, int* jr) {
+    int j_off = 0;
+    int cnt = J;
+#pragma unroll
+    for (int off = LP / 2; off >= 1; off >>= 1) {
+        if (cnt > 1) {
+            const bool hi = (lane & off) != 0;
+            const int half = cnt / 2;
+#pragma unroll
+            for (int i = 0; i < J / 2; ++i) {
+                if (i < half) {
+                    const float send = hi ? v[i] : v[i + half];
+                    const float mine = hi ? v[i + half] : v[i];
+                    v[i] = mine + __shfl_xor(send, off);
+                }
+            }
+            j_off += hi ? half : 0;
+            cnt = half;
+        } else {
+            v[0] += __shfl_xor(v[0], off);
+        }
+    }
+    *jr = j_off;
+    return v[0];
+}
+
+constexpr int kTileTMax = 16;
+constexpr size_t kTileBytesMax = 48 * 1024;
+
+// Stage the [nt][cnt] tile, element (tt, r) at src[base + (t0 + tt) s_t + r s_c], into
+// dst[tt * row + r] (floats); consecutive threads take consecutive addresses of whichever
+// index has the smaller stride.
+template <class D>
+__device__ __forceinline__ void stage_tile(const typename D::T* src, int64_t base, int64_t t0,
+                                           int64_t s_t, int64_t s_c, int nt, int cnt,
+                                           float* dst, int row) {
+    const int n = nt * cnt;
+    if (s_t < s_c) {
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int tt = i % nt, r = i / nt;
+            dst[tt * row + r] = D::load(src, base + (t0 + tt) * s_t + r * s_c);
+        }
+    } else {
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int r = i % cnt, tt = i / cnt;
+            dst[tt * row + r] = D::load(src, base + (t0 + tt) * s_t + r * s_c);
+        }
+    }
+}
+
 template <class D, int J>
 __global__ void __launch_bounds__(256)
-recurrent_kernel(RecurrentArgs a, int nthreads) {
+recurrent_kernel(RecurrentArgs a, int nthreads, int tile_t) {
     using T = typename D::T;
     const int tid = threadIdx.x;
     const int64_t h = blockIdx.x;
@@ -59,38 +120,73 @@ recurrent_kernel(RecurrentArgs a, int nthreads) {
     const T* bs = static_cast<const T*>(a.Bm);
     const T* cs = static_cast<const T*>(a.Cm);
     const float Ah = a.A[h];
-    for (int64_t t = 0; t < a.T; ++t) {
-        if (a.seq_idx && t > 0 && a.seq_idx[b * a.T + t] != a.seq_idx[b * a.T + t - 1]) {
+    // per staged token: B [N], C [N], x [P], dt, reset flag
+    extern __shared__ float s_in[];
+    const int N = static_cast<int>(a.N), P = static_cast<int>(a.P);
+    const int row = 2 * N + P + 2;
+    for (int64_t tb = 0; tb < a.T; tb += tile_t) {
+        const int nt = static_cast<int>(min(static_cast<int64_t>(tile_t), a.T - tb));
+        __syncthreads();  // the previous tile has been consumed
+        stage_tile<D>(bs, b * a.B_sb + g * a.N * a.B_sc, tb, a.B_st, a.B_sc, nt, N, s_in, row);
+        stage_tile<D>(cs, b * a.C_sb + g * a.N * a.C_sc, tb, a.C_st, a.C_sc, nt, N, s_in + N, row);
+        stage_tile<D>(xs, b * a.x_sb + h * a.P * a.x_sc, tb, a.x_st, a.x_sc, nt, P, s_in + 2 * N, row);
+        for (int tt = threadIdx.x; tt < nt; tt += blockDim.x) {
+            const int64_t t = tb + tt;
+            s_in[tt * row + 2 * N + P] = a.dt[(b * a.T + t) * a.H + h];
+            const bool reset = a.seq_idx && t > 0 && a.seq_idx[b * a.T + t] != a.seq_idx[b * a.T + t - 1];
+            s_in[tt * row + 2 * N + P + 1] = reset ? 1.0f : 0.0f;
+        }
+        __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+        const int64_t t = tb + tt;
+        const float* tin = s_in + tt * row;
+        if (tin[2 * N + P + 1] != 0.0f) {
 #pragma unroll
             for (int j = 0; j < J; ++j)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) st[j][k] = 0.0f;
         }
-        const float d = a.dt[(b * a.T + t) * a.H + h];
+        const float d = tin[2 * N + P];
         const float dec = __expf(d * Ah);
         float Bv[4], Cv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int64_t n = n0 + k;
-            Bv[k] = active ? D::load(bs, b * a.B_sb + t * a.B_st + (g * a.N + n) * a.B_sc) : 0.0f;
-            Cv[k] = active ? D::load(cs, b * a.C_sb + t * a.C_st + (g * a.N + n) * a.C_sc) : 0.0f;
+            Bv[k] = active ? tin[n0 + k] : 0.0f;
+            Cv[k] = active ? tin[N + n0 + k] : 0.0f;
         }
+        float part[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int64_t e = static_cast<int64_t>(j) * 4 * nthreads + 4 * tid;
             const bool live = active && e < PN;
             const int64_t p = live ? e / a.N : 0;
-            const float xp = live ? D::load(xs, b * a.x_sb + t * a.x_st + (h * a.P + p) * a.x_sc) : 0.0f;
+            const float xp = live ? tin[2 * N + p] : 0.0f;
             const float dx = d * xp;
-            float part = 0.0f;
+            float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 st[j][k] = __builtin_fmaf(dec, st[j][k], dx * Bv[k]);
-                part = __builtin_fmaf(Cv[k], st[j][k], part);
+                acc = __builtin_fmaf(Cv[k], st[j][k], acc);
             }
-            for (int off = lanes_per_p / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-            if (live && n0 == 0) D::store(y, ((b * a.T + t) * a.H + h) * a.P + p, part);
+            part[j] = acc;
         }
+        if (J == 8 && lanes_per_p == 32 && nthreads == 256 && PN == 8192) {
+            // run j of thread tid is channel p = 8 j + tid / 32; lanes tid % 32 share it
+            int jr;
+            const float yv = reduce_scatter<J, 32>(part, tid, &jr);
+            if ((tid & 3) == 0)
+                D::store(y, ((b * a.T + t) * a.H + h) * a.P + 8 * jr + tid / 32, yv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int64_t e = static_cast<int64_t>(j) * 4 * nthreads + 4 * tid;
+                const bool live = active && e < PN;
+                float v = part[j];
+                for (int off = lanes_per_p / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+                if (live && n0 == 0) D::store(y, ((b * a.T + t) * a.H + h) * a.P + e / a.N, v);
+            }
+        }
+    }
     }
     if (a.state_out) {
 #pragma unroll
@@ -120,7 +216,8 @@ bool recurrent_supported(int64_t P, int64_t N) {
     if (N % 4 != 0) return false;
     const int64_t lp = N / 4;
     if (lp > 64 || (lp & (lp - 1)) != 0) return false;
-    return P * N <= 256 * 4 * 16;
+    // one staged token (B, C, x, dt, flag) must fit the tile budget
+    return P * N <= 256 * 4 * 16 && (2 * N + P + 2) * 4 <= static_cast<int64_t>(kTileBytesMax);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream) {
@@ -133,12 +230,18 @@ hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream
     const int64_t runs = (PN + 4 * nthreads - 1) / (4 * nthreads);
     dim3 grid(a.H, a.B);
     const int nt = static_cast<int>(nthreads);
+    // tokens per staged tile: up to kTileTMax, within kTileBytesMax of LDS
+    const size_t row_bytes = static_cast<size_t>(2 * a.N + a.P + 2) * sizeof(float);
+    int tile_t = static_cast<int>(kTileBytesMax / row_bytes);
+    if (tile_t > kTileTMax) tile_t = kTileTMax;
+    if (tile_t < 1) return hipErrorInvalidValue;  // excluded by recurrent_supported
+    const size_t lds = static_cast<size_t>(tile_t) * row_bytes;
 #define SSM_REC(JJ)                                                                         \
     if (runs <= JJ) {                                                                       \
         if (dtype == SSM_BF16)                                                              \
-            recurrent_kernel<BF16, JJ><<<grid, block, 0, stream>>>(a, nt);                  \
+            recurrent_kernel<BF16, JJ><<<grid, block, lds, stream>>>(a, nt, tile_t);        \
         else                                                                                \
-            recurrent_kernel<F32, JJ><<<grid, block, 0, stream>>>(a, nt);                   \
+            recurrent_kernel<F32, JJ><<<grid, block, lds, stream>>>(a, nt, tile_t);         \
         return hipGetLastError();                                                           \
     }
     SSM_REC(1) SSM_REC(2) SSM_REC(4) SSM_REC(8) SSM_REC(16)
