@@ -668,6 +668,40 @@ __device__ __forceinline__ bf16x8 conv_fixups(const uint8_t* raw, int p, int j0,
     return x;
 }
 
+// With seq_idx: true when raw rows j0 .. j0+K+6 (the taps of a run's 8 outputs) carry one
+// sequence id, so the run's conv needs no masking.  j0 is a multiple of 8, so the ids come in
+// 16-byte reads (the id array has room for rows up to j0 + 15 <= 71); the comparisons are
+// combined without branches.
+template <int K>
+__device__ __forceinline__ bool window_one_id(const uint8_t* raw, int j0) {
+    static_assert(8 + K - 1 <= 16, "window fits four 16-byte reads");
+    uint32_t id[16];
+#pragma unroll
+    for (int q = 0; q < (8 + K - 1 + 3) / 4; ++q) {
+        const u32x4 v = lds_ld<u32x4>(raw, kRwSeq + (j0 + 4 * q) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) id[4 * q + e] = v[e];
+    }
+    uint32_t diff = 0;
+#pragma unroll
+    for (int r = 1; r < 8 + K - 1; ++r) diff |= id[r] ^ id[0];
+    return diff == 0;
+}
+
+// The conv of channel p over tokens j0 .. j0+7 with the sequence masks, one output at a
+// time, each written over the fast path's value at xs + off + 2e (the rare runs whose taps
+// straddle a sequence boundary)
+template <int K, int MODE>
+__device__ __noinline__ void conv_masked_run(const uint8_t* raw, int p, int j0,
+                                             const double (&cw)[K], double cbias, uint8_t* xs,
+                                             int off) {
+    for (int e = 0; e < 8; ++e) {
+        const double z = conv_z<K, MODE, true>(raw, p >> 3, (p & 7) * 2, j0 + e, cw, cbias);
+        const uint16_t v = MODE == 2 ? act_to_bf16(z, SSM_ACT_SILU) : f64_to_bf16(z);
+        *reinterpret_cast<uint16_t*>(xs + off + 2 * e) = v;
+    }
+}
+
 // conv weights and bias of x channel p of head h, as doubles (zeros without a conv)
 template <int K, int MODE>
 __device__ __forceinline__ void conv_weights(const ChunkedArgs& a, int64_t h, int p,
@@ -989,14 +1023,22 @@ ssd_main_kernel(ChunkedArgs a) {
         double cw[K], cbias;
         conv_weights<K, MODE>(a, h, p_conv, cw, cbias);
         auto conv_chunk = [&](const uint8_t* raw, uint8_t* xs) {
-            // both runs' fast paths first (independent chains), then the rare fix-ups
+            // both runs' fast paths first (independent chains, no sequence masks), then the
+            // rare fix-ups; with seq_idx, a run whose taps straddle a sequence boundary is
+            // redone with the masks
             uint32_t n0 = 0, n1 = 0;
-            bf16x8 x0 = conv_fast<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv, cw, cbias, &n0);
-            bf16x8 x1 = conv_fast<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv + 32, cw, cbias, &n1);
-            x0 = conv_fixups<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv, cw, cbias, n0, x0);
-            x1 = conv_fixups<K, MODE, HAS_SEQ>(raw, p_conv, j0_conv + 32, cw, cbias, n1, x1);
+            bf16x8 x0 = conv_fast<K, MODE, false>(raw, p_conv, j0_conv, cw, cbias, &n0);
+            bf16x8 x1 = conv_fast<K, MODE, false>(raw, p_conv, j0_conv + 32, cw, cbias, &n1);
+            x0 = conv_fixups<K, MODE, false>(raw, p_conv, j0_conv, cw, cbias, n0, x0);
+            x1 = conv_fixups<K, MODE, false>(raw, p_conv, j0_conv + 32, cw, cbias, n1, x1);
             lds_st(xs, xoff, x0);
             lds_st(xs, xoff + 16, x1);
+            if (HAS_SEQ && MODE != 0) {
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh)
+                    if (!window_one_id<K>(raw, j0_conv + 32 * sh))
+                        conv_masked_run<K, MODE>(raw, p_conv, j0_conv + 32 * sh, cw, cbias, xs, xoff + 16 * sh);
+            }
         };
         __syncthreads();  // raw rows of chunk 0 staged
         conv_chunk(sm_raw0, sm + kOffX);
