@@ -82,7 +82,8 @@ def _time_gpu(torch, fn, reps, warm=2):
 def other_ops(torch, ssm, workloads):
     """Achieved bandwidth of the other entry points on their workloads: the unfused conv at the
     1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
-    370M-like prefill and the 131072-token 780M-like call.  Seeded inputs drawn on the GPU
+    1.3B-like prefill with packed sequences, the 370M-like prefill and the 131072-token
+    780M-like call.  Seeded inputs drawn on the GPU
     (timing only; parity is the test suite's job)."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
@@ -113,6 +114,18 @@ def other_ops(torch, ssm, workloads):
     rep("conv1d_fwd", f"B{s.B} L{s.L} C{s.C} K{s.K} bf16 SiLU, states in/out", ms, s.B * s.L,
         2 * s.B * s.L * s.C * 2 + 2 * s.B * s.C * (s.K - 1) * 2 + s.C * (s.K + 1) * 4)
     del x, out
+
+    # the same 1.3B layer packed with 4 sequences per row (seq_idx), zero initial states
+    x, dt, w, b, A = prefill_inputs(s, 14)
+    seq = workloads.packed_seq_idx(s.B, s.L, 4).to(dev)
+    ws = torch.empty(ssm.workspace_size(s.B, s.L, s.H, s.P, s.G, s.N), dtype=torch.uint8, device=dev)
+    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, seq_idx=seq,
+                                                     workspace=ws), 10)
+    nb = (s.B * s.L * (s.C * 2 + s.H * 4 + s.H * s.P * 2 + 4) + s.B * s.H * s.P * s.N * 4
+          + s.B * s.C * (s.K - 1) * 2)
+    rep("conv_scan_fwd", f"1.3B-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N}, 4 packed sequences per "
+        "row (seq_idx), zero initial state", ms, s.B * s.L, nb)
+    del x, ws
 
     # 370M-like prefill, zero initial states
     s = workloads.shape_of("layer370m")

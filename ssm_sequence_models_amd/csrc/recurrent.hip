@@ -11,10 +11,11 @@
 // which makes the one read and one write of the state fully coalesced 16-byte accesses --
 // for the decode step the state traffic (2 x 32 KiB per request and head) is the whole cost.
 // The N/4 lanes that share a channel p are adjacent, so y[p] is a reduction over that lane
-// group.  When the runs tile the state exactly (P = 64, N = 128: 8 runs of 1024), the J sums
-// of a lane are reduced together, reduce-scatter style: at each halving of the lane span a
-// lane keeps half of its sums and adds its partner's matching half, so J = 8 sums over 32
-// lanes take 4 + 2 + 1 exchanges and two more for the last 4 lanes (9 instead of 40).
+// group.  When the runs tile the state exactly and N = 128 (32 lanes per channel; P = 64 gives
+// 4 runs of 2048 values at 512 threads), the J sums of a lane are reduced together,
+// reduce-scatter style: at each halving of the lane span a lane keeps half of its sums and
+// adds its partner's matching half, so J = 4 sums over 32 lanes take 2 + 1 exchanges and three
+// more for the last 8 lanes (6 instead of 20).
 // The token loop reads its inputs from LDS: tiles of up to 16 tokens of B, C, x and dt
 // (and the sequence resets) are staged by the whole block with loads ordered along the
 // contiguous dimension, so a token costs no memory round trip and the first tile's loads
@@ -78,8 +79,10 @@ __device__ __forceinline__ void stage_tile(const typename D::T* src, int64_t bas
     }
 }
 
+constexpr int kRecThreads = 512;
+
 template <class D, int J>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRecThreads)
 recurrent_kernel(RecurrentArgs a, int nthreads, int tile_t) {
     using T = typename D::T;
     const int tid = threadIdx.x;
@@ -170,12 +173,13 @@ recurrent_kernel(RecurrentArgs a, int nthreads, int tile_t) {
             }
             part[j] = acc;
         }
-        if (J == 8 && lanes_per_p == 32 && nthreads == 256 && PN == 8192) {
-            // run j of thread tid is channel p = 8 j + tid / 32; lanes tid % 32 share it
+        if (J <= 32 && lanes_per_p == 32 && PN == static_cast<int64_t>(J) * 4 * nthreads) {
+            // run j of thread tid is channel p = (4 nthreads / N) j + tid / 32; lanes tid % 32
+            // share it; after the reduce-scatter the lanes with tid % (32 / J) == 0 hold whole sums
             int jr;
             const float yv = reduce_scatter<J, 32>(part, tid, &jr);
-            if ((tid & 3) == 0)
-                D::store(y, ((b * a.T + t) * a.H + h) * a.P + 8 * jr + tid / 32, yv);
+            if ((tid & (32 / J - 1)) == 0)
+                D::store(y, ((b * a.T + t) * a.H + h) * a.P + (4 * nthreads / 128) * jr + tid / 32, yv);
         } else {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
@@ -211,20 +215,20 @@ __global__ void copy_or_zero_u8_kernel(uint8_t* dst, const uint8_t* src, int64_t
 }  // namespace
 
 // Lane groups of N/4 must be a power of two within one wavefront; P*N up to 16 float4 runs
-// per thread at 256 threads.
+// per thread at kRecThreads threads.
 bool recurrent_supported(int64_t P, int64_t N) {
     if (N % 4 != 0) return false;
     const int64_t lp = N / 4;
     if (lp > 64 || (lp & (lp - 1)) != 0) return false;
     // one staged token (B, C, x, dt, flag) must fit the tile budget
-    return P * N <= 256 * 4 * 16 && (2 * N + P + 2) * 4 <= static_cast<int64_t>(kTileBytesMax);
+    return P * N <= kRecThreads * 4 * 16 && (2 * N + P + 2) * 4 <= static_cast<int64_t>(kTileBytesMax);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     const int64_t PN = a.P * a.N;
     int64_t nthreads = PN / 4;
-    if (nthreads > 256) nthreads = 256;
+    if (nthreads > kRecThreads) nthreads = kRecThreads;
     // whole lane groups per thread run, and a block of whole wavefronts
     const int block = static_cast<int>(((nthreads + 63) / 64) * 64);
     const int64_t runs = (PN + 4 * nthreads - 1) / (4 * nthreads);
