@@ -26,6 +26,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+# MFMAs the main kernel issues per (batch row, head, 64-token chunk): 4 consumer waves x (12
+# intra-chunk + 32 initial-state + 32 state-update), each a 16x16x32 bf16 product
+MFMA_PER_CHUNK_HEAD = 4 * (12 + 32 + 32)
+FLOP_PER_MFMA = 2 * 16 * 16 * 32
 METRIC = "SSM scan+conv tokens/sec (B×L, 1.3B layer, L=8K) and % HBM/MFMA roofline"
 
 
@@ -79,7 +84,19 @@ def _time_gpu(torch, fn, reps, warm=2):
     return e0.elapsed_time(e1) / reps
 
 
-def other_ops(torch, ssm, workloads):
+def copy_bandwidth(torch):
+    """Read + write bandwidth of a plain 1 GiB device-to-device copy (GB/s): what streaming
+    code reaches on this machine, the reference for the fractions below beside the 8 TB/s peak."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ms = _time_gpu(torch, lambda: dst.copy_(src), 5)
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def other_ops(torch, ssm, workloads, copy_GBs):
     """Achieved bandwidth of the other entry points on their workloads: the unfused conv at the
     1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
     1.3B-like prefill with packed sequences, the 370M-like prefill and the 131072-token
@@ -92,7 +109,8 @@ def other_ops(torch, ssm, workloads):
     def rep(op, workload, ms, tokens, nbytes):
         res.append({"op": op, "workload": workload, "ms": ms, "tokens_per_s": tokens / (ms * 1e-3),
                     "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
-                    "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+                    "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "frac_of_copy": nbytes / (ms * 1e-3) / 1e9 / copy_GBs})
 
     def prefill_inputs(s, seed):
         g.manual_seed(seed)
@@ -256,6 +274,9 @@ def main():
     op_bytes, main_bytes = algorithmic_bytes(s)
     achieved = main_bytes / (main_ms_avg * 1e-3) / 1e9
     log(f"bench: {ms_per_step:.4f} ms/step, main kernel {main_ms_avg:.4f} ms")
+    n_chunks = (s.L + 63) // 64
+    mfma_flops = s.B * s.H * n_chunks * MFMA_PER_CHUNK_HEAD * FLOP_PER_MFMA
+    copy_GBs = copy_bandwidth(torch)
 
     result = {
         "metric": METRIC,
@@ -278,7 +299,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "ssd_main_kernel", "kernel_ms": main_ms_avg,
-                     "algorithmic_bytes_per_launch": main_bytes},
+                     "algorithmic_bytes_per_launch": main_bytes,
+                     "copy_GBs": copy_GBs, "frac_of_copy": achieved / copy_GBs},
+        "mfma": {"kernel": "ssd_main_kernel", "issued_flops_per_launch": mfma_flops,
+                 "achieved_TFLOPs": mfma_flops / (main_ms_avg * 1e-3) / 1e12,
+                 "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": mfma_flops / (main_ms_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "note": "bf16 MFMA flops issued, the hi/lo split of fp32 operands included"},
         "op_roofline": {"algorithmic_bytes": op_bytes, "ms": ms_per_step,
                         "achieved_GBs": op_bytes / (ms_per_step * 1e-3) / 1e9,
                         "frac": op_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
@@ -287,7 +314,7 @@ def main():
     }
     if not args.no_other_ops:
         log("bench: other entry points")
-        result["other_ops"] = other_ops(torch, ssm, workloads)
+        result["other_ops"] = other_ops(torch, ssm, workloads, copy_GBs)
     if not args.no_cpu_baseline:
         log("bench: fp64 oracle on the host (cpu baseline)")
         result["cpu_baseline"] = cpu_baseline(s, w, b, A, inp, cinit.cpu(), sinit.cpu())
