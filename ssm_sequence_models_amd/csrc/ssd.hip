@@ -809,18 +809,6 @@ ssd_main_kernel(ChunkedArgs a) {
             bf16x8 xv[2];
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) xv[sh] = lds_ld<bf16x8>(sm + kOffX + (cn & 1) * kXBytes, xoff + 16 * sh);
-            float eI[4];
-#pragma unroll
-            for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
-            float wj[2][8];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const f32x4 w0 = lds_ld<f32x4>(st, kStW + (32 * s + 8 * g4) * 4);
-                const f32x4 w1 = lds_ld<f32x4>(st, kStW + (32 * s + 8 * g4 + 4) * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { wj[s][e] = w0[e]; wj[s][4 + e] = w1[e]; }
-            }
-            const float decay = lds_ld<float>(st, kStDecay);
 
             // Y^T[p][i], p = 16 wave + 4 g4 + r, i = 16 I + li.  Each phase loads its LDS
             // operands before its MFMAs, and consecutive MFMAs use different accumulators
@@ -833,13 +821,13 @@ ssd_main_kernel(ChunkedArgs a) {
                 yi[I] = yo[I];
             }
             if constexpr (PASS == 0) {
-            // intra-chunk part: M tiles (I, s) with 32 s <= 16 I + 15
-            bf16x8 mh[6], ml[6];
+            // intra-chunk part: M tiles (I, s) with 32 s <= 16 I + 15; the hi tiles, then the
+            // lo tiles in the same registers (keeps the wave's peak register count down)
+            bf16x8 mt[6];
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                mh[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
-                ml[u] = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * sh + g4));
+                mt[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
             }
             bf16x8 cb[2][4];
 #pragma unroll
@@ -847,12 +835,17 @@ ssd_main_kernel(ChunkedArgs a) {
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                yi[I] = mfma(xv[sh], mh[u], yi[I]);
+                yi[I] = mfma(xv[sh], mt[u], yi[I]);
             }
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                yi[I] = mfma(xv[sh], ml[u], yi[I]);
+                mt[u] = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * sh + g4));
+            }
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                yi[I] = mfma(xv[sh], mt[u], yi[I]);
             }
             // initial-state part, one 32-wide slice m of the state at a time; the next
             // slice's C tiles load while this slice's MFMAs run
@@ -878,10 +871,18 @@ ssd_main_kernel(ChunkedArgs a) {
             }
             }
             // state update: h^T[n][p] = decay h^T + B^T (W o X)
+            const float decay = lds_ld<float>(st, kStDecay);
 #pragma unroll
             for (int t = 0; t < 8; ++t) acc[t] *= decay;
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) {
+                float wj[8];
+                {
+                    const f32x4 w0 = lds_ld<f32x4>(st, kStW + (32 * sh + 8 * g4) * 4);
+                    const f32x4 w1 = lds_ld<f32x4>(st, kStW + (32 * sh + 8 * g4 + 4) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { wj[e] = w0[e]; wj[4 + e] = w1[e]; }
+                }
                 bf16x8 bv[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
@@ -890,7 +891,7 @@ ssd_main_kernel(ChunkedArgs a) {
                 }
                 float wx[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) wx[e] = wj[sh][e] * static_cast<float>(xv[sh][e]);
+                for (int e = 0; e < 8; ++e) wx[e] = wj[e] * static_cast<float>(xv[sh][e]);
                 bf16x8 bh, bl;
                 split_hilo(wx, bh, bl);
 #pragma unroll
@@ -900,6 +901,9 @@ ssd_main_kernel(ChunkedArgs a) {
             }
             if constexpr (PASS == 0) {
                 // y tile of this chunk -> LDS (the producers store it next iteration)
+                float eI[4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     uint2 pk;
@@ -1015,10 +1019,13 @@ ssd_main_kernel(ChunkedArgs a) {
         }
         if (PASS == 0) store_y(bk, o, sm + kOffY + ((nCl - 1) & 1) * kYBytes, c0 + nCl - 1, true, pw, lane);
     } else {
+        // conv wave cv: channel p = 16 cv + li over tokens 32 r + 8 g4 .. +7 of a chunk (runs
+        // r = 0, 1), into the X slot lane that consumer wave cv reads.  (Eight conv waves, one
+        // run each, were measured slower: at 16 waves per group the 128-VGPR budget spills.)
         const int cv = wave - 8;
-        // the conv of channel p = 16 cv + li over tokens 32 s + 8 g4 .. +7 of a chunk (s = 0, 1),
-        // into the X slot lane the consumer wave cv reads
-        const int p_conv = 16 * cv + li, j0_conv = 8 * g4;
+        constexpr int kRuns = 2;
+        const int p_conv = 16 * cv + li;
+        const int j0_conv = 8 * g4;
         const int xoff = (cv * 64 + lane) * 32;
         double cw[K], cbias;
         conv_weights<K, MODE>(a, h, p_conv, cw, cbias);
@@ -1026,18 +1033,21 @@ ssd_main_kernel(ChunkedArgs a) {
             // both runs' fast paths first (independent chains, no sequence masks), then the
             // rare fix-ups; with seq_idx, a run whose taps straddle a sequence boundary is
             // redone with the masks
-            uint32_t n0 = 0, n1 = 0;
-            bf16x8 x0 = conv_fast<K, MODE, false>(raw, p_conv, j0_conv, cw, cbias, &n0);
-            bf16x8 x1 = conv_fast<K, MODE, false>(raw, p_conv, j0_conv + 32, cw, cbias, &n1);
-            x0 = conv_fixups<K, MODE, false>(raw, p_conv, j0_conv, cw, cbias, n0, x0);
-            x1 = conv_fixups<K, MODE, false>(raw, p_conv, j0_conv + 32, cw, cbias, n1, x1);
-            lds_st(xs, xoff, x0);
-            lds_st(xs, xoff + 16, x1);
+            uint32_t nr[kRuns];
+            bf16x8 xr[kRuns];
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r)
+                xr[r] = conv_fast<K, MODE, false>(raw, p_conv, j0_conv + 32 * r, cw, cbias, &nr[r]);
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r) {
+                xr[r] = conv_fixups<K, MODE, false>(raw, p_conv, j0_conv + 32 * r, cw, cbias, nr[r], xr[r]);
+                lds_st(xs, xoff + 16 * r, xr[r]);
+            }
             if (HAS_SEQ && MODE != 0) {
 #pragma unroll
-                for (int sh = 0; sh < 2; ++sh)
-                    if (!window_one_id<K>(raw, j0_conv + 32 * sh))
-                        conv_masked_run<K, MODE>(raw, p_conv, j0_conv + 32 * sh, cw, cbias, xs, xoff + 16 * sh);
+                for (int r = 0; r < kRuns; ++r)
+                    if (!window_one_id<K>(raw, j0_conv + 32 * r))
+                        conv_masked_run<K, MODE>(raw, p_conv, j0_conv + 32 * r, cw, cbias, xs, xoff + 16 * r);
             }
         };
         __syncthreads();  // raw rows of chunk 0 staged

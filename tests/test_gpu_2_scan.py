@@ -116,6 +116,32 @@ def test_conv_scan_fwd_matches_oracle(B, L, H, P, N, G, K, dtype, with_init, seg
     assert_bitexact(cfin, torch.from_numpy(rc).to(dtype), "conv final state")
 
 
+@pytest.mark.parametrize("K", [3, 4])
+def test_conv_scan_fwd_boundaries_at_run_and_chunk_edges(K):
+    """seq_idx changes placed where the fused conv's unmasked fast path and its masked redo
+    meet: token 1, the first and last taps of an 8-token run's window, the start of the second
+    32-token half of a chunk, chunk boundaries and the last token; the second row reuses an
+    earlier id after a short middle sequence (A, B, A), which the conv treats by equality."""
+    import ssm_sequence_models_amd as ssm
+    B, L, H, P, N, G = 2, 320, 2, 64, 128, 1
+    xBC, w, b, dt, A, cinit, sinit, _ = _fused_inputs(B, L, H, P, N, G, K, BF16, seed=41)
+    seq = torch.zeros(B, L, dtype=torch.int32)
+    for cut in (1, 8, 11, 32, 35, 64, 66, 127, 128, 200, 319):
+        seq[0, cut:] += 1
+    ids1 = [(0, 0), (3, 1), (31, 2), (40, 1), (63, 3), (96, 4), (97, 3), (250, 5)]
+    for start, v in ids1:
+        seq[1, start:] = v
+    y, cfin, sfin = ssm.conv_scan_fwd(dev(xBC), dev(w), dev(b), dev(dt), dev(A), H, P, G, N,
+                                      conv_initial_state=dev(cinit), initial_state=dev(sinit),
+                                      seq_idx=dev(seq))
+    torch.cuda.synchronize()
+    ry, rc, rs = oracle.conv_scan_fwd(xBC, w, b, cinit, dt, A, sinit, seq, H, P, G, N,
+                                      act="silu", out_dtype="bf16", state_dtype="f32")
+    assert_close(y, ry, "y")
+    assert_close(sfin, rs, "ssm final state")
+    assert_bitexact(cfin, torch.from_numpy(rc).to(BF16), "conv final state")
+
+
 def test_conv_scan_fwd_inplace_states_and_len0():
     import ssm_sequence_models_amd as ssm
     H, P, N, G, K = 2, 64, 128, 1, 4
