@@ -46,7 +46,7 @@ constexpr int kQ = 64;       // tokens per chunk
 constexpr int kP = 64;       // head channels (4 consumer waves x 16)
 constexpr int kN = 128;      // state size
 constexpr int kKmax = 8;     // widest conv handled
-constexpr int kPrepThreads = 512;
+constexpr int kPrepThreads = 1024;
 constexpr int kMainThreads = 768;  // 4 consumer, 4 producer and 4 conv wavefronts
 
 // workspace per (row, chunk, group)
@@ -169,11 +169,11 @@ ssd_prep_kernel(ChunkedArgs a) {
     }
     __syncthreads();
 
-    // one channel and one half of the chunk per thread (B channels 0..127, then C channels;
-    // tokens 32 half .. 32 half + 31), 8 tokens per batch
-    static_assert(kPrepThreads == 4 * kN, "two threads per conv channel");
+    // one channel and one quarter of the chunk per thread (B channels 0..127, then C channels;
+    // tokens 16 qt .. 16 qt + 15), 8 tokens per batch
+    static_assert(kPrepThreads == 8 * kN, "four threads per conv channel");
     {
-        const int ch = tid & (2 * kN - 1), half = tid / (2 * kN);
+        const int ch = tid & (2 * kN - 1), qt = tid / (2 * kN);
         const bool isC = ch >= kN;
         const int n = isC ? ch - kN : ch;
         const int64_t col = (isC ? a.c_col0 : a.b_col0) + g * kN + n;
@@ -183,7 +183,7 @@ ssd_prep_kernel(ChunkedArgs a) {
 #pragma unroll
             for (int k = 0; k < K; ++k) w[k] = a.conv_w[col * K + k];
             const double bias = a.conv_b ? a.conv_b[col] : 0.0f;
-            for (int j0 = half * (kQ / 2); j0 < (half + 1) * (kQ / 2); j0 += 8) {
+            for (int j0 = qt * (kQ / 4); j0 < (qt + 1) * (kQ / 4); j0 += 8) {
                 double u[8 + K - 1];
                 int32_t id[8 + K - 1];
 #pragma unroll
@@ -210,7 +210,7 @@ ssd_prep_kernel(ChunkedArgs a) {
                 }
             }
         } else {
-            for (int j = half * (kQ / 2); j < (half + 1) * (kQ / 2); ++j)
+            for (int j = qt * (kQ / 4); j < (qt + 1) * (kQ / 4); ++j)
                 *reinterpret_cast<uint16_t*>(dst + j * kPrepStride + n * 2) =
                     lds_ld<uint16_t>(sRaw, (j + K - 1) * kPrepRaw + ch * 2);
         }
@@ -239,11 +239,12 @@ ssd_prep_kernel(ChunkedArgs a) {
             u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
     // G = C B^T with the causal mask applied (G[i][j] = 0 for j > i), all 16 tiles written;
-    // wave w owns rows 16 (w % 4) .. +15 and the column tiles of parity w / 4
+    // wave w owns the tile of rows 16 (w % 4) .. +15 and columns 16 (w / 4) .. +15
     const int lane = tid & 63, li = lane & 15, g4 = lane >> 4;
-    const int wave = (tid >> 6) & 3, jpar = tid >> 8;
-    static_assert(kPrepThreads == 8 * 64, "eight waves");
-    for (int jt = jpar; jt < kQ / 16; jt += 2) {
+    const int wave = (tid >> 6) & 3;
+    static_assert(kPrepThreads == 16 * 64, "sixteen waves");
+    {
+        const int jt = tid >> 8;
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if (jt <= wave) {
 #pragma unroll
