@@ -73,14 +73,26 @@ __device__ __forceinline__ void lds_st(uint8_t* base, int off, const T& v) {
 
 // v = hi + lo, hi = rne(v), lo = rne(v - hi): one paired conversion for two his, their
 // widening by shift / mask, two exact subtractions and one paired conversion for the los
+// lo = v - hi in one instruction per value: the bf16 dot product of the hi pair with (-1, 0)
+// or (0, -1), accumulated onto v (the difference is exact in fp32, so the dot product's
+// rounding does not enter; checked bit for bit against the subtraction on the GPU).  The two
+// constant pairs go in as register values the compiler cannot see: as a source of this
+// instruction it encodes 0x0000BF80 as the inline constant -1.0, which the hardware reads as
+// the 32-bit pattern of -1.0f, the pair (0, -1).
 __device__ __forceinline__ void split_hilo(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    uint32_t c_lo = 0x0000BF80u, c_hi = 0xBF800000u;
+    asm volatile("" : "+s"(c_lo), "+s"(c_hi));
+    const bf16x2v neg_lo = __builtin_bit_cast(bf16x2v, c_lo);  // (-1, 0)
+    const bf16x2v neg_hi = __builtin_bit_cast(bf16x2v, c_hi);  // (0, -1)
     u32x4 h, l;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const uint32_t hp = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xFFFF0000u);
+        const bf16x2v hv = __builtin_bit_cast(bf16x2v, hp);
         h[e] = hp;
-        l[e] = pack_bf16x2(v[2 * e] - h0, v[2 * e + 1] - h1);
+        l[e] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(hv, neg_lo, v[2 * e], false),
+                           __builtin_amdgcn_fdot2_f32_bf16(hv, neg_hi, v[2 * e + 1], false));
     }
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, l);
