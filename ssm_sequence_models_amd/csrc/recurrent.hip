@@ -25,32 +25,57 @@
 namespace ssm {
 namespace {
 
-// Sum over the LP adjacent lanes sharing each of the J channels v[j] belongs to.  Returns the
-// sum for channel index jr = (lane's reduce-scatter position) in v[0]; *jr gets that index,
-// and the lane is the group's writer when (lane % (LP / J')) == 0 (see the caller).
-template <int J, int LP>
-__device__ __forceinline__ float reduce_scatter(float (&v)[J], int lane, int* jr) {
-    int j_off = 0;
-    int cnt = J;
+// Exchange with the partner lane of level `off` inside a 32-lane group: off 16 pairs lane i
+// with i ^ 16 (ds_swizzle), off 8 with i ^ 15 (DPP row_mirror), off 4 with i ^ 7 (DPP
+// row_half_mirror), off 2 and 1 with i ^ 2 and i ^ 1 (DPP quad_perm).  Each partner differs
+// from i in the bit `off`, and together the five relations reach all 32 lanes.
+template <int OFF>
+__device__ __forceinline__ float xchg(float v) {
+    const int b = __float_as_int(v);
+    int r;
+    if constexpr (OFF == 16) r = __builtin_amdgcn_ds_swizzle(b, 0x401F);  // and 0x1f, xor 0x10
+    else if constexpr (OFF == 8) r = __builtin_amdgcn_update_dpp(0, b, 0x140, 0xf, 0xf, false);
+    else if constexpr (OFF == 4) r = __builtin_amdgcn_update_dpp(0, b, 0x141, 0xf, 0xf, false);
+    else if constexpr (OFF == 2) r = __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xf, 0xf, false);
+    else r = __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xf, 0xf, false);
+    return __int_as_float(r);
+}
+
+// One level of the reduce-scatter over the J sums: a lane keeps the half of its `cnt` sums
+// chosen by bit OFF of its lane index and adds its partner's copy of that half; once one sum
+// is left, levels add the partner's sum.  The partner holds the same index set (it agrees with
+// the lane on every bit decided so far) and sums over a disjoint set of lanes.
+template <int J, int OFF>
+__device__ __forceinline__ void rs_level(float (&v)[J], int& cnt, int& j_off, int lane) {
+    if (cnt > 1) {
+        const bool hi = (lane & OFF) != 0;
+        const int half = cnt / 2;
 #pragma unroll
-    for (int off = LP / 2; off >= 1; off >>= 1) {
-        if (cnt > 1) {
-            const bool hi = (lane & off) != 0;
-            const int half = cnt / 2;
-#pragma unroll
-            for (int i = 0; i < J / 2; ++i) {
-                if (i < half) {
-                    const float send = hi ? v[i] : v[i + half];
-                    const float mine = hi ? v[i + half] : v[i];
-                    v[i] = mine + __shfl_xor(send, off);
-                }
+        for (int i = 0; i < J / 2; ++i) {
+            if (i < half) {
+                const float send = hi ? v[i] : v[i + half];
+                const float mine = hi ? v[i + half] : v[i];
+                v[i] = mine + xchg<OFF>(send);
             }
-            j_off += hi ? half : 0;
-            cnt = half;
-        } else {
-            v[0] += __shfl_xor(v[0], off);
         }
+        j_off += hi ? half : 0;
+        cnt = half;
+    } else {
+        v[0] += xchg<OFF>(v[0]);
     }
+}
+
+// Sum over the 32 adjacent lanes sharing each of the J channels v[j] belongs to.  Returns the
+// sum for channel index *jr (the lane's reduce-scatter position); the lanes with
+// lane % (32 / J) == 0 are the writers (see the caller).
+template <int J>
+__device__ __forceinline__ float reduce_scatter32(float (&v)[J], int lane, int* jr) {
+    int j_off = 0, cnt = J;
+    rs_level<J, 16>(v, cnt, j_off, lane);
+    rs_level<J, 8>(v, cnt, j_off, lane);
+    rs_level<J, 4>(v, cnt, j_off, lane);
+    rs_level<J, 2>(v, cnt, j_off, lane);
+    rs_level<J, 1>(v, cnt, j_off, lane);
     *jr = j_off;
     return v[0];
 }
@@ -177,7 +202,7 @@ recurrent_kernel(RecurrentArgs a, int nthreads, int tile_t) {
             // run j of thread tid is channel p = (4 nthreads / N) j + tid / 32; lanes tid % 32
             // share it; after the reduce-scatter the lanes with tid % (32 / J) == 0 hold whole sums
             int jr;
-            const float yv = reduce_scatter<J, 32>(part, tid, &jr);
+            const float yv = reduce_scatter32<J>(part, tid, &jr);
             if ((tid & (32 / J - 1)) == 0)
                 D::store(y, ((b * a.T + t) * a.H + h) * a.P + (4 * nthreads / 128) * jr + tid / 32, yv);
         } else {
