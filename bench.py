@@ -260,15 +260,21 @@ def main():
     ssm.timing_read()  # clear
     ssm.timing_enable(True)
     torch.cuda.synchronize()
+    # per-step events on the stream the library launches on (for the median and minimum)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e_start, e_end in ev:
+        e_start.record()
         step()
+        e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ssm.timing_enable(False)
     main_ms, launches = ssm.timing_read()
     assert launches == args.steps, (launches, args.steps)
     ms_per_step = wall * 1e3 / args.steps
+    step_ms = sorted(e_start.elapsed_time(e_end) for e_start, e_end in ev)
     main_ms_avg = main_ms / launches
     tokens = s.B * s.L
     op_bytes, main_bytes = algorithmic_bytes(s)
@@ -286,6 +292,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": step_ms[len(step_ms) // 2],
+        "ms_per_step_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

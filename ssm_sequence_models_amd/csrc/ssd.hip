@@ -982,6 +982,20 @@ ssd_main_kernel(ChunkedArgs a) {
         constexpr int kRows = kQ + K - 1;
         Fetch f;  // registers of the next chunk to produce
         int32_t seq_row = 0;
+        // In the state-only pass the producers have time to spare and the conv waves set the
+        // pace: there the producers convolve the second half of each chunk (tokens 32 .. 63)
+        // for channel 16 pw + li, into the X slot lane that consumer wave pw reads.
+        constexpr bool kProdConv = PASS == 1;
+        const int p_pc = 16 * pw + (lane & 15), j0_pc = 32 + 8 * (lane >> 4);
+        const int xoff_pc = (pw * 64 + lane) * 32 + 16;
+        double pcw[K], pcb = 0.0;
+        if (kProdConv) conv_weights<K, MODE>(a, h, p_pc, pcw, pcb);
+        auto prod_conv_finish = [&](const uint8_t* raw, uint8_t* xs, uint32_t near, bf16x8 x) {
+            x = conv_fixups<K, MODE, false>(raw, p_pc, j0_pc, pcw, pcb, near, x);
+            lds_st(xs, xoff_pc, x);
+            if (HAS_SEQ && MODE != 0 && !window_one_id<K>(raw, j0_pc))
+                conv_masked_run<K, MODE>(raw, p_pc, j0_pc, pcw, pcb, xs, xoff_pc);
+        };
         // prologue: the block's first chunk's tiles, registers and raw rows and the second
         // chunk's raw rows; then the first chunk produced.  Local chunk c is global chunk
         // c0 + c (LDS slots go by the local index, memory by the global one).
@@ -995,6 +1009,11 @@ ssd_main_kernel(ChunkedArgs a) {
         __syncthreads();  // raw rows of chunk 0 staged
         scalars_and_m<HAS_SEQ, PASS>(f, c0, bk.L, Ah2, pw, lane, sm, ps);
         fetch_regs<HAS_SEQ, PASS>(bk, o, nCl > 1 ? c0 + 1 : c0, pw, lane, f);
+        if (kProdConv) {
+            uint32_t near = 0;
+            const bf16x8 x = conv_fast<K, MODE, false>(sm_raw0, p_pc, j0_pc, pcw, pcb, &near);
+            prod_conv_finish(sm_raw0, sm + kOffX, near, x);
+        }
         __syncthreads();
         // chunk c: load chunk c+1's tiles (into stage (c+1)&1, free since chunk c-1 was
         // contracted) and chunk c+2's raw rows (into raw slot c&1, free since chunk c was
@@ -1022,9 +1041,16 @@ ssd_main_kernel(ChunkedArgs a) {
                 asm volatile("" ::: "memory");
                 if (PASS == 0)
                     store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c0 + c - 1, c > 0, pw, lane);
+                // (state-only pass) the unbranched part of the conv of chunk k's second half
+                // before the wait; its rare fix-ups after it
+                const uint8_t* raw_cv = half == 0 ? sm_raw1 : sm_raw0;  // slot k & 1
+                uint32_t near = 0;
+                bf16x8 xpc{};
+                if (kProdConv) xpc = conv_fast<K, MODE, false>(raw_cv, p_pc, j0_pc, pcw, pcb, &near);
                 scalars_and_m<HAS_SEQ, PASS>(f, c0 + kt, bk.L, Ah2, pw, lane, stk, ps);
                 __builtin_amdgcn_s_waitcnt(kWaitVm0);
                 fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + kr, pw, lane, f);
+                if (kProdConv) prod_conv_finish(raw_cv, sm + kOffX + (k & 1) * kXBytes, near, xpc);
                 if (HAS_SEQ && k + 1 < nCl && ptid < kRows)
                     reinterpret_cast<int32_t*>(raw_ld + kRwSeq)[ptid] = seq_row;
                 __syncthreads();
@@ -1036,7 +1062,7 @@ ssd_main_kernel(ChunkedArgs a) {
         // r = 0, 1), into the X slot lane that consumer wave cv reads.  (Eight conv waves, one
         // run each, were measured slower: at 16 waves per group the 128-VGPR budget spills.)
         const int cv = wave - 8;
-        constexpr int kRuns = 2;
+        constexpr int kRuns = PASS == 1 ? 1 : 2;  // the producers take run 1 in the state-only pass
         const int p_conv = 16 * cv + li;
         const int j0_conv = 8 * g4;
         const int xoff = (cv * 64 + lane) * 32;
