@@ -57,6 +57,7 @@ constexpr int64_t kWsG = static_cast<int64_t>(kQ) * kQ;    // fp32 elements, [i]
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -301,16 +302,12 @@ constexpr int kRwX = 0;                          // raw x [rows][8 pieces], piec
 constexpr int kRwSeq = (kRowsMax + 1) * 128;     // seq ids of the raw rows (after 72 row slots:
                                                  // the loads fill 9 blocks of 8 rows)
 constexpr int kRawBytes = kRwSeq + 72 * 4;
-//   y slot (two, by chunk parity): consumers write their Y^T tiles, producers store whole
-//   token rows one chunk later
-constexpr int kYBytes = kQ * kP * 2;             // [64 tok][16 slots of 8 B], slot ^ (tok & 15)
 //   producer-private scalars: cum, dtv, r of the chunk
 constexpr int kPsBytes = 4 * kQ * 4;  // per producer wave: cum2, dt, last reset, R
 //   X slot (two, by chunk parity): the conv waves' bf16 outputs (X operands), 16 bytes per
 //   (wave, lane, run), read back by the consumer lane with the same wave-in-role and lane index
 constexpr int kXBytes = kQ * kP * 2;
-constexpr int kOffY = 2 * kStageBytes;
-constexpr int kOffPs = kOffY + 2 * kYBytes;
+constexpr int kOffPs = 2 * kStageBytes;
 constexpr int kOffX = kOffPs + 4 * kPsBytes;
 constexpr int kMainLds = kOffX + 2 * kXBytes;
 static_assert(kMainLds + 2 * kCbBytes + 2 * kRawBytes <= 160 * 1024, "LDS budget");
@@ -326,8 +323,6 @@ __device__ __forceinline__ int sw_8(int row, int q) { return row * 128 + ((q ^ (
 __device__ __forceinline__ int sw_xr(int row, int q) {
     return row * 128 + ((q ^ (((row >> 3) & 3) << 1)) << 4);
 }
-// y tile: 16 lanes of a ds_write_b64 write 16 tokens at the same 8-byte column
-__device__ __forceinline__ int sw_y(int tok, int slot8) { return tok * 128 + ((slot8 ^ (tok & 15)) << 3); }
 
 // M tiles computed by each producer wave pw (uniform): unit u is the 16 x 32 tile (row
 // block I, column half S); the six tiles cover j <= i.  Waves 2 and 3 have one tile each
@@ -381,7 +376,6 @@ struct POff {
     uint32_t x[3];          // raw x LDS blocks r = pw, pw + 4, 8: row 8r + l/8, slot l%8
     uint32_t g[2];          // G piece of M unit u: row i, columns 8q .. 8q+7
     uint32_t dt;            // token = lane
-    uint32_t y[2];          // y piece ptid + 256 k: token, 8 channels
 };
 
 // Registers a producer lane loads for chunk k (its M tiles and scalars)
@@ -582,25 +576,6 @@ __device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, 
     }
 }
 
-// Store the y rows of chunk k (left in `yt` by the consumers): whole 128-byte token rows,
-// two 16-byte pieces per producer lane; rows past the end are dropped by the range check,
-// and all of them when `live` is false
-__device__ __forceinline__ void store_y(const Blk& bk, const POff& o, const uint8_t* yt,
-                                        int64_t k, bool live, int pw, int lane) {
-    const int t0 = static_cast<int>(k) * kQ;
-    const Rsrc ry = make_rsrc(bk.y + static_cast<int64_t>(live ? t0 : 0) * bk.H * kP,
-                              live ? static_cast<int64_t>(bk.L - t0) * bk.H * kP * 2 : 0);
-    const int ptid = pw * 64 + lane;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int idx = ptid + 256 * q;
-        const int tok = idx >> 3, c8 = idx & 7;
-        const uint2 lo = lds_ld<uint2>(yt, sw_y(tok, 2 * c8));
-        const uint2 hi = lds_ld<uint2>(yt, sw_y(tok, 2 * c8 + 1));
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo.x, lo.y, hi.x, hi.y}, ry, o.y[q], 0, 0);
-    }
-}
-
 // Consumer: the conv of channel p over tokens j0 .. j0+7 of a chunk from its staged raw rows
 // (row rho <-> token t0 - (K-1) + rho), rounded to bf16 -> one MFMA operand.  MODE 0: no conv
 // (the rows already hold x); 1: conv, identity phi; 2: conv + SiLU.  The fast path has no
@@ -783,10 +758,10 @@ ssd_main_kernel(ChunkedArgs a) {
     // to interleave.  All loops pass the same number of block barriers: two in the prologue
     // (raw rows of chunk 0 staged; chunk 0 produced and convolved), then one per chunk.
     // Between two barriers:
-    //   consumers  contract chunk c from stage c&1 and X slot c&1, write y(c) to y slot c&1;
+    //   consumers  contract chunk c from stage c&1 and X slot c&1 and store y(c);
     //   producers  load chunk c+1's tiles into stage (c+1)&1 and chunk c+2's raw rows into
-    //              raw slot c&1, store y(c-1) from y slot (c-1)&1, compute chunk c+1's
-    //              scalars and M tiles, then load chunk c+2's registers;
+    //              raw slot c&1, compute chunk c+1's scalars and M tiles, then load chunk
+    //              c+2's registers;
     //   conv waves convolve chunk c+1 from raw slot (c+1)&1 into X slot (c+1)&1.
     if (role == 0) {
         // state slice acc[t][r] = h[p][n], p = 16 wave + li, n = 32(t/2) + 8 g4 + 4(t%2) + r
@@ -814,11 +789,13 @@ ssd_main_kernel(ChunkedArgs a) {
         // X operands (lane: channel p_own, tokens 32 s + 8 g4 .. +7), convolved by the conv
         // wave with this wave's index
         const int xoff = (wave * 64 + lane) * 32;
+        // y: bytes between tokens, and this lane's offset from the chunk's first token row
+        const uint32_t y_tok = static_cast<uint32_t>(bk.H) * kP * 2;
+        const uint32_t y_off = li * y_tok + (16 * wave + 4 * g4) * 2;
         float dprod = 1.0f;  // decay product of the block's chunks (state-only pass)
         for (int64_t cn = 0; cn < nCl; ++cn) {
             const uint8_t* st = sm + (cn & 1) * kStageBytes;
             const uint8_t* cbt = sm_cb + (cn & 1) * kCbBytes;
-            uint8_t* yt = sm + kOffY + (cn & 1) * kYBytes;
             bf16x8 xv[2];
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) xv[sh] = lds_ld<bf16x8>(sm + kOffX + (cn & 1) * kXBytes, xoff + 16 * sh);
@@ -913,16 +890,21 @@ ssd_main_kernel(ChunkedArgs a) {
                 for (int t = 0; t < 8; ++t) acc[t] = mfma(bv[t], bl, acc[t]);
             }
             if constexpr (PASS == 0) {
-                // y tile of this chunk -> LDS (the producers store it next iteration)
+                // y of this chunk straight to memory: a lane stores 4 channels of token
+                // 16 I + li (8 bytes), the four waves fill each 128-byte token row; rows past
+                // the end of the row are dropped by the range check
                 float eI[4];
 #pragma unroll
                 for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
+                const int t0 = static_cast<int>(c0 + cn) * kQ;
+                const Rsrc ry = make_rsrc(bk.y + static_cast<int64_t>(t0) * bk.H * kP,
+                                          static_cast<int64_t>(bk.L - t0) * bk.H * kP * 2);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
-                    pk.y = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
-                    lds_st(yt, sw_y(16 * I + li, 4 * wave + g4), pk);
+                    u32x2 pk;
+                    pk[0] = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
+                    pk[1] = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, ry, y_off + 16 * I * y_tok, 0, 0);
                 }
             } else {
                 dprod *= decay;
@@ -971,12 +953,6 @@ ssd_main_kernel(ChunkedArgs a) {
                 o.g[u] = (i * kQ + 8 * q) * 4;
             }
             o.dt = lane * bk.H * 4;
-            const int ptid = pw * 64 + lane;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int idx = ptid + 256 * q;
-                o.y[q] = (idx >> 3) * bk.H * kP * 2 + (idx & 7) * 16;
-            }
         }
         const int ptid = pw * 64 + lane;
         constexpr int kRows = kQ + K - 1;
@@ -1017,15 +993,14 @@ ssd_main_kernel(ChunkedArgs a) {
         __syncthreads();
         // chunk c: load chunk c+1's tiles (into stage (c+1)&1, free since chunk c-1 was
         // contracted) and chunk c+2's raw rows (into raw slot c&1, free since chunk c was
-        // convolved), store y(c-1), convolve the second half of chunk c+1 and compute its
+        // convolved), (state-only pass) convolve the second half of chunk c+1, compute its
         // scalars and M tiles from the registers loaded during the previous chunk; then, once
         // this chunk's transfers have landed, load chunk c+2's registers, which only the next
         // chunk's M tiles wait for.  Unrolled by two so the raw slots are compile-time arrays.
         // The body has no branches between the loads and the LDS work (the compiler then
         // keeps track of which LDS array an outstanding transfer writes): past the last
         // chunk the indices are clamped, so the loads repeat the last chunk into slots
-        // nobody reads, the conv writes an X slot nobody reads, and the first iteration's y
-        // stores go to an empty range.
+        // nobody reads and the conv writes an X slot nobody reads.
         for (int64_t cn = 0; cn < nCl; cn += 2) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -1039,8 +1014,6 @@ ssd_main_kernel(ChunkedArgs a) {
                 fetch_tiles<PASS>(bk, o, c0 + kt, pw, sm_cb + (k & 1) * kCbBytes);
                 fetch_raw<K, HAS_SEQ>(bk, o, c0 + kr, kr >= 1, pw, lane, raw_ld, &seq_row);
                 asm volatile("" ::: "memory");
-                if (PASS == 0)
-                    store_y(bk, o, sm + kOffY + ((c - 1) & 1) * kYBytes, c0 + c - 1, c > 0, pw, lane);
                 // (state-only pass) the unbranched part of the conv of chunk k's second half
                 // before the wait; its rare fix-ups after it
                 const uint8_t* raw_cv = half == 0 ? sm_raw1 : sm_raw0;  // slot k & 1
@@ -1056,7 +1029,6 @@ ssd_main_kernel(ChunkedArgs a) {
                 __syncthreads();
             }
         }
-        if (PASS == 0) store_y(bk, o, sm + kOffY + ((nCl - 1) & 1) * kYBytes, c0 + nCl - 1, true, pw, lane);
     } else {
         // conv wave cv: channel p = 16 cv + li over tokens 32 r + 8 g4 .. +7 of a chunk (runs
         // r = 0, 1), into the X slot lane that consumer wave cv reads.  (Eight conv waves, one
