@@ -295,8 +295,9 @@ constexpr int kStE = kStMlo + kQ * 128;          // E_i = exp(cum_i) on the lead
 constexpr int kStW = kStE + kQ * 4;              // W_j = exp(cum_last - cum_j) dt_j
 constexpr int kStDecay = kStW + kQ * 4;          // exp(cum_last) (0 after a reset)
 constexpr int kStageBytes = kStDecay + 16;
-//   raw x slot (two, by chunk parity), loaded two chunks ahead: the conv of chunk c+1 runs
-//   while chunk c is contracted
+//   raw x slot (three, by chunk index mod 3), loaded two chunks ahead: the conv of chunk c+1
+//   runs while chunk c is contracted, and chunk c's rows stay for the consumers' exact
+//   recomputation of the conv outputs the fast path flagged
 constexpr int kRowsMax = kQ + kKmax - 1;         // raw x rows of a chunk incl. the conv halo
 constexpr int kRwX = 0;                          // raw x [rows][8 pieces], piece ^ xr_swz(row)
 constexpr int kRwSeq = (kRowsMax + 1) * 128;     // seq ids of the raw rows (after 72 row slots:
@@ -307,10 +308,18 @@ constexpr int kPsBytes = 4 * kQ * 4;  // per producer wave: cum2, dt, last reset
 //   X slot (two, by chunk parity): the conv waves' bf16 outputs (X operands), 16 bytes per
 //   (wave, lane, run), read back by the consumer lane with the same wave-in-role and lane index
 constexpr int kXBytes = kQ * kP * 2;
+//   flag slot (two, by chunk parity): per X slot lane, one 16-bit mask per 8-output run of
+//   the outputs the conv's fast path could not round with certainty
+constexpr int kFlBytes = 4 * 64 * 4;
 constexpr int kOffPs = 2 * kStageBytes;
 constexpr int kOffX = kOffPs + 4 * kPsBytes;
-constexpr int kMainLds = kOffX + 2 * kXBytes;
-static_assert(kMainLds + 2 * kCbBytes + 2 * kRawBytes <= 160 * 1024, "LDS budget");
+constexpr int kOffFl = kOffX + 2 * kXBytes;
+//   conv weights and bias of the head's x channels in double (SiLU conv only), for the
+//   consumers' recomputations: channel p at kOffW + p * kWStride
+constexpr int kWStride = (kKmax + 1) * 8;
+constexpr int kOffW = kOffFl + 2 * kFlBytes;
+constexpr int kMainLds = kOffW + kP * kWStride;
+static_assert(kMainLds + 2 * kCbBytes + 3 * kRawBytes <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int sw_c(int tok, int q) { return tok * 256 + ((q ^ (tok & 15)) << 4); }
 // B^T rows are read through the state-tile row map n = 32T + 8(l>>2) + 4(t&1) + (l&3):
@@ -656,6 +665,19 @@ __device__ __forceinline__ bf16x8 conv_fixups(const uint8_t* raw, int p, int j0,
     return x;
 }
 
+// One conv + SiLU output (channel p, taps from raw row r0), rounded exactly, with the weights
+// from the LDS table: the consumers' rare recomputation of a flagged output, out of line so
+// that its double-precision registers do not count against the contraction loop
+template <int K>
+__device__ __noinline__ uint32_t silu_conv_exact(const uint8_t* raw, const uint8_t* wt, int p, int r0) {
+    double cw[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) cw[k] = lds_ld<double>(wt, p * kWStride + 8 * k);
+    const double cbias = lds_ld<double>(wt, p * kWStride + 8 * K);
+    const double z = conv_z<K, 2, false>(raw, p >> 3, (p & 7) * 2, r0, cw, cbias);
+    return silu_f64_to_bf16(z);
+}
+
 // With seq_idx: true when raw rows j0 .. j0+K+6 (the taps of a run's 8 outputs) carry one
 // sequence id, so the run's conv needs no masking.  j0 is a multiple of 8, so the ids come in
 // 16-byte reads (the id array has room for rows up to j0 + 15 <= 71); the comparisons are
@@ -716,6 +738,7 @@ ssd_main_kernel(ChunkedArgs a) {
     // from reads of the other
     __shared__ __attribute__((aligned(16))) uint8_t sm_raw0[kRawBytes];
     __shared__ __attribute__((aligned(16))) uint8_t sm_raw1[kRawBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t sm_raw2[kRawBytes];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
     const int role = wave >> 2;  // 0 consumer, 1 producer, 2 conv
@@ -793,12 +816,15 @@ ssd_main_kernel(ChunkedArgs a) {
         const uint32_t y_tok = static_cast<uint32_t>(bk.H) * kP * 2;
         const uint32_t y_off = li * y_tok + (16 * wave + 4 * g4) * 2;
         float dprod = 1.0f;  // decay product of the block's chunks (state-only pass)
+        int rslot = 0;  // raw slot of chunk cn
         for (int64_t cn = 0; cn < nCl; ++cn) {
             const uint8_t* st = sm + (cn & 1) * kStageBytes;
             const uint8_t* cbt = sm_cb + (cn & 1) * kCbBytes;
             bf16x8 xv[2];
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) xv[sh] = lds_ld<bf16x8>(sm + kOffX + (cn & 1) * kXBytes, xoff + 16 * sh);
+            uint32_t flw = 0;  // bit 16 sh + e: output e of xv[sh] needs the exact recomputation
+            if constexpr (MODE == 2) flw = lds_ld<uint32_t>(sm + kOffFl + (cn & 1) * kFlBytes, (wave * 64 + lane) * 4);
 
             // Y^T[p][i], p = 16 wave + 4 g4 + r, i = 16 I + li.  Each phase loads its LDS
             // operands before its MFMAs, and consecutive MFMAs use different accumulators
@@ -811,34 +837,11 @@ ssd_main_kernel(ChunkedArgs a) {
                 yi[I] = yo[I];
             }
             if constexpr (PASS == 0) {
-            // intra-chunk part: M tiles (I, s) with 32 s <= 16 I + 15; the hi tiles, then the
-            // lo tiles in the same registers (keeps the wave's peak register count down)
-            bf16x8 mt[6];
-#pragma unroll
-            for (int u = 0; u < 6; ++u) {
-                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                mt[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
-            }
+            // initial-state part first (it does not need X), one 32-wide slice m of the state
+            // at a time; the next slice's C tiles load while this slice's MFMAs run
             bf16x8 cb[2][4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) cb[0][I] = lds_ld<bf16x8>(cbt, kCbC + sw_c(16 * I + li, g4));
-#pragma unroll
-            for (int u = 0; u < 6; ++u) {
-                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                yi[I] = mfma(xv[sh], mt[u], yi[I]);
-            }
-#pragma unroll
-            for (int u = 0; u < 6; ++u) {
-                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                mt[u] = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * sh + g4));
-            }
-#pragma unroll
-            for (int u = 0; u < 6; ++u) {
-                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                yi[I] = mfma(xv[sh], mt[u], yi[I]);
-            }
-            // initial-state part, one 32-wide slice m of the state at a time; the next
-            // slice's C tiles load while this slice's MFMAs run
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 if (m + 1 < 4) {
@@ -858,6 +861,56 @@ ssd_main_kernel(ChunkedArgs a) {
                 for (int I = 0; I < 4; ++I) yo[I] = mfma(hhi, cb[m & 1][I], yo[I]);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) yo[I] = mfma(hlo, cb[m & 1][I], yo[I]);
+            }
+            }
+            if constexpr (MODE == 2) {
+                // the conv outputs of this lane that the fast path flagged (rare): redone in
+                // double from the chunk's raw rows, which stay in their slot until the chunk
+                // ends, while the matrix cores work through the products above
+                if (flw != 0) {
+                    const uint8_t* rawc = rslot == 0 ? sm_raw0 : rslot == 1 ? sm_raw1 : sm_raw2;
+                    u32x4 xw[2] = {__builtin_bit_cast(u32x4, xv[0]), __builtin_bit_cast(u32x4, xv[1])};
+                    do {
+                        const int bit = __builtin_ctz(flw);
+                        flw &= flw - 1;
+                        const int sh = bit >> 4, e = bit & 7;
+                        const uint32_t v = silu_conv_exact<K>(rawc, sm + kOffW, p_own, 8 * g4 + 32 * sh + e);
+                        const int word = e >> 1, shift = 16 * (e & 1);
+#pragma unroll
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int d = 0; d < 4; ++d)
+                                if (t == sh && d == word)
+                                    xw[t][d] = (xw[t][d] & ~(0xFFFFu << shift)) | (v << shift);
+                    } while (flw != 0);
+                    xv[0] = __builtin_bit_cast(bf16x8, xw[0]);
+                    xv[1] = __builtin_bit_cast(bf16x8, xw[1]);
+                }
+            }
+            rslot = rslot == 2 ? 0 : rslot + 1;
+            if constexpr (PASS == 0) {
+            // intra-chunk part: M tiles (I, s) with 32 s <= 16 I + 15; the hi tiles, then the
+            // lo tiles in the same registers (keeps the wave's peak register count down)
+            bf16x8 mt[6];
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                mt[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
+            }
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                yi[I] = mfma(xv[sh], mt[u], yi[I]);
+            }
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                mt[u] = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * sh + g4));
+            }
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
+                yi[I] = mfma(xv[sh], mt[u], yi[I]);
             }
             }
             // state update: h^T[n][p] = decay h^T + B^T (W o X)
@@ -960,17 +1013,20 @@ ssd_main_kernel(ChunkedArgs a) {
         int32_t seq_row = 0;
         // In the state-only pass the producers have time to spare and the conv waves set the
         // pace: there the producers convolve the second half of each chunk (tokens 32 .. 63)
-        // for channel 16 pw + li, into the X slot lane that consumer wave pw reads.
+        // for channel 16 pw + li, into the X slot lane that consumer wave pw reads, and its
+        // flag mask into the upper half of that lane's flag word.
         constexpr bool kProdConv = PASS == 1;
         const int p_pc = 16 * pw + (lane & 15), j0_pc = 32 + 8 * (lane >> 4);
         const int xoff_pc = (pw * 64 + lane) * 32 + 16;
         double pcw[K], pcb = 0.0;
         if (kProdConv) conv_weights<K, MODE>(a, h, p_pc, pcw, pcb);
-        auto prod_conv_finish = [&](const uint8_t* raw, uint8_t* xs, uint32_t near, bf16x8 x) {
-            x = conv_fixups<K, MODE, false>(raw, p_pc, j0_pc, pcw, pcb, near, x);
+        auto prod_conv_finish = [&](const uint8_t* raw, uint8_t* xs, uint8_t* fl, uint32_t near, bf16x8 x) {
             lds_st(xs, xoff_pc, x);
-            if (HAS_SEQ && MODE != 0 && !window_one_id<K>(raw, j0_pc))
+            if (HAS_SEQ && MODE != 0 && !window_one_id<K>(raw, j0_pc)) {
                 conv_masked_run<K, MODE>(raw, p_pc, j0_pc, pcw, pcb, xs, xoff_pc);
+                near = 0;
+            }
+            lds_st(fl, (pw * 64 + lane) * 4 + 2, static_cast<uint16_t>(near));
         };
         // prologue: the block's first chunk's tiles, registers and raw rows and the second
         // chunk's raw rows; then the first chunk produced.  Local chunk c is global chunk
@@ -988,42 +1044,43 @@ ssd_main_kernel(ChunkedArgs a) {
         if (kProdConv) {
             uint32_t near = 0;
             const bf16x8 x = conv_fast<K, MODE, false>(sm_raw0, p_pc, j0_pc, pcw, pcb, &near);
-            prod_conv_finish(sm_raw0, sm + kOffX, near, x);
+            prod_conv_finish(sm_raw0, sm + kOffX, sm + kOffFl, near, x);
         }
         __syncthreads();
         // chunk c: load chunk c+1's tiles (into stage (c+1)&1, free since chunk c-1 was
-        // contracted) and chunk c+2's raw rows (into raw slot c&1, free since chunk c was
-        // convolved), (state-only pass) convolve the second half of chunk c+1, compute its
-        // scalars and M tiles from the registers loaded during the previous chunk; then, once
-        // this chunk's transfers have landed, load chunk c+2's registers, which only the next
-        // chunk's M tiles wait for.  Unrolled by two so the raw slots are compile-time arrays.
-        // The body has no branches between the loads and the LDS work (the compiler then
-        // keeps track of which LDS array an outstanding transfer writes): past the last
-        // chunk the indices are clamped, so the loads repeat the last chunk into slots
-        // nobody reads and the conv writes an X slot nobody reads.
-        for (int64_t cn = 0; cn < nCl; cn += 2) {
+        // contracted) and chunk c+2's raw rows (into raw slot (c+2)%3, free since chunk c-1's
+        // flagged outputs were redone), (state-only pass) convolve the second half of chunk
+        // c+1, compute its scalars and M tiles from the registers loaded during the previous
+        // chunk; then, once this chunk's transfers have landed, load chunk c+2's registers,
+        // which only the next chunk's M tiles wait for.  Unrolled by three so the raw slots
+        // are compile-time arrays.  The body has no branches between the loads and the LDS
+        // work (the compiler then keeps track of which LDS array an outstanding transfer
+        // writes): past the last chunk the indices are clamped, so the loads repeat the last
+        // chunk into slots nobody reads and the conv writes an X slot nobody reads.
+        for (int64_t cn = 0; cn < nCl; cn += 3) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int64_t c = cn + half;
+            for (int third = 0; third < 3; ++third) {
+                const int64_t c = cn + third;
                 if (c >= nCl) break;
                 const int64_t k = c + 1;
                 const int64_t kt = k < nCl ? k : nCl - 1;          // tiles of chunk c+1
                 const int64_t kr = k + 1 < nCl ? k + 1 : nCl - 1;  // raw rows, registers of c+2
                 uint8_t* stk = sm + (k & 1) * kStageBytes;
-                uint8_t* raw_ld = half == 0 ? sm_raw0 : sm_raw1;  // slot c & 1
+                uint8_t* raw_ld = third == 0 ? sm_raw2 : third == 1 ? sm_raw0 : sm_raw1;  // slot (c+2)%3
                 fetch_tiles<PASS>(bk, o, c0 + kt, pw, sm_cb + (k & 1) * kCbBytes);
                 fetch_raw<K, HAS_SEQ>(bk, o, c0 + kr, kr >= 1, pw, lane, raw_ld, &seq_row);
                 asm volatile("" ::: "memory");
                 // (state-only pass) the unbranched part of the conv of chunk k's second half
-                // before the wait; its rare fix-ups after it
-                const uint8_t* raw_cv = half == 0 ? sm_raw1 : sm_raw0;  // slot k & 1
+                // before the wait, the rest after it
+                const uint8_t* raw_cv = third == 0 ? sm_raw1 : third == 1 ? sm_raw2 : sm_raw0;  // slot k%3
                 uint32_t near = 0;
                 bf16x8 xpc{};
                 if (kProdConv) xpc = conv_fast<K, MODE, false>(raw_cv, p_pc, j0_pc, pcw, pcb, &near);
                 scalars_and_m<HAS_SEQ, PASS>(f, c0 + kt, bk.L, Ah2, pw, lane, stk, ps);
                 __builtin_amdgcn_s_waitcnt(kWaitVm0);
                 fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + kr, pw, lane, f);
-                if (kProdConv) prod_conv_finish(raw_cv, sm + kOffX + (k & 1) * kXBytes, near, xpc);
+                if (kProdConv)
+                    prod_conv_finish(raw_cv, sm + kOffX + (k & 1) * kXBytes, sm + kOffFl + (k & 1) * kFlBytes, near, xpc);
                 if (HAS_SEQ && k + 1 < nCl && ptid < kRows)
                     reinterpret_cast<int32_t*>(raw_ld + kRwSeq)[ptid] = seq_row;
                 __syncthreads();
@@ -1040,33 +1097,48 @@ ssd_main_kernel(ChunkedArgs a) {
         const int xoff = (cv * 64 + lane) * 32;
         double cw[K], cbias;
         conv_weights<K, MODE>(a, h, p_conv, cw, cbias);
-        auto conv_chunk = [&](const uint8_t* raw, uint8_t* xs) {
-            // both runs' fast paths first (independent chains, no sequence masks), then the
-            // rare fix-ups; with seq_idx, a run whose taps straddle a sequence boundary is
-            // redone with the masks
+        if (MODE == 2 && g4 == 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) lds_st(sm + kOffW, p_conv * kWStride + 8 * k, cw[k]);
+            lds_st(sm + kOffW, p_conv * kWStride + 8 * K, cbias);
+        }
+        // the flagged outputs go to the consumer lane that reads them (conv_fixups there), so
+        // the rare double-precision recomputations stay off this role, which sets the pace
+        auto conv_chunk = [&](const uint8_t* raw, uint8_t* xs, uint8_t* fl) {
+            // both runs' fast paths (independent chains, no sequence masks); with seq_idx, a
+            // run whose taps straddle a sequence boundary is redone with the masks (exactly
+            // rounded, so its flags are cleared)
             uint32_t nr[kRuns];
             bf16x8 xr[kRuns];
 #pragma unroll
-            for (int r = 0; r < kRuns; ++r)
-                xr[r] = conv_fast<K, MODE, false>(raw, p_conv, j0_conv + 32 * r, cw, cbias, &nr[r]);
-#pragma unroll
             for (int r = 0; r < kRuns; ++r) {
-                xr[r] = conv_fixups<K, MODE, false>(raw, p_conv, j0_conv + 32 * r, cw, cbias, nr[r], xr[r]);
-                lds_st(xs, xoff + 16 * r, xr[r]);
+                nr[r] = 0;
+                xr[r] = conv_fast<K, MODE, false>(raw, p_conv, j0_conv + 32 * r, cw, cbias, &nr[r]);
             }
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r) lds_st(xs, xoff + 16 * r, xr[r]);
             if (HAS_SEQ && MODE != 0) {
 #pragma unroll
                 for (int r = 0; r < kRuns; ++r)
-                    if (!window_one_id<K>(raw, j0_conv + 32 * r))
+                    if (!window_one_id<K>(raw, j0_conv + 32 * r)) {
                         conv_masked_run<K, MODE>(raw, p_conv, j0_conv + 32 * r, cw, cbias, xs, xoff + 16 * r);
+                        nr[r] = 0;
+                    }
             }
+            if (kRuns == 2)
+                lds_st(fl, (cv * 64 + lane) * 4, nr[0] | (nr[kRuns - 1] << 16));
+            else
+                lds_st(fl, (cv * 64 + lane) * 4, static_cast<uint16_t>(nr[0]));
         };
         __syncthreads();  // raw rows of chunk 0 staged
-        conv_chunk(sm_raw0, sm + kOffX);
+        conv_chunk(sm_raw0, sm + kOffX, sm + kOffFl);
         __syncthreads();
+        int slot = 1;  // raw slot of chunk cn + 1
         for (int64_t cn = 0; cn < nCl; ++cn) {
             if (cn + 1 < nCl)
-                conv_chunk((cn & 1) ? sm_raw0 : sm_raw1, sm + kOffX + ((cn + 1) & 1) * kXBytes);
+                conv_chunk(slot == 0 ? sm_raw0 : slot == 1 ? sm_raw1 : sm_raw2,
+                           sm + kOffX + ((cn + 1) & 1) * kXBytes, sm + kOffFl + ((cn + 1) & 1) * kFlBytes);
+            slot = slot == 2 ? 0 : slot + 1;
             __syncthreads();
         }
     }
