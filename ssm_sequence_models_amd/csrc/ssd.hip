@@ -830,15 +830,17 @@ ssd_main_kernel(ChunkedArgs a) {
             // operands before its MFMAs, and consecutive MFMAs use different accumulators
             // (all hi products, then all lo products), so neither LDS latency nor the MFMA
             // result latency sits between two issues.
-            f32x4 yo[4], yi[4];
+            // one accumulator per row block: Y_off, then scaled by E_i, then the intra-chunk
+            // products on top
+            f32x4 ya[4];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                yo[I] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                yi[I] = yo[I];
-            }
+            for (int I = 0; I < 4; ++I) ya[I] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const float decay = lds_ld<float>(st, kStDecay);
             if constexpr (PASS == 0) {
             // initial-state part first (it does not need X), one 32-wide slice m of the state
-            // at a time; the next slice's C tiles load while this slice's MFMAs run
+            // at a time; the next slice's C tiles load while this slice's MFMAs run.  The
+            // decayed state goes to new registers first, so the split may overwrite the old
+            // values in place (no copies for the lo parts).
             bf16x8 cb[2][4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) cb[0][I] = lds_ld<bf16x8>(cbt, kCbC + sw_c(16 * I + li, g4));
@@ -855,12 +857,18 @@ ssd_main_kernel(ChunkedArgs a) {
                     hv[e] = acc[2 * m][e];
                     hv[4 + e] = acc[2 * m + 1][e];
                 }
+                acc[2 * m] *= decay;
+                acc[2 * m + 1] *= decay;
+                // the split after the decay products (an empty statement that reads them):
+                // then it is the old values' last use and may overwrite them in place
+#pragma unroll
+                for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(hv[e]) : "v"(acc[2 * m + (e >> 2)][e & 3]));
                 bf16x8 hhi, hlo;
                 split_hilo(hv, hhi, hlo);
 #pragma unroll
-                for (int I = 0; I < 4; ++I) yo[I] = mfma(hhi, cb[m & 1][I], yo[I]);
+                for (int I = 0; I < 4; ++I) ya[I] = mfma(hhi, cb[m & 1][I], ya[I]);
 #pragma unroll
-                for (int I = 0; I < 4; ++I) yo[I] = mfma(hlo, cb[m & 1][I], yo[I]);
+                for (int I = 0; I < 4; ++I) ya[I] = mfma(hlo, cb[m & 1][I], ya[I]);
             }
             }
             if constexpr (MODE == 2) {
@@ -890,7 +898,8 @@ ssd_main_kernel(ChunkedArgs a) {
             rslot = rslot == 2 ? 0 : rslot + 1;
             if constexpr (PASS == 0) {
             // intra-chunk part: M tiles (I, s) with 32 s <= 16 I + 15; the hi tiles, then the
-            // lo tiles in the same registers (keeps the wave's peak register count down)
+            // lo tiles in the same registers (keeps the wave's peak register count down).  The
+            // M tiles load while Y_off is scaled by E_i (row i = 16 I + li of the lane).
             bf16x8 mt[6];
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
@@ -898,9 +907,11 @@ ssd_main_kernel(ChunkedArgs a) {
                 mt[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
             }
 #pragma unroll
+            for (int I = 0; I < 4; ++I) ya[I] *= lds_ld<float>(st, kStE + (16 * I + li) * 4);
+#pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                yi[I] = mfma(xv[sh], mt[u], yi[I]);
+                ya[I] = mfma(xv[sh], mt[u], ya[I]);
             }
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
@@ -910,13 +921,15 @@ ssd_main_kernel(ChunkedArgs a) {
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                yi[I] = mfma(xv[sh], mt[u], yi[I]);
+                ya[I] = mfma(xv[sh], mt[u], ya[I]);
             }
             }
-            // state update: h^T[n][p] = decay h^T + B^T (W o X)
-            const float decay = lds_ld<float>(st, kStDecay);
+            // state update: h^T[n][p] = decay h^T + B^T (W o X) (the decay is applied above
+            // in the full pass)
+            if constexpr (PASS == 1) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) acc[t] *= decay;
+                for (int t = 0; t < 8; ++t) acc[t] *= decay;
+            }
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) {
                 float wj[8];
@@ -946,17 +959,14 @@ ssd_main_kernel(ChunkedArgs a) {
                 // y of this chunk straight to memory: a lane stores 4 channels of token
                 // 16 I + li (8 bytes), the four waves fill each 128-byte token row; rows past
                 // the end of the row are dropped by the range check
-                float eI[4];
-#pragma unroll
-                for (int I = 0; I < 4; ++I) eI[I] = lds_ld<float>(st, kStE + (16 * I + li) * 4);
                 const int t0 = static_cast<int>(c0 + cn) * kQ;
                 const Rsrc ry = make_rsrc(bk.y + static_cast<int64_t>(t0) * bk.H * kP,
                                           static_cast<int64_t>(bk.L - t0) * bk.H * kP * 2);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     u32x2 pk;
-                    pk[0] = pack_bf16x2(eI[I] * yo[I][0] + yi[I][0], eI[I] * yo[I][1] + yi[I][1]);
-                    pk[1] = pack_bf16x2(eI[I] * yo[I][2] + yi[I][2], eI[I] * yo[I][3] + yi[I][3]);
+                    pk[0] = pack_bf16x2(ya[I][0], ya[I][1]);
+                    pk[1] = pack_bf16x2(ya[I][2], ya[I][3]);
                     __builtin_amdgcn_raw_buffer_store_b64(pk, ry, y_off + 16 * I * y_tok, 0, 0);
                 }
             } else {
