@@ -142,6 +142,40 @@ def test_conv_scan_fwd_boundaries_at_run_and_chunk_edges(K):
     assert_bitexact(cfin, torch.from_numpy(rc).to(BF16), "conv final state")
 
 
+@pytest.mark.parametrize("B,L,H,segs", [(2, 1000, 4, 0), (1, 3072, 2, 0), (2, 700, 3, 3)])
+def test_conv_scan_fwd_passes_the_conv_output_through_exactly(B, L, H, segs):
+    """The fused kernel's conv output X, observed bit for bit through a scan that passes it
+    through: B_t = C_t = the same one-hot vector (inputs 1.28125 -> SiLU rounds to 1.0, other
+    inputs 0 -> 0, conv weights (0, .., 0, 1), no bias), dt = 1 and A = -1e4, so every decay
+    underflows to 0 and y_t = (C_t . B_t) dt_t X_t = X_t exactly.  The x channels are random,
+    so the fast path flags some outputs near a bf16 rounding midpoint and the consumers redo
+    them; y must equal the oracle's correctly rounded conv1d output everywhere (the parity
+    tolerance on y elsewhere would hide a one-ulp slip in X)."""
+    import ssm_sequence_models_amd as ssm
+    P, N, G, K = 64, 128, 1, 4
+    xBC, w, b, dt, A, cinit, sinit, seq = _fused_inputs(B, L, H, P, N, G, K, BF16, seed=L + H,
+                                                        segs=segs)
+    hot = 37
+    xs = H * P
+    xBC[:, :, xs:] = 0
+    xBC[:, :, xs + hot] = 1.28125           # B channel `hot`
+    xBC[:, :, xs + G * N + hot] = 1.28125   # C channel `hot`
+    w[xs:] = 0
+    w[xs:, K - 1] = 1
+    b[xs:] = 0
+    cinit[:, xs:] = 0
+    dt = torch.ones(B, L, H)
+    A = torch.full((H,), -1.0e4)
+    y, _, _ = ssm.conv_scan_fwd(dev(xBC), dev(w), dev(b), dev(dt), dev(A), H, P, G, N,
+                                conv_initial_state=dev(cinit), initial_state=dev(sinit),
+                                seq_idx=dev(seq))
+    torch.cuda.synchronize()
+    conv, _ = oracle.conv1d_fwd(xBC, w, b, cinit, seq, act="silu", out_dtype="bf16")
+    assert np.all(conv[:, :, xs + hot] == 1.0) and np.all(conv[:, :, xs + G * N + hot] == 1.0)
+    X = torch.from_numpy(conv[:, :, :xs].reshape(B, L, H, P)).to(BF16)
+    assert_bitexact(y, X, "y = the fused conv output")
+
+
 def test_conv_scan_fwd_inplace_states_and_len0():
     import ssm_sequence_models_amd as ssm
     H, P, N, G, K = 2, 64, 128, 1, 4
