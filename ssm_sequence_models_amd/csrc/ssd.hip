@@ -72,8 +72,7 @@ __device__ __forceinline__ void lds_st(uint8_t* base, int off, const T& v) {
     *reinterpret_cast<T*>(base + off) = v;
 }
 
-// v = hi + lo, hi = rne(v), lo = rne(v - hi): one paired conversion for two his, their
-// widening by shift / mask, two exact subtractions and one paired conversion for the los
+// v = hi + lo, hi = rne(v), lo = rne(v - hi): one paired conversion for two his, then
 // lo = v - hi in one instruction per value: the bf16 dot product of the hi pair with (-1, 0)
 // or (0, -1), accumulated onto v (the difference is exact in fp32, so the dot product's
 // rounding does not enter; checked bit for bit against the subtraction on the GPU).  The two
