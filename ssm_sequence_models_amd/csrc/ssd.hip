@@ -313,8 +313,8 @@ constexpr int kFlBytes = 4 * 64 * 4;
 constexpr int kOffPs = 2 * kStageBytes;
 constexpr int kOffX = kOffPs + 4 * kPsBytes;
 constexpr int kOffFl = kOffX + 2 * kXBytes;
-//   conv weights and bias of the head's x channels in double (SiLU conv only), for the
-//   consumers' recomputations: channel p at kOffW + p * kWStride
+//   conv weights and bias of the head's x channels in double (with a conv), for the out-of-line
+//   recomputations (flagged outputs, masked runs): channel p at kOffW + p * kWStride
 constexpr int kWStride = (kKmax + 1) * 8;
 constexpr int kOffW = kOffFl + 2 * kFlBytes;
 constexpr int kMainLds = kOffW + kP * kWStride;
@@ -699,11 +699,15 @@ __device__ __forceinline__ bool window_one_id(const uint8_t* raw, int j0) {
 
 // The conv of channel p over tokens j0 .. j0+7 with the sequence masks, one output at a
 // time, each written over the fast path's value at xs + off + 2e (the rare runs whose taps
-// straddle a sequence boundary)
+// straddle a sequence boundary).  Out of line, with the weights from the LDS table: weights
+// passed in as an array would go through the stack, a round trip to memory per call.
 template <int K, int MODE>
-__device__ __noinline__ void conv_masked_run(const uint8_t* raw, int p, int j0,
-                                             const double (&cw)[K], double cbias, uint8_t* xs,
-                                             int off) {
+__device__ __noinline__ void conv_masked_run(const uint8_t* raw, const uint8_t* wt, int p, int j0,
+                                             uint8_t* xs, int off) {
+    double cw[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) cw[k] = lds_ld<double>(wt, p * kWStride + 8 * k);
+    const double cbias = lds_ld<double>(wt, p * kWStride + 8 * K);
     for (int e = 0; e < 8; ++e) {
         const double z = conv_z<K, MODE, true>(raw, p >> 3, (p & 7) * 2, j0 + e, cw, cbias);
         const uint16_t v = MODE == 2 ? act_to_bf16(z, SSM_ACT_SILU) : f64_to_bf16(z);
@@ -1029,10 +1033,11 @@ ssd_main_kernel(ChunkedArgs a) {
         const int xoff_pc = (pw * 64 + lane) * 32 + 16;
         double pcw[K], pcb = 0.0;
         if (kProdConv) conv_weights<K, MODE>(a, h, p_pc, pcw, pcb);
-        auto prod_conv_finish = [&](const uint8_t* raw, uint8_t* xs, uint8_t* fl, uint32_t near, bf16x8 x) {
+        auto prod_conv_finish = [&](const uint8_t* raw, uint8_t* xs, uint8_t* fl, uint32_t near, bf16x8 x,
+                                    bool clean) {
             lds_st(xs, xoff_pc, x);
-            if (HAS_SEQ && MODE != 0 && !window_one_id<K>(raw, j0_pc)) {
-                conv_masked_run<K, MODE>(raw, p_pc, j0_pc, pcw, pcb, xs, xoff_pc);
+            if (HAS_SEQ && MODE != 0 && !clean) {
+                conv_masked_run<K, MODE>(raw, sm + kOffW, p_pc, j0_pc, xs, xoff_pc);
                 near = 0;
             }
             lds_st(fl, (pw * 64 + lane) * 4 + 2, static_cast<uint16_t>(near));
@@ -1052,8 +1057,9 @@ ssd_main_kernel(ChunkedArgs a) {
         fetch_regs<HAS_SEQ, PASS>(bk, o, nCl > 1 ? c0 + 1 : c0, pw, lane, f);
         if (kProdConv) {
             uint32_t near = 0;
+            const bool clean = !(HAS_SEQ && MODE != 0) || window_one_id<K>(sm_raw0, j0_pc);
             const bf16x8 x = conv_fast<K, MODE, false>(sm_raw0, p_pc, j0_pc, pcw, pcb, &near);
-            prod_conv_finish(sm_raw0, sm + kOffX, sm + kOffFl, near, x);
+            prod_conv_finish(sm_raw0, sm + kOffX, sm + kOffFl, near, x, clean);
         }
         __syncthreads();
         // chunk c: load chunk c+1's tiles (into stage (c+1)&1, free since chunk c-1 was
@@ -1084,12 +1090,17 @@ ssd_main_kernel(ChunkedArgs a) {
                 const uint8_t* raw_cv = third == 0 ? sm_raw1 : third == 1 ? sm_raw2 : sm_raw0;  // slot k%3
                 uint32_t near = 0;
                 bf16x8 xpc{};
-                if (kProdConv) xpc = conv_fast<K, MODE, false>(raw_cv, p_pc, j0_pc, pcw, pcb, &near);
+                bool pclean = true;
+                if (kProdConv) {
+                    pclean = !(HAS_SEQ && MODE != 0) || window_one_id<K>(raw_cv, j0_pc);
+                    xpc = conv_fast<K, MODE, false>(raw_cv, p_pc, j0_pc, pcw, pcb, &near);
+                }
                 scalars_and_m<HAS_SEQ, PASS>(f, c0 + kt, bk.L, Ah2, pw, lane, stk, ps);
                 __builtin_amdgcn_s_waitcnt(kWaitVm0);
                 fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + kr, pw, lane, f);
                 if (kProdConv)
-                    prod_conv_finish(raw_cv, sm + kOffX + (k & 1) * kXBytes, sm + kOffFl + (k & 1) * kFlBytes, near, xpc);
+                    prod_conv_finish(raw_cv, sm + kOffX + (k & 1) * kXBytes, sm + kOffFl + (k & 1) * kFlBytes, near, xpc,
+                                     pclean);
                 if (HAS_SEQ && k + 1 < nCl && ptid < kRows)
                     reinterpret_cast<int32_t*>(raw_ld + kRwSeq)[ptid] = seq_row;
                 __syncthreads();
@@ -1106,7 +1117,7 @@ ssd_main_kernel(ChunkedArgs a) {
         const int xoff = (cv * 64 + lane) * 32;
         double cw[K], cbias;
         conv_weights<K, MODE>(a, h, p_conv, cw, cbias);
-        if (MODE == 2 && g4 == 0) {
+        if (MODE != 0 && g4 == 0) {
 #pragma unroll
             for (int k = 0; k < K; ++k) lds_st(sm + kOffW, p_conv * kWStride + 8 * k, cw[k]);
             lds_st(sm + kOffW, p_conv * kWStride + 8 * K, cbias);
@@ -1117,6 +1128,11 @@ ssd_main_kernel(ChunkedArgs a) {
             // both runs' fast paths (independent chains, no sequence masks); with seq_idx, a
             // run whose taps straddle a sequence boundary is redone with the masks (exactly
             // rounded, so its flags are cleared)
+            // the window checks first: their id reads then overlap the fast path
+            bool clean[kRuns];
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r)
+                clean[r] = !(HAS_SEQ && MODE != 0) || window_one_id<K>(raw, j0_conv + 32 * r);
             uint32_t nr[kRuns];
             bf16x8 xr[kRuns];
 #pragma unroll
@@ -1129,8 +1145,8 @@ ssd_main_kernel(ChunkedArgs a) {
             if (HAS_SEQ && MODE != 0) {
 #pragma unroll
                 for (int r = 0; r < kRuns; ++r)
-                    if (!window_one_id<K>(raw, j0_conv + 32 * r)) {
-                        conv_masked_run<K, MODE>(raw, p_conv, j0_conv + 32 * r, cw, cbias, xs, xoff + 16 * r);
+                    if (!clean[r]) {
+                        conv_masked_run<K, MODE>(raw, sm + kOffW, p_conv, j0_conv + 32 * r, xs, xoff + 16 * r);
                         nr[r] = 0;
                     }
             }
