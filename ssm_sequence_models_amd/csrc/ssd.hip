@@ -301,7 +301,8 @@ constexpr int kRowsMax = kQ + kKmax - 1;         // raw x rows of a chunk incl. 
 constexpr int kRwX = 0;                          // raw x [rows][8 pieces], piece ^ xr_swz(row)
 constexpr int kRwSeq = (kRowsMax + 1) * 128;     // seq ids of the raw rows (after 72 row slots:
                                                  // the loads fill 9 blocks of 8 rows)
-constexpr int kRawBytes = kRwSeq + 72 * 4;
+constexpr int kRwClean = kRwSeq + 72 * 4;        // bit r: run r's taps carry one id (see clean_runs)
+constexpr int kRawBytes = kRwClean + 16;
 //   producer-private scalars: cum, dtv, r of the chunk
 constexpr int kPsBytes = 4 * kQ * 4;  // per producer wave: cum2, dt, last reset, R
 //   X slot (two, by chunk parity): the conv waves' bf16 outputs (X operands), 16 bytes per
@@ -432,6 +433,30 @@ __device__ __forceinline__ void fetch_regs(const Blk& bk, const POff& o, int64_t
     }
 }
 
+// With seq_idx: bit r set when raw rows 8r .. 8r+K+6 (the taps of run r, tokens 8r .. 8r+7)
+// carry one sequence id.  Computed once per chunk by producer wave 0 from the ids of rows
+// 0 .. 63 (id_lo, row = lane) and 64 .. K+62 (id_hi, row = 64 + lane): a boundary bit per row
+// where the id differs from the row before, then one window test per run on the wave-uniform
+// masks.  The conv lanes read the word instead of comparing their windows' ids themselves.
+template <int K>
+__device__ __forceinline__ uint32_t clean_runs(int32_t id_lo, int32_t id_hi, int lane) {
+    constexpr int kRows = kQ + K - 1;
+    const int32_t prev_lo = __shfl_up(id_lo, 1);
+    const uint64_t b_lo = __ballot(lane >= 1 && id_lo != prev_lo);      // bit rho: rows rho-1, rho
+    const int32_t last = __builtin_amdgcn_readlane(id_lo, kQ - 1);
+    int32_t prev_hi = __shfl_up(id_hi, 1);
+    if (lane == 0) prev_hi = last;
+    const uint64_t b_hi = __ballot(lane < kRows - kQ && id_hi != prev_hi);  // bit l: row 64 + l
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < kQ / 8; ++r) {
+        const int j0 = 8 * r;  // boundaries that matter: rows j0+1 .. j0+K+6
+        const uint64_t w = (b_lo >> (j0 + 1)) | (b_hi << (kQ - 1 - j0));
+        if ((w & ((1ull << (K + 6)) - 1)) == 0) m |= 1u << r;
+    }
+    return m;
+}
+
 // Raw x rows of chunk k >= 1 (first row t0 - (K-1) >= 0) into raw slot `raw`; rows past the
 // end arrive as zeros, and all of them when `live` is false.  Every wave loads LDS blocks pw
 // and pw + 4 (rows 0-63) and block 8 (rows 64-71, the same data from every wave), with no
@@ -439,7 +464,8 @@ __device__ __forceinline__ void fetch_regs(const Blk& bk, const POff& o, int64_t
 // landed.
 template <int K, bool HAS_SEQ>
 __device__ __forceinline__ void fetch_raw(const Blk& bk, const POff& o, int64_t k, bool live,
-                                          int pw, int lane, uint8_t* raw, int32_t* seq_row) {
+                                          int pw, int lane, uint8_t* raw, int32_t* seq_row,
+                                          int32_t* seq_hi) {
     constexpr int kRows = kQ + K - 1;
     const int r0 = live ? static_cast<int>(k) * kQ - (K - 1) : 0;
     const Rsrc rx = make_rsrc(bk.x + static_cast<int64_t>(r0) * bk.x_row,
@@ -449,10 +475,10 @@ __device__ __forceinline__ void fetch_raw(const Blk& bk, const POff& o, int64_t 
     dma16(rx, o.x[2], raw + kRwX + 8 * 1024);
     if (HAS_SEQ) {
         const int ptid = pw * 64 + lane;
-        if (ptid < kRows) {
-            const Rsrc rs = make_rsrc(bk.seq + r0, live ? static_cast<int64_t>(bk.L - r0) * 4 : 0);
-            *seq_row = static_cast<int32_t>(bload32(rs, ptid * 4));
-        }
+        const Rsrc rs = make_rsrc(bk.seq + r0, live ? static_cast<int64_t>(bk.L - r0) * 4 : 0);
+        if (ptid < kRows) *seq_row = static_cast<int32_t>(bload32(rs, ptid * 4));
+        // wave 0 also takes rows 64 .. (the clean-run mask); the same values as wave 1's
+        if (pw == 0 && kQ + lane < kRows) *seq_hi = static_cast<int32_t>(bload32(rs, (kQ + lane) * 4));
     }
 }
 
@@ -486,10 +512,17 @@ __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk&
             lds_st(raw, kRwX + sw_xr(rho, q), v);
         }
     }
-    if (HAS_SEQ && ptid < kRows) {
-        int tr = t0 + ptid - (K - 1);
-        tr = tr < 0 ? 0 : (tr >= bk.L ? bk.L - 1 : tr);
-        reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = bk.seq[tr];
+    if (HAS_SEQ) {
+        auto id_of = [&](int rho) {
+            int tr = t0 + rho - (K - 1);
+            tr = tr < 0 ? 0 : (tr >= bk.L ? bk.L - 1 : tr);
+            return bk.seq[tr];
+        };
+        if (ptid < kRows) reinterpret_cast<int32_t*>(raw + kRwSeq)[ptid] = id_of(ptid);
+        if (pw == 0) {
+            const uint32_t m = clean_runs<K>(id_of(lane), kQ + lane < kRows ? id_of(kQ + lane) : 0, lane);
+            if (lane == 0) *reinterpret_cast<uint32_t*>(raw + kRwClean) = m;
+        }
     }
 }
 
@@ -675,26 +708,6 @@ __device__ __noinline__ uint32_t silu_conv_exact(const uint8_t* raw, const uint8
     const double cbias = lds_ld<double>(wt, p * kWStride + 8 * K);
     const double z = conv_z<K, 2, false>(raw, p >> 3, (p & 7) * 2, r0, cw, cbias);
     return silu_f64_to_bf16(z);
-}
-
-// With seq_idx: true when raw rows j0 .. j0+K+6 (the taps of a run's 8 outputs) carry one
-// sequence id, so the run's conv needs no masking.  j0 is a multiple of 8, so the ids come in
-// 16-byte reads (the id array has room for rows up to j0 + 15 <= 71); the comparisons are
-// combined without branches.
-template <int K>
-__device__ __forceinline__ bool window_one_id(const uint8_t* raw, int j0) {
-    static_assert(8 + K - 1 <= 16, "window fits four 16-byte reads");
-    uint32_t id[16];
-#pragma unroll
-    for (int q = 0; q < (8 + K - 1 + 3) / 4; ++q) {
-        const u32x4 v = lds_ld<u32x4>(raw, kRwSeq + (j0 + 4 * q) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) id[4 * q + e] = v[e];
-    }
-    uint32_t diff = 0;
-#pragma unroll
-    for (int r = 1; r < 8 + K - 1; ++r) diff |= id[r] ^ id[0];
-    return diff == 0;
 }
 
 // The conv of channel p over tokens j0 .. j0+7 with the sequence masks, one output at a
@@ -1023,7 +1036,7 @@ ssd_main_kernel(ChunkedArgs a) {
         const int ptid = pw * 64 + lane;
         constexpr int kRows = kQ + K - 1;
         Fetch f;  // registers of the next chunk to produce
-        int32_t seq_row = 0;
+        int32_t seq_row = 0, seq_hi = 0;
         // In the state-only pass the producers have time to spare and the conv waves set the
         // pace: there the producers convolve the second half of each chunk (tokens 32 .. 63)
         // for channel 16 pw + li, into the X slot lane that consumer wave pw reads, and its
@@ -1047,17 +1060,22 @@ ssd_main_kernel(ChunkedArgs a) {
         // c0 + c (LDS slots go by the local index, memory by the global one).
         fetch_tiles<PASS>(bk, o, c0, pw, sm_cb);
         fetch_regs<HAS_SEQ, PASS>(bk, o, c0, pw, lane, f);
-        fetch_raw<K, HAS_SEQ>(bk, o, c0 + 1, nCl > 1, pw, lane, sm_raw1, &seq_row);
+        fetch_raw<K, HAS_SEQ>(bk, o, c0 + 1, nCl > 1, pw, lane, sm_raw1, &seq_row, &seq_hi);
         stage_raw_first<K, MODE != 0, HAS_SEQ>(a, bk, b, h, static_cast<int>(c0 * kQ), pw, lane, sm_raw0);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        if (HAS_SEQ && nCl > 1 && ptid < kRows)
-            reinterpret_cast<int32_t*>(sm_raw1 + kRwSeq)[ptid] = seq_row;
+        if (HAS_SEQ && nCl > 1) {
+            if (ptid < kRows) reinterpret_cast<int32_t*>(sm_raw1 + kRwSeq)[ptid] = seq_row;
+            if (pw == 0) {
+                const uint32_t m = clean_runs<K>(seq_row, seq_hi, lane);
+                if (lane == 0) *reinterpret_cast<uint32_t*>(sm_raw1 + kRwClean) = m;
+            }
+        }
         __syncthreads();  // raw rows of chunk 0 staged
         scalars_and_m<HAS_SEQ, PASS>(f, c0, bk.L, Ah2, pw, lane, sm, ps);
         fetch_regs<HAS_SEQ, PASS>(bk, o, nCl > 1 ? c0 + 1 : c0, pw, lane, f);
         if (kProdConv) {
             uint32_t near = 0;
-            const bool clean = !(HAS_SEQ && MODE != 0) || window_one_id<K>(sm_raw0, j0_pc);
+            const bool clean = !(HAS_SEQ && MODE != 0) || ((lds_ld<uint32_t>(sm_raw0, kRwClean) >> (j0_pc / 8)) & 1u);
             const bf16x8 x = conv_fast<K, MODE, false>(sm_raw0, p_pc, j0_pc, pcw, pcb, &near);
             prod_conv_finish(sm_raw0, sm + kOffX, sm + kOffFl, near, x, clean);
         }
@@ -1083,7 +1101,7 @@ ssd_main_kernel(ChunkedArgs a) {
                 uint8_t* stk = sm + (k & 1) * kStageBytes;
                 uint8_t* raw_ld = third == 0 ? sm_raw2 : third == 1 ? sm_raw0 : sm_raw1;  // slot (c+2)%3
                 fetch_tiles<PASS>(bk, o, c0 + kt, pw, sm_cb + (k & 1) * kCbBytes);
-                fetch_raw<K, HAS_SEQ>(bk, o, c0 + kr, kr >= 1, pw, lane, raw_ld, &seq_row);
+                fetch_raw<K, HAS_SEQ>(bk, o, c0 + kr, kr >= 1, pw, lane, raw_ld, &seq_row, &seq_hi);
                 asm volatile("" ::: "memory");
                 // (state-only pass) the unbranched part of the conv of chunk k's second half
                 // before the wait, the rest after it
@@ -1092,7 +1110,7 @@ ssd_main_kernel(ChunkedArgs a) {
                 bf16x8 xpc{};
                 bool pclean = true;
                 if (kProdConv) {
-                    pclean = !(HAS_SEQ && MODE != 0) || window_one_id<K>(raw_cv, j0_pc);
+                    pclean = !(HAS_SEQ && MODE != 0) || ((lds_ld<uint32_t>(raw_cv, kRwClean) >> (j0_pc / 8)) & 1u);
                     xpc = conv_fast<K, MODE, false>(raw_cv, p_pc, j0_pc, pcw, pcb, &near);
                 }
                 scalars_and_m<HAS_SEQ, PASS>(f, c0 + kt, bk.L, Ah2, pw, lane, stk, ps);
@@ -1101,8 +1119,13 @@ ssd_main_kernel(ChunkedArgs a) {
                 if (kProdConv)
                     prod_conv_finish(raw_cv, sm + kOffX + (k & 1) * kXBytes, sm + kOffFl + (k & 1) * kFlBytes, near, xpc,
                                      pclean);
-                if (HAS_SEQ && k + 1 < nCl && ptid < kRows)
-                    reinterpret_cast<int32_t*>(raw_ld + kRwSeq)[ptid] = seq_row;
+                if (HAS_SEQ && k + 1 < nCl) {
+                    if (ptid < kRows) reinterpret_cast<int32_t*>(raw_ld + kRwSeq)[ptid] = seq_row;
+                    if (pw == 0) {
+                        const uint32_t m = clean_runs<K>(seq_row, seq_hi, lane);
+                        if (lane == 0) *reinterpret_cast<uint32_t*>(raw_ld + kRwClean) = m;
+                    }
+                }
                 __syncthreads();
             }
         }
@@ -1128,11 +1151,11 @@ ssd_main_kernel(ChunkedArgs a) {
             // both runs' fast paths (independent chains, no sequence masks); with seq_idx, a
             // run whose taps straddle a sequence boundary is redone with the masks (exactly
             // rounded, so its flags are cleared)
-            // the window checks first: their id reads then overlap the fast path
+            // which runs' taps carry one sequence id (a word the producers computed)
             bool clean[kRuns];
+            const uint32_t cm = (HAS_SEQ && MODE != 0) ? lds_ld<uint32_t>(raw, kRwClean) : 0xFFu;
 #pragma unroll
-            for (int r = 0; r < kRuns; ++r)
-                clean[r] = !(HAS_SEQ && MODE != 0) || window_one_id<K>(raw, j0_conv + 32 * r);
+            for (int r = 0; r < kRuns; ++r) clean[r] = (cm >> ((j0_conv + 32 * r) / 8)) & 1u;
             uint32_t nr[kRuns];
             bf16x8 xr[kRuns];
 #pragma unroll
