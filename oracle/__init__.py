@@ -17,7 +17,11 @@ Definitions followed (page title and section):
   * scan_fwd, step  length-generalization reading notes, Sec. 2.1 Eq. (1) and Sec. 2.5
                     Eq. (4), with the initial state in and the final state out (Sec. 2.6);
   * conv_scan_fwd   conv1d_fwd (phi applied, output rounded to the input dtype) followed by
-                    the split into x | B | C channels and scan_fwd.
+                    the split into x | B | C channels and scan_fwd;
+  * conv1d_bwd      causal-conv1d tutorial ch. 7, "backward with states, a unified derivation"
+                    (du over the extended sequence, dS, dx, dw, dbeta) and "chunked training";
+  * scan_bwd_h0     the gradient of the initial state through Eq. (4) of the reading notes
+                    (Sec. 2.5), with the final state's gradient added (Sec. 2.6).
 """
 from __future__ import annotations
 
@@ -67,7 +71,13 @@ def load_library(path: str):
                                  _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.orc_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _i64, _i64, _i64, _i64,
                              _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
-    for f in ("orc_conv1d_fwd", "orc_conv1d_update", "orc_scan_fwd", "orc_step"):
+    lib.orc_conv1d_bwd.argtypes = [_dp, _dp, _dp, _dp, _ip, _dp, _dp, _dp, _dp, _dp, _dp, _i64,
+                                   _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int]
+    lib.orc_scan_bwd_h0.argtypes = [_dp, _dp, _dp, _ip, _dp, _dp, _dp, _i64, _i64, _i64, _i64,
+                                    _i64, _i64, ctypes.c_int]
+    for f in ("orc_conv1d_fwd", "orc_conv1d_update", "orc_scan_fwd", "orc_step",
+              "orc_conv1d_bwd", "orc_scan_bwd_h0"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -177,6 +187,41 @@ def scan_fwd(x, dt, A, Bm, Cm, init_state=None, seq_idx=None, out_dtype="f64",
                      _p(seq_idx, _ip), _p(y), B, L, H, P, G, N, ROUND[out_dtype],
                      ROUND[state_dtype])
     return y, fin
+
+
+def conv1d_bwd(x, w, bias, init_state, seq_idx, dy, dfinal, act="none", dx_dtype="f64",
+               dstate_dtype="f64", dw_dtype="f64", lib=None):
+    """Backward of conv1d_fwd with state gradients.  x, dy [B, L, C]; w [C, K]; bias [C];
+    init_state, dfinal [B, C, K-1] (None = zero); seq_idx [B, L].
+
+    Returns (dx [B, L, C], dinit [B, C, K-1], dw [C, K], dbias [C])."""
+    lib = lib or _get()
+    x, w, bias, init_state, dy, dfinal = (_f64(v) for v in (x, w, bias, init_state, dy, dfinal))
+    seq_idx = _i32(seq_idx)
+    B, L, C = x.shape
+    K = w.shape[1]
+    dx = np.zeros((B, L, C))
+    dinit = np.zeros((B, C, K - 1))
+    dw = np.zeros((C, K))
+    dbias = np.zeros((C,))
+    lib.orc_conv1d_bwd(_p(x), _p(w), _p(bias), _p(init_state), _p(seq_idx, _ip), _p(dy),
+                       _p(dfinal), _p(dx), _p(dinit), _p(dw), _p(dbias), B, L, C, K, ACT[act],
+                       ROUND[dx_dtype], ROUND[dstate_dtype], ROUND[dw_dtype])
+    return dx, dinit, dw, dbias
+
+
+def scan_bwd_h0(dt, A, Cm, seq_idx, dy, dfinal, P, out_dtype="f64", lib=None):
+    """Gradient of the initial state: dt [B, L, H]; A [H]; Cm [B, L, G, N]; dy [B, L, H, P];
+    dfinal [B, H, P, N] (None = zero); seq_idx [B, L].  Returns dh0 [B, H, P, N]."""
+    lib = lib or _get()
+    dt, A, Cm, dy, dfinal = (_f64(v) for v in (dt, A, Cm, dy, dfinal))
+    seq_idx = _i32(seq_idx)
+    B, L, H = dt.shape
+    G, N = Cm.shape[2], Cm.shape[3]
+    dh0 = np.zeros((B, H, P, N))
+    lib.orc_scan_bwd_h0(_p(dt), _p(A), _p(Cm), _p(seq_idx, _ip), _p(dy), _p(dfinal), _p(dh0),
+                        B, L, H, P, G, N, ROUND[out_dtype])
+    return dh0
 
 
 def step(x, dt, A, Bm, Cm, pool, indices=None, out_dtype="f64", state_dtype="f64", lib=None):

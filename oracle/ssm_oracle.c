@@ -308,3 +308,140 @@ int orc_step(const double* x, const double* dt, const double* A, const double* B
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------
+ * Backward of the causal conv1d with state gradients ([CC] "backward with states, a unified
+ * derivation"; "chunked training and truncated back-propagation").
+ *
+ * The loss depends on the outputs out_t = phi(z_t) (gradient dy_t) and on the final state F
+ * (gradient q = dF).  With delta_t = dL/dz_t = dy_t * phi'(z_t) (the chain rule through phi;
+ * phi' = 1 for the identity, sigma(z)(1 + z(1 - sigma(z))) for SiLU):
+ *
+ *   du_j = sum_t sum_k delta_t w_k [j = t + k] + [L <= j < L+K-1] q_{j-L}
+ *   dS = du[0 : K-1],   dx = du[K-1 : K-1+L]
+ *   dw_k = sum_{b,t} delta_t u_{t+k},   dbeta = sum_{b,t} delta_t
+ *
+ * With seq_idx, tap k of output t enters exactly where it entered the forward (same token
+ * identity as output t); the direct path from F to the last K-1 inputs is unmasked, as F is.
+ * z is recomputed from x, S, w, beta.  dw and dbeta sum over the batch (rows share weights).
+ *
+ * Layouts: x, dy, dx [B][L][C]; w, dw [C][K]; bias, dbias [C]; init_state, dfinal, dinit
+ * [B][C][K-1]; seq_idx [B][L].  dfinal and init_state may be NULL (zero).
+ * ------------------------------------------------------------------------------------- */
+int orc_conv1d_bwd(const double* x, const double* w, const double* bias,
+                   const double* init_state, const int32_t* seq_idx, const double* dy,
+                   const double* dfinal, double* dx, double* dinit, double* dw, double* dbias,
+                   int64_t B, int64_t L, int64_t C, int64_t K, int act, int dx_round,
+                   int dstate_round, int dw_round) {
+    const int64_t U = K - 1 + L;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        const size_t nu = (size_t)(U > 0 ? U : 1);
+        double* ext = (double*)malloc(sizeof(double) * nu);    /* u, the extended sequence */
+        double* dext = (double*)malloc(sizeof(double) * nu);   /* dL/du */
+        double* dz = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));  /* delta */
+        int32_t* seg = (int32_t*)malloc(sizeof(int32_t) * nu); /* token identity of u_j */
+        double* dwc = (double*)calloc((size_t)K, sizeof(double));
+        double dbc = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int32_t* sq = seq_idx ? seq_idx + b * L : NULL;
+            for (int64_t j = 0; j < U; ++j) {
+                const int64_t tx = j - (K - 1); /* token of u_j; < 0 for the state */
+                ext[j] = tx < 0 ? (init_state ? init_state[(b * C + c) * (K - 1) + j] : 0.0)
+                                : x[(b * L + tx) * C + c];
+                seg[j] = sq ? sq[tx < 0 ? 0 : tx] : 0;
+                dext[j] = 0.0;
+            }
+            /* delta_t = dy_t phi'(z_t), z_t recomputed with the forward's taps */
+            for (int64_t t = 0; t < L; ++t) {
+                double zt = bias ? bias[c] : 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    if (!sq || seg[t + k] == seg[t + K - 1]) zt += w[c * K + k] * ext[t + k];
+                double dphi = 1.0;
+                if (act == ORC_ACT_SILU) {
+                    const double sg = 1.0 / (1.0 + exp(-zt));
+                    dphi = sg * (1.0 + zt * (1.0 - sg));
+                }
+                dz[t] = dy[(b * L + t) * C + c] * dphi;
+            }
+            /* the convolution term of du, the weight and bias sums, then the direct path
+             * from F to the last K-1 inputs */
+            for (int64_t t = 0; t < L; ++t) {
+                for (int64_t k = 0; k < K; ++k) {
+                    if (sq && seg[t + k] != seg[t + K - 1]) continue;
+                    dext[t + k] += dz[t] * w[c * K + k];
+                    dwc[k] += dz[t] * ext[t + k];
+                }
+                dbc += dz[t];
+            }
+            if (dfinal)
+                for (int64_t r = 0; r < K - 1; ++r) dext[L + r] += dfinal[(b * C + c) * (K - 1) + r];
+            if (dinit)
+                for (int64_t j = 0; j < K - 1; ++j)
+                    dinit[(b * C + c) * (K - 1) + j] = orc_round(dext[j], dstate_round);
+            for (int64_t t = 0; t < L; ++t)
+                dx[(b * L + t) * C + c] = orc_round(dext[K - 1 + t], dx_round);
+        }
+        if (dw)
+            for (int64_t k = 0; k < K; ++k) dw[c * K + k] = orc_round(dwc[k], dw_round);
+        if (dbias) dbias[c] = orc_round(dbc, dw_round);
+        free(ext);
+        free(dext);
+        free(dz);
+        free(seg);
+        free(dwc);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Gradient of the loss with respect to the scan's initial state ([LG] Sec. 2.5 Eq. (4), the
+ * unrolled form with a non-zero initial state; Sec. 2.6, the state handed between chunks).
+ *
+ * h_{-1} enters y_t only through C_t^T (prod_{tau=0..t} a_tau) h_{-1}, and the final state
+ * through (prod_{tau=0..L-1} a_tau) h_{-1}.  With dy (gradient of y) and dF (gradient of the
+ * final state), per head h and channel p:
+ *
+ *   dh_{-1}[p][n] = sum_t dy_t[p] (prod_{tau<=t} a_tau) C_t[n]  +  (prod_{tau<L} a_tau) dF[p][n]
+ *
+ * a_tau = exp(dt_tau A_h).  With seq_idx the state is zeroed where the id changes, so only
+ * tokens before the first change see h_{-1}, and dF reaches it only without any change.
+ * The products are taken in time order, as the definition reads.
+ *
+ * Layouts: dt [B][L][H]; Cm [B][L][G][N]; dy [B][L][H][P]; dfinal, dh0 [B][H][P][N];
+ * seq_idx [B][L].  dfinal may be NULL (zero).
+ * ------------------------------------------------------------------------------------- */
+int orc_scan_bwd_h0(const double* dt, const double* A, const double* Cm,
+                    const int32_t* seq_idx, const double* dy, const double* dfinal, double* dh0,
+                    int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                    int out_round) {
+    const int64_t heads_per_group = H / G;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t g = h / heads_per_group;
+            double* acc = (double*)calloc((size_t)(P * N), sizeof(double));
+            double prod = 1.0;
+            int alive = 1;
+            const int32_t* sq = seq_idx ? seq_idx + b * L : NULL;
+            for (int64_t t = 0; t < L && alive; ++t) {
+                if (sq && t > 0 && sq[t] != sq[t - 1]) {
+                    alive = 0;
+                    break;
+                }
+                prod *= exp(dt[(b * L + t) * H + h] * A[h]);
+                const double* Ct = Cm + ((b * L + t) * G + g) * N;
+                const double* dyt = dy + ((b * L + t) * H + h) * P;
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n) acc[p * N + n] += dyt[p] * prod * Ct[n];
+            }
+            for (int64_t e = 0; e < P * N; ++e) {
+                double v = acc[e];
+                if (alive && dfinal) v += prod * dfinal[(b * H + h) * P * N + e];
+                dh0[(b * H + h) * P * N + e] = orc_round(v, out_round);
+            }
+            free(acc);
+        }
+    }
+    return 0;
+}

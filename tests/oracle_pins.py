@@ -519,6 +519,129 @@ def check_round_bf16(lib):
     assert lib.orc_round(1.0 + 2.0 ** -30, 1) == 1.0
 
 
+# ------------------------------------------------------------------------------------------
+# backward with state gradients
+# ------------------------------------------------------------------------------------------
+
+def check_conv_bwd_single_token_k3(lib):
+    """causal-conv1d ch. 7, single-token chunk example (backward): dS = [w0 d, w1 d + q0],
+    dx = [w2 d + q1]; dw = d [a, b, c], dbeta = d (identity phi, so delta = dy)."""
+    g = _golden("conv_bwd_single_token_k3.json")
+    sym = g["symbols"]
+    S = np.array([[[sym["a"], sym["b"]]]])
+    x = np.array([[[sym["c"]]]])
+    w = np.array([g["w"]])
+    dy = np.array([[[g["delta"]]]])
+    q = np.array([[g["q"]]])
+    dx, dS, dw, db = oracle.conv1d_bwd(x, w, np.array([g["beta"]]), S, None, dy, q, lib=lib)
+    assert dS[0, 0].tolist() == g["dS"], dS
+    assert dx[0, :, 0].tolist() == g["dx"], dx
+    assert dw[0].tolist() == g["dw"], dw
+    assert db.tolist() == [g["dbeta"]], db
+
+
+def _conv_loss(x, w, b, S, seq, dy, q, act, lib):
+    out, fin = oracle.conv1d_fwd(x, w, b, S, seq, act=act, lib=lib)
+    return float((out * dy).sum() + (fin * q).sum())
+
+
+def check_conv_bwd_finite_differences(lib):
+    """Every gradient of the conv (dx, dS, dw, dbeta) against central differences of the
+    oracle's own forward on L = sum dy * out + sum q * F, with SiLU, packed sequences and an
+    initial state (the mathematics of the derivative, not the page's formula re-typed)."""
+    r = _rng(31)
+    B, L, C, K = 2, 9, 3, 4
+    x = r.normal(size=(B, L, C))
+    w = r.normal(size=(C, K))
+    b = r.normal(size=(C,))
+    S = r.normal(size=(B, C, K - 1))
+    seq = np.array([[0, 0, 0, 1, 1, 1, 1, 2, 2], [5, 5, 5, 5, 5, 5, 5, 5, 5]], np.int32)
+    dy = r.normal(size=(B, L, C))
+    q = r.normal(size=(B, C, K - 1))
+    for act in ("none", "silu"):
+        dx, dS, dw, db = oracle.conv1d_bwd(x, w, b, S, seq, dy, q, act=act, lib=lib)
+        eps = 1e-5
+        for arr, grad in ((x, dx), (S, dS), (w, dw), (b, db)):
+            num = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                keep = arr[idx]
+                arr[idx] = keep + eps
+                lp = _conv_loss(x, w, b, S, seq, dy, q, act, lib)
+                arr[idx] = keep - eps
+                lm = _conv_loss(x, w, b, S, seq, dy, q, act, lib)
+                arr[idx] = keep
+                num[idx] = (lp - lm) / (2 * eps)
+            np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7)
+
+
+def check_conv_bwd_chunking(lib):
+    """Chunked training ([CC] 'chunked training and truncated back-propagation'): with
+    S_B = F_A, passing dS_B back as dF_A reproduces the whole sequence's gradients, for every
+    split point (dw and dbeta add over the chunks)."""
+    r = _rng(32)
+    B, L, C, K = 2, 11, 2, 4
+    x = r.normal(size=(B, L, C))
+    w = r.normal(size=(C, K))
+    b = r.normal(size=(C,))
+    S = r.normal(size=(B, C, K - 1))
+    dy = r.normal(size=(B, L, C))
+    q = r.normal(size=(B, C, K - 1))
+    dx, dS, dw, db = oracle.conv1d_bwd(x, w, b, S, None, dy, q, act="silu", lib=lib)
+    for cut in range(0, L + 1):
+        _, FA = oracle.conv1d_fwd(x[:, :cut], w, b, S, act="silu", lib=lib)
+        dxB, dSB, dwB, dbB = oracle.conv1d_bwd(x[:, cut:], w, b, FA, None, dy[:, cut:], q,
+                                               act="silu", lib=lib)
+        dxA, dSA, dwA, dbA = oracle.conv1d_bwd(x[:, :cut], w, b, S, None, dy[:, :cut], dSB,
+                                               act="silu", lib=lib)
+        np.testing.assert_allclose(np.concatenate([dxA, dxB], axis=1), dx, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dSA, dS, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dwA + dwB, dw, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dbA + dbB, db, rtol=1e-12, atol=1e-12)
+
+
+def _scan_loss(x, dt, A, Bm, Cm, h0, seq, dy, dF, lib):
+    y, fin = oracle.scan_fwd(x, dt, A, Bm, Cm, h0, seq_idx=seq, lib=lib)
+    return float((y * dy).sum() + (fin * dF).sum())
+
+
+def check_scan_bwd_h0_finite_differences(lib):
+    """dh_{-1} against central differences of the oracle's forward scan on
+    L = sum dy * y + sum dF * h_final (L is linear in h_{-1}, so the differences are exact
+    up to rounding), with and without packed sequences (a reset cuts h_{-1} off)."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(33, B=2, L=9, H=4, P=3, N=5, G=2)
+    r = _rng(34)
+    dy = r.normal(size=x.shape)
+    dF = r.normal(size=h0.shape)
+    P = x.shape[3]
+    for seq in (None, np.array([[0, 0, 0, 0, 1, 1, 1, 1, 1], [3] * 9], np.int32)):
+        dh0 = oracle.scan_bwd_h0(dt, A, Cm, seq, dy, dF, P, lib=lib)
+        num = np.zeros_like(h0)
+        for idx in np.ndindex(h0.shape):
+            keep = h0[idx]
+            h0[idx] = keep + 0.5
+            lp = _scan_loss(x, dt, A, Bm, Cm, h0, seq, dy, dF, lib)
+            h0[idx] = keep - 0.5
+            lm = _scan_loss(x, dt, A, Bm, Cm, h0, seq, dy, dF, lib)
+            h0[idx] = keep
+            num[idx] = lp - lm
+        np.testing.assert_allclose(dh0, num, rtol=1e-9, atol=1e-9)
+
+
+def check_scan_bwd_h0_chunking(lib):
+    """State passing in the backward direction: the whole sequence's dh_{-1} equals chunk A's
+    with dF_A = chunk B's dh_{-1} (itself taking the external dF), for every split point."""
+    x, dt, A, Bm, Cm, h0 = _small_scan_inputs(35, B=2, L=10, H=2, P=3, N=4, G=1)
+    r = _rng(36)
+    dy = r.normal(size=x.shape)
+    dF = r.normal(size=h0.shape)
+    P = x.shape[3]
+    full = oracle.scan_bwd_h0(dt, A, Cm, None, dy, dF, P, lib=lib)
+    for cut in range(0, 11):
+        dB = oracle.scan_bwd_h0(dt[:, cut:], A, Cm[:, cut:], None, dy[:, cut:], dF, P, lib=lib)
+        dA = oracle.scan_bwd_h0(dt[:, :cut], A, Cm[:, :cut], None, dy[:, :cut], dB, P, lib=lib)
+        np.testing.assert_allclose(dA, full, rtol=1e-12, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_conv_worked_example_k4,
     check_conv_single_token_k3,
@@ -542,4 +665,9 @@ ALL_CHECKS = [
     check_scan_seq_idx_segments,
     check_step_equals_scan,
     check_round_bf16,
+    check_conv_bwd_single_token_k3,
+    check_conv_bwd_finite_differences,
+    check_conv_bwd_chunking,
+    check_scan_bwd_h0_finite_differences,
+    check_scan_bwd_h0_chunking,
 ]

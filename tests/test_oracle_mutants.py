@@ -65,6 +65,29 @@ MUTANTS = {
     # step: slot indices ignored
     "step_ignores_indices": ("const int64_t s = indices ? (int64_t)indices[b] : b;\n            if (s < 0 || s >= n_slots) {\n                for (int64_t t = 0; t < L_new; ++t)",
                              "const int64_t s = b;\n            if (s < 0 || s >= n_slots) {\n                for (int64_t t = 0; t < L_new; ++t)"),
+    # conv backward: the direct path from the final state to the last inputs dropped
+    "conv_bwd_no_dF": ("dext[L + r] += dfinal[(b * C + c) * (K - 1) + r];", "(void)r;"),
+    # conv backward: taps reversed in du
+    "conv_bwd_taps_reversed": ("dext[t + k] += dz[t] * w[c * K + k];",
+                               "dext[t + k] += dz[t] * w[c * K + (K - 1 - k)];"),
+    # conv backward: SiLU's derivative left out (delta = dy)
+    "conv_bwd_no_dphi": ("dphi = sg * (1.0 + zt * (1.0 - sg));", "dphi = 1.0;"),
+    # conv backward: SiLU's derivative taken as sigma(z) alone
+    "conv_bwd_dphi_sigma": ("dphi = sg * (1.0 + zt * (1.0 - sg));", "dphi = sg;"),
+    # conv backward: the weight gradient paired with the current input instead of the tap's
+    "conv_bwd_dw_wrong_input": ("dwc[k] += dz[t] * ext[t + k];", "dwc[k] += dz[t] * ext[t + K - 1];"),
+    # conv backward: dS / dx split one position off
+    "conv_bwd_split_off_by_one": ("dx[(b * L + t) * C + c] = orc_round(dext[K - 1 + t], dx_round);",
+                                  "dx[(b * L + t) * C + c] = orc_round(dext[K - 2 + t], dx_round);"),
+    # conv backward: the sequence mask ignored
+    "conv_bwd_no_mask": ("if (sq && seg[t + k] != seg[t + K - 1]) continue;", "if (0) continue;"),
+    # initial-state gradient: the decay applied one token late
+    "scan_bwd_decay_lag": ("prod *= exp(dt[(b * L + t) * H + h] * A[h]);\n                const double* Ct = Cm + ((b * L + t) * G + g) * N;\n                const double* dyt = dy + ((b * L + t) * H + h) * P;\n                for (int64_t p = 0; p < P; ++p)\n                    for (int64_t n = 0; n < N; ++n) acc[p * N + n] += dyt[p] * prod * Ct[n];",
+                           "const double* Ct = Cm + ((b * L + t) * G + g) * N;\n                const double* dyt = dy + ((b * L + t) * H + h) * P;\n                for (int64_t p = 0; p < P; ++p)\n                    for (int64_t n = 0; n < N; ++n) acc[p * N + n] += dyt[p] * prod * Ct[n];\n                prod *= exp(dt[(b * L + t) * H + h] * A[h]);"),
+    # initial-state gradient: packed-sequence resets ignored
+    "scan_bwd_no_reset": ("if (sq && t > 0 && sq[t] != sq[t - 1]) {", "if (0) {"),
+    # initial-state gradient: the final state's gradient dropped
+    "scan_bwd_no_dF": ("if (alive && dfinal) v += prod * dfinal[(b * H + h) * P * N + e];", "(void)alive;"),
     # bf16 rounding keeps 9 bits
     "bf16_nine_bits": ("int q = e - 8;", "int q = e - 9;"),
     # bf16 rounding truncates instead of nearest-even
