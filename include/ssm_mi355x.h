@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 /* hipStream_t is `struct ihipStream_t*`; this typedef is the same type. */
 struct ihipStream_t;
@@ -206,6 +206,66 @@ ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, c
                       const int32_t* state_indices, void* y, int64_t batch, int64_t n_new,
                       int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
                       int64_t n_slots, ssm_dtype_t dtype, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_conv1d_bwd -- backward of ssm_conv1d_fwd with state gradients.
+ * Defined in [CC] "backward with states, a unified derivation": over the extended sequence
+ * u = [S, x], with delta_t = dL/dz_t = dout_t * phi'(z_t) (z recomputed from x, S, w, bias),
+ *     du_j = sum_t sum_k delta_t w_k [j = t + k] + [L <= j < L+K-1] dF_{j-L},
+ *     dS = du[0 : K-1],  dx = du[K-1 : K-1+L],
+ *     dw_k = sum_{b,t} delta_t u_{t+k},  dbias = sum_{b,t} delta_t.
+ * With seq_idx the taps are masked exactly as in the forward; dF reaches the last K-1 inputs
+ * directly (F is their raw copy).  Chunked training ([CC] "chunked training and truncated
+ * back-propagation"): with S_B = F_A, passing chunk B's dS as chunk A's dF reproduces the
+ * whole sequence's gradients.
+ *
+ *   x, initial_state, seq_idx, w, bias   as ssm_conv1d_fwd (initial_state may be NULL)
+ *   dout            [batch, seqlen, channels]   dtype: dL/d(out)
+ *   dfinal_state    [batch, channels, width-1]  dtype: dL/dF, or NULL (= 0)
+ *   dx              [batch, seqlen, channels]   dtype
+ *   dinitial_state  [batch, channels, width-1]  dtype, or NULL (not written)
+ *   dw              [channels, width]           fp32 (summed over the batch)
+ *   dbias           [channels]                  fp32, or NULL (not written)
+ *   workspace       ssm_conv1d_bwd_workspace_size bytes (per-run partial sums of dw, dbias)
+ * Outputs must not overlap inputs.  dw and dbias are deterministic (a fixed summation
+ * order).  seqlen = 0: dinitial_state = dfinal_state, dw = dbias = 0.  batch = 0: no-op.
+ * ------------------------------------------------------------------------------------- */
+size_t ssm_conv1d_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t channels,
+                                     int64_t width);
+ssm_status_t ssm_conv1d_bwd(const void* x, const float* w, const float* bias,
+                            const void* initial_state, const int32_t* seq_idx, const void* dout,
+                            const void* dfinal_state, void* dx, void* dinitial_state, float* dw,
+                            float* dbias, void* workspace, size_t workspace_bytes, int64_t batch,
+                            int64_t seqlen, int64_t channels, int64_t width, ssm_dtype_t dtype,
+                            ssm_act_t act, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_scan_bwd_initial_state -- gradient of the loss with respect to the scan's initial
+ * state.  [LG] Sec. 2.5 Eq. (4): h_{-1} reaches y_t only through
+ * C_t^T (prod_{tau<=t} a_tau) h_{-1} and the final state through (prod_{tau<L} a_tau) h_{-1},
+ * a_tau = exp(dt_tau A_h), so
+ *     dh_{-1}[p][n] = sum_t dy_t[p] (prod_{tau<=t} a_tau) C_t[n] + (prod_{tau<L} a_tau) dF[p][n].
+ * With seq_idx the state is zeroed where the id changes, so only tokens before the first
+ * change reach h_{-1}, and dF does only when the row has no change.  Chunked training
+ * (Sec. 2.6): chunk B's result, passed as chunk A's dfinal_state, gives the whole sequence's.
+ *
+ *   dt               [batch, seqlen, nheads]            fp32
+ *   A                [nheads]                           fp32
+ *   C                [batch, seqlen, ngroups, dstate]   dtype
+ *   dy               [batch, seqlen, nheads, headdim]   dtype: dL/dy
+ *   seq_idx          [batch, seqlen] int32, or NULL
+ *   dfinal_state     [batch, nheads, headdim, dstate]   fp32, or NULL (= 0)
+ *   dinitial_state   [batch, nheads, headdim, dstate]   fp32; may alias dfinal_state
+ * headdim 64 / dstate 128 / bf16 run on the matrix cores (16-byte aligned C and dy); other
+ * shapes on a per-element loop.  Tokens after the decay product underflows to zero are not
+ * read (their terms are exactly zero).  batch = 0: no-op.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_scan_bwd_initial_state(const float* dt, const float* A, const void* C,
+                                        const void* dy, const int32_t* seq_idx,
+                                        const float* dfinal_state, float* dinitial_state,
+                                        int64_t batch, int64_t seqlen, int64_t nheads,
+                                        int64_t headdim, int64_t ngroups, int64_t dstate,
+                                        ssm_dtype_t dtype, ssm_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Measurement support (does not change any result).  When enabled, every launch of the

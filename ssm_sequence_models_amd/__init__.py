@@ -9,7 +9,7 @@ import fails loudly if the library has not been built.
 Sources of the operations (page title and section): the length-generalization reading
 notes on arXiv:2507.02782v2, Sec. 2.1 Eq. (1), Sec. 2.5 Eq. (4), Sec. 2.6 (scan with
 initial / final state); the causal-conv1d tutorial ch. 7 (conv state S / F, decode update,
-cache_seqlens, conv_state_indices, seq_idx).
+cache_seqlens, conv_state_indices, seq_idx, and the backward with state gradients).
 """
 from __future__ import annotations
 
@@ -56,11 +56,18 @@ def _load():
                                       i64, i64, i64, i64, ci, ci, vp, ctypes.c_size_t, vp]
     lib.ssm_step.argtypes = [vp, i64, i64, i64, fp, fp, vp, i64, i64, i64, vp, i64, i64, i64, fp,
                              i32p, vp, i64, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.ssm_conv1d_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_conv1d_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+    lib.ssm_conv1d_bwd.argtypes = [vp, fp, fp, vp, i32p, vp, vp, vp, vp, fp, fp, vp,
+                                   ctypes.c_size_t, i64, i64, i64, i64, ci, ci, vp]
+    lib.ssm_scan_bwd_initial_state.argtypes = [fp, fp, vp, vp, i32p, fp, fp, i64, i64, i64, i64,
+                                               i64, i64, ci, vp]
     lib.ssm_timing_enable.argtypes = [ci]
     lib.ssm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
-              "ssm_step", "ssm_timing_enable", "ssm_timing_read"):
+              "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state", "ssm_timing_enable",
+              "ssm_timing_read"):
         getattr(lib, f).restype = ci
     return lib
 
@@ -143,6 +150,68 @@ def conv1d_fwd(x, weight, bias=None, initial_state=None, seq_idx=None, activatio
         _ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(final_state), _ptr(seq_idx),
         _ptr(out), B, L, C, K, _dtype_code(x), ACT[activation], _stream()))
     return out, final_state
+
+
+def conv1d_bwd(x, weight, bias, dout, initial_state=None, dfinal_state=None, seq_idx=None,
+               activation=None, dx=None, dinitial_state=None, dweight=None, dbias=None,
+               workspace=None):
+    """Backward of conv1d_fwd with state gradients.  x, dout [B, L, C]; weight [C, K] fp32;
+    bias [C] fp32 or None; initial_state, dfinal_state [B, C, K-1] (None = zero); seq_idx
+    [B, L] int32.  Returns (dx [B, L, C], dinitial_state [B, C, K-1], dweight [C, K] fp32,
+    dbias [C] fp32)."""
+    B, L, C = x.shape
+    K = weight.shape[1]
+    _need(x, "x")
+    _need(weight, "weight", torch.float32, (C, K))
+    _need(bias, "bias", torch.float32, (C,))
+    _need(dout, "dout", x.dtype, (B, L, C))
+    _need(initial_state, "initial_state", x.dtype, (B, C, K - 1))
+    _need(dfinal_state, "dfinal_state", x.dtype, (B, C, K - 1))
+    _need(seq_idx, "seq_idx", torch.int32, (B, L))
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dinitial_state is None:
+        dinitial_state = torch.empty((B, C, K - 1), dtype=x.dtype, device=x.device)
+    if dweight is None:
+        dweight = torch.empty((C, K), dtype=torch.float32, device=x.device)
+    if dbias is None:
+        dbias = torch.empty((C,), dtype=torch.float32, device=x.device)
+    _need(dx, "dx", x.dtype, (B, L, C))
+    _need(dinitial_state, "dinitial_state", x.dtype, (B, C, K - 1))
+    _need(dweight, "dweight", torch.float32, (C, K))
+    _need(dbias, "dbias", torch.float32, (C,))
+    nbytes = int(_lib.ssm_conv1d_bwd_workspace_size(B, L, C, K))
+    ws, wsb = _workspace(workspace, nbytes, x.device)
+    _check("ssm_conv1d_bwd", _lib.ssm_conv1d_bwd(
+        _ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(seq_idx), _ptr(dout),
+        _ptr(dfinal_state), _ptr(dx), _ptr(dinitial_state), _ptr(dweight), _ptr(dbias),
+        _ptr(ws), wsb, B, L, C, K, _dtype_code(x), ACT[activation], _stream()))
+    return dx, dinitial_state, dweight, dbias
+
+
+def conv1d_bwd_workspace_size(batch, seqlen, channels, width) -> int:
+    return int(_lib.ssm_conv1d_bwd_workspace_size(batch, seqlen, channels, width))
+
+
+def scan_bwd_initial_state(dt, A, C, dy, dfinal_state=None, seq_idx=None, out=None):
+    """Gradient of the scan's initial state.  dt [b, L, H] fp32; A [H] fp32; C [b, L, G, N];
+    dy [b, L, H, P] (C's dtype); dfinal_state [b, H, P, N] fp32 or None; seq_idx [b, L]
+    int32.  Returns dinitial_state [b, H, P, N] fp32 (out may be dfinal_state itself)."""
+    b, L, H, P = dy.shape
+    G, N = C.shape[2], C.shape[3]
+    _need(dt, "dt", torch.float32, (b, L, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(C, "C", dy.dtype, (b, L, G, N))
+    _need(dy, "dy")
+    _need(dfinal_state, "dfinal_state", torch.float32, (b, H, P, N))
+    _need(seq_idx, "seq_idx", torch.int32, (b, L))
+    if out is None:
+        out = torch.empty((b, H, P, N), dtype=torch.float32, device=dy.device)
+    _need(out, "out", torch.float32, (b, H, P, N))
+    _check("ssm_scan_bwd_initial_state", _lib.ssm_scan_bwd_initial_state(
+        _ptr(dt), _ptr(A), _ptr(C), _ptr(dy), _ptr(seq_idx), _ptr(dfinal_state), _ptr(out),
+        b, L, H, P, G, N, _dtype_code(dy), _stream()))
+    return out
 
 
 def conv1d_update(x, conv_state, weight, bias=None, conv_state_indices=None,

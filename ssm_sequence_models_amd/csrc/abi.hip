@@ -448,6 +448,80 @@ ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, c
     return hip_status(ssm::launch_recurrent(r, dtype, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+size_t ssm_conv1d_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t channels,
+                                     int64_t width) {
+    if (batch <= 0 || seqlen <= 0 || channels < 1 || width < 2 || width > 8) return 0;
+    return static_cast<size_t>(ssm::conv1d_bwd_workspace_bytes(batch, seqlen, channels, width));
+}
+
+ssm_status_t ssm_conv1d_bwd(const void* x, const float* w, const float* bias,
+                            const void* initial_state, const int32_t* seq_idx, const void* dout,
+                            const void* dfinal_state, void* dx, void* dinitial_state, float* dw,
+                            float* dbias, void* workspace, size_t workspace_bytes, int64_t batch,
+                            int64_t seqlen, int64_t channels, int64_t width, ssm_dtype_t dtype,
+                            ssm_act_t act, ssm_stream_t stream) {
+    const char* fn = "ssm_conv1d_bwd";
+    if (!valid_dtype(dtype)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_bwd: bad dtype");
+    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_bwd: bad activation");
+    if (batch < 0 || seqlen < 0 || channels < 1)
+        return fail(SSM_ERR_INVALID_ARG, "ssm_conv1d_bwd: need batch >= 0, seqlen >= 0, channels >= 1");
+    if (width < 2 || width > 8)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv1d_bwd: width must be in [2, 8]");
+    const size_t es = esize(dtype);
+    const bool rows = batch > 0;
+    const bool work = rows && seqlen > 0;
+    ssm_status_t st = check_ptrs(fn, {{"x", x, work, es},
+                                      {"w", w, work, 4},
+                                      {"bias", bias, false, 4},
+                                      {"initial_state", initial_state, false, es},
+                                      {"seq_idx", seq_idx, false, 4},
+                                      {"dout", dout, work, es},
+                                      {"dfinal_state", dfinal_state, false, es},
+                                      {"dx", dx, work, es},
+                                      {"dinitial_state", dinitial_state, false, es},
+                                      {"dw", dw, rows, 4},
+                                      {"dbias", dbias, false, 4},
+                                      {"workspace", workspace, false, 4}});
+    if (st != SSM_OK) return st;
+    if (!rows) return ok();
+    const size_t need = ssm_conv1d_bwd_workspace_size(batch, seqlen, channels, width);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, "ssm_conv1d_bwd: workspace missing or smaller than "
+                                       "ssm_conv1d_bwd_workspace_size");
+    return hip_status(ssm::launch_conv1d_bwd(x, w, bias, initial_state, seq_idx, dout, dfinal_state,
+                                             dx, dinitial_state, dw, dbias, workspace, batch, seqlen,
+                                             channels, width, dtype, act,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+ssm_status_t ssm_scan_bwd_initial_state(const float* dt, const float* A, const void* C,
+                                        const void* dy, const int32_t* seq_idx,
+                                        const float* dfinal_state, float* dinitial_state,
+                                        int64_t batch, int64_t seqlen, int64_t nheads,
+                                        int64_t headdim, int64_t ngroups, int64_t dstate,
+                                        ssm_dtype_t dtype, ssm_stream_t stream) {
+    const char* fn = "ssm_scan_bwd_initial_state";
+    ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate, dtype);
+    if (st != SSM_OK) return st;
+    const size_t es = esize(dtype);
+    const bool rows = batch > 0;
+    const bool work = rows && seqlen > 0;
+    st = check_ptrs(fn, {{"dt", dt, work, 4},
+                         {"A", A, rows, 4},
+                         {"C", C, work, es},
+                         {"dy", dy, work, es},
+                         {"seq_idx", seq_idx, false, 4},
+                         {"dfinal_state", dfinal_state, false, 4},
+                         {"dinitial_state", dinitial_state, rows, 4}});
+    if (st != SSM_OK) return st;
+    if (!rows) return ok();
+    return hip_status(ssm::launch_scan_bwd_h0(dt, A, C, seq_idx, dy, dfinal_state, dinitial_state,
+                                              batch, seqlen, nheads, headdim, ngroups, dstate,
+                                              dtype, reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 ssm_status_t ssm_timing_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_tmu);
     g_timing = enable != 0;

@@ -1,0 +1,436 @@
+// bwd.hip -- backward kernels with state gradients.
+//
+// conv1d backward (causal-conv1d tutorial, ch. 7, "backward with states, a unified
+// derivation" and "chunked training and truncated back-propagation"): over the extended
+// sequence u = [S, x] and with delta_t = dL/dz_t = dy_t phi'(z_t),
+//     du_j = sum_t sum_k delta_t w_k [j = t + k] + [L <= j < L+K-1] q_{j-L},
+//     dS = du[0 : K-1],  dx = du[K-1 : K-1+L],  dw_k = sum delta_t u_{t+k},  dbeta = sum delta_t,
+// with the forward's sequence masks on the taps (q = dL/dF reaches the last K-1 inputs
+// directly, unmasked, as F is their raw copy).
+//
+// Initial-state gradient of the scan (length-generalization reading notes, Sec. 2.5 Eq. (4)
+// and Sec. 2.6): h_{-1} reaches y_t through C_t^T (prod_{tau<=t} a_tau) h_{-1}, so
+//     dh_{-1}[p][n] = sum_t dy_t[p] E_t C_t[n] + E_{L-1} dF[p][n],   E_t = prod_{tau<=t} a_tau,
+// where a packed-sequence change cuts h_{-1} off from every later token (and from F).
+#include "internal.h"
+
+namespace ssm {
+namespace {
+
+// ---------------------------------------------------------------------------------------
+// conv1d backward: thread = (row b, channel c, run r of kConvBwdRun tokens).  The thread
+// walks tokens t0 .. t1+K-2: it recomputes z_t from a register window of the K inputs of
+// output t, forms delta_t, adds the run's own tokens to its dw / dbeta partial sums, and
+// emits dx_s for s = t-K+1 once delta_{s .. s+K-1} are known.  Run 0 also forms dS from
+// delta_0 .. delta_{K-2}.  Consecutive threads take consecutive channels (coalesced rows).
+// ---------------------------------------------------------------------------------------
+constexpr int kConvBwdRun = 64;
+constexpr int kConvBwdThreads = 256;
+
+template <class D, int K>
+__global__ void __launch_bounds__(kConvBwdThreads)
+conv1d_bwd_kernel(const typename D::T* x, const float* w, const float* bias,
+                  const typename D::T* init, const int32_t* seq, const typename D::T* dy,
+                  const typename D::T* dfin, typename D::T* dx, typename D::T* dinit,
+                  float* part, int64_t L, int64_t C, int nruns, int silu) {
+    using T = typename D::T;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * kConvBwdThreads + threadIdx.x;
+    const int r = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    if (c >= C) return;  // no barriers in this kernel
+    const int64_t t0 = static_cast<int64_t>(r) * kConvBwdRun;
+    const int64_t t1 = min(t0 + kConvBwdRun, L);
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = w[c * K + k];
+    const float beta = bias ? bias[c] : 0.0f;
+    const int32_t* sq = seq ? seq + b * L : nullptr;
+    const int32_t id0 = sq ? sq[0] : 0;
+    // input at x index s (s < 0: the state, S_{K-1+s}) and its token identity
+    auto xval = [&](int64_t s) -> float {
+        if (s >= 0) return D::load(x, (b * L + s) * C + c);
+        return init ? D::load(init, (b * C + c) * (K - 1) + (K - 1) + s) : 0.0f;
+    };
+    auto sid = [&](int64_t s) -> int32_t { return sq ? sq[s < 0 ? 0 : s] : 0; };
+
+    float xv[K];     // inputs of output t: x indices t-K+1 .. t
+    int32_t xs[K];   // their identities
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) {
+        xv[k + 1] = xval(t0 - (K - 1) + k);
+        xs[k + 1] = sid(t0 - (K - 1) + k);
+    }
+    float dl[K];     // delta of tokens t-K+1 .. t (0 past the row's end)
+    int32_t ds[K];   // identities of those tokens
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        dl[k] = 0.0f;
+        ds[k] = 0;
+    }
+    float dwp[K], dbp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) dwp[k] = 0.0f;
+    float dsd[K];    // delta_0 .. delta_{K-2} (run 0: the dS terms)
+    int32_t dss[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        dsd[k] = 0.0f;
+        dss[k] = id0;
+    }
+
+    for (int64_t t = t0; t < t1 + K - 1; ++t) {
+        const bool live = t < L;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) {
+            xv[k] = xv[k + 1];
+            xs[k] = xs[k + 1];
+            dl[k] = dl[k + 1];
+            ds[k] = ds[k + 1];
+        }
+        float delta = 0.0f;
+        int32_t idt = 0;
+        if (live) {
+            xv[K - 1] = D::load(x, (b * L + t) * C + c);
+            xs[K - 1] = idt = sid(t);
+            float z = beta;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (!sq || xs[k] == idt) z = __builtin_fmaf(wk[k], xv[k], z);
+            float dphi = 1.0f;
+            if (silu) {
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+                dphi = sg * (1.0f + z * (1.0f - sg));
+            }
+            delta = D::load(dy, (b * L + t) * C + c) * dphi;
+            if (t < t1) {
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (!sq || xs[k] == idt) dwp[k] = __builtin_fmaf(delta, xv[k], dwp[k]);
+                dbp += delta;
+            }
+            if (t < K - 1) {
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k)
+                    if (k == t) {
+                        dsd[k] = delta;
+                        dss[k] = idt;
+                    }
+            }
+        }
+        dl[K - 1] = delta;
+        ds[K - 1] = idt;
+        // dx_s, s = t-K+1: taps m = 0 .. K-1 of outputs s+m through weight K-1-m
+        const int64_t s = t - (K - 1);
+        if (s >= t0 && s < t1) {
+            const int32_t ids = ds[0];  // identity of token s (its own output, m = 0)
+            float v = 0.0f;
+#pragma unroll
+            for (int m = 0; m < K; ++m)
+                if (!sq || ds[m] == ids) v = __builtin_fmaf(dl[m], wk[K - 1 - m], v);
+            if (dfin && s + K - 1 >= L) v += D::load(dfin, (b * C + c) * (K - 1) + (s + K - 1 - L));
+            D::store(dx, (b * L + s) * C + c, v);
+        }
+    }
+    if (r == 0 && dinit) {
+        // dS_j = sum_{t <= j} delta_t w_{j-t} (taps whose identity, the state's, matches
+        // output t) + q_{j-L} when j >= L
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+            float v = 0.0f;
+#pragma unroll
+            for (int t = 0; t <= j; ++t)
+                if (t < L && (!sq || dss[t] == id0)) v = __builtin_fmaf(dsd[t], wk[j - t], v);
+            if (dfin && j >= L) v += D::load(dfin, (b * C + c) * (K - 1) + (j - L));
+            D::store(dinit, (b * C + c) * (K - 1) + j, v);
+        }
+    }
+    float* pp = part + ((b * nruns + r) * C + c) * (K + 1);
+#pragma unroll
+    for (int k = 0; k < K; ++k) pp[k] = dwp[k];
+    pp[K] = dbp;
+}
+
+// dw[c][k] and dbias[c]: the runs' partial sums added in a fixed order, in double
+__global__ void conv1d_bwd_reduce_kernel(const float* part, float* dw, float* dbias, int64_t C,
+                                         int K, int64_t nparts) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= C * (K + 1)) return;
+    double acc = 0.0;
+    for (int64_t p = 0; p < nparts; ++p) acc += part[p * C * (K + 1) + i];
+    const int64_t c = i / (K + 1), k = i % (K + 1);
+    if (k < K) dw[c * K + k] = static_cast<float>(acc);
+    else if (dbias) dbias[c] = static_cast<float>(acc);
+}
+
+__global__ void fill_zero_f32_kernel(float* p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// L = 0: dS = q (F is S itself), dw = dbias = 0
+template <class D>
+__global__ void conv1d_bwd_empty_kernel(const typename D::T* dfin, typename D::T* dinit, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n && dinit) D::store(dinit, i, dfin ? D::load(dfin, i) : 0.0f);
+}
+
+// ---------------------------------------------------------------------------------------
+// dh_{-1}, MFMA path (P = 64, N = 128, bf16): one block per (b, h), four wavefronts; wave w
+// owns rows p = 16 w .. 16 w + 15 of dh_{-1}[p][0..127] in accumulators.  Per 64-token chunk:
+// dy^T and C^T are staged in LDS (token index contiguous), wave 0 forms E_t = 2^(offset +
+// prefix of dt A log2 e) with a DPP scan, then dh += (E o dy)^T C with E o dy split into two
+// bf16 halves (hi + lo, as the main scan) against the exact bf16 C.  The loop stops at the
+// first packed-sequence change and once E underflows to 0: every later term is exactly 0.
+// ---------------------------------------------------------------------------------------
+constexpr int kH0Q = 64, kH0P = 64, kH0N = 128;
+constexpr int kH0Row = kH0Q * 2 + 16;  // bytes per [row][64 tokens] bf16 row in LDS (padded)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h0_incl_sum(float v) {
+    const int z = __float_as_int(0.0f);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+__global__ void __launch_bounds__(256)
+scan_bwd_h0_mfma_kernel(const float* dt, const float* A, const uint16_t* Cm,
+                        const int32_t* seq, const uint16_t* dy, const float* dfin, float* dh0,
+                        int64_t L, int64_t H, int64_t G) {
+    __shared__ __attribute__((aligned(16))) uint8_t sCt[kH0N * kH0Row];  // C^T [n][t]
+    __shared__ __attribute__((aligned(16))) uint8_t sDy[kH0P * kH0Row];  // dy^T [p][t]
+    __shared__ float sE[kH0Q];
+    __shared__ int sStop;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
+    const int64_t h = blockIdx.x, b = blockIdx.y;
+    const int64_t g = h / (H / G);
+    const float a2 = A[h] * 1.4426950408889634f;
+    const int32_t* sq = seq ? seq + b * L : nullptr;
+    f32x4_t acc[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float offset = 0.0f;  // log2 of E at the end of the previous chunk (wave 0)
+    bool alive = true;    // no sequence change so far (wave 0, uniform)
+    for (int64_t t0 = 0; t0 < L; t0 += kH0Q) {
+        // stage C^T and dy^T: 16-byte pieces of a token row, written transposed
+        for (int i = tid; i < kH0Q * (kH0N / 8); i += 256) {
+            const int tt = i / (kH0N / 8), q = i % (kH0N / 8);
+            const int64_t t = t0 + tt;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (t < L) v = *reinterpret_cast<const u32x4_t*>(Cm + ((b * L + t) * G + g) * kH0N + 8 * q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<uint16_t*>(sCt + (8 * q + e) * kH0Row + 2 * tt) =
+                    static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
+        }
+        for (int i = tid; i < kH0Q * (kH0P / 8); i += 256) {
+            const int tt = i / (kH0P / 8), q = i % (kH0P / 8);
+            const int64_t t = t0 + tt;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (t < L) v = *reinterpret_cast<const u32x4_t*>(dy + ((b * L + t) * H + h) * kH0P + 8 * q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<uint16_t*>(sDy + (8 * q + e) * kH0Row + 2 * tt) =
+                    static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
+        }
+        if (wave == 0) {
+            const int64_t t = t0 + lane;
+            const bool in = t < L;
+            const float v = in ? dt[(b * L + t) * H + h] * a2 : 0.0f;
+            const float cum = h0_incl_sum(v);
+            bool cut = false;  // a sequence change at or before this token (within the chunk)
+            if (sq) {
+                const bool chg = in && t > 0 && sq[t] != sq[t - 1];
+                const uint64_t m = __ballot(chg);
+                const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // lanes 0 .. lane
+                cut = (m & upto) != 0;
+            }
+            const bool ok = alive && !cut && in;
+            sE[lane] = ok ? __builtin_amdgcn_exp2f(offset + cum) : 0.0f;
+            offset += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kH0Q - 1));
+            const bool any_cut = __ballot(cut) != 0;
+            alive = alive && !any_cut;
+            const float e_end = __builtin_amdgcn_exp2f(offset);
+            if (lane == 0) sStop = (!alive || e_end == 0.0f) ? 1 : 0;
+        }
+        __syncthreads();
+        // dh[p][n] += sum_t (E_t dy[t][p]) C[t][n]; lane: row p = 16 wave + li of the A operand,
+        // tokens 32 ks + 8 g4 .. +7
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int tb = 32 * ks + 8 * g4;
+            const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(sE + tb);
+            const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(sE + tb + 4);
+            const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(sDy + (16 * wave + li) * kH0Row + 2 * tb);
+            float av[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ee = e < 4 ? e0[e] : e1[e - 4];
+                const uint32_t bits = (dv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                av[e] = ee * __uint_as_float(bits << 16);
+            }
+            u32x4_t hv, lv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t hp = pack_bf16x2(av[2 * e], av[2 * e + 1]);
+                hv[e] = hp;
+                const float h0f = __uint_as_float(hp << 16), h1f = __uint_as_float(hp & 0xFFFF0000u);
+                lv[e] = pack_bf16x2(av[2 * e] - h0f, av[2 * e + 1] - h1f);
+            }
+            const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, hv), alo = __builtin_bit_cast(bf16x8_t, lv);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(sCt + (16 * n + li) * kH0Row + 2 * tb);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, acc[n], 0, 0, 0);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, acc[n], 0, 0, 0);
+            }
+        }
+        const bool stop = sStop != 0;
+        __syncthreads();  // the tiles are consumed before the next chunk overwrites them
+        if (stop) break;
+    }
+    // the final state's term, E_{L-1} dF (zero after a sequence change or an underflow);
+    // lane holds dh[p][n] for p = 16 wave + 4 g4 + r, n = 16 nt + li
+    __shared__ float sEnd;
+    if (wave == 0 && lane == 0) sEnd = alive ? __builtin_amdgcn_exp2f(offset) : 0.0f;
+    __syncthreads();
+    const float eend = sEnd;
+    float* out = dh0 + (b * H + h) * kH0P * kH0N;
+    const float* fin = dfin ? dfin + (b * H + h) * kH0P * kH0N : nullptr;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int p = 16 * wave + 4 * g4 + rr, n = 16 * nt + li;
+            float v = acc[nt][rr];
+            if (fin) v = __builtin_fmaf(eend, fin[p * kH0N + n], v);
+            out[p * kH0N + n] = v;
+        }
+    }
+}
+
+// dh_{-1}, general shapes: one thread per (b, h, p, n), the token loop of the definition
+// (stops at the first sequence change or once E underflows to 0)
+template <class D>
+__global__ void scan_bwd_h0_generic_kernel(const float* dt, const float* A,
+                                           const typename D::T* Cm, const int32_t* seq,
+                                           const typename D::T* dy, const float* dfin,
+                                           float* dh0, int64_t B, int64_t L, int64_t H,
+                                           int64_t P, int64_t G, int64_t N) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= B * H * P * N) return;
+    const int64_t n = i % N, p = (i / N) % P, h = (i / (N * P)) % H, b = i / (N * P * H);
+    const int64_t g = h / (H / G);
+    const int32_t* sq = seq ? seq + b * L : nullptr;
+    float e = 1.0f, acc = 0.0f;
+    bool alive = true;
+    for (int64_t t = 0; t < L; ++t) {
+        if (sq && t > 0 && sq[t] != sq[t - 1]) {
+            alive = false;
+            break;
+        }
+        e *= __expf(dt[(b * L + t) * H + h] * A[h]);
+        if (e == 0.0f) break;
+        acc = __builtin_fmaf(D::load(dy, ((b * L + t) * H + h) * P + p) * e,
+                             D::load(Cm, ((b * L + t) * G + g) * N + n), acc);
+    }
+    if (dfin && alive) acc = __builtin_fmaf(e, dfin[i], acc);
+    dh0[i] = acc;
+}
+
+}  // namespace
+
+int64_t conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t channels, int64_t width) {
+    if (batch <= 0 || seqlen <= 0) return 0;
+    const int64_t nruns = (seqlen + kConvBwdRun - 1) / kConvBwdRun;
+    return batch * nruns * channels * (width + 1) * static_cast<int64_t>(sizeof(float));
+}
+
+hipError_t launch_conv1d_bwd(const void* x, const float* w, const float* bias, const void* init,
+                             const int32_t* seq, const void* dy, const void* dfin, void* dx,
+                             void* dinit, float* dw, float* dbias, void* workspace,
+                             int64_t batch, int64_t seqlen, int64_t channels, int64_t width,
+                             ssm_dtype_t dtype, ssm_act_t act, hipStream_t stream) {
+    const int64_t C = channels, K = width;
+    if (seqlen == 0) {
+        const int64_t nst = batch * C * (K - 1);
+        if (dinit && nst > 0) {
+            const unsigned grid = static_cast<unsigned>((nst + 255) / 256);
+            if (dtype == SSM_BF16)
+                conv1d_bwd_empty_kernel<BF16><<<grid, 256, 0, stream>>>(
+                    static_cast<const uint16_t*>(dfin), static_cast<uint16_t*>(dinit), nst);
+            else
+                conv1d_bwd_empty_kernel<F32><<<grid, 256, 0, stream>>>(
+                    static_cast<const float*>(dfin), static_cast<float*>(dinit), nst);
+        }
+        fill_zero_f32_kernel<<<static_cast<unsigned>((C * K + 255) / 256), 256, 0, stream>>>(dw, C * K);
+        if (dbias) fill_zero_f32_kernel<<<static_cast<unsigned>((C + 255) / 256), 256, 0, stream>>>(dbias, C);
+        return hipGetLastError();
+    }
+    const int nruns = static_cast<int>((seqlen + kConvBwdRun - 1) / kConvBwdRun);
+    dim3 grid(static_cast<unsigned>((C + kConvBwdThreads - 1) / kConvBwdThreads),
+              static_cast<unsigned>(nruns), static_cast<unsigned>(batch));
+    float* part = static_cast<float*>(workspace);
+    const int silu = act == SSM_ACT_SILU ? 1 : 0;
+#define SSM_CBWD(KK)                                                                           \
+    case KK:                                                                                   \
+        if (dtype == SSM_BF16)                                                                 \
+            conv1d_bwd_kernel<BF16, KK><<<grid, kConvBwdThreads, 0, stream>>>(                 \
+                static_cast<const uint16_t*>(x), w, bias, static_cast<const uint16_t*>(init),   \
+                seq, static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(dfin),      \
+                static_cast<uint16_t*>(dx), static_cast<uint16_t*>(dinit), part, seqlen, C,     \
+                nruns, silu);                                                                  \
+        else                                                                                   \
+            conv1d_bwd_kernel<F32, KK><<<grid, kConvBwdThreads, 0, stream>>>(                  \
+                static_cast<const float*>(x), w, bias, static_cast<const float*>(init), seq,    \
+                static_cast<const float*>(dy), static_cast<const float*>(dfin),                \
+                static_cast<float*>(dx), static_cast<float*>(dinit), part, seqlen, C, nruns,    \
+                silu);                                                                         \
+        break;
+    switch (K) {
+        SSM_CBWD(2) SSM_CBWD(3) SSM_CBWD(4) SSM_CBWD(5) SSM_CBWD(6) SSM_CBWD(7) SSM_CBWD(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef SSM_CBWD
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nred = C * (K + 1);
+    conv1d_bwd_reduce_kernel<<<static_cast<unsigned>((nred + 255) / 256), 256, 0, stream>>>(
+        part, dw, dbias, C, static_cast<int>(K), batch * nruns);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd_h0(const float* dt, const float* A, const void* Cm,
+                              const int32_t* seq, const void* dy, const float* dfin, float* dh0,
+                              int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t ngroups, int64_t dstate, ssm_dtype_t dtype,
+                              hipStream_t stream) {
+    const bool a16 = (reinterpret_cast<uintptr_t>(Cm) % 16) == 0 && (reinterpret_cast<uintptr_t>(dy) % 16) == 0;
+    if (dtype == SSM_BF16 && headdim == kH0P && dstate == kH0N && a16 && seqlen > 0) {
+        dim3 grid(static_cast<unsigned>(nheads), static_cast<unsigned>(batch));
+        scan_bwd_h0_mfma_kernel<<<grid, 256, 0, stream>>>(
+            dt, A, static_cast<const uint16_t*>(Cm), seq, static_cast<const uint16_t*>(dy), dfin,
+            dh0, seqlen, nheads, ngroups);
+        return hipGetLastError();
+    }
+    const int64_t n = batch * nheads * headdim * dstate;
+    const unsigned grid = static_cast<unsigned>((n + 255) / 256);
+    if (dtype == SSM_BF16)
+        scan_bwd_h0_generic_kernel<BF16><<<grid, 256, 0, stream>>>(
+            dt, A, static_cast<const uint16_t*>(Cm), seq, static_cast<const uint16_t*>(dy), dfin,
+            dh0, batch, seqlen, nheads, headdim, ngroups, dstate);
+    else
+        scan_bwd_h0_generic_kernel<F32><<<grid, 256, 0, stream>>>(
+            dt, A, static_cast<const float*>(Cm), seq, static_cast<const float*>(dy), dfin, dh0,
+            batch, seqlen, nheads, headdim, ngroups, dstate);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -191,6 +191,17 @@ hipError_t launch_chunked(const ChunkedArgs& a, hipStream_t stream, hipEvent_t e
                           hipEvent_t ev_after_main);
 
 // small helpers
+int64_t conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t channels, int64_t width);
+hipError_t launch_conv1d_bwd(const void* x, const float* w, const float* bias, const void* init,
+                             const int32_t* seq, const void* dy, const void* dfin, void* dx,
+                             void* dinit, float* dw, float* dbias, void* workspace,
+                             int64_t batch, int64_t seqlen, int64_t channels, int64_t width,
+                             ssm_dtype_t dtype, ssm_act_t act, hipStream_t stream);
+hipError_t launch_scan_bwd_h0(const float* dt, const float* A, const void* Cm,
+                              const int32_t* seq, const void* dy, const float* dfin, float* dh0,
+                              int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t ngroups, int64_t dstate, ssm_dtype_t dtype,
+                              hipStream_t stream);
 hipError_t launch_copy_or_zero_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_copy_or_zero_bytes(void* dst, const void* src, int64_t nbytes, hipStream_t s);
 

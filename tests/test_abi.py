@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
               "ssm_step", "ssm_scan_workspace_size", "ssm_abi_version", "ssm_status_string",
-              "ssm_last_error"):
+              "ssm_last_error", "ssm_conv1d_bwd", "ssm_conv1d_bwd_workspace_size",
+              "ssm_scan_bwd_initial_state"):
         assert f in names
 
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
     for code in range(6):
         assert lib.ssm_status_string(code)
 
@@ -55,6 +56,10 @@ def test_workspace_query():
     import torch
     assert s.workspace_size(1, 64, 1, 4, 1, 4, torch.float32) == 64 * 12 * 4
     assert s.workspace_size(0, 64, 1, 4, 1, 4) == 0
+    # conv backward: one fp32 partial (dw_0 .. dw_{K-1}, dbias) per (row, 64-token run, channel)
+    assert s.conv1d_bwd_workspace_size(4, 8192, 4352, 4) == 4 * 128 * 4352 * 5 * 4
+    assert s.conv1d_bwd_workspace_size(2, 65, 3, 2) == 2 * 2 * 3 * 3 * 4
+    assert s.conv1d_bwd_workspace_size(2, 0, 3, 4) == 0
 
 
 def _c(v):
@@ -90,6 +95,18 @@ def test_argument_errors_return_status(lib):
     # unsupported state size for the general path
     assert lib.ssm_step(dummy, 0, 0, 1, dummy, dummy, dummy, 0, 0, 1, dummy, 0, 0, 1, dummy,
                         None, dummy, 1, 1, 1, 4, 1, 6, 4, 0, None) == 2
+    # conv backward: width outside [2, 8]; NULL dw; workspace too small
+    assert lib.ssm_conv1d_bwd(dummy, dummy, None, None, None, dummy, None, dummy, None, dummy,
+                              None, dummy, 1 << 20, 1, 4, 8, 1, 1, 0, None) == 2
+    assert lib.ssm_conv1d_bwd(dummy, dummy, None, None, None, dummy, None, dummy, None, None,
+                              None, dummy, 1 << 20, 1, 4, 8, 4, 1, 0, None) == 1
+    assert lib.ssm_conv1d_bwd(dummy, dummy, None, None, None, dummy, None, dummy, None, dummy,
+                              None, dummy, 16, 1, 4, 8, 4, 1, 0, None) == 4
+    # initial-state gradient: nheads not a multiple of ngroups; NULL output
+    assert lib.ssm_scan_bwd_initial_state(dummy, dummy, dummy, dummy, None, None, dummy, 1, 64,
+                                          3, 64, 2, 128, 1, None) == 1
+    assert lib.ssm_scan_bwd_initial_state(dummy, dummy, dummy, dummy, None, None, None, 1, 64,
+                                          4, 64, 1, 128, 1, None) == 1
     # zero-sized work is a no-op that succeeds without touching the device
     assert lib.ssm_conv1d_update(None, None, None, None, None, None, None, 0, 8, 1, 4, 3, 4, 1,
                                  0, None) == 0
