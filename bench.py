@@ -99,8 +99,9 @@ def copy_bandwidth(torch):
 def other_ops(torch, ssm, workloads, copy_GBs):
     """Achieved bandwidth of the other entry points on their workloads: the unfused conv at the
     1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
-    1.3B-like prefill with packed sequences, the 370M-like prefill and the 131072-token
-    780M-like call.  Seeded inputs drawn on the GPU
+    1.3B-like prefill with packed sequences, the 370M-like prefill, the 131072-token
+    780M-like call, and the backward entry points (conv with state gradients, the scan's
+    initial-state gradient) at the 1.3B shape.  Seeded inputs drawn on the GPU
     (timing only; parity is the test suite's job)."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
@@ -185,6 +186,46 @@ def other_ops(torch, ssm, workloads, copy_GBs):
         nb = (2 * R * H * P * N * 4 + 2 * R * C * d["state_len"] * 2 + 3 * R * C * L_new * 2
               + R * L_new * H * 4 + R * L_new * H * P * 2)
         rep("decode_step", f"{R} requests, {S}-slot pools (1.3B dims), L_new {L_new}", ms, R * L_new, nb)
+    del conv_pool, ssm_pool
+
+    # backward of the unfused conv at the 1.3B shape, with state gradients
+    s = workloads.shape_of("layer1p3b")
+    x, dt, w, b, A = prefill_inputs(s, 15)
+    g.manual_seed(16)
+    dy = torch.randn(s.B, s.L, s.C, generator=g, device=dev).to(torch.bfloat16)
+    init = torch.randn(s.B, s.C, s.K - 1, generator=g, device=dev).to(torch.bfloat16)
+    dF = torch.randn(s.B, s.C, s.K - 1, generator=g, device=dev).to(torch.bfloat16)
+    dx, dS = torch.empty_like(x), torch.empty_like(init)
+    dw = torch.empty(s.C, s.K, device=dev)
+    dbias = torch.empty(s.C, device=dev)
+    ws = torch.empty(ssm.conv1d_bwd_workspace_size(s.B, s.L, s.C, s.K), dtype=torch.uint8, device=dev)
+    ms = _time_gpu(torch, lambda: ssm.conv1d_bwd(x, w, b, dy, initial_state=init, dfinal_state=dF,
+                                                  activation="silu", dx=dx, dinitial_state=dS,
+                                                  dweight=dw, dbias=dbias, workspace=ws), 10)
+    rep("conv1d_bwd", f"B{s.B} L{s.L} C{s.C} K{s.K} bf16 SiLU: dx, dS, dw, dbias", ms, s.B * s.L,
+        3 * s.B * s.L * s.C * 2 + 3 * s.B * s.C * (s.K - 1) * 2 + 2 * s.C * (s.K + 1) * 4)
+    del x, dy, dx, ws
+
+    # initial-state gradient at the 1.3B shape: (a) the layer's dt / A, where the decay product
+    # underflows within a few hundred tokens and the kernel stops there; (b) slow decays that
+    # keep every token in play (a full pass over dy and C)
+    Cm = torch.randn(s.B, s.L, s.G, s.N, generator=g, device=dev).to(torch.bfloat16)
+    dyh = torch.randn(s.B, s.L, s.H, s.P, generator=g, device=dev).to(torch.bfloat16)
+    dFh = torch.randn(s.B, s.H, s.P, s.N, generator=g, device=dev)
+    dh0 = torch.empty_like(dFh)
+    for label, dts, As in (("layer dt / A (stops where the decay underflows)", dt, A),
+                           ("dt 0.01, A -0.05 (every token)", torch.full_like(dt, 0.01),
+                            torch.full_like(A, -0.05))):
+        ms = _time_gpu(torch, lambda: ssm.scan_bwd_initial_state(dts, As, Cm, dyh, dfinal_state=dFh,
+                                                                  out=dh0), 10)
+        # tokens a (b, h) block must read: up to the chunk where 2^(cum log2 e) underflows in fp32
+        cum = torch.cumsum(dts.double() * As.double(), dim=1) * (1.0 / math.log(2.0))
+        under = (cum < -150.0)
+        first = torch.where(under.any(dim=1), under.float().argmax(dim=1), torch.full_like(under[:, 0], s.L, dtype=torch.long))
+        toks = float(torch.clamp((first // 64 + 1) * 64, max=s.L).sum())
+        nb = toks * (s.P * 2 + s.N * 2 + 4) + 2 * s.B * s.H * s.P * s.N * 4
+        rep("scan_bwd_initial_state", f"B{s.B} L{s.L} H{s.H}x{s.P} N{s.N} bf16, {label}; "
+            f"{toks / (s.B * s.H):.0f} tokens read per (row, head)", ms, s.B * s.L, nb)
     return res
 
 

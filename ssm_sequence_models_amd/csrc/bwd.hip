@@ -150,16 +150,30 @@ conv1d_bwd_kernel(const typename D::T* x, const float* w, const float* bias,
     pp[K] = dbp;
 }
 
-// dw[c][k] and dbias[c]: the runs' partial sums added in a fixed order, in double
-__global__ void conv1d_bwd_reduce_kernel(const float* part, float* dw, float* dbias, int64_t C,
-                                         int K, int64_t nparts) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= C * (K + 1)) return;
+// dw[c][k] and dbias[c]: the runs' partial sums added in a fixed order, in double.  A block
+// takes 64 consecutive outputs (one per lane); its four wavefronts sum a quarter of the
+// partials each, and wave 0 adds the four in order.
+__global__ void __launch_bounds__(256)
+conv1d_bwd_reduce_kernel(const float* part, float* dw, float* dbias, int64_t C, int K,
+                         int64_t nparts) {
+    __shared__ double red[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t n = C * (K + 1);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + lane;
     double acc = 0.0;
-    for (int64_t p = 0; p < nparts; ++p) acc += part[p * C * (K + 1) + i];
-    const int64_t c = i / (K + 1), k = i % (K + 1);
-    if (k < K) dw[c * K + k] = static_cast<float>(acc);
-    else if (dbias) dbias[c] = static_cast<float>(acc);
+    if (i < n) {
+        const int64_t p0 = wv * nparts / 4, p1 = (wv + 1) * nparts / 4;
+#pragma unroll 8
+        for (int64_t p = p0; p < p1; ++p) acc += part[p * n + i];
+    }
+    red[wv][lane] = acc;
+    __syncthreads();
+    if (wv == 0 && i < n) {
+        const double v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        const int64_t c = i / (K + 1), k = i % (K + 1);
+        if (k < K) dw[c * K + k] = static_cast<float>(v);
+        else if (dbias) dbias[c] = static_cast<float>(v);
+    }
 }
 
 __global__ void fill_zero_f32_kernel(float* p, int64_t n) {
@@ -402,7 +416,7 @@ hipError_t launch_conv1d_bwd(const void* x, const float* w, const float* bias, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nred = C * (K + 1);
-    conv1d_bwd_reduce_kernel<<<static_cast<unsigned>((nred + 255) / 256), 256, 0, stream>>>(
+    conv1d_bwd_reduce_kernel<<<static_cast<unsigned>((nred + 63) / 64), 256, 0, stream>>>(
         part, dw, dbias, C, static_cast<int>(K), batch * nruns);
     return hipGetLastError();
 }
