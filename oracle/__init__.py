@@ -21,7 +21,9 @@ Definitions followed (page title and section):
   * conv1d_bwd      causal-conv1d tutorial ch. 7, "backward with states, a unified derivation"
                     (du over the extended sequence, dS, dx, dw, dbeta) and "chunked training";
   * scan_bwd_h0     the gradient of the initial state through Eq. (4) of the reading notes
-                    (Sec. 2.5), with the final state's gradient added (Sec. 2.6).
+                    (Sec. 2.5), with the final state's gradient added (Sec. 2.6);
+  * conv_scan_fwd_pooled  conv_scan_fwd with its states taken from and returned to the decode
+                    pools (tutorial ch. 7: the physical cache, circular mode, state indices).
 """
 from __future__ import annotations
 
@@ -222,6 +224,57 @@ def scan_bwd_h0(dt, A, Cm, seq_idx, dy, dfinal, P, out_dtype="f64", lib=None):
     lib.orc_scan_bwd_h0(_p(dt), _p(A), _p(Cm), _p(seq_idx, _ip), _p(dy), _p(dfinal), _p(dh0),
                         B, L, H, P, G, N, ROUND[out_dtype])
     return dh0
+
+
+def conv_scan_fwd_pooled(xBC, conv_w, conv_bias, dt, A, conv_pool, ssm_pool, indices,
+                         cache_seqlens, seq_idx, H, P, G, N, act="silu", out_dtype="f64",
+                         state_dtype="f64", lib=None):
+    """The fused prefill on decode pools (causal-conv1d tutorial ch. 7: the physical cache,
+    the circular mode's slot p mod S_len and history (p - j) mod S_len, state indices; the
+    closing distinction between another request's history, packed samples and continuing one
+    request's history).  Row b takes slot s = indices[b] (b if None): its conv history is the
+    pool's (circular: slots (p - j) mod S_len for j = K-1 .. 1, p = cache_seqlens[b]; linear:
+    the row's last K-1), its SSM initial state pool[s]; after conv_scan_fwd, the row's new raw
+    inputs go where conv1d_update would put them and pool[s] takes the final state.  Rows
+    with an out-of-range slot run from zero states and store nothing.
+
+    Returns (y [B, L, H, P], new conv pool, new ssm pool); the inputs are not modified."""
+    lib = lib or _get()
+    xBC = _f64(xBC)
+    conv_pool = np.array(_f64(conv_pool), copy=True)
+    ssm_pool = np.array(_f64(ssm_pool), copy=True)
+    B, L, C = xBC.shape
+    K = np.asarray(conv_w).shape[1]
+    S_len = conv_pool.shape[2]
+    n_slots = conv_pool.shape[0]
+    idx = None if indices is None else np.asarray(indices).astype(np.int64)
+    p_of = None if cache_seqlens is None else np.asarray(cache_seqlens).astype(np.int64)
+    ys = []
+    for b in range(B):
+        s = b if idx is None else int(idx[b])
+        ok = 0 <= s < n_slots
+        hist = np.zeros((1, C, K - 1))
+        h0 = np.zeros((1, H, P, N))
+        if ok:
+            for j in range(K - 1):  # oldest first: j steps ... 1 step back
+                back = (K - 1) - j
+                slot = (int(p_of[b]) - back) % S_len if p_of is not None else S_len - back
+                hist[0, :, j] = conv_pool[s, :, slot]
+            h0[0] = ssm_pool[s]
+        seq = None if seq_idx is None else np.asarray(seq_idx)[b:b + 1]
+        y, _, fin = conv_scan_fwd(xBC[b:b + 1], conv_w, conv_bias, hist, _f64(dt)[b:b + 1], A, h0,
+                                  seq, H, P, G, N, act=act, out_dtype=out_dtype,
+                                  state_dtype=state_dtype, lib=lib)
+        ys.append(y)
+        if ok:
+            if p_of is not None:
+                for t in range(L):
+                    conv_pool[s, :, (int(p_of[b]) + t) % S_len] = xBC[b, t, :]
+            else:
+                row = np.concatenate([conv_pool[s], xBC[b].T], axis=1)
+                conv_pool[s] = row[:, -S_len:]
+            ssm_pool[s] = fin[0]
+    return np.concatenate(ys, axis=0), conv_pool, ssm_pool
 
 
 def step(x, dt, A, Bm, Cm, pool, indices=None, out_dtype="f64", state_dtype="f64", lib=None):

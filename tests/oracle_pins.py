@@ -642,6 +642,115 @@ def check_scan_bwd_h0_chunking(lib):
         np.testing.assert_allclose(dA, full, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------------------------------
+# the prefill on the decode pools
+# ------------------------------------------------------------------------------------------
+
+def _pooled_layer(seed, B=2, L=11, H=2, P=3, N=4, G=1, K=4):
+    r = _rng(seed)
+    C = H * P + 2 * G * N
+    xBC = r.normal(size=(B, L, C))
+    w = r.uniform(-0.5, 0.5, size=(C, K))
+    b = r.uniform(-0.5, 0.5, size=(C,))
+    dt = np.log1p(np.exp(r.normal(size=(B, L, H)) - 2.0))
+    A = -np.exp(r.uniform(0.0, np.log(16.0), size=(H,)))
+    return xBC, w, b, dt, A, (H, P, G, N, K, C)
+
+
+def check_pooled_prefill_chain_equals_whole(lib):
+    """Continuing one request's history ([CC] ch. 7): pooled prefills of x[:L1] and then x[L1:]
+    (ring position advanced by L1 between them, circular and linear layouts) give the whole
+    prefill's outputs, SSM final state and raw-input history."""
+    xBC, w, b, dt, A, (H, P, G, N, K, C) = _pooled_layer(41)
+    B, L = xBC.shape[:2]
+    y_whole, _, fin_whole = oracle.conv_scan_fwd(xBC, w, b, None, dt, A, None, None, H, P, G, N,
+                                                 act="silu", out_dtype="f64", state_dtype="f64",
+                                                 lib=lib)
+    for S_len, circular in ((5, True), (K - 1, True), (6, False)):
+        for L1 in (0, 1, 2, 7, L):
+            cp = np.zeros((B, C, S_len))
+            sp = np.zeros((B, H, P, N))
+            seq0 = np.zeros(B, np.int32) if circular else None
+            ya, cp, sp = oracle.conv_scan_fwd_pooled(xBC[:, :L1], w, b, dt[:, :L1], A, cp, sp, None,
+                                                     seq0, None, H, P, G, N, out_dtype="f64",
+                                                     state_dtype="f64", lib=lib)
+            seq1 = np.full(B, L1, np.int32) if circular else None
+            yb, cp, sp = oracle.conv_scan_fwd_pooled(xBC[:, L1:], w, b, dt[:, L1:], A, cp, sp, None,
+                                                     seq1, None, H, P, G, N, out_dtype="f64",
+                                                     state_dtype="f64", lib=lib)
+            np.testing.assert_allclose(np.concatenate([ya, yb], axis=1), y_whole, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(sp, fin_whole, rtol=1e-12, atol=1e-12)
+            for j in range(1, min(S_len, L) + 1):   # the last inputs sit where the ring says
+                slot = (L - j) % S_len if circular else S_len - j
+                np.testing.assert_array_equal(cp[:, :, slot], xBC[:, L - j, :])
+
+
+def check_pooled_prefill_then_decode(lib):
+    """Prefill into the pools, then decode the rest one token at a time with the oracle's own
+    conv1d_update (circular, ring position advanced by the caller) and step on the same pools:
+    the outputs equal the whole prefill's (the pool layout is the decode path's)."""
+    xBC, w, b, dt, A, (H, P, G, N, K, C) = _pooled_layer(42, B=2, L=9)
+    B, L = xBC.shape[:2]
+    S_len, L1 = 5, 4
+    idx = np.array([2, 0], np.int32)                   # rows on slots 2 and 0 of 3
+    y_whole, _, _ = oracle.conv_scan_fwd(xBC, w, b, None, dt, A, None, None, H, P, G, N,
+                                         act="silu", out_dtype="f64", state_dtype="f64", lib=lib)
+    cp = np.zeros((3, C, S_len))
+    sp = np.zeros((3, H, P, N))
+    ya, cp, sp = oracle.conv_scan_fwd_pooled(xBC[:, :L1], w, b, dt[:, :L1], A, cp, sp, idx,
+                                             np.zeros(B, np.int32), None, H, P, G, N,
+                                             out_dtype="f64", state_dtype="f64", lib=lib)
+    np.testing.assert_allclose(ya, y_whole[:, :L1], rtol=1e-12, atol=1e-12)
+    for t in range(L1, L):
+        out, cp = oracle.conv1d_update(xBC[:, t, :, None], cp, w, b, idx,
+                                       np.full(B, t, np.int32), act="silu", lib=lib)
+        o = out[:, :, 0]
+        xs = o[:, :H * P].reshape(B, 1, H, P)
+        Bs = o[:, H * P:H * P + G * N].reshape(B, 1, G, N)
+        Cs = o[:, H * P + G * N:].reshape(B, 1, G, N)
+        yt, sp = oracle.step(xs, dt[:, t:t + 1], A, Bs, Cs, sp, idx, lib=lib)
+        np.testing.assert_allclose(yt[:, 0], y_whole[:, t], rtol=1e-12, atol=1e-12)
+
+
+def check_pooled_prefill_ring_example(lib):
+    """ch. 7 circular mode, K = 3, S_len = 4, p = 5: a one-token prefill reads its history
+    from slots 3 and 0 and writes the new input to slot 1; another row's slot, an
+    out-of-range row (zero states, nothing stored)."""
+    g = _golden("ring_buffer_k3.json")
+    K, S_len, p = g["K"], g["state_len"], g["p"]
+    H, P, G, N = 1, 1, 1, 1
+    C = H * P + 2 * G * N
+    cp = np.zeros((2, C, S_len))
+    cp[1, 0] = [10.0, 20.0, 30.0, 40.0]                 # slot 1, x channel: 10 (s + 1)
+    sp = np.zeros((2, H, P, N))
+    w = np.zeros((C, K))
+    w[0] = [1.0, 100.0, 10000.0]                          # w0 oldest .. w2 current
+    w[1, K - 1] = w[2, K - 1] = 1.0                       # B_t = C_t = their current input
+    xBC = np.zeros((2, 1, C))
+    xBC[:, 0, 0] = 7.0
+    xBC[:, 0, 1] = xBC[:, 0, 2] = 1.0
+    dt = np.ones((2, 1, H))
+    A = np.array([-1.0])
+    idx = np.array([1, 5], np.int32)                      # row 1: slot 5 of 2, out of range
+    y, cp2, sp2 = oracle.conv_scan_fwd_pooled(xBC, w, None, dt, A, cp, sp, idx,
+                                              np.array([p, p], np.int32), None, H, P, G, N,
+                                              act="none", out_dtype="f64", state_dtype="f64",
+                                              lib=lib)
+    # y_0 = C (dt x B) = the conv output of the x channel over the ring's history
+    older, newer = g["history_slots"]
+    expect_z = w[0, 0] * cp[1, 0, older] + w[0, 1] * cp[1, 0, newer] + w[0, 2] * 7.0
+    assert y[0, 0, 0, 0] == expect_z, (y, expect_z)
+    after = cp[1, 0].copy()
+    after[g["write_slot"]] = 7.0
+    np.testing.assert_array_equal(cp2[1, 0], after)
+    np.testing.assert_array_equal(cp2[0], cp[0])          # slot 0 untouched
+    np.testing.assert_array_equal(sp2[0], sp[0])
+    # the out-of-range row ran from zero states: its y is the plain prefill's
+    y0, _, _ = oracle.conv_scan_fwd(xBC[1:], w, None, None, dt[1:], A, None, None, H, P, G, N,
+                                    act="none", out_dtype="f64", state_dtype="f64", lib=lib)
+    np.testing.assert_array_equal(y[1:], y0)
+
+
 ALL_CHECKS = [
     check_conv_worked_example_k4,
     check_conv_single_token_k3,
@@ -670,4 +779,7 @@ ALL_CHECKS = [
     check_conv_bwd_chunking,
     check_scan_bwd_h0_finite_differences,
     check_scan_bwd_h0_chunking,
+    check_pooled_prefill_chain_equals_whole,
+    check_pooled_prefill_then_decode,
+    check_pooled_prefill_ring_example,
 ]
