@@ -100,9 +100,9 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     """Achieved bandwidth of the other entry points on their workloads: the unfused conv at the
     1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
     1.3B-like prefill with packed sequences, the 370M-like prefill, the 131072-token
-    780M-like call, and the backward entry points (conv with state gradients, the scan's
-    initial-state gradient) at the 1.3B shape.  Seeded inputs drawn on the GPU
-    (timing only; parity is the test suite's job)."""
+    780M-like call, the chunked prefill on the decode pools, and the backward entry points
+    (conv with state gradients, the scan's initial-state gradient) at the 1.3B shape.  Seeded
+    inputs drawn on the GPU (timing only; parity is the test suite's job)."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     res = []
@@ -187,6 +187,28 @@ def other_ops(torch, ssm, workloads, copy_GBs):
               + R * L_new * H * 4 + R * L_new * H * P * 2)
         rep("decode_step", f"{R} requests, {S}-slot pools (1.3B dims), L_new {L_new}", ms, R * L_new, nb)
     del conv_pool, ssm_pool
+
+    # chunked prefill on the decode pools (continuous batching): 16 requests each add a
+    # 2048-token chunk, states read from and written back to their ring-buffer slots
+    R, Lp = 16, 2048
+    g.manual_seed(17)
+    conv_pool = torch.randn(S, C, d["state_len"], generator=g, device=dev).to(torch.bfloat16)
+    ssm_pool = torch.randn(S, H, P, N, generator=g, device=dev)
+    idx = torch.randperm(S, generator=g, device=dev)[:R].to(torch.int32)
+    seqlens = torch.randint(0, d["max_seqlen"] + 1, (R,), generator=g, device=dev).to(torch.int32)
+    xp = torch.randn(R, Lp, C, generator=g, device=dev).to(torch.bfloat16)
+    dtp = torch.nn.functional.softplus(torch.randn(R, Lp, H, generator=g, device=dev) - 2).contiguous()
+    yp = torch.empty(R, Lp, H, P, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ssm.conv_scan_fwd_pooled_workspace_size(R, Lp, H, P, G, N, K) + 256,
+                     dtype=torch.uint8, device=dev)
+    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd_pooled(
+        xp, w, b, dtp, A, conv_pool, ssm_pool, H, P, G, N, state_indices=idx,
+        cache_seqlens=seqlens, y=yp, workspace=ws), 10)
+    nb = (R * Lp * (C * 2 + H * 4 + H * P * 2) + 2 * R * H * P * N * 4
+          + R * C * (K - 1 + min(Lp, d["state_len"])) * 2)
+    rep("conv_scan_fwd_pooled", f"{R} requests x {Lp}-token chunk into {S}-slot pools (1.3B dims, "
+        "ring layout)", ms, R * Lp, nb)
+    del conv_pool, ssm_pool, xp, yp, ws
 
     # backward of the unfused conv at the 1.3B shape, with state gradients
     s = workloads.shape_of("layer1p3b")

@@ -184,6 +184,43 @@ ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float
                                size_t workspace_bytes, ssm_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * ssm_conv_scan_fwd_pooled -- the fused prefill reading its initial states from, and writing
+ * its final states to, the decode pools, so a request moves from prefill to decode (or to its
+ * next prefill chunk) without dense state copies.  [CC] "the physical cache may exceed the
+ * minimal history", "state indices for continuous batching" and the chapter's closing
+ * distinction between choosing another request's history (the slot), blocking history across
+ * packed samples (seq_idx) and continuing one request's history (the ring position).
+ * Row b uses slot s = state_indices[b] (b when NULL):
+ *   conv history = ssm_conv1d_update's: circular (cache_seqlens != NULL, p = cache_seqlens[b])
+ *     slots (p - j) mod state_len, j = K-1 .. 1 (oldest first); linear: the row's last K-1;
+ *   SSM initial state = ssm_state[s];
+ *   then ssm_conv_scan_fwd over the row's L tokens, and afterwards, as ssm_conv1d_update
+ *   would leave them: circular: token i in slot (p + i) mod state_len; linear: the row is the
+ *   last state_len entries of (old row ++ new tokens); ssm_state[s] = the final state.
+ * cache_seqlens is read, never advanced (the caller adds seqlen).  A row whose slot is outside
+ * [0, n_slots) runs from zero states and stores nothing; two rows on one slot: undefined.
+ *
+ *   xBC, conv_w, conv_bias, dt, A, seq_idx, y    as ssm_conv_scan_fwd
+ *   conv_state      [n_slots, C_conv, state_len]     dtype, in / out (state_len >= width-1)
+ *   ssm_state       [n_slots, nheads, headdim, dstate] fp32, in / out
+ *   state_indices   [batch] int32, or NULL;  cache_seqlens [batch] int32 (>= 0), or NULL
+ *   workspace       ssm_conv_scan_fwd_pooled_workspace_size bytes, 256-byte aligned
+ * ------------------------------------------------------------------------------------- */
+size_t ssm_conv_scan_fwd_pooled_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                               int64_t headdim, int64_t ngroups, int64_t dstate,
+                                               int64_t width, ssm_dtype_t dtype);
+ssm_status_t ssm_conv_scan_fwd_pooled(const void* xBC, const float* conv_w,
+                                      const float* conv_bias, const float* dt, const float* A,
+                                      void* conv_state, float* ssm_state,
+                                      const int32_t* state_indices, const int32_t* cache_seqlens,
+                                      const int32_t* seq_idx, void* y, int64_t batch,
+                                      int64_t seqlen, int64_t nheads, int64_t headdim,
+                                      int64_t ngroups, int64_t dstate, int64_t width,
+                                      int64_t state_len, int64_t n_slots, ssm_dtype_t dtype,
+                                      ssm_act_t act, void* workspace, size_t workspace_bytes,
+                                      ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * ssm_step -- decode-time scan update on a state pool, n_new >= 1 tokens per request.
  * Same recurrence as ssm_scan_fwd ([LG] Eq. (1)), token by token, on pool slot
  * s = state_indices[b] (b when NULL); the state is kept in fp32 registers across the n_new

@@ -62,11 +62,17 @@ def _load():
                                    ctypes.c_size_t, i64, i64, i64, i64, ci, ci, vp]
     lib.ssm_scan_bwd_initial_state.argtypes = [fp, fp, vp, vp, i32p, fp, fp, i64, i64, i64, i64,
                                                i64, i64, ci, vp]
+    lib.ssm_conv_scan_fwd_pooled_workspace_size.restype = ctypes.c_size_t
+    lib.ssm_conv_scan_fwd_pooled_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci]
+    lib.ssm_conv_scan_fwd_pooled.argtypes = [vp, fp, fp, fp, fp, vp, fp, i32p, i32p, i32p, vp,
+                                             i64, i64, i64, i64, i64, i64, i64, i64, i64, ci, ci,
+                                             vp, ctypes.c_size_t, vp]
     lib.ssm_timing_enable.argtypes = [ci]
     lib.ssm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
-              "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state", "ssm_timing_enable",
+              "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
+              "ssm_conv_scan_fwd_pooled", "ssm_timing_enable",
               "ssm_timing_read"):
         getattr(lib, f).restype = ci
     return lib
@@ -150,6 +156,52 @@ def conv1d_fwd(x, weight, bias=None, initial_state=None, seq_idx=None, activatio
         _ptr(x), _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(final_state), _ptr(seq_idx),
         _ptr(out), B, L, C, K, _dtype_code(x), ACT[activation], _stream()))
     return out, final_state
+
+
+def conv_scan_fwd_pooled(xBC, conv_weight, conv_bias, dt, A, conv_state, ssm_state, nheads,
+                         headdim, ngroups, dstate, state_indices=None, cache_seqlens=None,
+                         seq_idx=None, activation="silu", y=None, workspace=None):
+    """The fused prefill on the decode pools: row b's initial conv history and SSM state come
+    from slot state_indices[b] (ring position cache_seqlens[b], or the linear layout), and its
+    new raw inputs and final state go back there.  conv_state [n_slots, C_conv, state_len]
+    (xBC's dtype) and ssm_state [n_slots, H, P, N] fp32 update in place; cache_seqlens is not
+    advanced.  Returns y [b, L, H, P]."""
+    b, L, C_conv = xBC.shape
+    K = conv_weight.shape[1]
+    n_slots, _, state_len = conv_state.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    _need(xBC, "xBC")
+    _need(conv_weight, "conv_weight", torch.float32, (C_conv, K))
+    _need(conv_bias, "conv_bias", torch.float32, (C_conv,))
+    _need(dt, "dt", torch.float32, (b, L, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(conv_state, "conv_state", xBC.dtype, (n_slots, C_conv, state_len))
+    _need(ssm_state, "ssm_state", torch.float32, (n_slots, H, P, N))
+    _need(state_indices, "state_indices", torch.int32, (b,))
+    _need(cache_seqlens, "cache_seqlens", torch.int32, (b,))
+    _need(seq_idx, "seq_idx", torch.int32, (b, L))
+    if y is None:
+        y = torch.empty((b, L, H, P), dtype=xBC.dtype, device=xBC.device)
+    _need(y, "y", xBC.dtype, (b, L, H, P))
+    nbytes = int(_lib.ssm_conv_scan_fwd_pooled_workspace_size(b, L, H, P, G, N, K, _dtype_code(xBC)))
+    if workspace is None:
+        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=xBC.device)
+    off = (-workspace.data_ptr()) % 256
+    if workspace.numel() - off < nbytes:
+        raise ValueError(f"workspace must hold {nbytes} bytes past a 256-byte boundary")
+    _check("ssm_conv_scan_fwd_pooled", _lib.ssm_conv_scan_fwd_pooled(
+        _ptr(xBC), _ptr(conv_weight), _ptr(conv_bias), _ptr(dt), _ptr(A), _ptr(conv_state),
+        _ptr(ssm_state), _ptr(state_indices), _ptr(cache_seqlens), _ptr(seq_idx), _ptr(y), b, L,
+        H, P, G, N, K, state_len, n_slots, _dtype_code(xBC), ACT[activation],
+        ctypes.c_void_p(workspace.data_ptr() + off), workspace.numel() - off, _stream()))
+    return y
+
+
+def conv_scan_fwd_pooled_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, width,
+                                        dtype=torch.bfloat16) -> int:
+    code = SSM_BF16 if dtype == torch.bfloat16 else SSM_F32
+    return int(_lib.ssm_conv_scan_fwd_pooled_workspace_size(batch, seqlen, nheads, headdim, ngroups,
+                                                            dstate, width, code))
 
 
 def conv1d_bwd(x, weight, bias, dout, initial_state=None, dfinal_state=None, seq_idx=None,

@@ -448,6 +448,88 @@ ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, c
     return hip_status(ssm::launch_recurrent(r, dtype, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+namespace {
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+}  // namespace
+
+size_t ssm_conv_scan_fwd_pooled_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                               int64_t headdim, int64_t ngroups, int64_t dstate,
+                                               int64_t width, ssm_dtype_t dtype) {
+    if (batch <= 0 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1 || width < 2 ||
+        width > 8 || !valid_dtype(dtype))
+        return 0;
+    const int64_t C_conv = nheads * headdim + 2 * ngroups * dstate;
+    const size_t scan = round256(ssm_scan_workspace_size(batch, seqlen, nheads, headdim, ngroups,
+                                                         dstate, dtype));
+    const size_t hist = round256(static_cast<size_t>(batch * C_conv * (width - 1)) * esize(dtype));
+    const size_t st = round256(static_cast<size_t>(batch * nheads * headdim * dstate) * 4);
+    return scan + hist + st;
+}
+
+ssm_status_t ssm_conv_scan_fwd_pooled(const void* xBC, const float* conv_w,
+                                      const float* conv_bias, const float* dt, const float* A,
+                                      void* conv_state, float* ssm_state,
+                                      const int32_t* state_indices, const int32_t* cache_seqlens,
+                                      const int32_t* seq_idx, void* y, int64_t batch,
+                                      int64_t seqlen, int64_t nheads, int64_t headdim,
+                                      int64_t ngroups, int64_t dstate, int64_t width,
+                                      int64_t state_len, int64_t n_slots, ssm_dtype_t dtype,
+                                      ssm_act_t act, void* workspace, size_t workspace_bytes,
+                                      ssm_stream_t stream) {
+    const char* fn = "ssm_conv_scan_fwd_pooled";
+    ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate, dtype);
+    if (st != SSM_OK) return st;
+    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv_scan_fwd_pooled: bad activation");
+    if (width < 2 || width > 8)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv_scan_fwd_pooled: width must be in [2, 8]");
+    if (n_slots < 1 || state_len < width - 1)
+        return fail(SSM_ERR_INVALID_ARG,
+                    "ssm_conv_scan_fwd_pooled: need n_slots >= 1 and state_len >= width - 1");
+    const size_t es = esize(dtype);
+    const bool rows = batch > 0;
+    // every pointer is checked before the first launch, so a rejected call leaves the pools
+    // and the workspace untouched
+    st = check_ptrs(fn, {{"xBC", xBC, rows, es},
+                         {"conv_w", conv_w, rows, 4},
+                         {"conv_bias", conv_bias, false, 4},
+                         {"dt", dt, rows, 4},
+                         {"A", A, rows, 4},
+                         {"conv_state", conv_state, rows, es},
+                         {"ssm_state", ssm_state, rows, 4},
+                         {"state_indices", state_indices, false, 4},
+                         {"cache_seqlens", cache_seqlens, false, 4},
+                         {"seq_idx", seq_idx, false, 4},
+                         {"y", y, rows, es}});
+    if (st != SSM_OK) return st;
+    if (!rows) return ok();
+    const size_t need = ssm_conv_scan_fwd_pooled_workspace_size(batch, seqlen, nheads, headdim,
+                                                                ngroups, dstate, width, dtype);
+    if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(SSM_ERR_WORKSPACE, std::string(fn) + ": workspace must be >= " +
+                                           std::to_string(need) + " bytes, 256-byte aligned");
+    const int64_t C_conv = nheads * headdim + 2 * ngroups * dstate;
+    const int64_t per = nheads * headdim * dstate;
+    const size_t scan = round256(ssm_scan_workspace_size(batch, seqlen, nheads, headdim, ngroups,
+                                                         dstate, dtype));
+    const size_t hist_b = round256(static_cast<size_t>(batch * C_conv * (width - 1)) * es);
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    void* hist = base + scan;
+    float* sstate = reinterpret_cast<float*>(base + scan + hist_b);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = ssm::launch_pool_gather(conv_state, ssm_state, state_indices, cache_seqlens,
+                                           hist, sstate, batch, C_conv, width, state_len, per,
+                                           n_slots, dtype, s);
+    if (e != hipSuccess) return hip_status(e, fn);
+    st = ssm_conv_scan_fwd(xBC, conv_w, conv_bias, hist, nullptr, dt, A, sstate, sstate, seq_idx,
+                           y, batch, seqlen, nheads, headdim, ngroups, dstate, width, dtype, act,
+                           scan > 0 ? workspace : nullptr, scan, stream);
+    if (st != SSM_OK) return st;
+    return hip_status(ssm::launch_pool_scatter(conv_state, ssm_state, state_indices, cache_seqlens,
+                                               xBC, sstate, batch, seqlen, C_conv, state_len, per,
+                                               n_slots, dtype, s),
+                      fn);
+}
+
 size_t ssm_conv1d_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t channels,
                                      int64_t width) {
     if (batch <= 0 || seqlen <= 0 || channels < 1 || width < 2 || width > 8) return 0;

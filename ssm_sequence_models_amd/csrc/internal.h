@@ -202,6 +202,16 @@ hipError_t launch_scan_bwd_h0(const float* dt, const float* A, const void* Cm,
                               int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                               int64_t ngroups, int64_t dstate, ssm_dtype_t dtype,
                               hipStream_t stream);
+hipError_t launch_pool_gather(const void* conv_pool, const float* ssm_pool, const int32_t* indices,
+                              const int32_t* seqlens, void* conv_hist, float* ssm_init,
+                              int64_t batch, int64_t C, int64_t K, int64_t state_len,
+                              int64_t ssm_per, int64_t n_slots, ssm_dtype_t dtype,
+                              hipStream_t stream);
+hipError_t launch_pool_scatter(void* conv_pool, float* ssm_pool, const int32_t* indices,
+                               const int32_t* seqlens, const void* x, const float* ssm_final,
+                               int64_t batch, int64_t L, int64_t C, int64_t state_len,
+                               int64_t ssm_per, int64_t n_slots, ssm_dtype_t dtype,
+                               hipStream_t stream);
 hipError_t launch_copy_or_zero_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_copy_or_zero_bytes(void* dst, const void* src, int64_t nbytes, hipStream_t s);
 

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
               "ssm_step", "ssm_scan_workspace_size", "ssm_abi_version", "ssm_status_string",
               "ssm_last_error", "ssm_conv1d_bwd", "ssm_conv1d_bwd_workspace_size",
-              "ssm_scan_bwd_initial_state"):
+              "ssm_scan_bwd_initial_state", "ssm_conv_scan_fwd_pooled",
+              "ssm_conv_scan_fwd_pooled_workspace_size"):
         assert f in names
 
 
@@ -60,6 +61,12 @@ def test_workspace_query():
     assert s.conv1d_bwd_workspace_size(4, 8192, 4352, 4) == 4 * 128 * 4352 * 5 * 4
     assert s.conv1d_bwd_workspace_size(2, 65, 3, 2) == 2 * 2 * 3 * 3 * 4
     assert s.conv1d_bwd_workspace_size(2, 0, 3, 4) == 0
+    # prefill on the pools: the scan's workspace, then the dense conv history [B, C, K-1] and
+    # the dense SSM state [B, H, P, N] fp32, each rounded up to 256 bytes
+    C = 64 * 64 + 2 * 128
+    assert s.conv_scan_fwd_pooled_workspace_size(4, 8192, 64, 64, 1, 128, 4) == (
+        s.workspace_size(4, 8192, 64, 64, 1, 128) + (4 * C * 3 * 2 + 255) // 256 * 256
+        + 4 * 64 * 64 * 128 * 4)
 
 
 def _c(v):
@@ -107,6 +114,14 @@ def test_argument_errors_return_status(lib):
                                           3, 64, 2, 128, 1, None) == 1
     assert lib.ssm_scan_bwd_initial_state(dummy, dummy, dummy, dummy, None, None, None, 1, 64,
                                           4, 64, 1, 128, 1, None) == 1
+    # prefill on the pools: state_len < width - 1; NULL ssm pool; NULL y; workspace too small
+    pooled = lambda y, pool, state_len, ws_bytes: lib.ssm_conv_scan_fwd_pooled(
+        dummy, dummy, None, dummy, dummy, dummy, pool, None, None, None, y, 1, 64, 4, 64, 1, 128,
+        4, state_len, 2, 1, 1, dummy, ws_bytes, None)
+    assert pooled(dummy, dummy, 2, 1 << 30) == 1
+    assert pooled(dummy, None, 4, 1 << 30) == 1 and b"ssm_state is NULL" in lib.ssm_last_error()
+    assert pooled(None, dummy, 4, 1 << 30) == 1 and b"y is NULL" in lib.ssm_last_error()
+    assert pooled(dummy, dummy, 4, 16) == 4
     # zero-sized work is a no-op that succeeds without touching the device
     assert lib.ssm_conv1d_update(None, None, None, None, None, None, None, 0, 8, 1, 4, 3, 4, 1,
                                  0, None) == 0
