@@ -23,7 +23,10 @@ Definitions followed (page title and section):
   * scan_bwd_h0     the gradient of the initial state through Eq. (4) of the reading notes
                     (Sec. 2.5), with the final state's gradient added (Sec. 2.6);
   * conv_scan_fwd_pooled  conv_scan_fwd with its states taken from and returned to the decode
-                    pools (tutorial ch. 7: the physical cache, circular mode, state indices).
+                    pools (tutorial ch. 7: the physical cache, circular mode, state indices);
+  * state_stats_update, initial_state_noise, state_reset  the initial-state distributions of
+                    the reading notes' Sec. 2.6 (Fitted Noise Eqs. (5)-(6), Random Noise, State
+                    Passing's reset), drawing from Philox4x64-10 (Salmon et al., SC 2011).
 """
 from __future__ import annotations
 
@@ -81,6 +84,16 @@ def load_library(path: str):
     for f in ("orc_conv1d_fwd", "orc_conv1d_update", "orc_scan_fwd", "orc_step",
               "orc_conv1d_bwd", "orc_scan_bwd_h0"):
         getattr(lib, f).restype = ctypes.c_int
+    _u64 = ctypes.c_uint64
+    _u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.orc_philox4x64_10.argtypes = [_u64p, _u64p, _u64p]
+    lib.orc_box_muller.argtypes = [ctypes.c_double, ctypes.c_double, _dp]
+    lib.orc_state_stats_update.argtypes = [_dp, _i64, _i64, _i64, _i64, ctypes.c_double, _dp,
+                                           _dp, ctypes.c_int]
+    lib.orc_initial_state_noise.argtypes = [_dp, _i64, _i64, _i64, _i64, _dp, _dp,
+                                            ctypes.c_double, _u64, _u64, ctypes.c_int]
+    lib.orc_state_reset.argtypes = [_dp, _dp, ctypes.POINTER(ctypes.c_uint8), _i64, _i64,
+                                    ctypes.c_double, _u64, _u64]
     return lib
 
 
@@ -311,3 +324,63 @@ def conv_scan_fwd(xBC, conv_w, conv_bias, conv_init, dt, A, ssm_init, seq_idx, H
     y, ssm_fin = scan_fwd(x, dt, A, Bm, Cm, ssm_init, seq_idx, out_dtype=out_dtype,
                           state_dtype=state_dtype, lib=lib)
     return y, conv_fin, ssm_fin
+
+
+def philox4x64_10(counter, key, lib=None):
+    """Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2,
+    3", SC 2011): four 64-bit counter words and two key words to four output words."""
+    lib = lib or _get()
+    c = (ctypes.c_uint64 * 4)(*[int(v) for v in counter])
+    k = (ctypes.c_uint64 * 2)(*[int(v) for v in key])
+    o = (ctypes.c_uint64 * 4)()
+    lib.orc_philox4x64_10(c, k, o)
+    return [int(v) for v in o]
+
+
+def box_muller(u1, u2, lib=None):
+    """(r cos 2 pi u2, r sin 2 pi u2), r = sqrt(-2 ln u1)."""
+    lib = lib or _get()
+    o = (ctypes.c_double * 2)()
+    lib.orc_box_muller(float(u1), float(u2), o)
+    return o[0], o[1]
+
+
+def state_stats_update(final_state, mean, var, beta=0.1, out_dtype="f32", lib=None):
+    """Fitted Noise statistics (reading notes Sec. 2.6, Eqs. (5)-(6)): per head, the batch's
+    Mean and (population) Variance of final_state [B, H, P, N] over rows, channels and state
+    dimension, blended as (1 - beta) new + beta old.  Returns new (mean [H], var [H])."""
+    lib = lib or _get()
+    fin = _f64(final_state)
+    B, H, P, N = fin.shape
+    m = np.array(_f64(mean), copy=True)
+    v = np.array(_f64(var), copy=True)
+    lib.orc_state_stats_update(_p(fin), B, H, P, N, float(beta), _p(m), _p(v), ROUND[out_dtype])
+    return m, v
+
+
+def initial_state_noise(shape, mean=None, var=None, sigma=1.0, seed=0, offset=0,
+                        out_dtype="f32", lib=None):
+    """Noise initial states (reading notes Sec. 2.6): Fitted Noise N(mean[h], var[h]) per head
+    when mean / var are given, Random Noise N(0, sigma^2) otherwise; shape (B, H, P, N)."""
+    lib = lib or _get()
+    B, H, P, N = shape
+    out = np.zeros((B, H, P, N))
+    m = None if mean is None else _f64(mean)
+    v = None if var is None else _f64(var)
+    lib.orc_initial_state_noise(_p(out), B, H, P, N, _p(m), _p(v), float(sigma), int(seed),
+                                int(offset), ROUND[out_dtype])
+    return out
+
+
+def state_reset(state, p=0.1, seed=0, offset=0, lib=None):
+    """State Passing's occasional reset (reading notes Sec. 2.6): each row of state [B, ...]
+    is zeroed with probability p.  Returns (new state, mask [B] uint8: 1 = zeroed)."""
+    lib = lib or _get()
+    src = _f64(state)
+    B = src.shape[0]
+    per = int(np.prod(src.shape[1:])) if src.ndim > 1 else 1
+    dst = np.zeros_like(src)
+    mask = np.zeros(B, dtype=np.uint8)
+    lib.orc_state_reset(_p(src), _p(dst), mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), B,
+                        per, float(p), int(seed), int(offset))
+    return dst, mask

@@ -445,3 +445,135 @@ int orc_scan_bwd_h0(const double* dt, const double* A, const double* Cm,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------
+ * Initial-state distributions for training ([LG] Sec. 2.6, the table of four interventions,
+ * the Fitted Noise update Eqs. (5)-(6) and the State Passing procedure).
+ *
+ * Random numbers come from Philox4x64-10, the counter-based generator of Salmon, Moraes,
+ * Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): a 256-bit counter
+ * and a 128-bit key pass through ten rounds; each round multiplies counter words 0 and 2 by
+ * fixed odd constants, keeps the 128-bit products' high and low halves, and mixes the high
+ * halves with the other counter words and the round key; the key advances by fixed Weyl
+ * increments between rounds.  Streams used here:
+ *   key = (seed, purpose), counter = (block, offset, 0, 0); purpose 0 draws the Gaussian
+ *   noise, purpose 1 the State Passing reset decisions.
+ * ------------------------------------------------------------------------------------- */
+#define ORC_PHILOX_M0 0xD2E7470EE14C6C93ULL
+#define ORC_PHILOX_M1 0xCA5A826395121157ULL
+#define ORC_PHILOX_W0 0x9E3779B97F4A7C15ULL
+#define ORC_PHILOX_W1 0xBB67AE8584CAA73BULL
+
+void orc_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]) {
+    uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) { /* the key schedule: bumped before every round after the first */
+            k0 += ORC_PHILOX_W0;
+            k1 += ORC_PHILOX_W1;
+        }
+        const unsigned __int128 p0 = (unsigned __int128)ORC_PHILOX_M0 * c0;
+        const unsigned __int128 p1 = (unsigned __int128)ORC_PHILOX_M1 * c2;
+        const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* Box-Muller: two uniforms u1 in (0, 1], u2 in [0, 1) give two independent standard normals
+ * r cos(2 pi u2) and r sin(2 pi u2), r = sqrt(-2 ln u1).  Here u1 = (top 24 bits + 1) 2^-24
+ * and u2 = (top 24 bits) 2^-24 of two generator words (both exact in fp32). */
+void orc_box_muller(double u1, double u2, double out[2]) {
+    const double two_pi = 2.0 * acos(-1.0);
+    const double r = sqrt(-2.0 * log(u1));
+    out[0] = r * cos(two_pi * u2);
+    out[1] = r * sin(two_pi * u2);
+}
+
+/* The standard normal of flat element e: block e / 4 of the purpose-0 stream, word pair
+ * (e % 4) / 2, the cosine branch for even e and the sine branch for odd e. */
+static double standard_normal(uint64_t seed, uint64_t offset, int64_t e) {
+    const uint64_t ctr[4] = {(uint64_t)(e / 4), offset, 0, 0};
+    const uint64_t key[2] = {seed, 0};
+    uint64_t w[4];
+    orc_philox4x64_10(ctr, key, w);
+    const int q = (int)((e % 4) / 2);
+    const double u1 = ((double)(w[2 * q] >> 40) + 1.0) * 0x1p-24;
+    const double u2 = (double)(w[2 * q + 1] >> 40) * 0x1p-24;
+    double z[2];
+    orc_box_muller(u1, u2, z);
+    return z[e % 2];
+}
+
+/* Fitted Noise statistics ([LG] Sec. 2.6, Eqs. (5)-(6)): per head h,
+ *   mean[h] <- (1 - beta) Mean(h_T) + beta mean[h],  var[h] <- (1 - beta) Variance(h_T) + beta var[h],
+ * with Mean and Variance taken over the head's channels and state dimension (and, reading,
+ * over the batch rows), Variance the population variance (mean squared deviation).  The new
+ * batch's statistics carry weight 1 - beta.  final_state [B][H][P][N]; mean, var [H] in/out. */
+int orc_state_stats_update(const double* fin, int64_t B, int64_t H, int64_t P, int64_t N,
+                           double beta, double* mean, double* var, int out_round) {
+    const int64_t per = P * N;
+    const double count = (double)(B * per);
+    for (int64_t h = 0; h < H; ++h) {
+        double s = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t e = 0; e < per; ++e) s += fin[(b * H + h) * per + e];
+        const double m = s / count;
+        double ss = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t e = 0; e < per; ++e) {
+                const double d = fin[(b * H + h) * per + e] - m;
+                ss += d * d;
+            }
+        const double v = ss / count;
+        mean[h] = orc_round((1.0 - beta) * m + beta * mean[h], out_round);
+        var[h] = orc_round((1.0 - beta) * v + beta * var[h], out_round);
+    }
+    return 0;
+}
+
+/* Noise initial states ([LG] Sec. 2.6): Fitted Noise draws every element of head h
+ * independently from N(mean[h], var[h]); Random Noise (mean == NULL) from N(0, sigma^2).
+ * out [B][H][P][N]. */
+int orc_initial_state_noise(double* out, int64_t B, int64_t H, int64_t P, int64_t N,
+                            const double* mean, const double* var, double sigma, uint64_t seed,
+                            uint64_t offset, int out_round) {
+    const int64_t per = P * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < B * H * per; ++e) {
+        const int64_t h = (e / per) % H;
+        const double z = standard_normal(seed, offset, e);
+        const double v = mean ? mean[h] + sqrt(var[h]) * z : sigma * z;
+        out[e] = orc_round(v, out_round);
+    }
+    return 0;
+}
+
+/* State Passing's occasional reset ([LG] Sec. 2.6): the carried state of row b is zeroed
+ * with probability p, decided by word b % 4 of block b / 4 of the purpose-1 stream: zero iff
+ * its top 32 bits are below floor(p 2^32).  Other rows are copied.  src, dst [B][per];
+ * mask [B] receives 1 for a zeroed row. */
+int orc_state_reset(const double* src, double* dst, uint8_t* mask, int64_t B, int64_t per,
+                    double p, uint64_t seed, uint64_t offset) {
+    double t = floor(p * 4294967296.0);
+    if (t < 0.0) t = 0.0;
+    if (t > 4294967296.0) t = 4294967296.0;
+    const uint64_t threshold = (uint64_t)t;
+    for (int64_t b = 0; b < B; ++b) {
+        const uint64_t ctr[4] = {(uint64_t)(b / 4), offset, 0, 0};
+        const uint64_t key[2] = {seed, 1};
+        uint64_t w[4];
+        orc_philox4x64_10(ctr, key, w);
+        const int zero = (w[b % 4] >> 32) < threshold;
+        mask[b] = (uint8_t)zero;
+        for (int64_t e = 0; e < per; ++e) dst[b * per + e] = zero ? 0.0 : src[b * per + e];
+    }
+    return 0;
+}

@@ -751,6 +751,133 @@ def check_pooled_prefill_ring_example(lib):
     np.testing.assert_array_equal(y[1:], y0)
 
 
+# ------------------------------------------------------------------------------------------
+# initial-state distributions for training (reading notes Sec. 2.6)
+# ------------------------------------------------------------------------------------------
+
+def check_philox_matches_numpy(lib):
+    """Philox4x64-10 against numpy's implementation of the same published generator
+    (numpy.random.Philox): numpy advances its 256-bit counter before each block, so its
+    stream from counter c is the blocks of c + 1, c + 2, ..."""
+    for key, ctr in (([0, 0], [0, 0, 0, 0]), ([5, 7], [0, 0, 0, 0]),
+                     ([2**64 - 1, 12345], [41, 9, 0, 0]), ([0x243F6A8885A308D3, 1], [7, 0, 3, 2**63])):
+        bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
+                              counter=np.array(ctr, dtype=np.uint64))
+        raw = [int(v) for v in bg.random_raw(12)]
+        for i in range(3):
+            c = list(ctr)
+            c[0] += i + 1
+            got = oracle.philox4x64_10(c, key, lib=lib)
+            assert got == raw[4 * i:4 * i + 4], (key, ctr, i, [hex(v) for v in got])
+
+
+def check_box_muller_closed_form(lib):
+    """r = sqrt(-2 ln u1), angle 2 pi u2: u1 = e^(-1/2) gives r = 1, so u2 = 0, 1/4, 1/2, 3/4
+    give the points (1, 0), (0, 1), (-1, 0), (0, -1); u1 = 1 gives the origin."""
+    u1 = math.exp(-0.5)
+    for u2, (c, s_) in ((0.0, (1.0, 0.0)), (0.25, (0.0, 1.0)), (0.5, (-1.0, 0.0)),
+                        (0.75, (0.0, -1.0))):
+        z0, z1 = oracle.box_muller(u1, u2, lib=lib)
+        assert abs(z0 - c) < 1e-12 and abs(z1 - s_) < 1e-12, (u2, z0, z1)
+    z0, z1 = oracle.box_muller(1.0, 0.3, lib=lib)
+    assert z0 == 0.0 and z1 == 0.0
+    z0, z1 = oracle.box_muller(math.exp(-2.0), 0.125, lib=lib)  # r = 2 at 45 degrees
+    assert abs(z0 - math.sqrt(2.0)) < 1e-12 and abs(z1 - math.sqrt(2.0)) < 1e-12
+
+
+def check_random_noise_is_normal(lib):
+    """Random Noise: every element an independent N(0, sigma^2) draw -- the sample mean and
+    variance within their sampling error, a Kolmogorov-Smirnov test against scipy's normal
+    CDF, no correlation between neighbouring elements (the two branches of one pair, and the
+    pairs of one block), a fresh stream for another offset and the same values for the same
+    seed and offset."""
+    from scipy import stats
+    sigma, shape = 2.5, (4, 8, 64, 128)
+    z = oracle.initial_state_noise(shape, sigma=sigma, seed=1234, offset=7, out_dtype="f64",
+                                   lib=lib).ravel()
+    n = z.size
+    assert abs(z.mean()) < 5 * sigma / math.sqrt(n), z.mean()
+    assert abs(z.var() / sigma**2 - 1.0) < 5 * math.sqrt(2.0 / n), z.var()
+    assert stats.kstest(z / sigma, "norm").pvalue > 1e-4
+    for lag in (1, 2, 3, 4):
+        r = np.corrcoef(z[:-lag], z[lag:])[0, 1]
+        assert abs(r) < 5 / math.sqrt(n), (lag, r)
+    z2 = oracle.initial_state_noise(shape, sigma=sigma, seed=1234, offset=8, out_dtype="f64",
+                                    lib=lib).ravel()
+    assert abs(np.corrcoef(z, z2)[0, 1]) < 5 / math.sqrt(n)
+    z3 = oracle.initial_state_noise(shape, sigma=sigma, seed=1234, offset=7, out_dtype="f64",
+                                    lib=lib).ravel()
+    assert np.array_equal(z, z3)
+
+
+def check_fitted_noise_per_head(lib):
+    """Fitted Noise: head h's elements are N(mean[h], var[h]) draws (per-head sample mean and
+    variance within their sampling error)."""
+    B, H, P, N = 4, 6, 32, 64
+    mean = np.array([0.0, 1.5, -3.0, 0.25, 10.0, -0.5])
+    var = np.array([1.0, 0.01, 4.0, 2.5, 0.5, 9.0])
+    z = oracle.initial_state_noise((B, H, P, N), mean=mean, var=var, seed=99, offset=3,
+                                   out_dtype="f64", lib=lib)
+    n = B * P * N
+    for h in range(H):
+        v = z[:, h].ravel()
+        sd = math.sqrt(var[h])
+        assert abs(v.mean() - mean[h]) < 5 * sd / math.sqrt(n), (h, v.mean())
+        assert abs(v.var() / var[h] - 1.0) < 5 * math.sqrt(2.0 / n), (h, v.var())
+
+
+def check_state_stats_update(lib):
+    """Fitted Noise statistics, Eqs. (5)-(6) with beta = 0.1: the new batch's statistics carry
+    weight 0.9 (the page stresses this).  Mean and Variance per head over rows, channels and
+    state dimension against numpy's mean / var (population); repeated updates with one final
+    state from zero statistics follow m (1 - 0.1^k); a constant state has variance 0; a large
+    common offset does not disturb the variance."""
+    rng = _rng(61)
+    B, H, P, N = 3, 4, 8, 16
+    fin = rng.normal(size=(B, H, P, N)) * np.array([1.0, 0.1, 3.0, 0.5])[None, :, None, None] \
+        + np.array([0.0, 2.0, -1.0, 1e4])[None, :, None, None]
+    m0, v0 = rng.normal(size=H), rng.uniform(0.1, 2.0, size=H)
+    m, v = oracle.state_stats_update(fin, m0, v0, beta=0.1, out_dtype="f64", lib=lib)
+    ref_m = fin.mean(axis=(0, 2, 3))
+    ref_v = fin.var(axis=(0, 2, 3))
+    np.testing.assert_allclose(m, 0.9 * ref_m + 0.1 * m0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(v, 0.9 * ref_v + 0.1 * v0, rtol=1e-9, atol=1e-12)
+    m, v = np.zeros(H), np.zeros(H)
+    for k in range(1, 6):
+        m, v = oracle.state_stats_update(fin, m, v, beta=0.1, out_dtype="f64", lib=lib)
+        np.testing.assert_allclose(m, ref_m * (1 - 0.1**k), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(v, ref_v * (1 - 0.1**k), rtol=1e-9, atol=1e-12)
+    const = np.full((2, H, P, N), 3.25)
+    m, v = oracle.state_stats_update(const, np.zeros(H), np.zeros(H), beta=0.1, out_dtype="f64",
+                                     lib=lib)
+    assert np.all(v == 0.0) and np.allclose(m, 0.9 * 3.25, rtol=1e-15)
+
+
+def check_state_reset(lib):
+    """State Passing's reset: p = 0 copies every row, p = 1 zeroes every row; at p = 0.1 the
+    zeroed fraction over 200000 rows lies within five binomial standard deviations, zeroed
+    rows are all zero and the others unchanged; the decisions depend on the row only (the
+    same for a conv-state tensor and an SSM-state tensor with the same seed and offset)."""
+    rng = _rng(62)
+    st = rng.normal(size=(64, 3, 5))
+    d0, m0 = oracle.state_reset(st, p=0.0, seed=5, offset=1, lib=lib)
+    assert m0.sum() == 0 and np.array_equal(d0, st)
+    d1, m1 = oracle.state_reset(st, p=1.0, seed=5, offset=1, lib=lib)
+    assert m1.sum() == 64 and not d1.any()
+    R = 200000
+    big = rng.normal(size=(R, 2)) + 1.0
+    d, m = oracle.state_reset(big, p=0.1, seed=11, offset=4, lib=lib)
+    frac = m.mean()
+    assert abs(frac - 0.1) < 5 * math.sqrt(0.1 * 0.9 / R), frac
+    z = m.astype(bool)
+    assert not d[z].any() and np.array_equal(d[~z], big[~z])
+    _, m_other = oracle.state_reset(rng.normal(size=(R, 7)), p=0.1, seed=11, offset=4, lib=lib)
+    assert np.array_equal(m, m_other)
+    _, m_next = oracle.state_reset(big, p=0.1, seed=11, offset=5, lib=lib)
+    agree = (m == m_next).mean()
+    assert abs(agree - 0.82) < 0.01, agree  # independent draws agree with probability 0.82
+
+
 ALL_CHECKS = [
     check_conv_worked_example_k4,
     check_conv_single_token_k3,
@@ -782,4 +909,10 @@ ALL_CHECKS = [
     check_pooled_prefill_chain_equals_whole,
     check_pooled_prefill_then_decode,
     check_pooled_prefill_ring_example,
+    check_philox_matches_numpy,
+    check_box_muller_closed_form,
+    check_random_noise_is_normal,
+    check_fitted_noise_per_head,
+    check_state_stats_update,
+    check_state_reset,
 ]

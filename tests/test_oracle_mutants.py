@@ -88,6 +88,31 @@ MUTANTS = {
     "scan_bwd_no_reset": ("if (sq && t > 0 && sq[t] != sq[t - 1]) {", "if (0) {"),
     # initial-state gradient: the final state's gradient dropped
     "scan_bwd_no_dF": ("if (alive && dfinal) v += prod * dfinal[(b * H + h) * P * N + e];", "(void)alive;"),
+    # Philox with nine rounds
+    "philox_nine_rounds": ("for (int round = 0; round < 10; ++round) {",
+                           "for (int round = 0; round < 9; ++round) {"),
+    # Philox key schedule not advanced
+    "philox_key_fixed": ("k0 += ORC_PHILOX_W0;", "k0 += 0;"),
+    # Box-Muller with cosine and sine swapped
+    "box_muller_swapped": ("out[0] = r * cos(two_pi * u2);\n    out[1] = r * sin(two_pi * u2);",
+                           "out[0] = r * sin(two_pi * u2);\n    out[1] = r * cos(two_pi * u2);"),
+    # Box-Muller radius without the factor 2
+    "box_muller_radius": ("const double r = sqrt(-2.0 * log(u1));", "const double r = sqrt(-log(u1));"),
+    # both elements of a pair take the cosine branch
+    "noise_pair_shared": ("return z[e % 2];", "return z[0];"),
+    # fitted noise scaled by the variance instead of the standard deviation
+    "fitted_noise_var_scale": ("mean[h] + sqrt(var[h]) * z", "mean[h] + var[h] * z"),
+    # EMA weights the other way round (the common convention the page warns against)
+    "stats_ema_swapped": ("mean[h] = orc_round((1.0 - beta) * m + beta * mean[h], out_round);",
+                          "mean[h] = orc_round(beta * m + (1.0 - beta) * mean[h], out_round);"),
+    # variance without subtracting the mean
+    "stats_var_uncentred": ("const double d = fin[(b * H + h) * per + e] - m;",
+                            "const double d = fin[(b * H + h) * per + e];"),
+    # sample variance instead of the population variance
+    "stats_var_n_minus_1": ("const double v = ss / count;", "const double v = ss / (count - 1.0);"),
+    # reset decision inverted (zero with probability 1 - p)
+    "reset_inverted": ("const int zero = (w[b % 4] >> 32) < threshold;",
+                       "const int zero = (w[b % 4] >> 32) >= threshold;"),
     # bf16 rounding keeps 9 bits
     "bf16_nine_bits": ("int q = e - 8;", "int q = e - 9;"),
     # bf16 rounding truncates instead of nearest-even
