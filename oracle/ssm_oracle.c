@@ -488,8 +488,7 @@ void orc_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint6
 }
 
 /* Box-Muller: two uniforms u1 in (0, 1], u2 in [0, 1) give two independent standard normals
- * r cos(2 pi u2) and r sin(2 pi u2), r = sqrt(-2 ln u1).  Here u1 = (top 24 bits + 1) 2^-24
- * and u2 = (top 24 bits) 2^-24 of two generator words (both exact in fp32). */
+ * r cos(2 pi u2) and r sin(2 pi u2), r = sqrt(-2 ln u1). */
 void orc_box_muller(double u1, double u2, double out[2]) {
     const double two_pi = 2.0 * acos(-1.0);
     const double r = sqrt(-2.0 * log(u1));
@@ -497,16 +496,18 @@ void orc_box_muller(double u1, double u2, double out[2]) {
     out[1] = r * sin(two_pi * u2);
 }
 
-/* The standard normal of flat element e: block e / 4 of the purpose-0 stream, word pair
- * (e % 4) / 2, the cosine branch for even e and the sine branch for odd e. */
+/* The standard normal of flat element e: block e / 8 of the purpose-0 stream gives four
+ * pairs, pair j = (e % 8) / 2 from word j: u1 = (bits 40-63 + 1) 2^-24, u2 = (bits 8-31)
+ * 2^-24 (24 bits from each 32-bit half; both exact in fp32); the cosine branch for even e
+ * and the sine branch for odd e. */
 static double standard_normal(uint64_t seed, uint64_t offset, int64_t e) {
-    const uint64_t ctr[4] = {(uint64_t)(e / 4), offset, 0, 0};
+    const uint64_t ctr[4] = {(uint64_t)(e / 8), offset, 0, 0};
     const uint64_t key[2] = {seed, 0};
     uint64_t w[4];
     orc_philox4x64_10(ctr, key, w);
-    const int q = (int)((e % 4) / 2);
-    const double u1 = ((double)(w[2 * q] >> 40) + 1.0) * 0x1p-24;
-    const double u2 = (double)(w[2 * q + 1] >> 40) * 0x1p-24;
+    const uint64_t word = w[(e % 8) / 2];
+    const double u1 = ((double)(word >> 40) + 1.0) * 0x1p-24;
+    const double u2 = (double)((word >> 8) & 0xFFFFFFu) * 0x1p-24;
     double z[2];
     orc_box_muller(u1, u2, z);
     return z[e % 2];

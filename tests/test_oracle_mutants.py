@@ -100,6 +100,9 @@ MUTANTS = {
     "box_muller_radius": ("const double r = sqrt(-2.0 * log(u1));", "const double r = sqrt(-log(u1));"),
     # both elements of a pair take the cosine branch
     "noise_pair_shared": ("return z[e % 2];", "return z[0];"),
+    # the last two pairs of a block reuse the first two words
+    "noise_word_reused": ("const uint64_t word = w[(e % 8) / 2];",
+                          "const uint64_t word = w[(e % 4) / 2];"),
     # fitted noise scaled by the variance instead of the standard deviation
     "fitted_noise_var_scale": ("mean[h] + sqrt(var[h]) * z", "mean[h] + var[h] * z"),
     # EMA weights the other way round (the common convention the page warns against)
