@@ -100,8 +100,9 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     """Achieved bandwidth of the other entry points on their workloads: the unfused conv at the
     1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
     1.3B-like prefill with packed sequences, the 370M-like prefill, the 131072-token
-    780M-like call, the chunked prefill on the decode pools, and the backward entry points
-    (conv with state gradients, the scan's initial-state gradient) at the 1.3B shape.  Seeded
+    780M-like call, the chunked prefill on the decode pools, the initial-state distributions
+    for training, and the backward entry points (conv with state gradients, the scan's
+    initial-state gradient) at the 1.3B shape.  Seeded
     inputs drawn on the GPU (timing only; parity is the test suite's job)."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
@@ -209,6 +210,28 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     rep("conv_scan_fwd_pooled", f"{R} requests x {Lp}-token chunk into {S}-slot pools (1.3B dims, "
         "ring layout)", ms, R * Lp, nb)
     del conv_pool, ssm_pool, xp, yp, ws
+
+    # initial-state distributions for training on 64 carried SSM states of the 1.3B layer
+    # (64 x 64 heads x 64 x 128 fp32 = 128 MiB): the Fitted Noise statistics update, Fitted
+    # Noise sampling, and State Passing's reset (out of place)
+    Rs = 64
+    g.manual_seed(18)
+    st = torch.randn(Rs, H, P, N, generator=g, device=dev)
+    mean, var = torch.zeros(H, device=dev), torch.ones(H, device=dev)
+    nbs = Rs * H * P * N * 4
+    ms = _time_gpu(torch, lambda: ssm.state_stats_update(st, mean, var, beta=0.1), 10)
+    rep("state_stats_update", f"{Rs} x H{H}x{P} N{N} fp32 final states, per-head mean / variance",
+        ms, Rs, nbs)
+    noise = torch.empty_like(st)
+    ms = _time_gpu(torch, lambda: ssm.initial_state_noise(Rs, H, P, N, mean=mean, var=var, seed=1,
+                                                          offset=2, out=noise), 10)
+    rep("initial_state_noise", f"{Rs} x H{H}x{P} N{N} fp32, Fitted Noise (Philox4x64-10)", ms, Rs,
+        nbs)
+    kept = torch.empty_like(st)
+    mask = torch.empty(Rs, dtype=torch.uint8, device=dev)
+    ms = _time_gpu(torch, lambda: ssm.state_reset(st, p=0.1, seed=1, offset=3, out=kept, mask=mask), 10)
+    rep("state_reset", f"{Rs} x H{H}x{P} N{N} fp32, p 0.1, out of place", ms, Rs, 2 * nbs)
+    del st, noise, kept
 
     # backward of the unfused conv at the 1.3B shape, with state gradients
     s = workloads.shape_of("layer1p3b")

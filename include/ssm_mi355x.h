@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 /* hipStream_t is `struct ihipStream_t*`; this typedef is the same type. */
 struct ihipStream_t;
@@ -303,6 +303,58 @@ ssm_status_t ssm_scan_bwd_initial_state(const float* dt, const float* A, const v
                                         int64_t batch, int64_t seqlen, int64_t nheads,
                                         int64_t headdim, int64_t ngroups, int64_t dstate,
                                         ssm_dtype_t dtype, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Initial-state distributions for training ([LG] Sec. 2.6: the four interventions -- Random
+ * Noise, Fitted Noise, State Passing, TBTT -- and the Fitted Noise update, Eqs. (5)-(6)).
+ * Random numbers: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011), key (seed, purpose), counter (block, offset, 0, 0).  The same
+ * (seed, offset) always gives the same draws; a training step passes its own offset.
+ * Gaussian initial states are for training only: [LG] evaluates from the zero state.
+ * ------------------------------------------------------------------------------------- */
+
+/* ssm_state_stats_update -- the Fitted Noise statistics, per head h:
+ *   mean[h] <- (1 - beta) Mean(h_T) + beta mean[h],  var[h] <- (1 - beta) Var(h_T) + beta var[h]
+ * ([LG] Eqs. (5)-(6), beta = 0.1 there: the new batch carries weight 1 - beta).  Mean and Var
+ * are taken over the head's batch rows, channels and state dimension; Var is the population
+ * variance (mean squared deviation), both accumulated in double (two passes).
+ *   final_state  [batch, nheads, headdim, dstate]   fp32
+ *   mean, var    [nheads]                           fp32, in / out (the caller initialises)
+ * batch = 0: no-op (nothing observed).  Deterministic (fixed reduction order).
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_state_stats_update(const float* final_state, int64_t batch, int64_t nheads,
+                                    int64_t headdim, int64_t dstate, float beta, float* mean,
+                                    float* var, ssm_stream_t stream);
+
+/* ssm_initial_state_noise -- noise initial states: with mean and var (Fitted Noise) element
+ * (b, h, p, n) is drawn from N(mean[h], var[h]); with both NULL (Random Noise) from
+ * N(0, sigma^2).  Element e (flat index) reads word j = (e % 8) / 2 of Philox block e / 8
+ * (purpose 0): u1 = (bits 40-63, plus 1) 2^-24 in (0, 1], u2 = (bits 8-31) 2^-24 in [0, 1),
+ * r = sqrt(-2 ln u1) (Box-Muller), and z = r cos(2 pi u2) for even e, r sin(2 pi u2) for
+ * odd e.  fp32 arithmetic.
+ *   out       [batch, nheads, headdim, dstate]   fp32
+ *   mean, var [nheads] fp32 (var >= 0), or both NULL
+ * batch = 0: no-op.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_initial_state_noise(float* out, int64_t batch, int64_t nheads, int64_t headdim,
+                                     int64_t dstate, const float* mean, const float* var,
+                                     float sigma, uint64_t seed, uint64_t offset,
+                                     ssm_stream_t stream);
+
+/* ssm_state_reset -- State Passing's occasional reset ([LG] Sec. 2.6): row b of a carried
+ * state (any tensor whose leading dimension is the batch row: the SSM state, the conv
+ * state) is zeroed with probability p, else copied.  The decision for row b is word b % 4 of
+ * Philox block b / 4 (purpose 1): zero iff its top 32 bits < floor(p 2^32) (p clipped to
+ * [0, 1]).  It depends only on (seed, offset, b), so the SSM and conv states of one row,
+ * reset with the same seed and offset, are zeroed together.
+ *   src        [batch, row_bytes]   any type, row_bytes even, 2-byte aligned
+ *   dst        [batch, row_bytes]   may alias src (then kept rows are not rewritten)
+ *   reset_mask [batch] uint8, or NULL: 1 for a zeroed row
+ * batch = 0: no-op.  p NaN: SSM_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_state_reset(const void* src, void* dst, uint8_t* reset_mask, int64_t batch,
+                             int64_t row_bytes, double p, uint64_t seed, uint64_t offset,
+                             ssm_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Measurement support (does not change any result).  When enabled, every launch of the

@@ -36,7 +36,7 @@ class SSMError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it first (python -m ssm_sequence_models_amd.build "
+            f"{LIB_PATH} is missing: build it first (python ssm_sequence_models_amd/build.py "
             "or __graft_entry__.build()); there is no non-HIP fallback")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32p, fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
@@ -67,12 +67,18 @@ def _load():
     lib.ssm_conv_scan_fwd_pooled.argtypes = [vp, fp, fp, fp, fp, vp, fp, i32p, i32p, i32p, vp,
                                              i64, i64, i64, i64, i64, i64, i64, i64, i64, ci, ci,
                                              vp, ctypes.c_size_t, vp]
+    u64 = ctypes.c_uint64
+    lib.ssm_state_stats_update.argtypes = [fp, i64, i64, i64, i64, ctypes.c_float, fp, fp, vp]
+    lib.ssm_initial_state_noise.argtypes = [fp, i64, i64, i64, i64, fp, fp, ctypes.c_float, u64,
+                                            u64, vp]
+    lib.ssm_state_reset.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, u64, u64, vp]
     lib.ssm_timing_enable.argtypes = [ci]
     lib.ssm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
               "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
-              "ssm_conv_scan_fwd_pooled", "ssm_timing_enable",
+              "ssm_conv_scan_fwd_pooled", "ssm_state_stats_update",
+              "ssm_initial_state_noise", "ssm_state_reset", "ssm_timing_enable",
               "ssm_timing_read"):
         getattr(lib, f).restype = ci
     return lib
@@ -203,6 +209,55 @@ def conv_scan_fwd_pooled_workspace_size(batch, seqlen, nheads, headdim, ngroups,
     return int(_lib.ssm_conv_scan_fwd_pooled_workspace_size(batch, seqlen, nheads, headdim, ngroups,
                                                             dstate, width, code))
 
+
+def state_stats_update(final_state, mean, var, beta=0.1):
+    """Fitted Noise statistics (length-generalization notes Sec. 2.6, Eqs. (5)-(6)): per head,
+    mean <- (1 - beta) Mean(final_state) + beta mean, var likewise with the population
+    variance, over batch rows, channels and state dimension.  final_state [b, H, P, N] fp32;
+    mean, var [H] fp32, updated in place and returned."""
+    b, H, P, N = final_state.shape
+    _need(final_state, "final_state", torch.float32)
+    _need(mean, "mean", torch.float32, (H,))
+    _need(var, "var", torch.float32, (H,))
+    _check("ssm_state_stats_update", _lib.ssm_state_stats_update(
+        _ptr(final_state), b, H, P, N, float(beta), _ptr(mean), _ptr(var), _stream()))
+    return mean, var
+
+
+def initial_state_noise(batch, nheads, headdim, dstate, mean=None, var=None, sigma=1.0, seed=0,
+                        offset=0, out=None, device="cuda"):
+    """Noise initial states (Sec. 2.6): Fitted Noise N(mean[h], var[h]) per head when mean and
+    var [H] are given, Random Noise N(0, sigma^2) otherwise, drawn from Philox4x64-10 with
+    (seed, offset).  Returns out [batch, H, P, N] fp32."""
+    shape = (batch, nheads, headdim, dstate)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=device)
+    _need(out, "out", torch.float32, shape)
+    _need(mean, "mean", torch.float32, (nheads,))
+    _need(var, "var", torch.float32, (nheads,))
+    _check("ssm_initial_state_noise", _lib.ssm_initial_state_noise(
+        _ptr(out), batch, nheads, headdim, dstate, _ptr(mean), _ptr(var), float(sigma),
+        int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), _stream()))
+    return out
+
+
+def state_reset(state, p=0.1, seed=0, offset=0, out=None, mask=None):
+    """State Passing's occasional reset (Sec. 2.6): each row of state [b, ...] (any dtype) is
+    zeroed with probability p, decided by (seed, offset, row) alone.  out may be state itself.
+    Returns (out, mask [b] uint8, 1 = zeroed)."""
+    b = state.shape[0]
+    _need(state, "state")
+    if out is None:
+        out = torch.empty_like(state)
+    _need(out, "out", state.dtype, tuple(state.shape))
+    if mask is None:
+        mask = torch.empty(b, dtype=torch.uint8, device=state.device)
+    _need(mask, "mask", torch.uint8, (b,))
+    row_bytes = state[0].numel() * state.element_size() if b > 0 else 0
+    _check("ssm_state_reset", _lib.ssm_state_reset(
+        _ptr(state), _ptr(out), _ptr(mask), b, row_bytes, float(p), int(seed) & (2**64 - 1),
+        int(offset) & (2**64 - 1), _stream()))
+    return out, mask
 
 def conv1d_bwd(x, weight, bias, dout, initial_state=None, dfinal_state=None, seq_idx=None,
                activation=None, dx=None, dinitial_state=None, dweight=None, dbias=None,

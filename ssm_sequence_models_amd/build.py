@@ -1,6 +1,7 @@
 """Build the HIP library libssm_mi355x.so in-tree for gfx950 (hipcc cross-compiles; no GPU
-needed).  Used by ``__graft_entry__.build()`` and runnable as ``python -m
-ssm_sequence_models_amd.build``."""
+needed).  Used by ``__graft_entry__.build()`` and runnable as ``python
+ssm_sequence_models_amd/build.py``; it imports nothing from the package, whose import loads
+the library this file builds."""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -13,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_mi355x.so")
-SOURCES = ["abi.hip", "bwd.hip", "conv.hip", "pool.hip", "recurrent.hip", "ssd.hip"]
+SOURCES = ["abi.hip", "bwd.hip", "conv.hip", "init_state.hip", "pool.hip", "recurrent.hip", "ssd.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code (hipcc's host pass

@@ -1,6 +1,7 @@
 // abi.hip -- the C ABI (include/ssm_mi355x.h): argument checks, path selection, launches.
 // Host code only; every computation runs in the kernels of conv.hip, recurrent.hip and
 // ssd.hip.  Nothing here allocates device memory, synchronises, throws or prints.
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -601,6 +602,84 @@ ssm_status_t ssm_scan_bwd_initial_state(const float* dt, const float* A, const v
     return hip_status(ssm::launch_scan_bwd_h0(dt, A, C, seq_idx, dy, dfinal_state, dinitial_state,
                                               batch, seqlen, nheads, headdim, ngroups, dstate,
                                               dtype, reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+namespace {
+ssm_status_t check_state_dims(const char* fn, int64_t batch, int64_t nheads, int64_t headdim,
+                              int64_t dstate) {
+    if (batch < 0) return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": negative batch");
+    if (nheads < 1 || headdim < 1 || dstate < 1)
+        return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": nheads, headdim, dstate must be >= 1");
+    return SSM_OK;
+}
+}  // namespace
+
+ssm_status_t ssm_state_stats_update(const float* final_state, int64_t batch, int64_t nheads,
+                                    int64_t headdim, int64_t dstate, float beta, float* mean,
+                                    float* var, ssm_stream_t stream) {
+    const char* fn = "ssm_state_stats_update";
+    ssm_status_t st = check_state_dims(fn, batch, nheads, headdim, dstate);
+    if (st != SSM_OK) return st;
+    if (!(beta == beta)) return fail(SSM_ERR_INVALID_ARG, "ssm_state_stats_update: beta is NaN");
+    const bool rows = batch > 0;
+    st = check_ptrs(fn, {{"final_state", final_state, rows, 4},
+                         {"mean", mean, rows, 4},
+                         {"var", var, rows, 4}});
+    if (st != SSM_OK) return st;
+    if (!rows) return ok();
+    if (nheads > 0x7FFFFFFF)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_state_stats_update: too many heads");
+    return hip_status(ssm::launch_state_stats(final_state, batch, nheads, headdim * dstate,
+                                              static_cast<double>(beta), mean, var,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+ssm_status_t ssm_initial_state_noise(float* out, int64_t batch, int64_t nheads, int64_t headdim,
+                                     int64_t dstate, const float* mean, const float* var,
+                                     float sigma, uint64_t seed, uint64_t offset,
+                                     ssm_stream_t stream) {
+    const char* fn = "ssm_initial_state_noise";
+    ssm_status_t st = check_state_dims(fn, batch, nheads, headdim, dstate);
+    if (st != SSM_OK) return st;
+    if ((mean == nullptr) != (var == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, "ssm_initial_state_noise: give both mean and var, or neither");
+    const bool rows = batch > 0;
+    st = check_ptrs(fn, {{"out", out, rows, 4}, {"mean", mean, false, 4}, {"var", var, false, 4}});
+    if (st != SSM_OK) return st;
+    if (!rows) return ok();
+    const int64_t n = batch * nheads * headdim * dstate;
+    if ((n + 7) / 8 > static_cast<int64_t>(0xFFFFFFFFll) * 256)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_initial_state_noise: tensor too large");
+    return hip_status(ssm::launch_state_noise(out, n, nheads, headdim * dstate, mean, var, sigma,
+                                              seed, offset, reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+ssm_status_t ssm_state_reset(const void* src, void* dst, uint8_t* reset_mask, int64_t batch,
+                             int64_t row_bytes, double p, uint64_t seed, uint64_t offset,
+                             ssm_stream_t stream) {
+    const char* fn = "ssm_state_reset";
+    if (batch < 0 || row_bytes < 0 || (row_bytes & 1))
+        return fail(SSM_ERR_INVALID_ARG, "ssm_state_reset: need batch >= 0 and an even row_bytes >= 0");
+    if (!(p == p)) return fail(SSM_ERR_INVALID_ARG, "ssm_state_reset: p is NaN");
+    const bool rows = batch > 0;
+    ssm_status_t st = check_ptrs(fn, {{"src", src, rows && row_bytes > 0, 2},
+                                      {"dst", dst, rows && row_bytes > 0, 2}});
+    if (st != SSM_OK) return st;
+    if (!rows) return ok();
+    // threshold = floor(p 2^32), p clipped to [0, 1] (the scaling by 2^32 is exact)
+    double t = std::floor((p < 0.0 ? 0.0 : p > 1.0 ? 1.0 : p) * 4294967296.0);
+    const uint64_t threshold = static_cast<uint64_t>(t);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
+    const int unit = ((a & 15) == 0 && row_bytes % 16 == 0) ? 16
+                     : ((a & 3) == 0 && row_bytes % 4 == 0) ? 4 : 2;
+    if (ssm::state_reset_blocks(batch, row_bytes, unit) > 0x7FFFFFFFll)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_state_reset: tensor too large");
+    return hip_status(ssm::launch_state_reset(src, dst, reset_mask, batch, row_bytes, unit,
+                                              threshold, seed, offset,
+                                              reinterpret_cast<hipStream_t>(stream)),
                       fn);
 }
 

@@ -212,6 +212,15 @@ hipError_t launch_pool_scatter(void* conv_pool, float* ssm_pool, const int32_t* 
                                int64_t batch, int64_t L, int64_t C, int64_t state_len,
                                int64_t ssm_per, int64_t n_slots, ssm_dtype_t dtype,
                                hipStream_t stream);
+hipError_t launch_state_stats(const float* fin, int64_t B, int64_t H, int64_t per, double beta,
+                              float* mean, float* var, hipStream_t stream);
+hipError_t launch_state_noise(float* out, int64_t n, int64_t H, int64_t per, const float* mean,
+                              const float* var, float sigma, uint64_t seed, uint64_t offset,
+                              hipStream_t stream);
+int64_t state_reset_blocks(int64_t B, int64_t row_bytes, int unit);
+hipError_t launch_state_reset(const void* src, void* dst, uint8_t* mask, int64_t B,
+                              int64_t row_bytes, int unit, uint64_t threshold, uint64_t seed,
+                              uint64_t offset, hipStream_t stream);
 hipError_t launch_copy_or_zero_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_copy_or_zero_bytes(void* dst, const void* src, int64_t nbytes, hipStream_t s);
 

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
               "ssm_step", "ssm_scan_workspace_size", "ssm_abi_version", "ssm_status_string",
               "ssm_last_error", "ssm_conv1d_bwd", "ssm_conv1d_bwd_workspace_size",
               "ssm_scan_bwd_initial_state", "ssm_conv_scan_fwd_pooled",
-              "ssm_conv_scan_fwd_pooled_workspace_size"):
+              "ssm_conv_scan_fwd_pooled_workspace_size", "ssm_state_stats_update",
+              "ssm_initial_state_noise", "ssm_state_reset"):
         assert f in names
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
     for code in range(6):
         assert lib.ssm_status_string(code)
 
@@ -122,6 +123,17 @@ def test_argument_errors_return_status(lib):
     assert pooled(dummy, None, 4, 1 << 30) == 1 and b"ssm_state is NULL" in lib.ssm_last_error()
     assert pooled(None, dummy, 4, 1 << 30) == 1 and b"y is NULL" in lib.ssm_last_error()
     assert pooled(dummy, dummy, 4, 16) == 4
+    # initial-state distributions: NULL mean; mean without var; odd row size; NaN p; NaN beta
+    assert lib.ssm_state_stats_update(dummy, 2, 4, 8, 16, 0.1, None, dummy, None) == 1
+    assert lib.ssm_state_stats_update(dummy, 2, 4, 8, 16, float("nan"), dummy, dummy, None) == 1
+    assert lib.ssm_initial_state_noise(dummy, 2, 4, 8, 16, dummy, None, 1.0, 0, 0, None) == 1
+    assert lib.ssm_initial_state_noise(_c(258), 2, 4, 8, 16, None, None, 1.0, 0, 0, None) == 3
+    assert lib.ssm_state_reset(dummy, dummy, None, 4, 7, 0.1, 0, 0, None) == 1
+    assert lib.ssm_state_reset(dummy, dummy, None, 4, 8, float("nan"), 0, 0, None) == 1
+    assert lib.ssm_state_reset(_c(257), dummy, None, 4, 8, 0.1, 0, 0, None) == 3
+    assert lib.ssm_state_stats_update(None, 0, 4, 8, 16, 0.1, None, None, None) == 0
+    assert lib.ssm_initial_state_noise(None, 0, 4, 8, 16, None, None, 1.0, 0, 0, None) == 0
+    assert lib.ssm_state_reset(None, None, None, 0, 8, 0.1, 0, 0, None) == 0
     # zero-sized work is a no-op that succeeds without touching the device
     assert lib.ssm_conv1d_update(None, None, None, None, None, None, None, 0, 8, 1, 4, 3, 4, 1,
                                  0, None) == 0
