@@ -24,6 +24,8 @@ Definitions followed (page title and section):
                     (Sec. 2.5), with the final state's gradient added (Sec. 2.6);
   * conv_scan_fwd_pooled  conv_scan_fwd with its states taken from and returned to the decode
                     pools (tutorial ch. 7: the physical cache, circular mode, state indices);
+  * scan_fwd_vdecay the scan with a diagonal (per-state-dimension) transition, Eq. (1) with
+                    A_t = diag(a_t), from log gates or from dt times a per-dimension rate;
   * state_stats_update, initial_state_noise, state_reset  the initial-state distributions of
                     the reading notes' Sec. 2.6 (Fitted Noise Eqs. (5)-(6), Random Noise, State
                     Passing's reset), drawing from Philox4x64-10 (Salmon et al., SC 2011).
@@ -84,6 +86,8 @@ def load_library(path: str):
     for f in ("orc_conv1d_fwd", "orc_conv1d_update", "orc_scan_fwd", "orc_step",
               "orc_conv1d_bwd", "orc_scan_bwd_h0"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.orc_scan_fwd_vdecay.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _i64,
+                                        _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     _u64 = ctypes.c_uint64
     _u64p = ctypes.POINTER(ctypes.c_uint64)
     lib.orc_philox4x64_10.argtypes = [_u64p, _u64p, _u64p]
@@ -384,3 +388,26 @@ def state_reset(state, p=0.1, seed=0, offset=0, lib=None):
     lib.orc_state_reset(_p(src), _p(dst), mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), B,
                         per, float(p), int(seed), int(offset))
     return dst, mask
+
+
+def scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=None, A_vec=None, init_state=None, seq_idx=None,
+                    out_dtype="f64", state_dtype="f64", lib=None):
+    """The scan with a diagonal transition A_t = diag(a_t) (reading notes Sec. 2.1 Eq. (1),
+    Sec. 2.5).  x [B, L, H, P]; dt [B, L, H] or None (= 1); Bm, Cm [B, L, G, N]; log a_t from
+    log_decay [B, L, H, N], else dt * A_vec [H, N].
+
+    Returns (y [B, L, H, P], final_state [B, H, P, N])."""
+    lib = lib or _get()
+    x, dt, Bm, Cm, ld, Av, init_state = (_f64(v) for v in (x, dt, Bm, Cm, log_decay, A_vec,
+                                                             init_state))
+    seq_idx = _i32(seq_idx)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    assert (ld is None) != (Av is None), "give log_decay or A_vec"
+    assert ld is not None or dt is not None, "A_vec needs dt"
+    y = np.zeros((B, L, H, P))
+    fin = np.zeros((B, H, P, N))
+    lib.orc_scan_fwd_vdecay(_p(x), _p(dt), _p(ld), _p(Av), _p(Bm), _p(Cm), _p(init_state),
+                            _p(fin), _p(seq_idx, _ip), _p(y), B, L, H, P, G, N, ROUND[out_dtype],
+                            ROUND[state_dtype])
+    return y, fin

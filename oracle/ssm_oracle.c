@@ -578,3 +578,60 @@ int orc_state_reset(const double* src, double* dst, uint8_t* mask, int64_t B, in
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------------
+ * Selective scan with a diagonal (per-state-dimension) transition ([LG] Sec. 2.1 Eq. (1)
+ * with A_t = diag(a_t); Sec. 2.5: the diagonal case, its transition taken from log
+ * coefficients).  For every (b, h), with g = h / (H / G), per state dimension n:
+ *
+ *   log a_t[n] = log_decay[b][t][h][n]       when log_decay is given (data-dependent gates),
+ *              = dt[b][t][h] * A_vec[h][n]    otherwise (a fixed rate per state dimension);
+ *   u_t = dt[b][t][h] (1 when dt is NULL)
+ *   state[p][n] = a_t[n] state[p][n] + u_t x[b][t][h][p] Bm[b][t][g][n]
+ *   y[b][t][h][p] = round(sum_n Cm[b][t][g][n] state[p][n])
+ *
+ * from h_{-1} (0 if absent), zeroed where seq_idx changes, final state returned.
+ * Layouts as orc_scan_fwd; log_decay [B][L][H][N]; A_vec [H][N].
+ * ------------------------------------------------------------------------------------- */
+int orc_scan_fwd_vdecay(const double* x, const double* dt, const double* log_decay,
+                        const double* A_vec, const double* Bm, const double* Cm,
+                        const double* init_state, double* final_state, const int32_t* seq_idx,
+                        double* y, int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                        int64_t N, int y_round, int state_round) {
+    const int64_t heads_per_group = H / G;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t grp = h / heads_per_group;
+            double* hs = (double*)malloc(sizeof(double) * (size_t)(P * N));
+            double* an = (double*)malloc(sizeof(double) * (size_t)N);
+            for (int64_t e = 0; e < P * N; ++e)
+                hs[e] = init_state ? init_state[(b * H + h) * P * N + e] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                if (seq_idx && t > 0 && seq_idx[b * L + t] != seq_idx[b * L + t - 1])
+                    for (int64_t e = 0; e < P * N; ++e) hs[e] = 0.0;
+                const double u = dt ? dt[(b * L + t) * H + h] : 1.0;
+                for (int64_t n = 0; n < N; ++n)
+                    an[n] = log_decay ? exp(log_decay[((b * L + t) * H + h) * N + n])
+                                      : exp(u * A_vec[h * N + n]);
+                const double* xt = x + ((b * L + t) * H + h) * P;
+                const double* Bt = Bm + ((b * L + t) * G + grp) * N;
+                const double* Ct = Cm + ((b * L + t) * G + grp) * N;
+                for (int64_t p = 0; p < P; ++p) {
+                    double out = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        hs[p * N + n] = an[n] * hs[p * N + n] + u * xt[p] * Bt[n];
+                        out += Ct[n] * hs[p * N + n];
+                    }
+                    y[((b * L + t) * H + h) * P + p] = orc_round(out, y_round);
+                }
+            }
+            if (final_state)
+                for (int64_t e = 0; e < P * N; ++e)
+                    final_state[(b * H + h) * P * N + e] = orc_round(hs[e], state_round);
+            free(an);
+            free(hs);
+        }
+    }
+    return 0;
+}

@@ -878,6 +878,114 @@ def check_state_reset(lib):
     assert abs(agree - 0.82) < 0.01, agree  # independent draws agree with probability 0.82
 
 
+# ------------------------------------------------------------------------------------------
+# the scan with a diagonal (per-state-dimension) transition (reading notes Sec. 2.1, 2.5)
+# ------------------------------------------------------------------------------------------
+
+def _vdecay_inputs(seed, B=2, L=9, H=4, P=3, N=5, G=2):
+    rng = _rng(seed)
+    x = rng.normal(size=(B, L, H, P))
+    dt = rng.uniform(0.05, 0.6, size=(B, L, H))
+    Bm = rng.normal(size=(B, L, G, N))
+    Cm = rng.normal(size=(B, L, G, N))
+    gate = -rng.uniform(0.01, 1.5, size=(B, L, H, N))
+    h0 = rng.normal(size=(B, H, P, N))
+    return x, dt, Bm, Cm, gate, h0
+
+
+def check_vdecay_bruteforce_eq4(lib):
+    """Eq. (4) with diagonal transitions, written as explicit per-dimension products: h_t[p, n]
+    = sum_s (prod_{s<tau<=t} a_tau[n]) u_s x_s[p] B_s[n] + (prod_{tau<=t} a_tau[n]) h_{-1}[p, n],
+    y_t = C_t . h_t (G = 2 groups)."""
+    x, dt, Bm, Cm, gate, h0 = _vdecay_inputs(71)
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    y, fin = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=gate, init_state=h0, lib=lib)
+    a = np.exp(gate)
+    ref_y = np.zeros_like(y)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // G)
+            for t in range(L):
+                st = np.prod(a[b, :t + 1, h, :], axis=0)[None, :] * h0[b, h]
+                for s_ in range(t + 1):
+                    prod = np.prod(a[b, s_ + 1:t + 1, h, :], axis=0)
+                    st = st + prod[None, :] * dt[b, s_, h] * np.outer(x[b, s_, h], Bm[b, s_, g])
+                ref_y[b, t, h] = st @ Cm[b, t, g]
+                if t == L - 1:
+                    np.testing.assert_allclose(fin[b, h], st, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y, ref_y, rtol=1e-12, atol=1e-12)
+
+
+def check_vdecay_uniform_gate_is_scalar_scan(lib):
+    """A gate equal in every state dimension, log a_t[n] = dt_t A_h, is the scalar-decay scan."""
+    x, dt, Bm, Cm, _, h0 = _vdecay_inputs(72)
+    H, N = x.shape[2], Bm.shape[3]
+    A = -_rng(73).uniform(0.2, 3.0, size=H)
+    gate = np.repeat((dt * A[None, None, :])[..., None], N, axis=3)
+    y, fin = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=gate, init_state=h0, lib=lib)
+    ry, rfin = oracle.scan_fwd(x, dt, A, Bm, Cm, init_state=h0, lib=lib)
+    np.testing.assert_allclose(y, ry, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(fin, rfin, rtol=1e-13, atol=1e-13)
+
+
+def check_vdecay_rate_form_is_gate_form(lib):
+    """The per-dimension rate form (a_t[n] = exp(dt_t A[h, n])) is the gate form with
+    log a = dt A."""
+    x, dt, Bm, Cm, _, h0 = _vdecay_inputs(74)
+    H, N = x.shape[2], Bm.shape[3]
+    Av = -_rng(75).uniform(0.1, 4.0, size=(H, N))
+    y1, f1 = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, A_vec=Av, init_state=h0, lib=lib)
+    y2, f2 = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=dt[..., None] * Av[None, None],
+                                    init_state=h0, lib=lib)
+    np.testing.assert_allclose(y1, y2, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(f1, f2, rtol=1e-14, atol=1e-14)
+
+
+def check_vdecay_constant_rates_lfilter(lib):
+    """Time-constant decays a_n and no dt: every (p, n) is a first-order IIR filter, so the
+    state is scipy.signal.lfilter([1], [1, -a_n], x_t[p] B_t[n]) started from a_n h_{-1}."""
+    from scipy.signal import lfilter
+    rng = _rng(76)
+    B, L, H, P, N, G = 1, 40, 2, 3, 6, 1
+    x = rng.normal(size=(B, L, H, P))
+    Bm, Cm = rng.normal(size=(B, L, G, N)), rng.normal(size=(B, L, G, N))
+    an = rng.uniform(0.3, 0.99, size=(H, N))
+    gate = np.broadcast_to(np.log(an)[None, None], (B, L, H, N)).copy()
+    h0 = rng.normal(size=(B, H, P, N))
+    y, fin = oracle.scan_fwd_vdecay(x, None, Bm, Cm, log_decay=gate, init_state=h0, lib=lib)
+    for h in range(H):
+        st = np.zeros((L, P, N))
+        for p in range(P):
+            for n in range(N):
+                st[:, p, n] = lfilter([1.0], [1.0, -an[h, n]], x[0, :, h, p] * Bm[0, :, 0, n],
+                                      zi=[an[h, n] * h0[0, h, p, n]])[0]
+        np.testing.assert_allclose(y[0, :, h], np.einsum("tpn,tn->tp", st, Cm[0, :, 0]),
+                                   rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(fin[0, h], st[-1], rtol=1e-11, atol=1e-11)
+
+
+def check_vdecay_chunks_and_resets(lib):
+    """Chunk continuation (final state of A = initial state of B, every split point) and
+    packed sequences (a row cut by seq_idx = separate rows, each from zero)."""
+    x, dt, Bm, Cm, gate, h0 = _vdecay_inputs(77, B=1, L=12)
+    y, fin = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=gate, init_state=h0, lib=lib)
+    for cut in range(1, 12):
+        ya, fa = oracle.scan_fwd_vdecay(x[:, :cut], dt[:, :cut], Bm[:, :cut], Cm[:, :cut],
+                                        log_decay=gate[:, :cut], init_state=h0, lib=lib)
+        yb, fb = oracle.scan_fwd_vdecay(x[:, cut:], dt[:, cut:], Bm[:, cut:], Cm[:, cut:],
+                                        log_decay=gate[:, cut:], init_state=fa, lib=lib)
+        np.testing.assert_allclose(np.concatenate([ya, yb], axis=1), y, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(fb, fin, rtol=1e-12, atol=1e-12)
+    seq = np.array([[0] * 5 + [1] * 7], dtype=np.int32)
+    ys, _ = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=gate, init_state=h0, seq_idx=seq,
+                                   lib=lib)
+    y2, _ = oracle.scan_fwd_vdecay(x[:, 5:], dt[:, 5:], Bm[:, 5:], Cm[:, 5:],
+                                   log_decay=gate[:, 5:], lib=lib)
+    np.testing.assert_allclose(ys[:, :5], y[:, :5], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(ys[:, 5:], y2, rtol=1e-13, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_conv_worked_example_k4,
     check_conv_single_token_k3,
@@ -915,4 +1023,9 @@ ALL_CHECKS = [
     check_fitted_noise_per_head,
     check_state_stats_update,
     check_state_reset,
+    check_vdecay_bruteforce_eq4,
+    check_vdecay_uniform_gate_is_scalar_scan,
+    check_vdecay_rate_form_is_gate_form,
+    check_vdecay_constant_rates_lfilter,
+    check_vdecay_chunks_and_resets,
 ]

@@ -116,6 +116,20 @@ MUTANTS = {
     # reset decision inverted (zero with probability 1 - p)
     "reset_inverted": ("const int zero = (w[b % 4] >> 32) < threshold;",
                        "const int zero = (w[b % 4] >> 32) >= threshold;"),
+    # vector decay: the decay of the neighbouring state dimension
+    "vdecay_wrong_dimension": ("hs[p * N + n] = an[n] * hs[p * N + n] + u * xt[p] * Bt[n];",
+                               "hs[p * N + n] = an[(n + 1) % N] * hs[p * N + n] + u * xt[p] * Bt[n];"),
+    # vector decay: dt dropped from the input term
+    "vdecay_input_no_dt": ("hs[p * N + n] = an[n] * hs[p * N + n] + u * xt[p] * Bt[n];",
+                           "hs[p * N + n] = an[n] * hs[p * N + n] + xt[p] * Bt[n];"),
+    # vector decay: the rate form without dt
+    "vdecay_rate_no_dt": (": exp(u * A_vec[h * N + n]);", ": exp(A_vec[h * N + n]);"),
+    # vector decay: every head reads head 0's gates
+    "vdecay_gate_head_0": ("an[n] = log_decay ? exp(log_decay[((b * L + t) * H + h) * N + n])",
+                           "an[n] = log_decay ? exp(log_decay[((b * L + t) * H + 0) * N + n])"),
+    # vector decay: read-out before the update
+    "vdecay_readout_lag": ("hs[p * N + n] = an[n] * hs[p * N + n] + u * xt[p] * Bt[n];\n                        out += Ct[n] * hs[p * N + n];",
+                           "out += Ct[n] * hs[p * N + n];\n                        hs[p * N + n] = an[n] * hs[p * N + n] + u * xt[p] * Bt[n];"),
     # bf16 rounding keeps 9 bits
     "bf16_nine_bits": ("int q = e - 8;", "int q = e - 9;"),
     # bf16 rounding truncates instead of nearest-even
