@@ -101,7 +101,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
     1.3B-like prefill with packed sequences, the 370M-like prefill, the 131072-token
     780M-like call, the chunked prefill on the decode pools, the initial-state distributions
-    for training, and the backward entry points (conv with state gradients, the scan's
+    for training, the per-dimension (vector) decay scan, and the backward entry points (conv with state gradients, the scan's
     initial-state gradient) at the 1.3B shape.  Seeded
     inputs drawn on the GPU (timing only; parity is the test suite's job)."""
     dev = torch.device("cuda:0")
@@ -232,6 +232,28 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     ms = _time_gpu(torch, lambda: ssm.state_reset(st, p=0.1, seed=1, offset=3, out=kept, mask=mask), 10)
     rep("state_reset", f"{Rs} x H{H}x{P} N{N} fp32, p 0.1, out of place", ms, Rs, 2 * nbs)
     del st, noise, kept
+
+    # the scan with a diagonal, per-state-dimension transition at the 1.3B-like shape:
+    # GLA-like data-dependent log gates [B, L, H, N] fp32 (1 GiB, most of the bytes), dt,
+    # initial and final states
+    s = workloads.shape_of("layer1p3b")
+    g.manual_seed(19)
+    xv = torch.randn(s.B, s.L, s.H, s.P, generator=g, device=dev).to(torch.bfloat16)
+    Bv = torch.randn(s.B, s.L, 1, s.N, generator=g, device=dev).to(torch.bfloat16)
+    Cv = torch.randn(s.B, s.L, 1, s.N, generator=g, device=dev).to(torch.bfloat16)
+    dtv = torch.nn.functional.softplus(torch.randn(s.B, s.L, s.H, generator=g, device=dev) - 2)
+    gate = workloads.vector_decay_gates(s.B, s.L, s.H, s.N, 20, device=dev)
+    h0 = torch.randn(s.B, s.H, s.P, s.N, generator=g, device=dev)
+    yv = torch.empty_like(xv)
+    fv = torch.empty_like(h0)
+    ms = _time_gpu(torch, lambda: ssm.scan_fwd_vector_decay(xv, Bv, Cv, log_decay=gate, dt=dtv,
+                                                            initial_state=h0, final_state=fv,
+                                                            y=yv), 5)
+    nb = (s.B * s.L * (2 * s.H * s.P * 2 + s.H * s.N * 4 + 2 * s.N * 2 + s.H * 4)
+          + 2 * s.B * s.H * s.P * s.N * 4)
+    rep("scan_fwd_vector_decay", f"1.3B-like B{s.B} L{s.L} H{s.H}x{s.P} N{s.N} bf16, per-dimension "
+        "log gates [B, L, H, N] fp32, dt, initial / final state", ms, s.B * s.L, nb)
+    del xv, Bv, Cv, dtv, gate, yv
 
     # backward of the unfused conv at the 1.3B shape, with state gradients
     s = workloads.shape_of("layer1p3b")

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 /* hipStream_t is `struct ihipStream_t*`; this typedef is the same type. */
 struct ihipStream_t;
@@ -161,6 +161,35 @@ ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const 
                           int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
                           ssm_dtype_t dtype, void* workspace, size_t workspace_bytes,
                           ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ssm_scan_fwd_vector_decay -- the scan with a diagonal transition, one decay per state
+ * dimension ([LG] Sec. 2.1 Eq. (1) with A_t = diag(a_t); Sec. 2.5, the diagonal case taken
+ * from log transition coefficients), per head h, channel p and state dimension n:
+ *     state[p][n] <- a_t[n] state[p][n] + u_t x_t[p] B_t[n],   y_t[p] = C_t . state[p][:]
+ * with log a_t[n] = log_decay[b][t][h][n] (data-dependent gates) or dt_t[h] A_vec[h][n] (a
+ * fixed rate per dimension), and u_t = dt_t[h] (1 when dt is NULL).  Initial / final state
+ * and seq_idx resets as ssm_scan_fwd.
+ *
+ *   x, y           [batch, seqlen, nheads, headdim]   dtype
+ *   dt             [batch, seqlen, nheads] fp32, or NULL (= 1; not with A_vec)
+ *   log_decay      [batch, seqlen, nheads, dstate] fp32 (<= 0 for a contraction), or NULL
+ *   A_vec          [nheads, dstate] fp32, or NULL -- exactly one of log_decay, A_vec
+ *   B, C           [batch, seqlen, ngroups, dstate]   dtype
+ *   initial_state, final_state  [batch, nheads, headdim, dstate] fp32, 16-byte aligned, or
+ *                  NULL; final_state may alias initial_state
+ *   seq_idx        [batch, seqlen] int32, or NULL
+ * Token-sequential: the state stays in registers, the decays a_t[n] are formed once per
+ * token and dimension.  dstate = 4 * 2^k <= 256, headdim * dstate <= 16384.
+ * seqlen = 0: final_state = initial_state (or zero).
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_scan_fwd_vector_decay(const void* x, const float* dt, const float* log_decay,
+                                       const float* A_vec, const void* B, const void* C,
+                                       const float* initial_state, float* final_state,
+                                       const int32_t* seq_idx, void* y, int64_t batch,
+                                       int64_t seqlen, int64_t nheads, int64_t headdim,
+                                       int64_t ngroups, int64_t dstate, ssm_dtype_t dtype,
+                                       ssm_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * ssm_conv_scan_fwd -- the fused prefill: ssm_conv1d_fwd over the channels of xBC (with

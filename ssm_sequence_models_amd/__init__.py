@@ -67,6 +67,8 @@ def _load():
     lib.ssm_conv_scan_fwd_pooled.argtypes = [vp, fp, fp, fp, fp, vp, fp, i32p, i32p, i32p, vp,
                                              i64, i64, i64, i64, i64, i64, i64, i64, i64, ci, ci,
                                              vp, ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd_vector_decay.argtypes = [vp, fp, fp, fp, vp, vp, fp, fp, i32p, vp, i64, i64,
+                                              i64, i64, i64, i64, ci, vp]
     u64 = ctypes.c_uint64
     lib.ssm_state_stats_update.argtypes = [fp, i64, i64, i64, i64, ctypes.c_float, fp, fp, vp]
     lib.ssm_initial_state_noise.argtypes = [fp, i64, i64, i64, i64, fp, fp, ctypes.c_float, u64,
@@ -77,7 +79,7 @@ def _load():
                                     ctypes.POINTER(ctypes.c_int64)]
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
               "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
-              "ssm_conv_scan_fwd_pooled", "ssm_state_stats_update",
+              "ssm_conv_scan_fwd_pooled", "ssm_state_stats_update", "ssm_scan_fwd_vector_decay",
               "ssm_initial_state_noise", "ssm_state_reset", "ssm_timing_enable",
               "ssm_timing_read"):
         getattr(lib, f).restype = ci
@@ -209,6 +211,34 @@ def conv_scan_fwd_pooled_workspace_size(batch, seqlen, nheads, headdim, ngroups,
     return int(_lib.ssm_conv_scan_fwd_pooled_workspace_size(batch, seqlen, nheads, headdim, ngroups,
                                                             dstate, width, code))
 
+
+def scan_fwd_vector_decay(x, B, C, log_decay=None, A_vec=None, dt=None, initial_state=None,
+                          seq_idx=None, return_final_state=True, final_state=None, y=None):
+    """The scan with a diagonal transition, one decay per state dimension (length-
+    generalization notes Sec. 2.1 Eq. (1) with A_t = diag(a_t), Sec. 2.5): log a_t[n] from
+    log_decay [b, L, H, N] fp32, or dt * A_vec [H, N].  x [b, L, H, P]; B, C [b, L, G, N];
+    dt [b, L, H] fp32 or None (= 1).  Returns (y [b, L, H, P], final_state or None)."""
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _need(x, "x")
+    _need(B, "B", x.dtype, (bsz, L, G, N))
+    _need(C, "C", x.dtype, (bsz, L, G, N))
+    _need(log_decay, "log_decay", torch.float32, (bsz, L, H, N))
+    _need(A_vec, "A_vec", torch.float32, (H, N))
+    _need(dt, "dt", torch.float32, (bsz, L, H))
+    _need(initial_state, "initial_state", torch.float32, (bsz, H, P, N))
+    _need(seq_idx, "seq_idx", torch.int32, (bsz, L))
+    if y is None:
+        y = torch.empty((bsz, L, H, P), dtype=x.dtype, device=x.device)
+    _need(y, "y", x.dtype, (bsz, L, H, P))
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
+    _need(final_state, "final_state", torch.float32, (bsz, H, P, N))
+    _check("ssm_scan_fwd_vector_decay", _lib.ssm_scan_fwd_vector_decay(
+        _ptr(x), _ptr(dt), _ptr(log_decay), _ptr(A_vec), _ptr(B), _ptr(C), _ptr(initial_state),
+        _ptr(final_state), _ptr(seq_idx), _ptr(y), bsz, L, H, P, G, N, _dtype_code(x),
+        _stream()))
+    return y, final_state
 
 def state_stats_update(final_state, mean, var, beta=0.1):
     """Fitted Noise statistics (length-generalization notes Sec. 2.6, Eqs. (5)-(6)): per head,

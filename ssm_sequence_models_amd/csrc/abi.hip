@@ -449,6 +449,78 @@ ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, c
     return hip_status(ssm::launch_recurrent(r, dtype, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+ssm_status_t ssm_scan_fwd_vector_decay(const void* x, const float* dt, const float* log_decay,
+                                       const float* A_vec, const void* Bm, const void* Cm,
+                                       const float* initial_state, float* final_state,
+                                       const int32_t* seq_idx, void* y, int64_t batch,
+                                       int64_t seqlen, int64_t nheads, int64_t headdim,
+                                       int64_t ngroups, int64_t dstate, ssm_dtype_t dtype,
+                                       ssm_stream_t stream) {
+    const char* fn = "ssm_scan_fwd_vector_decay";
+    ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate, dtype);
+    if (st != SSM_OK) return st;
+    const size_t es = esize(dtype);
+    const bool rows = batch > 0;
+    const bool work = rows && seqlen > 0;
+    // the decay source matters only when there are tokens (an empty tensor has no address)
+    if (work && (log_decay == nullptr) == (A_vec == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, "ssm_scan_fwd_vector_decay: give exactly one of log_decay and A_vec");
+    if (work && A_vec != nullptr && dt == nullptr)
+        return fail(SSM_ERR_INVALID_ARG, "ssm_scan_fwd_vector_decay: the A_vec form needs dt");
+    if (!ssm::recurrent_supported(headdim, dstate, true))
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_scan_fwd_vector_decay: dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
+    st = check_ptrs(fn, {{"x", x, work, es},
+                         {"dt", dt, false, 4},
+                         {"log_decay", log_decay, false, 4},
+                         {"A_vec", A_vec, false, 4},
+                         {"B", Bm, work, es},
+                         {"C", Cm, work, es},
+                         {"initial_state", initial_state, false, 16},
+                         {"final_state", final_state, false, 16},
+                         {"seq_idx", seq_idx, false, 4},
+                         {"y", y, work, es}});
+    if (st != SSM_OK) return st;
+    if (!rows) return ok();
+    if (!work)  // no tokens: the final state is the initial state (or zero)
+        return hip_status(ssm::launch_copy_or_zero_f32(final_state, initial_state,
+                                                       batch * nheads * headdim * dstate,
+                                                       reinterpret_cast<hipStream_t>(stream)),
+                          fn);
+    ssm::RecurrentArgs r{};
+    r.x = x;
+    r.x_sb = seqlen * nheads * headdim;
+    r.x_st = nheads * headdim;
+    r.x_sc = 1;
+    r.dt = dt;
+    r.A = nullptr;
+    r.Bm = Bm;
+    r.B_sb = seqlen * ngroups * dstate;
+    r.B_st = ngroups * dstate;
+    r.B_sc = 1;
+    r.Cm = Cm;
+    r.C_sb = r.B_sb;
+    r.C_st = r.B_st;
+    r.C_sc = 1;
+    r.state_in = initial_state;
+    r.state_out = final_state;
+    r.indices = nullptr;
+    r.n_slots = batch;
+    r.seq_idx = seq_idx;
+    r.y = y;
+    r.B = batch;
+    r.T = seqlen;
+    r.H = nheads;
+    r.P = headdim;
+    r.G = ngroups;
+    r.N = dstate;
+    r.log_decay = log_decay;
+    r.A_vec = A_vec;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (ssm::vdecay_supported(headdim, dstate))
+        return hip_status(ssm::launch_vdecay(r, dtype, s), fn);
+    return hip_status(ssm::launch_recurrent(r, dtype, s), fn);
+}
+
 namespace {
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 }  // namespace

@@ -147,9 +147,17 @@ struct RecurrentArgs {
     const int32_t* seq_idx;   // [B, T] or NULL
     void* y;                  // [B, T, H, P]
     int64_t B, T, H, P, G, N;
+    // diagonal (per-state-dimension) transition: log a_t[n] from log_decay [B, T, H, N], or
+    // dt_t A_vec[h][n] from A_vec [H, N]; both NULL = the scalar exp(dt_t A[h])
+    const float* log_decay;
+    const float* A_vec;
 };
-bool recurrent_supported(int64_t P, int64_t N);
+bool recurrent_supported(int64_t P, int64_t N, bool vector_decay = false);
 hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream);
+// the diagonal-transition scan for long rows (headdim 64, dstate 64 or 128; contiguous
+// states, 16-byte aligned); launch_recurrent covers the other shapes
+bool vdecay_supported(int64_t P, int64_t N);
+hipError_t launch_vdecay(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream);
 
 // Chunked (SSD) scan on MFMA for bf16 inputs with headdim 64, dstate 128.
 bool chunked_supported(int64_t P, int64_t N, ssm_dtype_t dtype);

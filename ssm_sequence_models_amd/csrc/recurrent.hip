@@ -20,6 +20,10 @@
 // (and the sequence resets) are staged by the whole block with loads ordered along the
 // contiguous dimension, so a token costs no memory round trip and the first tile's loads
 // overlap the state load.
+// VEC: the diagonal transition of Eq. (1) (A_t = diag(a_t), one decay per state dimension,
+// Sec. 2.5's diagonal case): the tile also holds a_t[n] = exp(log a_t[n]) for every n,
+// computed once per token by the staging threads, and each state element takes its own
+// dimension's decay; dt may be absent (= 1).
 #include "internal.h"
 
 namespace ssm {
@@ -106,7 +110,7 @@ __device__ __forceinline__ void stage_tile(const typename D::T* src, int64_t bas
 
 constexpr int kRecThreads = 512;
 
-template <class D, int J>
+template <class D, int J, bool VEC>
 __global__ void __launch_bounds__(kRecThreads)
 recurrent_kernel(RecurrentArgs a, int nthreads, int tile_t) {
     using T = typename D::T;
@@ -147,72 +151,99 @@ recurrent_kernel(RecurrentArgs a, int nthreads, int tile_t) {
     const T* xs = static_cast<const T*>(a.x);
     const T* bs = static_cast<const T*>(a.Bm);
     const T* cs = static_cast<const T*>(a.Cm);
-    const float Ah = a.A[h];
-    // per staged token: B [N], C [N], x [P], dt, reset flag
-    extern __shared__ float s_in[];
+    const float Ah = VEC ? 0.0f : a.A[h];
+    // per staged token: B [N], C [N], (with VEC the decays [N]), x [P], dt, reset flag, padded
+    // to whole 16-byte units so the per-lane B / C / decay quadruples are single LDS reads
+    extern __shared__ float4 s_in4[];
+    float* s_in = reinterpret_cast<float*>(s_in4);
     const int N = static_cast<int>(a.N), P = static_cast<int>(a.P);
-    const int row = 2 * N + P + 2;
+    const int oD = 2 * N, oX = VEC ? 3 * N : 2 * N, oDt = oX + P, oF = oDt + 1;
+    const int row = (oF + 1 + 3) & ~3;
+    // per run: its channel p (or -1 when the run is past the state), fixed for the whole loop
+    int p_of[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int64_t e = static_cast<int64_t>(j) * 4 * nthreads + 4 * tid;
+        p_of[j] = (active && e < PN) ? static_cast<int>(e / a.N) : -1;
+    }
+    const bool rs_path = J <= 32 && lanes_per_p == 32 && PN == static_cast<int64_t>(J) * 4 * nthreads;
+    T* y_bh = y + (b * a.T * a.H + h) * a.P;  // y[b, 0, h, 0]; token t adds t * H * P
+    const int64_t y_tok = a.H * a.P;
     for (int64_t tb = 0; tb < a.T; tb += tile_t) {
         const int nt = static_cast<int>(min(static_cast<int64_t>(tile_t), a.T - tb));
         __syncthreads();  // the previous tile has been consumed
         stage_tile<D>(bs, b * a.B_sb + g * a.N * a.B_sc, tb, a.B_st, a.B_sc, nt, N, s_in, row);
         stage_tile<D>(cs, b * a.C_sb + g * a.N * a.C_sc, tb, a.C_st, a.C_sc, nt, N, s_in + N, row);
-        stage_tile<D>(xs, b * a.x_sb + h * a.P * a.x_sc, tb, a.x_st, a.x_sc, nt, P, s_in + 2 * N, row);
+        stage_tile<D>(xs, b * a.x_sb + h * a.P * a.x_sc, tb, a.x_st, a.x_sc, nt, P, s_in + oX, row);
+        if constexpr (VEC) {
+            // a_t[n], consecutive threads on consecutive n (the contiguous index of log_decay)
+            for (int i = threadIdx.x; i < nt * N; i += blockDim.x) {
+                const int tt = i / N, n = i % N;
+                const int64_t t = tb + tt;
+                const float lg = a.log_decay
+                                     ? a.log_decay[((b * a.T + t) * a.H + h) * a.N + n]
+                                     : a.dt[(b * a.T + t) * a.H + h] * a.A_vec[h * a.N + n];
+                s_in[tt * row + oD + n] = __expf(lg);
+            }
+        }
         for (int tt = threadIdx.x; tt < nt; tt += blockDim.x) {
             const int64_t t = tb + tt;
-            s_in[tt * row + 2 * N + P] = a.dt[(b * a.T + t) * a.H + h];
+            s_in[tt * row + oDt] = a.dt ? a.dt[(b * a.T + t) * a.H + h] : 1.0f;
             const bool reset = a.seq_idx && t > 0 && a.seq_idx[b * a.T + t] != a.seq_idx[b * a.T + t - 1];
-            s_in[tt * row + 2 * N + P + 1] = reset ? 1.0f : 0.0f;
+            s_in[tt * row + oF] = reset ? 1.0f : 0.0f;
         }
         __syncthreads();
     for (int tt = 0; tt < nt; ++tt) {
         const int64_t t = tb + tt;
         const float* tin = s_in + tt * row;
-        if (tin[2 * N + P + 1] != 0.0f) {
+        if (tin[oF] != 0.0f) {
 #pragma unroll
             for (int j = 0; j < J; ++j)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) st[j][k] = 0.0f;
         }
-        const float d = tin[2 * N + P];
-        const float dec = __expf(d * Ah);
-        float Bv[4], Cv[4];
+        const float d = tin[oDt];
+        // row % 4 == 0 and n0 % 4 == 0: 16-byte aligned quadruples
+        const float4 b4 = active ? *reinterpret_cast<const float4*>(tin + n0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 c4 = active ? *reinterpret_cast<const float4*>(tin + N + n0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float Bv[4] = {b4.x, b4.y, b4.z, b4.w};
+        const float Cv[4] = {c4.x, c4.y, c4.z, c4.w};
+        float dec[4];
+        if constexpr (VEC) {
+            const float4 d4 = active ? *reinterpret_cast<const float4*>(tin + oD + n0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            dec[0] = d4.x; dec[1] = d4.y; dec[2] = d4.z; dec[3] = d4.w;
+        } else {
+            const float dsc = __expf(d * Ah);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            Bv[k] = active ? tin[n0 + k] : 0.0f;
-            Cv[k] = active ? tin[N + n0 + k] : 0.0f;
+            for (int k = 0; k < 4; ++k) dec[k] = dsc;
         }
         float part[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int64_t e = static_cast<int64_t>(j) * 4 * nthreads + 4 * tid;
-            const bool live = active && e < PN;
-            const int64_t p = live ? e / a.N : 0;
-            const float xp = live ? tin[2 * N + p] : 0.0f;
+            const float xp = p_of[j] >= 0 ? tin[oX + p_of[j]] : 0.0f;
             const float dx = d * xp;
             float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                st[j][k] = __builtin_fmaf(dec, st[j][k], dx * Bv[k]);
+                st[j][k] = __builtin_fmaf(dec[k], st[j][k], dx * Bv[k]);
                 acc = __builtin_fmaf(Cv[k], st[j][k], acc);
             }
             part[j] = acc;
         }
-        if (J <= 32 && lanes_per_p == 32 && PN == static_cast<int64_t>(J) * 4 * nthreads) {
+        T* y_t = y_bh + t * y_tok;
+        if (rs_path) {
             // run j of thread tid is channel p = (4 nthreads / N) j + tid / 32; lanes tid % 32
             // share it; after the reduce-scatter the lanes with tid % (32 / J) == 0 hold whole sums
             int jr;
             const float yv = reduce_scatter32<J>(part, tid, &jr);
             if ((tid & (32 / J - 1)) == 0)
-                D::store(y, ((b * a.T + t) * a.H + h) * a.P + (4 * nthreads / 128) * jr + tid / 32, yv);
+                D::store(y_t, (4 * nthreads / 128) * jr + tid / 32, yv);
         } else {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const int64_t e = static_cast<int64_t>(j) * 4 * nthreads + 4 * tid;
-                const bool live = active && e < PN;
                 float v = part[j];
                 for (int off = lanes_per_p / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-                if (live && n0 == 0) D::store(y, ((b * a.T + t) * a.H + h) * a.P + e / a.N, v);
+                if (p_of[j] >= 0 && n0 == 0) D::store(y_t, p_of[j], v);
             }
         }
     }
@@ -241,12 +272,13 @@ __global__ void copy_or_zero_u8_kernel(uint8_t* dst, const uint8_t* src, int64_t
 
 // Lane groups of N/4 must be a power of two within one wavefront; P*N up to 16 float4 runs
 // per thread at kRecThreads threads.
-bool recurrent_supported(int64_t P, int64_t N) {
+bool recurrent_supported(int64_t P, int64_t N, bool vector_decay) {
     if (N % 4 != 0) return false;
     const int64_t lp = N / 4;
     if (lp > 64 || (lp & (lp - 1)) != 0) return false;
-    // one staged token (B, C, x, dt, flag) must fit the tile budget
-    return P * N <= kRecThreads * 4 * 16 && (2 * N + P + 2) * 4 <= static_cast<int64_t>(kTileBytesMax);
+    // one staged token (B, C, x, dt, flag, and the decays) must fit the tile budget
+    const int64_t row = ((vector_decay ? 3 * N : 2 * N) + P + 2 + 3) / 4 * 4;
+    return P * N <= kRecThreads * 4 * 16 && row * 4 <= static_cast<int64_t>(kTileBytesMax);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream) {
@@ -260,17 +292,24 @@ hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream
     dim3 grid(a.H, a.B);
     const int nt = static_cast<int>(nthreads);
     // tokens per staged tile: up to kTileTMax, within kTileBytesMax of LDS
-    const size_t row_bytes = static_cast<size_t>(2 * a.N + a.P + 2) * sizeof(float);
+    const bool vec = a.log_decay != nullptr || a.A_vec != nullptr;
+    // the kernel's padded token row: (B, C, [decays,] x, dt, flag) rounded up to 4 floats
+    const size_t row_bytes =
+        static_cast<size_t>(((vec ? 3 : 2) * a.N + a.P + 2 + 3) / 4 * 4) * sizeof(float);
     int tile_t = static_cast<int>(kTileBytesMax / row_bytes);
     if (tile_t > kTileTMax) tile_t = kTileTMax;
     if (tile_t < 1) return hipErrorInvalidValue;  // excluded by recurrent_supported
     const size_t lds = static_cast<size_t>(tile_t) * row_bytes;
 #define SSM_REC(JJ)                                                                         \
     if (runs <= JJ) {                                                                       \
-        if (dtype == SSM_BF16)                                                              \
-            recurrent_kernel<BF16, JJ><<<grid, block, lds, stream>>>(a, nt, tile_t);        \
+        if (dtype == SSM_BF16 && vec)                                                       \
+            recurrent_kernel<BF16, JJ, true><<<grid, block, lds, stream>>>(a, nt, tile_t);  \
+        else if (dtype == SSM_BF16)                                                         \
+            recurrent_kernel<BF16, JJ, false><<<grid, block, lds, stream>>>(a, nt, tile_t); \
+        else if (vec)                                                                       \
+            recurrent_kernel<F32, JJ, true><<<grid, block, lds, stream>>>(a, nt, tile_t);   \
         else                                                                                \
-            recurrent_kernel<F32, JJ><<<grid, block, lds, stream>>>(a, nt, tile_t);         \
+            recurrent_kernel<F32, JJ, false><<<grid, block, lds, stream>>>(a, nt, tile_t);  \
         return hipGetLastError();                                                           \
     }
     SSM_REC(1) SSM_REC(2) SSM_REC(4) SSM_REC(8) SSM_REC(16)

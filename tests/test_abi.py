@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
               "ssm_last_error", "ssm_conv1d_bwd", "ssm_conv1d_bwd_workspace_size",
               "ssm_scan_bwd_initial_state", "ssm_conv_scan_fwd_pooled",
               "ssm_conv_scan_fwd_pooled_workspace_size", "ssm_state_stats_update",
-              "ssm_initial_state_noise", "ssm_state_reset"):
+              "ssm_initial_state_noise", "ssm_state_reset", "ssm_scan_fwd_vector_decay"):
         assert f in names
 
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_abi_version() == 3
+    assert lib.ssm_abi_version() == 4
     for code in range(6):
         assert lib.ssm_status_string(code)
 
@@ -134,6 +134,13 @@ def test_argument_errors_return_status(lib):
     assert lib.ssm_state_stats_update(None, 0, 4, 8, 16, 0.1, None, None, None) == 0
     assert lib.ssm_initial_state_noise(None, 0, 4, 8, 16, None, None, 1.0, 0, 0, None) == 0
     assert lib.ssm_state_reset(None, None, None, 0, 8, 0.1, 0, 0, None) == 0
+    # vector decay: both decay forms / neither; A_vec without dt; state not 16-byte aligned
+    vd = lambda dt, ld, av, init: lib.ssm_scan_fwd_vector_decay(
+        dummy, dt, ld, av, dummy, dummy, init, None, None, dummy, 1, 8, 4, 16, 1, 32, 1, None)
+    assert vd(dummy, dummy, dummy, None) == 1
+    assert vd(dummy, None, None, None) == 1
+    assert vd(None, None, dummy, None) == 1
+    assert vd(dummy, dummy, None, _c(260)) == 3
     # zero-sized work is a no-op that succeeds without touching the device
     assert lib.ssm_conv1d_update(None, None, None, None, None, None, None, 0, 8, 1, 4, 3, 4, 1,
                                  0, None) == 0

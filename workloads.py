@@ -17,6 +17,10 @@ Distributions (fixed recipe):
   A (one per head)        = -exp(U(log 1, log 16)), fp32
   conv weight, bias       ~ U(-0.5, 0.5) = U(-1/sqrt(K), 1/sqrt(K)) for K = 4, fp32
   packed seq_idx          3 distinct cut points uniform in 1 .. L-1 per row -> ids 0..3
+  per-dimension log gates = logsigmoid(N(0, 1)) / 16, fp32 (mean ~ -0.05; the data-dependent
+                            gates of the diagonal-transition models, with the normaliser 16
+                            gated linear attention uses)
+  per-dimension rates     = -exp(U(log 1, log 16)) per (head, state dimension), fp32
 """
 from __future__ import annotations
 
@@ -176,3 +180,18 @@ def decode_inputs(L_new: int = 1, seed: int | None = None, R: int | None = None,
     out["conv_w"], out["conv_b"] = w, b
     out["A"] = _neg_exp_uniform(d["H"], _gen(d["seed"] * 1000 + 29))
     return out
+
+
+def vector_decay_gates(B: int, L: int, H: int, N: int, seed: int,
+                       device: str | torch.device = "cpu") -> torch.Tensor:
+    """log_decay [B, L, H, N] fp32 = logsigmoid(N(0, 1)) / 16 (generated on `device` with a
+    generator seeded there, so large tensors need not cross the bus)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    z = torch.randn(B, L, H, N, generator=g, device=device)
+    return torch.nn.functional.logsigmoid(z) / 16.0
+
+
+def vector_decay_rates(H: int, N: int, seed: int) -> torch.Tensor:
+    """A_vec [H, N] fp32 = -exp(U(log 1, log 16)): one rate per head and state dimension."""
+    g = _gen(seed)
+    return -torch.exp(torch.rand(H, N, generator=g) * math.log(16.0))
