@@ -15,7 +15,11 @@
 //     leaves y_t[p] of one channel in every fourth lane.  A quarter-row-per-lane layout spent
 //     its time returning LDS data (24 16-byte reads per token and lane; 4.6 ms against 4.1 ms
 //     at the 1.3B-like shape); pairing tokens under one reduce-scatter raised the register
-//     count to 139 and ran slower (5.5 ms);
+//     count to 139 and ran slower (5.5 ms).  Each token's reduce-scatter runs in the next
+//     token's iteration, where nothing depends on it, so its exchange latency overlaps that
+//     token's updates.  Letting all eight waves compute (4 x 4 blocks, a 32-lane reduction
+//     through ds_swizzle, tiles prefetched into registers) ran slower too (3.65-3.80 ms
+//     against 3.3 ms);
 //   - the staging waves copy a tile of 32 tokens (B, C, x, dt, and a_t[n] = exp(log a_t[n]),
 //     formed here once per token and dimension; a_t = 0 where seq_idx starts a new sequence,
 //     which is the reset) into one of two LDS
@@ -204,11 +208,23 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
             const float* buf = lds + (k & 1) * (kVdTile * R);
             const int64_t t0 = k * kVdTile;
             const int nt = static_cast<int>(min(static_cast<int64_t>(kVdTile), a.T - t0));
+            // software pipeline: token tt's reduction runs in the next iteration, where
+            // nothing it computes depends on it, so its exchange latency overlaps token
+            // tt + 1's updates
+            float pend[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             for (int tt = 0; tt < nt; ++tt) {
                 float acc[4];
                 token(buf + tt * R, acc);
-                const float yv = rs16x4(acc, tid);
-                if ((tid & 3) == 0) D::store(y_p, (t0 + tt) * y_tok, yv);
+                if (tt > 0) {
+                    const float yv = rs16x4(pend, tid);
+                    if ((tid & 3) == 0) D::store(y_p, (t0 + tt - 1) * y_tok, yv);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pend[i] = acc[i];
+            }
+            if (nt > 0) {
+                const float yv = rs16x4(pend, tid);
+                if ((tid & 3) == 0) D::store(y_p, (t0 + nt - 1) * y_tok, yv);
             }
         } else if (k + 1 < ntiles) {
             stage(k + 1);
