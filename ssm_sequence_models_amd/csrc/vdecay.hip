@@ -6,25 +6,30 @@
 // with log a_t[n] = log_decay[b][t][h][n] or dt_t A_vec[h][n], u_t = dt_t (or 1).
 //
 // Token-sequential, laid out for issue rate rather than for the decode step's one token:
-//   - one block per (row, head), 512 threads: waves 0-3 compute, waves 4-7 stage;
-//   - a compute lane owns a 4 x NL block of the state (channels p = 4 (tid / 16) .. +3,
-//     dimensions n = NL (tid % 16) .. +NL-1, NL = N / 16) in registers for the whole row.
-//     Per token it reads its NL values of B, C and a_t and its 4 values of x from LDS (lanes
-//     sharing them read the same addresses), issues 4 NL independent decay-and-input updates
-//     and 4 NL read-out products, and a reduce-scatter over the 16 lanes of its channel block
-//     leaves y_t[p] of one channel in every fourth lane.  A quarter-row-per-lane layout spent
-//     its time returning LDS data (24 16-byte reads per token and lane; 4.6 ms against 4.1 ms
-//     at the 1.3B-like shape); pairing tokens under one reduce-scatter raised the register
-//     count to 139 and ran slower (5.5 ms).  Each token's reduce-scatter runs in the next
-//     token's iteration, where nothing depends on it, so its exchange latency overlaps that
-//     token's updates.  Letting all eight waves compute (4 x 4 blocks, a 32-lane reduction
-//     through ds_swizzle, tiles prefetched into registers) ran slower too (3.65-3.80 ms
-//     against 3.3 ms);
-//   - the staging waves copy a tile of 32 tokens (B, C, x, dt, and a_t[n] = exp(log a_t[n]),
-//     formed here once per token and dimension; a_t = 0 where seq_idx starts a new sequence,
-//     which is the reset) into one of two LDS
-//     buffers while the compute waves consume the other: one barrier per tile, global
-//     latency hidden behind the previous tile's arithmetic.
+//   - one block per (row, head, half of the head's 64 channels), 512 threads: waves 0-3
+//     compute, waves 4-7 stage.  Two blocks share a CU, so each SIMD runs two compute waves
+//     and one hides the other's LDS and DPP latency;
+//   - a compute lane owns a 2 x NL block of the state (channels p0, p0 + 1 with
+//     p0 = 32 half + 2 (tid / 16), dimensions n = NL (tid % 16) .. +NL-1, NL = N / 16) in
+//     registers for the whole row.  Per token it reads its NL values of B, C and a_t and 2 of
+//     x from LDS (lanes sharing them read the same addresses), issues 2 NL decay multiplies,
+//     2 NL input accumulates and 2 NL read-out accumulates, and a reduce-scatter over the 16
+//     lanes of its channel block leaves y_t[p] of one channel in every eighth lane.  The
+//     reduce-scatter of a token runs in the next token's iteration, where nothing depends on
+//     it, so its exchange latency overlaps that token's updates;
+//   - the staging waves copy a tile of 16 tokens (B, C, the block's x, dt, and
+//     a_t[n] = exp(log a_t[n]), formed once per token and dimension; a_t = 0 where seq_idx
+//     starts a new sequence, which is the reset) into one of two LDS buffers while the
+//     compute waves consume the other; every load of a tile is issued before the first LDS
+//     store; one barrier per tile.
+// Measured at the 1.3B-like shape (B 4, L 8192, 64 heads, gates [B, L, H, N]): one block per
+// (row, head) with a quarter row per lane 4.6 ms (LDS-return bound at 24 reads per token);
+// 4 x 8 blocks per lane 4.1 ms, 3.37 ms with batched staging loads, 3.31 ms with the
+// pipelined reduce-scatter (compute alone 2.54 ms: one compute wave per SIMD leaves every
+// latency exposed); pairing tokens under one reduce-scatter 5.5 ms (139 VGPRs); all eight
+// waves computing 4 x 4 blocks with a 32-lane ds_swizzle reduction 3.65-3.80 ms; this
+// layout, halves of the channels in two blocks per CU, 2.75 ms; quarters (one channel per
+// lane, four blocks per (row, head) re-staging the same gates) 4.9 ms.
 // P = 64 and N in {64, 128}; other shapes use the general token-sequential kernel.
 #include "internal.h"
 
@@ -34,12 +39,13 @@ namespace {
 constexpr int kVdThreads = 512;  // 256 compute + 256 staging
 constexpr int kVdCompute = 256;
 constexpr int kVdP = 64;
-constexpr int kVdTile = 32;      // tokens per staged tile
+constexpr int kVdTile = 16;      // tokens per staged tile
+constexpr int kVdPh = kVdP / 2;  // channels per block
 
-// floats per staged token: B [N], C [N], a [N] (0 on a reset token), x [64], u, padding
+// floats per staged token: B [N], C [N], a [N] (0 on a reset token), x [32], u, padding
 template <int N>
 constexpr int vd_row() {
-    return 3 * N + kVdP + 4;
+    return 3 * N + kVdPh + 4;
 }
 
 // Exchange with lane i ^ 8 (DPP row_mirror, i <-> 15 - i within 16 lanes), i ^ 4 (DPP
@@ -56,18 +62,14 @@ __device__ __forceinline__ float vd_xchg(float v) {
     return __int_as_float(r);
 }
 
-// Sums of v[0..3] over the 16 lanes of a row, reduce-scatter style: at the bit-3 level a lane
-// keeps the pair {0, 1} (bit clear) or {2, 3} (bit set) and adds its partner's copy of that
-// pair; at bit 2 it keeps one of the two; bits 1 and 0 add the partner's single sum.  Lane i
-// ends with the whole sum of index 2 bit3(i) + bit2(i).  Each partner agrees with the lane on
+// Sums of v[0..1] over the 16 lanes of a row, reduce-scatter style: at bit 3 a lane keeps
+// v[bit3] and adds its partner's copy of it; bits 2, 1 and 0 add the partner's single sum.
+// Lane i ends with the whole sum of index bit3(i).  Each partner agrees with the lane on
 // every bit decided before and holds sums over a disjoint set of lanes.
-__device__ __forceinline__ float rs16x4(const float (&v)[4], int lane) {
-    const bool h8 = (lane & 8) != 0, h4 = (lane & 4) != 0;
-    const float k0 = h8 ? v[2] : v[0], k1 = h8 ? v[3] : v[1];
-    const float s0 = h8 ? v[0] : v[2], s1 = h8 ? v[1] : v[3];
-    const float w0 = k0 + vd_xchg<8>(s0), w1 = k1 + vd_xchg<8>(s1);
-    const float keep = h4 ? w1 : w0, send = h4 ? w0 : w1;
-    float r = keep + vd_xchg<4>(send);
+__device__ __forceinline__ float rs16x2(const float (&v)[2], int lane) {
+    const bool h8 = (lane & 8) != 0;
+    float r = (h8 ? v[1] : v[0]) + vd_xchg<8>(h8 ? v[0] : v[1]);
+    r += vd_xchg<4>(r);
     r += vd_xchg<2>(r);
     r += vd_xchg<1>(r);
     return r;
@@ -77,11 +79,12 @@ template <class D, int N>
 __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     using T = typename D::T;
     constexpr int R = vd_row<N>();
-    constexpr int oC = N, oA = 2 * N, oX = 3 * N, oU = 3 * N + kVdP;
+    constexpr int oC = N, oA = 2 * N, oX = 3 * N, oU = 3 * N + kVdPh;
     __shared__ __attribute__((aligned(16))) float lds[2 * kVdTile * R];  // two tile buffers
 
     const int tid = threadIdx.x;
     const int64_t h = blockIdx.x, b = blockIdx.y;
+    const int half = blockIdx.z;  // channels 32 half .. 32 half + 31
     const int64_t g = h / (a.H / a.G);
     const int64_t ntiles = (a.T + kVdTile - 1) / kVdTile;
     const T* xs = static_cast<const T*>(a.x);
@@ -93,7 +96,7 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     // the tile costs about one global latency rather than one per element.
     auto stage = [&](int64_t k) {
         constexpr int kItems = kVdTile * N / kVdCompute;   // B / C / gate values per thread
-        constexpr int kXItems = kVdTile * kVdP / kVdCompute;
+        constexpr int kXItems = kVdTile * kVdPh / kVdCompute;
         const int st = tid - kVdCompute;
         float* buf = lds + (k & 1) * (kVdTile * R);
         const int64_t t0 = k * kVdTile;
@@ -120,8 +123,9 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
 #pragma unroll
         for (int j = 0; j < kXItems; ++j) {
             const int i = st + j * kVdCompute;
-            const int tt = i / kVdP, p = i % kVdP;
-            vx[j] = tt < nt ? D::load(xs, b * a.x_sb + (t0 + tt) * a.x_st + (h * kVdP + p) * a.x_sc)
+            const int tt = i / kVdPh, p = i % kVdPh;
+            vx[j] = tt < nt ? D::load(xs, b * a.x_sb + (t0 + tt) * a.x_st +
+                                              (h * kVdP + kVdPh * half + p) * a.x_sc)
                             : 0.0f;
         }
         float vu = 1.0f;
@@ -140,21 +144,22 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
 #pragma unroll
         for (int j = 0; j < kXItems; ++j) {
             const int i = st + j * kVdCompute;
-            const int tt = i / kVdP, p = i % kVdP;
+            const int tt = i / kVdPh, p = i % kVdPh;
             if (tt < nt) buf[tt * R + oX + p] = vx[j];
         }
         if (st < nt) buf[st * R + oU] = vu;
     };
 
-    // compute lanes: channels p0 .. p0 + 3, dimensions n0 .. n0 + NL - 1
+    // compute lanes: channels p0, p0 + 1, dimensions n0 .. n0 + NL - 1
     constexpr int NL = N / 16;
-    const int p0 = 4 * (tid / 16), n0 = NL * (tid % 16);
+    const int pl = 2 * (tid / 16);  // channel within the block's half
+    const int p0 = kVdPh * half + pl, n0 = NL * (tid % 16);
     const bool compute = tid < kVdCompute;
-    float st[4][NL];
+    float st[2][NL];
     const int64_t sbase = ((b * a.H + h) * kVdP + p0) * N + n0;
     if (compute) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int c = 0; c < NL / 4; ++c) {
                 float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -170,15 +175,15 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
 
     T* y = static_cast<T*>(a.y);
     const int64_t y_tok = a.H * kVdP;
-    // after the reduce-scatter lane tid holds channel p0 + 2 bit3 + bit2 of tid; lanes with
-    // tid % 4 == 0 write it
-    const int p_out = p0 + ((tid >> 2) & 3);
+    // after the reduce-scatter lane tid holds channel p0 + bit3 of tid; lanes with
+    // tid % 8 == 0 write it
+    const int p_out = p0 + ((tid >> 3) & 1);
     T* y_p = y + (b * a.T * a.H + h) * kVdP + p_out;  // y[b, 0, h, p_out]
-    // one token: reset if flagged, decay-and-input update, per-channel read-out into acc[0..3]
+    // one token: decay-and-input update, per-channel read-out into acc[0..1]
     auto token = [&](const float* row, float* acc) {
         const float u = row[oU];
-        const float4 x4 = *reinterpret_cast<const float4*>(row + oX + p0);
-        const float dx[4] = {u * x4.x, u * x4.y, u * x4.z, u * x4.w};
+        const float2 x2 = *reinterpret_cast<const float2*>(row + oX + pl);
+        const float dx[2] = {u * x2.x, u * x2.y};
         float bv[NL], av[NL], cv[NL];
 #pragma unroll
         for (int c = 0; c < NL / 4; ++c) {
@@ -190,7 +195,7 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
             cv[4 * c] = c4.x; cv[4 * c + 1] = c4.y; cv[4 * c + 2] = c4.z; cv[4 * c + 3] = c4.w;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             float s_ = 0.0f;
 #pragma unroll
             for (int e = 0; e < NL; ++e) {
@@ -208,23 +213,20 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
             const float* buf = lds + (k & 1) * (kVdTile * R);
             const int64_t t0 = k * kVdTile;
             const int nt = static_cast<int>(min(static_cast<int64_t>(kVdTile), a.T - t0));
-            // software pipeline: token tt's reduction runs in the next iteration, where
-            // nothing it computes depends on it, so its exchange latency overlaps token
-            // tt + 1's updates
-            float pend[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float pend[2] = {0.0f, 0.0f};
             for (int tt = 0; tt < nt; ++tt) {
-                float acc[4];
+                float acc[2];
                 token(buf + tt * R, acc);
                 if (tt > 0) {
-                    const float yv = rs16x4(pend, tid);
-                    if ((tid & 3) == 0) D::store(y_p, (t0 + tt - 1) * y_tok, yv);
+                    const float yv = rs16x2(pend, tid);
+                    if ((tid & 7) == 0) D::store(y_p, (t0 + tt - 1) * y_tok, yv);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pend[i] = acc[i];
+                pend[0] = acc[0];
+                pend[1] = acc[1];
             }
             if (nt > 0) {
-                const float yv = rs16x4(pend, tid);
-                if ((tid & 3) == 0) D::store(y_p, (t0 + nt - 1) * y_tok, yv);
+                const float yv = rs16x2(pend, tid);
+                if ((tid & 7) == 0) D::store(y_p, (t0 + nt - 1) * y_tok, yv);
             }
         } else if (k + 1 < ntiles) {
             stage(k + 1);
@@ -233,7 +235,7 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     }
     if (compute && a.state_out) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int c = 0; c < NL / 4; ++c)
                 *reinterpret_cast<float4*>(a.state_out + sbase + i * N + 4 * c) =
@@ -247,7 +249,7 @@ bool vdecay_supported(int64_t P, int64_t N) { return P == kVdP && (N == 64 || N 
 
 hipError_t launch_vdecay(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
+    dim3 grid(static_cast<unsigned>(a.H), static_cast<unsigned>(a.B), 2);  // z: channel half
     if (a.N == 128) {
         if (dtype == SSM_BF16)
             vdecay_kernel<BF16, 128><<<grid, kVdThreads, 0, stream>>>(a);
