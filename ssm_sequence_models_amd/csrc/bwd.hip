@@ -360,8 +360,8 @@ __global__ void conv1d_bwd_empty_kernel(const typename D::T* dfin, typename D::T
 }
 
 // ---------------------------------------------------------------------------------------
-// dh_{-1}, MFMA path (P = 64, N = 128, bf16): one block per (b, h), four wavefronts; wave w
-// owns rows p = 16 w .. 16 w + 15 of dh_{-1}[p][0..127] in accumulators.  Per 64-token chunk:
+// dh_{-1}, MFMA path (P = 64, N = 128, bf16): one block per (b, h, column half), four
+// wavefronts; wave w owns rows p = 16 w .. 16 w + 15 of the half in accumulators.  Per chunk:
 // dy^T and C^T are staged in LDS (token index contiguous), wave 0 forms E_t = 2^(offset +
 // prefix of dt A log2 e) with a DPP scan, then dh += (E o dy)^T C with E o dy split into two
 // bf16 halves (hi + lo, as the main scan) against the exact bf16 C.  The loop stops at the
@@ -385,80 +385,106 @@ __device__ __forceinline__ float h0_incl_sum(float v) {
     return v;
 }
 
+// Block = (b, h, half of the 128 state columns), so two blocks share a CU.  Per 64-token
+// chunk each thread moves one 16-byte piece of two consecutive token rows of C and of dy into
+// LDS transposed ([column][token]), packing the two tokens into one 4-byte store (consecutive
+// lanes take consecutive token pairs: conflict-free stores).  The loads for chunk k+1 are
+// issued before chunk k's products and stored after them, into the other of two buffers.
 __global__ void __launch_bounds__(256)
 scan_bwd_h0_mfma_kernel(const float* dt, const float* A, const uint16_t* Cm,
                         const int32_t* seq, const uint16_t* dy, const float* dfin, float* dh0,
                         int64_t L, int64_t H, int64_t G) {
-    __shared__ __attribute__((aligned(16))) uint8_t sCt[kH0N * kH0Row];  // C^T [n][t]
-    __shared__ __attribute__((aligned(16))) uint8_t sDy[kH0P * kH0Row];  // dy^T [p][t]
-    __shared__ float sE[kH0Q];
-    __shared__ int sStop;
+    constexpr int kNh = kH0N / 2;  // columns per block
+    __shared__ __attribute__((aligned(16))) uint8_t sCt[2][kNh * kH0Row];  // C^T [n][t]
+    __shared__ __attribute__((aligned(16))) uint8_t sDy[2][kH0P * kH0Row];  // dy^T [p][t]
+    __shared__ float sE[2][kH0Q];
+    __shared__ int sStop[2];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
     const int64_t h = blockIdx.x, b = blockIdx.y;
+    const int nh = blockIdx.z;
     const int64_t g = h / (H / G);
     const float a2 = A[h] * 1.4426950408889634f;
     const int32_t* sq = seq ? seq + b * L : nullptr;
-    f32x4_t acc[8];
+    const int64_t nchunks = (L + kH0Q - 1) / kH0Q;
+    // this thread's staging unit: token pair tp, 8-column piece q (of C's half and of dy)
+    const int tp = tid & 31, q = tid >> 5;
+    u32x4_t rc0, rc1, rd0, rd1;
+    auto load = [&](int64_t k) {
+        const int64_t t = k * kH0Q + 2 * tp;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        rc0 = rc1 = rd0 = rd1 = z;
+        if (t < L) {
+            rc0 = *reinterpret_cast<const u32x4_t*>(Cm + ((b * L + t) * G + g) * kH0N + kNh * nh + 8 * q);
+            rd0 = *reinterpret_cast<const u32x4_t*>(dy + ((b * L + t) * H + h) * kH0P + 8 * q);
+        }
+        if (t + 1 < L) {
+            rc1 = *reinterpret_cast<const u32x4_t*>(Cm + ((b * L + t + 1) * G + g) * kH0N + kNh * nh + 8 * q);
+            rd1 = *reinterpret_cast<const u32x4_t*>(dy + ((b * L + t + 1) * H + h) * kH0P + 8 * q);
+        }
+    };
+    // column 8 q + e of the pair: (token 2 tp, token 2 tp + 1) as one 4-byte word
+    auto store = [&](int64_t k) {
+        uint8_t* ct = sCt[k & 1];
+        uint8_t* dv = sDy[k & 1];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int e = 0; e < 8; ++e) {
+            const int sh = 16 * (e & 1);
+            const uint32_t c2 = ((rc0[e >> 1] >> sh) & 0xFFFFu) | (((rc1[e >> 1] >> sh) & 0xFFFFu) << 16);
+            const uint32_t d2 = ((rd0[e >> 1] >> sh) & 0xFFFFu) | (((rd1[e >> 1] >> sh) & 0xFFFFu) << 16);
+            *reinterpret_cast<uint32_t*>(ct + (8 * q + e) * kH0Row + 4 * tp) = c2;
+            *reinterpret_cast<uint32_t*>(dv + (8 * q + e) * kH0Row + 4 * tp) = d2;
+        }
+    };
     float offset = 0.0f;  // log2 of E at the end of the previous chunk (wave 0)
     bool alive = true;    // no sequence change so far (wave 0, uniform)
-    for (int64_t t0 = 0; t0 < L; t0 += kH0Q) {
-        // stage C^T and dy^T: 16-byte pieces of a token row, written transposed
-        for (int i = tid; i < kH0Q * (kH0N / 8); i += 256) {
-            const int tt = i / (kH0N / 8), q = i % (kH0N / 8);
-            const int64_t t = t0 + tt;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (t < L) v = *reinterpret_cast<const u32x4_t*>(Cm + ((b * L + t) * G + g) * kH0N + 8 * q);
+    // E_t of chunk k into sE[k & 1]; sStop[k & 1] = nothing after chunk k contributes
+    auto scan_e = [&](int64_t k) {
+        const int64_t t = k * kH0Q + lane;
+        const bool in = t < L;
+        const float v = in ? dt[(b * L + t) * H + h] * a2 : 0.0f;
+        const float cum = h0_incl_sum(v);
+        bool cut = false;  // a sequence change at or before this token (within the chunk)
+        if (sq) {
+            const bool chg = in && t > 0 && sq[t] != sq[t - 1];
+            const uint64_t m = __ballot(chg);
+            const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // lanes 0 .. lane
+            cut = (m & upto) != 0;
+        }
+        const bool ok = alive && !cut && in;
+        sE[k & 1][lane] = ok ? __builtin_amdgcn_exp2f(offset + cum) : 0.0f;
+        offset += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kH0Q - 1));
+        const bool any_cut = __ballot(cut) != 0;
+        alive = alive && !any_cut;
+        const float e_end = __builtin_amdgcn_exp2f(offset);
+        if (lane == 0) sStop[k & 1] = (!alive || e_end == 0.0f || k + 1 >= nchunks) ? 1 : 0;
+    };
+    f32x4_t acc[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint16_t*>(sCt + (8 * q + e) * kH0Row + 2 * tt) =
-                    static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
-        }
-        for (int i = tid; i < kH0Q * (kH0P / 8); i += 256) {
-            const int tt = i / (kH0P / 8), q = i % (kH0P / 8);
-            const int64_t t = t0 + tt;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (t < L) v = *reinterpret_cast<const u32x4_t*>(dy + ((b * L + t) * H + h) * kH0P + 8 * q);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint16_t*>(sDy + (8 * q + e) * kH0Row + 2 * tt) =
-                    static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
-        }
-        if (wave == 0) {
-            const int64_t t = t0 + lane;
-            const bool in = t < L;
-            const float v = in ? dt[(b * L + t) * H + h] * a2 : 0.0f;
-            const float cum = h0_incl_sum(v);
-            bool cut = false;  // a sequence change at or before this token (within the chunk)
-            if (sq) {
-                const bool chg = in && t > 0 && sq[t] != sq[t - 1];
-                const uint64_t m = __ballot(chg);
-                const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);  // lanes 0 .. lane
-                cut = (m & upto) != 0;
-            }
-            const bool ok = alive && !cut && in;
-            sE[lane] = ok ? __builtin_amdgcn_exp2f(offset + cum) : 0.0f;
-            offset += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kH0Q - 1));
-            const bool any_cut = __ballot(cut) != 0;
-            alive = alive && !any_cut;
-            const float e_end = __builtin_amdgcn_exp2f(offset);
-            if (lane == 0) sStop = (!alive || e_end == 0.0f) ? 1 : 0;
-        }
-        __syncthreads();
-        // dh[p][n] += sum_t (E_t dy[t][p]) C[t][n]; lane: row p = 16 wave + li of the A operand,
-        // tokens 32 ks + 8 g4 .. +7
+    for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (nchunks > 0) {
+        load(0);
+        store(0);
+        if (wave == 0) scan_e(0);
+    }
+    __syncthreads();
+    for (int64_t k = 0; k < nchunks; ++k) {
+        const bool stop = sStop[k & 1] != 0;
+        if (!stop) load(k + 1);
+        const uint8_t* ct = sCt[k & 1];
+        const uint8_t* dv = sDy[k & 1];
+        // dh[p][n] += sum_t (E_t dy[t][p]) C[t][n]; lane: row p = 16 wave + li of the A
+        // operand, tokens 32 ks + 8 g4 .. +7
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int tb = 32 * ks + 8 * g4;
-            const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(sE + tb);
-            const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(sE + tb + 4);
-            const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(sDy + (16 * wave + li) * kH0Row + 2 * tb);
+            const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(&sE[k & 1][tb]);
+            const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(&sE[k & 1][tb + 4]);
+            const u32x4_t dw = *reinterpret_cast<const u32x4_t*>(dv + (16 * wave + li) * kH0Row + 2 * tb);
             float av[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float ee = e < 4 ? e0[e] : e1[e - 4];
-                const uint32_t bits = (dv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t bits = (dw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                 av[e] = ee * __uint_as_float(bits << 16);
             }
             u32x4_t hv, lv;
@@ -471,29 +497,31 @@ scan_bwd_h0_mfma_kernel(const float* dt, const float* A, const uint16_t* Cm,
             }
             const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, hv), alo = __builtin_bit_cast(bf16x8_t, lv);
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(sCt + (16 * n + li) * kH0Row + 2 * tb);
+            for (int n = 0; n < 4; ++n) {
+                const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(ct + (16 * n + li) * kH0Row + 2 * tb);
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, acc[n], 0, 0, 0);
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, acc[n], 0, 0, 0);
             }
         }
-        const bool stop = sStop != 0;
-        __syncthreads();  // the tiles are consumed before the next chunk overwrites them
-        if (stop) break;
+        if (stop) break;  // uniform: every thread read the same flag
+        store(k + 1);     // the other buffer, last read before the previous barrier
+        if (wave == 0) scan_e(k + 1);
+        __syncthreads();
     }
     // the final state's term, E_{L-1} dF (zero after a sequence change or an underflow);
-    // lane holds dh[p][n] for p = 16 wave + 4 g4 + r, n = 16 nt + li
+    // lane holds dh[p][n] for p = 16 wave + 4 g4 + r, n = 64 nh + 16 nt + li
     __shared__ float sEnd;
+    __syncthreads();
     if (wave == 0 && lane == 0) sEnd = alive ? __builtin_amdgcn_exp2f(offset) : 0.0f;
     __syncthreads();
     const float eend = sEnd;
     float* out = dh0 + (b * H + h) * kH0P * kH0N;
     const float* fin = dfin ? dfin + (b * H + h) * kH0P * kH0N : nullptr;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int p = 16 * wave + 4 * g4 + rr, n = 16 * nt + li;
+            const int p = 16 * wave + 4 * g4 + rr, n = kNh * nh + 16 * nt + li;
             float v = acc[nt][rr];
             if (fin) v = __builtin_fmaf(eend, fin[p * kH0N + n], v);
             out[p * kH0N + n] = v;
@@ -620,7 +648,7 @@ hipError_t launch_scan_bwd_h0(const float* dt, const float* A, const void* Cm,
                               hipStream_t stream) {
     const bool a16 = (reinterpret_cast<uintptr_t>(Cm) % 16) == 0 && (reinterpret_cast<uintptr_t>(dy) % 16) == 0;
     if (dtype == SSM_BF16 && headdim == kH0P && dstate == kH0N && a16 && seqlen > 0) {
-        dim3 grid(static_cast<unsigned>(nheads), static_cast<unsigned>(batch));
+        dim3 grid(static_cast<unsigned>(nheads), static_cast<unsigned>(batch), 2);  // z: column half
         scan_bwd_h0_mfma_kernel<<<grid, 256, 0, stream>>>(
             dt, A, static_cast<const uint16_t*>(Cm), seq, static_cast<const uint16_t*>(dy), dfin,
             dh0, seqlen, nheads, ngroups);
