@@ -605,10 +605,11 @@ int orc_scan_fwd_vdecay(const double* x, const double* dt, const double* log_dec
             const int64_t grp = h / heads_per_group;
             double* hs = (double*)malloc(sizeof(double) * (size_t)(P * N));
             double* an = (double*)malloc(sizeof(double) * (size_t)N);
+            const int32_t* row_ids = seq_idx ? seq_idx + b * L : NULL;
             for (int64_t e = 0; e < P * N; ++e)
                 hs[e] = init_state ? init_state[(b * H + h) * P * N + e] : 0.0;
             for (int64_t t = 0; t < L; ++t) {
-                if (seq_idx && t > 0 && seq_idx[b * L + t] != seq_idx[b * L + t - 1])
+                if (row_ids && t > 0 && row_ids[t] != row_ids[t - 1])
                     for (int64_t e = 0; e < P * N; ++e) hs[e] = 0.0;
                 const double u = dt ? dt[(b * L + t) * H + h] : 1.0;
                 for (int64_t n = 0; n < N; ++n)

@@ -1000,7 +1000,6 @@ ALL_CHECKS = [
     check_update_equals_fwd,
     check_update_state_len_invariance,
     check_update_indices_and_range,
-    check_scan_variance_closed_form,
     check_scan_bruteforce_eq4,
     check_scan_initial_state_term,
     check_scan_superposition,
@@ -1028,4 +1027,6 @@ ALL_CHECKS = [
     check_vdecay_rate_form_is_gate_form,
     check_vdecay_constant_rates_lfilter,
     check_vdecay_chunks_and_resets,
+    # last: the Monte Carlo pin is the slowest, and the mutant test stops at the first failure
+    check_scan_variance_closed_form,
 ]

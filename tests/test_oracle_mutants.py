@@ -127,6 +127,8 @@ MUTANTS = {
     # vector decay: every head reads head 0's gates
     "vdecay_gate_head_0": ("an[n] = log_decay ? exp(log_decay[((b * L + t) * H + h) * N + n])",
                            "an[n] = log_decay ? exp(log_decay[((b * L + t) * H + 0) * N + n])"),
+    # vector decay: packed-sequence resets ignored
+    "vdecay_no_reset": ("if (row_ids && t > 0 && row_ids[t] != row_ids[t - 1])", "if (0)"),
     # vector decay: read-out before the update
     "vdecay_readout_lag": ("hs[p * N + n] = an[n] * hs[p * N + n] + u * xt[p] * Bt[n];\n                        out += Ct[n] * hs[p * N + n];",
                            "out += Ct[n] * hs[p * N + n];\n                        hs[p * N + n] = an[n] * hs[p * N + n] + u * xt[p] * Bt[n];"),
