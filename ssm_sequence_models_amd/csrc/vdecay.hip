@@ -20,8 +20,9 @@
 //   - the staging waves copy a tile of 16 tokens (B, C, the block's x, dt, and
 //     a_t[n] = exp(log a_t[n]), formed once per token and dimension; a_t = 0 where seq_idx
 //     starts a new sequence, which is the reset) into one of two LDS buffers while the
-//     compute waves consume the other; every load of a tile is issued before the first LDS
-//     store; one barrier per tile.
+//     compute waves consume the other.  A staging thread moves one (token, 8 dimensions)
+//     piece with 16-byte loads, and issues tile k+2's loads as soon as it has stored tile
+//     k+1, so they have a whole tile of compute to arrive; one barrier per tile.
 // Measured at the 1.3B-like shape (B 4, L 8192, 64 heads, gates [B, L, H, N]): one block per
 // (row, head) with a quarter row per lane 4.6 ms (LDS-return bound at 24 reads per token);
 // 4 x 8 blocks per lane 4.1 ms, 3.37 ms with batched staging loads, 3.31 ms with the
@@ -30,8 +31,10 @@
 // waves computing 4 x 4 blocks with a 32-lane ds_swizzle reduction 3.65-3.80 ms; this
 // layout, halves of the channels in two blocks per CU, 2.75 ms; quarters (one channel per
 // lane, four blocks per (row, head) re-staging the same gates) 4.9 ms; one block per (row,
-// head) with eight compute and four staging waves (no gate re-staging) 3.2 ms.
-// P = 64 and N in {64, 128}; other shapes use the general token-sequential kernel.
+// head) with eight compute and four staging waves (no gate re-staging) 3.2 ms.  With staging
+// switched off (work copy) the halves took 1.97 ms against 2.65: staging was not hidden;
+// 16-byte staging loads issued a tile ahead took the call to 2.37 ms.
+// bf16, P = 64 and N in {64, 128}; other cases use the general token-sequential kernel.
 #include "internal.h"
 
 namespace ssm {
@@ -76,8 +79,9 @@ __device__ __forceinline__ float rs16x2(const float (&v)[2], int lane) {
     return r;
 }
 
-template <class D, int N>
+template <int N>
 __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
+    using D = BF16;
     using T = typename D::T;
     constexpr int R = vd_row<N>();
     constexpr int oC = N, oA = 2 * N, oX = 3 * N, oU = 3 * N + kVdPh;
@@ -92,63 +96,81 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     const T* bs = static_cast<const T*>(a.Bm);
     const T* cs = static_cast<const T*>(a.Cm);
 
-    // staging: tile k of tokens into buffer k & 1 (staging waves only).  Every load of the
-    // tile is issued before the first LDS store (the loops have compile-time trip counts), so
-    // the tile costs about one global latency rather than one per element.
-    auto stage = [&](int64_t k) {
-        constexpr int kItems = kVdTile * N / kVdCompute;   // B / C / gate values per thread
-        constexpr int kXItems = kVdTile * kVdPh / kVdCompute;
-        const int st = tid - kVdCompute;
-        float* buf = lds + (k & 1) * (kVdTile * R);
+    // staging (waves 4-7): thread sti handles one (token, 8 dimensions) unit of B, C and the
+    // gates and one pair of x values per tile, as 16-byte (B, C, gates) and 4-byte (x) loads.
+    // The loads of tile k+2 are issued right after tile k+1 is stored, so they have a whole
+    // tile of compute to arrive (the registers hold one tile).
+    const int sti = tid - kVdCompute;
+    constexpr int kOct = N / 8;                    // 8-dimension pieces per token
+    const int su_t = sti / kOct, su_q = sti % kOct;  // unit: token su_t of the tile, piece su_q
+    const bool su_live = sti < kVdTile * kOct;
+    const int sx_t = sti / (kVdPh / 2), sx_p = 2 * (sti % (kVdPh / 2));  // x pair
+    uint4 rb, rc;
+    float4 rg0, rg1;
+    bool rr;
+    uint32_t rx;
+    float ru;
+    auto load_tile = [&](int64_t k) {
         const int64_t t0 = k * kVdTile;
         const int nt = static_cast<int>(min(static_cast<int64_t>(kVdTile), a.T - t0));
-        float vb[kItems], vc[kItems], vg[kItems], vx[kXItems];
-        bool rs[kItems];
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const int i = st + j * kVdCompute;
-            const int tt = i / N, n = i % N;
-            const int64_t t = t0 + tt;
-            vb[j] = vc[j] = vg[j] = 0.0f;
-            rs[j] = false;
-            if (tt < nt) {
-                vb[j] = D::load(bs, b * a.B_sb + t * a.B_st + (g * a.N + n) * a.B_sc);
-                vc[j] = D::load(cs, b * a.C_sb + t * a.C_st + (g * a.N + n) * a.C_sc);
-                vg[j] = a.log_decay ? a.log_decay[((b * a.T + t) * a.H + h) * N + n]
-                                    : a.dt[(b * a.T + t) * a.H + h] * a.A_vec[h * N + n];
-                // a reset (new sequence at t) zeroes the state before token t's update, which
-                // is the update with a_t = 0 (the state is finite)
-                rs[j] = a.seq_idx && t > 0 && a.seq_idx[b * a.T + t] != a.seq_idx[b * a.T + t - 1];
+        rb = rc = make_uint4(0, 0, 0, 0);
+        rg0 = rg1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        rr = false;
+        if (su_live && su_t < nt) {
+            const int64_t t = t0 + su_t;
+            rb = *reinterpret_cast<const uint4*>(bs + b * a.B_sb + t * a.B_st + g * a.N + 8 * su_q);
+            rc = *reinterpret_cast<const uint4*>(cs + b * a.C_sb + t * a.C_st + g * a.N + 8 * su_q);
+            if (a.log_decay) {
+                const float* gp = a.log_decay + ((b * a.T + t) * a.H + h) * N + 8 * su_q;
+                rg0 = *reinterpret_cast<const float4*>(gp);
+                rg1 = *reinterpret_cast<const float4*>(gp + 4);
+            } else {
+                const float d = a.dt[(b * a.T + t) * a.H + h];
+                const float4 v0 = *reinterpret_cast<const float4*>(a.A_vec + h * N + 8 * su_q);
+                const float4 v1 = *reinterpret_cast<const float4*>(a.A_vec + h * N + 8 * su_q + 4);
+                rg0 = make_float4(d * v0.x, d * v0.y, d * v0.z, d * v0.w);
+                rg1 = make_float4(d * v1.x, d * v1.y, d * v1.z, d * v1.w);
             }
+            // a reset (new sequence at t) zeroes the state before token t's update, which is
+            // the update with a_t = 0 (the state is finite)
+            rr = a.seq_idx && t > 0 && a.seq_idx[b * a.T + t] != a.seq_idx[b * a.T + t - 1];
         }
+        rx = 0u;
+        if (sx_t < nt)
+            rx = *reinterpret_cast<const uint32_t*>(xs + b * a.x_sb + (t0 + sx_t) * a.x_st +
+                                                    h * kVdP + kVdPh * half + sx_p);
+        ru = (sti < nt && a.dt) ? a.dt[(b * a.T + t0 + sti) * a.H + h] : 1.0f;
+    };
+    auto store_tile = [&](int64_t k) {
+        float* buf = lds + (k & 1) * (kVdTile * R);
+        const int nt = static_cast<int>(min(static_cast<int64_t>(kVdTile), a.T - k * kVdTile));
+        if (su_live && su_t < nt) {
+            float* row = buf + su_t * R + 8 * su_q;
+            const uint32_t wb[4] = {rb.x, rb.y, rb.z, rb.w}, wc[4] = {rc.x, rc.y, rc.z, rc.w};
+            float fb[8], fc[8];
 #pragma unroll
-        for (int j = 0; j < kXItems; ++j) {
-            const int i = st + j * kVdCompute;
-            const int tt = i / kVdPh, p = i % kVdPh;
-            vx[j] = tt < nt ? D::load(xs, b * a.x_sb + (t0 + tt) * a.x_st +
-                                              (h * kVdP + kVdPh * half + p) * a.x_sc)
-                            : 0.0f;
-        }
-        float vu = 1.0f;
-        if (st < nt && a.dt) vu = a.dt[(b * a.T + t0 + st) * a.H + h];
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const int i = st + j * kVdCompute;
-            const int tt = i / N, n = i % N;
-            if (tt < nt) {
-                float* row = buf + tt * R;
-                row[n] = vb[j];
-                row[oC + n] = vc[j];
-                row[oA + n] = rs[j] ? 0.0f : __expf(vg[j]);
+            for (int e = 0; e < 4; ++e) {
+                fb[2 * e] = __uint_as_float(wb[e] << 16);
+                fb[2 * e + 1] = __uint_as_float(wb[e] & 0xFFFF0000u);
+                fc[2 * e] = __uint_as_float(wc[e] << 16);
+                fc[2 * e + 1] = __uint_as_float(wc[e] & 0xFFFF0000u);
             }
+            *reinterpret_cast<float4*>(row) = make_float4(fb[0], fb[1], fb[2], fb[3]);
+            *reinterpret_cast<float4*>(row + 4) = make_float4(fb[4], fb[5], fb[6], fb[7]);
+            *reinterpret_cast<float4*>(row + oC) = make_float4(fc[0], fc[1], fc[2], fc[3]);
+            *reinterpret_cast<float4*>(row + oC + 4) = make_float4(fc[4], fc[5], fc[6], fc[7]);
+            float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+            if (!rr) {
+                a0 = make_float4(__expf(rg0.x), __expf(rg0.y), __expf(rg0.z), __expf(rg0.w));
+                a1 = make_float4(__expf(rg1.x), __expf(rg1.y), __expf(rg1.z), __expf(rg1.w));
+            }
+            *reinterpret_cast<float4*>(row + oA) = a0;
+            *reinterpret_cast<float4*>(row + oA + 4) = a1;
         }
-#pragma unroll
-        for (int j = 0; j < kXItems; ++j) {
-            const int i = st + j * kVdCompute;
-            const int tt = i / kVdPh, p = i % kVdPh;
-            if (tt < nt) buf[tt * R + oX + p] = vx[j];
-        }
-        if (st < nt) buf[st * R + oU] = vu;
+        if (sx_t < nt)
+            *reinterpret_cast<float2*>(buf + sx_t * R + oX + sx_p) =
+                make_float2(__uint_as_float(rx << 16), __uint_as_float(rx & 0xFFFF0000u));
+        if (sti < nt) buf[sti * R + oU] = ru;
     };
 
     // compute lanes: channels p0, p0 + 1, dimensions n0 .. n0 + NL - 1
@@ -170,7 +192,9 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
                 st[i][4 * c + 2] = v.z; st[i][4 * c + 3] = v.w;
             }
     } else {
-        stage(0);
+        load_tile(0);
+        store_tile(0);
+        if (ntiles > 1) load_tile(1);
     }
     __syncthreads();
 
@@ -230,7 +254,8 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
                 if ((tid & 7) == 0) D::store(y_p, (t0 + nt - 1) * y_tok, yv);
             }
         } else if (k + 1 < ntiles) {
-            stage(k + 1);
+            store_tile(k + 1);  // the other buffer, last read before the previous barrier
+            if (k + 2 < ntiles) load_tile(k + 2);
         }
         __syncthreads();
     }
@@ -248,20 +273,23 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
 
 bool vdecay_supported(int64_t P, int64_t N) { return P == kVdP && (N == 64 || N == 128); }
 
+// bf16 rows with 16-byte aligned, contiguous B / C / gate pieces take vdecay_kernel; anything
+// else the general token-sequential kernel's vector mode
 hipError_t launch_vdecay(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
+    const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.Bm) |
+                         reinterpret_cast<uintptr_t>(a.Cm) | reinterpret_cast<uintptr_t>(a.log_decay) |
+                         reinterpret_cast<uintptr_t>(a.A_vec);
+    const bool fast = dtype == SSM_BF16 && vdecay_supported(a.P, a.N) && (al & 15) == 0 &&
+                      a.x_sc == 1 && a.B_sc == 1 && a.C_sc == 1 && a.B_st % 8 == 0 &&
+                      a.C_st % 8 == 0 && a.B_sb % 8 == 0 && a.C_sb % 8 == 0 &&
+                      a.x_st % 2 == 0 && a.x_sb % 2 == 0;
+    if (!fast) return launch_recurrent(a, dtype, stream);
     dim3 grid(static_cast<unsigned>(a.H), static_cast<unsigned>(a.B), 2);  // z: channel half
-    if (a.N == 128) {
-        if (dtype == SSM_BF16)
-            vdecay_kernel<BF16, 128><<<grid, kVdThreads, 0, stream>>>(a);
-        else
-            vdecay_kernel<F32, 128><<<grid, kVdThreads, 0, stream>>>(a);
-    } else {
-        if (dtype == SSM_BF16)
-            vdecay_kernel<BF16, 64><<<grid, kVdThreads, 0, stream>>>(a);
-        else
-            vdecay_kernel<F32, 64><<<grid, kVdThreads, 0, stream>>>(a);
-    }
+    if (a.N == 128)
+        vdecay_kernel<128><<<grid, kVdThreads, 0, stream>>>(a);
+    else
+        vdecay_kernel<64><<<grid, kVdThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
