@@ -128,11 +128,21 @@ __global__ __launch_bounds__(256) void noise_kernel(float* out, int64_t n, int64
 #pragma unroll
     for (int j = 0; j < 4; ++j) box_muller(w.v[j], z[2 * j], z[2 * j + 1]);
     if (mean) {
-        // the eight elements span at most two heads when per >= 8
+        // one 64-bit division per thread: with per >= 8 the eight elements span at most two
+        // heads, h0 and the next one
+        const int64_t q = e0 / per, rem = e0 - q * per, h0 = q % H;
+        const int64_t h1 = h0 + 1 == H ? 0 : h0 + 1;
+        const float m0 = mean[h0], s0 = sqrtf(var[h0]);
+        const float m1 = mean[h1], s1 = sqrtf(var[h1]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t h = ((e0 + j) / per) % H;
-            z[j] = mean[h] + sqrtf(var[h]) * z[j];
+            if (per >= 8) {
+                const bool next = rem + j >= per;
+                z[j] = (next ? m1 : m0) + (next ? s1 : s0) * z[j];
+            } else {
+                const int64_t h = ((e0 + j) / per) % H;
+                z[j] = mean[h] + sqrtf(var[h]) * z[j];
+            }
         }
     } else {
 #pragma unroll
