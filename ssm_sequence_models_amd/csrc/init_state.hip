@@ -84,18 +84,34 @@ __global__ __launch_bounds__(kStatsThreads) void state_stats_kernel(
     const bool vec = (per % 4) == 0 && (reinterpret_cast<uintptr_t>(fin) & 15) == 0;
     const double shift = fin[h * per];
     double s1 = 0.0, s2 = 0.0;
-    for (int64_t b = 0; b < B; ++b) {
+    auto acc4 = [&](const float4 q) {
+        const double d0 = q.x - shift, d1 = q.y - shift, d2 = q.z - shift, d3 = q.w - shift;
+        s1 += (d0 + d1) + (d2 + d3);
+        s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+    };
+    int64_t b0 = 0;
+    if (vec) {
+        // four rows at a time, so each thread has several 16-byte loads in flight (a head's
+        // slice of one row is only a couple of loads per thread)
+        const int64_t n4 = per / 4;
+        for (; b0 + 4 <= B; b0 += 4) {
+            for (int64_t i = threadIdx.x; i < n4; i += kStatsThreads) {
+                float4 q[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    q[r] = reinterpret_cast<const float4*>(fin + ((b0 + r) * H + h) * per)[i];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc4(q[r]);
+            }
+        }
+    }
+    for (int64_t b = b0; b < B; ++b) {
         const float* row = fin + (b * H + h) * per;
         if (vec) {
             const float4* r4 = reinterpret_cast<const float4*>(row);
             const int64_t n4 = per / 4;
 #pragma unroll 4
-            for (int64_t i = threadIdx.x; i < n4; i += kStatsThreads) {
-                const float4 q = r4[i];
-                const double d0 = q.x - shift, d1 = q.y - shift, d2 = q.z - shift, d3 = q.w - shift;
-                s1 += (d0 + d1) + (d2 + d3);
-                s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
-            }
+            for (int64_t i = threadIdx.x; i < n4; i += kStatsThreads) acc4(r4[i]);
         } else {
             for (int64_t i = threadIdx.x; i < per; i += kStatsThreads) {
                 const double d = row[i] - shift;
