@@ -34,6 +34,8 @@ POOL_CASES = [
     (3, 70, 2, 64, 128, 1, 4, BF16, 3, 4, True, [2, 7, 0], 0),   # row 1: slot out of range
     (2, 40, 2, 16, 32, 1, 4, F32, 3, 5, True, [1, 2], 0),        # general shapes
     (2, 2, 2, 64, 128, 1, 4, BF16, 2, 4, True, [1, 0], 0),       # L < K-1
+    (2, 2, 2, 64, 128, 1, 4, BF16, 3, 5, False, [2, 0], 0),      # linear, L < state_len
+    (3, 90, 2, 64, 128, 1, 4, BF16, 4, 4, False, [3, 1, 0], 2),  # linear, packed rows
 ]
 
 

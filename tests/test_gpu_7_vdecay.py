@@ -37,6 +37,8 @@ CASES = [
     (2, 100, 4, 16, 32, 2, F32, "gate", True, True, 2),
     (1, 77, 3, 4, 8, 1, F32, "rate", True, True, 0),
     (2, 1, 2, 64, 128, 1, BF16, "gate", True, True, 0),      # one token
+    (2, 150, 4, 64, 128, 1, BF16, "rate", True, True, 3),    # rates, resets folded into a_t = 0
+    (1, 70, 2, 64, 128, 1, F32, "gate", True, True, 2),      # fp32: the general kernel
 ]
 
 
