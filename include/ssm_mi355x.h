@@ -180,8 +180,10 @@ ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const 
  *                  NULL; final_state may alias initial_state
  *   seq_idx        [batch, seqlen] int32, or NULL
  * Token-sequential: the state stays in registers, the decays a_t[n] are formed once per
- * token and dimension.  dstate = 4 * 2^k <= 256, headdim * dstate <= 16384.
- * seqlen = 0: final_state = initial_state (or zero).
+ * token and dimension.  dstate = 4 * 2^k <= 256, headdim * dstate <= 16384.  bf16 with
+ * headdim 64, dstate 64 or 128 and 16-byte aligned x, B, C, log_decay / A_vec runs on the
+ * long-row kernel; other cases on the general token-sequential one (same results to
+ * rounding).  seqlen = 0: final_state = initial_state (or zero).
  * ------------------------------------------------------------------------------------- */
 ssm_status_t ssm_scan_fwd_vector_decay(const void* x, const float* dt, const float* log_decay,
                                        const float* A_vec, const void* B, const void* C,
