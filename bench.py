@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (FMA counted as two flops)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 # MFMAs the main kernel issues per (batch row, head, 64-token chunk): 4 consumer waves x (12
 # intra-chunk + 32 initial-state + 32 state-update), each a 16x16x32 bf16 product
@@ -108,11 +109,11 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     g = torch.Generator(device=dev)
     res = []
 
-    def rep(op, workload, ms, tokens, nbytes):
+    def rep(op, workload, ms, tokens, nbytes, extra=None):
         res.append({"op": op, "workload": workload, "ms": ms, "tokens_per_s": tokens / (ms * 1e-3),
                     "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                     "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "frac_of_copy": nbytes / (ms * 1e-3) / 1e9 / copy_GBs})
+                    "frac_of_copy": nbytes / (ms * 1e-3) / 1e9 / copy_GBs, **(extra or {})})
 
     def prefill_inputs(s, seed):
         g.manual_seed(seed)
@@ -251,8 +252,17 @@ def other_ops(torch, ssm, workloads, copy_GBs):
                                                             y=yv), 5)
     nb = (s.B * s.L * (2 * s.H * s.P * 2 + s.H * s.N * 4 + 2 * s.N * 2 + s.H * 4)
           + 2 * s.B * s.H * s.P * s.N * 4)
+    # the recurrence is bound by fp32 vector arithmetic, not HBM: per (token, channel, state
+    # dimension) one decay multiply and two fused multiply-adds (input, read-out), 5 flops;
+    # the issue floor counts those 3 instructions at 64 lanes per CU per clock (no packed fp32)
+    elems = s.B * s.L * s.H * s.P * s.N
+    floor_ms = 3 * elems / (256 * 64 * 2.4e9) * 1e3
     rep("scan_fwd_vector_decay", f"1.3B-like B{s.B} L{s.L} H{s.H}x{s.P} N{s.N} bf16, per-dimension "
-        "log gates [B, L, H, N] fp32, dt, initial / final state", ms, s.B * s.L, nb)
+        "log gates [B, L, H, N] fp32, dt, initial / final state", ms, s.B * s.L, nb,
+        {"bound": "alu", "flops": 5 * elems, "achieved_TFLOPs": 5 * elems / (ms * 1e-3) / 1e12,
+         "peak_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
+         "frac_alu": 5 * elems / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+         "issue_floor_ms": floor_ms, "frac_of_issue_floor": floor_ms / ms})
     del xv, Bv, Cv, dtv, gate, yv
 
     # backward of the unfused conv at the 1.3B shape, with state gradients
