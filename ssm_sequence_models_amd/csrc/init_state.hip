@@ -21,6 +21,19 @@ struct U64x4 {
     uint64_t v[4];
 };
 
+// The full 128-bit product m c from four 32 x 32 -> 64-bit partial products, shared by both
+// halves (a separate high product and 64-bit low product recompute some of them).  No sum
+// overflows: (2^32 - 1)^2 + 2 (2^32 - 1) < 2^64.
+__device__ __forceinline__ void mul128(uint64_t m, uint64_t c, uint64_t& hi, uint64_t& lo) {
+    const uint64_t ml = static_cast<uint32_t>(m), mh = m >> 32;
+    const uint64_t cl = static_cast<uint32_t>(c), ch = c >> 32;
+    const uint64_t ll = ml * cl;
+    const uint64_t t = ml * ch + (ll >> 32);
+    const uint64_t u = mh * cl + static_cast<uint32_t>(t);
+    hi = mh * ch + (t >> 32) + (u >> 32);
+    lo = (u << 32) | static_cast<uint32_t>(ll);
+}
+
 // ten rounds: multiply counter words 0 and 2 by the two round constants, swap the 128-bit
 // products' halves into the new counter with the round key mixed into the high halves, and
 // advance the key by the Weyl increments between rounds
@@ -30,8 +43,9 @@ __device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_
     constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint64_t hi0 = __umul64hi(kM0, c0), lo0 = kM0 * c0;
-        const uint64_t hi1 = __umul64hi(kM1, c2), lo1 = kM1 * c2;
+        uint64_t hi0, lo0, hi1, lo1;
+        mul128(kM0, c0, hi0, lo0);
+        mul128(kM1, c2, hi1, lo1);
         const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
         c0 = n0;
         c1 = lo1;
