@@ -36,6 +36,7 @@
 // 16-byte staging loads issued a tile ahead took the call to 2.37 ms.  In this layout, 4 x 4
 // blocks per lane (four LDS reads per token instead of seven, a 32-lane reduce-scatter with
 // one ds_swizzle level) ran 2.25 ms against 2.13 for 2 x 8 blocks, timed side by side.
+// Raising the compute or the staging waves' issue priority (s_setprio 2) changed nothing.
 // bf16, P = 64 and N in {64, 128}; other cases use the general token-sequential kernel.
 #include "internal.h"
 
