@@ -98,6 +98,22 @@ __device__ __forceinline__ void split_hilo(const float (&v)[8], bf16x8& hi, bf16
     lo = __builtin_bit_cast(bf16x8, l);
 }
 
+__device__ __forceinline__ void split_hilo4(const float (&v)[4], u32x2& hi, u32x2& lo) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    uint32_t c_lo = 0x0000BF80u, c_hi = 0xBF800000u;
+    asm volatile("" : "+s"(c_lo), "+s"(c_hi));
+    const bf16x2v neg_lo = __builtin_bit_cast(bf16x2v, c_lo);  // (-1, 0)
+    const bf16x2v neg_hi = __builtin_bit_cast(bf16x2v, c_hi);  // (0, -1)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const uint32_t hp = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        const bf16x2v hv = __builtin_bit_cast(bf16x2v, hp);
+        hi[e] = hp;
+        lo[e] = pack_bf16x2(__builtin_amdgcn_fdot2_f32_bf16(hv, neg_lo, v[2 * e], false),
+                            __builtin_amdgcn_fdot2_f32_bf16(hv, neg_hi, v[2 * e + 1], false));
+    }
+}
+
 // Inclusive prefix over the 64 lanes of a wavefront with DPP: row_shr 1/2/4/8 inside each
 // row of 16 lanes, then row_bcast 15 / 31 carry the row totals forward.
 __device__ __forceinline__ float wave_incl_sum(float v) {
@@ -287,13 +303,22 @@ ssd_prep_kernel(ChunkedArgs a) {
 constexpr int kCbC = 0;                          // C   [64 tok][16 pieces], piece ^ (tok & 15)
 constexpr int kCbBt = kCbC + kQ * 256;           // B^T [128 n][8 pieces], piece ^ bt_swz(n)
 constexpr int kCbBytes = kCbBt + kN * 128;
-//   stage s (two, by chunk parity), produced one chunk ahead of its use:
+//   M stage s (two, by chunk parity), produced one chunk ahead of its use:
 constexpr int kStMhi = 0;                        // M   [64 i][8 pieces], piece ^ (i & 7)
 constexpr int kStMlo = kStMhi + kQ * 128;
-constexpr int kStE = kStMlo + kQ * 128;          // E_i = exp(cum_i) on the leading segment
-constexpr int kStW = kStE + kQ * 4;              // W_j = exp(cum_last - cum_j) dt_j
-constexpr int kStDecay = kStW + kQ * 4;          // exp(cum_last) (0 after a reset)
-constexpr int kStageBytes = kStDecay + 16;
+constexpr int kStageBytes = kStMlo + kQ * 128;
+//   scalar stage (three, by chunk index mod 3), produced two chunks ahead of its use: in the
+//   iteration that contracts chunk c, the consumers read chunk c's E / W / decay, the
+//   producers build chunk c+1's M tiles from its cum / R / r, and write chunk c+2's scalars
+constexpr int kScCum = 0;                        // cum2_j = log2(e) sum_{tau<=j} dt_tau A
+constexpr int kScDt = kScCum + kQ * 4;           // dt_j
+constexpr int kScR = kScDt + kQ * 4;             // r_j, the last reset <= j (-1: none)
+constexpr int kScRf = kScR + kQ * 4;             // R_j = 2^(cum2_{j&~7} - cum2_j) dt_j
+constexpr int kScE = kScRf + kQ * 4;             // E_i = exp(cum_i) on the leading segment
+constexpr int kScW = kScE + kQ * 4;              // W_j = exp(cum_last - cum_j) dt_j
+constexpr int kScDecay = kScW + kQ * 4;          // exp(cum_last) (0 after a reset), 4 copies
+constexpr int kScFactored = kScDecay + 16;       // 1 when the factored M exponentials apply
+constexpr int kScBytes = kScFactored + 16;
 //   raw x slot (three, by chunk index mod 3), loaded two chunks ahead: the conv of chunk c+1
 //   runs while chunk c is contracted, and chunk c's rows stay for the consumers' exact
 //   recomputation of the conv outputs the fast path flagged
@@ -303,23 +328,21 @@ constexpr int kRwSeq = (kRowsMax + 1) * 128;     // seq ids of the raw rows (aft
                                                  // the loads fill 9 blocks of 8 rows)
 constexpr int kRwClean = kRwSeq + 72 * 4;        // bit r: run r's taps carry one id (see clean_runs)
 constexpr int kRawBytes = kRwClean + 16;
-//   producer-private scalars: cum, dtv, r of the chunk
-constexpr int kPsBytes = 4 * kQ * 4;  // per producer wave: cum2, dt, last reset, R
 //   X slot (two, by chunk parity): the conv waves' bf16 outputs (X operands), 16 bytes per
 //   (wave, lane, run), read back by the consumer lane with the same wave-in-role and lane index
 constexpr int kXBytes = kQ * kP * 2;
 //   flag slot (two, by chunk parity): per X slot lane, one 16-bit mask per 8-output run of
 //   the outputs the conv's fast path could not round with certainty
 constexpr int kFlBytes = 4 * 64 * 4;
-constexpr int kOffPs = 2 * kStageBytes;
-constexpr int kOffX = kOffPs + 4 * kPsBytes;
+constexpr int kOffSc = 0;
+constexpr int kOffX = kOffSc + 3 * kScBytes;
 constexpr int kOffFl = kOffX + 2 * kXBytes;
 //   conv weights and bias of the head's x channels in double (with a conv), for the out-of-line
 //   recomputations (flagged outputs, masked runs): channel p at kOffW + p * kWStride
 constexpr int kWStride = (kKmax + 1) * 8;
 constexpr int kOffW = kOffFl + 2 * kFlBytes;
 constexpr int kMainLds = kOffW + kP * kWStride;
-static_assert(kMainLds + 2 * kCbBytes + 3 * kRawBytes <= 160 * 1024, "LDS budget");
+static_assert(kMainLds + 2 * kStageBytes + 2 * kCbBytes + 3 * kRawBytes <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int sw_c(int tok, int q) { return tok * 256 + ((q ^ (tok & 15)) << 4); }
 // B^T rows are read through the state-tile row map n = 32T + 8(l>>2) + 4(t&1) + (l&3):
@@ -333,15 +356,16 @@ __device__ __forceinline__ int sw_xr(int row, int q) {
     return row * 128 + ((q ^ (((row >> 3) & 3) << 1)) << 4);
 }
 
-// M tiles computed by each producer wave pw (uniform): unit u is the 16 x 32 tile (row
-// block I, column half S); the six tiles cover j <= i.  Waves 2 and 3 have one tile each
-// and compute it twice (identical values to identical addresses), which keeps the code free
-// of branches.
-//   pw 0: (0,0) (3,0)   pw 1: (1,0) (2,1)   pw 2: (2,0) (2,0)   pw 3: (3,1) (3,1)
-__device__ __forceinline__ int unit_I(int pw, int u) { return (u == 0 || pw >= 2) ? pw : 3 - pw; }
-__device__ __forceinline__ int unit_S(int pw, int u) {
-    return (u == 0 || pw >= 2) ? (pw == 3 ? 1 : 0) : pw;
-}
+// M is built in 16 x 16 blocks (row block I, column block J <= I: ten blocks cover j <= i);
+// the consumers read it as six 16 x 32 MFMA operands, whose two blocks above the diagonal,
+// (0, 1) and (2, 3), stay zero (written once).  Each producer wave pw (uniform) builds three
+// blocks, slot s; waves 2 and 3 have two blocks each and build one of them twice
+// (identical values to identical addresses), which keeps the code free of branches.
+//   pw 0: (0,0) (1,0) (1,1)   pw 1: (2,0) (2,1) (2,2)   pw 2: (3,0) (3,1) (3,0)
+//   pw 3: (3,2) (3,3) (3,2)
+//   (two bits per entry, entry 3 pw + s)
+__device__ __forceinline__ int blk_I(int pw, int s) { return (0xFFFA94u >> (2 * (3 * pw + s))) & 3; }
+__device__ __forceinline__ int blk_J(int pw, int s) { return (0xB84910u >> (2 * (3 * pw + s))) & 3; }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0 and stores past
 // it are dropped by the hardware range check, which handles the ragged last chunk.
@@ -349,6 +373,9 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
 // 11:8): wait until at most 0 / 2 vector-memory operations are outstanding
 constexpr int kWaitVm0 = 0x0F70;
+// vector-memory loads of the producer's registers (fetch_g, fetch_s) per iteration
+template <bool HAS_SEQ, int PASS>
+constexpr int reg_loads() { return (PASS == 0 ? 3 : 0) + 1 + (HAS_SEQ ? 2 : 0); }
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7FFFFFFFLL ? 0x7FFFFFFFLL : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
@@ -383,15 +410,18 @@ struct POff {
     uint32_t c[4];          // C tile LDS block r = 4 pw + k: token 4r + l/16, slot l%16
     uint32_t bt[4];         // B^T tile LDS block r = 4 pw + k: row n = 8r + l/8, slot l%8
     uint32_t x[3];          // raw x LDS blocks r = pw, pw + 4, 8: row 8r + l/8, slot l%8
-    uint32_t g[2];          // G piece of M unit u: row i, columns 8q .. 8q+7
+    uint32_t g[3];          // G piece of M block slot s: row i, columns 4 lanes' worth
     uint32_t dt;            // token = lane
 };
 
-// Registers a producer lane loads for chunk k (its M tiles and scalars)
-struct Fetch {
-    u32x4 gm[2][2];
+// Registers a producer lane loads ahead of use: a chunk's dt and ids (its scalars, two
+// chunks ahead of the contraction) and a chunk's G pieces (its M blocks, one chunk ahead)
+struct FetchS {
     uint32_t dt;
     int32_t seq_j, seq_prev;
+};
+struct FetchG {
+    u32x4 gm[3];
 };
 
 __device__ __forceinline__ void dma16(Rsrc r, uint32_t voff, uint8_t* lds) {
@@ -411,25 +441,27 @@ __device__ __forceinline__ void fetch_tiles(const Blk& bk, const POff& o, int64_
     }
 }
 
-// Chunk k's G pieces (not in the state-only pass), dt and ids into registers
-template <bool HAS_SEQ, int PASS>
-__device__ __forceinline__ void fetch_regs(const Blk& bk, const POff& o, int64_t k, int pw,
-                                           int lane, Fetch& f) {
-    const int t0 = static_cast<int>(k) * kQ;
-    const Rsrc rg = make_rsrc(bk.wsG + k * bk.ws_step * kWsG, kWsG * 4);
+// Chunk k's G pieces into registers (the state-only pass has no M)
+template <int PASS>
+__device__ __forceinline__ void fetch_g(const Blk& bk, const POff& o, int64_t k, FetchG& f) {
+    if (PASS == 0) {
+        const Rsrc rg = make_rsrc(bk.wsG + k * bk.ws_step * kWsG, kWsG * 4);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        if (PASS == 0) {
-            f.gm[u][0] = bload128(rg, o.g[u]);
-            f.gm[u][1] = bload128(rg, o.g[u] + 16);
-        }
+        for (int s = 0; s < 3; ++s) f.gm[s] = bload128(rg, o.g[s]);
     }
+}
+
+// Chunk k's dt and ids into registers; past the row's end the range check returns zeros
+template <bool HAS_SEQ>
+__device__ __forceinline__ void fetch_s(const Blk& bk, const POff& o, int64_t k, int lane,
+                                        FetchS& f) {
+    const int t0 = static_cast<int>(k) * kQ;
     const Rsrc rd = make_rsrc(bk.dt + static_cast<int64_t>(t0) * bk.H, static_cast<int64_t>(bk.L - t0) * bk.H * 4);
     f.dt = bload32(rd, o.dt);
     if (HAS_SEQ) {
         const Rsrc rs = make_rsrc(bk.seq + t0, static_cast<int64_t>(bk.L - t0) * 4);
         f.seq_j = static_cast<int32_t>(bload32(rs, lane * 4));
-        f.seq_prev = bk.seq[t0 > 0 ? t0 - 1 : 0];
+        f.seq_prev = bk.seq[t0 <= 0 ? 0 : (t0 <= bk.L ? t0 - 1 : bk.L - 1)];
     }
 }
 
@@ -526,23 +558,17 @@ __device__ __forceinline__ void stage_raw_first(const ChunkedArgs& a, const Blk&
     }
 }
 
-// Chunk scalars and this wave's M tiles for chunk k, from the fetched dt / ids / G pieces:
+// Chunk k's scalars from its fetched dt / ids, into scalar stage `sc` (every producer wave
+// computes and writes the same values, which keeps the code free of branches):
 //   cum2_j = log2(e) * sum_{tau<=j} dt_tau A (wave prefix scan), r_j = last reset <= j,
 //   E_i = 2^cum2_i, W_j = 2^(cum2_last - cum2_j) dt_j, decay = 2^cum2_last,
-//   M[i][j] = G[i][j] 2^(cum2_i - cum2_j) dt_j on r_i <= j <= i (G is 0 above the diagonal).
-// A lane's M entries share the row i and a group of 8 columns j0 = 8 floor(j/8) .. j0+7, so
-// the exponential splits into 2^(cum2_i - cum2_j0) (one per lane) times
-// R_j = 2^(cum2_j0 - cum2_j) dt_j (one per column, shared by all rows).  That product stays in
-// range when cum2 never increases within the chunk and each group spans at most 64 (then
-// R_j <= 2^64 dt_j and the row factor <= 1 on and below the diagonal); a chunk that breaks
-// either condition takes one exponential per entry.
+//   R_j = 2^(cum2_{j0} - cum2_j) dt_j with j0 = j & ~7 (the column factor of M, below).
+// The factored form of M's exponentials holds when cum2 never increases within the chunk and
+// each 8-column group spans at most 64 (then R_j <= 2^64 dt_j and the row factor <= 1 on and
+// below the diagonal); otherwise the M blocks take one exponential per entry.
 template <bool HAS_SEQ, int PASS>
-__device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, float Ah2,
-                                              int pw, int lane, uint8_t* st, uint8_t* ps) {
-    float* pcum = reinterpret_cast<float*>(ps);
-    float* pdtv = pcum + kQ;
-    int32_t* pr = reinterpret_cast<int32_t*>(pdtv + kQ);
-    float* pR = reinterpret_cast<float*>(pr + kQ);
+__device__ __forceinline__ void chunk_scalars(const FetchS& f, int64_t k, int L, float Ah2,
+                                              int lane, uint8_t* sc) {
     const int t0 = static_cast<int>(k) * kQ;
     const int j = lane;
     const float dtv = __uint_as_float(f.dt);
@@ -555,65 +581,83 @@ __device__ __forceinline__ void scalars_and_m(const Fetch& f, int64_t k, int L, 
         const int rst = (t0 + j < L && t0 + j > 0 && f.seq_j != sjm1) ? j : -1;
         r = wave_incl_max(rst);
     }
-    pcum[j] = cum;
-    pdtv[j] = dtv;
-    if (HAS_SEQ) pr[j] = r;
-    {
-        // every producer wave writes the same E / W / decay values (no branch)
-        const float cum_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kQ - 1));
-        const int r_last = HAS_SEQ ? __builtin_amdgcn_readlane(r, kQ - 1) : -1;
-        float* sE = reinterpret_cast<float*>(st + kStE);
-        float* sW = reinterpret_cast<float*>(st + kStW);
-        sE[j] = r < 0 ? __builtin_amdgcn_exp2f(cum) : 0.0f;
-        sW[j] = j >= r_last ? __builtin_amdgcn_exp2f(cum_last - cum) * dtv : 0.0f;
-        // decay slot: lanes 0-3 of each wave write 4 copies; consumers read copy 0
-        const float dec = r_last < 0 ? __builtin_amdgcn_exp2f(cum_last) : 0.0f;
-        reinterpret_cast<float*>(st + kStDecay)[j & 3] = dec;
-    }
+    const float cum_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kQ - 1));
+    const int r_last = HAS_SEQ ? __builtin_amdgcn_readlane(r, kQ - 1) : -1;
+    reinterpret_cast<float*>(sc + kScE)[j] = r < 0 ? __builtin_amdgcn_exp2f(cum) : 0.0f;
+    reinterpret_cast<float*>(sc + kScW)[j] = j >= r_last ? __builtin_amdgcn_exp2f(cum_last - cum) * dtv : 0.0f;
+    // decay slot: lanes 0-3 write 4 copies; consumers read copy 0
+    reinterpret_cast<float*>(sc + kScDecay)[j & 3] = r_last < 0 ? __builtin_amdgcn_exp2f(cum_last) : 0.0f;
     if (PASS == 1) return;  // the state-only pass needs W and the decay alone
-    // column factors: cum2 of the group's first column from lane j & ~7 (swizzle within
-    // 32-lane halves: and-mask 0x18)
+    reinterpret_cast<float*>(sc + kScCum)[j] = cum;
+    reinterpret_cast<float*>(sc + kScDt)[j] = dtv;
+    if (HAS_SEQ) reinterpret_cast<int32_t*>(sc + kScR)[j] = r;
+    // cum2 of the group's first column from lane j & ~7 (swizzle within 32-lane halves:
+    // and-mask 0x18)
     const float cg = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(cum), 0x0018));
     const float span = cg - cum;
-    pR[j] = __builtin_amdgcn_exp2f(span) * dtv;
+    reinterpret_cast<float*>(sc + kScRf)[j] = __builtin_amdgcn_exp2f(span) * dtv;
     const bool factored = __ballot(!(a2 <= 0.0f && span <= 64.0f)) == 0;  // NaN -> direct
+    reinterpret_cast<int32_t*>(sc + kScFactored)[j & 3] = factored ? 1 : 0;
+}
+
+// This wave's three 16 x 16 blocks of chunk k's M = G o 2^(cum2_i - cum2_j) dt_j on
+// r_i <= j <= i (G is 0 above the diagonal), from the chunk's scalar stage `sc` (written in an
+// earlier iteration) and the G pieces fetched for it, split hi / lo (MBlk, stored into an M
+// stage by store_m).  A lane holds row i = 16 I + l % 16 and columns j0 .. j0+3,
+// j0 = 16 J + 4 (l / 16); these share the 8-column group of j0 & ~7, so the exponential
+// splits into the row factor 2^(cum2_i - cum2_{j0 & ~7}) (one per lane) times the column
+// factors R_j.
+struct MBlk {
+    u32x2 hi[3], lo[3];
+};
+template <bool HAS_SEQ>
+__device__ __forceinline__ void m_blocks(const FetchG& f, int pw, int lane, const uint8_t* sc,
+                                         MBlk& mb) {
+    const bool factored = __builtin_amdgcn_readfirstlane(lds_ld<int32_t>(sc, kScFactored)) != 0;
+    float mv[3][4];
+    if (factored) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int I = unit_I(pw, u), S = unit_S(pw, u);
-        const bool diag = 32 * S + 31 > 16 * I;
-        const int i = 16 * I + (lane & 15), q = 4 * S + (lane >> 4), j0 = 8 * q;
-        const float ci = pcum[i];
-        const int ri = HAS_SEQ ? pr[i] : -1;
-        float mv[8];
-        if (factored) {
-            const float prow = __builtin_amdgcn_exp2f(ci - pcum[j0]);
-            const f32x4 r0 = lds_ld<f32x4>(ps, 3 * kQ * 4 + j0 * 4), r1 = lds_ld<f32x4>(ps, 3 * kQ * 4 + j0 * 4 + 16);
+        for (int s = 0; s < 3; ++s) {
+            const int i = 16 * blk_I(pw, s) + (lane & 15), j0 = 16 * blk_J(pw, s) + 4 * (lane >> 4);
+            const float prow = __builtin_amdgcn_exp2f(lds_ld<float>(sc, kScCum + i * 4) -
+                                                      lds_ld<float>(sc, kScCum + (j0 & ~7) * 4));
+            const f32x4 rj = lds_ld<f32x4>(sc, kScRf + j0 * 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float rj = e < 4 ? r0[e] : r1[e - 4];
-                mv[e] = __uint_as_float(f.gm[u][e >> 2][e & 3]) * rj * prow;
-            }
-        } else {
-            const f32x4 cj0 = lds_ld<f32x4>(ps, j0 * 4), cj1 = lds_ld<f32x4>(ps, j0 * 4 + 16);
-            const f32x4 dj0 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4), dj1 = lds_ld<f32x4>(ps, kQ * 4 + j0 * 4 + 16);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float cj = e < 4 ? cj0[e] : cj1[e - 4];
-                const float dj = e < 4 ? dj0[e] : dj1[e - 4];
-                mv[e] = __uint_as_float(f.gm[u][e >> 2][e & 3]) * __builtin_amdgcn_exp2f(ci - cj) * dj;
-            }
+            for (int e = 0; e < 4; ++e) mv[s][e] = __uint_as_float(f.gm[s][e]) * rj[e] * prow;
         }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float m = mv[e];
-            if (diag) m = j0 + e <= i ? m : 0.0f;   // overflow / 0 * inf above the diagonal
+        for (int s = 0; s < 3; ++s) {
+            const int i = 16 * blk_I(pw, s) + (lane & 15), j0 = 16 * blk_J(pw, s) + 4 * (lane >> 4);
+            const float ci = lds_ld<float>(sc, kScCum + i * 4);
+            const f32x4 cj = lds_ld<f32x4>(sc, kScCum + j0 * 4);
+            const f32x4 dj = lds_ld<f32x4>(sc, kScDt + j0 * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mv[s][e] = __uint_as_float(f.gm[s][e]) * __builtin_amdgcn_exp2f(ci - cj[e]) * dj[e];
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int i = 16 * blk_I(pw, s) + (lane & 15), j0 = 16 * blk_J(pw, s) + 4 * (lane >> 4);
+        const int ri = HAS_SEQ ? lds_ld<int32_t>(sc, kScR + i * 4) : -1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float m = mv[s][e];
+            m = j0 + e <= i ? m : 0.0f;   // overflow / 0 * inf above the diagonal
             if (HAS_SEQ) m = j0 + e >= ri ? m : 0.0f;
-            mv[e] = m;
+            mv[s][e] = m;
         }
-        bf16x8 hi, lo;
-        split_hilo(mv, hi, lo);
-        lds_st(st, kStMhi + sw_8(i, q), hi);
-        lds_st(st, kStMlo + sw_8(i, q), lo);
+        split_hilo4(mv[s], mb.hi[s], mb.lo[s]);
+    }
+}
+__device__ __forceinline__ void store_m(const MBlk& mb, int pw, int lane, uint8_t* st) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int i = 16 * blk_I(pw, s) + (lane & 15), j0 = 16 * blk_J(pw, s) + 4 * (lane >> 4);
+        const int off = sw_8(i, j0 >> 3) + (j0 & 4) * 2;
+        lds_st(st, kStMhi + off, mb.hi[s]);
+        lds_st(st, kStMlo + off, mb.lo[s]);
     }
 }
 
@@ -656,7 +700,7 @@ __device__ __forceinline__ bf16x8 conv_fast(const uint8_t* raw, int p, int j0,
         u[tau] = bf16_to_f32(lds_ld<uint16_t>(raw, kRwX + sw_xr(j0 + tau, q) + byte));
         id[tau] = HAS_SEQ ? lds_ld<int32_t>(raw, kRwSeq + (j0 + tau) * 4) : 0;
     }
-    uint32_t nb = 0;
+    float zf[8], sv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         double z = cbias;
@@ -666,15 +710,40 @@ __device__ __forceinline__ bf16x8 conv_fast(const uint8_t* raw, int p, int j0,
             z = fma(cw[k], tap, z);
         }
         if (MODE == 2) {
-            bool nr;
-            const float sv = silu_f32(z, nr);
-            out[e] = static_cast<__bf16>(sv);
-            nb |= static_cast<uint32_t>(nr) << e;
+            zf[e] = static_cast<float>(z);
+            sv[e] = zf[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-zf[e]));
         } else {
             out[e] = __builtin_bit_cast(__bf16, f64_to_bf16(z));
         }
     }
-    if (MODE == 2) *near = nb;   // bit e: output e
+    if (MODE == 2) {
+        // near a bf16 rounding midpoint: the fp32 SiLU of the exactly summed z is within
+        // 7 + 3|z| ulps of the exact value (see silu_f32), so an output whose low 16 bits lie
+        // within 8 + 4|z| of 0x8000 cannot be rounded with certainty.  One bound per run (its
+        // largest |z|, rounded up to an integer, at most 0x8000: then every output is near);
+        // the test is lo16 - (0x8000 - bnd) <= 2 bnd modulo 2^16.  The per-output tests land
+        // in lane masks, and only when some lane has a flagged output are they turned into
+        // per-lane bits.
+        float zm = fabsf(zf[0]);
+#pragma unroll
+        for (int e = 1; e < 8; ++e) zm = fmaxf(zm, fabsf(zf[e]));
+        const uint32_t bnd = min(static_cast<uint32_t>(fmaf(4.0f, zm, 9.0f)), 0x8000u);
+        const uint16_t edge = static_cast<uint16_t>(0x8000u - bnd);
+        uint64_t m[8], any = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t t = static_cast<uint16_t>(static_cast<uint16_t>(__float_as_uint(sv[e])) - edge);
+            m[e] = __builtin_amdgcn_ballot_w64(static_cast<uint32_t>(t) <= 2u * bnd);
+            any |= m[e];
+            out[e] = static_cast<__bf16>(sv[e]);
+        }
+        uint32_t nb = 0;
+        if (any != 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nb |= __builtin_amdgcn_inverse_ballot_w64(m[e]) ? (1u << e) : 0u;
+        }
+        *near = nb;   // bit e: output e
+    }
     return out;
 }
 
@@ -749,6 +818,9 @@ template <int K, int MODE, bool HAS_SEQ, int PASS>
 __global__ void __launch_bounds__(kMainThreads, 1)
 ssd_main_kernel(ChunkedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t sm[kMainLds];
+    // the M stages are an array of their own: the compiler then orders the producers' M
+    // stores after an outstanding memory-to-LDS transfer only when they may overlap
+    __shared__ __attribute__((aligned(16))) uint8_t sm_m[2 * kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t sm_cb[2 * kCbBytes];
     // raw slots 0 and 1 are separate arrays, so the compiler can tell a load into one slot
     // from reads of the other
@@ -794,14 +866,16 @@ ssd_main_kernel(ChunkedArgs a) {
 
     // The three roles run separate loops (a wave's role never changes), so the register
     // allocator sees each role's live ranges alone, and each SIMD holds one wave of each role
-    // to interleave.  All loops pass the same number of block barriers: two in the prologue
-    // (raw rows of chunk 0 staged; chunk 0 produced and convolved), then one per chunk.
+    // to interleave.  All loops pass the same number of block barriers: three in the prologue
+    // (raw rows of chunk 0 staged; scalars of chunks 0 and 1 written; chunk 0 produced and
+    // convolved), then one per chunk.
     // Between two barriers:
-    //   consumers  contract chunk c from stage c&1 and X slot c&1 and store y(c);
-    //   producers  load chunk c+1's tiles into stage (c+1)&1 and chunk c+2's raw rows into
-    //              raw slot c&1, compute chunk c+1's scalars and M tiles, then load chunk
-    //              c+2's registers;
-    //   conv waves convolve chunk c+1 from raw slot (c+1)&1 into X slot (c+1)&1.
+    //   consumers  contract chunk c from M stage c&1, scalar stage c%3 and X slot c&1 and
+    //              store y(c);
+    //   producers  load chunk c+1's tiles into tile stage (c+1)&1 and chunk c+2's raw rows
+    //              into raw slot (c+2)%3, compute chunk c+2's scalars and chunk c+1's M
+    //              blocks, then load the registers those need one iteration later;
+    //   conv waves convolve chunk c+1 from raw slot (c+1)%3 into X slot (c+1)&1.
     if (role == 0) {
         // state slice acc[t][r] = h[p][n], p = 16 wave + li, n = 32(t/2) + 8 g4 + 4(t%2) + r
         // (the MFMA row of tile t that lane group g4 holds)
@@ -824,6 +898,7 @@ ssd_main_kernel(ChunkedArgs a) {
             }
         }
         __syncthreads();  // raw rows of chunk 0 staged
+        __syncthreads();  // scalars of chunks 0 and 1 written
         __syncthreads();  // stage 0 and X(0) ready
         // X operands (lane: channel p_own, tokens 32 s + 8 g4 .. +7), convolved by the conv
         // wave with this wave's index
@@ -834,7 +909,8 @@ ssd_main_kernel(ChunkedArgs a) {
         float dprod = 1.0f;  // decay product of the block's chunks (state-only pass)
         int rslot = 0;  // raw slot of chunk cn
         for (int64_t cn = 0; cn < nCl; ++cn) {
-            const uint8_t* st = sm + (cn & 1) * kStageBytes;
+            const uint8_t* st = sm_m + (cn & 1) * kStageBytes;
+            const uint8_t* sc = sm + kOffSc + rslot * kScBytes;  // scalar stage cn % 3
             const uint8_t* cbt = sm_cb + (cn & 1) * kCbBytes;
             bf16x8 xv[2];
 #pragma unroll
@@ -851,7 +927,7 @@ ssd_main_kernel(ChunkedArgs a) {
             f32x4 ya[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) ya[I] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const float decay = lds_ld<float>(st, kStDecay);
+            const float decay = lds_ld<float>(sc, kScDecay);
             if constexpr (PASS == 0) {
             // initial-state part first (it does not need X), one 32-wide slice m of the state
             // at a time; the next slice's C tiles load while this slice's MFMAs run.  The
@@ -923,7 +999,7 @@ ssd_main_kernel(ChunkedArgs a) {
                 mt[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
             }
 #pragma unroll
-            for (int I = 0; I < 4; ++I) ya[I] *= lds_ld<float>(st, kStE + (16 * I + li) * 4);
+            for (int I = 0; I < 4; ++I) ya[I] *= lds_ld<float>(sc, kScE + (16 * I + li) * 4);
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
@@ -950,8 +1026,8 @@ ssd_main_kernel(ChunkedArgs a) {
             for (int sh = 0; sh < 2; ++sh) {
                 float wj[8];
                 {
-                    const f32x4 w0 = lds_ld<f32x4>(st, kStW + (32 * sh + 8 * g4) * 4);
-                    const f32x4 w1 = lds_ld<f32x4>(st, kStW + (32 * sh + 8 * g4 + 4) * 4);
+                    const f32x4 w0 = lds_ld<f32x4>(sc, kScW + (32 * sh + 8 * g4) * 4);
+                    const f32x4 w1 = lds_ld<f32x4>(sc, kScW + (32 * sh + 8 * g4 + 4) * 4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) { wj[e] = w0[e]; wj[4 + e] = w1[e]; }
                 }
@@ -1008,7 +1084,6 @@ ssd_main_kernel(ChunkedArgs a) {
         if (PASS == 1 && wave == 0 && lane == 0) a.seg_decay[(b * a.H + h) * a.nseg + seg] = dprod;
     } else if (role == 1) {
         const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
-        uint8_t* ps = sm + kOffPs + pw * kPsBytes;
         const float Ah2 = Ah * 1.4426950408889634f;  // exponents in base 2
         POff o;
         {
@@ -1027,16 +1102,21 @@ ssd_main_kernel(ChunkedArgs a) {
                 o.x[q] = row * bk.x_row * 2 + ((sl ^ (((row >> 3) & 3) << 1)) << 4);
             }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = 16 * unit_I(pw, u) + (lane & 15), q = 4 * unit_S(pw, u) + (lane >> 4);
-                o.g[u] = (i * kQ + 8 * q) * 4;
+            for (int s = 0; s < 3; ++s) {
+                const int i = 16 * blk_I(pw, s) + (lane & 15), j0 = 16 * blk_J(pw, s) + 4 * (lane >> 4);
+                o.g[s] = (i * kQ + j0) * 4;
             }
             o.dt = lane * bk.H * 4;
         }
         const int ptid = pw * 64 + lane;
         constexpr int kRows = kQ + K - 1;
-        Fetch f;  // registers of the next chunk to produce
+        FetchS fs;  // dt / ids of the chunk whose scalars come next
+        FetchG fg;  // G pieces of the chunk whose M blocks come next
         int32_t seq_row = 0, seq_hi = 0;
+        auto scal = [&](int s) { return sm + kOffSc + s * kScBytes; };
+        const int64_t last = nCl - 1;
+        constexpr int kRegLoads = reg_loads<HAS_SEQ, PASS>();
+        static_assert(kRegLoads < 16, "vmcnt field");
         // In the state-only pass the producers have time to spare and the conv waves set the
         // pace: there the producers convolve the second half of each chunk (tokens 32 .. 63)
         // for channel 16 pw + li, into the X slot lane that consumer wave pw reads, and its
@@ -1055,13 +1135,21 @@ ssd_main_kernel(ChunkedArgs a) {
             }
             lds_st(fl, (pw * 64 + lane) * 4 + 2, static_cast<uint16_t>(near));
         };
-        // prologue: the block's first chunk's tiles, registers and raw rows and the second
-        // chunk's raw rows; then the first chunk produced.  Local chunk c is global chunk
-        // c0 + c (LDS slots go by the local index, memory by the global one).
+        // prologue: the block's first chunk's tiles, dt and raw rows and the second chunk's
+        // raw rows; then the scalars of the first two chunks and the first chunk's M blocks.
+        // Local chunk c is global chunk c0 + c (LDS slots go by the local index, memory by the
+        // global one).
         fetch_tiles<PASS>(bk, o, c0, pw, sm_cb);
-        fetch_regs<HAS_SEQ, PASS>(bk, o, c0, pw, lane, f);
+        fetch_s<HAS_SEQ>(bk, o, c0, lane, fs);
         fetch_raw<K, HAS_SEQ>(bk, o, c0 + 1, nCl > 1, pw, lane, sm_raw1, &seq_row, &seq_hi);
         stage_raw_first<K, MODE != 0, HAS_SEQ>(a, bk, b, h, static_cast<int>(c0 * kQ), pw, lane, sm_raw0);
+        if (PASS == 0) {
+            // the M blocks above the diagonal, (0, 1) and (2, 3): zero in both stages, hi and lo
+            const int zb = (ptid >> 5) & 1, zrow = (zb ? 32 : 0) + ((ptid >> 1) & 15);
+            const int zq = (zb ? 6 : 2) + (ptid & 1);
+            lds_st(sm_m + (ptid >> 7) * kStageBytes + (((ptid >> 6) & 1) ? kStMlo : kStMhi), sw_8(zrow, zq),
+                   u32x4{0u, 0u, 0u, 0u});
+        }
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         if (HAS_SEQ && nCl > 1) {
             if (ptid < kRows) reinterpret_cast<int32_t*>(sm_raw1 + kRwSeq)[ptid] = seq_row;
@@ -1071,8 +1159,19 @@ ssd_main_kernel(ChunkedArgs a) {
             }
         }
         __syncthreads();  // raw rows of chunk 0 staged
-        scalars_and_m<HAS_SEQ, PASS>(f, c0, bk.L, Ah2, pw, lane, sm, ps);
-        fetch_regs<HAS_SEQ, PASS>(bk, o, nCl > 1 ? c0 + 1 : c0, pw, lane, f);
+        chunk_scalars<HAS_SEQ, PASS>(fs, c0, bk.L, Ah2, lane, scal(0));
+        fetch_s<HAS_SEQ>(bk, o, c0 + min<int64_t>(1, last), lane, fs);
+        fetch_g<PASS>(bk, o, c0, fg);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        chunk_scalars<HAS_SEQ, PASS>(fs, c0 + min<int64_t>(1, last), bk.L, Ah2, lane, scal(1));
+        fetch_s<HAS_SEQ>(bk, o, c0 + min<int64_t>(2, last), lane, fs);
+        __syncthreads();  // scalars of chunks 0 and 1 written
+        if (PASS == 0) {
+            MBlk mb;
+            m_blocks<HAS_SEQ>(fg, pw, lane, scal(0), mb);
+            store_m(mb, pw, lane, sm_m);
+        }
+        fetch_g<PASS>(bk, o, c0 + min<int64_t>(1, last), fg);
         if (kProdConv) {
             uint32_t near = 0;
             const bool clean = !(HAS_SEQ && MODE != 0) || ((lds_ld<uint32_t>(sm_raw0, kRwClean) >> (j0_pc / 8)) & 1u);
@@ -1083,22 +1182,24 @@ ssd_main_kernel(ChunkedArgs a) {
         // chunk c: load chunk c+1's tiles (into stage (c+1)&1, free since chunk c-1 was
         // contracted) and chunk c+2's raw rows (into raw slot (c+2)%3, free since chunk c-1's
         // flagged outputs were redone), (state-only pass) convolve the second half of chunk
-        // c+1, compute its scalars and M tiles from the registers loaded during the previous
-        // chunk; then, once this chunk's transfers have landed, load chunk c+2's registers,
-        // which only the next chunk's M tiles wait for.  Unrolled by three so the raw slots
-        // are compile-time arrays.  The body has no branches between the loads and the LDS
-        // work (the compiler then keeps track of which LDS array an outstanding transfer
-        // writes): past the last chunk the indices are clamped, so the loads repeat the last
-        // chunk into slots nobody reads and the conv writes an X slot nobody reads.
+        // c+1, compute chunk c+2's scalars into scalar stage (c+2)%3 and chunk c+1's M blocks
+        // from the scalars written in the previous iteration, so the two are independent
+        // work; then, once this chunk's transfers have landed, load chunk c+2's G pieces and
+        // chunk c+3's dt, which are used one iteration later.  Unrolled by three so the raw
+        // slots and scalar stages are compile-time arrays.  The body has no branches between
+        // the loads and the LDS work (the compiler then keeps track of which LDS array an
+        // outstanding transfer writes): past the last chunk the indices are clamped, so the
+        // loads repeat the last chunk into slots nobody reads and the conv writes an X slot
+        // nobody reads.
         for (int64_t cn = 0; cn < nCl; cn += 3) {
 #pragma unroll
             for (int third = 0; third < 3; ++third) {
                 const int64_t c = cn + third;
                 if (c >= nCl) break;
                 const int64_t k = c + 1;
-                const int64_t kt = k < nCl ? k : nCl - 1;          // tiles of chunk c+1
-                const int64_t kr = k + 1 < nCl ? k + 1 : nCl - 1;  // raw rows, registers of c+2
-                uint8_t* stk = sm + (k & 1) * kStageBytes;
+                const int64_t kt = k < nCl ? k : last;             // tiles of chunk c+1
+                const int64_t kr = k + 1 < nCl ? k + 1 : last;     // raw rows, scalars of c+2
+                uint8_t* stk = sm_m + (k & 1) * kStageBytes;
                 uint8_t* raw_ld = third == 0 ? sm_raw2 : third == 1 ? sm_raw0 : sm_raw1;  // slot (c+2)%3
                 fetch_tiles<PASS>(bk, o, c0 + kt, pw, sm_cb + (k & 1) * kCbBytes);
                 fetch_raw<K, HAS_SEQ>(bk, o, c0 + kr, kr >= 1, pw, lane, raw_ld, &seq_row, &seq_hi);
@@ -1113,9 +1214,19 @@ ssd_main_kernel(ChunkedArgs a) {
                     pclean = !(HAS_SEQ && MODE != 0) || ((lds_ld<uint32_t>(raw_cv, kRwClean) >> (j0_pc / 8)) & 1u);
                     xpc = conv_fast<K, MODE, false>(raw_cv, p_pc, j0_pc, pcw, pcb, &near);
                 }
-                scalars_and_m<HAS_SEQ, PASS>(f, c0 + kt, bk.L, Ah2, pw, lane, stk, ps);
-                __builtin_amdgcn_s_waitcnt(kWaitVm0);
-                fetch_regs<HAS_SEQ, PASS>(bk, o, c0 + kr, pw, lane, f);
+                chunk_scalars<HAS_SEQ, PASS>(fs, c0 + kr, bk.L, Ah2, lane, scal((third + 2) % 3));
+                MBlk mb;
+                if (PASS == 0) m_blocks<HAS_SEQ>(fg, pw, lane, scal((third + 1) % 3), mb);
+                // the registers the next iteration uses load while this iteration's transfers
+                // land; vector memory loads complete in issue order, so waiting until only
+                // those loads are outstanding means the transfers are in LDS.  The M blocks
+                // are stored after that wait: LDS stores issued while transfers into LDS are
+                // outstanding make the compiler wait for all of them.
+                fetch_g<PASS>(bk, o, c0 + kr, fg);
+                fetch_s<HAS_SEQ>(bk, o, c0 + (k + 2 < nCl ? k + 2 : last), lane, fs);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(kWaitVm0 | kRegLoads);
+                if (PASS == 0) store_m(mb, pw, lane, stk);
                 if (kProdConv)
                     prod_conv_finish(raw_cv, sm + kOffX + (k & 1) * kXBytes, sm + kOffFl + (k & 1) * kFlBytes, near, xpc,
                                      pclean);
@@ -1180,6 +1291,7 @@ ssd_main_kernel(ChunkedArgs a) {
         };
         __syncthreads();  // raw rows of chunk 0 staged
         conv_chunk(sm_raw0, sm + kOffX, sm + kOffFl);
+        __syncthreads();  // scalars of chunks 0 and 1 written
         __syncthreads();
         int slot = 1;  // raw slot of chunk cn + 1
         for (int64_t cn = 0; cn < nCl; ++cn) {
@@ -1193,15 +1305,17 @@ ssd_main_kernel(ChunkedArgs a) {
 
     // ---- final conv state F = u[L .. L+K-2] for this head's x channels and for slice h of
     // the B / C channels: all reads first, then a barrier, then the writes, so an in-place
-    // state pair is never read after being overwritten ----
+    // state pair is never read after being overwritten.  Each block takes whole channel rows
+    // (all K-1 entries of a channel): when L < K-1, F reads the initial state of the same
+    // channel, which then no other block writes. ----
     if (MODE != 0 && a.conv_final && PASS == 0 && seg == 0) {
         constexpr int km1 = K - 1;
         const int64_t nx = kP * km1;
-        const int64_t nbc_all = 2 * a.G * kN * km1;
-        const int64_t per = (nbc_all + a.H - 1) / a.H;
-        const int64_t bc_lo = min(h * per, nbc_all), bc_hi = min((h + 1) * per, nbc_all);
+        const int64_t nbc_ch = 2 * a.G * kN;
+        const int64_t per_ch = (nbc_ch + a.H - 1) / a.H;
+        const int64_t bc_lo = min(h * per_ch, nbc_ch) * km1, bc_hi = min((h + 1) * per_ch, nbc_ch) * km1;
         const int64_t total = nx + (bc_hi - bc_lo);
-        constexpr int kMaxItems = 6;  // >= ceil((64*7 + 2*128*7) / 512) for every G <= H
+        constexpr int kMaxItems = 6;  // >= ceil((64*7 + 2*128*7) / 768) for every G <= H
         uint16_t fv[kMaxItems];
         int64_t fidx[kMaxItems];
         int cnt = 0;

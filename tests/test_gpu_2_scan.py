@@ -195,6 +195,25 @@ def test_conv_scan_fwd_inplace_states_and_len0():
     assert_bitexact(cs, torch.from_numpy(rc).to(BF16), "conv state (in place)")
 
 
+@pytest.mark.parametrize("H,L,K", [(3, 1, 4), (3, 2, 4), (48, 1, 4), (48, 2, 4), (5, 3, 6)])
+def test_conv_scan_fwd_short_inplace_conv_state_many_heads(H, L, K):
+    """L < K-1 with the conv state pair in place: the final state keeps entries of the initial
+    state (causal-conv1d ch. 7, a chunk shorter than the history), and the B / C channels'
+    state rows are shared out over the heads' blocks, whose count does not divide them."""
+    import ssm_sequence_models_amd as ssm
+    P, N, G = 64, 128, 1
+    xBC, w, b, dt, A, cinit, sinit, _ = _fused_inputs(2, L, H, P, N, G, K, BF16, seed=40 + H + L)
+    cs, ss = dev(cinit).clone(), dev(sinit).clone()
+    y, _, _ = ssm.conv_scan_fwd(dev(xBC), dev(w), dev(b), dev(dt), dev(A), H, P, G, N,
+                                conv_initial_state=cs, initial_state=ss, conv_final_state=cs,
+                                final_state=ss)
+    torch.cuda.synchronize()
+    ry, rc, rs = oracle.conv_scan_fwd(xBC, w, b, cinit, dt, A, sinit, None, H, P, G, N)
+    assert_close(y, ry, "y (short, in place)")
+    assert_close(ss, rs, "ssm state (short, in place)")
+    assert_bitexact(cs, torch.from_numpy(rc).to(BF16), "conv state (short, in place)")
+
+
 def test_conv_scan_fwd_segmented_inplace_states():
     """A row long enough to run as segments side by side, with both state pairs updated in
     place (the final states overwrite the initial ones)."""
