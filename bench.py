@@ -8,7 +8,10 @@ tensors already resident in HBM.
 
 Prints one JSON line: whole-job tokens/s, the roofline of the dominant kernel (the chunked
 scan main kernel; its launch time comes from HIP events the library records around it on the
-call's stream) and the fp64 CPU oracle timed on the host cores on the same workload.
+call's stream, in a separate instrumented pass) and the fp64 CPU oracle timed on the host
+cores on the same workload.  Before every timed step (the headline's and every other entry
+point's) a 512 MiB buffer is written, outside the timed interval, so no timed call finds its
+inputs in the 256 MB last-level cache; each step is timed by events on the launch stream.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -70,19 +73,41 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+_FLUSH = {}
+
+
+def cache_flush(torch):
+    """Write 512 MiB (twice the MI355X last-level cache) on the current stream."""
+    buf = _FLUSH.get("buf")
+    if buf is None:
+        buf = _FLUSH["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    _FLUSH["v"] = (_FLUSH.get("v", 0) + 1) & 0xFF
+    buf.fill_(_FLUSH["v"])
+
+
+def _time_steps(torch, fn, reps, flush=True):
+    """Per-call milliseconds of fn() for reps calls, each bracketed by events on torch's
+    current stream (the library launches on that stream), with the cache flush before each
+    call outside the bracket."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        if flush:
+            cache_flush(torch)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
 def _time_gpu(torch, fn, reps, warm=2):
-    """Mean milliseconds of fn() over reps calls, by events on torch's current stream (the
-    library launches on that stream)."""
+    """Mean milliseconds of fn() over reps calls (cache flushed before each, see _time_steps)."""
     for _ in range(warm):
         fn()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    t = _time_steps(torch, fn, reps)
+    return sum(t) / len(t)
 
 
 def copy_bandwidth(torch):
@@ -166,6 +191,32 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     nb = s.B * s.L * (s.C * 2 + s.H * 4 + s.H * s.P * 2) + s.B * s.H * s.P * s.N * 4 + s.B * s.C * (s.K - 1) * 2
     rep("conv_scan_fwd", f"780M-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N}, one call", ms, s.B * s.L, nb)
     del x, ws
+
+    # 780M-like layer as 64 chained 2048-token calls, each call's final states written in place
+    # over its initial states (state passing / truncated BPTT over one long sequence)
+    Lc = workloads.CONFIGS["layer780m"]["chunk_len"]
+    x, dt, w, b, A = prefill_inputs(s, 13)
+    ncalls = s.L // Lc
+    xs = [x[:, i * Lc:(i + 1) * Lc].contiguous() for i in range(ncalls)]
+    dts = [dt[:, i * Lc:(i + 1) * Lc].contiguous() for i in range(ncalls)]
+    del x, dt
+    ws = torch.empty(ssm.workspace_size(s.B, Lc, s.H, s.P, s.G, s.N), dtype=torch.uint8, device=dev)
+    cst = torch.zeros(s.B, s.C, s.K - 1, dtype=torch.bfloat16, device=dev)
+    sst = torch.zeros(s.B, s.H, s.P, s.N, device=dev)
+    yc = torch.empty(s.B, Lc, s.H, s.P, dtype=torch.bfloat16, device=dev)
+
+    def chain():
+        for i in range(ncalls):
+            ssm.conv_scan_fwd(xs[i], w, b, dts[i], A, s.H, s.P, s.G, s.N, conv_initial_state=cst,
+                              initial_state=sst, conv_final_state=cst, final_state=sst, y=yc,
+                              workspace=ws)
+    ms = _time_gpu(torch, chain, 3, 1)
+    per_call = (s.B * Lc * (s.C * 2 + s.H * 4 + s.H * s.P * 2) + 2 * s.B * s.H * s.P * s.N * 4
+                + 2 * s.B * s.C * (s.K - 1) * 2)
+    rep("conv_scan_fwd", f"780M-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N} as {ncalls} chained "
+        f"{Lc}-token calls, states passed in place", ms, s.B * s.L, ncalls * per_call,
+        {"calls": ncalls, "ms_per_call": ms / ncalls})
+    del xs, dts, ws, yc
 
     # decode step: conv update + SSM step on 512-slot pools, 256 requests
     d = workloads.DECODE
@@ -306,13 +357,38 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def environment(torch):
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "rocm": rocm,
+            "gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "cpu_model": cpu_model(),
+            "cache_flush_bytes": 512 << 20}
+
+
 def cpu_baseline(s, w, b, A, inp, cinit, sinit):
     import oracle
     t0 = time.perf_counter()
     oracle.conv_scan_fwd(inp["xBC"], w, b, cinit, inp["dt"], A, sinit, None, s.H, s.P, s.G, s.N)
     dt = time.perf_counter() - t0
     return {"value": s.B * s.L / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"one whole step (batch {s.B} x {s.L} tokens, all {s.H} heads), "
                       f"fp64 C oracle, {dt:.2f} s wall"}
 
@@ -375,24 +451,22 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"bench: {args.warmup} warmup steps done; timing {args.steps}")
+    # the timed steps: library timing off, the cache flushed before each step (outside its
+    # events), the whole loop bracketed by device synchronisation
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ms = _time_steps(torch, step, args.steps)
+    wall = time.perf_counter() - t0
+    ms_per_step = sum(step_ms) / len(step_ms)
+    step_ms = sorted(step_ms)
+    # a separate instrumented pass for the main kernel's own duration (the library records
+    # HIP events around its launch on the call's stream)
     ssm.timing_read()  # clear
     ssm.timing_enable(True)
-    torch.cuda.synchronize()
-    # per-step events on the stream the library launches on (for the median and minimum)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e_start, e_end in ev:
-        e_start.record()
-        step()
-        e_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    _time_steps(torch, step, args.steps)
     ssm.timing_enable(False)
     main_ms, launches = ssm.timing_read()
     assert launches == args.steps, (launches, args.steps)
-    ms_per_step = wall * 1e3 / args.steps
-    step_ms = sorted(e_start.elapsed_time(e_end) for e_start, e_end in ev)
     main_ms_avg = main_ms / launches
     tokens = s.B * s.L
     op_bytes, main_bytes = algorithmic_bytes(s)
@@ -412,6 +486,7 @@ def main():
         "ms_per_step": ms_per_step,
         "ms_per_step_median": step_ms[len(step_ms) // 2],
         "ms_per_step_min": step_ms[0],
+        "wall_ms_per_step_incl_cache_flush": wall * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -437,6 +512,7 @@ def main():
                         "frac": op_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "cpu_baseline": None,
         "other_ops": None,
+        "environment": environment(torch),
     }
     if not args.no_other_ops:
         log("bench: other entry points")

@@ -59,15 +59,21 @@ typedef enum {
     SSM_ERR_HIP = 5          /* a HIP launch/runtime error; see ssm_last_error() */
 } ssm_status_t;
 
-typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+/* Element type codes.  The parameter type is a plain 32-bit integer, not the enum, so that a
+   caller may pass any value and get SSM_ERR_INVALID_ARG back for one outside the list (an enum
+   object holding a value outside its enumerators' range is undefined behaviour in C++). */
+enum { SSM_F32 = 0, SSM_BF16 = 1 };
+typedef int32_t ssm_dtype_t;
 
-/* phi of [CC] "single-token update maths": identity or SiLU(z) = z / (1 + exp(-z)). */
-typedef enum { SSM_ACT_NONE = 0, SSM_ACT_SILU = 1 } ssm_act_t;
+/* phi of [CC] "single-token update maths": identity or SiLU(z) = z / (1 + exp(-z)).  A plain
+   32-bit integer for the same reason as ssm_dtype_t. */
+enum { SSM_ACT_NONE = 0, SSM_ACT_SILU = 1 };
+typedef int32_t ssm_act_t;
 
 /* Library ABI version (SSM_ABI_VERSION of the build). */
 int ssm_abi_version(void);
-/* Static English text for a status code. */
-const char* ssm_status_string(ssm_status_t status);
+/* Static English text for a status code; "unknown status" for any other integer. */
+const char* ssm_status_string(int32_t status);
 /* Detail of the last failure on the calling thread ("" if none).  Valid until the next call
  * on the same thread. */
 const char* ssm_last_error(void);
@@ -154,6 +160,9 @@ size_t ssm_scan_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, in
  *   seq_idx       [batch, seqlen] int32, or NULL
  *   y             [batch, seqlen, nheads, headdim]   dtype
  *   workspace     device scratch of >= ssm_scan_workspace_size(...) bytes (NULL if 0)
+ * bf16 with headdim 64 and dstate 128 runs chunked on the matrix cores when x, Bm and Cm are
+ * 16-byte and y 8-byte aligned (the workspace is then required); other shapes, fp32 and
+ * other alignments run token-sequentially (same results to rounding).
  * ------------------------------------------------------------------------------------- */
 ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const void* Bm,
                           const void* Cm, const float* initial_state, float* final_state,

@@ -105,7 +105,9 @@ def _get():
     global _lib
     with _lock:
         if _lib is None:
-            _lib = load_library(build())
+            # ORACLE_LIB_PATH: a separately built copy (the sanitizer build of the oracle)
+            path = os.environ.get("ORACLE_LIB_PATH")
+            _lib = load_library(path if path else build())
         return _lib
 
 

@@ -19,12 +19,34 @@ import os
 import torch  # must precede the library load: it binds the process's HIP runtime
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
+# SSM_LIB_PATH selects another build of the same sources (the host-sanitizer build of the
+# argument checks runs the ABI tests against one)
+LIB_PATH = os.environ.get("SSM_LIB_PATH") or os.path.join(_HERE, "libssm_mi355x.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 ACT = {None: 0, "none": 0, "silu": 1}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "misaligned pointer",
            4: "workspace", 5: "HIP error"}
+
+
+# Debug checks of caller contracts the kernels do not verify (they cost a device-to-host
+# copy): with SSM_DEBUG_CHECKS=1 in the environment (or DEBUG_CHECKS = True), the calls that
+# update state pools refuse two active rows on one slot (causal-conv1d ch. 7, state indices
+# for continuous batching: a duplicate is a caller error, undefined in the kernels).
+DEBUG_CHECKS = os.environ.get("SSM_DEBUG_CHECKS", "") == "1"
+
+
+def check_distinct_slots(indices, n_slots: int, name: str = "indices") -> None:
+    """Raise ValueError if two entries of `indices` inside [0, n_slots) are equal (rows
+    outside that range are skipped by the kernels and may repeat)."""
+    if indices is None:
+        return
+    v = indices.detach().to("cpu").to(torch.int64)
+    v = v[(v >= 0) & (v < n_slots)]
+    if v.numel() != torch.unique(v).numel():
+        vals, counts = torch.unique(v, return_counts=True)
+        raise ValueError(f"{name}: slot(s) {vals[counts > 1].tolist()} used by more than one "
+                         "active row")
 
 
 class SSMError(RuntimeError):
@@ -186,6 +208,8 @@ def conv_scan_fwd_pooled(xBC, conv_weight, conv_bias, dt, A, conv_state, ssm_sta
     _need(conv_state, "conv_state", xBC.dtype, (n_slots, C_conv, state_len))
     _need(ssm_state, "ssm_state", torch.float32, (n_slots, H, P, N))
     _need(state_indices, "state_indices", torch.int32, (b,))
+    if DEBUG_CHECKS:
+        check_distinct_slots(state_indices, ssm_state.shape[0], "state_indices")
     _need(cache_seqlens, "cache_seqlens", torch.int32, (b,))
     _need(seq_idx, "seq_idx", torch.int32, (b, L))
     if y is None:
@@ -364,6 +388,8 @@ def conv1d_update(x, conv_state, weight, bias=None, conv_state_indices=None,
     _need(weight, "weight", torch.float32, (C, K))
     _need(bias, "bias", torch.float32, (C,))
     _need(conv_state_indices, "conv_state_indices", torch.int32, (B,))
+    if DEBUG_CHECKS:
+        check_distinct_slots(conv_state_indices, conv_state.shape[0], "conv_state_indices")
     _need(cache_seqlens, "cache_seqlens", torch.int32, (B,))
     if out is None:
         out = torch.empty_like(x)
@@ -447,15 +473,25 @@ def step(x, dt, A, B, C, state, state_indices=None, y=None, nheads=None, ngroups
     state_indices [b] int32.  Returns y [b, n_new, H, P]."""
     n_slots, H, P, N = state.shape
     bsz, n_new, HP = x.shape
+    if B.dim() != 3 or B.shape[2] % N != 0:
+        raise ValueError(f"B must be [b, n_new, G*N] with N = {N} (the state's last dimension)")
     G = B.shape[2] // N
     if HP != H * P or C.shape != B.shape or B.shape[:2] != x.shape[:2]:
         raise ValueError("x must be [b, n_new, H*P] and B, C [b, n_new, G*N]")
+    if nheads is not None and nheads != H:
+        raise ValueError(f"nheads {nheads} does not match the state's {H} heads")
+    if ngroups is not None and ngroups != G:
+        raise ValueError(f"ngroups {ngroups} does not match B's width {B.shape[2]} / N {N}")
+    if H % G != 0:
+        raise ValueError(f"nheads {H} must be a multiple of ngroups {G}")
     for t, name in ((x, "x"), (B, "B"), (C, "C")):
         _need(t, name, contiguous=False)
     _need(dt, "dt", torch.float32, (bsz, n_new, H))
     _need(A, "A", torch.float32, (H,))
     _need(state, "state", torch.float32)
     _need(state_indices, "state_indices", torch.int32, (bsz,))
+    if DEBUG_CHECKS:
+        check_distinct_slots(state_indices, n_slots, "state_indices")
     if y is None:
         y = torch.empty((bsz, n_new, H, P), dtype=x.dtype, device=x.device)
     _need(y, "y", x.dtype, (bsz, n_new, H, P))

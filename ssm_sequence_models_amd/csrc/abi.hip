@@ -74,7 +74,7 @@ extern "C" {
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
-const char* ssm_status_string(ssm_status_t s) {
+const char* ssm_status_string(int32_t s) {
     switch (s) {
         case SSM_OK: return "ok";
         case SSM_ERR_INVALID_ARG: return "invalid argument";
@@ -245,13 +245,14 @@ ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const 
         return hip_status(ssm::launch_copy_or_zero_f32(final_state, initial_state,
                                                        batch * nheads * headdim * dstate, s),
                           fn);
-    if (ssm::chunked_supported(headdim, dstate, dtype)) {
+    // the matrix-core path loads x, Bm and Cm rows in 16-byte pieces and stores y in 8-byte
+    // pieces; other alignments take the token-sequential path
+    if (ssm::chunked_supported(headdim, dstate, dtype) && aligned(x, 16) && aligned(Bm, 16) &&
+        aligned(Cm, 16) && aligned(y, 8)) {
         const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, nheads, ngroups, dstate);
         if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
             return fail(SSM_ERR_WORKSPACE, "ssm_scan_fwd: workspace must be >= " +
                                                std::to_string(need) + " bytes, 16-byte aligned");
-        if (!aligned(x, 16) || !aligned(y, 8))
-            return fail(SSM_ERR_ALIGNMENT, "ssm_scan_fwd: x must be 16-byte and y 8-byte aligned");
         ssm::ChunkedArgs a{};
         a.x = static_cast<const uint16_t*>(x);
         a.x_row = nheads * headdim;

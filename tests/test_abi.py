@@ -42,8 +42,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.ssm_abi_version() == 4
-    for code in range(6):
-        assert lib.ssm_status_string(code)
+    texts = [lib.ssm_status_string(code) for code in range(6)]
+    assert all(texts) and len(set(texts)) == 6 and b"unknown status" not in texts
+    for code in (-1, 6, 1 << 30):
+        assert lib.ssm_status_string(code) == b"unknown status"
 
 
 def test_workspace_query():
@@ -146,3 +148,17 @@ def test_argument_errors_return_status(lib):
                                  0, None) == 0
     assert lib.ssm_step(None, 0, 0, 1, None, None, None, 0, 0, 1, None, 0, 0, 1, None, None,
                         None, 3, 0, 2, 4, 1, 8, 4, 0, None) == 0
+
+
+def test_check_distinct_slots():
+    """The optional host check for pooled calls: two active rows naming one slot is an error;
+    rows outside [0, n_slots) are padding and may repeat."""
+    import torch
+    import ssm_sequence_models_amd as s
+    s.check_distinct_slots(None, 4)
+    s.check_distinct_slots(torch.tensor([3, 0, 2, 1], dtype=torch.int32), 4)
+    s.check_distinct_slots(torch.tensor([-1, 2, -1, 4, 4, 0], dtype=torch.int32), 4)
+    with pytest.raises(ValueError, match=r"slot\(s\) \[2\]"):
+        s.check_distinct_slots(torch.tensor([2, 0, 2, -1], dtype=torch.int32), 4, "idx")
+    with pytest.raises(ValueError, match=r"\[0, 3\]"):
+        s.check_distinct_slots(torch.tensor([3, 0, 3, 0, 1], dtype=torch.int32), 4)
