@@ -224,6 +224,35 @@ ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float
                                size_t workspace_bytes, ssm_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * ssm_conv_scan_fwd_noalloc -- ssm_conv_scan_fwd for callers that cannot allocate device
+ * memory (code under stream/graph capture, tight serving loops, hosts that forbid
+ * hipMalloc): the same operation, arguments and results, minus the workspace, which is a
+ * static device array of the library, ssm_noalloc_scratch_bytes() = 32 MiB per GPU, created
+ * when the library is first used on that GPU and held until the process ends.  The call
+ * allocates nothing: no hipMalloc / hipFree, no allocating library routine, and no timing
+ * events even while ssm_timing_enable is on.
+ *   - Sizes whose ssm_scan_workspace_size exceeds the scratch return SSM_ERR_WORKSPACE.  On
+ *     the matrix-core path that is 48 KiB per 64-token chunk per row and group, plus the
+ *     segment states of rows split across blocks (1.3B-like layer, batch 4 x 8192 tokens:
+ *     24 MiB; batch 1 x 8192: 14 MiB; one 131072-token row: 104 MiB, rejected).
+ *   - The scratch belongs to the current device (hipGetDevice); `stream` must be a stream of
+ *     that device.  The first call on a device looks its address up (hipGetSymbolAddress).
+ *   - Every call on one GPU shares that GPU's scratch: calls that may overlap in time on one
+ *     GPU (different streams, or several host threads) race and give wrong results; order
+ *     them on one stream.  No part of the scratch needs clearing between calls: each call
+ *     writes every byte it reads before reading it.
+ * ------------------------------------------------------------------------------------- */
+size_t ssm_noalloc_scratch_bytes(void);
+ssm_status_t ssm_conv_scan_fwd_noalloc(const void* xBC, const float* conv_w,
+                                       const float* conv_bias, const void* conv_initial_state,
+                                       void* conv_final_state, const float* dt, const float* A,
+                                       const float* initial_state, float* final_state,
+                                       const int32_t* seq_idx, void* y, int64_t batch,
+                                       int64_t seqlen, int64_t nheads, int64_t headdim,
+                                       int64_t ngroups, int64_t dstate, int64_t width,
+                                       ssm_dtype_t dtype, ssm_act_t act, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * ssm_conv_scan_fwd_pooled -- the fused prefill reading its initial states from, and writing
  * its final states to, the decode pools, so a request moves from prefill to decode (or to its
  * next prefill chunk) without dense state copies.  [CC] "the physical cache may exceed the

@@ -76,6 +76,10 @@ def _load():
                                  i64, ci, vp, ctypes.c_size_t, vp]
     lib.ssm_conv_scan_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp, fp, fp, i32p, vp, i64, i64, i64,
                                       i64, i64, i64, i64, ci, ci, vp, ctypes.c_size_t, vp]
+    lib.ssm_conv_scan_fwd_noalloc.argtypes = [vp, fp, fp, vp, vp, fp, fp, fp, fp, i32p, vp, i64,
+                                              i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    lib.ssm_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.ssm_noalloc_scratch_bytes.argtypes = []
     lib.ssm_step.argtypes = [vp, i64, i64, i64, fp, fp, vp, i64, i64, i64, vp, i64, i64, i64, fp,
                              i32p, vp, i64, i64, i64, i64, i64, i64, i64, ci, vp]
     lib.ssm_conv1d_bwd_workspace_size.restype = ctypes.c_size_t
@@ -100,7 +104,7 @@ def _load():
     lib.ssm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
-              "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
+              "ssm_conv_scan_fwd_noalloc", "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
               "ssm_conv_scan_fwd_pooled", "ssm_state_stats_update", "ssm_scan_fwd_vector_decay",
               "ssm_initial_state_noise", "ssm_state_reset", "ssm_timing_enable",
               "ssm_timing_read"):
@@ -463,6 +467,44 @@ def conv_scan_fwd(xBC, conv_weight, conv_bias, dt, A, nheads, headdim, ngroups, 
         _ptr(conv_final_state), _ptr(dt), _ptr(A), _ptr(initial_state), _ptr(final_state),
         _ptr(seq_idx), _ptr(y), bsz, L, H, P, G, N, K, _dtype_code(xBC), ACT[activation], _ptr(ws),
         nbytes, _stream()))
+    return y, conv_final_state, final_state
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the library's static per-GPU scratch that conv_scan_fwd_noalloc works in."""
+    return int(_lib.ssm_noalloc_scratch_bytes())
+
+
+def conv_scan_fwd_noalloc(xBC, conv_weight, conv_bias, dt, A, nheads, headdim, ngroups, dstate,
+                          y, conv_final_state=None, final_state=None, conv_initial_state=None,
+                          initial_state=None, seq_idx=None, activation="silu"):
+    """conv_scan_fwd without a workspace: the library works in its static per-GPU scratch
+    (noalloc_scratch_bytes()), so nothing is allocated; the caller passes y and the final-state
+    buffers it wants (None: not written).  Calls that may overlap on one GPU race on the
+    scratch; sizes needing more scratch raise SSMError (status SSM_ERR_WORKSPACE)."""
+    bsz, L, Cc = xBC.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    if Cc != H * P + 2 * G * N:
+        raise ValueError("xBC channel count must be nheads*headdim + 2*ngroups*dstate")
+    K = conv_weight.shape[1]
+    if y is None:
+        raise ValueError("y is required: this call allocates nothing")
+    _need(xBC, "xBC")
+    _need(conv_weight, "conv_weight", torch.float32, (Cc, K))
+    _need(conv_bias, "conv_bias", torch.float32, (Cc,))
+    _need(conv_initial_state, "conv_initial_state", xBC.dtype, (bsz, Cc, K - 1))
+    _need(dt, "dt", torch.float32, (bsz, L, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(initial_state, "initial_state", torch.float32, (bsz, H, P, N))
+    _need(seq_idx, "seq_idx", torch.int32, (bsz, L))
+    _need(y, "y", xBC.dtype, (bsz, L, H, P))
+    _need(conv_final_state, "conv_final_state", xBC.dtype, (bsz, Cc, K - 1))
+    _need(final_state, "final_state", torch.float32, (bsz, H, P, N))
+    _check("ssm_conv_scan_fwd_noalloc", _lib.ssm_conv_scan_fwd_noalloc(
+        _ptr(xBC), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_initial_state),
+        _ptr(conv_final_state), _ptr(dt), _ptr(A), _ptr(initial_state), _ptr(final_state),
+        _ptr(seq_idx), _ptr(y), bsz, L, H, P, G, N, K, _dtype_code(xBC), ACT[activation],
+        _stream()))
     return y, conv_final_state, final_state
 
 

@@ -292,20 +292,23 @@ ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const 
                               headdim, ngroups, dstate, dtype, s);
 }
 
-ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float* conv_bias,
-                               const void* conv_initial_state, void* conv_final_state,
-                               const float* dt, const float* A, const float* initial_state,
-                               float* final_state, const int32_t* seq_idx, void* y,
-                               int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
-                               int64_t ngroups, int64_t dstate, int64_t width,
-                               ssm_dtype_t dtype, ssm_act_t act, void* workspace,
-                               size_t workspace_bytes, ssm_stream_t stream) {
-    const char* fn = "ssm_conv_scan_fwd";
+namespace {
+
+// Body of ssm_conv_scan_fwd and ssm_conv_scan_fwd_noalloc; `timed` lets the main-kernel
+// timing record (when switched on) create its events.
+ssm_status_t conv_scan_fwd_impl(const char* fn, const void* xBC, const float* conv_w,
+                                const float* conv_bias, const void* conv_initial_state,
+                                void* conv_final_state, const float* dt, const float* A,
+                                const float* initial_state, float* final_state,
+                                const int32_t* seq_idx, void* y, int64_t batch, int64_t seqlen,
+                                int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                                int64_t width, ssm_dtype_t dtype, ssm_act_t act, void* workspace,
+                                size_t workspace_bytes, bool timed, ssm_stream_t stream) {
     ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate, dtype);
     if (st != SSM_OK) return st;
-    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, "ssm_conv_scan_fwd: bad activation");
+    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": bad activation");
     if (width < 2 || width > 8)
-        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv_scan_fwd: width must be in [2, 8]");
+        return fail(SSM_ERR_UNSUPPORTED, std::string(fn) + ": width must be in [2, 8]");
     const size_t es = esize(dtype);
     const bool work = batch > 0 && seqlen > 0;
     st = check_ptrs(fn, {{"xBC", xBC, work, es},
@@ -335,11 +338,11 @@ ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float
     if (ssm::chunked_supported(headdim, dstate, dtype)) {
         const size_t need = ssm::chunked_workspace_bytes(batch, seqlen, nheads, ngroups, dstate);
         if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
-            return fail(SSM_ERR_WORKSPACE, "ssm_conv_scan_fwd: workspace must be >= " +
+            return fail(SSM_ERR_WORKSPACE, std::string(fn) + ": workspace must be >= " +
                                                std::to_string(need) + " bytes, 16-byte aligned");
         if (!aligned(xBC, 16) || C_conv % 8 != 0 || !aligned(y, 8))
             return fail(SSM_ERR_ALIGNMENT,
-                        "ssm_conv_scan_fwd: xBC must be 16-byte aligned with a channel count "
+                        std::string(fn) + ": xBC must be 16-byte aligned with a channel count "
                         "divisible by 8, y 8-byte aligned");
         ssm::ChunkedArgs a{};
         a.x = static_cast<const uint16_t*>(xBC);
@@ -372,18 +375,20 @@ ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float
         a.G = ngroups;
         a.N = dstate;
         a.workspace = workspace;
-        hipEvent_t e0, e1;
-        st = timing_events(&e0, &e1);
-        if (st != SSM_OK) return st;
+        hipEvent_t e0 = g_none, e1 = g_none;
+        if (timed) {
+            st = timing_events(&e0, &e1);
+            if (st != SSM_OK) return st;
+        }
         return hip_status(ssm::launch_chunked(a, s, e0, e1), fn);
     }
     // general shapes: conv into the workspace, then the token-sequential scan reading its
     // x | B | C channel ranges in place
     if (!ssm::recurrent_supported(headdim, dstate))
-        return fail(SSM_ERR_UNSUPPORTED, "ssm_conv_scan_fwd: dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
+        return fail(SSM_ERR_UNSUPPORTED, std::string(fn) + ": dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
     const size_t need = static_cast<size_t>(batch * seqlen * C_conv) * es;
     if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
-        return fail(SSM_ERR_WORKSPACE, "ssm_conv_scan_fwd: workspace must be >= " +
+        return fail(SSM_ERR_WORKSPACE, std::string(fn) + ": workspace must be >= " +
                                            std::to_string(need) + " bytes, 16-byte aligned");
     hipError_t e = ssm::launch_conv1d_fwd(xBC, conv_w, conv_bias, conv_initial_state,
                                           conv_final_state, seq_idx, workspace, batch, seqlen,
@@ -394,6 +399,93 @@ ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float
                               base + (nheads * headdim + ngroups * dstate) * es, C_conv, dt, A,
                               initial_state, final_state, seq_idx, y, batch, seqlen, nheads,
                               headdim, ngroups, dstate, dtype, s);
+}
+
+}  // namespace
+
+ssm_status_t ssm_conv_scan_fwd(const void* xBC, const float* conv_w, const float* conv_bias,
+                               const void* conv_initial_state, void* conv_final_state,
+                               const float* dt, const float* A, const float* initial_state,
+                               float* final_state, const int32_t* seq_idx, void* y,
+                               int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t ngroups, int64_t dstate, int64_t width,
+                               ssm_dtype_t dtype, ssm_act_t act, void* workspace,
+                               size_t workspace_bytes, ssm_stream_t stream) {
+    return conv_scan_fwd_impl("ssm_conv_scan_fwd", xBC, conv_w, conv_bias, conv_initial_state,
+                              conv_final_state, dt, A, initial_state, final_state, seq_idx, y,
+                              batch, seqlen, nheads, headdim, ngroups, dstate, width, dtype, act,
+                              workspace, workspace_bytes, true, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// Allocation-free fused prefill: the workspace is a static device array of the library.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU, created when the library's code object is loaded on that GPU and held
+// until the process ends.  Host code never passes `scratch` itself to a kernel (its host-side
+// name is not a device address); it uses the per-device address from scratch_address().
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device.
+ssm_status_t scratch_address(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SSM_ERR_UNSUPPORTED, std::string(fn) + ": device ordinal " +
+                                             std::to_string(dev) + " beyond the scratch table");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (p == nullptr) return fail(SSM_ERR_HIP, std::string(fn) + ": scratch has no address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSM_OK;
+}
+
+}  // namespace
+
+size_t ssm_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+ssm_status_t ssm_conv_scan_fwd_noalloc(const void* xBC, const float* conv_w,
+                                       const float* conv_bias, const void* conv_initial_state,
+                                       void* conv_final_state, const float* dt, const float* A,
+                                       const float* initial_state, float* final_state,
+                                       const int32_t* seq_idx, void* y, int64_t batch,
+                                       int64_t seqlen, int64_t nheads, int64_t headdim,
+                                       int64_t ngroups, int64_t dstate, int64_t width,
+                                       ssm_dtype_t dtype, ssm_act_t act, ssm_stream_t stream) {
+    const char* fn = "ssm_conv_scan_fwd_noalloc";
+    const size_t need = ssm_scan_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate,
+                                                dtype);
+    if (need > kScratchBytes)
+        return fail(SSM_ERR_WORKSPACE, std::string(fn) + ": these sizes need " +
+                                           std::to_string(need) + " bytes of scratch; the static "
+                                           "scratch holds " + std::to_string(kScratchBytes) +
+                                           " (ssm_conv_scan_fwd takes a workspace of any size)");
+    void* ws = nullptr;
+    if (batch > 0 && seqlen > 0) {
+        // argument errors are reported before the scratch is looked up
+        ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate,
+                                          dtype);
+        if (st != SSM_OK) return st;
+        st = scratch_address(fn, &ws);
+        if (st != SSM_OK) return st;
+    }
+    return conv_scan_fwd_impl(fn, xBC, conv_w, conv_bias, conv_initial_state, conv_final_state,
+                              dt, A, initial_state, final_state, seq_idx, y, batch, seqlen,
+                              nheads, headdim, ngroups, dstate, width, dtype, act, ws,
+                              ws ? kScratchBytes : 0, false, stream);
 }
 
 ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, const float* dt,

@@ -143,6 +143,15 @@ def test_argument_errors_return_status(lib):
     assert vd(dummy, None, None, None) == 1
     assert vd(None, None, dummy, None) == 1
     assert vd(dummy, dummy, None, _c(260)) == 3
+    # allocation-free prefill: sizes beyond its static scratch; argument errors come first
+    assert lib.ssm_conv_scan_fwd_noalloc(dummy, dummy, None, None, None, dummy, dummy, None,
+                                         None, None, dummy, 1, 131072, 48, 64, 1, 128, 4, 1, 1,
+                                         None) == 4
+    assert b"bytes of scratch" in lib.ssm_last_error()
+    assert lib.ssm_conv_scan_fwd_noalloc(dummy, dummy, None, None, None, dummy, dummy, None,
+                                         None, None, dummy, 1, 64, 3, 64, 2, 128, 4, 1, 1,
+                                         None) == 1
+    assert lib.ssm_noalloc_scratch_bytes() == 32 << 20
     # zero-sized work is a no-op that succeeds without touching the device
     assert lib.ssm_conv1d_update(None, None, None, None, None, None, None, 0, 8, 1, 4, 3, 4, 1,
                                  0, None) == 0
