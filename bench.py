@@ -122,7 +122,7 @@ def copy_bandwidth(torch):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
-def other_ops(torch, ssm, workloads, copy_GBs):
+def other_ops(torch, ssm, workloads, copy_GBs, only=None):
     """Achieved bandwidth of the other entry points on their workloads: the unfused conv at the
     1.3B shape, the decode step (conv update + SSM step, 256 requests, L_new 1 and 4), the
     1.3B-like prefill with packed sequences, the 370M-like prefill, the 131072-token
@@ -134,7 +134,14 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     g = torch.Generator(device=dev)
     res = []
 
+    def timed(key, fn, reps, warm=2):
+        """_time_gpu for the entry points `only` selects (all when None); None otherwise: their
+        inputs are still drawn, so the random streams of the later ones do not change."""
+        return _time_gpu(torch, fn, reps, warm) if only is None or key in only else None
+
     def rep(op, workload, ms, tokens, nbytes, extra=None):
+        if ms is None:
+            return
         res.append({"op": op, "workload": workload, "ms": ms, "tokens_per_s": tokens / (ms * 1e-3),
                     "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                     "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -155,7 +162,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     init = torch.zeros(s.B, s.C, s.K - 1, dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(x)
     fin = torch.empty_like(init)
-    ms = _time_gpu(torch, lambda: ssm.conv1d_fwd(x, w, b, initial_state=init, activation="silu",
+    ms = timed("conv1d_fwd", lambda: ssm.conv1d_fwd(x, w, b, initial_state=init, activation="silu",
                                                   final_state=fin, out=out), 10)
     rep("conv1d_fwd", f"B{s.B} L{s.L} C{s.C} K{s.K} bf16 SiLU, states in/out", ms, s.B * s.L,
         2 * s.B * s.L * s.C * 2 + 2 * s.B * s.C * (s.K - 1) * 2 + s.C * (s.K + 1) * 4)
@@ -165,7 +172,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     x, dt, w, b, A = prefill_inputs(s, 14)
     seq = workloads.packed_seq_idx(s.B, s.L, 4).to(dev)
     ws = torch.empty(ssm.workspace_size(s.B, s.L, s.H, s.P, s.G, s.N), dtype=torch.uint8, device=dev)
-    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, seq_idx=seq,
+    ms = timed("packed1p3b", lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, seq_idx=seq,
                                                      workspace=ws), 10)
     nb = (s.B * s.L * (s.C * 2 + s.H * 4 + s.H * s.P * 2 + 4) + s.B * s.H * s.P * s.N * 4
           + s.B * s.C * (s.K - 1) * 2)
@@ -177,7 +184,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     s = workloads.shape_of("layer370m")
     x, dt, w, b, A = prefill_inputs(s, 12)
     ws = torch.empty(ssm.workspace_size(s.B, s.L, s.H, s.P, s.G, s.N), dtype=torch.uint8, device=dev)
-    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, workspace=ws), 10)
+    ms = timed("layer370m", lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, workspace=ws), 10)
     nb = s.B * s.L * (s.C * 2 + s.H * 4 + s.H * s.P * 2) + s.B * s.H * s.P * s.N * 4 + s.B * s.C * (s.K - 1) * 2
     rep("conv_scan_fwd", f"370M-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N}, zero initial state", ms,
         s.B * s.L, nb)
@@ -187,7 +194,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     s = workloads.shape_of("layer780m")
     x, dt, w, b, A = prefill_inputs(s, 13)
     ws = torch.empty(ssm.workspace_size(s.B, s.L, s.H, s.P, s.G, s.N), dtype=torch.uint8, device=dev)
-    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, workspace=ws), 3, 1)
+    ms = timed("layer780m", lambda: ssm.conv_scan_fwd(x, w, b, dt, A, s.H, s.P, s.G, s.N, workspace=ws), 3, 1)
     nb = s.B * s.L * (s.C * 2 + s.H * 4 + s.H * s.P * 2) + s.B * s.H * s.P * s.N * 4 + s.B * s.C * (s.K - 1) * 2
     rep("conv_scan_fwd", f"780M-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N}, one call", ms, s.B * s.L, nb)
     del x, ws
@@ -210,12 +217,12 @@ def other_ops(torch, ssm, workloads, copy_GBs):
             ssm.conv_scan_fwd(xs[i], w, b, dts[i], A, s.H, s.P, s.G, s.N, conv_initial_state=cst,
                               initial_state=sst, conv_final_state=cst, final_state=sst, y=yc,
                               workspace=ws)
-    ms = _time_gpu(torch, chain, 3, 1)
+    ms = timed("layer780m_chained", chain, 3, 1)
     per_call = (s.B * Lc * (s.C * 2 + s.H * 4 + s.H * s.P * 2) + 2 * s.B * s.H * s.P * s.N * 4
                 + 2 * s.B * s.C * (s.K - 1) * 2)
     rep("conv_scan_fwd", f"780M-like layer B{s.B} L{s.L} H{s.H}x{s.P} N{s.N} as {ncalls} chained "
         f"{Lc}-token calls, states passed in place", ms, s.B * s.L, ncalls * per_call,
-        {"calls": ncalls, "ms_per_call": ms / ncalls})
+        {"calls": ncalls, "ms_per_call": ms / ncalls} if ms is not None else None)
     del xs, dts, ws, yc
 
     # decode step: conv update + SSM step on 512-slot pools, 256 requests
@@ -234,7 +241,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     for L_new in (1, 4):
         xn = torch.randn(R, C, L_new, generator=g, device=dev).to(torch.bfloat16)
         dtn = torch.nn.functional.softplus(torch.randn(R, L_new, H, generator=g, device=dev) - 2).contiguous()
-        ms = _time_gpu(torch, lambda: ssm.decode_step(xn, conv_pool, w, b, dtn, A, ssm_pool, H, P, G, N,
+        ms = timed("decode", lambda: ssm.decode_step(xn, conv_pool, w, b, dtn, A, ssm_pool, H, P, G, N,
                                                        conv_state_indices=idx, cache_seqlens=seqlens), 20)
         nb = (2 * R * H * P * N * 4 + 2 * R * C * d["state_len"] * 2 + 3 * R * C * L_new * 2
               + R * L_new * H * 4 + R * L_new * H * P * 2)
@@ -254,7 +261,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     yp = torch.empty(R, Lp, H, P, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(ssm.conv_scan_fwd_pooled_workspace_size(R, Lp, H, P, G, N, K) + 256,
                      dtype=torch.uint8, device=dev)
-    ms = _time_gpu(torch, lambda: ssm.conv_scan_fwd_pooled(
+    ms = timed("pooled", lambda: ssm.conv_scan_fwd_pooled(
         xp, w, b, dtp, A, conv_pool, ssm_pool, H, P, G, N, state_indices=idx,
         cache_seqlens=seqlens, y=yp, workspace=ws), 10)
     nb = (R * Lp * (C * 2 + H * 4 + H * P * 2) + 2 * R * H * P * N * 4
@@ -271,17 +278,17 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     st = torch.randn(Rs, H, P, N, generator=g, device=dev)
     mean, var = torch.zeros(H, device=dev), torch.ones(H, device=dev)
     nbs = Rs * H * P * N * 4
-    ms = _time_gpu(torch, lambda: ssm.state_stats_update(st, mean, var, beta=0.1), 10)
+    ms = timed("init_state", lambda: ssm.state_stats_update(st, mean, var, beta=0.1), 10)
     rep("state_stats_update", f"{Rs} x H{H}x{P} N{N} fp32 final states, per-head mean / variance",
         ms, Rs, nbs)
     noise = torch.empty_like(st)
-    ms = _time_gpu(torch, lambda: ssm.initial_state_noise(Rs, H, P, N, mean=mean, var=var, seed=1,
+    ms = timed("init_state", lambda: ssm.initial_state_noise(Rs, H, P, N, mean=mean, var=var, seed=1,
                                                           offset=2, out=noise), 10)
     rep("initial_state_noise", f"{Rs} x H{H}x{P} N{N} fp32, Fitted Noise (Philox4x64-10)", ms, Rs,
         nbs)
     kept = torch.empty_like(st)
     mask = torch.empty(Rs, dtype=torch.uint8, device=dev)
-    ms = _time_gpu(torch, lambda: ssm.state_reset(st, p=0.1, seed=1, offset=3, out=kept, mask=mask), 10)
+    ms = timed("init_state", lambda: ssm.state_reset(st, p=0.1, seed=1, offset=3, out=kept, mask=mask), 10)
     rep("state_reset", f"{Rs} x H{H}x{P} N{N} fp32, p 0.1, out of place", ms, Rs, 2 * nbs)
     del st, noise, kept
 
@@ -298,7 +305,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     h0 = torch.randn(s.B, s.H, s.P, s.N, generator=g, device=dev)
     yv = torch.empty_like(xv)
     fv = torch.empty_like(h0)
-    ms = _time_gpu(torch, lambda: ssm.scan_fwd_vector_decay(xv, Bv, Cv, log_decay=gate, dt=dtv,
+    ms = timed("vector_decay", lambda: ssm.scan_fwd_vector_decay(xv, Bv, Cv, log_decay=gate, dt=dtv,
                                                             initial_state=h0, final_state=fv,
                                                             y=yv), 5)
     nb = (s.B * s.L * (2 * s.H * s.P * 2 + s.H * s.N * 4 + 2 * s.N * 2 + s.H * 4)
@@ -313,7 +320,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
         {"bound": "alu", "flops": 5 * elems, "achieved_TFLOPs": 5 * elems / (ms * 1e-3) / 1e12,
          "peak_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
          "frac_alu": 5 * elems / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-         "issue_floor_ms": floor_ms, "frac_of_issue_floor": floor_ms / ms})
+         "issue_floor_ms": floor_ms, "frac_of_issue_floor": floor_ms / ms} if ms is not None else None)
     del xv, Bv, Cv, dtv, gate, yv
 
     # backward of the unfused conv at the 1.3B shape, with state gradients
@@ -327,7 +334,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     dw = torch.empty(s.C, s.K, device=dev)
     dbias = torch.empty(s.C, device=dev)
     ws = torch.empty(ssm.conv1d_bwd_workspace_size(s.B, s.L, s.C, s.K), dtype=torch.uint8, device=dev)
-    ms = _time_gpu(torch, lambda: ssm.conv1d_bwd(x, w, b, dy, initial_state=init, dfinal_state=dF,
+    ms = timed("conv1d_bwd", lambda: ssm.conv1d_bwd(x, w, b, dy, initial_state=init, dfinal_state=dF,
                                                   activation="silu", dx=dx, dinitial_state=dS,
                                                   dweight=dw, dbias=dbias, workspace=ws), 10)
     rep("conv1d_bwd", f"B{s.B} L{s.L} C{s.C} K{s.K} bf16 SiLU: dx, dS, dw, dbias", ms, s.B * s.L,
@@ -344,7 +351,7 @@ def other_ops(torch, ssm, workloads, copy_GBs):
     for label, dts, As in (("layer dt / A (stops where the decay underflows)", dt, A),
                            ("dt 0.01, A -0.05 (every token)", torch.full_like(dt, 0.01),
                             torch.full_like(A, -0.05))):
-        ms = _time_gpu(torch, lambda: ssm.scan_bwd_initial_state(dts, As, Cm, dyh, dfinal_state=dFh,
+        ms = timed("scan_bwd", lambda: ssm.scan_bwd_initial_state(dts, As, Cm, dyh, dfinal_state=dFh,
                                                                   out=dh0), 10)
         # tokens a (b, h) block must read: up to the chunk where 2^(cum log2 e) underflows in fp32
         cum = torch.cumsum(dts.double() * As.double(), dim=1) * (1.0 / math.log(2.0))
@@ -401,6 +408,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-ops", action="store_true",
                     help="skip the bandwidth figures of the other entry points")
+    ap.add_argument("--ops", default=None,
+                    help="comma-separated subset of the other entry points to time (conv1d_fwd, "
+                         "packed1p3b, layer370m, layer780m, layer780m_chained, decode, pooled, "
+                         "init_state, vector_decay, conv1d_bwd, scan_bwd); default all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times), the reference "
                          "the HBM traffic counters are scaled by")
@@ -516,7 +527,8 @@ def main():
     }
     if not args.no_other_ops:
         log("bench: other entry points")
-        result["other_ops"] = other_ops(torch, ssm, workloads, copy_GBs)
+        result["other_ops"] = other_ops(torch, ssm, workloads, copy_GBs,
+                                        args.ops.split(",") if args.ops else None)
     if not args.no_cpu_baseline:
         log("bench: fp64 oracle on the host (cpu baseline)")
         result["cpu_baseline"] = cpu_baseline(s, w, b, A, inp, cinit.cpu(), sinit.cpu())
