@@ -172,6 +172,40 @@ ssm_status_t ssm_scan_fwd(const void* x, const float* dt, const float* A, const 
                           ssm_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * ssm_decode_step -- one decode step of a layer on its pools: ssm_conv1d_update over the
+ * x | B | C channels of x_new, then ssm_step reading the channel ranges of that conv output.
+ * [CC] "single-token update maths" (the ring cache, the K-1 inputs before position p) and
+ * "state indices for continuous batching"; [LG] Sec. 2.1 Eq. (1) for the state update.
+ * Results are exactly those of the two calls in sequence (same roundings, same bits).
+ *
+ *   x_new              [batch, C, n_new]  dtype, C = nheads*headdim + 2*ngroups*dstate
+ *   conv_state         [n_conv_slots, C, state_len]  dtype, updated in place as by
+ *                      ssm_conv1d_update (circular with cache_seqlens, else linear)
+ *   conv_w, conv_bias  [C, width], [C] fp32 (bias may be NULL)
+ *   conv_state_indices [batch] int32 slot of each row in conv_state, or NULL (= row)
+ *   cache_seqlens      [batch] int32 ring positions, or NULL (linear layout); read only
+ *   dt                 [batch, n_new, nheads] fp32;  A  [nheads] fp32
+ *   ssm_state          [n_ssm_slots, nheads, headdim, dstate] fp32, 16-byte aligned,
+ *                      updated in place
+ *   state_indices      [batch] int32 slot of each row in ssm_state, or NULL (= the conv
+ *                      slot, conv_state_indices)
+ *   conv_out           [batch, C, n_new] dtype, written (the conv outputs)
+ *   y                  [batch, n_new, nheads, headdim] dtype
+ * Rows whose slot lies outside a pool are handled as by the two calls (zero conv outputs /
+ * zero y, that pool untouched).  Two rows naming one slot of a pool race (caller contract).
+ * Runs the two kernels of those calls back to back on `stream` (one entry, one argument
+ * check); the conv output is the step's input, so conv_out is required.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_decode_step(const void* x_new, void* conv_state, const float* conv_w,
+                             const float* conv_bias, const int32_t* conv_state_indices,
+                             const int32_t* cache_seqlens, const float* dt, const float* A,
+                             float* ssm_state, const int32_t* state_indices, void* conv_out,
+                             void* y, int64_t batch, int64_t n_new, int64_t nheads,
+                             int64_t headdim, int64_t ngroups, int64_t dstate, int64_t width,
+                             int64_t state_len, int64_t n_conv_slots, int64_t n_ssm_slots,
+                             ssm_dtype_t dtype, ssm_act_t act, ssm_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * ssm_scan_fwd_vector_decay -- the scan with a diagonal transition, one decay per state
  * dimension ([LG] Sec. 2.1 Eq. (1) with A_t = diag(a_t); Sec. 2.5, the diagonal case taken
  * from log transition coefficients), per head h, channel p and state dimension n:

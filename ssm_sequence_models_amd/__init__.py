@@ -82,6 +82,8 @@ def _load():
     lib.ssm_noalloc_scratch_bytes.argtypes = []
     lib.ssm_step.argtypes = [vp, i64, i64, i64, fp, fp, vp, i64, i64, i64, vp, i64, i64, i64, fp,
                              i32p, vp, i64, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.ssm_decode_step.argtypes = [vp, vp, fp, fp, i32p, i32p, fp, fp, fp, i32p, vp, vp, i64,
+                                    i64, i64, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
     lib.ssm_conv1d_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ssm_conv1d_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
     lib.ssm_conv1d_bwd.argtypes = [vp, fp, fp, vp, i32p, vp, vp, vp, vp, fp, fp, vp,
@@ -104,7 +106,7 @@ def _load():
     lib.ssm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
-              "ssm_conv_scan_fwd_noalloc", "ssm_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
+              "ssm_conv_scan_fwd_noalloc", "ssm_step", "ssm_decode_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
               "ssm_conv_scan_fwd_pooled", "ssm_state_stats_update", "ssm_scan_fwd_vector_decay",
               "ssm_initial_state_noise", "ssm_state_reset", "ssm_timing_enable",
               "ssm_timing_read"):
@@ -548,17 +550,44 @@ def step(x, dt, A, B, C, state, state_indices=None, y=None, nheads=None, ngroups
 def decode_step(x_new, conv_state, conv_weight, conv_bias, dt, A, ssm_state, nheads, headdim,
                 ngroups, dstate, conv_state_indices=None, cache_seqlens=None,
                 state_indices=None, activation="silu", conv_out=None, y=None):
-    """One decode step: conv1d_update over x_new [b, C_conv, n_new], then step reading the
-    x | B | C channel ranges of the conv output in place.  Both pools update in place;
-    cache_seqlens is not advanced.  Returns y [b, n_new, H, P]."""
-    HP, GN = nheads * headdim, ngroups * dstate
-    co = conv1d_update(x_new, conv_state, conv_weight, conv_bias, conv_state_indices,
-                       cache_seqlens, activation, out=conv_out)
-    xv = co[:, :HP, :].transpose(1, 2)
-    Bv = co[:, HP:HP + GN, :].transpose(1, 2)
-    Cv = co[:, HP + GN:, :].transpose(1, 2)
-    return step(xv, dt, A, Bv, Cv, ssm_state, state_indices if state_indices is not None
-                else conv_state_indices, y=y)
+    """One decode step on the pools (ssm_decode_step): the conv update over x_new
+    [b, C_conv, n_new], then the SSM step reading the x | B | C channel ranges of its output.
+    Both pools update in place; cache_seqlens is not advanced.  state_indices defaults to
+    conv_state_indices.  Returns y [b, n_new, H, P]."""
+    bsz, C, n_new = x_new.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    if C != H * P + 2 * G * N:
+        raise ValueError("x_new channel count must be nheads*headdim + 2*ngroups*dstate")
+    n_cslots, _, state_len = conv_state.shape
+    K = conv_weight.shape[1]
+    _need(x_new, "x_new")
+    _need(conv_state, "conv_state", x_new.dtype, (n_cslots, C, state_len))
+    _need(conv_weight, "conv_weight", torch.float32, (C, K))
+    _need(conv_bias, "conv_bias", torch.float32, (C,))
+    _need(dt, "dt", torch.float32, (bsz, n_new, H))
+    _need(A, "A", torch.float32, (H,))
+    if ssm_state.dim() != 4 or tuple(ssm_state.shape[1:]) != (H, P, N):
+        raise ValueError(f"ssm_state must be [n_slots, {H}, {P}, {N}]")
+    _need(ssm_state, "ssm_state", torch.float32)
+    _need(conv_state_indices, "conv_state_indices", torch.int32, (bsz,))
+    _need(cache_seqlens, "cache_seqlens", torch.int32, (bsz,))
+    _need(state_indices, "state_indices", torch.int32, (bsz,))
+    if DEBUG_CHECKS:
+        check_distinct_slots(conv_state_indices, n_cslots, "conv_state_indices")
+        check_distinct_slots(state_indices if state_indices is not None else conv_state_indices,
+                             ssm_state.shape[0], "state_indices")
+    if conv_out is None:
+        conv_out = torch.empty_like(x_new)
+    _need(conv_out, "conv_out", x_new.dtype, (bsz, C, n_new))
+    if y is None:
+        y = torch.empty((bsz, n_new, H, P), dtype=x_new.dtype, device=x_new.device)
+    _need(y, "y", x_new.dtype, (bsz, n_new, H, P))
+    _check("ssm_decode_step", _lib.ssm_decode_step(
+        _ptr(x_new), _ptr(conv_state), _ptr(conv_weight), _ptr(conv_bias),
+        _ptr(conv_state_indices), _ptr(cache_seqlens), _ptr(dt), _ptr(A), _ptr(ssm_state),
+        _ptr(state_indices), _ptr(conv_out), _ptr(y), bsz, n_new, H, P, G, N, K, state_len,
+        n_cslots, ssm_state.shape[0], _dtype_code(x_new), ACT[activation], _stream()))
+    return y
 
 
 def timing_enable(enable: bool = True):

@@ -542,6 +542,80 @@ ssm_status_t ssm_step(const void* x, int64_t x_sb, int64_t x_st, int64_t x_sc, c
     return hip_status(ssm::launch_recurrent(r, dtype, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+ssm_status_t ssm_decode_step(const void* x_new, void* conv_state, const float* conv_w,
+                             const float* conv_bias, const int32_t* conv_state_indices,
+                             const int32_t* cache_seqlens, const float* dt, const float* A,
+                             float* ssm_state, const int32_t* state_indices, void* conv_out,
+                             void* y, int64_t batch, int64_t n_new, int64_t nheads,
+                             int64_t headdim, int64_t ngroups, int64_t dstate, int64_t width,
+                             int64_t state_len, int64_t n_conv_slots, int64_t n_ssm_slots,
+                             ssm_dtype_t dtype, ssm_act_t act, ssm_stream_t stream) {
+    const char* fn = "ssm_decode_step";
+    ssm_status_t st = check_scan_dims(fn, batch, n_new, nheads, headdim, ngroups, dstate, dtype);
+    if (st != SSM_OK) return st;
+    if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": bad activation");
+    if (n_conv_slots < 1 || n_ssm_slots < 1)
+        return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": n_conv_slots and n_ssm_slots must be >= 1");
+    if (width < 2 || width > 8)
+        return fail(SSM_ERR_UNSUPPORTED, std::string(fn) + ": width must be in [2, 8]");
+    if (state_len < width - 1)
+        return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": state_len < width - 1");
+    if (!ssm::recurrent_supported(headdim, dstate))
+        return fail(SSM_ERR_UNSUPPORTED, std::string(fn) + ": dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
+    const size_t es = esize(dtype);
+    const bool work = batch > 0 && n_new > 0;
+    st = check_ptrs(fn, {{"x_new", x_new, work, es},
+                         {"conv_state", conv_state, work, es},
+                         {"conv_w", conv_w, work, 4},
+                         {"conv_bias", conv_bias, false, 4},
+                         {"conv_state_indices", conv_state_indices, false, 4},
+                         {"cache_seqlens", cache_seqlens, false, 4},
+                         {"dt", dt, work, 4},
+                         {"A", A, work, 4},
+                         {"ssm_state", ssm_state, work, 16},
+                         {"state_indices", state_indices, false, 4},
+                         {"conv_out", conv_out, work, es},
+                         {"y", y, work, es}});
+    if (st != SSM_OK) return st;
+    if (!work) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t C = nheads * headdim + 2 * ngroups * dstate;
+    const int64_t HP = nheads * headdim, GN = ngroups * dstate;
+    ssm::RecurrentArgs r{};
+    r.x = conv_out;  // x | B | C channel ranges of the conv output [batch, C, n_new]
+    r.x_sb = C * n_new;
+    r.x_st = 1;
+    r.x_sc = n_new;
+    r.dt = dt;
+    r.A = A;
+    r.Bm = static_cast<const uint8_t*>(conv_out) + HP * n_new * es;
+    r.B_sb = C * n_new;
+    r.B_st = 1;
+    r.B_sc = n_new;
+    r.Cm = static_cast<const uint8_t*>(conv_out) + (HP + GN) * n_new * es;
+    r.C_sb = C * n_new;
+    r.C_st = 1;
+    r.C_sc = n_new;
+    r.state_in = ssm_state;
+    r.state_out = ssm_state;
+    r.indices = state_indices ? state_indices : conv_state_indices;
+    r.n_slots = n_ssm_slots;
+    r.seq_idx = nullptr;
+    r.y = y;
+    r.B = batch;
+    r.T = n_new;
+    r.H = nheads;
+    r.P = headdim;
+    r.G = ngroups;
+    r.N = dstate;
+    hipError_t e = ssm::launch_conv1d_update(x_new, conv_state, conv_w, conv_bias,
+                                             conv_state_indices, cache_seqlens, conv_out, batch,
+                                             C, n_new, width, state_len, n_conv_slots, dtype, act,
+                                             s);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(ssm::launch_recurrent(r, dtype, s), fn);
+}
+
 ssm_status_t ssm_scan_fwd_vector_decay(const void* x, const float* dt, const float* log_decay,
                                        const float* A_vec, const void* Bm, const void* Cm,
                                        const float* initial_state, float* final_state,
