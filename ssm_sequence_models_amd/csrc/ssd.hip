@@ -1411,7 +1411,7 @@ hipError_t launch_k(const ChunkedArgs& a, hipStream_t stream, hipEvent_t ev0, hi
 // Rows with few heads leave most CUs idle on the per-(row, head) sequential scan; they are
 // split into segments (at least kMinSegChunks chunks each) so about kTargetBlocks blocks run.
 constexpr int64_t kTargetBlocks = 256;
-constexpr int64_t kMinSegChunks = 16;
+constexpr int64_t kMinSegChunks = 4;
 
 int64_t chunked_nseg(int64_t B, int64_t L, int64_t H) {
     const int64_t nC = (L + kQ - 1) / kQ;
