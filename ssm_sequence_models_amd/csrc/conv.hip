@@ -13,6 +13,8 @@
 // reads its K-1 history values from the pool row into registers first, then produces the
 // n_new outputs and only then writes the raw new inputs back into the ring (or shifts the
 // linear row), so nothing it still needs is overwritten.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ssm {
@@ -218,20 +220,23 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
         for (int k = 0; k < K; ++k) wr[v][k] = w[(c0 + v) * K + k];
         bv[v] = bias ? bias[c0 + v] : 0.0f;
     }
-    // u-positions t0-K+1 .. t0-1 (oldest first): from x, or from the state for pos < 0
-    double hist[K - 1][V];
-    int32_t hid[K - 1];
+    // The window of a group of kGroup tokens: rows 0 .. K-2 hold the K-1 inputs before the
+    // group (oldest first), row K-1+u the group's token u; output u takes rows u .. u+K-1.
+    // The history moves once per group (K-1 rows), not once per token.  First the u-positions
+    // t0-K+1 .. t0-1: from x, or from the state for pos < 0.
+    double win[kGroup + K - 1][V];
+    int32_t wid[kGroup + K - 1];
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) {
         const int64_t pos = t0 - (K - 1) + j;
         if (pos >= 0) {
-            unpack4(*reinterpret_cast<const uint2*>(xrow + pos * C), hist[j]);
-            hid[j] = HAS_SEQ ? srow[pos] : 0;
+            unpack4(*reinterpret_cast<const uint2*>(xrow + pos * C), win[j]);
+            wid[j] = HAS_SEQ ? srow[pos] : 0;
         } else {
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                hist[j][v] = init_state ? bf16_to_f32(init_state[(b * C + c0 + v) * (K - 1) + (K - 1) + pos]) : 0.0f;
-            hid[j] = HAS_SEQ ? srow[0] : 0;
+                win[j][v] = init_state ? bf16_to_f32(init_state[(b * C + c0 + v) * (K - 1) + (K - 1) + pos]) : 0.0f;
+            wid[j] = HAS_SEQ ? srow[0] : 0;
         }
     }
 
@@ -245,32 +250,29 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
         xa[u] = t < t1 ? *reinterpret_cast<const uint2*>(xrow + t * C) : uint2{0u, 0u};
         ia[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
     }
-    for (int64_t tg = t0; tg < t1; tg += kGroup) {
-        uint2 xb[kGroup];
-        int32_t ib[kGroup];
+    // One group; FULL groups lie inside the run and skip the per-token bound checks.
+    auto group = [&](int64_t tg, auto full) -> uint32_t {
+        constexpr bool FULL = decltype(full)::value;
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
-            const int64_t t = tg + kGroup + u;
-            xb[u] = t < t1 ? *reinterpret_cast<const uint2*>(xrow + t * C) : uint2{0u, 0u};
-            ib[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
+            unpack4(xa[u], win[K - 1 + u]);
+            wid[K - 1 + u] = ia[u];
         }
         uint32_t near = 0;  // bit 4u + v: output (token tg + u, channel c0 + v) flagged
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
             const int64_t t = tg + u;
-            if (t < t1) {
-                double xv[V];
-                unpack4(xa[u], xv);
+            if (FULL || t < t1) {
                 double z[V];
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
                     double acc = bv[v];
 #pragma unroll
                     for (int k = 0; k < K - 1; ++k) {
-                        const double tap = (!HAS_SEQ || hid[k] == ia[u]) ? hist[k][v] : 0.0;
+                        const double tap = (!HAS_SEQ || wid[u + k] == wid[u + K - 1]) ? win[u + k][v] : 0.0;
                         acc = fma(wr[v][k], tap, acc);
                     }
-                    z[v] = fma(wr[v][K - 1], xv[v], acc);
+                    z[v] = fma(wr[v][K - 1], win[u + K - 1][v], acc);
                 }
                 uint16_t o[V];
 #pragma unroll
@@ -286,23 +288,39 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
                 *reinterpret_cast<uint2*>(orow + t * C) =
                     uint2{o[0] | (static_cast<uint32_t>(o[1]) << 16),
                           o[2] | (static_cast<uint32_t>(o[3]) << 16)};
-#pragma unroll
-                for (int k = 0; k < K - 2; ++k) {
-#pragma unroll
-                    for (int v = 0; v < V; ++v) hist[k][v] = hist[k + 1][v];
-                    hid[k] = hid[k + 1];
-                }
-#pragma unroll
-                for (int v = 0; v < V; ++v) hist[K - 2][v] = xv[v];
-                hid[K - 2] = ia[u];
             }
         }
+        if (FULL) {
+#pragma unroll
+            for (int j = 0; j < K - 1; ++j) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) win[j][v] = win[kGroup + j][v];
+                wid[j] = wid[kGroup + j];
+            }
+        }
+        return near;
+    };
+    int64_t tg = t0;
+    for (; tg + kGroup <= t1; tg += kGroup) {
+        uint2 xb[kGroup];
+        int32_t ib[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const int64_t t = tg + kGroup + u;
+            xb[u] = t < t1 ? *reinterpret_cast<const uint2*>(xrow + t * C) : uint2{0u, 0u};
+            ib[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
+        }
+        const uint32_t near = group(tg, std::true_type{});
         if (SILU) flags[(tg - t0) / kGroup][threadIdx.x] = near;
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
             xa[u] = xb[u];
             ia[u] = ib[u];
         }
+    }
+    if (tg < t1) {
+        const uint32_t near = group(tg, std::false_type{});
+        if (SILU) flags[(tg - t0) / kGroup][threadIdx.x] = near;
     }
 
     // rare: each iteration redoes one flagged output per lane (this thread stored the fast
