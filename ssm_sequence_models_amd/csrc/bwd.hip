@@ -28,6 +28,7 @@ namespace {
 // ---------------------------------------------------------------------------------------
 constexpr int kConvBwdRun = 64;
 constexpr int kConvBwdThreads = 256;
+constexpr int kBwdGroup = 4;  // tokens per group of the bf16x4 kernel's main range
 
 template <class D, int K>
 __global__ void __launch_bounds__(kConvBwdThreads)
@@ -218,7 +219,8 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
 #pragma unroll
     for (int j = 0; j < V; ++j) dbp[j] = 0.0f;
 
-    for (int64_t t = t0; t < t1 + K - 1; ++t) {
+    // one token, general case (the run's first K-1 tokens, its last K-1 steps and short runs)
+    auto token = [&](int64_t t) {
         const bool live = t < L;
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) {
@@ -297,7 +299,119 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
             o.y = pack_bf16x2(v[2], v[3]);
             *reinterpret_cast<uint2*>(dx + (b * L + s_) * C + c4) = o;
         }
+    };
+    // Tokens ta .. tb-1 (all inside the run, at least K-1 after its start) in groups of
+    // kBwdGroup: every token is live, accumulates into dw / dbeta and emits dx for s = t-K+1
+    // inside the run, so no per-token checks.  The inputs, deltas and identities sit in
+    // windows (rows 0 .. K-2 the K-1 before the group, row K-1+u token u) that move once per
+    // group, and the next group's x and dy load while this one is computed.  Same arithmetic
+    // in the same order as the general case.
+    const int64_t ta = min(t0 + K - 1, t1), tb = t1;
+    int64_t t = t0;
+    for (; t < ta; ++t) token(t);
+    if (tb - t >= kBwdGroup) {
+        constexpr int G = kBwdGroup;
+        float xw[G + K - 1][V], dlw[G + K - 1][V];
+        int32_t idw[G + K - 1];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                xw[j][v] = xv[j + 1][v];
+                dlw[j][v] = dl[j + 1][v];
+            }
+            idw[j] = xs[j + 1];
+        }
+        uint2 xq[G], gq[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            xq[u] = *reinterpret_cast<const uint2*>(x + (b * L + t + u) * C + c4);
+            gq[u] = *reinterpret_cast<const uint2*>(dy + (b * L + t + u) * C + c4);
+        }
+        for (; t + G <= tb; t += G) {
+            uint2 xn[G], gn[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                const int64_t tt = t + G + u;
+                xn[u] = tt < L ? *reinterpret_cast<const uint2*>(x + (b * L + tt) * C + c4) : uint2{0u, 0u};
+                gn[u] = tt < L ? *reinterpret_cast<const uint2*>(dy + (b * L + tt) * C + c4) : uint2{0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                bf16x4_to_f32(xq[u], xw[K - 1 + u]);
+                idw[K - 1 + u] = sid(t + u);
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                float g[V];
+                bf16x4_to_f32(gq[u], g);
+                bool tap[K];
+#pragma unroll
+                for (int k = 0; k < K; ++k) tap[k] = !sq || idw[u + k] == idw[u + K - 1];
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    float z = beta[j];
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        if (tap[k]) z = __builtin_fmaf(wk[k][j], xw[u + k][j], z);
+                    float dphi = 1.0f;
+                    if (silu) {
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+                        dphi = sg * (1.0f + z * (1.0f - sg));
+                    }
+                    dlw[K - 1 + u][j] = g[j] * dphi;
+                }
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (tap[k]) {
+#pragma unroll
+                        for (int j = 0; j < V; ++j) dwp[k][j] = __builtin_fmaf(dlw[K - 1 + u][j], xw[u + k][j], dwp[k][j]);
+                    }
+#pragma unroll
+                for (int j = 0; j < V; ++j) dbp[j] += dlw[K - 1 + u][j];
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                const int64_t s_ = t + u - (K - 1);
+                float v[V] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int m = 0; m < K; ++m)
+                    if (!sq || idw[u + m] == idw[u]) {
+#pragma unroll
+                        for (int j = 0; j < V; ++j) v[j] = __builtin_fmaf(dlw[u + m][j], wk[K - 1 - m][j], v[j]);
+                    }
+                uint2 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(dx + (b * L + s_) * C + c4) = o;
+            }
+#pragma unroll
+            for (int j = 0; j < K - 1; ++j) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    xw[j][v] = xw[G + j][v];
+                    dlw[j][v] = dlw[G + j][v];
+                }
+                idw[j] = idw[G + j];
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                xq[u] = xn[u];
+                gq[u] = gn[u];
+            }
+        }
+        // back to the general case's windows (inputs and deltas of the last K-1 tokens)
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                xv[j + 1][v] = xw[j][v];
+                dl[j + 1][v] = dlw[j][v];
+            }
+            xs[j + 1] = ds[j + 1] = idw[j];
+        }
     }
+    for (; t < t1 + K - 1; ++t) token(t);
     if (r == 0 && dinit) {
 #pragma unroll
         for (int jj = 0; jj < K - 1; ++jj) {
