@@ -304,9 +304,12 @@ constexpr int kCbC = 0;                          // C   [64 tok][16 pieces], pie
 constexpr int kCbBt = kCbC + kQ * 256;           // B^T [128 n][8 pieces], piece ^ bt_swz(n)
 constexpr int kCbBytes = kCbBt + kN * 128;
 //   M stage s (two, by chunk parity), produced one chunk ahead of its use:
-constexpr int kStMhi = 0;                        // M   [64 i][8 pieces], piece ^ (i & 7)
-constexpr int kStMlo = kStMhi + kQ * 128;
-constexpr int kStageBytes = kStMlo + kQ * 128;
+// M: only j <= i is used, so rows 0-31 hold pieces 0-3 (64 bytes) and rows 32-63 all eight
+// (128 bytes): 6 KB each for hi and lo (see sw_m)
+constexpr int kMBytes = 32 * 64 + 32 * 128;
+constexpr int kStMhi = 0;
+constexpr int kStMlo = kStMhi + kMBytes;
+constexpr int kStageBytes = kStMlo + kMBytes;
 //   scalar stage (three, by chunk index mod 3), produced two chunks ahead of its use: in the
 //   iteration that contracts chunk c, the consumers read chunk c's E / W / decay, the
 //   producers build chunk c+1's M tiles from its cum / R / r, and write chunk c+2's scalars
@@ -350,7 +353,13 @@ __device__ __forceinline__ int sw_c(int tok, int q) { return tok * 256 + ((q ^ (
 __device__ __forceinline__ int sw_bt(int n, int q) {
     return n * 128 + ((q ^ ((n & 3) | (((n >> 3) & 1) << 2))) << 4);
 }
-__device__ __forceinline__ int sw_8(int row, int q) { return row * 128 + ((q ^ (row & 7)) << 4); }
+// byte offset of 16-byte piece q (8 bf16 columns) of M row `row`; rows below 32 have pieces
+// 0-3 only.  The swizzles keep a 16-row x 16-byte MFMA operand read at two lanes per bank
+// group (the minimum for 256 bytes per 16 lanes).
+__device__ __forceinline__ int sw_m(int row, int q) {
+    return row < 32 ? row * 64 + ((q ^ ((row >> 1) & 3)) << 4)
+                    : 32 * 64 + (row - 32) * 128 + ((q ^ (row & 7)) << 4);
+}
 // raw x rows: the consumers' 2-byte reads hit rows 8 apart in the four 16-lane groups
 __device__ __forceinline__ int sw_xr(int row, int q) {
     return row * 128 + ((q ^ (((row >> 3) & 3) << 1)) << 4);
@@ -655,7 +664,7 @@ __device__ __forceinline__ void store_m(const MBlk& mb, int pw, int lane, uint8_
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
         const int i = 16 * blk_I(pw, s) + (lane & 15), j0 = 16 * blk_J(pw, s) + 4 * (lane >> 4);
-        const int off = sw_8(i, j0 >> 3) + (j0 & 4) * 2;
+        const int off = sw_m(i, j0 >> 3) + (j0 & 4) * 2;
         lds_st(st, kStMhi + off, mb.hi[s]);
         lds_st(st, kStMlo + off, mb.lo[s]);
     }
@@ -996,7 +1005,7 @@ ssd_main_kernel(ChunkedArgs a) {
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                mt[u] = lds_ld<bf16x8>(st, kStMhi + sw_8(16 * I + li, 4 * sh + g4));
+                mt[u] = lds_ld<bf16x8>(st, kStMhi + sw_m(16 * I + li, 4 * sh + g4));
             }
 #pragma unroll
             for (int I = 0; I < 4; ++I) ya[I] *= lds_ld<float>(sc, kScE + (16 * I + li) * 4);
@@ -1008,7 +1017,7 @@ ssd_main_kernel(ChunkedArgs a) {
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
                 const int I = u < 2 ? u : (u < 4 ? 2 : 3), sh = u < 2 ? 0 : ((u & 1) ? 1 : 0);
-                mt[u] = lds_ld<bf16x8>(st, kStMlo + sw_8(16 * I + li, 4 * sh + g4));
+                mt[u] = lds_ld<bf16x8>(st, kStMlo + sw_m(16 * I + li, 4 * sh + g4));
             }
 #pragma unroll
             for (int u = 0; u < 6; ++u) {
@@ -1147,7 +1156,7 @@ ssd_main_kernel(ChunkedArgs a) {
             // the M blocks above the diagonal, (0, 1) and (2, 3): zero in both stages, hi and lo
             const int zb = (ptid >> 5) & 1, zrow = (zb ? 32 : 0) + ((ptid >> 1) & 15);
             const int zq = (zb ? 6 : 2) + (ptid & 1);
-            lds_st(sm_m + (ptid >> 7) * kStageBytes + (((ptid >> 6) & 1) ? kStMlo : kStMhi), sw_8(zrow, zq),
+            lds_st(sm_m + (ptid >> 7) * kStageBytes + (((ptid >> 6) & 1) ? kStMlo : kStMhi), sw_m(zrow, zq),
                    u32x4{0u, 0u, 0u, 0u});
         }
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
