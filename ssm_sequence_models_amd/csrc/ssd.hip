@@ -136,6 +136,69 @@ __device__ __forceinline__ int wave_incl_max(int v) {
     return v;
 }
 
+// The state-only pass of a segment (its end state from a zero start) may begin at the last
+// chunk c from which the segment's remaining log-decay sum S(c) = sum of dt_t A over the
+// tokens from chunk c to the segment end is below -208: every token before chunk c then
+// reaches the end state with a factor exp(sum of its later dt A) <= exp(S(c)) < 1e-90, as
+// long as each skipped token has dt A <= 0, which is checked (a NaN or positive dt A among
+// them keeps the whole segment).  The skipped tokens' part of the end state is below fp32's
+// smallest subnormal for any state of magnitude up to 1e44; the segment's decay product is
+// then exactly 0 in fp32 as well.  Returns the number of chunks to skip (0: none).  All
+// threads of the block call it; it uses 66 floats of LDS at scr and ends with a barrier.
+template <int NT>
+__device__ int64_t state_pass_skip(const float* dtc, int64_t H, int64_t L, int64_t c0,
+                                   int64_t nCl, float A, float* scr, int tid) {
+    constexpr int NW = NT / 64;
+    constexpr int PER = (64 + NW - 1) / NW;  // chunks per wave in a window of 64
+    constexpr float kCut = -208.0f;
+    const int wave = tid >> 6, lane = tid & 63;
+    int64_t hit = -1;  // chunk index (in the segment) of the last crossing
+    float carry = 0.0f;
+    for (int64_t w0 = nCl; w0 > 0; w0 -= 64) {
+        // chunk sums of dt A for the window's chunks w0 - 1 - l (l < 64) into scr[l]
+        const int nw = static_cast<int>(min<int64_t>(64, w0));
+        float v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int l = wave + NW * i;
+            const int64_t t = (c0 + w0 - 1 - l) * kQ + lane;
+            v[i] = (l < nw && t < L) ? dtc[t * H] * A : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int l = wave + NW * i;
+            const float sum = wave_incl_sum(v[i]);
+            if (l < nw && lane == 63) scr[l] = sum;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l: the sum from chunk w0 - 1 - l to the segment end
+            const float S = wave_incl_sum(lane < nw ? scr[lane] : 0.0f) + carry;
+            const uint64_t m = __ballot(lane < nw && S < kCut);
+            const float tot = __shfl(S, 63);
+            if (lane == 0) {
+                scr[64] = m ? static_cast<float>(__builtin_ctzll(m)) : -1.0f;
+                scr[65] = tot;
+            }
+        }
+        __syncthreads();
+        const float r = scr[64];
+        carry = scr[65];
+        __syncthreads();  // scr is rewritten by the next window
+        if (r >= 0.0f) {
+            hit = w0 - 1 - static_cast<int64_t>(r);
+            break;
+        }
+    }
+    if (hit <= 0) return 0;
+    // every skipped token must have dt A <= 0 (not NaN, not positive)
+    int bad = 0;
+    const int64_t t_end = (c0 + hit) * kQ;
+#pragma unroll 4
+    for (int64_t t = c0 * kQ + tid; t < t_end; t += NT) bad |= !(dtc[t * H] * A <= 0.0f);
+    return __syncthreads_or(bad) ? 0 : hit;
+}
+
 __device__ __forceinline__ int64_t ws_unit(const ChunkedArgs& a, int64_t b, int64_t c,
                                            int64_t g, int64_t nC) {
     return (b * nC + c) * a.G + g;
@@ -852,9 +915,18 @@ ssd_main_kernel(ChunkedArgs a) {
     const int64_t L = a.L;
     const int64_t nC = (L + kQ - 1) / kQ;
     // this block's chunks: global chunk c0 + c for c < nCl
-    const int64_t c0 = seg * a.seg_chunks;
-    const int64_t nCl = min(a.seg_chunks, nC - c0);
+    int64_t c0 = seg * a.seg_chunks;
+    int64_t nCl = min(a.seg_chunks, nC - c0);
     const float Ah = a.A[h];
+    // the state-only pass starts where the earlier chunks can no longer reach the end state
+    bool skipped = false;
+    if constexpr (PASS == 1) {
+        const int64_t skip = state_pass_skip<kMainThreads>(a.dt + b * L * a.H + h, a.H, L, c0, nCl,
+                                                           Ah, reinterpret_cast<float*>(sm), tid);
+        c0 += skip;
+        nCl -= skip;
+        skipped = skip > 0;
+    }
     Blk bk;
     bk.x = a.x + b * L * a.x_row + a.x_col0 + h * kP;
     bk.dt = a.dt + b * L * a.H + h;
@@ -1090,7 +1162,9 @@ ssd_main_kernel(ChunkedArgs a) {
                 *reinterpret_cast<f32x4*>(dst + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
             }
         }
-        if (PASS == 1 && wave == 0 && lane == 0) a.seg_decay[(b * a.H + h) * a.nseg + seg] = dprod;
+        // a skipped start means the decay product over the segment is below 1e-90: 0 in fp32
+        if (PASS == 1 && wave == 0 && lane == 0)
+            a.seg_decay[(b * a.H + h) * a.nseg + seg] = skipped ? 0.0f : dprod;
     } else if (role == 1) {
         const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
         const float Ah2 = Ah * 1.4426950408889634f;  // exponents in base 2
