@@ -297,7 +297,7 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
             uint2 o;
             o.x = pack_bf16x2(v[0], v[1]);
             o.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(dx + (b * L + s_) * C + c4) = o;
+            st_stream_u2(dx + (b * L + s_) * C + c4, o);
         }
     };
     // Tokens ta .. tb-1 (all inside the run, at least K-1 after its start) in groups of
@@ -325,16 +325,16 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
         uint2 xq[G], gq[G];
 #pragma unroll
         for (int u = 0; u < G; ++u) {
-            xq[u] = *reinterpret_cast<const uint2*>(x + (b * L + t + u) * C + c4);
-            gq[u] = *reinterpret_cast<const uint2*>(dy + (b * L + t + u) * C + c4);
+            xq[u] = ld_stream_u2(x + (b * L + t + u) * C + c4);
+            gq[u] = ld_stream_u2(dy + (b * L + t + u) * C + c4);
         }
         for (; t + G <= tb; t += G) {
             uint2 xn[G], gn[G];
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 const int64_t tt = t + G + u;
-                xn[u] = tt < L ? *reinterpret_cast<const uint2*>(x + (b * L + tt) * C + c4) : uint2{0u, 0u};
-                gn[u] = tt < L ? *reinterpret_cast<const uint2*>(dy + (b * L + tt) * C + c4) : uint2{0u, 0u};
+                xn[u] = tt < L ? ld_stream_u2(x + (b * L + tt) * C + c4) : uint2{0u, 0u};
+                gn[u] = tt < L ? ld_stream_u2(dy + (b * L + tt) * C + c4) : uint2{0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < G; ++u) {
@@ -383,7 +383,7 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
                 uint2 o;
                 o.x = pack_bf16x2(v[0], v[1]);
                 o.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(dx + (b * L + s_) * C + c4) = o;
+                st_stream_u2(dx + (b * L + s_) * C + c4, o);
             }
 #pragma unroll
             for (int j = 0; j < K - 1; ++j) {

@@ -247,7 +247,7 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
         const int64_t t = t0 + u;
-        xa[u] = t < t1 ? *reinterpret_cast<const uint2*>(xrow + t * C) : uint2{0u, 0u};
+        xa[u] = t < t1 ? ld_stream_u2(xrow + t * C) : uint2{0u, 0u};
         ia[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
     }
     // One group; FULL groups lie inside the run and skip the per-token bound checks.
@@ -285,9 +285,8 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
                         o[v] = f64_to_bf16(z[v]);
                     }
                 }
-                *reinterpret_cast<uint2*>(orow + t * C) =
-                    uint2{o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                          o[2] | (static_cast<uint32_t>(o[3]) << 16)};
+                st_stream_u2(orow + t * C, uint2{o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                                                 o[2] | (static_cast<uint32_t>(o[3]) << 16)});
             }
         }
         if (FULL) {
@@ -307,7 +306,7 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
             const int64_t t = tg + kGroup + u;
-            xb[u] = t < t1 ? *reinterpret_cast<const uint2*>(xrow + t * C) : uint2{0u, 0u};
+            xb[u] = t < t1 ? ld_stream_u2(xrow + t * C) : uint2{0u, 0u};
             ib[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
         }
         const uint32_t near = group(tg, std::true_type{});

@@ -23,6 +23,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+// 8-byte accesses of data streamed once (read once or written once): non-temporal, so they do
+// not displace what other blocks re-read; measured faster on plain 1 GiB copies
+__device__ __forceinline__ uint2 ld_stream_u2(const uint16_t* p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return uint2{v[0], v[1]};
+}
+__device__ __forceinline__ void st_stream_u2(uint16_t* p, uint2 v) {
+    __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
+}
 // two floats -> two bf16 (nearest even) in one word, lo in bits 0-15 (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
