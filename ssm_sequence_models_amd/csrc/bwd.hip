@@ -485,7 +485,6 @@ constexpr int kH0Q = 64, kH0P = 64, kH0N = 128;
 constexpr int kH0Row = kH0Q * 2 + 16;  // bytes per [row][64 tokens] bf16 row in LDS (padded)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float h0_incl_sum(float v) {
     const int z = __float_as_int(0.0f);

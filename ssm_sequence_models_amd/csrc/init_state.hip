@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kStatsThreads) void state_stats_kernel(
                 float4 q[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    q[r] = reinterpret_cast<const float4*>(fin + ((b0 + r) * H + h) * per)[i];
+                    q[r] = ld_stream_f4(reinterpret_cast<const float4*>(fin + ((b0 + r) * H + h) * per) + i);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc4(q[r]);
             }
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kStatsThreads) void state_stats_kernel(
             const float4* r4 = reinterpret_cast<const float4*>(row);
             const int64_t n4 = per / 4;
 #pragma unroll 4
-            for (int64_t i = threadIdx.x; i < n4; i += kStatsThreads) acc4(r4[i]);
+            for (int64_t i = threadIdx.x; i < n4; i += kStatsThreads) acc4(ld_stream_f4(r4 + i));
         } else {
             for (int64_t i = threadIdx.x; i < per; i += kStatsThreads) {
                 const double d = row[i] - shift;
@@ -179,9 +179,9 @@ __global__ __launch_bounds__(256) void noise_kernel(float* out, int64_t n, int64
         for (int j = 0; j < 8; ++j) z[j] = sigma * z[j];
     }
     if (e0 + 7 < n && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-        float4* o = reinterpret_cast<float4*>(out + e0);
-        o[0] = make_float4(z[0], z[1], z[2], z[3]);
-        o[1] = make_float4(z[4], z[5], z[6], z[7]);
+        f32x4_t* o = reinterpret_cast<f32x4_t*>(out + e0);
+        __builtin_nontemporal_store(f32x4_t{z[0], z[1], z[2], z[3]}, o);
+        __builtin_nontemporal_store(f32x4_t{z[4], z[5], z[6], z[7]}, o + 1);
     } else {
         for (int j = 0; j < 8 && e0 + j < n; ++j) out[e0 + j] = z[j];
     }
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void reset_kernel(const U* src, U* dst, uint8_
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         const int64_t u = start + k * 256;
-        if (u < units) dst[base + u] = zero ? U{} : src[base + u];
+        if (u < units) __builtin_nontemporal_store(zero ? U{} : __builtin_nontemporal_load(src + base + u), dst + base + u);
     }
 }
 
@@ -241,8 +241,8 @@ hipError_t launch_state_reset(const void* src, void* dst, uint8_t* mask, int64_t
     const int64_t bpr = units > 0 ? (units + 1023) / 1024 : 1;
     const unsigned grid = static_cast<unsigned>(B * bpr);
     if (unit == 16)
-        reset_kernel<uint4><<<grid, 256, 0, stream>>>(static_cast<const uint4*>(src),
-                                                       static_cast<uint4*>(dst), mask, units, bpr,
+        reset_kernel<u32x4_t><<<grid, 256, 0, stream>>>(static_cast<const u32x4_t*>(src),
+                                                         static_cast<u32x4_t*>(dst), mask, units, bpr,
                                                        threshold, seed, offset);
     else if (unit == 4)
         reset_kernel<uint32_t><<<grid, 256, 0, stream>>>(static_cast<const uint32_t*>(src),

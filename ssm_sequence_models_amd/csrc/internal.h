@@ -33,6 +33,11 @@ __device__ __forceinline__ uint2 ld_stream_u2(const uint16_t* p) {
 __device__ __forceinline__ void st_stream_u2(uint16_t* p, uint2 v) {
     __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
 }
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream_f4(const float4* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
 // two floats -> two bf16 (nearest even) in one word, lo in bits 0-15 (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
