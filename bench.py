@@ -110,16 +110,19 @@ def _time_gpu(torch, fn, reps, warm=2):
     return sum(t) / len(t)
 
 
-def copy_bandwidth(torch):
-    """Read + write bandwidth of a plain 1 GiB device-to-device copy (GB/s): what streaming
-    code reaches on this machine, the reference for the fractions below beside the 8 TB/s peak."""
+def copy_bandwidth(torch, ssm):
+    """Read + write bandwidth (GB/s) of two plain 1 GiB device-to-device copies: the runtime's
+    own (torch's copy_) and the library's streaming copy (non-temporal 16-byte accesses, which
+    outruns the runtime's on this GPU).  The faster is the reference for the fractions below,
+    beside the 8 TB/s peak: what streaming code reaches on this machine."""
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
     src.fill_(1)
-    ms = _time_gpu(torch, lambda: dst.copy_(src), 5)
+    rt = 2 * n / (_time_gpu(torch, lambda: dst.copy_(src), 5) * 1e-3) / 1e9
+    st = 2 * n / (_time_gpu(torch, lambda: ssm.stream_copy(src, dst), 5) * 1e-3) / 1e9
     del src, dst
-    return 2 * n / (ms * 1e-3) / 1e9
+    return max(rt, st), {"runtime_copy_GBs": rt, "stream_copy_GBs": st}
 
 
 def other_ops(torch, ssm, workloads, copy_GBs, only=None):
@@ -485,7 +488,7 @@ def main():
     log(f"bench: {ms_per_step:.4f} ms/step, main kernel {main_ms_avg:.4f} ms")
     n_chunks = (s.L + 63) // 64
     mfma_flops = s.B * s.H * n_chunks * MFMA_PER_CHUNK_HEAD * FLOP_PER_MFMA
-    copy_GBs = copy_bandwidth(torch)
+    copy_GBs, copy_detail = copy_bandwidth(torch, ssm)
 
     result = {
         "metric": METRIC,
@@ -512,7 +515,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "ssd_main_kernel", "kernel_ms": main_ms_avg,
                      "algorithmic_bytes_per_launch": main_bytes,
-                     "copy_GBs": copy_GBs, "frac_of_copy": achieved / copy_GBs},
+                     "copy_GBs": copy_GBs, **copy_detail, "frac_of_copy": achieved / copy_GBs},
         "mfma": {"kernel": "ssd_main_kernel", "issued_flops_per_launch": mfma_flops,
                  "achieved_TFLOPs": mfma_flops / (main_ms_avg * 1e-3) / 1e12,
                  "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,

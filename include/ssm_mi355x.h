@@ -469,6 +469,15 @@ ssm_status_t ssm_state_reset(const void* src, void* dst, uint8_t* reset_mask, in
 ssm_status_t ssm_timing_enable(int enable);
 ssm_status_t ssm_timing_read(double* total_ms, int64_t* launches);
 
+/* ssm_stream_copy -- a plain device-to-device copy of `bytes` bytes with non-temporal 16-byte
+ * accesses (byte accesses for a tail, or when either pointer is not 16-byte aligned).  Not
+ * part of the method: it is the streaming reference the benchmark reports beside the HBM
+ * peak, since a copy with these accesses outruns the runtime's own device copy on this GPU.
+ *   src, dst   device memory, must not overlap (SSM_ERR_INVALID_ARG if they do)
+ * bytes = 0: no-op (pointers may be NULL).  bytes < 0: SSM_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------------------- */
+ssm_status_t ssm_stream_copy(const void* src, void* dst, int64_t bytes, ssm_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -102,14 +102,15 @@ def _load():
     lib.ssm_initial_state_noise.argtypes = [fp, i64, i64, i64, i64, fp, fp, ctypes.c_float, u64,
                                             u64, vp]
     lib.ssm_state_reset.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, u64, u64, vp]
+    lib.ssm_stream_copy.argtypes = [vp, vp, i64, vp]
     lib.ssm_timing_enable.argtypes = [ci]
     lib.ssm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
     for f in ("ssm_conv1d_fwd", "ssm_conv1d_update", "ssm_scan_fwd", "ssm_conv_scan_fwd",
               "ssm_conv_scan_fwd_noalloc", "ssm_step", "ssm_decode_step", "ssm_conv1d_bwd", "ssm_scan_bwd_initial_state",
               "ssm_conv_scan_fwd_pooled", "ssm_state_stats_update", "ssm_scan_fwd_vector_decay",
-              "ssm_initial_state_noise", "ssm_state_reset", "ssm_timing_enable",
-              "ssm_timing_read"):
+              "ssm_initial_state_noise", "ssm_state_reset", "ssm_stream_copy",
+              "ssm_timing_enable", "ssm_timing_read"):
         getattr(lib, f).restype = ci
     return lib
 
@@ -588,6 +589,18 @@ def decode_step(x_new, conv_state, conv_weight, conv_bias, dt, A, ssm_state, nhe
         _ptr(state_indices), _ptr(conv_out), _ptr(y), bsz, n_new, H, P, G, N, K, state_len,
         n_cslots, ssm_state.shape[0], _dtype_code(x_new), ACT[activation], _stream()))
     return y
+
+
+def stream_copy(src, dst):
+    """dst <- src (same number of bytes, no overlap) with the library's streaming copy: the
+    bandwidth reference of the benchmark, not part of the method."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("stream_copy: src and dst differ in size")
+    _need(src, "src")
+    _need(dst, "dst")
+    _check("ssm_stream_copy", _lib.ssm_stream_copy(_ptr(src), _ptr(dst), nb, _stream()))
+    return dst
 
 
 def timing_enable(enable: bool = True):

@@ -922,6 +922,18 @@ ssm_status_t ssm_state_reset(const void* src, void* dst, uint8_t* reset_mask, in
                       fn);
 }
 
+ssm_status_t ssm_stream_copy(const void* src, void* dst, int64_t bytes, ssm_stream_t stream) {
+    const char* fn = "ssm_stream_copy";
+    if (bytes < 0) return fail(SSM_ERR_INVALID_ARG, "ssm_stream_copy: need bytes >= 0");
+    ssm_status_t st = check_ptrs(fn, {{"src", src, bytes > 0, 1}, {"dst", dst, bytes > 0, 1}});
+    if (st != SSM_OK) return st;
+    if (bytes == 0) return ok();
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + static_cast<uintptr_t>(bytes) && d0 < s0 + static_cast<uintptr_t>(bytes))
+        return fail(SSM_ERR_INVALID_ARG, "ssm_stream_copy: src and dst overlap");
+    return hip_status(ssm::launch_stream_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 ssm_status_t ssm_timing_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_tmu);
     g_timing = enable != 0;

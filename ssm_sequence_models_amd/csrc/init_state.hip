@@ -12,6 +12,8 @@
 // purpose 0 is the Gaussian noise (Box-Muller on 24 bits of each half of a word: eight
 // normals per block), purpose 1 the reset decisions (top 32 bits of one word against
 // floor(p 2^32)).
+#include <algorithm>
+
 #include "internal.h"
 
 namespace ssm {
@@ -210,7 +212,46 @@ __global__ __launch_bounds__(256) void reset_kernel(const U* src, U* dst, uint8_
     }
 }
 
+// A plain device-to-device copy with non-temporal 16-byte accesses, four units per thread in
+// flight: the streaming reference the benchmark sets beside the HBM peak.  Bytes past the last
+// whole unit (and every byte of a copy whose pointers are not 16-byte aligned) go one at a time.
+__global__ void __launch_bounds__(256) stream_copy_kernel(const u32x4_t* src, u32x4_t* dst,
+                                                          int64_t units) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 1024;
+    for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x; i0 < units; i0 += stride) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + 256 * u < units) v[u] = __builtin_nontemporal_load(src + i0 + 256 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + 256 * u < units) __builtin_nontemporal_store(v[u], dst + i0 + 256 * u);
+    }
+}
+
+__global__ void __launch_bounds__(256) byte_copy_kernel(const uint8_t* src, uint8_t* dst, int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
+    const int64_t units = (a & 15) == 0 ? bytes / 16 : 0;
+    if (units > 0) {
+        const int64_t blocks = std::min<int64_t>((units + 1023) / 1024, 16384);
+        stream_copy_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+            static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), units);
+    }
+    const int64_t rest = bytes - 16 * units;
+    if (rest > 0) {
+        const int64_t blocks = std::min<int64_t>((rest + 255) / 256, 16384);
+        byte_copy_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
+            static_cast<const uint8_t*>(src) + 16 * units, static_cast<uint8_t*>(dst) + 16 * units, rest);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_state_stats(const float* fin, int64_t B, int64_t H, int64_t per, double beta,
                               float* mean, float* var, hipStream_t stream) {
@@ -243,7 +284,7 @@ hipError_t launch_state_reset(const void* src, void* dst, uint8_t* mask, int64_t
     if (unit == 16)
         reset_kernel<u32x4_t><<<grid, 256, 0, stream>>>(static_cast<const u32x4_t*>(src),
                                                          static_cast<u32x4_t*>(dst), mask, units, bpr,
-                                                       threshold, seed, offset);
+                                                         threshold, seed, offset);
     else if (unit == 4)
         reset_kernel<uint32_t><<<grid, 256, 0, stream>>>(static_cast<const uint32_t*>(src),
                                                          static_cast<uint32_t*>(dst), mask, units,

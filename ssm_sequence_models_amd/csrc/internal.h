@@ -242,6 +242,7 @@ hipError_t launch_state_noise(float* out, int64_t n, int64_t H, int64_t per, con
                               const float* var, float sigma, uint64_t seed, uint64_t offset,
                               hipStream_t stream);
 int64_t state_reset_blocks(int64_t B, int64_t row_bytes, int unit);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_state_reset(const void* src, void* dst, uint8_t* mask, int64_t B,
                               int64_t row_bytes, int unit, uint64_t threshold, uint64_t seed,
                               uint64_t offset, hipStream_t stream);

@@ -152,7 +152,13 @@ def test_argument_errors_return_status(lib):
                                          None, None, dummy, 1, 64, 3, 64, 2, 128, 4, 1, 1,
                                          None) == 1
     assert lib.ssm_noalloc_scratch_bytes() == 32 << 20
+    # streaming copy: negative size, overlapping ranges (rejected before any launch)
+    assert lib.ssm_stream_copy(dummy, dummy, -1, None) == 1
+    assert lib.ssm_stream_copy(_c(256), _c(300), 100, None) == 1
+    assert b"overlap" in lib.ssm_last_error()
+    assert lib.ssm_stream_copy(None, dummy, 16, None) == 1
     # zero-sized work is a no-op that succeeds without touching the device
+    assert lib.ssm_stream_copy(None, None, 0, None) == 0
     assert lib.ssm_conv1d_update(None, None, None, None, None, None, None, 0, 8, 1, 4, 3, 4, 1,
                                  0, None) == 0
     assert lib.ssm_step(None, 0, 0, 1, None, None, None, 0, 0, 1, None, 0, 0, 1, None, None,

@@ -155,3 +155,23 @@ def test_debug_checks_reject_shared_slots(monkeypatch):
     padded = dev(torch.tensor([-1, 1, -1, 2], dtype=torch.int32))
     ssm.decode_step(x, pool, w, b, dt, A, spool, H, P, G, N, conv_state_indices=padded)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("nbytes,src_off,dst_off", [
+    (1 << 20, 0, 0), ((1 << 20) + 7, 0, 0), (4096 * 1024 + 48, 16, 32),   # 16-byte path + tail
+    (1000, 1, 0), (33, 0, 3), (1, 5, 9),                                  # byte path
+])
+def test_stream_copy_copies_every_byte(nbytes, src_off, dst_off):
+    """The benchmark's streaming copy reference: dst equals src byte for byte, and the bytes
+    around dst are untouched."""
+    import ssm_sequence_models_amd as ssm
+    g = torch.Generator().manual_seed(nbytes)
+    src_buf = torch.randint(0, 256, (nbytes + 64,), generator=g, dtype=torch.uint8).to("cuda")
+    dst_buf = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    src = src_buf[src_off:src_off + nbytes]
+    dst = dst_buf[dst_off:dst_off + nbytes]
+    ssm.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), src.cpu())
+    assert (dst_buf[:dst_off].cpu() == 0xA5).all() and (dst_buf[dst_off + nbytes:].cpu() == 0xA5).all()
+
