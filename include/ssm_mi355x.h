@@ -239,7 +239,10 @@ ssm_status_t ssm_scan_fwd_vector_decay(const void* x, const float* dt, const flo
 /* ---------------------------------------------------------------------------------------
  * ssm_conv_scan_fwd -- the fused prefill: ssm_conv1d_fwd over the channels of xBC (with
  * phi; its output rounded to dtype exactly as the standalone call would store it), split
- * into x | B | C channel ranges, then ssm_scan_fwd.  One pass over HBM for x.
+ * into x | B | C channel ranges, then ssm_scan_fwd.  One pass over HBM for x.  The conv is
+ * the extended-sequence definition with its carried state ([CC] ch. 7, "defining the state
+ * through the extended sequence"); the scan is [LG] Sec. 2.1 Eq. (1) started from the
+ * initial state (Sec. 2.5 Eq. (4)) and returning the final state (Sec. 2.6 State Passing).
  *
  *   xBC                [batch, seqlen, nheads*headdim + 2*ngroups*dstate]  dtype;
  *                      channels [0, H*P) are x (head-major), then B (group-major), then C
@@ -464,7 +467,9 @@ ssm_status_t ssm_state_reset(const void* src, void* dst, uint8_t* reset_mask, in
  * chunked-scan main kernel (the dominant kernel of ssm_scan_fwd / ssm_conv_scan_fwd) is
  * bracketed by a pair of HIP events recorded on the call's stream.  ssm_timing_read waits
  * for the recorded events, returns the summed kernel time in milliseconds and the number of
- * launches, and clears the record.  Not thread-safe with concurrent calls on other threads.
+ * launches, and clears the record.  Event pairs are created the first time they are needed
+ * and kept for reuse after a read, so a timed loop creates events only until its first read.
+ * Not thread-safe with concurrent calls on other threads.
  * ------------------------------------------------------------------------------------- */
 ssm_status_t ssm_timing_enable(int enable);
 ssm_status_t ssm_timing_read(double* total_ms, int64_t* launches);

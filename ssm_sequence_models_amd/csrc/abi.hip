@@ -34,7 +34,12 @@ bool valid_act(int a) { return a == SSM_ACT_NONE || a == SSM_ACT_SILU; }
 // ---- optional kernel timing (measurement only) ----
 std::mutex g_tmu;
 bool g_timing = false;
-std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
+struct EventPair {
+    hipEvent_t e0, e1;
+    int dev;
+};
+std::vector<EventPair> g_events;  // recorded, not yet read
+std::vector<EventPair> g_spare;   // read, kept for reuse (created once, never per launch)
 
 // Pointer arguments: name, pointer, required?, element alignment.
 struct PtrCheck {
@@ -204,15 +209,29 @@ ssm_status_t run_recurrent_scan(const char* fn, const void* x, int64_t x_row, co
 
 hipEvent_t g_none = nullptr;
 
-// Events for the timing record (both NULL when timing is off).
+// Events for the timing record (both NULL when timing is off): a pair from the spare list
+// of the current device when there is one, else a new pair (created once; ssm_timing_read
+// returns pairs to the spare list instead of destroying them).
 ssm_status_t timing_events(hipEvent_t* ev0, hipEvent_t* ev1) {
     *ev0 = *ev1 = g_none;
     std::lock_guard<std::mutex> lk(g_tmu);
     if (!g_timing) return SSM_OK;
-    hipError_t e = hipEventCreate(ev0);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "timing");
+    for (size_t i = g_spare.size(); i-- > 0;) {
+        if (g_spare[i].dev == dev) {
+            g_events.push_back(g_spare[i]);
+            g_spare.erase(g_spare.begin() + static_cast<std::ptrdiff_t>(i));
+            *ev0 = g_events.back().e0;
+            *ev1 = g_events.back().e1;
+            return SSM_OK;
+        }
+    }
+    e = hipEventCreate(ev0);
     if (e == hipSuccess) e = hipEventCreate(ev1);
     if (e != hipSuccess) return hip_status(e, "timing");
-    g_events.emplace_back(*ev0, *ev1);
+    g_events.push_back({*ev0, *ev1, dev});
     return SSM_OK;
 }
 
@@ -942,7 +961,7 @@ ssm_status_t ssm_timing_enable(int enable) {
 
 ssm_status_t ssm_timing_read(double* total_ms, int64_t* launches) {
     if (!total_ms || !launches) return fail(SSM_ERR_INVALID_ARG, "ssm_timing_read: NULL output");
-    std::vector<std::pair<hipEvent_t, hipEvent_t>> evs;
+    std::vector<EventPair> evs;
     {
         std::lock_guard<std::mutex> lk(g_tmu);
         evs.swap(g_events);
@@ -951,12 +970,14 @@ ssm_status_t ssm_timing_read(double* total_ms, int64_t* launches) {
     hipError_t err = hipSuccess;
     for (auto& pr : evs) {
         float ms = 0.0f;
-        hipError_t e = hipEventSynchronize(pr.second);
-        if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+        hipError_t e = hipEventSynchronize(pr.e1);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.e0, pr.e1);
         if (e != hipSuccess && err == hipSuccess) err = e;
         sum += ms;
-        hipEventDestroy(pr.first);
-        hipEventDestroy(pr.second);
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_tmu);
+        g_spare.insert(g_spare.end(), evs.begin(), evs.end());
     }
     *total_ms = sum;
     *launches = static_cast<int64_t>(evs.size());
