@@ -38,6 +38,8 @@
 // one ds_swizzle level) ran 2.25 ms against 2.13 for 2 x 8 blocks, timed side by side.
 // Raising the compute or the staging waves' issue priority (s_setprio 2) changed nothing.
 // bf16, P = 64 and N in {64, 128}; other cases use the general token-sequential kernel.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ssm {
@@ -82,13 +84,34 @@ __device__ __forceinline__ float rs16x2(const float (&v)[2], int lane) {
     return r;
 }
 
+// Inclusive prefix sum over the 16 lanes of a DPP row (row_shr 1, 2, 4, 8; lanes without a
+// source add 0).
+__device__ __forceinline__ float vd_row_prefix(float v) {
+    const int z = __float_as_int(0.0f);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    return v;
+}
+
+// A piece's tile prefix of log a must stay within +-kVdSpan for the rescaled form (the factors
+// e^{+-L} stay within 2^{+-64}, so B / P and C P keep their precision)
+constexpr float kVdSpan = 44.0f;
+
 template <int N>
 __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     using D = BF16;
     using T = typename D::T;
     constexpr int R = vd_row<N>();
     constexpr int oC = N, oA = 2 * N, oX = 3 * N, oU = 3 * N + kVdPh;
-    __shared__ __attribute__((aligned(16))) float lds[2 * kVdTile * R];  // two tile buffers
+    // two tile buffers: kVdTile rows of R floats, then the tile's end factors P [N] and one
+    // word per 8-dimension piece (1: the piece is stored in the rescaled form)
+    constexpr int kOct = N / 8;  // 8-dimension pieces per token
+    constexpr int kBuf = kVdTile * R + N + kOct;
+    constexpr int oP = kVdTile * R, oF = kVdTile * R + N;
+    static_assert(kBuf % 4 == 0, "16-byte aligned buffers");
+    __shared__ __attribute__((aligned(16))) float lds[2 * kBuf];
 
     const int tid = threadIdx.x;
     const int64_t h = blockIdx.x, b = blockIdx.y;
@@ -99,14 +122,16 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     const T* bs = static_cast<const T*>(a.Bm);
     const T* cs = static_cast<const T*>(a.Cm);
 
-    // staging (waves 4-7): thread sti handles one (token, 8 dimensions) unit of B, C and the
-    // gates and one pair of x values per tile, as 16-byte (B, C, gates) and 4-byte (x) loads.
-    // The loads of tile k+2 are issued right after tile k+1 is stored, so they have a whole
-    // tile of compute to arrive (the registers hold one tile).
+    // staging (waves 4-7): lane sl of staging wave sw handles token sl % 16 of the tile and the
+    // 8-dimension piece kPPW sw + sl / 16 of B, C and the gates (so a piece's 16 tokens are the
+    // 16 lanes of one DPP row), and thread sti one pair of x values, as 16-byte (B, C, gates)
+    // and 4-byte (x) loads.  The loads of tile k+2 are issued right after tile k+1 is stored,
+    // so they have a whole tile of compute to arrive (the registers hold one tile).
     const int sti = tid - kVdCompute;
-    constexpr int kOct = N / 8;                    // 8-dimension pieces per token
-    const int su_t = sti / kOct, su_q = sti % kOct;  // unit: token su_t of the tile, piece su_q
-    const bool su_live = sti < kVdTile * kOct;
+    constexpr int kPPW = kOct / 4;  // pieces per staging wave
+    const int sl = tid & 63;
+    const int su_t = sl & 15, su_q = kPPW * ((sti >> 6) & 3) + (sl >> 4);
+    const bool su_live = (sl >> 4) < kPPW;
     const int sx_t = sti / (kVdPh / 2), sx_p = 2 * (sti % (kVdPh / 2));  // x pair
     uint4 rb, rc;
     float4 rg0, rg1;
@@ -144,13 +169,33 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
                                                     h * kVdP + kVdPh * half + sx_p);
         ru = (sti < nt && a.dt) ? a.dt[(b * a.T + t0 + sti) * a.H + h] : 1.0f;
     };
+    // Within a tile the compute lanes keep the state rescaled, S~_t = S_t / P_t with
+    // P_t = a_1 ... a_t (per dimension, from the tile's start): then
+    //     S~_t = S~_{t-1} + u_t x_t (B_t / P_t),    y_t = (C_t P_t) . S~_t,
+    // two fused multiply-adds per element instead of a multiply and two, and S = P_end S~ at
+    // the tile's end.  The staging lanes form L_t = log P_t (a prefix over their row), and
+    // store B / P, C P and a = 1 for a piece whose L stays within +-kVdSpan on every token;
+    // any other piece (a reset, a fast decay, a NaN) keeps the plain form: B, C, a_t and an end
+    // factor of 1.
     auto store_tile = [&](int64_t k) {
-        float* buf = lds + (k & 1) * (kVdTile * R);
+        float* buf = lds + (k & 1) * kBuf;
         const int nt = static_cast<int>(min(static_cast<int64_t>(kVdTile), a.T - k * kVdTile));
-        if (su_live && su_t < nt) {
+        const bool tok = su_live && su_t < nt;
+        const float lg[8] = {rg0.x, rg0.y, rg0.z, rg0.w, rg1.x, rg1.y, rg1.z, rg1.w};
+        float L[8];
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // tokens past the tile's end add 0, so the row's last lane holds the end value
+            L[e] = vd_row_prefix(!tok ? 0.0f : rr ? -__builtin_huge_valf() : lg[e]);
+            ok = ok && L[e] >= -kVdSpan && L[e] <= kVdSpan;
+        }
+        const uint64_t badm = __ballot(!ok);
+        const bool scaled = ((badm >> (sl & 48)) & 0xFFFFull) == 0;
+        if (tok) {
             float* row = buf + su_t * R + 8 * su_q;
             const uint32_t wb[4] = {rb.x, rb.y, rb.z, rb.w}, wc[4] = {rc.x, rc.y, rc.z, rc.w};
-            float fb[8], fc[8];
+            float fb[8], fc[8], fa[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 fb[2 * e] = __uint_as_float(wb[e] << 16);
@@ -158,17 +203,32 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
                 fc[2 * e] = __uint_as_float(wc[e] << 16);
                 fc[2 * e + 1] = __uint_as_float(wc[e] & 0xFFFF0000u);
             }
+            if (scaled) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    fb[e] *= __expf(-L[e]);
+                    fc[e] *= __expf(L[e]);
+                    fa[e] = 1.0f;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fa[e] = rr ? 0.0f : __expf(lg[e]);
+            }
             *reinterpret_cast<float4*>(row) = make_float4(fb[0], fb[1], fb[2], fb[3]);
             *reinterpret_cast<float4*>(row + 4) = make_float4(fb[4], fb[5], fb[6], fb[7]);
             *reinterpret_cast<float4*>(row + oC) = make_float4(fc[0], fc[1], fc[2], fc[3]);
             *reinterpret_cast<float4*>(row + oC + 4) = make_float4(fc[4], fc[5], fc[6], fc[7]);
-            float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-            if (!rr) {
-                a0 = make_float4(__expf(rg0.x), __expf(rg0.y), __expf(rg0.z), __expf(rg0.w));
-                a1 = make_float4(__expf(rg1.x), __expf(rg1.y), __expf(rg1.z), __expf(rg1.w));
-            }
-            *reinterpret_cast<float4*>(row + oA) = a0;
-            *reinterpret_cast<float4*>(row + oA + 4) = a1;
+            *reinterpret_cast<float4*>(row + oA) = make_float4(fa[0], fa[1], fa[2], fa[3]);
+            *reinterpret_cast<float4*>(row + oA + 4) = make_float4(fa[4], fa[5], fa[6], fa[7]);
+        }
+        if (su_live && su_t == kVdTile - 1) {
+            // the row's last lane: the piece's end factors and its form
+            float pe[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pe[e] = scaled ? __expf(L[e]) : 1.0f;
+            *reinterpret_cast<float4*>(buf + oP + 8 * su_q) = make_float4(pe[0], pe[1], pe[2], pe[3]);
+            *reinterpret_cast<float4*>(buf + oP + 8 * su_q + 4) = make_float4(pe[4], pe[5], pe[6], pe[7]);
+            reinterpret_cast<uint32_t*>(buf + oF)[su_q] = scaled ? 1u : 0u;
         }
         if (sx_t < nt)
             *reinterpret_cast<float2*>(buf + sx_t * R + oX + sx_p) =
@@ -207,8 +267,10 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     // tid % 8 == 0 write it
     const int p_out = p0 + ((tid >> 3) & 1);
     T* y_p = y + (b * a.T * a.H + h) * kVdP + p_out;  // y[b, 0, h, p_out]
-    // one token: decay-and-input update, per-channel read-out into acc[0..1]
-    auto token = [&](const float* row, float* acc) {
+    // one token: decay-and-input update, per-channel read-out into acc[0..1]; TWO: every
+    // piece of this wave is in the rescaled form (a = 1), so the decay multiply is left out
+    auto token = [&](const float* row, float* acc, auto two) {
+        constexpr bool TWO = decltype(two)::value;
         const float u = row[oU];
         const float2 x2 = *reinterpret_cast<const float2*>(row + oX + pl);
         const float dx[2] = {u * x2.x, u * x2.y};
@@ -216,11 +278,13 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
 #pragma unroll
         for (int c = 0; c < NL / 4; ++c) {
             const float4 b4 = *reinterpret_cast<const float4*>(row + n0 + 4 * c);
-            const float4 a4 = *reinterpret_cast<const float4*>(row + oA + n0 + 4 * c);
             const float4 c4 = *reinterpret_cast<const float4*>(row + oC + n0 + 4 * c);
             bv[4 * c] = b4.x; bv[4 * c + 1] = b4.y; bv[4 * c + 2] = b4.z; bv[4 * c + 3] = b4.w;
-            av[4 * c] = a4.x; av[4 * c + 1] = a4.y; av[4 * c + 2] = a4.z; av[4 * c + 3] = a4.w;
             cv[4 * c] = c4.x; cv[4 * c + 1] = c4.y; cv[4 * c + 2] = c4.z; cv[4 * c + 3] = c4.w;
+            if (!TWO) {
+                const float4 a4 = *reinterpret_cast<const float4*>(row + oA + n0 + 4 * c);
+                av[4 * c] = a4.x; av[4 * c + 1] = a4.y; av[4 * c + 2] = a4.z; av[4 * c + 3] = a4.w;
+            }
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -229,32 +293,50 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
             for (int e = 0; e < NL; ++e) {
                 // both steps update the state register in place (a multiply, then an
                 // accumulate), so the loop carries no register copies
-                st[i][e] *= av[e];
+                if (!TWO) st[i][e] *= av[e];
                 st[i][e] = __builtin_fmaf(dx[i], bv[e], st[i][e]);
                 s_ = __builtin_fmaf(cv[e], st[i][e], s_);
             }
             acc[i] = s_;
         }
     };
+    // a tile's tokens; the reduce-scatter of a token runs in the next token's iteration
+    auto tile_tokens = [&](const float* buf, int64_t t0, int nt, auto two) {
+        float pend[2] = {0.0f, 0.0f};
+        for (int tt = 0; tt < nt; ++tt) {
+            float acc[2];
+            token(buf + tt * R, acc, two);
+            if (tt > 0) {
+                const float yv = rs16x2(pend, tid);
+                if ((tid & 7) == 0) D::store(y_p, (t0 + tt - 1) * y_tok, yv);
+            }
+            pend[0] = acc[0];
+            pend[1] = acc[1];
+        }
+        if (nt > 0) {
+            const float yv = rs16x2(pend, tid);
+            if ((tid & 7) == 0) D::store(y_p, (t0 + nt - 1) * y_tok, yv);
+        }
+    };
     for (int64_t k = 0; k < ntiles; ++k) {
         if (compute) {
-            const float* buf = lds + (k & 1) * (kVdTile * R);
+            const float* buf = lds + (k & 1) * kBuf;
             const int64_t t0 = k * kVdTile;
             const int nt = static_cast<int>(min(static_cast<int64_t>(kVdTile), a.T - t0));
-            float pend[2] = {0.0f, 0.0f};
-            for (int tt = 0; tt < nt; ++tt) {
-                float acc[2];
-                token(buf + tt * R, acc);
-                if (tt > 0) {
-                    const float yv = rs16x2(pend, tid);
-                    if ((tid & 7) == 0) D::store(y_p, (t0 + tt - 1) * y_tok, yv);
-                }
-                pend[0] = acc[0];
-                pend[1] = acc[1];
-            }
-            if (nt > 0) {
-                const float yv = rs16x2(pend, tid);
-                if ((tid & 7) == 0) D::store(y_p, (t0 + nt - 1) * y_tok, yv);
+            const bool lane_scaled = reinterpret_cast<const uint32_t*>(buf + oF)[n0 / 8] != 0;
+            if (__ballot(!lane_scaled) == 0)
+                tile_tokens(buf, t0, nt, std::true_type{});
+            else
+                tile_tokens(buf, t0, nt, std::false_type{});
+            // back from the rescaled state (end factor 1 for a piece in the plain form)
+#pragma unroll
+            for (int c = 0; c < NL / 4; ++c) {
+                const float4 p4 = *reinterpret_cast<const float4*>(buf + oP + n0 + 4 * c);
+                const float pe[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st[i][4 * c + e] *= pe[e];
             }
         } else if (k + 1 < ntiles) {
             store_tile(k + 1);  // the other buffer, last read before the previous barrier
