@@ -303,6 +303,7 @@ __global__ void __launch_bounds__(kVdThreads) vdecay_kernel(RecurrentArgs a) {
     // a tile's tokens; the reduce-scatter of a token runs in the next token's iteration
     auto tile_tokens = [&](const float* buf, int64_t t0, int nt, auto two) {
         float pend[2] = {0.0f, 0.0f};
+#pragma unroll 4
         for (int tt = 0; tt < nt; ++tt) {
             float acc[2];
             token(buf + tt * R, acc, two);
