@@ -471,6 +471,42 @@ conv1d_update_kernel(const typename D::T* __restrict__ x, typename D::T* pool,
     for (int k = 0; k < K; ++k) wr[k] = w[c * K + k];
     const AT bv = bias ? bias[c] : 0.0f;
 
+    if constexpr (std::is_same<D, BF16>::value && K <= 5) {
+        // bf16 rows of 4 entries (the usual width-4 decode cache): the row is one 8-byte word,
+        // read once, updated in a register (ring insert, or shift for the linear layout) and
+        // written once; entry k sits in bits 16k .. 16k + 15.  Same arithmetic as below.
+        if (state_len == 4 && (reinterpret_cast<uintptr_t>(row) & 7) == 0) {
+            uint64_t r64 = *reinterpret_cast<const uint64_t*>(row);
+            auto entry = [&](int64_t slot) -> AT {
+                return bf16_to_f32(static_cast<uint16_t>(r64 >> (16 * slot)));
+            };
+            AT hist4[K - 1];
+#pragma unroll
+            for (int j = 1; j <= K - 1; ++j)
+                hist4[K - 1 - j] = entry(seqlens ? floor_mod(p - j, 4) : 4 - j);
+            for (int64_t i = 0; i < L_new; ++i) {
+                const uint16_t xb = xr[i];
+                const AT xv = bf16_to_f32(xb);
+                AT acc = bv;
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k) acc = fma(wr[k], hist4[k], acc);
+                acc = fma(wr[K - 1], xv, acc);
+                D::store(o, i, Acc<D>::out(acc, act));
+#pragma unroll
+                for (int k = 0; k < K - 2; ++k) hist4[k] = hist4[k + 1];
+                hist4[K - 2] = xv;
+                if (seqlens) {
+                    const int sh = 16 * static_cast<int>(floor_mod(p + i, 4));
+                    r64 = (r64 & ~(0xFFFFull << sh)) | (static_cast<uint64_t>(xb) << sh);
+                } else {
+                    r64 = (r64 >> 16) | (static_cast<uint64_t>(xb) << 48);
+                }
+            }
+            *reinterpret_cast<uint64_t*>(row) = r64;
+            return;
+        }
+    }
+
     // history, oldest first: hist[K-1-j] = value j steps back (read before any write)
     AT hist[K - 1];
 #pragma unroll
