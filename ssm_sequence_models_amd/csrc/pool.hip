@@ -45,13 +45,26 @@ __global__ void pool_gather_conv_kernel(const typename D::T* pool, const int32_t
     }
 }
 
-__global__ void pool_gather_ssm_kernel(const float* pool, const int32_t* indices, float* init,
-                                       int64_t B, int64_t per, int64_t n_slots) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= B * per) return;
-    const int64_t b = i / per, e = i % per;
+// SSM states: block (x, y) moves elements 1024 x .. 1024 x + 1023 of the states of rows
+// b = y, y + gridDim.y, ..., four per thread, as non-temporal 16-byte accesses when `vec`
+// (per % 4 == 0 and both bases 16-byte aligned); a row's slot is looked up once per block
+__global__ void __launch_bounds__(256) pool_gather_ssm_kernel(const float* pool,
+                                                              const int32_t* indices, float* init,
+                                                              int64_t B, int64_t per,
+                                                              int64_t n_slots, bool vec) {
+    const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (e >= per) return;
+    for (int64_t b = blockIdx.y; b < B; b += gridDim.y) {
     const int64_t s = indices ? static_cast<int64_t>(indices[b]) : b;
-    init[i] = (s >= 0 && s < n_slots) ? pool[s * per + e] : 0.0f;
+    const bool ok = s >= 0 && s < n_slots;
+    if (vec) {
+        const f32x4_t v = ok ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pool + s * per + e))
+                             : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(init + b * per + e));
+    } else {
+        for (int64_t k = e; k < e + 4 && k < per; ++k) init[b * per + k] = ok ? pool[s * per + k] : 0.0f;
+    }
+    }
 }
 
 template <class D>
@@ -78,13 +91,31 @@ __global__ void pool_scatter_conv_kernel(typename D::T* pool, const int32_t* ind
     }
 }
 
-__global__ void pool_scatter_ssm_kernel(float* pool, const int32_t* indices, const float* fin,
-                                        int64_t B, int64_t per, int64_t n_slots) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= B * per) return;
-    const int64_t b = i / per, e = i % per;
+__global__ void __launch_bounds__(256) pool_scatter_ssm_kernel(float* pool, const int32_t* indices,
+                                                               const float* fin, int64_t B,
+                                                               int64_t per, int64_t n_slots,
+                                                               bool vec) {
+    const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (e >= per) return;
+    for (int64_t b = blockIdx.y; b < B; b += gridDim.y) {
     const int64_t s = indices ? static_cast<int64_t>(indices[b]) : b;
-    if (s >= 0 && s < n_slots) pool[s * per + e] = fin[i];
+    if (s < 0 || s >= n_slots) continue;
+    if (vec) {
+        __builtin_nontemporal_store(
+            __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(fin + b * per + e)),
+            reinterpret_cast<f32x4_t*>(pool + s * per + e));
+    } else {
+        for (int64_t k = e; k < e + 4 && k < per; ++k) pool[s * per + k] = fin[b * per + k];
+    }
+    }
+}
+
+dim3 ssm_grid(int64_t batch, int64_t per) {
+    return dim3(static_cast<unsigned>((per + 1023) / 1024),
+                static_cast<unsigned>(batch < 65535 ? batch : 65535));
+}
+bool ssm_vec(const float* p, const float* q, int64_t per) {
+    return per % 4 == 0 && ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q)) & 15) == 0;
 }
 
 unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
@@ -104,8 +135,9 @@ hipError_t launch_pool_gather(const void* conv_pool, const float* ssm_pool, cons
         pool_gather_conv_kernel<F32><<<blocks_for(batch * C), 256, 0, stream>>>(
             static_cast<const float*>(conv_pool), indices, seqlens, static_cast<float*>(conv_hist),
             batch, C, K, state_len, n_slots);
-    pool_gather_ssm_kernel<<<blocks_for(batch * ssm_per), 256, 0, stream>>>(
-        ssm_pool, indices, ssm_init, batch, ssm_per, n_slots);
+    if (batch > 0 && ssm_per > 0)
+        pool_gather_ssm_kernel<<<ssm_grid(batch, ssm_per), 256, 0, stream>>>(
+            ssm_pool, indices, ssm_init, batch, ssm_per, n_slots, ssm_vec(ssm_pool, ssm_init, ssm_per));
     return hipGetLastError();
 }
 
@@ -122,8 +154,9 @@ hipError_t launch_pool_scatter(void* conv_pool, float* ssm_pool, const int32_t* 
         pool_scatter_conv_kernel<F32><<<blocks_for(batch * C), 256, 0, stream>>>(
             static_cast<float*>(conv_pool), indices, seqlens, static_cast<const float*>(x), batch,
             L, C, state_len, n_slots);
-    pool_scatter_ssm_kernel<<<blocks_for(batch * ssm_per), 256, 0, stream>>>(
-        ssm_pool, indices, ssm_final, batch, ssm_per, n_slots);
+    if (batch > 0 && ssm_per > 0)
+        pool_scatter_ssm_kernel<<<ssm_grid(batch, ssm_per), 256, 0, stream>>>(
+            ssm_pool, indices, ssm_final, batch, ssm_per, n_slots, ssm_vec(ssm_pool, ssm_final, ssm_per));
     return hipGetLastError();
 }
 
