@@ -171,10 +171,22 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
                          const uint16_t* dfin, uint16_t* dx, uint16_t* dinit, float* part,
                          int64_t L, int64_t C, int nruns, int silu) {
     constexpr int V = 4;
-    const int64_t c4 = (static_cast<int64_t>(blockIdx.x) * kConvBwdThreads + threadIdx.x) * V;
-    const int r = blockIdx.y;
+    // block = 64 channel quads x four consecutive runs, one run per wavefront; the four runs'
+    // dw / dbeta partial sums are added in the block (in order) before they leave
+    // the wave index through readfirstlane: the compiler then keeps the run's token bounds in
+    // scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t c4 = (static_cast<int64_t>(blockIdx.x) * 64 + lane) * V;
+    const int r = 4 * static_cast<int>(blockIdx.y) + wave;
     const int64_t b = blockIdx.z;
-    if (c4 >= C) return;  // no barriers in this kernel
+    float dwp[K][V], dbp[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        dbp[j] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) dwp[k][j] = 0.0f;
+    }
+    if (c4 < C && r < nruns) {
     const int64_t t0 = static_cast<int64_t>(r) * kConvBwdRun;
     const int64_t t1 = min(t0 + kConvBwdRun, L);
     float wk[K][V], beta[V];
@@ -207,17 +219,15 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
     }
     float dl[K][V];   // delta of tokens t-K+1 .. t (0 past the row's end)
     int32_t ds[K];
-    float dwp[K][V], dbp[V], dsd[K][V];
+    float dsd[K][V];
     int32_t dss[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         ds[k] = 0;
         dss[k] = id0;
 #pragma unroll
-        for (int j = 0; j < V; ++j) dl[k][j] = dwp[k][j] = dsd[k][j] = 0.0f;
+        for (int j = 0; j < V; ++j) dl[k][j] = dsd[k][j] = 0.0f;
     }
-#pragma unroll
-    for (int j = 0; j < V; ++j) dbp[j] = 0.0f;
 
     // one token, general case (the run's first K-1 tokens, its last K-1 steps and short runs)
     auto token = [&](int64_t t) {
@@ -426,12 +436,26 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
             }
         }
     }
-    float* pp = part + ((b * nruns + r) * C + c4) * (K + 1);
+    }
+    __shared__ float red[4][K + 1][V][64];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) pp[j * (K + 1) + k] = dwp[k][j];
-        pp[j * (K + 1) + K] = dbp[j];
+        for (int k = 0; k < K; ++k) red[wave][k][j][lane] = dwp[k][j];
+        red[wave][K][j][lane] = dbp[j];
+    }
+    __syncthreads();
+    if (wave == 0 && c4 < C) {
+        const int64_t ngroups = (nruns + 3) / 4;
+        float* pp = part + ((b * ngroups + blockIdx.y) * C + c4) * (K + 1);
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+#pragma unroll
+            for (int k = 0; k <= K; ++k) {
+                const double v = ((static_cast<double>(red[0][k][j][lane]) + red[1][k][j][lane]) +
+                                  red[2][k][j][lane]) + red[3][k][j][lane];
+                pp[j * (K + 1) + k] = static_cast<float>(v);
+            }
     }
 }
 
@@ -723,8 +747,8 @@ hipError_t launch_conv1d_bwd(const void* x, const float* w, const float* bias, c
                       ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dy) |
                         reinterpret_cast<uintptr_t>(dx)) & 7) == 0;
     if (vec4) {
-        const dim3 grid4(static_cast<unsigned>((C / 4 + kConvBwdThreads - 1) / kConvBwdThreads),
-                         static_cast<unsigned>(nruns), static_cast<unsigned>(batch));
+        const dim3 grid4(static_cast<unsigned>((C / 4 + 63) / 64),
+                         static_cast<unsigned>((nruns + 3) / 4), static_cast<unsigned>(batch));
 #define SSM_CBWD4(KK)                                                                          \
     case KK:                                                                                   \
         conv1d_bwd_bf16x4_kernel<KK><<<grid4, kConvBwdThreads, 0, stream>>>(                   \
@@ -748,8 +772,10 @@ hipError_t launch_conv1d_bwd(const void* x, const float* w, const float* bias, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nred = C * (K + 1);
+    // the four-channel kernel leaves one partial per group of four runs
+    const int64_t nparts = vec4 ? batch * ((nruns + 3) / 4) : batch * nruns;
     conv1d_bwd_reduce_kernel<<<static_cast<unsigned>((nred + 63) / 64), 256, 0, stream>>>(
-        part, dw, dbias, C, static_cast<int>(K), batch * nruns);
+        part, dw, dbias, C, static_cast<int>(K), nparts);
     return hipGetLastError();
 }
 
