@@ -322,7 +322,10 @@ ssm_status_t conv_scan_fwd_impl(const char* fn, const void* xBC, const float* co
                                 const int32_t* seq_idx, void* y, int64_t batch, int64_t seqlen,
                                 int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
                                 int64_t width, ssm_dtype_t dtype, ssm_act_t act, void* workspace,
-                                size_t workspace_bytes, bool timed, ssm_stream_t stream) {
+                                size_t workspace_bytes, bool timed, ssm_stream_t stream,
+                                const int32_t* state_slots = nullptr, int64_t n_state_slots = 0) {
+    // n_state_slots > 0 (the pooled prefill, chunked shapes only): the SSM states are rows
+    // state_slots[b] of an [n_state_slots, H, P, N] pool, read and written in place
     ssm_status_t st = check_scan_dims(fn, batch, seqlen, nheads, headdim, ngroups, dstate, dtype);
     if (st != SSM_OK) return st;
     if (!valid_act(act)) return fail(SSM_ERR_INVALID_ARG, std::string(fn) + ": bad activation");
@@ -349,7 +352,8 @@ ssm_status_t conv_scan_fwd_impl(const char* fn, const void* xBC, const float* co
         hipError_t e = ssm::launch_conv1d_fwd(nullptr, conv_w, conv_bias, conv_initial_state,
                                               conv_final_state, nullptr, nullptr, batch, 0,
                                               C_conv, width, dtype, act, s);
-        if (e == hipSuccess)
+        // pool rows stay where they are: nothing to copy
+        if (e == hipSuccess && n_state_slots <= 0)
             e = ssm::launch_copy_or_zero_f32(final_state, initial_state,
                                              batch * nheads * headdim * dstate, s);
         return hip_status(e, fn);
@@ -385,6 +389,8 @@ ssm_status_t conv_scan_fwd_impl(const char* fn, const void* xBC, const float* co
         a.A = A;
         a.init_state = initial_state;
         a.final_state = final_state;
+        a.state_slots = state_slots;
+        a.n_state_slots = n_state_slots;
         a.seq_idx = seq_idx;
         a.y = static_cast<uint16_t*>(y);
         a.B = batch;
@@ -403,6 +409,8 @@ ssm_status_t conv_scan_fwd_impl(const char* fn, const void* xBC, const float* co
     }
     // general shapes: conv into the workspace, then the token-sequential scan reading its
     // x | B | C channel ranges in place
+    if (n_state_slots > 0)
+        return fail(SSM_ERR_UNSUPPORTED, std::string(fn) + ": pool rows need the chunked path");
     if (!ssm::recurrent_supported(headdim, dstate))
         return fail(SSM_ERR_UNSUPPORTED, std::string(fn) + ": dstate must be 4 * 2^k <= 256 and headdim*dstate <= 16384");
     const size_t need = static_cast<size_t>(batch * seqlen * C_conv) * es;
@@ -775,17 +783,27 @@ ssm_status_t ssm_conv_scan_fwd_pooled(const void* xBC, const float* conv_w,
     void* hist = base + scan;
     float* sstate = reinterpret_cast<float*>(base + scan + hist_b);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // The chunked scan reads and writes the SSM pool rows itself (no gather or scatter of
+    // states); other shapes run the states through the workspace.
+    const bool in_pool = ssm::chunked_supported(headdim, dstate, dtype) && aligned(ssm_state, 16);
+    const int64_t moved = in_pool ? 0 : per;
     hipError_t e = ssm::launch_pool_gather(conv_state, ssm_state, state_indices, cache_seqlens,
-                                           hist, sstate, batch, C_conv, width, state_len, per,
+                                           hist, sstate, batch, C_conv, width, state_len, moved,
                                            n_slots, dtype, s);
     if (e != hipSuccess) return hip_status(e, fn);
-    st = ssm_conv_scan_fwd(xBC, conv_w, conv_bias, hist, nullptr, dt, A, sstate, sstate, seq_idx,
-                           y, batch, seqlen, nheads, headdim, ngroups, dstate, width, dtype, act,
-                           scan > 0 ? workspace : nullptr, scan, stream);
+    if (in_pool)
+        st = conv_scan_fwd_impl(fn, xBC, conv_w, conv_bias, hist, nullptr, dt, A, ssm_state,
+                                ssm_state, seq_idx, y, batch, seqlen, nheads, headdim, ngroups,
+                                dstate, width, dtype, act, scan > 0 ? workspace : nullptr, scan,
+                                true, stream, state_indices, n_slots);
+    else
+        st = ssm_conv_scan_fwd(xBC, conv_w, conv_bias, hist, nullptr, dt, A, sstate, sstate,
+                               seq_idx, y, batch, seqlen, nheads, headdim, ngroups, dstate, width,
+                               dtype, act, scan > 0 ? workspace : nullptr, scan, stream);
     if (st != SSM_OK) return st;
     return hip_status(ssm::launch_pool_scatter(conv_state, ssm_state, state_indices, cache_seqlens,
-                                               xBC, sstate, batch, seqlen, C_conv, state_len, per,
-                                               n_slots, dtype, s),
+                                               xBC, sstate, batch, seqlen, C_conv, state_len,
+                                               moved, n_slots, dtype, s),
                       fn);
 }
 

@@ -198,8 +198,13 @@ struct ChunkedArgs {
     int act;
     const float* dt;            // [B, L, H]
     const float* A;             // [H]
-    const float* init_state;    // [B, H, P, N] or NULL
+    const float* init_state;    // [B, H, P, N] or NULL (rows: see state_slots)
     float* final_state;         // [B, H, P, N] or NULL
+    // With n_state_slots > 0 the states are rows of [n_state_slots, H, P, N]: row b's at
+    // s = state_slots[b] (s = b without state_slots); a row whose s lies outside
+    // [0, n_state_slots) starts from zero and stores no final state
+    const int32_t* state_slots;
+    int64_t n_state_slots;
     const int32_t* seq_idx;     // [B, L] or NULL
     uint16_t* y;                // [B, L, H, P]
     int64_t B, L, H, P, G, N;

@@ -914,6 +914,9 @@ ssd_main_kernel(ChunkedArgs a) {
     const int64_t g = h / (a.H / a.G);
     const int64_t L = a.L;
     const int64_t nC = (L + kQ - 1) / kQ;
+    // the row of the initial / final state arrays this batch row uses
+    const int64_t srow = a.state_slots ? static_cast<int64_t>(a.state_slots[b]) : b;
+    const bool srow_ok = a.n_state_slots <= 0 || (srow >= 0 && srow < a.n_state_slots);
     // this block's chunks: global chunk c0 + c for c < nCl
     int64_t c0 = seg * a.seg_chunks;
     int64_t nCl = min(a.seg_chunks, nC - c0);
@@ -966,7 +969,7 @@ ssd_main_kernel(ChunkedArgs a) {
             const float* src =
                 PASS == 1 ? nullptr
                 : a.nseg > 1 ? a.seg_state + (((b * a.H + h) * a.nseg + seg) * kP + p_own) * kN
-                : a.init_state ? a.init_state + ((b * a.H + h) * kP + p_own) * kN : nullptr;
+                : a.init_state && srow_ok ? a.init_state + ((srow * a.H + h) * kP + p_own) * kN : nullptr;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
@@ -1153,8 +1156,8 @@ ssd_main_kernel(ChunkedArgs a) {
         float* dst = nullptr;
         if (PASS == 1)
             dst = a.seg_state + (((b * a.H + h) * a.nseg + seg + 1) * kP + p_own) * kN;
-        else if (a.final_state && seg == a.nseg - 1)
-            dst = a.final_state + ((b * a.H + h) * kP + p_own) * kN;
+        else if (a.final_state && srow_ok && seg == a.nseg - 1)
+            dst = a.final_state + ((srow * a.H + h) * kP + p_own) * kN;
         if (dst) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -1442,7 +1445,10 @@ __global__ void __launch_bounds__(256) seg_combine_kernel(ChunkedArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= a.B * a.H * per) return;
     const int64_t bh = i / per, e = i % per;
-    float hs = a.init_state ? a.init_state[bh * per + e] : 0.0f;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t srow = a.state_slots ? static_cast<int64_t>(a.state_slots[b]) : b;
+    const bool srow_ok = a.n_state_slots <= 0 || (srow >= 0 && srow < a.n_state_slots);
+    float hs = a.init_state && srow_ok ? a.init_state[(srow * a.H + h) * per + e] : 0.0f;
     float* st = a.seg_state + bh * a.nseg * per + e;
     st[0] = hs;
     for (int64_t sg = 1; sg < a.nseg; ++sg) {
