@@ -210,8 +210,9 @@ struct ChunkedArgs {
     int64_t B, L, H, P, G, N;
     void* workspace;            // chunked_workspace_bytes(B, L, H, G, N)
     // Set by launch_chunked.  Rows with few heads split into nseg segments of seg_chunks
-    // chunks run side by side: seg_state [B, H, nseg, P, N] holds each segment's entry state
-    // (first its local end state), seg_decay [B, H, nseg] each segment's decay product.
+    // chunks run side by side: seg_state [B, H, nseg, P, N] holds in slot 0 the initial state
+    // and in slot s >= 1 segment s-1's local end state from a zero start; seg_decay [B, H, nseg]
+    // each segment's decay product.
     int64_t nseg, seg_chunks;
     float* seg_state;
     float* seg_decay;

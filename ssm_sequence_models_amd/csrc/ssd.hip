@@ -966,10 +966,16 @@ ssd_main_kernel(ChunkedArgs a) {
         const int p_own = 16 * wave + li;
         f32x4 acc[8];
         {
-            const float* src =
-                PASS == 1 ? nullptr
-                : a.nseg > 1 ? a.seg_state + (((b * a.H + h) * a.nseg + seg) * kP + p_own) * kN
-                : a.init_state && srow_ok ? a.init_state + ((srow * a.H + h) * kP + p_own) * kN : nullptr;
+            // Row segments keep their states in the slots seg_state[b, h, s]: slot 0 the
+            // initial state (copied there by segment 0's state-only block, so the full pass
+            // never reads initial_state, which an in-place final state may overwrite), slot
+            // s >= 1 segment s-1's local end state l_{s-1}.  A full-pass block composes its
+            // entry state e_seg in order: e_0 = slot 0, e_s = D_{s-1} e_{s-1} + l_{s-1} ([LG]
+            // Sec. 2.5's initial-state increment, applied segment by segment).
+            const float* init =
+                a.init_state && srow_ok ? a.init_state + ((srow * a.H + h) * kP + p_own) * kN : nullptr;
+            float* slots = a.nseg > 1 ? a.seg_state + ((b * a.H + h) * a.nseg * kP + p_own) * kN : nullptr;
+            const float* src = PASS == 1 ? (seg == 0 ? init : nullptr) : (a.nseg > 1 ? slots : init);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 v0 = {0.0f, 0.0f, 0.0f, 0.0f}, v1 = v0;
@@ -979,6 +985,27 @@ ssd_main_kernel(ChunkedArgs a) {
                 }
                 acc[2 * m] = v0;
                 acc[2 * m + 1] = v1;
+            }
+            if (PASS == 1) {
+                if (seg == 0) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        *reinterpret_cast<f32x4*>(slots + 32 * m + 8 * g4) = acc[2 * m];
+                        *reinterpret_cast<f32x4*>(slots + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            } else if (a.nseg > 1) {
+                for (int64_t sg = 1; sg <= seg; ++sg) {
+                    const float d = a.seg_decay[(b * a.H + h) * a.nseg + sg - 1];
+                    const float* ls = slots + sg * (kP * kN);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        acc[2 * m] = d * acc[2 * m] + *reinterpret_cast<const f32x4*>(ls + 32 * m + 8 * g4);
+                        acc[2 * m + 1] = d * acc[2 * m + 1] + *reinterpret_cast<const f32x4*>(ls + 32 * m + 8 * g4 + 4);
+                    }
+                }
             }
         }
         __syncthreads();  // raw rows of chunk 0 staged
@@ -1150,9 +1177,9 @@ ssd_main_kernel(ChunkedArgs a) {
             }
             __syncthreads();
         }
-        // end state: a segment's local end state goes to the next segment's entry slot (the
-        // combine step turns it into that segment's entry state); the last segment (or the
-        // only one) writes the final state
+        // end state: a segment's local end state goes to slot seg + 1 (the full pass of the
+        // later segments composes its entry state from it); the last segment (or the only
+        // one) writes the final state
         float* dst = nullptr;
         if (PASS == 1)
             dst = a.seg_state + (((b * a.H + h) * a.nseg + seg + 1) * kP + p_own) * kN;
@@ -1436,27 +1463,6 @@ ssd_main_kernel(ChunkedArgs a) {
     }
 }
 
-// Entry states of the segments, in order: e_0 = h_{-1} (or 0), e_s = D_{s-1} e_{s-1} + l_{s-1},
-// where l_{s-1} (the local end state of segment s-1 from a zero start) sits in e_s's slot and
-// D_{s-1} is that segment's decay product (0 if a reset falls inside it).  This is [LG]
-// Sec. 2.5's increment, applied to the state a segment starts from.
-__global__ void __launch_bounds__(256) seg_combine_kernel(ChunkedArgs a) {
-    const int64_t per = static_cast<int64_t>(kP) * kN;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= a.B * a.H * per) return;
-    const int64_t bh = i / per, e = i % per;
-    const int64_t b = bh / a.H, h = bh % a.H;
-    const int64_t srow = a.state_slots ? static_cast<int64_t>(a.state_slots[b]) : b;
-    const bool srow_ok = a.n_state_slots <= 0 || (srow >= 0 && srow < a.n_state_slots);
-    float hs = a.init_state && srow_ok ? a.init_state[(srow * a.H + h) * per + e] : 0.0f;
-    float* st = a.seg_state + bh * a.nseg * per + e;
-    st[0] = hs;
-    for (int64_t sg = 1; sg < a.nseg; ++sg) {
-        hs = a.seg_decay[bh * a.nseg + sg - 1] * hs + st[sg * per];
-        st[sg * per] = hs;
-    }
-}
-
 template <int K, int MODE, int PASS>
 hipError_t launch_main(const ChunkedArgs& a, hipStream_t stream, int64_t nsl) {
     const dim3 grid(static_cast<unsigned>(a.B * a.H * nsl));
@@ -1469,10 +1475,6 @@ template <int K, int MODE>
 hipError_t launch_passes(const ChunkedArgs& a, hipStream_t stream) {
     if (a.nseg > 1) {
         hipError_t e = launch_main<K, MODE, 1>(a, stream, a.nseg - 1);
-        if (e != hipSuccess) return e;
-        const int64_t n = a.B * a.H * kP * kN;
-        seg_combine_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(a);
-        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return launch_main<K, MODE, 0>(a, stream, a.nseg);

@@ -36,8 +36,8 @@ POOL_CASES = [
     (2, 2, 2, 64, 128, 1, 4, BF16, 2, 4, True, [1, 0], 0),       # L < K-1
     (2, 2, 2, 64, 128, 1, 4, BF16, 3, 5, False, [2, 0], 0),      # linear, L < state_len
     (3, 90, 2, 64, 128, 1, 4, BF16, 4, 4, False, [3, 1, 0], 2),  # linear, packed rows
-    # long rows over few heads run as segments (state pass, combine, output pass) that read
-    # and write the pool rows in place
+    # long rows over few heads run as segments (a state pass, then the output pass that
+    # composes each segment's entry state), which read and write the pool rows in place
     (1, 4096, 2, 64, 128, 1, 4, BF16, 3, 4, True, [2], 0),
     (2, 2048, 1, 64, 128, 1, 4, BF16, 3, 4, True, [5, 1], 2),   # row 0: slot out of range
 ]
