@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_mi355x.so")
-SOURCES = ["abi.hip", "bwd.hip", "conv.hip", "init_state.hip", "pool.hip", "recurrent.hip", "ssd.hip", "vdecay.hip"]
+SOURCES = ["abi.hip", "bwd.hip", "conv.hip", "init_state.hip", "pool.hip", "recurrent.hip", "ssd.hip", "vchunk.hip", "vdecay.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code (hipcc's host pass

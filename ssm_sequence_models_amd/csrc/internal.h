@@ -174,6 +174,10 @@ hipError_t launch_recurrent(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream
 // states, 16-byte aligned); launch_recurrent covers the other shapes
 bool vdecay_supported(int64_t P, int64_t N);
 hipError_t launch_vdecay(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream);
+// the chunked (matrix-core) form of the diagonal-transition scan: gate form, bf16, headdim 64,
+// dstate 128, contiguous 16-byte aligned rows, no slot map (launch_vdecay dispatches to it)
+bool vchunk_supported(const RecurrentArgs& a, ssm_dtype_t dtype);
+hipError_t launch_vchunk(const RecurrentArgs& a, hipStream_t stream);
 
 // Chunked (SSD) scan on MFMA for bf16 inputs with headdim 64, dstate 128.
 bool chunked_supported(int64_t P, int64_t N, ssm_dtype_t dtype);

@@ -1,0 +1,578 @@
+// vchunk.hip -- the scan with a diagonal transition (one decay per state dimension), chunked
+// onto the matrix cores: length-generalization reading notes, Sec. 2.1 Eq. (1) with
+// A_t = diag(a_t), and Sec. 2.5, where the transition over a span of tokens is the
+// exponential of a sum of log coefficients.  Per head h, channel p and dimension n:
+//     state[p][n] <- a_t[n] state[p][n] + u_t x_t[p] B_t[n],    y_t[p] = C_t . state[p][:]
+// with log a_t[n] = log_decay[b][t][h][n] and u_t = dt_t[h] (1 without dt).
+//
+// Chunks of 64 tokens.  With G_t[n] the sum of log a over the chunk's tokens 0 .. t
+// (inclusive), the unrolled recurrence of a chunk that starts from state S is
+//     y_t[p] = sum_n C_t[n] e^{G_t[n]} S[p][n]                                   (inter)
+//            + sum_{s<=t} u_s x_s[p] sum_n C_t[n] e^{G_t[n]} B_s[n] e^{-G_s[n]}  (intra)
+//     S'[p][n] = e^{G_63[n]} S[p][n] + sum_s u_s x_s[p] B_s[n] e^{G_63[n] - G_s[n]}
+// so every product over p, n or s is a matrix product:
+//     A[t][s]  = (C o e^G)(B o e^-G)^T          (64 x 64, contraction over n = 128)
+//     Y_intra  = (A o causal mask o u) x        (contraction over s)
+//     Y_inter  = (C o e^G) S^T                   (contraction over n)
+//     S'       = e^{G_63} o S + (B o u o e^{G_63 - G})^T x   (contraction over s)
+// The factors e^{+-G} are referred to the chunk start, so they stay finite only while every
+// |G_t[n]| of the chunk is moderate: the kernel requires |G| <= 40 (natural log; e^40 ~ 2e17)
+// for every token and dimension of a chunk.  A chunk that breaks it (fast decays, NaN or
+// infinite gates) runs token by token instead (the recurrence itself, in the same registers),
+// so the result never depends on the gates' range, only the speed does.  The GLA-like gates
+// of the benchmark (mean log a ~ -0.05) stay within |G| < 16 over a chunk.
+//
+// fp32 operands go to the bf16 matrix cores split hi + lo (|lo| <= 2^-9 |hi|), as in the
+// scalar-decay kernel: x, B and C are exact in bf16; C o e^G, B o e^-G, A o u and the state
+// are split, and the products hi.hi + hi.lo + lo.hi keep the operand error near 2^-17.
+//
+// One block of 512 threads per (row, head), the state S [64 p][128 n] in the MFMA
+// accumulators of waves 0-3 (16 channels each) for the whole row.  Per chunk, in lockstep:
+//   1. all eight waves: the prefix sums G over the 64 tokens (a DPP scan per dimension, lane =
+//      token, wave w takes dimensions 16w .. 16w+15), the exponentials, the operand splits
+//      into LDS, the range check; then the loads of the next chunk are issued into the same
+//      registers, so they arrive under steps 2 and 3;
+//   2. all eight waves: the ten 16 x 16 tiles of A on or below the diagonal, masked (s <= t,
+//      no sequence start between s and t), scaled by u_s, split into LDS;
+//   3. waves 0-3: Y_inter, the row mask (no initial state after a sequence start), Y_intra,
+//      y to memory, then the state's decay and update.
+// seq_idx starts are handled as in the scalar chunked scan: pairs across a start are masked,
+// the initial state reaches only tokens before the chunk's first start, and the end state
+// takes only the tokens from the last start on (its decay factor is 0 then).
+#include "internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kVcQ = 64;   // tokens per chunk
+constexpr int kVcP = 64;   // channels
+constexpr int kVcN = 128;  // state dimensions
+constexpr int kVcThreads = 512;
+constexpr float kVcSpan2 = 57.0f;  // |G| bound in log2 units (40 / ln 2 = 57.7)
+
+typedef __bf16 vbf16x8 __attribute__((ext_vector_type(8)));
+typedef float vf32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t vu32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ vf32x4 vc_mfma(vbf16x8 a, vbf16x8 b, vf32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS layout (bytes).  Row-major tiles of 16-byte pieces, the piece index XORed with a row
+// function so that the 16 lanes of an MFMA operand read (16 rows, one piece each) spread over
+// the bank groups.
+//   CE hi / lo, BE hi / lo: [64 t][128 n] bf16 (256-byte rows, 16 pieces, piece ^ (t & 15))
+//   BW hi / lo (transposed): [128 n][64 s] bf16 (128-byte rows, 8 pieces, piece ^ f(n))
+//   AM hi / lo: [64 t][64 s] bf16 (128-byte rows, piece ^ (t & 7))
+//   XT: [64 p][64 s] bf16 (x transposed, piece ^ (p & 7))
+//   the token-by-token path reuses the first 96 KB as a / B / C [64 t][128 n] fp32
+constexpr int kVcCEh = 0;
+constexpr int kVcCEl = kVcCEh + kVcQ * kVcN * 2;
+constexpr int kVcBEh = kVcCEl + kVcQ * kVcN * 2;
+constexpr int kVcBEl = kVcBEh + kVcQ * kVcN * 2;
+constexpr int kVcBWh = kVcBEl + kVcQ * kVcN * 2;
+constexpr int kVcBWl = kVcBWh + kVcN * kVcQ * 2;
+constexpr int kVcAMh = kVcBWl + kVcN * kVcQ * 2;
+constexpr int kVcAMl = kVcAMh + kVcQ * kVcQ * 2;
+constexpr int kVcXT = kVcAMl + kVcQ * kVcQ * 2;
+constexpr int kVcEend = kVcXT + kVcP * kVcQ * 2;  // [128] fp32: e^{G_63[n]} (0 after a start)
+constexpr int kVcR = kVcEend + kVcN * 4;          // [64] int32: the last start <= t (-1 none)
+constexpr int kVcU = kVcR + kVcQ * 4;             // [64] fp32: u_t (0 past the row's end)
+constexpr int kVcFlag = kVcU + kVcQ * 4;          // [8] int32: per wave, a dimension out of range
+constexpr int kVcLds = kVcFlag + 8 * 4;
+constexpr int kVcFa = 0;                          // token-by-token path: a [t][n] fp32
+constexpr int kVcFb = kVcQ * kVcN * 4;            // B [t][n] fp32
+constexpr int kVcFc = 2 * kVcQ * kVcN * 4;        // C [t][n] fp32
+static_assert(kVcFc + kVcQ * kVcN * 4 <= kVcAMh, "token-by-token arrays alias the operands only");
+static_assert(kVcLds <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ int vc_ce(int t, int q) { return t * 256 + ((q ^ (t & 15)) << 4); }
+__device__ __forceinline__ int vc_bw_swz(int n) { return (n & 3) | (((n >> 3) & 1) << 2); }
+__device__ __forceinline__ int vc_bw(int n, int q) { return n * 128 + ((q ^ vc_bw_swz(n)) << 4); }
+__device__ __forceinline__ int vc_sq(int r, int q) { return r * 128 + ((q ^ (r & 7)) << 4); }
+
+template <class T>
+__device__ __forceinline__ T vc_ld(const uint8_t* base, int off) {
+    return *reinterpret_cast<const T*>(base + off);
+}
+template <class T>
+__device__ __forceinline__ void vc_st(uint8_t* base, int off, const T& v) {
+    *reinterpret_cast<T*>(base + off) = v;
+}
+
+// inclusive prefix over the 64 lanes (DPP row_shr 1/2/4/8, then row_bcast 15 / 31)
+__device__ __forceinline__ float vc_scan(float v) {
+    const int z = __float_as_int(0.0f);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+__device__ __forceinline__ int vc_scan_max(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x111, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x112, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x114, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x118, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x142, 0xa, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+// hi = rne(v), lo = rne(v - hi) for two values, packed as bf16 pairs
+__device__ __forceinline__ void vc_split2(float v0, float v1, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf16x2(v0, v1);
+    const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
+    lo = pack_bf16x2(v0 - h0, v1 - h1);
+}
+__device__ __forceinline__ void vc_split8(const float (&v)[8], vbf16x8& hi, vbf16x8& lo) {
+    vu32x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t he, le;
+        vc_split2(v[2 * e], v[2 * e + 1], he, le);
+        h[e] = he;
+        l[e] = le;
+    }
+    hi = __builtin_bit_cast(vbf16x8, h);
+    lo = __builtin_bit_cast(vbf16x8, l);
+}
+
+// the raw inputs of one chunk, held in registers between their loads and step 1: lane t of
+// wave w holds token t's gates, B and C for dimensions 16w .. 16w+15; thread i one 16-byte
+// piece of x (token i / 8, channels 8 (i % 8) ..)
+struct VcRaw {
+    vf32x4 g[4];
+    vu32x4 bq[2], cq[2];
+    vu32x4 xq;
+    float u;
+    int32_t id, id_prev;
+};
+
+__global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kVcLds];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, li = lane & 15, g4 = lane >> 4;
+    const int64_t h = blockIdx.x, b = blockIdx.y;
+    const int64_t grp = h / (a.H / a.G);
+    const int64_t L = a.T;
+    const int64_t nC = (L + kVcQ - 1) / kVcQ;
+    const uint16_t* xs = static_cast<const uint16_t*>(a.x);
+    const uint16_t* bs = static_cast<const uint16_t*>(a.Bm);
+    const uint16_t* cs = static_cast<const uint16_t*>(a.Cm);
+    uint16_t* ys = static_cast<uint16_t*>(a.y);
+    const int n0 = 16 * wave;  // this wave's dimensions in step 1
+    const int xt = tid >> 3, xp = 8 * (tid & 7);
+
+    VcRaw rw;
+    auto load_chunk = [&](int64_t c) {
+        const int64_t t0 = c * kVcQ;
+        const int64_t t = t0 + lane;
+        const bool live = t < L;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rw.g[q] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) rw.bq[q] = rw.cq[q] = vu32x4{0u, 0u, 0u, 0u};
+        rw.u = 0.0f;
+        rw.id = rw.id_prev = 0;
+        if (live) {
+            const vf32x4* gp = reinterpret_cast<const vf32x4*>(a.log_decay + ((b * L + t) * a.H + h) * kVcN + n0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rw.g[q] = gp[q];
+            const vu32x4* bp = reinterpret_cast<const vu32x4*>(bs + b * a.B_sb + t * a.B_st + grp * kVcN + n0);
+            const vu32x4* cp = reinterpret_cast<const vu32x4*>(cs + b * a.C_sb + t * a.C_st + grp * kVcN + n0);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                rw.bq[q] = bp[q];
+                rw.cq[q] = cp[q];
+            }
+            rw.u = a.dt ? a.dt[(b * L + t) * a.H + h] : 1.0f;
+            if (a.seq_idx) {
+                rw.id = a.seq_idx[b * L + t];
+                rw.id_prev = t > 0 ? a.seq_idx[b * L + t - 1] : rw.id;
+            }
+        }
+        rw.xq = vu32x4{0u, 0u, 0u, 0u};
+        if (t0 + xt < L)
+            rw.xq = __builtin_nontemporal_load(
+                reinterpret_cast<const vu32x4*>(xs + b * a.x_sb + (t0 + xt) * a.x_st + h * kVcP + xp));
+    };
+
+    const bool consumer = wave < 4;
+    const int p_own = 16 * wave + li;
+    const int64_t sbase = ((b * a.H + h) * kVcP + p_own) * kVcN;
+    // per-lane byte offsets of the MFMA operand reads (the rest of each address is a constant):
+    //   CE / BE row 16 I + li, piece 4 m + g4:  I * 4096 + ce_b[m]
+    //   BW^T row 32 (T / 2) + 8 (li / 4) + 4 (T % 2) + li % 4, piece 4 sh + g4:
+    //                                        (32 (T / 2) + 4 (T % 2)) * 128 + bw_b[sh]
+    //   A' row 16 I + li, piece 4 sh + g4:    I * 2048 + am_b[sh]
+    //   XT row p_own, piece 4 sh + g4:         xt_b[sh]
+    int ce_b[4], bw_b[2], am_b[2], xt_b[2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) ce_b[m] = li * 256 + (((4 * m + g4) ^ li) << 4);
+    {
+        const int swz = (li & 3) | (((li >> 2) & 1) << 2);
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+            bw_b[sh] = (8 * (li >> 2) + (li & 3)) * 128 + (((4 * sh + g4) ^ swz) << 4);
+            am_b[sh] = li * 128 + (((4 * sh + g4) ^ (li & 7)) << 4);
+            xt_b[sh] = p_own * 128 + (((4 * sh + g4) ^ (li & 7)) << 4);
+        }
+    }
+    // A's blocks (0, 1) and (2, 3) lie above the diagonal but inside the 16 x 32 operands the
+    // intra products read: zero, hi and lo, written once (step 2 never writes them)
+    {
+        const int blk = tid >> 8, e = tid & 255;  // 2 blocks x 16 rows x 16 columns
+        const int t = (blk ? 32 : 0) + (e >> 4), s = (blk ? 48 : 16) + (e & 15);
+        const int off = vc_sq(t, s >> 3) + 2 * (s & 7);
+        *reinterpret_cast<uint16_t*>(sm + kVcAMh + off) = 0;
+        *reinterpret_cast<uint16_t*>(sm + kVcAMl + off) = 0;
+    }
+
+    // ---- step 1 of chunk c from the registers rw: operands, resets, range flag ----
+    int r_t = -1;  // the last sequence start <= lane's token inside the chunk (-1: none)
+    auto step1 = [&](int64_t c) __attribute__((always_inline)) {
+        const int64_t t0 = c * kVcQ;
+        int rst = -1;
+        if (a.seq_idx && t0 + lane < L && t0 + lane > 0 && rw.id != rw.id_prev) rst = lane;
+        r_t = vc_scan_max(rst);
+        const int r_last = __builtin_amdgcn_readlane(r_t, kVcQ - 1);
+        const float u = rw.u;
+        if (wave == 0) {
+            reinterpret_cast<int32_t*>(sm + kVcR)[lane] = r_t;
+            reinterpret_cast<float*>(sm + kVcU)[lane] = u;
+        }
+        // x transposed into XT[p][s]: eight 2-byte stores per thread
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t v = static_cast<uint16_t>(rw.xq[e >> 1] >> (16 * (e & 1)));
+            *reinterpret_cast<uint16_t*>(sm + kVcXT + vc_sq(xp + e, xt >> 3) + 2 * (xt & 7)) = v;
+        }
+        bool bad = false;
+        // one 8-dimension piece at a time (its operands written before the next starts, which
+        // keeps the live registers down)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint32_t ceh[4], cel[4], beh[4], bel[4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                float ce2[2], be2[2], bw2v[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int jj = 8 * q + j + e;
+                    const float gl = rw.g[jj >> 2][jj & 3] * 1.4426950408889634f;
+                    const float G = vc_scan(gl);
+                    bad |= !(fabsf(G) <= kVcSpan2);
+                    const float Gend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kVcQ - 1));
+                    const float ep = __builtin_amdgcn_exp2f(G), em = __builtin_amdgcn_exp2f(-G);
+                    const uint32_t bw2 = rw.bq[q][(j >> 1) & 3], cw2 = rw.cq[q][(j >> 1) & 3];
+                    const float bf = __uint_as_float(e ? (bw2 & 0xFFFF0000u) : (bw2 << 16));
+                    const float cf = __uint_as_float(e ? (cw2 & 0xFFFF0000u) : (cw2 << 16));
+                    ce2[e] = cf * ep;
+                    be2[e] = bf * em;
+                    const float eend = __builtin_amdgcn_exp2f(Gend);
+                    const float bw = bf * u * (em * eend);
+                    bw2v[e] = lane >= r_last ? bw : 0.0f;
+                    if (lane == 0)
+                        reinterpret_cast<float*>(sm + kVcEend)[n0 + jj] = r_last < 0 ? eend : 0.0f;
+                }
+                vc_split2(ce2[0], ce2[1], ceh[j >> 1], cel[j >> 1]);
+                vc_split2(be2[0], be2[1], beh[j >> 1], bel[j >> 1]);
+                {
+                    // B o u o e^{G_63 - G} of dimensions n, n + 1 into rows of BW^T
+                    const int n = n0 + 8 * q + j;
+                    uint32_t bwh, bwl;
+                    vc_split2(bw2v[0], bw2v[1], bwh, bwl);
+                    const int o0 = vc_bw(n, lane >> 3) + 2 * (lane & 7);
+                    const int o1 = vc_bw(n + 1, lane >> 3) + 2 * (lane & 7);
+                    *reinterpret_cast<uint16_t*>(sm + kVcBWh + o0) = static_cast<uint16_t>(bwh);
+                    *reinterpret_cast<uint16_t*>(sm + kVcBWl + o0) = static_cast<uint16_t>(bwl);
+                    *reinterpret_cast<uint16_t*>(sm + kVcBWh + o1) = static_cast<uint16_t>(bwh >> 16);
+                    *reinterpret_cast<uint16_t*>(sm + kVcBWl + o1) = static_cast<uint16_t>(bwl >> 16);
+                }
+            }
+            const int qq = 2 * wave + q;  // 16-byte piece of the row
+            vc_st(sm, kVcCEh + vc_ce(lane, qq), vu32x4{ceh[0], ceh[1], ceh[2], ceh[3]});
+            vc_st(sm, kVcCEl + vc_ce(lane, qq), vu32x4{cel[0], cel[1], cel[2], cel[3]});
+            vc_st(sm, kVcBEh + vc_ce(lane, qq), vu32x4{beh[0], beh[1], beh[2], beh[3]});
+            vc_st(sm, kVcBEl + vc_ce(lane, qq), vu32x4{bel[0], bel[1], bel[2], bel[3]});
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint64_t anybad = __builtin_amdgcn_ballot_w64(bad);
+        if (lane == 0) reinterpret_cast<int32_t*>(sm + kVcFlag)[wave] = anybad != 0 ? 1 : 0;
+    };
+    auto slow_chunk = [&]() -> bool {
+        const vu32x4 f0 = vc_ld<vu32x4>(sm, kVcFlag), f1 = vc_ld<vu32x4>(sm, kVcFlag + 16);
+        return (f0[0] | f0[1] | f0[2] | f0[3] | f1[0] | f1[1] | f1[2] | f1[3]) != 0;
+    };
+    // the token-by-token chunk's a_t[n] (0 at a sequence start), B and C in fp32 over the
+    // operand area, from the registers rw
+    auto fallback_write = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+            vf32x4 av, bv, cv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int jj = j + e;
+                av[e] = lane == r_t ? 0.0f : __expf(rw.g[jj >> 2][jj & 3]);
+                const uint32_t bw2 = rw.bq[jj >> 3][(jj >> 1) & 3], cw2 = rw.cq[jj >> 3][(jj >> 1) & 3];
+                bv[e] = __uint_as_float((jj & 1) ? (bw2 & 0xFFFF0000u) : (bw2 << 16));
+                cv[e] = __uint_as_float((jj & 1) ? (cw2 & 0xFFFF0000u) : (cw2 << 16));
+            }
+            vc_st(sm, kVcFa + (lane * kVcN + n0 + j) * 4, av);
+            vc_st(sm, kVcFb + (lane * kVcN + n0 + j) * 4, bv);
+            vc_st(sm, kVcFc + (lane * kVcN + n0 + j) * 4, cv);
+        }
+    };
+    // ---- step 2: the tiles of A on or below the diagonal, tile k = wave and wave + 8 in the
+    // order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3) ----
+    auto step2 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int rep = 0; rep < 2; ++rep) {
+            const int k = wave + 8 * rep;
+            if (k < 10) {
+                const int I = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+                const int J = k - (I * (I + 1)) / 2;
+                vbf16x8 ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    ah[m] = vc_ld<vbf16x8>(sm, kVcCEh + I * 4096 + ce_b[m]);
+                    al[m] = vc_ld<vbf16x8>(sm, kVcCEl + I * 4096 + ce_b[m]);
+                    bh[m] = vc_ld<vbf16x8>(sm, kVcBEh + J * 4096 + ce_b[m]);
+                    bl[m] = vc_ld<vbf16x8>(sm, kVcBEl + J * 4096 + ce_b[m]);
+                }
+                // three independent accumulation chains (hi.hi, hi.lo, lo.hi)
+                vf32x4 d0 = vf32x4{0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0, d2 = d0;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    d0 = vc_mfma(ah[m], bh[m], d0);
+                    d1 = vc_mfma(ah[m], bl[m], d1);
+                    d2 = vc_mfma(al[m], bh[m], d2);
+                }
+                const vf32x4 d = d0 + (d1 + d2);
+                // lane holds A[t][s], t = 16 I + 4 g4 + r, s = 16 J + li
+                const int s = 16 * J + li;
+                const float us = reinterpret_cast<const float*>(sm + kVcU)[s];
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * I + 4 * g4 + r;
+                    const int rt = reinterpret_cast<const int32_t*>(sm + kVcR)[t];
+                    v[r] = (s <= t && s >= rt) ? d[r] * us : 0.0f;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r += 2) {
+                    uint32_t vh, vl;
+                    vc_split2(v[r], v[r + 1], vh, vl);
+                    const int t = 16 * I + 4 * g4 + r;
+                    const int o0 = vc_sq(t, s >> 3) + 2 * (s & 7), o1 = vc_sq(t + 1, s >> 3) + 2 * (s & 7);
+                    *reinterpret_cast<uint16_t*>(sm + kVcAMh + o0) = static_cast<uint16_t>(vh);
+                    *reinterpret_cast<uint16_t*>(sm + kVcAMl + o0) = static_cast<uint16_t>(vl);
+                    *reinterpret_cast<uint16_t*>(sm + kVcAMh + o1) = static_cast<uint16_t>(vh >> 16);
+                    *reinterpret_cast<uint16_t*>(sm + kVcAMl + o1) = static_cast<uint16_t>(vl >> 16);
+                }
+            }
+        }
+    };
+
+    load_chunk(0);
+    if (consumer) {
+        // the state slice of consumer wave w: acc[T][r] = S[p][n], p = 16 w + li,
+        // n = 32 (T / 2) + 8 g4 + 4 (T % 2) + r (the output rows of the update's tile T, whose
+        // A operand row li holds dimension 32 (T / 2) + 8 (li / 4) + 4 (T % 2) + li % 4)
+        vf32x4 acc[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            acc[2 * m] = acc[2 * m + 1] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (a.state_in) {
+                acc[2 * m] = *reinterpret_cast<const vf32x4*>(a.state_in + sbase + 32 * m + 8 * g4);
+                acc[2 * m + 1] = *reinterpret_cast<const vf32x4*>(a.state_in + sbase + 32 * m + 8 * g4 + 4);
+            }
+        }
+        for (int64_t c = 0; c < nC; ++c) {
+            const int64_t t0 = c * kVcQ;
+            const int nvalid = static_cast<int>(min<int64_t>(kVcQ, L - t0));
+            step1(c);
+            __syncthreads();
+            if (!slow_chunk()) {
+                if (c + 1 < nC) load_chunk(c + 1);
+                step2();
+                __syncthreads();
+                // ---- step 3 ----
+                vbf16x8 xo[2];
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh) xo[sh] = vc_ld<vbf16x8>(sm, kVcXT + xt_b[sh]);
+                vf32x4 ya[4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) ya[I] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                // Y_inter = (C o e^G) S^T from the state before this chunk: per 32-dimension
+                // slice, the four row blocks' operands first, then hi.hi, hi.lo and lo.hi
+                // products into four independent accumulators
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    vbf16x8 ch[4], cl[4];
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        ch[I] = vc_ld<vbf16x8>(sm, kVcCEh + I * 4096 + ce_b[m]);
+                        cl[I] = vc_ld<vbf16x8>(sm, kVcCEl + I * 4096 + ce_b[m]);
+                    }
+                    float hv[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hv[e] = acc[2 * m][e];
+                        hv[4 + e] = acc[2 * m + 1][e];
+                    }
+                    vbf16x8 hh, hl;
+                    vc_split8(hv, hh, hl);
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) ya[I] = vc_mfma(hh, ch[I], ya[I]);
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) ya[I] = vc_mfma(hh, cl[I], ya[I]);
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) ya[I] = vc_mfma(hl, ch[I], ya[I]);
+                }
+                // the initial state reaches only the tokens before the chunk's first start
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int rt = reinterpret_cast<const int32_t*>(sm + kVcR)[16 * I + li];
+                    if (rt >= 0) ya[I] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+                // Y_intra = A' x over the tiles with 32 sh <= 16 I + 15
+                {
+                    vbf16x8 mh[6], ml[6];
+#pragma unroll
+                    for (int u6 = 0; u6 < 6; ++u6) {
+                        const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
+                        mh[u6] = vc_ld<vbf16x8>(sm, kVcAMh + I * 2048 + am_b[sh]);
+                        ml[u6] = vc_ld<vbf16x8>(sm, kVcAMl + I * 2048 + am_b[sh]);
+                    }
+#pragma unroll
+                    for (int u6 = 0; u6 < 6; ++u6) {
+                        const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
+                        ya[I] = vc_mfma(xo[sh], mh[u6], ya[I]);
+                    }
+#pragma unroll
+                    for (int u6 = 0; u6 < 6; ++u6) {
+                        const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
+                        ya[I] = vc_mfma(xo[sh], ml[u6], ya[I]);
+                    }
+                }
+                // y[t][p], p = 16 wave + 4 g4 + r: 8 bytes per lane and token
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int t = 16 * I + li;
+                    if (t < nvalid) {
+                        uint2 pk;
+                        pk.x = pack_bf16x2(ya[I][0], ya[I][1]);
+                        pk.y = pack_bf16x2(ya[I][2], ya[I][3]);
+                        *reinterpret_cast<uint2*>(ys + (b * L + t0 + t) * a.H * kVcP + h * kVcP + 16 * wave + 4 * g4) = pk;
+                    }
+                }
+                // S <- e^{G_63} o S + BW^T x, per half of the chunk: the eight tiles' operands
+                // first, then the hi products, then the lo products
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const vf32x4 e0 = vc_ld<vf32x4>(sm, kVcEend + (32 * m + 8 * g4) * 4);
+                    const vf32x4 e1 = vc_ld<vf32x4>(sm, kVcEend + (32 * m + 8 * g4 + 4) * 4);
+                    acc[2 * m] *= e0;
+                    acc[2 * m + 1] *= e1;
+                }
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh) {
+                    vbf16x8 bh[8], bl[8];
+#pragma unroll
+                    for (int T = 0; T < 8; ++T) {
+                        const int tb = (32 * (T >> 1) + 4 * (T & 1)) * 128;
+                        bh[T] = vc_ld<vbf16x8>(sm, kVcBWh + tb + bw_b[sh]);
+                        bl[T] = vc_ld<vbf16x8>(sm, kVcBWl + tb + bw_b[sh]);
+                    }
+#pragma unroll
+                    for (int T = 0; T < 8; ++T) acc[T] = vc_mfma(bh[T], xo[sh], acc[T]);
+#pragma unroll
+                    for (int T = 0; T < 8; ++T) acc[T] = vc_mfma(bl[T], xo[sh], acc[T]);
+                }
+                __syncthreads();
+            } else {
+                fallback_write();
+                if (c + 1 < nC) load_chunk(c + 1);
+                __syncthreads();
+                for (int t = 0; t < nvalid; ++t) {
+                    const float ut = reinterpret_cast<const float*>(sm + kVcU)[t];
+                    const float xv = bf16_to_f32(vc_ld<uint16_t>(sm, kVcXT + vc_sq(p_own, t >> 3) + 2 * (t & 7)));
+                    const float ux = ut * xv;
+                    float part = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int n = 32 * m + 8 * g4 + 4 * hf;
+                            const vf32x4 av = vc_ld<vf32x4>(sm, kVcFa + (t * kVcN + n) * 4);
+                            const vf32x4 bv = vc_ld<vf32x4>(sm, kVcFb + (t * kVcN + n) * 4);
+                            const vf32x4 cv = vc_ld<vf32x4>(sm, kVcFc + (t * kVcN + n) * 4);
+                            vf32x4& sv = acc[2 * m + hf];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                sv[e] = av[e] * sv[e] + ux * bv[e];
+                                part += cv[e] * sv[e];
+                            }
+                        }
+                    }
+                    part += __shfl_xor(part, 16);
+                    part += __shfl_xor(part, 32);
+                    if (g4 == 0)
+                        ys[(b * L + t0 + t) * a.H * kVcP + h * kVcP + p_own] = f32_to_bf16(part);
+                }
+                __syncthreads();
+            }
+        }
+        if (a.state_out) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                *reinterpret_cast<vf32x4*>(a.state_out + sbase + 32 * m + 8 * g4) = acc[2 * m];
+                *reinterpret_cast<vf32x4*>(a.state_out + sbase + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
+            }
+        }
+    } else {
+        // waves 4-7: steps 1 and 2 (and the token-by-token chunks' arrays), the same barriers
+        for (int64_t c = 0; c < nC; ++c) {
+            step1(c);
+            __syncthreads();
+            if (!slow_chunk()) {
+                if (c + 1 < nC) load_chunk(c + 1);
+                step2();
+                __syncthreads();
+                __syncthreads();
+            } else {
+                fallback_write();
+                if (c + 1 < nC) load_chunk(c + 1);
+                __syncthreads();
+                __syncthreads();
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// the gate form with bf16 rows of 64 channels and 128 dimensions, contiguous and 16-byte
+// aligned, the rows' own states (no slot map)
+bool vchunk_supported(const RecurrentArgs& a, ssm_dtype_t dtype) {
+    const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.Bm) |
+                         reinterpret_cast<uintptr_t>(a.Cm) | reinterpret_cast<uintptr_t>(a.log_decay) |
+                         reinterpret_cast<uintptr_t>(a.state_in) | reinterpret_cast<uintptr_t>(a.state_out) |
+                         reinterpret_cast<uintptr_t>(a.y);
+    return dtype == SSM_BF16 && a.log_decay != nullptr && a.A_vec == nullptr && a.indices == nullptr &&
+           a.P == kVcP && a.N == kVcN && (al & 15) == 0 && a.x_sc == 1 && a.B_sc == 1 &&
+           a.C_sc == 1 && a.x_st % 8 == 0 && a.x_sb % 8 == 0 && a.B_st % 8 == 0 &&
+           a.C_st % 8 == 0 && a.B_sb % 8 == 0 && a.C_sb % 8 == 0 && a.x_st == a.H * kVcP;
+}
+
+hipError_t launch_vchunk(const RecurrentArgs& a, hipStream_t stream) {
+    if (a.B == 0 || a.T == 0) return hipSuccess;
+    vchunk_kernel<<<dim3(static_cast<unsigned>(a.H), static_cast<unsigned>(a.B)), kVcThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

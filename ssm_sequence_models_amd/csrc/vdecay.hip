@@ -363,6 +363,7 @@ bool vdecay_supported(int64_t P, int64_t N) { return P == kVdP && (N == 64 || N 
 // else the general token-sequential kernel's vector mode
 hipError_t launch_vdecay(const RecurrentArgs& a, ssm_dtype_t dtype, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
+    if (vchunk_supported(a, dtype)) return launch_vchunk(a, stream);
     const uintptr_t al = reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.Bm) |
                          reinterpret_cast<uintptr_t>(a.Cm) | reinterpret_cast<uintptr_t>(a.log_decay) |
                          reinterpret_cast<uintptr_t>(a.A_vec);

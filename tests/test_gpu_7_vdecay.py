@@ -104,3 +104,51 @@ def test_scan_fwd_vector_decay_full_size_sampled_heads():
                                       out_dtype="bf16", state_dtype="f32")
     assert_close(y[:, :, heads], ry, "y (sampled heads)")
     assert_close(fin[:, heads], rfin, "final state (sampled heads)")
+
+
+# The chunked (matrix-core) kernel takes the gate form with bf16, 64 channels and 128
+# dimensions; a chunk whose summed log decay leaves its range runs token by token.  These rows
+# mix such chunks with ordinary ones: gates scaled up over a stretch of the row (fast decays,
+# one token's gate alone below the bound), with and without packed sequences and dt.
+FALLBACK_CASES = [
+    # B, L, H, scale, stretch (first, last token), dt, segments
+    (2, 333, 3, 60.0, (64, 200), True, 0),
+    (1, 256, 2, 200.0, (0, 256), False, 3),
+    (2, 190, 2, 1000.0, (100, 101), True, 2),
+]
+
+
+@pytest.mark.parametrize("B,L,H,scale,stretch,with_dt,segs", FALLBACK_CASES)
+def test_scan_fwd_vector_decay_fast_decay_chunks(B, L, H, scale, stretch, with_dt, segs):
+    import ssm_sequence_models_amd as ssm
+    x, Bm, Cm, dt, gate, _, h0, seq = _inputs(B, L, H, 64, 128, 1, BF16, 7 + L, "gate", with_dt,
+                                              True, segs)
+    gate = gate.clone()
+    gate[:, stretch[0]:stretch[1]] *= scale
+    y, fin = ssm.scan_fwd_vector_decay(dev(x), dev(Bm), dev(Cm), log_decay=dev(gate), dt=dev(dt),
+                                       initial_state=dev(h0), seq_idx=dev(seq))
+    torch.cuda.synchronize()
+    ry, rfin = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=gate, init_state=h0, seq_idx=seq,
+                                      out_dtype="bf16", state_dtype="f32")
+    assert_close(y, ry, "y")
+    assert_close(fin, rfin, "final state")
+
+
+def test_scan_fwd_vector_decay_nan_gate_propagates():
+    """A NaN gate at token t of one dimension reaches that dimension's state from t on, as in
+    the recurrence itself; the other rows and heads stay finite and match the oracle."""
+    import ssm_sequence_models_amd as ssm
+    x, Bm, Cm, dt, gate, _, h0, _ = _inputs(2, 150, 2, 64, 128, 1, BF16, 19, "gate", True, True, 0)
+    gate = gate.clone()
+    gate[0, 70, 1, 5] = float("nan")
+    y, fin = ssm.scan_fwd_vector_decay(dev(x), dev(Bm), dev(Cm), log_decay=dev(gate), dt=dev(dt),
+                                       initial_state=dev(h0))
+    torch.cuda.synchronize()
+    ry, rfin = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=gate, init_state=h0,
+                                      out_dtype="bf16", state_dtype="f32")
+    yc, fc = y.cpu().float(), fin.cpu()
+    ry_t, rf_t = torch.from_numpy(np.asarray(ry)).float(), torch.from_numpy(np.asarray(rfin)).float()
+    assert torch.equal(torch.isnan(yc), torch.isnan(ry_t)), "NaN pattern of y"
+    assert torch.equal(torch.isnan(fc), torch.isnan(rf_t)), "NaN pattern of the final state"
+    ok = ~torch.isnan(ry_t)
+    assert_close(torch.where(ok, yc, torch.zeros_like(yc)), torch.where(ok, ry_t, torch.zeros_like(ry_t)).double().numpy(), "finite y")
