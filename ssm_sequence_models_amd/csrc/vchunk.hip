@@ -79,7 +79,8 @@ constexpr int kVcEend = kVcXT + kVcP * kVcQ * 2;  // [128] fp32: e^{G_63[n]} (0 
 constexpr int kVcR = kVcEend + kVcN * 4;          // [64] int32: the last start <= t (-1 none)
 constexpr int kVcU = kVcR + kVcQ * 4;             // [64] fp32: u_t (0 past the row's end)
 constexpr int kVcFlag = kVcU + kVcQ * 4;          // [8] int32: per wave, a dimension out of range
-constexpr int kVcLds = kVcFlag + 8 * 4;
+constexpr int kVcS = kVcFlag + 8 * 4;              // [64 p][128 n] fp32: the state between chunks
+constexpr int kVcLds = kVcS + kVcP * kVcN * 4;
 constexpr int kVcFa = 0;                          // token-by-token path: a [t][n] fp32
 constexpr int kVcFb = kVcQ * kVcN * 4;            // B [t][n] fp32
 constexpr int kVcFc = 2 * kVcQ * kVcN * 4;        // C [t][n] fp32
@@ -90,6 +91,8 @@ __device__ __forceinline__ int vc_ce(int t, int q) { return t * 256 + ((q ^ (t &
 __device__ __forceinline__ int vc_bw_swz(int n) { return (n & 3) | (((n >> 3) & 1) << 2); }
 __device__ __forceinline__ int vc_bw(int n, int q) { return n * 128 + ((q ^ vc_bw_swz(n)) << 4); }
 __device__ __forceinline__ int vc_sq(int r, int q) { return r * 128 + ((q ^ (r & 7)) << 4); }
+// state row p, 16-byte piece q (of 32): the 16 rows an MFMA lane group reads spread over banks
+__device__ __forceinline__ int vc_st_off(int p, int q) { return kVcS + p * 512 + ((q ^ (p & 15)) << 4); }
 
 template <class T>
 __device__ __forceinline__ T vc_ld(const uint8_t* base, int off) {
@@ -151,6 +154,41 @@ struct VcRaw {
     int32_t id, id_prev;
 };
 
+// The chunk token by token (a chunk whose summed log decay leaves the range of the chunked
+// form): consumer lane (li, g4) of wave w holds S[p][n] for p = 16 w + li and the 32
+// dimensions n = 32 m + 8 g4 + 4 hf + e of st[2 m + hf][e]; a_t, B_t, C_t come from the fp32
+// arrays in LDS, u_t and x_t[p] from the chunk's u and XT slots.  Out of line: this rare path
+// keeps its registers away from the chunked loop's.
+__device__ __noinline__ void vc_token_chunk(const uint8_t* sm, vf32x4* st, uint16_t* yrow,
+                                            int64_t ystride, int p_own, int g4, int nvalid) {
+    for (int t = 0; t < nvalid; ++t) {
+        const float ut = reinterpret_cast<const float*>(sm + kVcU)[t];
+        const float xv = bf16_to_f32(vc_ld<uint16_t>(sm, kVcXT + vc_sq(p_own, t >> 3) + 2 * (t & 7)));
+        const float ux = ut * xv;
+        float part = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int n = 32 * m + 8 * g4 + 4 * hf;
+                const vf32x4 av = vc_ld<vf32x4>(sm, kVcFa + (t * kVcN + n) * 4);
+                const vf32x4 bv = vc_ld<vf32x4>(sm, kVcFb + (t * kVcN + n) * 4);
+                const vf32x4 cv = vc_ld<vf32x4>(sm, kVcFc + (t * kVcN + n) * 4);
+                vf32x4 sv = st[2 * m + hf];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sv[e] = av[e] * sv[e] + ux * bv[e];
+                    part += cv[e] * sv[e];
+                }
+                st[2 * m + hf] = sv;
+            }
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (g4 == 0) yrow[t * ystride + p_own] = f32_to_bf16(part);
+    }
+}
+
 __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t sm[kVcLds];
     const int tid = threadIdx.x;
@@ -166,38 +204,53 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
     const int n0 = 16 * wave;  // this wave's dimensions in step 1
     const int xt = tid >> 3, xp = 8 * (tid & 7);
 
+    // Register loads of chunk c through buffer resources whose base is the chunk's first token
+    // (per-lane offsets are 32-bit and loop-invariant; reads past the row's end return 0, the
+    // ragged last chunk's padding)
+    const uint32_t vo_g = static_cast<uint32_t>(lane * a.H * kVcN * 4 + n0 * 4);
+    const uint32_t vo_b = static_cast<uint32_t>(lane * a.B_st * 2 + (grp * kVcN + n0) * 2);
+    const uint32_t vo_c = static_cast<uint32_t>(lane * a.C_st * 2 + (grp * kVcN + n0) * 2);
+    const uint32_t vo_u = static_cast<uint32_t>(lane * a.H * 4);
+    const uint32_t vo_x = static_cast<uint32_t>(xt * a.x_st * 2 + (h * kVcP + xp) * 2);
     VcRaw rw;
-    auto load_chunk = [&](int64_t c) {
+    auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
         const int64_t t0 = c * kVcQ;
-        const int64_t t = t0 + lane;
-        const bool live = t < L;
+        const int64_t nv = min<int64_t>(kVcQ, L - t0);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.log_decay + ((b * L + t0) * a.H + h) * kVcN), 0,
+            static_cast<int>(nv * a.H * kVcN * 4), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(bs + b * a.B_sb + t0 * a.B_st), 0, static_cast<int>(nv * a.B_st * 2), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(cs + b * a.C_sb + t0 * a.C_st), 0, static_cast<int>(nv * a.C_st * 2), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(xs + b * a.x_sb + t0 * a.x_st), 0, static_cast<int>(nv * a.x_st * 2), 0x00020000);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rw.g[q] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < 4; ++q)
+            rw.g[q] = __builtin_bit_cast(vf32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, vo_g + 16 * q, 0, 0));
 #pragma unroll
-        for (int q = 0; q < 2; ++q) rw.bq[q] = rw.cq[q] = vu32x4{0u, 0u, 0u, 0u};
-        rw.u = 0.0f;
-        rw.id = rw.id_prev = 0;
-        if (live) {
-            const vf32x4* gp = reinterpret_cast<const vf32x4*>(a.log_decay + ((b * L + t) * a.H + h) * kVcN + n0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) rw.g[q] = gp[q];
-            const vu32x4* bp = reinterpret_cast<const vu32x4*>(bs + b * a.B_sb + t * a.B_st + grp * kVcN + n0);
-            const vu32x4* cp = reinterpret_cast<const vu32x4*>(cs + b * a.C_sb + t * a.C_st + grp * kVcN + n0);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                rw.bq[q] = bp[q];
-                rw.cq[q] = cp[q];
-            }
-            rw.u = a.dt ? a.dt[(b * L + t) * a.H + h] : 1.0f;
-            if (a.seq_idx) {
-                rw.id = a.seq_idx[b * L + t];
-                rw.id_prev = t > 0 ? a.seq_idx[b * L + t - 1] : rw.id;
-            }
+        for (int q = 0; q < 2; ++q) {
+            rw.bq[q] = __builtin_bit_cast(vu32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, vo_b + 16 * q, 0, 0));
+            rw.cq[q] = __builtin_bit_cast(vu32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c + 16 * q, 0, 0));
         }
-        rw.xq = vu32x4{0u, 0u, 0u, 0u};
-        if (t0 + xt < L)
-            rw.xq = __builtin_nontemporal_load(
-                reinterpret_cast<const vu32x4*>(xs + b * a.x_sb + (t0 + xt) * a.x_st + h * kVcP + xp));
+        rw.xq = __builtin_bit_cast(vu32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, vo_x, 0, 2));  // nt
+        rw.u = 0.0f;
+        if (lane < nv) rw.u = 1.0f;
+        if (a.dt) {
+            const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.dt + (b * L + t0) * a.H + h), 0, static_cast<int>(nv * a.H * 4), 0x00020000);
+            rw.u = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ru, vo_u, 0, 0));
+        }
+        rw.id = rw.id_prev = 0;
+        if (a.seq_idx) {
+            // the token's id and the previous token's, both plain loads from the row (token -1
+            // is out of the resource's range and reads 0; no start is taken at token 0)
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<int32_t*>(a.seq_idx + b * L), 0, static_cast<int>(L * 4), 0x00020000);
+            const uint32_t o = static_cast<uint32_t>((t0 + lane) * 4);
+            rw.id = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0));
+            rw.id_prev = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, o - 4u, 0, 0));
+        }
     };
 
     const bool consumer = wave < 4;
@@ -335,21 +388,17 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
             if (k < 10) {
                 const int I = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
                 const int J = k - (I * (I + 1)) / 2;
-                vbf16x8 ah[4], al[4], bh[4], bl[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    ah[m] = vc_ld<vbf16x8>(sm, kVcCEh + I * 4096 + ce_b[m]);
-                    al[m] = vc_ld<vbf16x8>(sm, kVcCEl + I * 4096 + ce_b[m]);
-                    bh[m] = vc_ld<vbf16x8>(sm, kVcBEh + J * 4096 + ce_b[m]);
-                    bl[m] = vc_ld<vbf16x8>(sm, kVcBEl + J * 4096 + ce_b[m]);
-                }
                 // three independent accumulation chains (hi.hi, hi.lo, lo.hi)
                 vf32x4 d0 = vf32x4{0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0, d2 = d0;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    d0 = vc_mfma(ah[m], bh[m], d0);
-                    d1 = vc_mfma(ah[m], bl[m], d1);
-                    d2 = vc_mfma(al[m], bh[m], d2);
+                    const vbf16x8 ah = vc_ld<vbf16x8>(sm, kVcCEh + I * 4096 + ce_b[m]);
+                    const vbf16x8 al = vc_ld<vbf16x8>(sm, kVcCEl + I * 4096 + ce_b[m]);
+                    const vbf16x8 bh = vc_ld<vbf16x8>(sm, kVcBEh + J * 4096 + ce_b[m]);
+                    const vbf16x8 bl = vc_ld<vbf16x8>(sm, kVcBEl + J * 4096 + ce_b[m]);
+                    d0 = vc_mfma(ah, bh, d0);
+                    d1 = vc_mfma(ah, bl, d1);
+                    d2 = vc_mfma(al, bh, d2);
                 }
                 const vf32x4 d = d0 + (d1 + d2);
                 // lane holds A[t][s], t = 16 I + 4 g4 + r, s = 16 J + li
@@ -377,30 +426,39 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
         }
     };
 
-    load_chunk(0);
+    // the state S lives in LDS between chunks (registers only while step 3 uses it): consumer
+    // lane (li, g4) of wave w owns S[p][n], p = 16 w + li, n = 32 m + 8 g4 + e (e < 8), the
+    // pieces 8 m + 2 g4 and 8 m + 2 g4 + 1 of row p
     if (consumer) {
-        // the state slice of consumer wave w: acc[T][r] = S[p][n], p = 16 w + li,
-        // n = 32 (T / 2) + 8 g4 + 4 (T % 2) + r (the output rows of the update's tile T, whose
-        // A operand row li holds dimension 32 (T / 2) + 8 (li / 4) + 4 (T % 2) + li % 4)
-        vf32x4 acc[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            acc[2 * m] = acc[2 * m + 1] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (a.state_in) {
-                acc[2 * m] = *reinterpret_cast<const vf32x4*>(a.state_in + sbase + 32 * m + 8 * g4);
-                acc[2 * m + 1] = *reinterpret_cast<const vf32x4*>(a.state_in + sbase + 32 * m + 8 * g4 + 4);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                vf32x4 v = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (a.state_in) v = *reinterpret_cast<const vf32x4*>(a.state_in + sbase + 32 * m + 8 * g4 + 4 * hf);
+                vc_st(sm, vc_st_off(p_own, 8 * m + 2 * g4 + hf), v);
             }
         }
-        for (int64_t c = 0; c < nC; ++c) {
-            const int64_t t0 = c * kVcQ;
-            const int nvalid = static_cast<int>(min<int64_t>(kVcQ, L - t0));
-            step1(c);
+    }
+    load_chunk(0);
+    for (int64_t c = 0; c < nC; ++c) {
+        const int64_t t0 = c * kVcQ;
+        const int nvalid = static_cast<int>(min<int64_t>(kVcQ, L - t0));
+        step1(c);
+        __syncthreads();
+        const bool slow = slow_chunk();
+        if (slow) fallback_write();  // from this chunk's registers, before the next chunk's loads
+        if (c + 1 < nC) load_chunk(c + 1);
+        if (!slow) {
+            step2();
             __syncthreads();
-            if (!slow_chunk()) {
-                if (c + 1 < nC) load_chunk(c + 1);
-                step2();
-                __syncthreads();
-                // ---- step 3 ----
+            if (consumer) {
+                // ---- step 3: acc[T][r] = S[p][n], n = 32 (T / 2) + 8 g4 + 4 (T % 2) + r (the
+                // output rows of the update's tile T, whose A operand row li holds dimension
+                // 32 (T / 2) + 8 (li / 4) + 4 (T % 2) + li % 4) ----
+                vf32x4 acc[8];
+#pragma unroll
+                for (int T = 0; T < 8; ++T) acc[T] = vc_ld<vf32x4>(sm, vc_st_off(p_own, 8 * (T >> 1) + 2 * g4 + (T & 1)));
                 vbf16x8 xo[2];
 #pragma unroll
                 for (int sh = 0; sh < 2; ++sh) xo[sh] = vc_ld<vbf16x8>(sm, kVcXT + xt_b[sh]);
@@ -439,24 +497,21 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
                     const int rt = reinterpret_cast<const int32_t*>(sm + kVcR)[16 * I + li];
                     if (rt >= 0) ya[I] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 }
-                // Y_intra = A' x over the tiles with 32 sh <= 16 I + 15
+                // Y_intra = A' x over the tiles with 32 sh <= 16 I + 15 (hi tiles, then lo)
                 {
-                    vbf16x8 mh[6], ml[6];
+                    vbf16x8 mt[6];
 #pragma unroll
-                    for (int u6 = 0; u6 < 6; ++u6) {
-                        const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
-                        mh[u6] = vc_ld<vbf16x8>(sm, kVcAMh + I * 2048 + am_b[sh]);
-                        ml[u6] = vc_ld<vbf16x8>(sm, kVcAMl + I * 2048 + am_b[sh]);
-                    }
+                    for (int hl = 0; hl < 2; ++hl) {
 #pragma unroll
-                    for (int u6 = 0; u6 < 6; ++u6) {
-                        const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
-                        ya[I] = vc_mfma(xo[sh], mh[u6], ya[I]);
-                    }
+                        for (int u6 = 0; u6 < 6; ++u6) {
+                            const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
+                            mt[u6] = vc_ld<vbf16x8>(sm, (hl ? kVcAMl : kVcAMh) + I * 2048 + am_b[sh]);
+                        }
 #pragma unroll
-                    for (int u6 = 0; u6 < 6; ++u6) {
-                        const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
-                        ya[I] = vc_mfma(xo[sh], ml[u6], ya[I]);
+                        for (int u6 = 0; u6 < 6; ++u6) {
+                            const int I = u6 < 2 ? u6 : (u6 < 4 ? 2 : 3), sh = u6 < 2 ? 0 : (u6 & 1);
+                            ya[I] = vc_mfma(xo[sh], mt[u6], ya[I]);
+                        }
                     }
                 }
                 // y[t][p], p = 16 wave + 4 g4 + r: 8 bytes per lane and token
@@ -470,8 +525,8 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
                         *reinterpret_cast<uint2*>(ys + (b * L + t0 + t) * a.H * kVcP + h * kVcP + 16 * wave + 4 * g4) = pk;
                     }
                 }
-                // S <- e^{G_63} o S + BW^T x, per half of the chunk: the eight tiles' operands
-                // first, then the hi products, then the lo products
+                // S <- e^{G_63} o S + BW^T x, per half of the chunk and half of the tiles: the
+                // operands first, then the hi products, then the lo products
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const vf32x4 e0 = vc_ld<vf32x4>(sm, kVcEend + (32 * m + 8 * g4) * 4);
@@ -481,76 +536,46 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
                 }
 #pragma unroll
                 for (int sh = 0; sh < 2; ++sh) {
-                    vbf16x8 bh[8], bl[8];
 #pragma unroll
-                    for (int T = 0; T < 8; ++T) {
-                        const int tb = (32 * (T >> 1) + 4 * (T & 1)) * 128;
-                        bh[T] = vc_ld<vbf16x8>(sm, kVcBWh + tb + bw_b[sh]);
-                        bl[T] = vc_ld<vbf16x8>(sm, kVcBWl + tb + bw_b[sh]);
-                    }
+                    for (int th = 0; th < 2; ++th) {
+                        vbf16x8 bh[4], bl[4];
 #pragma unroll
-                    for (int T = 0; T < 8; ++T) acc[T] = vc_mfma(bh[T], xo[sh], acc[T]);
-#pragma unroll
-                    for (int T = 0; T < 8; ++T) acc[T] = vc_mfma(bl[T], xo[sh], acc[T]);
-                }
-                __syncthreads();
-            } else {
-                fallback_write();
-                if (c + 1 < nC) load_chunk(c + 1);
-                __syncthreads();
-                for (int t = 0; t < nvalid; ++t) {
-                    const float ut = reinterpret_cast<const float*>(sm + kVcU)[t];
-                    const float xv = bf16_to_f32(vc_ld<uint16_t>(sm, kVcXT + vc_sq(p_own, t >> 3) + 2 * (t & 7)));
-                    const float ux = ut * xv;
-                    float part = 0.0f;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) {
-                            const int n = 32 * m + 8 * g4 + 4 * hf;
-                            const vf32x4 av = vc_ld<vf32x4>(sm, kVcFa + (t * kVcN + n) * 4);
-                            const vf32x4 bv = vc_ld<vf32x4>(sm, kVcFb + (t * kVcN + n) * 4);
-                            const vf32x4 cv = vc_ld<vf32x4>(sm, kVcFc + (t * kVcN + n) * 4);
-                            vf32x4& sv = acc[2 * m + hf];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                sv[e] = av[e] * sv[e] + ux * bv[e];
-                                part += cv[e] * sv[e];
-                            }
+                        for (int k4 = 0; k4 < 4; ++k4) {
+                            const int T = 4 * th + k4;
+                            const int tb = (32 * (T >> 1) + 4 * (T & 1)) * 128;
+                            bh[k4] = vc_ld<vbf16x8>(sm, kVcBWh + tb + bw_b[sh]);
+                            bl[k4] = vc_ld<vbf16x8>(sm, kVcBWl + tb + bw_b[sh]);
                         }
-                    }
-                    part += __shfl_xor(part, 16);
-                    part += __shfl_xor(part, 32);
-                    if (g4 == 0)
-                        ys[(b * L + t0 + t) * a.H * kVcP + h * kVcP + p_own] = f32_to_bf16(part);
-                }
-                __syncthreads();
-            }
-        }
-        if (a.state_out) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                *reinterpret_cast<vf32x4*>(a.state_out + sbase + 32 * m + 8 * g4) = acc[2 * m];
-                *reinterpret_cast<vf32x4*>(a.state_out + sbase + 32 * m + 8 * g4 + 4) = acc[2 * m + 1];
+                        for (int k4 = 0; k4 < 4; ++k4) acc[4 * th + k4] = vc_mfma(bh[k4], xo[sh], acc[4 * th + k4]);
+#pragma unroll
+                        for (int k4 = 0; k4 < 4; ++k4) acc[4 * th + k4] = vc_mfma(bl[k4], xo[sh], acc[4 * th + k4]);
+                    }
+                }
+#pragma unroll
+                for (int T = 0; T < 8; ++T) vc_st(sm, vc_st_off(p_own, 8 * (T >> 1) + 2 * g4 + (T & 1)), acc[T]);
             }
-        }
-    } else {
-        // waves 4-7: steps 1 and 2 (and the token-by-token chunks' arrays), the same barriers
-        for (int64_t c = 0; c < nC; ++c) {
-            step1(c);
             __syncthreads();
-            if (!slow_chunk()) {
-                if (c + 1 < nC) load_chunk(c + 1);
-                step2();
-                __syncthreads();
-                __syncthreads();
-            } else {
-                fallback_write();
-                if (c + 1 < nC) load_chunk(c + 1);
-                __syncthreads();
-                __syncthreads();
+        } else {
+            __syncthreads();
+            if (consumer) {
+                vf32x4 st[8];
+#pragma unroll
+                for (int T = 0; T < 8; ++T) st[T] = vc_ld<vf32x4>(sm, vc_st_off(p_own, 8 * (T >> 1) + 2 * g4 + (T & 1)));
+                vc_token_chunk(sm, st, ys + (b * L + t0) * a.H * kVcP + h * kVcP, a.H * kVcP, p_own, g4, nvalid);
+#pragma unroll
+                for (int T = 0; T < 8; ++T) vc_st(sm, vc_st_off(p_own, 8 * (T >> 1) + 2 * g4 + (T & 1)), st[T]);
             }
+            __syncthreads();
         }
+    }
+    if (consumer && a.state_out) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                *reinterpret_cast<vf32x4*>(a.state_out + sbase + 32 * m + 8 * g4 + 4 * hf) =
+                    vc_ld<vf32x4>(sm, vc_st_off(p_own, 8 * m + 2 * g4 + hf));
     }
 }
 
