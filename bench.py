@@ -29,7 +29,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (FMA counted as two flops)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 # MFMAs the main kernel issues per (batch row, head, 64-token chunk): 4 consumer waves x (12
 # intra-chunk + 32 initial-state + 32 state-update), each a 16x16x32 bf16 product
@@ -313,17 +312,22 @@ def other_ops(torch, ssm, workloads, copy_GBs, only=None):
                                                             y=yv), 5)
     nb = (s.B * s.L * (2 * s.H * s.P * 2 + s.H * s.N * 4 + 2 * s.N * 2 + s.H * 4)
           + 2 * s.B * s.H * s.P * s.N * 4)
-    # the recurrence is bound by fp32 vector arithmetic, not HBM: per (token, channel, state
-    # dimension) one decay multiply and two fused multiply-adds (input, read-out), 5 flops;
-    # the issue floor counts those 3 instructions at 64 lanes per CU per clock (no packed fp32)
+    # the gate form runs chunked on the matrix cores (64-token chunks): per (row, head, chunk)
+    # 10 tiles x 12 MFMAs for the intra-chunk matrix and 4 waves x 92 for the inter / intra /
+    # state products, 16x16x32 bf16 (16,384 flops each, hi / lo splits included).  Context: the
+    # token-sequential form's issue floor (3 fp32 instructions per token, channel and
+    # dimension at 64 lanes per CU per clock) is what this form is not bound by.
+    n_chunk = (s.L + 63) // 64
+    mfma_flops = s.B * s.H * n_chunk * (10 * 12 + 4 * 92) * 16384
     elems = s.B * s.L * s.H * s.P * s.N
     floor_ms = 3 * elems / (256 * 64 * 2.4e9) * 1e3
     rep("scan_fwd_vector_decay", f"1.3B-like B{s.B} L{s.L} H{s.H}x{s.P} N{s.N} bf16, per-dimension "
-        "log gates [B, L, H, N] fp32, dt, initial / final state", ms, s.B * s.L, nb,
-        {"bound": "alu", "flops": 5 * elems, "achieved_TFLOPs": 5 * elems / (ms * 1e-3) / 1e12,
-         "peak_TFLOPs": FP32_VECTOR_PEAK_TFLOPS,
-         "frac_alu": 5 * elems / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-         "issue_floor_ms": floor_ms, "frac_of_issue_floor": floor_ms / ms} if ms is not None else None)
+        "log gates [B, L, H, N] fp32, dt, initial / final state (chunked on the matrix cores)", ms,
+        s.B * s.L, nb,
+        {"bound": "hbm", "mfma_issued_flops": mfma_flops,
+         "mfma_achieved_TFLOPs": mfma_flops / (ms * 1e-3) / 1e12,
+         "mfma_frac": mfma_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+         "token_form_issue_floor_ms": floor_ms} if ms is not None else None)
     del xv, Bv, Cv, dtv, gate, yv
 
     # backward of the unfused conv at the 1.3B shape, with state gradients

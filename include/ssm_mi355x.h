@@ -222,10 +222,12 @@ ssm_status_t ssm_decode_step(const void* x_new, void* conv_state, const float* c
  *   initial_state, final_state  [batch, nheads, headdim, dstate] fp32, 16-byte aligned, or
  *                  NULL; final_state may alias initial_state
  *   seq_idx        [batch, seqlen] int32, or NULL
- * Token-sequential: the state stays in registers, the decays a_t[n] are formed once per
- * token and dimension.  dstate = 4 * 2^k <= 256, headdim * dstate <= 16384.  bf16 with
- * headdim 64, dstate 64 or 128 and 16-byte aligned x, B, C, log_decay / A_vec runs on the
- * long-row kernel; other cases on the general token-sequential one (same results to
+ * dstate = 4 * 2^k <= 256, headdim * dstate <= 16384.  The gate form (log_decay) with bf16,
+ * headdim 64, dstate 128, contiguous 16-byte aligned rows and states runs chunked on the
+ * matrix cores (64-token chunks, [LG] Sec. 2.5: the decay over a span is the exponential of
+ * a sum of log coefficients; a chunk whose summed log decay leaves +-40 runs token by
+ * token); other bf16 shapes with headdim 64 and dstate 64 or 128 (and the A_vec form) run a
+ * token-sequential long-row kernel, the rest the general token-sequential one (all agree to
  * rounding).  seqlen = 0: final_state = initial_state (or zero).
  * ------------------------------------------------------------------------------------- */
 ssm_status_t ssm_scan_fwd_vector_decay(const void* x, const float* dt, const float* log_decay,
