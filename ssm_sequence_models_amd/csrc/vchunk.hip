@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
     };
 
     const bool consumer = wave < 4;
-    const int p_own = 16 * wave + li;
+    const int p_own = 16 * (wave & 3) + li;  // state row of this lane (waves w and w + 4 share rows)
     const int64_t sbase = ((b * a.H + h) * kVcP + p_own) * kVcN;
     // per-lane byte offsets of the MFMA operand reads (the rest of each address is a constant):
     //   CE / BE row 16 I + li, piece 4 m + g4:  I * 4096 + ce_b[m]
@@ -326,7 +326,7 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
                     ce2[e] = cf * ep;
                     be2[e] = bf * em;
                     const float eend = __builtin_amdgcn_exp2f(Gend);
-                    const float bw = bf * u * (em * eend);
+                    const float bw = be2[e] * (u * eend);  // B u e^{G_63 - G}
                     bw2v[e] = lane >= r_last ? bw : 0.0f;
                     if (lane == 0)
                         reinterpret_cast<float*>(sm + kVcEend)[n0 + jj] = r_last < 0 ? eend : 0.0f;
@@ -452,16 +452,19 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
         if (!slow) {
             step2();
             __syncthreads();
+            // ---- step 3: both wave groups read the old state rows p = 16 (wave % 4) + li:
+            // acc[T][r] = S[p][n], n = 32 (T / 2) + 8 g4 + 4 (T % 2) + r (the output rows of
+            // the update's tile T, whose A operand row li holds dimension
+            // 32 (T / 2) + 8 (li / 4) + 4 (T % 2) + li % 4); then waves 0-3 form y from it
+            // while waves 4-7 decay and update it ----
+            vf32x4 acc[8];
+#pragma unroll
+            for (int T = 0; T < 8; ++T) acc[T] = vc_ld<vf32x4>(sm, vc_st_off(p_own, 8 * (T >> 1) + 2 * g4 + (T & 1)));
+            vbf16x8 xo[2];
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) xo[sh] = vc_ld<vbf16x8>(sm, kVcXT + xt_b[sh]);
+            __syncthreads();  // every read of the old state is done before it is overwritten
             if (consumer) {
-                // ---- step 3: acc[T][r] = S[p][n], n = 32 (T / 2) + 8 g4 + 4 (T % 2) + r (the
-                // output rows of the update's tile T, whose A operand row li holds dimension
-                // 32 (T / 2) + 8 (li / 4) + 4 (T % 2) + li % 4) ----
-                vf32x4 acc[8];
-#pragma unroll
-                for (int T = 0; T < 8; ++T) acc[T] = vc_ld<vf32x4>(sm, vc_st_off(p_own, 8 * (T >> 1) + 2 * g4 + (T & 1)));
-                vbf16x8 xo[2];
-#pragma unroll
-                for (int sh = 0; sh < 2; ++sh) xo[sh] = vc_ld<vbf16x8>(sm, kVcXT + xt_b[sh]);
                 vf32x4 ya[4];
 #pragma unroll
                 for (int I = 0; I < 4; ++I) ya[I] = vf32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -525,6 +528,7 @@ __global__ void __launch_bounds__(kVcThreads) vchunk_kernel(RecurrentArgs a) {
                         *reinterpret_cast<uint2*>(ys + (b * L + t0 + t) * a.H * kVcP + h * kVcP + 16 * wave + 4 * g4) = pk;
                     }
                 }
+            } else {
                 // S <- e^{G_63} o S + BW^T x, per half of the chunk and half of the tiles: the
                 // operands first, then the hi products, then the lo products
 #pragma unroll
