@@ -39,6 +39,10 @@ CASES = [
     (2, 1, 2, 64, 128, 1, BF16, "gate", True, True, 0),      # one token
     (2, 150, 4, 64, 128, 1, BF16, "rate", True, True, 3),    # rates, resets folded into a_t = 0
     (1, 70, 2, 64, 128, 1, F32, "gate", True, True, 2),      # fp32: the general kernel
+    # the chunked kernel: two groups, exactly one chunk, one token past a chunk
+    (2, 130, 4, 64, 128, 2, BF16, "gate", True, True, 2),
+    (1, 64, 3, 64, 128, 1, BF16, "gate", False, False, 0),
+    (2, 65, 2, 64, 128, 1, BF16, "gate", True, True, 0),
 ]
 
 
@@ -152,3 +156,21 @@ def test_scan_fwd_vector_decay_nan_gate_propagates():
     assert torch.equal(torch.isnan(fc), torch.isnan(rf_t)), "NaN pattern of the final state"
     ok = ~torch.isnan(ry_t)
     assert_close(torch.where(ok, yc, torch.zeros_like(yc)), torch.where(ok, ry_t, torch.zeros_like(ry_t)).double().numpy(), "finite y")
+
+
+def test_scan_fwd_vector_decay_starts_at_chunk_edges():
+    """Sequence starts at tokens 64 and 128 (the first tokens of chunks 1 and 2 of the chunked
+    kernel), at 129 and at 191 (a chunk's last token): the state must be zero before each."""
+    import ssm_sequence_models_amd as ssm
+    x, Bm, Cm, dt, gate, _, h0, _ = _inputs(2, 200, 2, 64, 128, 1, BF16, 23, "gate", True, True, 0)
+    seq = torch.zeros(2, 200, dtype=torch.int32)
+    for t in (64, 128, 129, 191):
+        seq[:, t:] += 1
+    seq[1, 192:] += 1  # row 1 also starts one at 192
+    y, fin = ssm.scan_fwd_vector_decay(dev(x), dev(Bm), dev(Cm), log_decay=dev(gate), dt=dev(dt),
+                                       initial_state=dev(h0), seq_idx=dev(seq))
+    torch.cuda.synchronize()
+    ry, rfin = oracle.scan_fwd_vdecay(x, dt, Bm, Cm, log_decay=gate, init_state=h0, seq_idx=seq,
+                                      out_dtype="bf16", state_dtype="f32")
+    assert_close(y, ry, "y")
+    assert_close(fin, rfin, "final state")
