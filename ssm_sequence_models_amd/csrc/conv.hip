@@ -5,7 +5,7 @@
 // u = [S, x]; F = u[L : L+K-1].  Each thread owns V adjacent channels of one batch row and a
 // run of TT tokens; the K-1 previous inputs live in registers and slide along the run, so
 // every input element is read from HBM once (plus a K-1 halo per run).  Channel-last rows
-// give coalesced vector loads/stores (4 bf16 channels per thread in the bf16 kernel below,
+// give coalesced vector loads/stores (2 bf16 channels per thread in the bf16 kernel below,
 // 4 fp32 channels in the generic one).
 //
 // Decode, same chapter, "single-token update maths", "the physical cache may exceed the
@@ -154,18 +154,20 @@ conv1d_fwd_kernel(const typename D::T* __restrict__ x, const float* __restrict__
     }
 }
 
-// bf16 prefill, the main case: each thread owns 4 adjacent channels of one batch row (8-byte
-// loads and stores, 512 contiguous bytes per wavefront) and a run of kConvTokens tokens.
-// Weights, bias and the K-1 previous inputs stay in registers as doubles (about 64 VGPRs, so
-// four wavefronts fit on a SIMD); the next group of kGroup tokens' inputs are loaded as
-// packed bf16 while the current group is computed.  SiLU outputs too close to a bf16
-// rounding midpoint for the fp32 evaluation (see silu_f32) are flagged (one bit mask per
-// group, kept in the thread's own LDS slots); after the run, when the fast path's registers
+// bf16 prefill, the main case: each lane owns 2 adjacent channels of one batch row (4-byte
+// loads and stores, 256 contiguous bytes per wavefront) and a run of kRun2 tokens.  Weights,
+// bias and the K-1 previous inputs stay in registers as doubles.  Two channels keep a lane
+// near 70 VGPRs, so seven wavefronts share a SIMD and one wave's loads overlap the others'
+// arithmetic; four channels per lane needed 128 VGPRs (four waves) and ran 15-18% slower
+// at the 1.3B layer shape, the same instructions per output either way.  The next group of
+// kGroup2 tokens is loaded while the current group is computed.  SiLU outputs too close to
+// a bf16 rounding midpoint for the fp32 evaluation (see silu_f32) are flagged (one mask per
+// group, kept in the lane's own LDS words); after the run, when the fast path's registers
 // are free, one loop recomputes the flagged outputs in double from memory and overwrites
 // them.
-constexpr int kRun4 = 32;  // tokens per thread run (64 and 128 measured no faster)
-constexpr int kGroup = 4;   // tokens per prefetch group (2 slower, 8 no faster)
-constexpr int kGroupsPerRun = kRun4 / kGroup;
+constexpr int kRun2 = 32;   // tokens per lane run
+constexpr int kGroup2 = 4;  // tokens per prefetch group
+constexpr int kGroupsPerRun = kRun2 / kGroup2;
 
 // Exact conv value at token t, channel ch of batch row b (the slow path's recomputation):
 // taps at u-positions t-K+1 .. t, from x or from the initial state, each zeroed when its
@@ -190,146 +192,182 @@ __device__ double conv_exact_bf16(const uint16_t* x, const float* w, const float
     return z;
 }
 
-__device__ __forceinline__ void unpack4(uint2 q, double (&v)[4]) {
-    v[0] = __uint_as_float(q.x << 16);
-    v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16);
-    v[3] = __uint_as_float(q.y & 0xffff0000u);
+__device__ __forceinline__ void unpack2(uint32_t q, double (&v)[2]) {
+    v[0] = __uint_as_float(q << 16);
+    v[1] = __uint_as_float(q & 0xffff0000u);
 }
 
 template <int K, bool HAS_SEQ, bool SILU>
-__global__ void __launch_bounds__(kConvThreads) __attribute__((amdgpu_waves_per_eu(K <= 4 && SILU ? 4 : 1)))
-conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
+__global__ void __launch_bounds__(kConvThreads) __attribute__((amdgpu_waves_per_eu(4)))
+conv1d_fwd_bf16x2_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
                          const float* __restrict__ bias, const uint16_t* init_state,
                          uint16_t* final_state, const int32_t* __restrict__ seq_idx,
                          uint16_t* __restrict__ out, int64_t L, int64_t C) {
-    constexpr int V = 4;
-    const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x) * V;
+    constexpr int V = 2;
+    const int64_t cblk = static_cast<int64_t>(blockIdx.x) * kConvThreads * V;
+    const int64_t c0 = cblk + threadIdx.x * V;
     if (c0 >= C) return;
     const int64_t b = blockIdx.z;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kRun4;
-    const int64_t t1 = min(t0 + kRun4, L);
-    const uint16_t* xrow = x + b * L * C + c0;
-    uint16_t* orow = out + b * L * C + c0;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kRun2;
+    const int64_t t1 = min(t0 + kRun2, L);
+    // a token row's base is uniform across the wavefront; each lane adds a 32-bit offset
+    const uint16_t* xb = x + b * L * C + cblk;
+    uint16_t* ob = out + b * L * C + cblk;
+    const uint32_t lane_off = threadIdx.x * 4u;
     const int32_t* srow = HAS_SEQ ? seq_idx + b * L : nullptr;
+    auto ld_hist = [&](int64_t t) {  // rows shared with the previous run: plain loads (L2)
+        return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(xb + t * C) + lane_off);
+    };
+    auto ld_run = [&](int64_t t) {  // rows read once: non-temporal
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(xb + t * C) + lane_off));
+    };
+    auto st_run = [&](int64_t t, uint32_t v) {
+        __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ob + t * C) + lane_off));
+    };
 
+    // set-up loads carry no branches around them, so they are in flight together
     double wr[V][K], bv[V];
+    const float* bsrc = bias ? bias : w;  // read either way; the value is dropped without bias
 #pragma unroll
     for (int v = 0; v < V; ++v) {
 #pragma unroll
         for (int k = 0; k < K; ++k) wr[v][k] = w[(c0 + v) * K + k];
-        bv[v] = bias ? bias[c0 + v] : 0.0f;
+        const float bq = bsrc[c0 + v];
+        bv[v] = bias ? bq : 0.0f;
     }
-    // The window of a group of kGroup tokens: rows 0 .. K-2 hold the K-1 inputs before the
-    // group (oldest first), row K-1+u the group's token u; output u takes rows u .. u+K-1.
-    // The history moves once per group (K-1 rows), not once per token.  First the u-positions
-    // t0-K+1 .. t0-1: from x, or from the state for pos < 0.
-    double win[kGroup + K - 1][V];
-    int32_t wid[kGroup + K - 1];
+    // The window of a group: rows 0 .. K-2 hold the K-1 inputs before the group (oldest
+    // first), row K-1+u the group's token u; output u takes rows u .. u+K-1.  First the
+    // u-positions t0-K+1 .. t0-1: from x, or from the state for pos < 0.
+    double win[kGroup2 + K - 1][V];
+    int32_t wid[kGroup2 + K - 1];
+    if (t0 >= K - 1) {
+        uint32_t hq[K - 1];
 #pragma unroll
-    for (int j = 0; j < K - 1; ++j) {
-        const int64_t pos = t0 - (K - 1) + j;
-        if (pos >= 0) {
-            unpack4(*reinterpret_cast<const uint2*>(xrow + pos * C), win[j]);
-            wid[j] = HAS_SEQ ? srow[pos] : 0;
-        } else {
+        for (int j = 0; j < K - 1; ++j) {
+            hq[j] = ld_hist(t0 - (K - 1) + j);
+            wid[j] = HAS_SEQ ? srow[t0 - (K - 1) + j] : 0;
+        }
 #pragma unroll
-            for (int v = 0; v < V; ++v)
-                win[j][v] = init_state ? bf16_to_f32(init_state[(b * C + c0 + v) * (K - 1) + (K - 1) + pos]) : 0.0f;
-            wid[j] = HAS_SEQ ? srow[0] : 0;
+        for (int j = 0; j < K - 1; ++j) unpack2(hq[j], win[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+            const int64_t pos = t0 - (K - 1) + j;
+            if (pos >= 0) {
+                unpack2(ld_hist(pos), win[j]);
+                wid[j] = HAS_SEQ ? srow[pos] : 0;
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    win[j][v] = init_state ? bf16_to_f32(init_state[(b * C + c0 + v) * (K - 1) + (K - 1) + pos]) : 0.0f;
+                wid[j] = HAS_SEQ ? srow[0] : 0;
+            }
         }
     }
-
-    static_assert(4 * kGroup <= 32, "flag mask");
-    __shared__ uint32_t flags[kGroupsPerRun][kConvThreads];
-    uint2 xa[kGroup];
-    int32_t ia[kGroup];
+    // a loaded group into window rows K-1 .. K+2
+    auto fill = [&](const uint32_t (&xa)[kGroup2], const int32_t (&ia)[kGroup2]) {
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-        const int64_t t = t0 + u;
-        xa[u] = t < t1 ? ld_stream_u2(xrow + t * C) : uint2{0u, 0u};
-        ia[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
-    }
-    // One group; FULL groups lie inside the run and skip the per-token bound checks.
-    auto group = [&](int64_t tg, auto full) -> uint32_t {
-        constexpr bool FULL = decltype(full)::value;
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            unpack4(xa[u], win[K - 1 + u]);
+        for (int u = 0; u < kGroup2; ++u) {
+            unpack2(xa[u], win[K - 1 + u]);
             wid[K - 1 + u] = ia[u];
         }
-        uint32_t near = 0;  // bit 4u + v: output (token tg + u, channel c0 + v) flagged
+    };
+    // One group; FULL groups lie inside the run and skip the per-token bound checks.  Bit
+    // 2*kGroup2-1 - (V*u + v) of the result flags output (token tg+u, channel c0+v).
+    auto group = [&](int64_t tg, auto full) -> uint32_t {
+        constexpr bool FULL = decltype(full)::value;
+        uint32_t near = 0;
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
+        for (int u = 0; u < kGroup2; ++u) {
             const int64_t t = tg + u;
-            if (FULL || t < t1) {
-                double z[V];
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    double acc = bv[v];
-#pragma unroll
-                    for (int k = 0; k < K - 1; ++k) {
-                        const double tap = (!HAS_SEQ || wid[u + k] == wid[u + K - 1]) ? win[u + k][v] : 0.0;
-                        acc = fma(wr[v][k], tap, acc);
-                    }
-                    z[v] = fma(wr[v][K - 1], win[u + K - 1][v], acc);
-                }
-                uint16_t o[V];
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    if (SILU) {
-                        bool nr;
-                        o[v] = f32_to_bf16(silu_f32(z[v], nr));
-                        near |= static_cast<uint32_t>(nr) << (4 * u + v);
-                    } else {
-                        o[v] = f64_to_bf16(z[v]);
-                    }
-                }
-                st_stream_u2(orow + t * C, uint2{o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                                                 o[2] | (static_cast<uint32_t>(o[3]) << 16)});
+            if (!FULL && t >= t1) {
+                if (SILU) near <<= V;
+                continue;
             }
+            double z[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                double acc = bv[v];
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k) {
+                    const double tap = (!HAS_SEQ || wid[u + k] == wid[u + K - 1]) ? win[u + k][v] : 0.0;
+                    acc = fma(wr[v][k], tap, acc);
+                }
+                z[v] = fma(wr[v][K - 1], win[u + K - 1][v], acc);
+            }
+            uint16_t o[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (SILU) {
+                    bool nr;
+                    o[v] = f32_to_bf16(silu_f32(z[v], nr));
+                    near = near + near + static_cast<uint32_t>(nr);
+                } else {
+                    o[v] = f64_to_bf16(z[v]);
+                }
+            }
+            st_run(t, o[0] | (static_cast<uint32_t>(o[1]) << 16));
         }
-        if (FULL) {
 #pragma unroll
-            for (int j = 0; j < K - 1; ++j) {
+        for (int j = 0; j < K - 1; ++j) {
 #pragma unroll
-                for (int v = 0; v < V; ++v) win[j][v] = win[kGroup + j][v];
-                wid[j] = wid[kGroup + j];
-            }
+            for (int v = 0; v < V; ++v) win[j][v] = win[kGroup2 + j][v];
+            wid[j] = wid[kGroup2 + j];
         }
         return near;
     };
-    int64_t tg = t0;
-    for (; tg + kGroup <= t1; tg += kGroup) {
-        uint2 xb[kGroup];
-        int32_t ib[kGroup];
+    static_assert(V * kGroup2 <= 32, "flag mask");
+    __shared__ uint32_t flags[kGroupsPerRun][kConvThreads];
+    if (t1 - t0 == kRun2) {
+        // a whole run: every load in range, no per-token checks; the next group's loads are
+        // issued before the current group's arithmetic and unpacked after it
+        uint32_t xa[kGroup2];
+        int32_t ia[kGroup2];
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            const int64_t t = tg + kGroup + u;
-            xb[u] = t < t1 ? ld_stream_u2(xrow + t * C) : uint2{0u, 0u};
-            ib[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
+        for (int u = 0; u < kGroup2; ++u) {
+            xa[u] = ld_run(t0 + u);
+            ia[u] = HAS_SEQ ? srow[t0 + u] : 0;
         }
-        const uint32_t near = group(tg, std::true_type{});
-        if (SILU) flags[(tg - t0) / kGroup][threadIdx.x] = near;
+        fill(xa, ia);
+#pragma unroll 1
+        for (int g = 0; g < kGroupsPerRun - 1; ++g) {
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            xa[u] = xb[u];
-            ia[u] = ib[u];
+            for (int u = 0; u < kGroup2; ++u) {
+                xa[u] = ld_run(t0 + kGroup2 * (g + 1) + u);
+                ia[u] = HAS_SEQ ? srow[t0 + kGroup2 * (g + 1) + u] : 0;
+            }
+            const uint32_t m = group(t0 + kGroup2 * g, std::true_type{});
+            if (SILU) flags[g][threadIdx.x] = m;
+            fill(xa, ia);
         }
-    }
-    if (tg < t1) {
-        const uint32_t near = group(tg, std::false_type{});
-        if (SILU) flags[(tg - t0) / kGroup][threadIdx.x] = near;
+        const uint32_t m = group(t0 + kGroup2 * (kGroupsPerRun - 1), std::true_type{});
+        if (SILU) flags[kGroupsPerRun - 1][threadIdx.x] = m;
+    } else {
+        // the row's last, shorter run
+        for (int64_t tg = t0; tg < t1; tg += kGroup2) {
+            uint32_t xa[kGroup2];
+            int32_t ia[kGroup2];
+#pragma unroll
+            for (int u = 0; u < kGroup2; ++u) {
+                const int64_t t = tg + u;
+                xa[u] = t < t1 ? ld_run(t) : 0u;
+                ia[u] = HAS_SEQ && t < t1 ? srow[t] : 0;
+            }
+            fill(xa, ia);
+            const uint32_t m = group(tg, std::false_type{});
+            if (SILU) flags[(tg - t0) / kGroup2][threadIdx.x] = m;
+        }
     }
 
-    // rare: each iteration redoes one flagged output per lane (this thread stored the fast
+    // rare: each iteration redoes one flagged output per lane (this lane stored the fast
     // value earlier, so the overwrite lands after it)
     if (SILU) {
-        const int ng = static_cast<int>((t1 - t0 + kGroup - 1) / kGroup);
+        const int ng = static_cast<int>((t1 - t0 + kGroup2 - 1) / kGroup2);
         for (int g = 0; g < ng; ++g) {
             for (uint32_t m = flags[g][threadIdx.x]; m != 0; m &= m - 1) {
-                const int bit = __builtin_ctz(m);
-                const int64_t t = t0 + g * kGroup + (bit >> 2), ch = c0 + (bit & 3);
+                const int idx = V * kGroup2 - 1 - __builtin_ctz(m);
+                const int64_t t = t0 + g * kGroup2 + idx / V, ch = c0 + idx % V;
                 const double z = conv_exact_bf16<K, HAS_SEQ>(x, w, bias, init_state, srow, b, L, C, t, ch);
                 out[(b * L + t) * C + ch] = silu_f64_to_bf16(z);
             }
@@ -346,7 +384,7 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
 #pragma unroll
             for (int v = 0; v < V; ++v)
                 fv[v][r] = m < K - 1 ? (init_state ? init_state[(b * C + c0 + v) * (K - 1) + m] : uint16_t(0))
-                                     : xrow[(m - (K - 1)) * C + v];
+                                     : x[(b * L + m - (K - 1)) * C + c0 + v];
         }
 #pragma unroll
         for (int v = 0; v < V; ++v)
@@ -356,44 +394,44 @@ conv1d_fwd_bf16x4_kernel(const uint16_t* __restrict__ x, const float* __restrict
 }
 
 template <int K>
-hipError_t conv_fwd_bf16x4_dispatch_seq(const void* x, const float* w, const float* bias,
+hipError_t conv_fwd_bf16x2_dispatch_seq(const void* x, const float* w, const float* bias,
                                         const void* init_state, void* final_state,
                                         const int32_t* seq_idx, void* out, int64_t B, int64_t L,
                                         int64_t C, int act, hipStream_t stream) {
-    const int64_t threads_needed = C / 4;
+    const int64_t threads_needed = C / 2;
     dim3 grid((threads_needed + kConvThreads - 1) / kConvThreads,
-              (L + kRun4 - 1) / kRun4, B);
+              (L + kRun2 - 1) / kRun2, B);
     using U16 = uint16_t;
-#define SSM_CONV4_LAUNCH(SEQ, SL)                                                             \
-    conv1d_fwd_bf16x4_kernel<K, SEQ, SL><<<grid, kConvThreads, 0, stream>>>(                  \
+#define SSM_CONV2_LAUNCH(SEQ, SL)                                                             \
+    conv1d_fwd_bf16x2_kernel<K, SEQ, SL><<<grid, kConvThreads, 0, stream>>>(                  \
         (const U16*)x, w, bias, (const U16*)init_state, (U16*)final_state, seq_idx, (U16*)out, \
         L, C)
     const bool silu = act == SSM_ACT_SILU;
     if (seq_idx) {
-        if (silu) SSM_CONV4_LAUNCH(true, true);
-        else SSM_CONV4_LAUNCH(true, false);
+        if (silu) SSM_CONV2_LAUNCH(true, true);
+        else SSM_CONV2_LAUNCH(true, false);
     } else {
-        if (silu) SSM_CONV4_LAUNCH(false, true);
-        else SSM_CONV4_LAUNCH(false, false);
+        if (silu) SSM_CONV2_LAUNCH(false, true);
+        else SSM_CONV2_LAUNCH(false, false);
     }
-#undef SSM_CONV4_LAUNCH
+#undef SSM_CONV2_LAUNCH
     return hipGetLastError();
 }
 
-hipError_t conv_fwd_bf16x4_dispatch(int64_t K, const void* x, const float* w, const float* bias,
+hipError_t conv_fwd_bf16x2_dispatch(int64_t K, const void* x, const float* w, const float* bias,
                                     const void* init_state, void* final_state,
                                     const int32_t* seq_idx, void* out, int64_t B, int64_t L,
                                     int64_t C, int act, hipStream_t stream) {
-#define SSM_CONV4_K(KK)                                                                      \
+#define SSM_CONV2_K(KK)                                                                      \
     case KK:                                                                                 \
-        return conv_fwd_bf16x4_dispatch_seq<KK>(x, w, bias, init_state, final_state, seq_idx, \
+        return conv_fwd_bf16x2_dispatch_seq<KK>(x, w, bias, init_state, final_state, seq_idx, \
                                                 out, B, L, C, act, stream);
     switch (K) {
-        SSM_CONV4_K(2) SSM_CONV4_K(3) SSM_CONV4_K(4) SSM_CONV4_K(5) SSM_CONV4_K(6)
-        SSM_CONV4_K(7) SSM_CONV4_K(8)
+        SSM_CONV2_K(2) SSM_CONV2_K(3) SSM_CONV2_K(4) SSM_CONV2_K(5) SSM_CONV2_K(6)
+        SSM_CONV2_K(7) SSM_CONV2_K(8)
         default: return hipErrorInvalidValue;
     }
-#undef SSM_CONV4_K
+#undef SSM_CONV2_K
 }
 
 // seqlen == 0: F = S (or zeros)
@@ -582,8 +620,8 @@ hipError_t launch_conv1d_fwd(const void* x, const float* w, const float* bias,
     }
     const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out);
     if (dtype == SSM_BF16) {
-        if (C % 4 == 0 && (align & 7) == 0)
-            return conv_fwd_bf16x4_dispatch(K, x, w, bias, init_state, final_state, seq_idx, out,
+        if (C % 2 == 0 && (align & 3) == 0)
+            return conv_fwd_bf16x2_dispatch(K, x, w, bias, init_state, final_state, seq_idx, out,
                                             B, L, C, act, stream);
         return conv_fwd_dispatch_k<BF16, 1>(K, x, w, bias, init_state, final_state, seq_idx,
                                            out, B, L, C, act, stream);

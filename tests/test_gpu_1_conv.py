@@ -31,11 +31,12 @@ CASES = [
     # B, L, C, K, dtype, init, segments, act
     (1, 64, 12, 4, F32, True, 0, "silu"),     # the tiny layer's 4 + 2*4 channels
     (1, 64, 12, 4, F32, True, 0, None),
-    (2, 200, 264, 4, BF16, True, 0, "silu"),  # 4-channel vector path, ragged token runs
+    (2, 200, 264, 4, BF16, True, 0, "silu"),  # 2-channel vector path, ragged token runs
     (2, 130, 36, 4, BF16, True, 0, "silu"),   # 9 threads per row: a partial wavefront
     (1, 96, 24, 4, BF16, False, 0, None),     # vector path, identity, no initial state
     (2, 200, 264, 4, BF16, True, 4, "silu"),  # packed sequences
     (1, 77, 13, 3, BF16, True, 3, None),      # odd channel count: scalar path
+    (2, 70, 18, 4, BF16, True, 2, "silu"),    # C % 4 = 2: vector path, one partial wavefront
     (3, 2, 16, 4, BF16, True, 0, "silu"),     # L < K-1: F keeps state entries
     (2, 1, 8, 2, F32, False, 0, None),
     (2, 45, 40, 8, BF16, True, 2, "silu"),    # widest conv
