@@ -23,12 +23,12 @@ namespace {
 // output t, forms delta_t, adds the run's own tokens to its dw / dbeta partial sums, and
 // emits dx_s for s = t-K+1 once delta_{s .. s+K-1} are known.  Run 0 also forms dS from
 // delta_0 .. delta_{K-2}.  Consecutive threads take consecutive channels (coalesced rows).
-// Used for fp32, odd channel counts and unaligned rows; bf16 rows of whole 4-channel groups
-// take conv1d_bwd_bf16x4_kernel below (0.33 -> 0.27 ms at the 1.3B layer's xBC).
+// Used for fp32, odd channel counts and unaligned rows; bf16 rows of whole 2-channel groups
+// take conv1d_bwd_bf16vec_kernel below.
 // ---------------------------------------------------------------------------------------
 constexpr int kConvBwdRun = 64;
 constexpr int kConvBwdThreads = 256;
-constexpr int kBwdGroup = 4;  // tokens per group of the bf16x4 kernel's main range
+constexpr int kBwdGroup = 4;  // tokens per group of the bf16 vector kernel's main range
 
 template <class D, int K>
 __global__ void __launch_bounds__(kConvBwdThreads)
@@ -153,25 +153,53 @@ conv1d_bwd_kernel(const typename D::T* x, const float* w, const float* bias,
     pp[K] = dbp;
 }
 
-// The same walk for bf16 with four adjacent channels per thread (C % 4 == 0, x / dy / dx
-// 8-byte aligned): each load and store of x, dy and dx moves 8 bytes, so a wavefront
-// instruction covers 512 contiguous bytes instead of 128; the token identities and the
-// sequence masks are shared by the four channels.
-__device__ __forceinline__ void bf16x4_to_f32(uint2 r, float (&v)[4]) {
-    v[0] = __uint_as_float(r.x << 16);
-    v[1] = __uint_as_float(r.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(r.y << 16);
-    v[3] = __uint_as_float(r.y & 0xFFFF0000u);
-}
+// The same walk for bf16 with V adjacent channels per thread (C % V == 0, x / dy / dx
+// aligned to 2V bytes): each load and store of x, dy and dx moves 2V bytes, and the token
+// identities and the sequence masks are shared by the V channels.  V = 2 is the one
+// launched: about 70 VGPRs, so seven wavefronts share a SIMD and one wave's loads overlap the
+// others' arithmetic, where V = 4 needed 118 VGPRs (four waves).
+template <int V>
+struct BwdVec;
+template <>
+struct BwdVec<4> {
+    using Q = uint2;
+    __device__ static Q ld(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ static Q ld_stream(const uint16_t* p) { return ld_stream_u2(p); }
+    __device__ static void st_stream(uint16_t* p, const float (&v)[4]) {
+        st_stream_u2(p, uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+    }
+    __device__ static void unpack(Q r, float (&v)[4]) {
+        v[0] = __uint_as_float(r.x << 16);
+        v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(r.y << 16);
+        v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    }
+};
+template <>
+struct BwdVec<2> {
+    using Q = uint32_t;
+    __device__ static Q ld(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    __device__ static Q ld_stream(const uint16_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
+    __device__ static void st_stream(uint16_t* p, const float (&v)[2]) {
+        __builtin_nontemporal_store(pack_bf16x2(v[0], v[1]), reinterpret_cast<uint32_t*>(p));
+    }
+    __device__ static void unpack(Q r, float (&v)[2]) {
+        v[0] = __uint_as_float(r << 16);
+        v[1] = __uint_as_float(r & 0xFFFF0000u);
+    }
+};
 
-template <int K>
+template <int K, int V>
 __global__ void __launch_bounds__(kConvBwdThreads)
-conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
-                         const uint16_t* init, const int32_t* seq, const uint16_t* dy,
-                         const uint16_t* dfin, uint16_t* dx, uint16_t* dinit, float* part,
-                         int64_t L, int64_t C, int nruns, int silu) {
-    constexpr int V = 4;
-    // block = 64 channel quads x four consecutive runs, one run per wavefront; the four runs'
+conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
+                          const uint16_t* init, const int32_t* seq, const uint16_t* dy,
+                          const uint16_t* dfin, uint16_t* dx, uint16_t* dinit, float* part,
+                          int64_t L, int64_t C, int nruns, int silu) {
+    using VQ = BwdVec<V>;
+    using Q = typename VQ::Q;
+    // block = 64 groups of V channels x four consecutive runs, one run per wavefront; the four runs'
     // dw / dbeta partial sums are added in the block (in order) before they leave
     // the wave index through readfirstlane: the compiler then keeps the run's token bounds in
     // scalar registers
@@ -200,7 +228,7 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
     const int32_t id0 = sq ? sq[0] : 0;
     auto sid = [&](int64_t s) -> int32_t { return sq ? sq[s < 0 ? 0 : s] : 0; };
     auto load4 = [&](const uint16_t* p, int64_t t, float (&v)[V]) {
-        bf16x4_to_f32(*reinterpret_cast<const uint2*>(p + (b * L + t) * C + c4), v);
+        VQ::unpack(VQ::ld(p + (b * L + t) * C + c4), v);
     };
 
     float xv[K][V];   // inputs of output t: x indices t-K+1 .. t
@@ -242,7 +270,7 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
                 dl[k][j] = dl[k + 1][j];
             }
         }
-        float delta[V] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float delta[V] = {};
         int32_t idt = 0;
         if (live) {
             load4(x, t, xv[K - 1]);
@@ -292,7 +320,7 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
         const int64_t s_ = t - (K - 1);
         if (s_ >= t0 && s_ < t1) {
             const int32_t ids = ds[0];
-            float v[V] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float v[V] = {};
 #pragma unroll
             for (int m = 0; m < K; ++m)
                 if (!sq || ds[m] == ids) {
@@ -304,10 +332,7 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
                 for (int j = 0; j < V; ++j)
                     v[j] += bf16_to_f32(dfin[(b * C + c4 + j) * (K - 1) + (s_ + K - 1 - L)]);
             }
-            uint2 o;
-            o.x = pack_bf16x2(v[0], v[1]);
-            o.y = pack_bf16x2(v[2], v[3]);
-            st_stream_u2(dx + (b * L + s_) * C + c4, o);
+            VQ::st_stream(dx + (b * L + s_) * C + c4, v);
         }
     };
     // Tokens ta .. tb-1 (all inside the run, at least K-1 after its start) in groups of
@@ -332,29 +357,29 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
             }
             idw[j] = xs[j + 1];
         }
-        uint2 xq[G], gq[G];
+        Q xq[G], gq[G];
 #pragma unroll
         for (int u = 0; u < G; ++u) {
-            xq[u] = ld_stream_u2(x + (b * L + t + u) * C + c4);
-            gq[u] = ld_stream_u2(dy + (b * L + t + u) * C + c4);
+            xq[u] = VQ::ld_stream(x + (b * L + t + u) * C + c4);
+            gq[u] = VQ::ld_stream(dy + (b * L + t + u) * C + c4);
         }
         for (; t + G <= tb; t += G) {
-            uint2 xn[G], gn[G];
+            Q xn[G], gn[G];
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 const int64_t tt = t + G + u;
-                xn[u] = tt < L ? ld_stream_u2(x + (b * L + tt) * C + c4) : uint2{0u, 0u};
-                gn[u] = tt < L ? ld_stream_u2(dy + (b * L + tt) * C + c4) : uint2{0u, 0u};
+                xn[u] = tt < L ? VQ::ld_stream(x + (b * L + tt) * C + c4) : Q{};
+                gn[u] = tt < L ? VQ::ld_stream(dy + (b * L + tt) * C + c4) : Q{};
             }
 #pragma unroll
             for (int u = 0; u < G; ++u) {
-                bf16x4_to_f32(xq[u], xw[K - 1 + u]);
+                VQ::unpack(xq[u], xw[K - 1 + u]);
                 idw[K - 1 + u] = sid(t + u);
             }
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 float g[V];
-                bf16x4_to_f32(gq[u], g);
+                VQ::unpack(gq[u], g);
                 bool tap[K];
 #pragma unroll
                 for (int k = 0; k < K; ++k) tap[k] = !sq || idw[u + k] == idw[u + K - 1];
@@ -383,17 +408,14 @@ conv1d_bwd_bf16x4_kernel(const uint16_t* x, const float* w, const float* bias,
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 const int64_t s_ = t + u - (K - 1);
-                float v[V] = {0.0f, 0.0f, 0.0f, 0.0f};
+                float v[V] = {};
 #pragma unroll
                 for (int m = 0; m < K; ++m)
                     if (!sq || idw[u + m] == idw[u]) {
 #pragma unroll
                         for (int j = 0; j < V; ++j) v[j] = __builtin_fmaf(dlw[u + m][j], wk[K - 1 - m][j], v[j]);
                     }
-                uint2 o;
-                o.x = pack_bf16x2(v[0], v[1]);
-                o.y = pack_bf16x2(v[2], v[3]);
-                st_stream_u2(dx + (b * L + s_) * C + c4, o);
+                VQ::st_stream(dx + (b * L + s_) * C + c4, v);
             }
 #pragma unroll
             for (int j = 0; j < K - 1; ++j) {
@@ -743,15 +765,16 @@ hipError_t launch_conv1d_bwd(const void* x, const float* w, const float* bias, c
                 static_cast<float*>(dx), static_cast<float*>(dinit), part, seqlen, C, nruns,    \
                 silu);                                                                         \
         break;
-    const bool vec4 = dtype == SSM_BF16 && C % 4 == 0 &&
-                      ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dy) |
-                        reinterpret_cast<uintptr_t>(dx)) & 7) == 0;
-    if (vec4) {
-        const dim3 grid4(static_cast<unsigned>((C / 4 + 63) / 64),
+    constexpr int kVec = 2;  // channels per thread of the bf16 vector kernel
+    const bool vec = dtype == SSM_BF16 && C % kVec == 0 &&
+                     ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dy) |
+                       reinterpret_cast<uintptr_t>(dx)) & (2 * kVec - 1)) == 0;
+    if (vec) {
+        const dim3 grid4(static_cast<unsigned>((C / kVec + 63) / 64),
                          static_cast<unsigned>((nruns + 3) / 4), static_cast<unsigned>(batch));
 #define SSM_CBWD4(KK)                                                                          \
     case KK:                                                                                   \
-        conv1d_bwd_bf16x4_kernel<KK><<<grid4, kConvBwdThreads, 0, stream>>>(                   \
+        conv1d_bwd_bf16vec_kernel<KK, kVec><<<grid4, kConvBwdThreads, 0, stream>>>(            \
             static_cast<const uint16_t*>(x), w, bias, static_cast<const uint16_t*>(init), seq,  \
             static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(dfin),              \
             static_cast<uint16_t*>(dx), static_cast<uint16_t*>(dinit), part, seqlen, C, nruns, \
@@ -772,8 +795,8 @@ hipError_t launch_conv1d_bwd(const void* x, const float* w, const float* bias, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nred = C * (K + 1);
-    // the four-channel kernel leaves one partial per group of four runs
-    const int64_t nparts = vec4 ? batch * ((nruns + 3) / 4) : batch * nruns;
+    // the vector kernel leaves one partial per group of four runs
+    const int64_t nparts = vec ? batch * ((nruns + 3) / 4) : batch * nruns;
     conv1d_bwd_reduce_kernel<<<static_cast<unsigned>((nred + 63) / 64), 256, 0, stream>>>(
         part, dw, dbias, C, static_cast<int>(K), nparts);
     return hipGetLastError();

@@ -37,6 +37,7 @@ CONV_CASES = [
     (2, 2, 8, 4, F32, "none", True, True, 0),         # L < K-1: dS takes part of dF
     (1, 1, 4, 5, F32, "silu", True, True, 0),
     (3, 64, 33, 4, BF16, "none", False, False, 0),    # exactly one run
+    (2, 150, 18, 4, BF16, "silu", True, True, 2),     # C % 4 = 2: vector path, partial wavefront
 ]
 
 
