@@ -217,12 +217,17 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
     if (c4 < C && r < nruns) {
     const int64_t t0 = static_cast<int64_t>(r) * kConvBwdRun;
     const int64_t t1 = min(t0 + kConvBwdRun, L);
+    // The set-up loads carry no branches around them, so they are in flight together: the
+    // weights, the bias (read from w when there is none, and dropped), the x and dy of the
+    // run's first K-1 tokens (clamped into the row) and the K-1 inputs before the run.
     float wk[K][V], beta[V];
+    const float* bsrc = bias ? bias : w;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
 #pragma unroll
         for (int k = 0; k < K; ++k) wk[k][j] = w[(c4 + j) * K + k];
-        beta[j] = bias ? bias[c4 + j] : 0.0f;
+        const float bq = bsrc[c4 + j];
+        beta[j] = bias ? bq : 0.0f;
     }
     const int32_t* sq = seq ? seq + b * L : nullptr;
     const int32_t id0 = sq ? sq[0] : 0;
@@ -230,20 +235,38 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
     auto load4 = [&](const uint16_t* p, int64_t t, float (&v)[V]) {
         VQ::unpack(VQ::ld(p + (b * L + t) * C + c4), v);
     };
+    Q hx[K - 1], hg[K - 1];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) {
+        const int64_t tc = min(t0 + k, L - 1);
+        hx[k] = VQ::ld(x + (b * L + tc) * C + c4);
+        hg[k] = VQ::ld(dy + (b * L + tc) * C + c4);
+    }
 
     float xv[K][V];   // inputs of output t: x indices t-K+1 .. t
     int32_t xs[K];    // their identities
+    if (t0 >= K - 1) {
+        Q hq[K - 1];
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k) {
-        const int64_t s_ = t0 - (K - 1) + k;
-        if (s_ >= 0) {
-            load4(x, s_, xv[k + 1]);
-        } else {
+        for (int k = 0; k < K - 1; ++k) hq[k] = VQ::ld(x + (b * L + t0 - (K - 1) + k) * C + c4);
 #pragma unroll
-            for (int j = 0; j < V; ++j)
-                xv[k + 1][j] = init ? bf16_to_f32(init[(b * C + c4 + j) * (K - 1) + (K - 1) + s_]) : 0.0f;
+        for (int k = 0; k < K - 1; ++k) {
+            VQ::unpack(hq[k], xv[k + 1]);
+            xs[k + 1] = sid(t0 - (K - 1) + k);
         }
-        xs[k + 1] = sid(s_);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) {
+            const int64_t s_ = t0 - (K - 1) + k;
+            if (s_ >= 0) {
+                load4(x, s_, xv[k + 1]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    xv[k + 1][j] = init ? bf16_to_f32(init[(b * C + c4 + j) * (K - 1) + (K - 1) + s_]) : 0.0f;
+            }
+            xs[k + 1] = sid(s_);
+        }
     }
     float dl[K][V];   // delta of tokens t-K+1 .. t (0 past the row's end)
     int32_t ds[K];
@@ -257,8 +280,10 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
         for (int j = 0; j < V; ++j) dl[k][j] = dsd[k][j] = 0.0f;
     }
 
-    // one token, general case (the run's first K-1 tokens, its last K-1 steps and short runs)
-    auto token = [&](int64_t t) {
+    // one token, general case (the run's first K-1 tokens, its last K-1 steps and short
+    // runs); PRE: x_t and dy_t already loaded (qx, qg), else loaded here
+    auto token = [&](int64_t t, Q qx, Q qg, auto pre) {
+        constexpr bool PRE = decltype(pre)::value;
         const bool live = t < L;
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) {
@@ -273,10 +298,15 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
         float delta[V] = {};
         int32_t idt = 0;
         if (live) {
-            load4(x, t, xv[K - 1]);
-            xs[K - 1] = idt = sid(t);
             float g[V];
-            load4(dy, t, g);
+            if (PRE) {
+                VQ::unpack(qx, xv[K - 1]);
+                VQ::unpack(qg, g);
+            } else {
+                load4(x, t, xv[K - 1]);
+                load4(dy, t, g);
+            }
+            xs[K - 1] = idt = sid(t);
             bool tap[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) tap[k] = !sq || xs[k] == idt;
@@ -343,7 +373,12 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
     // in the same order as the general case.
     const int64_t ta = min(t0 + K - 1, t1), tb = t1;
     int64_t t = t0;
-    for (; t < ta; ++t) token(t);
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+        if (t < ta) {
+            token(t, hx[k], hg[k], std::true_type{});
+            ++t;
+        }
     if (tb - t >= kBwdGroup) {
         constexpr int G = kBwdGroup;
         float xw[G + K - 1][V], dlw[G + K - 1][V];
@@ -442,8 +477,15 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
             }
             xs[j + 1] = ds[j + 1] = idw[j];
         }
+        // the loop's last prefetch holds x and dy of the next G tokens (zeros past the row)
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+            if (t < t1 + K - 1) {
+                token(t, xq[u], gq[u], std::true_type{});
+                ++t;
+            }
     }
-    for (; t < t1 + K - 1; ++t) token(t);
+    for (; t < t1 + K - 1; ++t) token(t, Q{}, Q{}, std::false_type{});
     if (r == 0 && dinit) {
 #pragma unroll
         for (int jj = 0; jj < K - 1; ++jj) {
