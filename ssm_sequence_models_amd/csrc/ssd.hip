@@ -235,18 +235,33 @@ ssd_prep_kernel(ChunkedArgs a) {
         sSeq[tid] = a.seq_idx[b * L + t];
     }
     // raw rows t0-(K-1) .. t0+Q-1 of the group's B and C channels, 16 bytes per load
-    // (B and C channels of a group are each 128 contiguous bf16 of a token row)
-    for (int idx = tid; idx < kRows * 32; idx += kPrepThreads) {
+    // (B and C channels of a group are each 128 contiguous bf16 of a token row).  A thread's
+    // pieces are all loaded before any is stored: each load reads a row clamped into
+    // 0 .. L-1, so none sits behind a branch, and a select drops the clamped ones afterwards.
+    constexpr int kPieces = kRows * 32;
+    constexpr int kPer = (kPieces + kPrepThreads - 1) / kPrepThreads;
+    u32x4 raw[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = min(tid + i * kPrepThreads, kPieces - 1);
         const int rho = idx >> 5, piece = idx & 31;
         const bool isC = piece >= 16;
-        const int n0 = (piece & 15) * 8;
         const int64_t t = t0 - (K - 1) + rho;
+        const int64_t tc = t < 0 ? 0 : (t >= L ? L - 1 : t);
         const int64_t row = isC ? a.c_row : a.b_row;
-        const int64_t col = (isC ? a.c_col0 : a.b_col0) + g * kN + n0;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (t >= 0 && t < L) {
-            v = *reinterpret_cast<const u32x4*>((isC ? a.csrc : a.bsrc) + (b * L + t) * row + col);
-        } else if (t < 0 && a.fused_conv && a.conv_init) {
+        const int64_t col = (isC ? a.c_col0 : a.b_col0) + g * kN + (piece & 15) * 8;
+        raw[i] = *reinterpret_cast<const u32x4*>((isC ? a.csrc : a.bsrc) + (b * L + tc) * row + col);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = tid + i * kPrepThreads;
+        if (idx >= kPieces) break;
+        const int rho = idx >> 5, piece = idx & 31;
+        const int64_t t = t0 - (K - 1) + rho;
+        u32x4 v = t >= 0 && t < L ? raw[i] : u32x4{0u, 0u, 0u, 0u};
+        if (t < 0 && a.fused_conv && a.conv_init) {
+            const bool isC = piece >= 16;
+            const int64_t col = (isC ? a.c_col0 : a.b_col0) + g * kN + (piece & 15) * 8;
             uint32_t w4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
