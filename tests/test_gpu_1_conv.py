@@ -37,6 +37,8 @@ CASES = [
     (2, 200, 264, 4, BF16, True, 4, "silu"),  # packed sequences
     (1, 77, 13, 3, BF16, True, 3, None),      # odd channel count: scalar path
     (2, 70, 18, 4, BF16, True, 2, "silu"),    # C % 4 = 2: vector path, one partial wavefront
+    (1, 100, 24, 8, BF16, True, 0, "silu"),   # widest conv over whole runs after the first
+    (1, 70, 20, 2, BF16, True, 2, None),      # narrowest conv, vector path, packed sequences
     (3, 2, 16, 4, BF16, True, 0, "silu"),     # L < K-1: F keeps state entries
     (2, 1, 8, 2, F32, False, 0, None),
     (2, 45, 40, 8, BF16, True, 2, "silu"),    # widest conv

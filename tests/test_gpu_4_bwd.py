@@ -38,6 +38,8 @@ CONV_CASES = [
     (1, 1, 4, 5, F32, "silu", True, True, 0),
     (3, 64, 33, 4, BF16, "none", False, False, 0),    # exactly one run
     (2, 150, 18, 4, BF16, "silu", True, True, 2),     # C % 4 = 2: vector path, partial wavefront
+    (1, 150, 10, 2, BF16, "silu", True, True, 0),     # narrowest conv on the vector path
+    (1, 300, 12, 8, BF16, "none", True, True, 3),     # widest: head and tail steps of K-1 = 7
 ]
 
 
