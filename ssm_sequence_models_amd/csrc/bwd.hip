@@ -204,7 +204,7 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
     // the wave index through readfirstlane: the compiler then keeps the run's token bounds in
     // scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t c4 = (static_cast<int64_t>(blockIdx.x) * 64 + lane) * V;
+    const int64_t cv = (static_cast<int64_t>(blockIdx.x) * 64 + lane) * V;
     const int r = 4 * static_cast<int>(blockIdx.y) + wave;
     const int64_t b = blockIdx.z;
     float dwp[K][V], dbp[V];
@@ -214,7 +214,7 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
 #pragma unroll
         for (int k = 0; k < K; ++k) dwp[k][j] = 0.0f;
     }
-    if (c4 < C && r < nruns) {
+    if (cv < C && r < nruns) {
     const int64_t t0 = static_cast<int64_t>(r) * kConvBwdRun;
     const int64_t t1 = min(t0 + kConvBwdRun, L);
     // The set-up loads carry no branches around them, so they are in flight together: the
@@ -225,22 +225,22 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
 #pragma unroll
     for (int j = 0; j < V; ++j) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) wk[k][j] = w[(c4 + j) * K + k];
-        const float bq = bsrc[c4 + j];
+        for (int k = 0; k < K; ++k) wk[k][j] = w[(cv + j) * K + k];
+        const float bq = bsrc[cv + j];
         beta[j] = bias ? bq : 0.0f;
     }
     const int32_t* sq = seq ? seq + b * L : nullptr;
     const int32_t id0 = sq ? sq[0] : 0;
     auto sid = [&](int64_t s) -> int32_t { return sq ? sq[s < 0 ? 0 : s] : 0; };
     auto load4 = [&](const uint16_t* p, int64_t t, float (&v)[V]) {
-        VQ::unpack(VQ::ld(p + (b * L + t) * C + c4), v);
+        VQ::unpack(VQ::ld(p + (b * L + t) * C + cv), v);
     };
     Q hx[K - 1], hg[K - 1];
 #pragma unroll
     for (int k = 0; k < K - 1; ++k) {
         const int64_t tc = min(t0 + k, L - 1);
-        hx[k] = VQ::ld(x + (b * L + tc) * C + c4);
-        hg[k] = VQ::ld(dy + (b * L + tc) * C + c4);
+        hx[k] = VQ::ld(x + (b * L + tc) * C + cv);
+        hg[k] = VQ::ld(dy + (b * L + tc) * C + cv);
     }
 
     float xv[K][V];   // inputs of output t: x indices t-K+1 .. t
@@ -248,7 +248,7 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
     if (t0 >= K - 1) {
         Q hq[K - 1];
 #pragma unroll
-        for (int k = 0; k < K - 1; ++k) hq[k] = VQ::ld(x + (b * L + t0 - (K - 1) + k) * C + c4);
+        for (int k = 0; k < K - 1; ++k) hq[k] = VQ::ld(x + (b * L + t0 - (K - 1) + k) * C + cv);
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) {
             VQ::unpack(hq[k], xv[k + 1]);
@@ -263,7 +263,7 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
             } else {
 #pragma unroll
                 for (int j = 0; j < V; ++j)
-                    xv[k + 1][j] = init ? bf16_to_f32(init[(b * C + c4 + j) * (K - 1) + (K - 1) + s_]) : 0.0f;
+                    xv[k + 1][j] = init ? bf16_to_f32(init[(b * C + cv + j) * (K - 1) + (K - 1) + s_]) : 0.0f;
             }
             xs[k + 1] = sid(s_);
         }
@@ -360,9 +360,9 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
             if (dfin && s_ + K - 1 >= L) {
 #pragma unroll
                 for (int j = 0; j < V; ++j)
-                    v[j] += bf16_to_f32(dfin[(b * C + c4 + j) * (K - 1) + (s_ + K - 1 - L)]);
+                    v[j] += bf16_to_f32(dfin[(b * C + cv + j) * (K - 1) + (s_ + K - 1 - L)]);
             }
-            VQ::st_stream(dx + (b * L + s_) * C + c4, v);
+            VQ::st_stream(dx + (b * L + s_) * C + cv, v);
         }
     };
     // Tokens ta .. tb-1 (all inside the run, at least K-1 after its start) in groups of
@@ -395,16 +395,16 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
         Q xq[G], gq[G];
 #pragma unroll
         for (int u = 0; u < G; ++u) {
-            xq[u] = VQ::ld_stream(x + (b * L + t + u) * C + c4);
-            gq[u] = VQ::ld_stream(dy + (b * L + t + u) * C + c4);
+            xq[u] = VQ::ld_stream(x + (b * L + t + u) * C + cv);
+            gq[u] = VQ::ld_stream(dy + (b * L + t + u) * C + cv);
         }
         for (; t + G <= tb; t += G) {
             Q xn[G], gn[G];
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 const int64_t tt = t + G + u;
-                xn[u] = tt < L ? VQ::ld_stream(x + (b * L + tt) * C + c4) : Q{};
-                gn[u] = tt < L ? VQ::ld_stream(dy + (b * L + tt) * C + c4) : Q{};
+                xn[u] = tt < L ? VQ::ld_stream(x + (b * L + tt) * C + cv) : Q{};
+                gn[u] = tt < L ? VQ::ld_stream(dy + (b * L + tt) * C + cv) : Q{};
             }
 #pragma unroll
             for (int u = 0; u < G; ++u) {
@@ -450,7 +450,7 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
 #pragma unroll
                         for (int j = 0; j < V; ++j) v[j] = __builtin_fmaf(dlw[u + m][j], wk[K - 1 - m][j], v[j]);
                     }
-                VQ::st_stream(dx + (b * L + s_) * C + c4, v);
+                VQ::st_stream(dx + (b * L + s_) * C + cv, v);
             }
 #pragma unroll
             for (int j = 0; j < K - 1; ++j) {
@@ -495,8 +495,8 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
 #pragma unroll
                 for (int t = 0; t <= jj; ++t)
                     if (t < L && (!sq || dss[t] == id0)) v = __builtin_fmaf(dsd[t][j], wk[jj - t][j], v);
-                if (dfin && jj >= L) v += bf16_to_f32(dfin[(b * C + c4 + j) * (K - 1) + (jj - L)]);
-                dinit[(b * C + c4 + j) * (K - 1) + jj] = f32_to_bf16(v);
+                if (dfin && jj >= L) v += bf16_to_f32(dfin[(b * C + cv + j) * (K - 1) + (jj - L)]);
+                dinit[(b * C + cv + j) * (K - 1) + jj] = f32_to_bf16(v);
             }
         }
     }
@@ -509,9 +509,9 @@ conv1d_bwd_bf16vec_kernel(const uint16_t* x, const float* w, const float* bias,
         red[wave][K][j][lane] = dbp[j];
     }
     __syncthreads();
-    if (wave == 0 && c4 < C) {
+    if (wave == 0 && cv < C) {
         const int64_t ngroups = (nruns + 3) / 4;
-        float* pp = part + ((b * ngroups + blockIdx.y) * C + c4) * (K + 1);
+        float* pp = part + ((b * ngroups + blockIdx.y) * C + cv) * (K + 1);
 #pragma unroll
         for (int j = 0; j < V; ++j)
 #pragma unroll
