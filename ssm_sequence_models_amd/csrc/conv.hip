@@ -273,10 +273,12 @@ conv1d_fwd_bf16x2_kernel(const uint16_t* __restrict__ x, const float* __restrict
             wid[K - 1 + u] = ia[u];
         }
     };
-    // One group; FULL groups lie inside the run and skip the per-token bound checks.  Bit
-    // 2*kGroup2-1 - (V*u + v) of the result flags output (token tg+u, channel c0+v).
-    auto group = [&](int64_t tg, auto full) -> uint32_t {
+    // One group; FULL groups lie inside the run and skip the per-token bound checks; MASK
+    // zeroes the taps from another sequence.  Bit 2*kGroup2-1 - (V*u + v) of the result flags
+    // output (token tg+u, channel c0+v).
+    auto group_body = [&](int64_t tg, auto full, auto mask) -> uint32_t {
         constexpr bool FULL = decltype(full)::value;
+        constexpr bool MASK = decltype(mask)::value;
         uint32_t near = 0;
 #pragma unroll
         for (int u = 0; u < kGroup2; ++u) {
@@ -291,7 +293,7 @@ conv1d_fwd_bf16x2_kernel(const uint16_t* __restrict__ x, const float* __restrict
                 double acc = bv[v];
 #pragma unroll
                 for (int k = 0; k < K - 1; ++k) {
-                    const double tap = (!HAS_SEQ || wid[u + k] == wid[u + K - 1]) ? win[u + k][v] : 0.0;
+                    const double tap = (!MASK || wid[u + k] == wid[u + K - 1]) ? win[u + k][v] : 0.0;
                     acc = fma(wr[v][k], tap, acc);
                 }
                 z[v] = fma(wr[v][K - 1], win[u + K - 1][v], acc);
@@ -316,6 +318,19 @@ conv1d_fwd_bf16x2_kernel(const uint16_t* __restrict__ x, const float* __restrict
             wid[j] = wid[kGroup2 + j];
         }
         return near;
+    };
+    // sequence ids are wave-uniform: with SiLU, a window inside one sequence (the usual case)
+    // takes the unmasked body, so only windows that cross a boundary pay for the per-tap
+    // selects (the identity kernels and K = 8 keep one masked body: two bodies spill there)
+    auto group = [&](int64_t tg, auto full) -> uint32_t {
+        if constexpr (HAS_SEQ && SILU && K <= 7) {
+            bool same = true;
+#pragma unroll
+            for (int j = 1; j < kGroup2 + K - 1; ++j) same = same && wid[j] == wid[0];
+            if (!same) return group_body(tg, full, std::true_type{});
+            return group_body(tg, full, std::false_type{});
+        }
+        return group_body(tg, full, std::bool_constant<HAS_SEQ>{});
     };
     static_assert(V * kGroup2 <= 32, "flag mask");
     __shared__ uint32_t flags[kGroupsPerRun][kConvThreads];
